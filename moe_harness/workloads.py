@@ -1,0 +1,154 @@
+"""Workload shapes and seeded synthetic inputs for the fused MoE forward pass.
+
+This module holds no arithmetic of the method.  It only fixes shapes, value distributions and a
+seeded generator, and it is the one module that both the GPU path's tests and the CPU oracle
+receive their inputs from.
+
+Shapes follow the model-shaped workloads of the TileOPs "MoE" benchmark page (FusedMoEFwd and
+FusedMoESharedExpertFwd tables): Qwen3-30B decode, Qwen3-235B batch, DeepSeek-V3 grouped
+prefill and Kimi-K2 with a shared expert, plus a tiny case.  The pages' workloads are themselves
+synthetic tensors of these shapes; no dataset is involved.
+
+Distributions: hidden_states ~ N(0,1) rounded to bf16; gating_output ~ N(0,1) f32;
+correction_bias ~ N(0, 0.1^2) f32; every weight ~ N(0, 1/fan_in) (std 1/sqrt(fan_in)) rounded
+to bf16, fan_in = H for w_gate_up and shared_w_gate_up, F for w_down, S for shared_w_down.
+Rounding to bf16 is torch's f32 -> bf16 conversion (nearest-even).
+
+Seeding: seed 42 by default; each tensor draws from its own torch generator seeded with
+``seed * 1000 + stream`` (streams: hidden 1, gating 2, bias 3, w_gate_up 4, w_down 5,
+shared_w_gate_up 6, shared_w_down 7), filled one expert slice at a time on the target device.
+The same (seed, device type, shape) always gives the same bytes; CPU and GPU generators give
+different streams, so a test draws once and hands the same bytes to both sides.
+"""
+from dataclasses import dataclass, replace
+from typing import Optional
+
+import torch
+
+STREAM_HIDDEN = 1
+STREAM_GATING = 2
+STREAM_BIAS = 3
+STREAM_W_GATE_UP = 4
+STREAM_W_DOWN = 5
+STREAM_SHARED_GATE_UP = 6
+STREAM_SHARED_DOWN = 7
+STREAM_SKEW = 8
+
+
+@dataclass(frozen=True)
+class MoEConfig:
+    name: str
+    T: int            # tokens
+    H: int            # hidden size
+    E: int            # experts
+    F: int            # expert intermediate size
+    k: int            # top_k
+    scoring: str = "softmax"       # "softmax" | "sigmoid"
+    renormalize: bool = True
+    num_expert_group: int = 1
+    topk_group: int = 1
+    rsf: float = 1.0               # routed_scaling_factor
+    bias: bool = False             # correction_bias present
+    S: int = 0                     # shared expert intermediate size (0 = none)
+
+    def with_tokens(self, T: int) -> "MoEConfig":
+        return replace(self, T=T)
+
+
+CONFIGS = {
+    "tiny": MoEConfig("tiny", T=4, H=128, E=8, F=64, k=2),
+    "qwen3-30b-decode": MoEConfig("qwen3-30b-decode", T=32, H=2048, E=128, F=768, k=8),
+    "qwen3-235b-batch": MoEConfig("qwen3-235b-batch", T=512, H=4096, E=128, F=1536, k=8),
+    "ds-v3-grouped-prefill": MoEConfig("ds-v3-grouped-prefill", T=4096, H=7168, E=256, F=2048,
+                                       k=8, scoring="sigmoid", num_expert_group=8,
+                                       topk_group=4, rsf=2.5, bias=True),
+    "kimi-k2-shared": MoEConfig("kimi-k2-shared", T=512, H=7168, E=384, F=2048, k=8,
+                                scoring="sigmoid", rsf=2.827, bias=True, S=18432),
+}
+
+# the configuration the benchmark times by default: Qwen3-30B-style decode, 32 tokens
+BENCH_CONFIG = "qwen3-30b-decode"
+
+
+def _gen(device, seed: int, stream: int) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 1000 + int(stream))
+    return g
+
+
+def _normal(shape, std: float, dtype, device, seed: int, stream: int) -> torch.Tensor:
+    """N(0, std^2) samples, drawn as f32, scaled, converted to ``dtype``; filled slice by slice
+    along dim 0 so large weight tensors never need a full f32 copy."""
+    g = _gen(device, seed, stream)
+    out = torch.empty(shape, dtype=dtype, device=device)
+    if len(shape) == 0 or shape[0] == 0:
+        return out
+    rows = shape[0]
+    per = 1
+    for s in shape[1:]:
+        per *= s
+    chunk = max(1, (1 << 26) // max(per, 1))  # about 64M values per draw
+    for r0 in range(0, rows, chunk):
+        r1 = min(rows, r0 + chunk)
+        v = torch.randn((r1 - r0,) + tuple(shape[1:]), generator=g, device=device,
+                        dtype=torch.float32)
+        if std != 1.0:
+            v.mul_(std)
+        out[r0:r1].copy_(v.to(dtype))
+        del v
+    return out
+
+
+def make_inputs(cfg: MoEConfig, device="cpu", seed: int = 42, weights: bool = True,
+                num_tokens: Optional[int] = None) -> dict:
+    """Seeded synthetic tensors for ``cfg`` on ``device``.
+
+    Returns a dict with hidden_states [T,H] bf16, gating_output [T,E] f32, correction_bias [E]
+    f32 or None, w_gate_up [E,2F,H] bf16, w_down [E,H,F] bf16 and, for S > 0,
+    shared_w_gate_up [2S,H] / shared_w_down [H,S] bf16.  ``num_tokens`` overrides T (token
+    sweeps); weights do not depend on it.  ``weights=False`` skips the weight tensors."""
+    T = cfg.T if num_tokens is None else int(num_tokens)
+    H, E, F, S = cfg.H, cfg.E, cfg.F, cfg.S
+    d = {
+        "hidden_states": _normal((T, H), 1.0, torch.bfloat16, device, seed, STREAM_HIDDEN),
+        "gating_output": _normal((T, E), 1.0, torch.float32, device, seed, STREAM_GATING),
+        "correction_bias": (_normal((E,), 0.1, torch.float32, device, seed, STREAM_BIAS)
+                            if cfg.bias else None),
+    }
+    if weights:
+        d["w_gate_up"] = _normal((E, 2 * F, H), H ** -0.5, torch.bfloat16, device, seed,
+                                 STREAM_W_GATE_UP)
+        d["w_down"] = _normal((E, H, F), F ** -0.5, torch.bfloat16, device, seed, STREAM_W_DOWN)
+        if S > 0:
+            d["shared_w_gate_up"] = _normal((2 * S, H), H ** -0.5, torch.bfloat16, device, seed,
+                                            STREAM_SHARED_GATE_UP)
+            d["shared_w_down"] = _normal((H, S), S ** -0.5, torch.bfloat16, device, seed,
+                                         STREAM_SHARED_DOWN)
+    return d
+
+
+def random_topk_ids(T: int, k: int, E: int, seed: int = 42, device="cpu",
+                    pad_fraction: float = 0.0, allow_repeats: bool = False) -> torch.Tensor:
+    """Seeded synthetic topk_ids [T,k] int32 for the routing-given entry points: k distinct
+    experts per token (or independent draws with ``allow_repeats``), a fraction of entries
+    replaced by -1 padding routes."""
+    g = _gen("cpu", seed, 9)
+    if allow_repeats:
+        ids = torch.randint(0, E, (T, k), generator=g, dtype=torch.int64)
+    else:
+        ids = torch.argsort(torch.rand((T, E), generator=g), dim=1)[:, :k]
+    if pad_fraction > 0.0:
+        mask = torch.rand((T, k), generator=g) < pad_fraction
+        ids = torch.where(mask, torch.full_like(ids, -1), ids)
+    return ids.to(torch.int32).to(device)
+
+
+def random_topk_weights(T: int, k: int, seed: int = 42, device="cpu") -> torch.Tensor:
+    """Seeded positive route weights [T,k] f32 in [0.05, 1)."""
+    g = _gen("cpu", seed, 10)
+    return (torch.rand((T, k), generator=g) * 0.95 + 0.05).to(torch.float32).to(device)
+
+
+def to_u16(t: torch.Tensor):
+    """bf16 tensor (any device) -> numpy uint16 bit patterns on the host."""
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view("uint16")

@@ -1,0 +1,168 @@
+"""CPU oracle of the fused MoE forward pass -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may use
+this package.  It wraps ``moe_oracle.c`` (plain C11 + OpenMP, double precision) with ctypes and
+numpy; it imports nothing from the GPU package and the GPU package imports nothing from it.
+
+Arrays are numpy.  bf16 tensors travel as ``uint16`` bit patterns.
+
+Functions (each follows the passage cited in ``moe_oracle.c``):
+  route(gating, bias, k, scoring, renormalize, num_expert_group, topk_group, rsf)
+      -> (topk_ids int32 [T,k], topk_weights float32 [T,k])
+  align_sort(topk_ids, num_experts, block_m) -> dict of int32 arrays
+  experts(x, w_gate_up, w_down, topk_ids, topk_weights, shared_w_gate_up=None,
+          shared_w_down=None, tokens=None, num_threads=0) -> (acc float64 [n,H], out uint16 [n,H])
+  forward(...) = route + experts, the whole pass
+  double_to_bf16(values) -> uint16 (one rounding, nearest-even)
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmoe_oracle.so")
+_lib = None
+
+SOFTMAX = 0
+SIGMOID = 1
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _build
+        _build.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.oracle_route.argtypes = [_P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_double, _P, _P]
+    lib.oracle_route.restype = _I
+    lib.oracle_align_sort.argtypes = [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P]
+    lib.oracle_align_sort.restype = _I
+    lib.oracle_experts.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _I,
+                                   _P, _P, _I]
+    lib.oracle_experts.restype = _I
+    lib.oracle_double_to_bf16.argtypes = [ctypes.c_double]
+    lib.oracle_double_to_bf16.restype = ctypes.c_uint16
+    lib.oracle_max_threads.argtypes = []
+    lib.oracle_max_threads.restype = _I
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def _scoring_code(scoring):
+    if isinstance(scoring, str):
+        return {"softmax": SOFTMAX, "sigmoid": SIGMOID}[scoring]
+    return int(scoring)
+
+
+def route(gating, bias=None, k=2, scoring="softmax", renormalize=True, num_expert_group=1,
+          topk_group=1, rsf=1.0):
+    g = _c(gating, np.float32)
+    T, E = g.shape
+    b = None if bias is None else _c(bias, np.float32)
+    ids = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float32)
+    st = _load().oracle_route(_ptr(g), _ptr(b), T, E, k, _scoring_code(scoring),
+                              int(bool(renormalize)), num_expert_group, topk_group, float(rsf),
+                              _ptr(ids), _ptr(w))
+    if st != 0:
+        raise ValueError("oracle_route rejected its arguments (status %d)" % st)
+    return ids, w
+
+
+def align_sort(topk_ids, num_experts, block_m):
+    ids = _c(topk_ids, np.int32)
+    T, k = ids.shape
+    P = T * k
+    sorted_ids = np.empty(P + num_experts * (block_m - 1), np.int32)
+    offsets = np.empty(num_experts + 1, np.int32)
+    tile_expert = np.empty(P // block_m + num_experts, np.int32)
+    inverse = np.empty(P, np.int32)
+    n_tiles = np.empty(1, np.int32)
+    st = _load().oracle_align_sort(_ptr(ids), T, k, num_experts, block_m, _ptr(sorted_ids),
+                                   _ptr(offsets), _ptr(tile_expert), _ptr(inverse), _ptr(n_tiles))
+    if st != 0:
+        raise ValueError("oracle_align_sort rejected its arguments (status %d)" % st)
+    return {"sorted_route_ids": sorted_ids, "expert_offsets": offsets,
+            "tile_expert": tile_expert, "inverse_pos": inverse, "n_tiles": int(n_tiles[0])}
+
+
+def experts(x, w_gate_up, w_down, topk_ids, topk_weights, shared_w_gate_up=None,
+            shared_w_down=None, tokens=None, num_threads=0):
+    """x [T,H] u16; w_gate_up [E,2F,H] u16; w_down [E,H,F] u16; ids/weights [T,k].
+
+    tokens: optional list of token indices to evaluate (rows of the result follow it).
+    Returns (acc float64 [n,H] before rounding, out uint16 [n,H] bf16 bits)."""
+    x = _c(x, np.uint16)
+    w_gate_up = _c(w_gate_up, np.uint16)
+    w_down = _c(w_down, np.uint16)
+    ids = _c(topk_ids, np.int32)
+    w = _c(topk_weights, np.float32)
+    T, H = x.shape
+    E, F2, H2 = w_gate_up.shape
+    F = F2 // 2
+    assert H2 == H and F2 == 2 * F and w_down.shape == (E, H, F), "weight shapes"
+    k = ids.shape[1]
+    assert ids.shape == (T, k) and w.shape == (T, k)
+    S = 0
+    sgu = sd = None
+    if shared_w_gate_up is not None:
+        sgu = _c(shared_w_gate_up, np.uint16)
+        sd = _c(shared_w_down, np.uint16)
+        S = sgu.shape[0] // 2
+        assert sgu.shape == (2 * S, H) and sd.shape == (H, S), "shared weight shapes"
+    if tokens is None:
+        tok = None
+        n = T
+    else:
+        tok = _c(tokens, np.int32)
+        assert tok.ndim == 1 and (tok.size == 0 or (tok.min() >= 0 and tok.max() < T))
+        n = tok.size
+    acc = np.empty((n, H), np.float64)
+    out = np.empty((n, H), np.uint16)
+    st = _load().oracle_experts(_ptr(x), _ptr(w_gate_up), _ptr(w_down), _ptr(ids), _ptr(w),
+                                _ptr(sgu), _ptr(sd), S, H, E, F, k, _ptr(tok), n, _ptr(acc),
+                                _ptr(out), int(num_threads))
+    if st != 0:
+        raise ValueError("oracle_experts failed (status %d)" % st)
+    return acc, out
+
+
+def forward(x, gating, w_gate_up, w_down, bias=None, k=2, scoring="softmax", renormalize=True,
+            num_expert_group=1, topk_group=1, rsf=1.0, shared_w_gate_up=None,
+            shared_w_down=None, tokens=None, num_threads=0):
+    """The whole pass: route every token, then evaluate the experts for ``tokens``."""
+    ids, w = route(gating, bias, k, scoring, renormalize, num_expert_group, topk_group, rsf)
+    acc, out = experts(x, w_gate_up, w_down, ids, w, shared_w_gate_up, shared_w_down, tokens,
+                       num_threads)
+    return {"topk_ids": ids, "topk_weights": w, "acc": acc, "out": out}
+
+
+def double_to_bf16(values):
+    lib = _load()
+    v = np.asarray(values, np.float64)
+    flat = np.array([lib.oracle_double_to_bf16(float(a)) for a in v.ravel()], np.uint16)
+    return flat.reshape(v.shape)
+
+
+def bf16_bits_to_float(bits):
+    """uint16 bf16 patterns -> float32 values (exact widening)."""
+    b = np.asarray(bits, np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32)

@@ -1,0 +1,306 @@
+#!/usr/bin/env python
+"""Benchmark of the fused MoE forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+
+A step is one whole fused MoE forward (routing, align/sort, gate-up GEMM + SiLU*up, down GEMM,
+shared expert if the workload has one, weighted combine) over one batch of seeded synthetic
+inputs already resident in HBM.  The default workload is the Qwen3-30B-style decode layer
+(T=32 tokens, H=2048, E=128 experts, F=768, top-8 softmax routing).
+
+To keep the expert weights cold (the weights are what the pass streams), the inputs come in R
+rotating sets -- separate weights, hidden states and gating per set -- with R chosen so the
+sets together exceed 16x the 256 MB last-level cache; step i uses set i mod R.
+
+Two timed loops of K steps each (W warm-up steps first), bracketed by synchronize():
+  1. fused_moe_fwd calls -> ``value`` / ``ms_per_step``;
+  2. the same pass as moe_route + fused_moe_experts_stage calls with HIP events between the
+     stages on the stream they run on -> per-stage device times, and the dominant kernel's
+     roofline (gate-up GEMM: its algorithmic bytes / its average duration vs 8 TB/s HBM).
+The CPU oracle is then timed on the host's cores on a bounded sample of the same workload.
+Prints ONE JSON line on stdout (diagnostics go to stderr).
+"""
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+LLC_BYTES = 256 * 2 ** 20
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default=None)
+    ap.add_argument("--rotate", type=int, default=0, help="input sets (0 = automatic)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d "
+              "requested). Run with --gpus 1." % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mixture_experts_forward_amd as moe
+    from moe_harness import perfmodel
+    from moe_harness.workloads import BENCH_CONFIG, CONFIGS, make_inputs
+
+    cfg = CONFIGS[args.config or BENCH_CONFIG]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    moe.lib()
+
+    wbytes = cfg.E * 6.0 * cfg.H * cfg.F + 6.0 * cfg.H * cfg.S
+    R = args.rotate or max(1, min(8, math.ceil(16 * LLC_BYTES / wbytes)))
+    log("workload %s, %d input sets of %.2f GB weights" % (cfg.name, R, wbytes / 1e9))
+    sets = [make_inputs(cfg, dev, seed=42 + i) for i in range(R)]
+    torch.cuda.synchronize()
+
+    S = cfg.S
+    p = moe.make_params(cfg.T, cfg.H, cfg.E, cfg.F, cfg.k, cfg.scoring, cfg.renormalize,
+                        cfg.num_expert_group, cfg.topk_group, cfg.rsf)
+    ws = torch.empty(max(256, moe.workspace_bytes(p, S)), dtype=torch.uint8, device=dev)
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
+    ids = [torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev) for _ in range(R)]
+    wts = [torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev) for _ in range(R)]
+
+    def fused_step(i):
+        d = sets[i % R]
+        if S > 0:
+            moe.fused_moe_shared_fwd(d["hidden_states"], d["gating_output"], d["w_gate_up"],
+                                     d["w_down"], d["shared_w_gate_up"], d["shared_w_down"],
+                                     cfg.k, d["correction_bias"], cfg.scoring, cfg.renormalize,
+                                     cfg.num_expert_group, cfg.topk_group, cfg.rsf, out=out,
+                                     workspace=ws)
+        else:
+            moe.fused_moe_fwd(d["hidden_states"], d["gating_output"], d["w_gate_up"],
+                              d["w_down"], cfg.k, d["correction_bias"], cfg.scoring,
+                              cfg.renormalize, cfg.num_expert_group, cfg.topk_group, cfg.rsf,
+                              out=out, workspace=ws)
+
+    stages = [moe.STAGE_ALIGN, moe.STAGE_GATE_UP, moe.STAGE_DOWN]
+    if S > 0:
+        stages.append(moe.STAGE_SHARED)
+    stages.append(moe.STAGE_COMBINE)
+    names = ["route"] + [moe.STAGE_NAMES[s] for s in stages]
+
+    def staged_step(i, events=None):
+        d = sets[i % R]
+        j = i % R
+        if events is not None:
+            events[0].record()
+        st = moe.lib().moe_route(moe._ptr(d["gating_output"]), moe._ptr(d["correction_bias"]),
+                                 ctypes.byref(p), moe._ptr(ids[j]),
+                                 moe._ptr(wts[j]), moe._stream(dev))
+        if st != 0:
+            raise moe.MoEError(st, "moe_route")
+        if events is not None:
+            events[1].record()
+        for n, s in enumerate(stages):
+            moe.fused_moe_experts_stage(s, p, d["hidden_states"], d["w_gate_up"], d["w_down"],
+                                        ids[j], wts[j], out, ws, d.get("shared_w_gate_up"),
+                                        d.get("shared_w_down"))
+            if events is not None:
+                events[n + 2].record()
+
+    # ---- loop 1: fused calls
+    for i in range(args.warmup):
+        fused_step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        fused_step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fused_ms = e0.elapsed_time(e1) / args.steps
+    log("fused: %.4f ms/step (device), %.4f ms/step (wall)" % (fused_ms,
+                                                                 wall * 1e3 / args.steps))
+
+    # ---- loop 2: staged calls with events between the stages
+    for i in range(args.warmup):
+        staged_step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        staged_step(i, evs[i])
+    torch.cuda.synchronize()
+    per_stage = {n: 0.0 for n in names}
+    for i in range(args.steps):
+        for n, name in enumerate(names):
+            per_stage[name] += evs[i][n].elapsed_time(evs[i][n + 1]) / args.steps
+    staged_ms = evs[0][0].elapsed_time(evs[-1][-1]) / args.steps
+    log("staged: %.4f ms/step; per stage (ms): %s" % (
+        staged_ms, ", ".join("%s %.4f" % (k, v) for k, v in per_stage.items())))
+
+    # ---- roofline of the pass and of the dominant kernel, from the realized routing
+    touched = []
+    loads = []
+    for j in range(R):
+        idj = ids[j].cpu().numpy()
+        touched.append(perfmodel.touched_experts(idj, cfg.E))
+        loads.append(perfmodel.load_stats(idj, cfg.E))
+    touched_mean = float(np.mean([touched[i % R] for i in range(args.steps)]))
+    P = cfg.T * cfg.k
+    pass_bytes = perfmodel.algorithmic_bytes(cfg.T, cfg.H, cfg.E, cfg.F, cfg.k, touched_mean,
+                                             cfg.S, cfg.bias)
+    pass_flops = perfmodel.flops(cfg.T, cfg.k, cfg.H, cfg.F, cfg.S)
+    gu_bytes = touched_mean * 4.0 * cfg.H * cfg.F + 2.0 * cfg.T * cfg.H + 2.0 * P * cfg.F
+    gu_ms = per_stage["gate_up"]
+    gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
+    peak_gbs = perfmodel.HBM_PEAK_BYTES_PER_S / 1e9
+    traffic = read_traffic(cfg.name)
+
+    # ---- CPU baseline: the oracle on this host
+    cpu = None if args.no_cpu_baseline else cpu_baseline(cfg, sets[0], args.cpu_seconds)
+
+    ms = fused_ms
+    base = BASELINE_MS.get(cfg.name)
+    line = {
+        "metric": "fused-MoE fwd ms; achieved TB/s (decode) / TFLOP/s (prefill) vs roofline",
+        "value": round(ms, 5),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": round(ms / base["ms"], 4) if base else None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; %d rotating input sets)" % R,
+        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "F": cfg.F,
+                   "top_k": cfg.k, "scoring": cfg.scoring, "renormalize": cfg.renormalize,
+                   "num_expert_group": cfg.num_expert_group, "topk_group": cfg.topk_group,
+                   "routed_scaling_factor": cfg.rsf, "correction_bias": cfg.bias,
+                   "shared_inter": cfg.S, "parallelism": "single GPU"},
+        "achieved_tbps": round(pass_bytes / (ms * 1e-3) / 1e12, 4),
+        "achieved_tflops": round(pass_flops / (ms * 1e-3) / 1e12, 3),
+        "hbm_roofline_frac": round(pass_bytes / (ms * 1e-3) / perfmodel.HBM_PEAK_BYTES_PER_S, 4),
+        "mfma_roofline_frac": round(pass_flops / (ms * 1e-3) /
+                                    perfmodel.BF16_MFMA_PEAK_FLOP_PER_S, 4),
+        "algorithmic_bytes": pass_bytes,
+        "flops": pass_flops,
+        "touched_experts": touched_mean,
+        "rows_per_expert": loads[0],
+        "staged_ms_per_step": round(staged_ms, 5),
+        "stage_ms": {k: round(v, 5) for k, v in per_stage.items()},
+        "roofline": {"kernel": "gate_up (k_ws_gemm gate-up)", "bound": "hbm",
+                     "achieved": round(gu_gbs, 1), "peak": peak_gbs, "unit": "GB/s",
+                     "frac": round(gu_gbs / peak_gbs, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": gu_bytes},
+        "cpu_baseline": cpu,
+        "baseline_context": base,
+    }
+    print(json.dumps(line), flush=True)
+
+
+# The pages' own figure for this exact workload (another, unnamed GPU): context only.
+BASELINE_MS = {
+    "qwen3-30b-decode": {"ms": 0.2656, "source": "TileOPs MoE page, FusedMoEFwd "
+                         "qwen3-30b-decode-b32 bf16", "hardware": "not named on the page"},
+    "qwen3-235b-batch": {"ms": 1.2042, "source": "TileOPs MoE page, FusedMoEFwd "
+                         "qwen3-235b-decode bf16", "hardware": "not named on the page"},
+    "ds-v3-grouped-prefill": {"ms": 7.1078, "source": "TileOPs MoE page, FusedMoEFwd "
+                              "ds-v3-grouped-prefill bf16", "hardware": "not named on the page"},
+    "kimi-k2-shared": {"ms": 5.0723, "source": "TileOPs MoE page, FusedMoESharedExpertFwd "
+                       "kimi-k2-t512 bf16", "hardware": "not named on the page"},
+}
+
+
+def read_traffic(workload):
+    """HBM traffic of the dominant kernel from the committed rocprofv3 counter summary
+    (profiles/gate_up_<workload>_pmc.txt: a line 'traffic_bytes_per_launch: N' and the
+    library hash it was taken on), or None when absent or taken on another build."""
+    path = os.path.join(PROFILE_DIR, "gate_up_%s_pmc.txt" % workload)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    src = os.path.join(ROOT, "mixture_experts_forward_amd", "csrc", "moe_gemm_ws.hip")
+    h.update(open(src, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(cfg, d, seconds):
+    """The oracle, as it stands, on this host: route every token, evaluate the experts of a
+    sample of tokens; the time is scaled to one whole forward of T tokens."""
+    import numpy as np
+
+    import oracle
+    from moe_harness.workloads import to_u16
+
+    g = d["gating_output"].cpu().numpy()
+    b = None if d["correction_bias"] is None else d["correction_bias"].cpu().numpy()
+    x = to_u16(d["hidden_states"])
+    t0 = time.perf_counter()
+    ids, w = oracle.route(g, b, cfg.k, cfg.scoring, cfg.renormalize, cfg.num_expert_group,
+                          cfg.topk_group, float(np.float32(cfg.rsf)))
+    route_s = time.perf_counter() - t0
+    import torch
+    used = np.unique(ids)
+    sel = torch.as_tensor(used, device=d["w_gate_up"].device)
+    wgu = to_u16(d["w_gate_up"].index_select(0, sel))
+    wd = to_u16(d["w_down"].index_select(0, sel))
+    remap = np.full(cfg.E, -1, np.int64)
+    remap[used] = np.arange(used.size)
+    lids = remap[ids].astype(np.int32)
+    sgu = to_u16(d["shared_w_gate_up"]) if cfg.S else None
+    sd = to_u16(d["shared_w_down"]) if cfg.S else None
+    threads = oracle.max_threads()
+    # calibrate on one token, then size the sample to about `seconds`
+    t0 = time.perf_counter()
+    oracle.experts(x, wgu, wd, lids, w, sgu, sd, tokens=[0])
+    one = max(time.perf_counter() - t0, 1e-6)
+    n = int(max(1, min(cfg.T, seconds * max(1, threads) / one)))
+    tokens = np.linspace(0, cfg.T - 1, n).round().astype(np.int32)
+    t0 = time.perf_counter()
+    oracle.experts(x, wgu, wd, lids, w, sgu, sd, tokens=tokens)
+    exp_s = time.perf_counter() - t0
+    per_forward_ms = (route_s + exp_s * cfg.T / n) * 1e3
+    log("cpu oracle: %d of %d tokens in %.2f s on %d threads -> %.1f ms per forward"
+        % (n, cfg.T, exp_s, threads, per_forward_ms))
+    return {"value": round(per_forward_ms, 2), "unit": "ms", "cores": threads, "kind": "oracle",
+            "sample": "routing of all %d tokens + experts of %d of %d tokens (evenly spaced), "
+                      "scaled to %d tokens" % (cfg.T, n, cfg.T, cfg.T)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,233 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) fused mixture-of-experts forward pass.
+ *
+ * The pass (TileOPs "MoE" benchmark page, FusedMoEFwd / FusedMoESharedExpertFwd):
+ *   route    gating_output [T,E] f32 (+ correction_bias [E] f32) -> top-k ids and f32 weights
+ *   align    stable sort of the T*k routes by expert, segments padded to a row tile
+ *   gate-up  per expert: h = silu(X W_gate^T) * (X W_up^T), bf16 MFMA, f32 accumulate
+ *   down     per expert: y = h W_down^T
+ *   combine  out[t] = bf16( sum_j w[t,j] * y[t,j] (+ shared expert) ), fixed j order
+ *
+ * Conventions for every entry point:
+ *   - Tensors are dense, row-major and contiguous in GPU device memory.  bf16 tensors are
+ *     passed as uint16_t bit patterns.
+ *   - stream is a hipStream_t passed as void* (NULL = the default stream).  Every call only
+ *     enqueues work on that stream; nothing synchronises with the host and nothing is copied
+ *     back to the host.
+ *   - The caller owns every buffer (inputs, outputs, workspace).  The library never allocates,
+ *     frees, caches or keeps a pointer after the call returns, so fixed buffers stay valid for
+ *     graph capture (FlashInfer BF16-activation MoE PR: preallocated sort/workspace buffers
+ *     keep graph addresses stable; invocation-local scratch, no module-global arena).
+ *   - All arguments are validated on the host before anything is enqueued: a call that returns
+ *     an error has launched nothing.  The library never falls back silently to another path.
+ *   - Results are bitwise deterministic for identical inputs: no floating-point atomics; the
+ *     only atomics are integer counters in the align step, whose results do not depend on
+ *     their order.
+ *   - Inputs are assumed finite.  T = 0 returns MOE_OK and enqueues nothing (pointers may then
+ *     be NULL); moe_align_sort is the exception: with T = 0 it still writes its (empty) layout.
+ *   - Route ids outside [0, E) (the -1 padding routes of the aiter MI308 decoding PR,
+ *     "Changes": routes with expert id -1 are skipped) are skipped wherever ids are inputs.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+/* status codes */
+enum {
+    MOE_OK = 0,
+    MOE_ERR_NULL = -1,        /* a required pointer is NULL */
+    MOE_ERR_SHAPE = -2,       /* a size is non-positive (T may be 0) or top_k > num_experts */
+    MOE_ERR_UNSUPPORTED = -3, /* a combination the kernels do not implement (see moe_params) */
+    MOE_ERR_WORKSPACE = -4,   /* workspace smaller than the *_workspace_bytes query */
+    MOE_ERR_LAUNCH = -5       /* the HIP runtime reported an error when enqueueing */
+};
+
+enum { MOE_SCORING_SOFTMAX = 0, MOE_SCORING_SIGMOID = 1 };
+
+/* Path selection for fused_moe_fwd / fused_moe_shared_fwd / fused_moe_experts_fwd.
+ * AUTO: DIRECT when T*k <= MOE_DIRECT_MAX_ROUTES, SORTED otherwise.
+ * DIRECT: no sort; one workgroup per (route, column block) reads topk_ids straight away, the
+ *   first route of each expert gathers every route of that expert (aiter MI308 decoding PR,
+ *   "Changes": direct decoding from topk_ids over tokens x routes).  Requires
+ *   T*k <= MOE_DIRECT_MAX_ROUTES, else MOE_ERR_UNSUPPORTED.
+ * SORTED: align/sort first, then expert-contiguous grouped GEMMs. */
+enum { MOE_PATH_AUTO = 0, MOE_PATH_DIRECT = 1, MOE_PATH_SORTED = 2 };
+#define MOE_DIRECT_MAX_ROUTES 64
+
+/* Attributes of the pass (TileOPs "MoE" page, FusedMoEFwd and FusedTopKFwd attributes).
+ *   num_tokens T >= 0; hidden H; num_experts E; inter F (expert intermediate size); top_k k.
+ *   scoring: MOE_SCORING_SOFTMAX (the page's default when no scoring_func is given) or
+ *     MOE_SCORING_SIGMOID.
+ *   renormalize: 0/1 -- divide the chosen weights by their sum.
+ *   num_expert_group, topk_group: DeepSeek-style grouped top-k; (1, 1) = ungrouped.
+ *   routed_scaling_factor: multiplies every routed weight (after renormalisation); 1 = none.
+ *   path: MOE_PATH_*.
+ * Supported: 1 <= k <= 32, k <= E <= 1024, E % num_expert_group == 0,
+ *   1 <= topk_group <= num_expert_group <= 64, k <= topk_group * E / num_expert_group,
+ *   H % 64 == 0 and F % 64 == 0; softmax only with no correction_bias and no grouping.
+ *   Anything else returns MOE_ERR_UNSUPPORTED (MOE_ERR_SHAPE for non-positive sizes). */
+typedef struct moe_params {
+    int32_t num_tokens;
+    int32_t hidden;
+    int32_t num_experts;
+    int32_t inter;
+    int32_t top_k;
+    int32_t scoring;
+    int32_t renormalize;
+    int32_t num_expert_group;
+    int32_t topk_group;
+    float routed_scaling_factor;
+    int32_t path;
+} moe_params_t;
+
+/* MOE_ABI_VERSION of the loaded library. */
+int moe_abi_version(void);
+
+/* Static, NUL-terminated description of a status code.  Never NULL. */
+const char *moe_status_string(int status);
+
+/* Checks *p against the support rules above without touching the GPU.  correction_bias_given
+ * and shared_inter (S, 0 = no shared expert) take part in the check.  Returns a status. */
+int moe_check_params(const moe_params_t *p, int correction_bias_given, int32_t shared_inter);
+
+/* ---------------------------------------------------------------------------------------
+ * moe_route -- top-k routing (TileOPs "MoE" page, FusedTopKFwd: gating_output [T,E] with
+ * top_k, renormalize, scoring_func, correction_bias [E] f32, num_expert_group, topk_group,
+ * routed_scaling_factor).
+ *   gating_output   [T,E] f32, device.
+ *   correction_bias [E] f32, device, or NULL.  Sigmoid only; it shifts the selection keys
+ *                   and never the weights.
+ *   topk_ids        [T,k] int32, device, written: chosen experts in descending key order
+ *                   (ties: lower expert index).
+ *   topk_weights    [T,k] f32, device, written: score of each chosen expert (softmax
+ *                   probability or sigmoid), divided by the chosen scores' sum if
+ *                   renormalize, times routed_scaling_factor.
+ * Selection keys: softmax selects on the f32 logit; sigmoid on f32(f32(sigmoid(g)) + bias).
+ * A group's score is the f32 sum of its two largest keys; groups and experts tie to the lower
+ * index.  Scores and weights are computed in double and rounded to f32 once.
+ * Errors: MOE_ERR_NULL (gating/ids/weights/p NULL), MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED,
+ * MOE_ERR_LAUNCH.  Only p's T, E, k, scoring, renormalize, grouping and scaling are read. */
+int moe_route(const float *gating_output, const float *correction_bias, const moe_params_t *p,
+              int32_t *topk_ids, float *topk_weights, void *stream);
+
+/* ---------------------------------------------------------------------------------------
+ * moe_align_sort -- expert histogram, padded prefix sum and stable permutation of the routes
+ * (TileOPs "MoE" page, MoEPermuteAlignFwd on topk_ids [T,K] i32; MoEPostPermuteFwd's
+ * inverse_indices [T*K]; block_m = 1 is that page's tight packing with alignment 1).
+ *   topk_ids          [T,k] int32, device.  Route r = t*k + j.  Ids outside [0,E) are
+ *                     skipped.  Repeated ids of one token are each counted.
+ *   block_m           row tile, 1..1024: every expert's segment is padded up to a multiple.
+ *   sorted_route_ids  [T*k + E*(block_m-1)] int32, device, written: route r of each row of
+ *                     the expert-contiguous order, routes of one expert in increasing r;
+ *                     padding and unused rows hold -1.
+ *   expert_offsets    [E+1] int32, device, written: first row of each expert's padded
+ *                     segment; expert_offsets[E] = total padded rows.
+ *   tile_expert       [T*k/block_m + E] int32, device, written: expert of each block_m-row
+ *                     tile, -1 past the last tile.
+ *   inverse_pos       [T*k] int32, device, written: row of route r, -1 for skipped routes.
+ *   n_tiles           [1] int32, device, written: number of tiles (expert_offsets[E]/block_m).
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (T < 0, k < 1, E < 1), MOE_ERR_UNSUPPORTED
+ * (E > 1024, block_m outside 1..1024, T*k >= 2^30), MOE_ERR_LAUNCH. */
+int moe_align_sort(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E, int32_t block_m,
+                   int32_t *sorted_route_ids, int32_t *expert_offsets, int32_t *tile_expert,
+                   int32_t *inverse_pos, int32_t *n_tiles, void *stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Workspace of the fused entry points: device memory the caller allocates (256-byte aligned)
+ * and passes in.  Its size depends on p (T, H, E, F, k, path) and shared_inter; contents on
+ * entry are ignored and on return are unspecified.  One workspace must not be used by two
+ * calls that can run at the same time. */
+size_t fused_moe_workspace_bytes(const moe_params_t *p, int32_t shared_inter);
+
+/* fused_moe_fwd -- the whole pass (TileOPs "MoE" page, FusedMoEFwd: hidden_states [T,H],
+ * gating_output [T,E] f32, w_gate_up [E,2F,H], w_down [E,H,F], optional correction_bias [E]).
+ *   hidden_states  [T,H] bf16.
+ *   gating_output  [T,E] f32.
+ *   w_gate_up      [E,2F,H] bf16: rows [0,F) of each expert are the gate projection,
+ *                  rows [F,2F) the up projection.
+ *   w_down         [E,H,F] bf16.
+ *   correction_bias [E] f32 or NULL.
+ *   out            [T,H] bf16, written (every row; no prior clear needed).
+ *   topk_ids_out   [T,k] int32 or NULL: receives the routing.
+ *   topk_weights_out [T,k] f32 or NULL: receives the route weights.
+ *   workspace / workspace_bytes: see fused_moe_workspace_bytes.
+ * The intermediate h is rounded to bf16 after SiLU(gate)*up, and expert output rows are
+ * rounded to bf16 before the f32 weighted combine.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE,
+ * MOE_ERR_LAUNCH. */
+int fused_moe_fwd(const uint16_t *hidden_states, const float *gating_output,
+                  const uint16_t *w_gate_up, const uint16_t *w_down,
+                  const float *correction_bias, const moe_params_t *p, uint16_t *out,
+                  int32_t *topk_ids_out, float *topk_weights_out, void *workspace,
+                  size_t workspace_bytes, void *stream);
+
+/* fused_moe_shared_fwd -- fused_moe_fwd plus a shared expert added unweighted (TileOPs "MoE"
+ * page, FusedMoESharedExpertFwd: shared_w_gate_up [2S,H], shared_w_down [H,S]).
+ *   shared_w_gate_up [2S,H] bf16 (rows [0,S) gate, [S,2S) up); shared_w_down [H,S] bf16;
+ *   shared_inter S >= 64, S % 64 == 0.  The routed scaling factor does not apply to it.
+ * Other arguments and errors as fused_moe_fwd. */
+int fused_moe_shared_fwd(const uint16_t *hidden_states, const float *gating_output,
+                         const uint16_t *w_gate_up, const uint16_t *w_down,
+                         const float *correction_bias, const uint16_t *shared_w_gate_up,
+                         const uint16_t *shared_w_down, int32_t shared_inter,
+                         const moe_params_t *p, uint16_t *out, int32_t *topk_ids_out,
+                         float *topk_weights_out, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+/* fused_moe_experts_fwd -- the pass with the routing given (TileOPs "MoE" page,
+ * FusedMoEExpertsFwd: hidden_states [T,H], w_gate_up, w_down, topk_weights [T,K] f32,
+ * topk_ids [T,K] i32).  topk_ids may hold -1 (skipped) and repeated ids (each counted).
+ * Only p's T, H, E, F, k and path are read.  Workspace as fused_moe_fwd's with the same p.
+ * Errors as fused_moe_fwd. */
+int fused_moe_experts_fwd(const uint16_t *hidden_states, const uint16_t *w_gate_up,
+                          const uint16_t *w_down, const int32_t *topk_ids,
+                          const float *topk_weights, const moe_params_t *p, uint16_t *out,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------
+ * fused_moe_experts_stage -- one step of the expert part of the pass, on the caller's
+ * workspace, so that each step can be timed or checked on its own.  Calling the stages
+ * MOE_STAGE_ALIGN, MOE_STAGE_GATE_UP, MOE_STAGE_DOWN, MOE_STAGE_SHARED (only with a shared
+ * expert) and MOE_STAGE_COMBINE in that order, on one stream with one workspace, enqueues
+ * exactly the kernels of fused_moe_experts_fwd (or of the expert part of
+ * fused_moe_shared_fwd), with the same results.
+ *   MOE_STAGE_ALIGN    sorted path: moe_align_sort into the workspace; direct path: nothing.
+ *   MOE_STAGE_GATE_UP  gate-up grouped GEMM with the SiLU(gate)*up epilogue -> h (workspace)
+ *                      (TileOPs "MoE" page, MoEGroupedGemmFwd activation=silu_and_mul).
+ *   MOE_STAGE_DOWN     down grouped GEMM -> expert output rows (workspace)
+ *                      (MoEGroupedGemmFwd on w_down [E,H,F]).
+ *   MOE_STAGE_SHARED   shared expert's dense SwiGLU MLP -> its output rows (workspace)
+ *                      (SharedExpertMLPFwd).
+ *   MOE_STAGE_COMBINE  weighted combine -> out (MoEPostPermuteFwd).
+ * Arguments as fused_moe_experts_fwd, plus the shared weights (NULL and shared_inter 0 when
+ * there is no shared expert); each stage reads only what it needs, the others may be NULL.
+ * The workspace size is fused_moe_workspace_bytes(p, shared_inter).
+ * Errors as fused_moe_experts_fwd; an unknown stage, or MOE_STAGE_SHARED without a shared
+ * expert, is MOE_ERR_UNSUPPORTED. */
+enum {
+    MOE_STAGE_ALIGN = 1,
+    MOE_STAGE_GATE_UP = 2,
+    MOE_STAGE_DOWN = 3,
+    MOE_STAGE_SHARED = 4,
+    MOE_STAGE_COMBINE = 5
+};
+int fused_moe_experts_stage(int stage, const uint16_t *hidden_states, const uint16_t *w_gate_up,
+                            const uint16_t *w_down, const int32_t *topk_ids,
+                            const float *topk_weights, const uint16_t *shared_w_gate_up,
+                            const uint16_t *shared_w_down, int32_t shared_inter,
+                            const moe_params_t *p, uint16_t *out, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

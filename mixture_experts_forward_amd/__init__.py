@@ -1,0 +1,284 @@
+"""MI355X-native fused mixture-of-experts forward pass.
+
+Python binding over ``libmoe_mi355x.so`` (the HIP kernels for gfx950 behind the C ABI of
+``include/moe.h``).  This module only marshals arguments: it checks tensor shapes, dtypes and
+devices, allocates outputs and the workspace with torch, and passes raw device pointers and the
+current HIP stream to the library.  Every step of the pass runs in the library's kernels; if
+the library is missing, importing a function raises instead of falling back to anything else.
+
+Entry points (same names as the C ABI):
+  moe_route(gating_output, top_k, ...)                        -> (topk_ids, topk_weights)
+  moe_align_sort(topk_ids, num_experts, block_m)              -> dict of int32 tensors
+  fused_moe_fwd(hidden_states, gating_output, w_gate_up, w_down, top_k, ...) -> out
+  fused_moe_shared_fwd(..., shared_w_gate_up, shared_w_down)  -> out
+  fused_moe_experts_fwd(hidden_states, w_gate_up, w_down, topk_ids, topk_weights) -> out
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
+
+MOE_OK = 0
+SCORING = {"softmax": 0, "sigmoid": 1}
+PATHS = {"auto": 0, "direct": 1, "sorted": 2}
+DIRECT_MAX_ROUTES = 64
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (where, status_string(status), status))
+
+
+class MoEParams(ctypes.Structure):
+    _fields_ = [("num_tokens", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("num_experts", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("scoring", ctypes.c_int32),
+                ("renormalize", ctypes.c_int32), ("num_expert_group", ctypes.c_int32),
+                ("topk_group", ctypes.c_int32), ("routed_scaling_factor", ctypes.c_float),
+                ("path", ctypes.c_int32)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_SZ = ctypes.c_size_t
+
+# symbol -> (restype, argtypes); every function declared in include/moe.h
+SIGNATURES = {
+    "moe_abi_version": (ctypes.c_int, []),
+    "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "moe_check_params": (ctypes.c_int, [_P, ctypes.c_int, _I32]),
+    "moe_route": (ctypes.c_int, [_P, _P, _P, _P, _P, _P]),
+    "moe_align_sort": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P]),
+    "fused_moe_workspace_bytes": (_SZ, [_P, _I32]),
+    "fused_moe_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "fused_moe_shared_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P,
+                                            _P, _SZ, _P]),
+    "fused_moe_experts_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "fused_moe_experts_stage": (ctypes.c_int, [ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _I32,
+                                               _P, _P, _P, _SZ, _P]),
+}
+
+# stages of fused_moe_experts_stage, in the order fused_moe_experts_fwd runs them
+STAGE_ALIGN, STAGE_GATE_UP, STAGE_DOWN, STAGE_SHARED, STAGE_COMBINE = 1, 2, 3, 4, 5
+STAGE_NAMES = {1: "align", 2: "gate_up", 3: "down", 4: "shared", 5: "combine"}
+
+
+def lib():
+    """The loaded library.  Raises if it has not been built (no fallback exists)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("%s is not built; run `python -m mixture_experts_forward_amd.build`"
+                               % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(status):
+    return lib().moe_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(t, name, dtype, shape, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a GPU device, got %s" % (name, t.device))
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def make_params(T, H, E, F, k, scoring="softmax", renormalize=True, num_expert_group=1,
+                topk_group=1, routed_scaling_factor=1.0, path="auto"):
+    return MoEParams(int(T), int(H), int(E), int(F), int(k), SCORING[scoring],
+                     int(bool(renormalize)), int(num_expert_group), int(topk_group),
+                     float(routed_scaling_factor), PATHS[path])
+
+
+def workspace_bytes(params, shared_inter=0):
+    return int(lib().fused_moe_workspace_bytes(ctypes.byref(params), int(shared_inter)))
+
+
+def _workspace(params, shared_inter, device, workspace):
+    n = workspace_bytes(params, shared_inter)
+    if workspace is None:
+        return torch.empty(max(n, 256), dtype=torch.uint8, device=device), n
+    if workspace.dtype != torch.uint8 or workspace.device != device or workspace.numel() < n:
+        raise ValueError("workspace must be a uint8 tensor on %s with >= %d bytes" % (device, n))
+    return workspace, workspace.numel()
+
+
+def moe_route(gating_output, top_k, correction_bias=None, scoring="softmax", renormalize=True,
+              num_expert_group=1, topk_group=1, routed_scaling_factor=1.0):
+    T, E = gating_output.shape
+    dev = gating_output.device
+    _check(gating_output, "gating_output", torch.float32, (T, E))
+    if correction_bias is not None:
+        _check(correction_bias, "correction_bias", torch.float32, (E,), dev)
+    p = make_params(T, 64, E, 64, top_k, scoring, renormalize, num_expert_group, topk_group,
+                    routed_scaling_factor)
+    ids = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        st = lib().moe_route(_ptr(gating_output), _ptr(correction_bias), ctypes.byref(p),
+                             _ptr(ids), _ptr(w), _stream(dev))
+    if st != MOE_OK:
+        raise MoEError(st, "moe_route")
+    return ids, w
+
+
+def moe_align_sort(topk_ids, num_experts, block_m):
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    _check(topk_ids, "topk_ids", torch.int32, (T, k))
+    P = T * k
+    E = int(num_experts)
+    out = {
+        "sorted_route_ids": torch.empty(P + E * (block_m - 1), dtype=torch.int32, device=dev),
+        "expert_offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+        "tile_expert": torch.empty(P // block_m + E, dtype=torch.int32, device=dev),
+        "inverse_pos": torch.empty(P, dtype=torch.int32, device=dev),
+        "n_tiles": torch.empty(1, dtype=torch.int32, device=dev),
+    }
+    with torch.cuda.device(dev):
+        st = lib().moe_align_sort(_ptr(topk_ids), T, k, E, int(block_m),
+                                  _ptr(out["sorted_route_ids"]), _ptr(out["expert_offsets"]),
+                                  _ptr(out["tile_expert"]), _ptr(out["inverse_pos"]),
+                                  _ptr(out["n_tiles"]), _stream(dev))
+    if st != MOE_OK:
+        raise MoEError(st, "moe_align_sort")
+    return out
+
+
+def _fused(hidden_states, gating_output, w_gate_up, w_down, top_k, correction_bias, scoring,
+           renormalize, num_expert_group, topk_group, routed_scaling_factor,
+           shared_w_gate_up, shared_w_down, path, out, workspace, return_routing):
+    T, H = hidden_states.shape
+    E, F2, _ = w_gate_up.shape
+    F = F2 // 2
+    dev = hidden_states.device
+    _check(hidden_states, "hidden_states", torch.bfloat16, (T, H))
+    _check(gating_output, "gating_output", torch.float32, (T, E), dev)
+    _check(w_gate_up, "w_gate_up", torch.bfloat16, (E, 2 * F, H), dev)
+    _check(w_down, "w_down", torch.bfloat16, (E, H, F), dev)
+    if correction_bias is not None:
+        _check(correction_bias, "correction_bias", torch.float32, (E,), dev)
+    S = 0
+    if shared_w_gate_up is not None:
+        S = shared_w_gate_up.shape[0] // 2
+        _check(shared_w_gate_up, "shared_w_gate_up", torch.bfloat16, (2 * S, H), dev)
+        _check(shared_w_down, "shared_w_down", torch.bfloat16, (H, S), dev)
+    p = make_params(T, H, E, F, top_k, scoring, renormalize, num_expert_group, topk_group,
+                    routed_scaling_factor, path)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _check(out, "out", torch.bfloat16, (T, H), dev)
+    ids = torch.empty((T, top_k), dtype=torch.int32, device=dev) if return_routing else None
+    w = torch.empty((T, top_k), dtype=torch.float32, device=dev) if return_routing else None
+    with torch.cuda.device(dev):
+        ws, nbytes = _workspace(p, S, dev, workspace)
+        if S > 0:
+            st = lib().fused_moe_shared_fwd(
+                _ptr(hidden_states), _ptr(gating_output), _ptr(w_gate_up), _ptr(w_down),
+                _ptr(correction_bias), _ptr(shared_w_gate_up), _ptr(shared_w_down), S,
+                ctypes.byref(p), _ptr(out), _ptr(ids), _ptr(w), _ptr(ws), nbytes, _stream(dev))
+            where = "fused_moe_shared_fwd"
+        else:
+            st = lib().fused_moe_fwd(
+                _ptr(hidden_states), _ptr(gating_output), _ptr(w_gate_up), _ptr(w_down),
+                _ptr(correction_bias), ctypes.byref(p), _ptr(out), _ptr(ids), _ptr(w),
+                _ptr(ws), nbytes, _stream(dev))
+            where = "fused_moe_fwd"
+    if st != MOE_OK:
+        raise MoEError(st, where)
+    if return_routing:
+        return out, ids, w
+    return out
+
+
+def fused_moe_fwd(hidden_states, gating_output, w_gate_up, w_down, top_k, correction_bias=None,
+                  scoring="softmax", renormalize=True, num_expert_group=1, topk_group=1,
+                  routed_scaling_factor=1.0, path="auto", out=None, workspace=None,
+                  return_routing=False):
+    return _fused(hidden_states, gating_output, w_gate_up, w_down, top_k, correction_bias,
+                  scoring, renormalize, num_expert_group, topk_group, routed_scaling_factor,
+                  None, None, path, out, workspace, return_routing)
+
+
+def fused_moe_shared_fwd(hidden_states, gating_output, w_gate_up, w_down, shared_w_gate_up,
+                         shared_w_down, top_k, correction_bias=None, scoring="softmax",
+                         renormalize=True, num_expert_group=1, topk_group=1,
+                         routed_scaling_factor=1.0, path="auto", out=None, workspace=None,
+                         return_routing=False):
+    if shared_w_gate_up is None or shared_w_down is None:
+        raise ValueError("fused_moe_shared_fwd needs shared_w_gate_up and shared_w_down")
+    return _fused(hidden_states, gating_output, w_gate_up, w_down, top_k, correction_bias,
+                  scoring, renormalize, num_expert_group, topk_group, routed_scaling_factor,
+                  shared_w_gate_up, shared_w_down, path, out, workspace, return_routing)
+
+
+def fused_moe_experts_fwd(hidden_states, w_gate_up, w_down, topk_ids, topk_weights, path="auto",
+                          out=None, workspace=None):
+    T, H = hidden_states.shape
+    E, F2, _ = w_gate_up.shape
+    F = F2 // 2
+    k = topk_ids.shape[1]
+    dev = hidden_states.device
+    _check(hidden_states, "hidden_states", torch.bfloat16, (T, H))
+    _check(w_gate_up, "w_gate_up", torch.bfloat16, (E, 2 * F, H), dev)
+    _check(w_down, "w_down", torch.bfloat16, (E, H, F), dev)
+    _check(topk_ids, "topk_ids", torch.int32, (T, k), dev)
+    _check(topk_weights, "topk_weights", torch.float32, (T, k), dev)
+    p = make_params(T, H, E, F, k, path=path)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _check(out, "out", torch.bfloat16, (T, H), dev)
+    with torch.cuda.device(dev):
+        ws, nbytes = _workspace(p, 0, dev, workspace)
+        st = lib().fused_moe_experts_fwd(_ptr(hidden_states), _ptr(w_gate_up), _ptr(w_down),
+                                         _ptr(topk_ids), _ptr(topk_weights), ctypes.byref(p),
+                                         _ptr(out), _ptr(ws), nbytes, _stream(dev))
+    if st != MOE_OK:
+        raise MoEError(st, "fused_moe_experts_fwd")
+    return out
+
+
+def fused_moe_experts_stage(stage, params, hidden_states, w_gate_up, w_down, topk_ids,
+                            topk_weights, out, workspace, shared_w_gate_up=None,
+                            shared_w_down=None):
+    """One stage of the expert part (see include/moe.h).  Low level: ``params`` is a
+    MoEParams matching the tensors (built with make_params) and ``workspace`` a uint8 tensor of
+    at least workspace_bytes(params, S) bytes; the caller keeps both across the stages of one
+    pass.  Tensors are assumed checked by the caller."""
+    S = 0 if shared_w_gate_up is None else shared_w_gate_up.shape[0] // 2
+    dev = hidden_states.device
+    with torch.cuda.device(dev):
+        st = lib().fused_moe_experts_stage(
+            int(stage), _ptr(hidden_states), _ptr(w_gate_up), _ptr(w_down), _ptr(topk_ids),
+            _ptr(topk_weights), _ptr(shared_w_gate_up), _ptr(shared_w_down), S,
+            ctypes.byref(params), _ptr(out), _ptr(workspace), workspace.numel(), _stream(dev))
+    if st != MOE_OK:
+        raise MoEError(st, "fused_moe_experts_stage(%s)" % STAGE_NAMES.get(stage, stage))

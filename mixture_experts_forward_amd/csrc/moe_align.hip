@@ -1,0 +1,161 @@
+// moe_align.hip -- expert histogram, padded prefix sum and stable permutation of routes.
+//
+// Computes the expert-contiguous route order of the TileOPs "MoE" page's MoEPermuteAlignFwd
+// (topk_ids [T,K] i32 -> per-expert prefix sums of the contiguous layout) together with the
+// inverse map of its MoEPostPermuteFwd (inverse_indices [T*K]): every expert's routes in
+// increasing route index r = t*k + j, each expert's segment padded up to block_m rows.
+//
+// One workgroup of 1024 threads (16 waves) does the whole job in LDS:
+//   1. histogram with LDS integer atomics (order-independent, so deterministic);
+//   2. block-wide exclusive scan of the padded counts -> expert_offsets, tile_expert, n_tiles,
+//      and the -1 fill of padding slots;
+//   3. rounds of 1024 routes: a route's row = its expert's running base + the count of the same
+//      expert in earlier waves of the round (per-wave histograms packed as two 16-bit counters
+//      per word) + its rank among earlier lanes of its own wave (LDS broadcast compare).
+// Every slot of sorted_route_ids and tile_expert is written exactly once.
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+constexpr int kMaxExperts = 1024;
+
+__device__ __forceinline__ int wave_inclusive_scan(int v, int lane)
+{
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(v, off);
+        if (lane >= off)
+            v += o;
+    }
+    return v;
+}
+
+__global__ __launch_bounds__(kThreads) void k_align_sort(
+    const int32_t *__restrict__ ids, int P, int E, int bm, int slots, int tiles_cap,
+    int32_t *__restrict__ sorted_ids, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ tile_expert, int32_t *__restrict__ inverse,
+    int32_t *__restrict__ n_tiles)
+{
+    __shared__ int s_count[kMaxExperts];
+    __shared__ int s_base[kMaxExperts];
+    __shared__ uint32_t s_hist[kWaves][kMaxExperts / 2];  // two 16-bit counters per word
+    __shared__ int s_round_ids[kThreads];
+    __shared__ int s_wave_total[kWaves];
+    __shared__ int s_total;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = tid >> 6;
+    const int half_words = (E + 1) / 2;
+
+    if (tid < E)
+        s_count[tid] = 0;
+    for (int x = tid; x < kWaves * half_words; x += kThreads)
+        s_hist[x / half_words][x % half_words] = 0;
+    __syncthreads();
+
+    // 1. histogram
+    for (int r = tid; r < P; r += kThreads) {
+        const int e = ids[r];
+        if (e >= 0 && e < E)
+            atomicAdd(&s_count[e], 1);
+    }
+    __syncthreads();
+
+    // 2. exclusive scan of the padded counts (thread e owns expert e)
+    const int c = (tid < E) ? s_count[tid] : 0;
+    const int padded = (c + bm - 1) / bm * bm;
+    int incl = wave_inclusive_scan(padded, lane);
+    if (lane == 63)
+        s_wave_total[wv] = incl;
+    __syncthreads();
+    int before_wave = 0;
+    for (int w = 0; w < wv; ++w)
+        before_wave += s_wave_total[w];
+    incl += before_wave;
+    const int excl = incl - padded;
+    if (tid < E) {
+        offsets[tid] = excl;
+        s_base[tid] = excl;
+        for (int s = excl + c; s < excl + padded; ++s)
+            sorted_ids[s] = -1;
+        for (int i = excl / bm; i < (excl + padded) / bm; ++i)
+            tile_expert[i] = tid;
+    }
+    if (tid == E - 1) {
+        offsets[E] = incl;
+        *n_tiles = incl / bm;
+        s_total = incl;
+    }
+    __syncthreads();
+    const int total = s_total;
+    for (int s = total + tid; s < slots; s += kThreads)
+        sorted_ids[s] = -1;
+    for (int i = total / bm + tid; i < tiles_cap; i += kThreads)
+        tile_expert[i] = -1;
+
+    // 3. stable scatter, 1024 routes per round
+    for (int r0 = 0; r0 < P; r0 += kThreads) {
+        const int r = r0 + tid;
+        int e = (r < P) ? ids[r] : -1;
+        const bool valid = (e >= 0 && e < E);
+        if (!valid)
+            e = -1;
+        s_round_ids[tid] = e;
+        __syncthreads();
+        int rank = 0;
+        if (valid) {
+            const int4 *w4 = reinterpret_cast<const int4 *>(&s_round_ids[wv * 64]);
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int4 v = w4[q];
+                rank += (4 * q + 0 < lane && v.x == e);
+                rank += (4 * q + 1 < lane && v.y == e);
+                rank += (4 * q + 2 < lane && v.z == e);
+                rank += (4 * q + 3 < lane && v.w == e);
+            }
+            atomicAdd(&s_hist[wv][e >> 1], 1u << ((e & 1) * 16));
+        }
+        __syncthreads();
+        if (valid) {
+            int before = 0;
+            for (int w = 0; w < wv; ++w)
+                before += (s_hist[w][e >> 1] >> ((e & 1) * 16)) & 0xffff;
+            const int pos = s_base[e] + before + rank;
+            sorted_ids[pos] = r;
+            inverse[r] = pos;
+        } else if (r < P) {
+            inverse[r] = -1;
+        }
+        __syncthreads();
+        if (tid < E) {
+            int sum = 0;
+            for (int w = 0; w < kWaves; ++w)
+                sum += (s_hist[w][tid >> 1] >> ((tid & 1) * 16)) & 0xffff;
+            s_base[tid] += sum;
+        }
+        __syncthreads();
+        for (int x = tid; x < kWaves * half_words; x += kThreads)
+            s_hist[x / half_words][x % half_words] = 0;
+        // the next round's first barrier orders this clear before its atomics
+    }
+}
+
+}  // namespace
+
+namespace moe {
+
+void launch_align_sort(const int32_t *ids, int P, int E, int block_m, int32_t *sorted_ids,
+                       int32_t *offsets, int32_t *tile_expert, int32_t *inverse, int32_t *n_tiles,
+                       hipStream_t stream)
+{
+    const int slots = P + E * (block_m - 1);
+    const int tiles_cap = P / block_m + E;
+    hipLaunchKernelGGL(k_align_sort, dim3(1), dim3(kThreads), 0, stream, ids, P, E, block_m,
+                       slots, tiles_cap, sorted_ids, offsets, tile_expert, inverse, n_tiles);
+}
+
+}  // namespace moe

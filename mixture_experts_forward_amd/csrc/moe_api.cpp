@@ -1,0 +1,355 @@
+// moe_api.cpp -- the extern "C" entry points declared in include/moe.h.
+//
+// Each entry point validates everything on the host first (moe_plan.cpp), then enqueues its
+// kernels on the caller's stream and returns; no host synchronisation, no device->host copy,
+// no allocation.
+#include <hip/hip_runtime.h>
+
+#include "../../include/moe.h"
+#include "moe_internal.h"
+#include "moe_plan.h"
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int launch_status()
+{
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
+template <typename T>
+T *ws_at(void *ws, size_t off)
+{
+    return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
+}
+
+// Everything one expert-part stage needs.
+struct Ctx {
+    const uint16_t *hidden, *w_gate_up, *w_down, *s_gu, *s_d;
+    const int32_t *ids;
+    const float *weights;
+    uint16_t *out;
+    void *ws;
+    hipStream_t stream;
+};
+
+// Workspace-resident sorted layout (sorted path) and the GEMM problems of a plan.
+moe::GemmProblem gate_up_problem(const moe::Plan &pl, const Ctx &c)
+{
+    moe::GemmProblem g = {};
+    g.act = c.hidden;
+    g.weight = c.w_gate_up;
+    g.out = ws_at<uint16_t>(c.ws, pl.off_h);
+    g.topk_ids = c.ids;
+    g.K = pl.H;
+    g.n_out = pl.F;
+    g.top_k = pl.k;
+    g.P = pl.P;
+    g.num_experts = pl.E;
+    if (pl.path == MOE_PATH_SORTED) {
+        g.sorted_ids = ws_at<int32_t>(c.ws, pl.off_sorted);
+        g.offsets = ws_at<int32_t>(c.ws, pl.off_offsets);
+        g.num_groups = pl.E;
+    } else {
+        g.num_groups = pl.P;
+    }
+    return g;
+}
+
+moe::GemmProblem shared_problem(const moe::Plan &pl, const Ctx &c, bool gate_up)
+{
+    moe::GemmProblem g = {};
+    const moe::TileChoice &t = gate_up ? pl.shared_gate_up : pl.shared_down;
+    g.act = gate_up ? c.hidden : ws_at<uint16_t>(c.ws, pl.off_hs);
+    g.weight = gate_up ? c.s_gu : c.s_d;
+    g.out = ws_at<uint16_t>(c.ws, gate_up ? pl.off_hs : pl.off_ys);
+    g.K = gate_up ? pl.H : pl.S;
+    g.n_out = gate_up ? pl.S : pl.H;
+    g.top_k = 1;
+    g.rows = pl.T;
+    g.num_experts = 1;
+    g.num_groups = (pl.T + 16 * t.mt - 1) / (16 * t.mt);
+    return g;
+}
+
+moe::WsTile ws_tile(const moe::TileChoice &t) { return moe::WsTile{t.nt, t.mt, t.ksplit}; }
+
+int run_stage(int stage, const moe::Plan &pl, const Ctx &c)
+{
+    const moe::RowSource src = pl.path == MOE_PATH_SORTED ? moe::ROWS_SORTED : moe::ROWS_DIRECT;
+    switch (stage) {
+    case MOE_STAGE_ALIGN:
+        if (pl.path == MOE_PATH_SORTED)
+            moe::launch_align_sort(c.ids, pl.P, pl.E, pl.block_m,
+                                   ws_at<int32_t>(c.ws, pl.off_sorted),
+                                   ws_at<int32_t>(c.ws, pl.off_offsets),
+                                   ws_at<int32_t>(c.ws, pl.off_tile_expert),
+                                   ws_at<int32_t>(c.ws, pl.off_inverse),
+                                   ws_at<int32_t>(c.ws, pl.off_n_tiles), c.stream);
+        break;
+    case MOE_STAGE_GATE_UP:
+        if (!moe::launch_gate_up(gate_up_problem(pl, c), src, ws_tile(pl.gate_up), c.stream))
+            return MOE_ERR_LAUNCH;
+        break;
+    case MOE_STAGE_DOWN: {
+        moe::GemmProblem g = gate_up_problem(pl, c);
+        g.act = ws_at<uint16_t>(c.ws, pl.off_h);
+        g.weight = c.w_down;
+        g.out = ws_at<uint16_t>(c.ws, pl.off_y);
+        g.K = pl.F;
+        g.n_out = pl.H;
+        if (!moe::launch_down(g, src, ws_tile(pl.down), c.stream))
+            return MOE_ERR_LAUNCH;
+        break;
+    }
+    case MOE_STAGE_SHARED:
+        if (pl.S <= 0)
+            return MOE_ERR_UNSUPPORTED;
+        if (!moe::launch_gate_up(shared_problem(pl, c, true), moe::ROWS_DENSE,
+                                 ws_tile(pl.shared_gate_up), c.stream) ||
+            !moe::launch_down(shared_problem(pl, c, false), moe::ROWS_DENSE,
+                              ws_tile(pl.shared_down), c.stream))
+            return MOE_ERR_LAUNCH;
+        break;
+    case MOE_STAGE_COMBINE:
+        moe::launch_combine(ws_at<uint16_t>(c.ws, pl.off_y), c.ids, c.weights,
+                            pl.S > 0 ? ws_at<uint16_t>(c.ws, pl.off_ys) : nullptr, c.out, pl.T,
+                            pl.H, pl.k, pl.E, c.stream);
+        break;
+    default:
+        return MOE_ERR_UNSUPPORTED;
+    }
+    return launch_status();
+}
+
+// Routed experts (+ shared expert) and the combine, with the routing already in ids/weights.
+int experts_impl(const moe::Plan &pl, const Ctx &c)
+{
+    for (int stage = MOE_STAGE_ALIGN; stage <= MOE_STAGE_COMBINE; ++stage) {
+        if (stage == MOE_STAGE_SHARED && pl.S == 0)
+            continue;
+        const int st = run_stage(stage, pl, c);
+        if (st != MOE_OK)
+            return st;
+    }
+    return MOE_OK;
+}
+
+int fused_impl(const uint16_t *hidden, const float *gating, const uint16_t *w_gate_up,
+               const uint16_t *w_down, const float *bias, const uint16_t *s_gu,
+               const uint16_t *s_d, int32_t S, const moe_params_t *p, uint16_t *out,
+               int32_t *ids_out, float *weights_out, void *ws, size_t ws_bytes, void *stream)
+{
+    int st = moe::check_dims(p);
+    if (st != MOE_OK)
+        return st;
+    if ((st = moe::check_routing(p, bias != nullptr)) != MOE_OK)
+        return st;
+    if ((st = moe::check_shared(S)) != MOE_OK)
+        return st;
+    if (p->num_tokens == 0)
+        return MOE_OK;  // empty tensors may have NULL data pointers
+    if (!hidden || !gating || !w_gate_up || !w_down || !out)
+        return MOE_ERR_NULL;
+    if (S > 0 && (!s_gu || !s_d))
+        return MOE_ERR_NULL;
+    moe::Plan pl;
+    moe::make_plan(p, S, &pl);
+    if (!ws)
+        return MOE_ERR_NULL;
+    if (ws_bytes < pl.total)
+        return MOE_ERR_WORKSPACE;
+    if (!aligned16(hidden) || !aligned16(w_gate_up) || !aligned16(w_down) || !aligned16(out) ||
+        !aligned16(ws) || (S > 0 && (!aligned16(s_gu) || !aligned16(s_d))))
+        return MOE_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    int32_t *ids = ids_out ? ids_out : ws_at<int32_t>(ws, pl.off_ids);
+    float *weights = weights_out ? weights_out : ws_at<float>(ws, pl.off_weights);
+    moe::launch_route(gating, bias, pl.T, pl.E, pl.k, p->scoring == MOE_SCORING_SIGMOID,
+                      p->renormalize, p->num_expert_group, p->topk_group,
+                      p->routed_scaling_factor, ids, weights, s);
+    const Ctx c = {hidden, w_gate_up, w_down, s_gu, s_d, ids, weights, out, ws, s};
+    return experts_impl(pl, c);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char *moe_status_string(int status)
+{
+    switch (status) {
+    case MOE_OK:
+        return "ok";
+    case MOE_ERR_NULL:
+        return "a required pointer is NULL";
+    case MOE_ERR_SHAPE:
+        return "invalid size (non-positive dimension or top_k > num_experts)";
+    case MOE_ERR_UNSUPPORTED:
+        return "unsupported combination of arguments";
+    case MOE_ERR_WORKSPACE:
+        return "workspace too small";
+    case MOE_ERR_LAUNCH:
+        return "kernel launch failed";
+    default:
+        return "unknown status";
+    }
+}
+
+int moe_check_params(const moe_params_t *p, int correction_bias_given, int32_t shared_inter)
+{
+    int st = moe::check_dims(p);
+    if (st == MOE_OK)
+        st = moe::check_routing(p, correction_bias_given);
+    if (st == MOE_OK)
+        st = moe::check_shared(shared_inter);
+    return st;
+}
+
+int moe_route(const float *gating_output, const float *correction_bias, const moe_params_t *p,
+              int32_t *topk_ids, float *topk_weights, void *stream)
+{
+    if (!p)
+        return MOE_ERR_NULL;
+    if (p->num_tokens < 0 || p->num_experts <= 0 || p->top_k <= 0 ||
+        p->top_k > p->num_experts)
+        return MOE_ERR_SHAPE;
+    if (p->top_k > moe::kMaxTopK || p->num_experts > moe::kMaxExperts)
+        return MOE_ERR_UNSUPPORTED;
+    int st = moe::check_routing(p, correction_bias != nullptr);
+    if (st != MOE_OK)
+        return st;
+    if (p->num_tokens == 0)
+        return MOE_OK;
+    if (!gating_output || !topk_ids || !topk_weights)
+        return MOE_ERR_NULL;
+    moe::launch_route(gating_output, correction_bias, p->num_tokens, p->num_experts, p->top_k,
+                      p->scoring == MOE_SCORING_SIGMOID, p->renormalize, p->num_expert_group,
+                      p->topk_group, p->routed_scaling_factor, topk_ids, topk_weights,
+                      static_cast<hipStream_t>(stream));
+    return launch_status();
+}
+
+int moe_align_sort(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E, int32_t block_m,
+                   int32_t *sorted_route_ids, int32_t *expert_offsets, int32_t *tile_expert,
+                   int32_t *inverse_pos, int32_t *n_tiles, void *stream)
+{
+    if (T < 0 || k < 1 || E < 1)
+        return MOE_ERR_SHAPE;
+    if (E > moe::kMaxExperts || block_m < 1 || block_m > 1024 || (int64_t)T * k >= (1ll << 30))
+        return MOE_ERR_UNSUPPORTED;
+    if (!sorted_route_ids || !expert_offsets || !tile_expert || !n_tiles ||
+        (T > 0 && (!topk_ids || !inverse_pos)))
+        return MOE_ERR_NULL;
+    if (((int64_t)T * k + (int64_t)E * (block_m - 1)) >= (1ll << 31))
+        return MOE_ERR_UNSUPPORTED;
+    moe::launch_align_sort(topk_ids, T * k, E, block_m, sorted_route_ids, expert_offsets,
+                           tile_expert, inverse_pos, n_tiles, static_cast<hipStream_t>(stream));
+    return launch_status();
+}
+
+size_t fused_moe_workspace_bytes(const moe_params_t *p, int32_t shared_inter)
+{
+    if (moe::check_dims(p) != MOE_OK || moe::check_shared(shared_inter) != MOE_OK)
+        return 0;
+    if (p->num_tokens == 0)
+        return 0;
+    moe::Plan pl;
+    moe::make_plan(p, shared_inter, &pl);
+    return pl.total;
+}
+
+int fused_moe_fwd(const uint16_t *hidden_states, const float *gating_output,
+                  const uint16_t *w_gate_up, const uint16_t *w_down,
+                  const float *correction_bias, const moe_params_t *p, uint16_t *out,
+                  int32_t *topk_ids_out, float *topk_weights_out, void *workspace,
+                  size_t workspace_bytes, void *stream)
+{
+    return fused_impl(hidden_states, gating_output, w_gate_up, w_down, correction_bias, nullptr,
+                      nullptr, 0, p, out, topk_ids_out, topk_weights_out, workspace,
+                      workspace_bytes, stream);
+}
+
+int fused_moe_shared_fwd(const uint16_t *hidden_states, const float *gating_output,
+                         const uint16_t *w_gate_up, const uint16_t *w_down,
+                         const float *correction_bias, const uint16_t *shared_w_gate_up,
+                         const uint16_t *shared_w_down, int32_t shared_inter,
+                         const moe_params_t *p, uint16_t *out, int32_t *topk_ids_out,
+                         float *topk_weights_out, void *workspace, size_t workspace_bytes,
+                         void *stream)
+{
+    if (shared_inter == 0)
+        return MOE_ERR_SHAPE;
+    return fused_impl(hidden_states, gating_output, w_gate_up, w_down, correction_bias,
+                      shared_w_gate_up, shared_w_down, shared_inter, p, out, topk_ids_out,
+                      topk_weights_out, workspace, workspace_bytes, stream);
+}
+
+int fused_moe_experts_fwd(const uint16_t *hidden_states, const uint16_t *w_gate_up,
+                          const uint16_t *w_down, const int32_t *topk_ids,
+                          const float *topk_weights, const moe_params_t *p, uint16_t *out,
+                          void *workspace, size_t workspace_bytes, void *stream)
+{
+    int st = moe::check_dims(p);
+    if (st != MOE_OK)
+        return st;
+    if (p->num_tokens == 0)
+        return MOE_OK;
+    if (!hidden_states || !w_gate_up || !w_down || !topk_ids || !topk_weights || !out)
+        return MOE_ERR_NULL;
+    moe::Plan pl;
+    moe::make_plan(p, 0, &pl);
+    if (!workspace)
+        return MOE_ERR_NULL;
+    if (workspace_bytes < pl.total)
+        return MOE_ERR_WORKSPACE;
+    if (!aligned16(hidden_states) || !aligned16(w_gate_up) || !aligned16(w_down) ||
+        !aligned16(out) || !aligned16(workspace))
+        return MOE_ERR_UNSUPPORTED;
+    const Ctx c = {hidden_states, w_gate_up, w_down, nullptr, nullptr, topk_ids, topk_weights,
+                   out, workspace, static_cast<hipStream_t>(stream)};
+    return experts_impl(pl, c);
+}
+
+int fused_moe_experts_stage(int stage, const uint16_t *hidden_states, const uint16_t *w_gate_up,
+                            const uint16_t *w_down, const int32_t *topk_ids,
+                            const float *topk_weights, const uint16_t *shared_w_gate_up,
+                            const uint16_t *shared_w_down, int32_t shared_inter,
+                            const moe_params_t *p, uint16_t *out, void *workspace,
+                            size_t workspace_bytes, void *stream)
+{
+    int st = moe::check_dims(p);
+    if (st != MOE_OK)
+        return st;
+    if ((st = moe::check_shared(shared_inter)) != MOE_OK)
+        return st;
+    if (stage < MOE_STAGE_ALIGN || stage > MOE_STAGE_COMBINE ||
+        (stage == MOE_STAGE_SHARED && shared_inter == 0))
+        return MOE_ERR_UNSUPPORTED;
+    if (p->num_tokens == 0)
+        return MOE_OK;
+    const bool need_x = stage == MOE_STAGE_GATE_UP || stage == MOE_STAGE_SHARED;
+    if (!workspace || !topk_ids || (need_x && !hidden_states) ||
+        (stage == MOE_STAGE_GATE_UP && !w_gate_up) || (stage == MOE_STAGE_DOWN && !w_down) ||
+        (stage == MOE_STAGE_SHARED && (!shared_w_gate_up || !shared_w_down)) ||
+        (stage == MOE_STAGE_COMBINE && (!topk_weights || !out)))
+        return MOE_ERR_NULL;
+    moe::Plan pl;
+    moe::make_plan(p, shared_inter, &pl);
+    if (workspace_bytes < pl.total)
+        return MOE_ERR_WORKSPACE;
+    if (!aligned16(workspace) || (hidden_states && !aligned16(hidden_states)) ||
+        (w_gate_up && !aligned16(w_gate_up)) || (w_down && !aligned16(w_down)) ||
+        (out && !aligned16(out)) || (shared_w_gate_up && !aligned16(shared_w_gate_up)) ||
+        (shared_w_down && !aligned16(shared_w_down)))
+        return MOE_ERR_UNSUPPORTED;
+    const Ctx c = {hidden_states, w_gate_up, w_down, shared_w_gate_up, shared_w_down, topk_ids,
+                   topk_weights, out, workspace, static_cast<hipStream_t>(stream)};
+    return run_stage(stage, pl, c);
+}
+
+}  // extern "C"

@@ -1,0 +1,68 @@
+// moe_combine.hip -- deterministic weighted combine of the expert output rows.
+//
+// out[t, c] = bf16( sum_{j<k} w[t,j] * y[t*k + j, c]  (+ ys[t, c]) ), j ascending, f32 sums
+// (TileOPs "MoE" page, MoEPostPermuteFwd: expert_output, topk_weights [T,K] f32; the shared
+// expert of FusedMoESharedExpertFwd is added with weight one).  Routes whose id is outside
+// [0, E) are skipped.  The expert GEMMs write y indexed by route, so a token's k rows are
+// contiguous and each 16-byte load covers eight columns.  Every output row is written, so the
+// output needs no clear beforehand (the aiter MI308 decoding PR drops its output clear for the
+// same reason).
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void k_combine(
+    const uint16_t *__restrict__ y, const int32_t *__restrict__ ids,
+    const float *__restrict__ weights, const uint16_t *__restrict__ ys, uint16_t *__restrict__ out,
+    int H, int k, int E)
+{
+    const int t = blockIdx.x;
+    const int c = (blockIdx.y * kThreads + threadIdx.x) * 8;
+    if (c >= H)
+        return;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+        const size_t r = (size_t)t * k + j;
+        const int e = ids[r];
+        if (e < 0 || e >= E)
+            continue;
+        const float w = weights[r];
+        const moe_u32x4 v = *reinterpret_cast<const moe_u32x4 *>(y + r * H + c);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            acc[2 * q] += w * moe_bf16_to_f32(v[q] & 0xffffu);
+            acc[2 * q + 1] += w * moe_bf16_to_f32(v[q] >> 16);
+        }
+    }
+    if (ys) {
+        const moe_u32x4 v = *reinterpret_cast<const moe_u32x4 *>(ys + (size_t)t * H + c);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            acc[2 * q] += moe_bf16_to_f32(v[q] & 0xffffu);
+            acc[2 * q + 1] += moe_bf16_to_f32(v[q] >> 16);
+        }
+    }
+    moe_u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        o[q] = moe_pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+    *reinterpret_cast<moe_u32x4 *>(out + (size_t)t * H + c) = o;
+}
+
+}  // namespace
+
+namespace moe {
+
+void launch_combine(const uint16_t *y, const int32_t *ids, const float *weights,
+                    const uint16_t *ys, uint16_t *out, int T, int H, int k, int E,
+                    hipStream_t stream)
+{
+    const dim3 grid(T, (H / 8 + kThreads - 1) / kThreads);
+    hipLaunchKernelGGL(k_combine, grid, dim3(kThreads), 0, stream, y, ids, weights, ys, out, H,
+                       k, E);
+}
+
+}  // namespace moe

@@ -1,0 +1,60 @@
+// moe_internal.h -- host-side interfaces between the C ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------- routing
+void launch_route(const float *gating, const float *bias, int T, int E, int k, int sigmoid,
+                  int renormalize, int n_group, int topk_group, float rsf, int32_t *ids,
+                  float *weights, hipStream_t stream);
+
+// ---------------------------------------------------------------- align / sort
+void launch_align_sort(const int32_t *ids, int P, int E, int block_m, int32_t *sorted_ids,
+                       int32_t *offsets, int32_t *tile_expert, int32_t *inverse, int32_t *n_tiles,
+                       hipStream_t stream);
+
+// ---------------------------------------------------------------- expert GEMMs
+// Where a GEMM takes its rows from.
+enum RowSource {
+    ROWS_SORTED = 0,  // rows of one expert's padded segment of the sorted route list
+    ROWS_DIRECT = 1,  // routes of one expert found by scanning topk_ids (no sort)
+    ROWS_DENSE = 2,   // every token, one weight matrix (shared expert)
+};
+
+struct GemmProblem {
+    const uint16_t *act;        // activation rows [*, K] bf16
+    const uint16_t *weight;     // [experts][n_weight_rows][K] bf16
+    uint16_t *out;              // output rows [*, n_out] bf16
+    const int32_t *sorted_ids;  // ROWS_SORTED
+    const int32_t *offsets;     // ROWS_SORTED: [E+1]
+    const int32_t *topk_ids;    // ROWS_DIRECT: [P]
+    int K;                      // reduction length
+    int n_out;                  // output columns (F for gate-up, H for down)
+    int top_k;                  // routes per token
+    int num_groups;             // experts (SORTED), routes (DIRECT), row blocks (DENSE)
+    int P;                      // routes (DIRECT)
+    int rows;                   // tokens (DENSE)
+    int num_experts;            // E (valid expert ids are [0, E))
+};
+
+// Tile shape of one weight-streaming launch: NT 16-column tiles per workgroup (per half for
+// gate-up), MT 16-row tiles per pass, KSPLIT waves splitting the K loop.
+struct WsTile {
+    int nt, mt, ksplit;
+};
+
+// false: no kernel is instantiated for this tile shape (nothing launched)
+bool launch_gate_up(const GemmProblem &g, RowSource src, WsTile tile, hipStream_t stream);
+bool launch_down(const GemmProblem &g, RowSource src, WsTile tile, hipStream_t stream);
+
+// ---------------------------------------------------------------- combine
+// out[t] = bf16( sum_j w[t,j] * y[t*k+j] (+ ys[t]) ), routes with ids outside [0,E) skipped.
+void launch_combine(const uint16_t *y, const int32_t *ids, const float *weights,
+                    const uint16_t *ys, uint16_t *out, int T, int H, int k, int E,
+                    hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,133 @@
+// moe_plan.cpp -- host-only argument checks, path/tile choice and workspace layout.
+#include "moe_plan.h"
+
+namespace moe {
+
+namespace {
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Row tiles per pass from the expected routed rows per expert, T*k/E: a weight tile is
+// streamed once per pass, so one pass should cover a typical expert (the tile tiers of the
+// FlashInfer BF16-activation PR follow the same routed-rows-per-expert density).
+int rows_tier(int P, int E)
+{
+    const double mean = (double)P / (double)E;
+    if (mean <= 8.0)
+        return 1;
+    if (mean <= 24.0)
+        return 2;
+    return 4;
+}
+
+}  // namespace
+
+int check_dims(const moe_params_t *p)
+{
+    if (!p)
+        return MOE_ERR_NULL;
+    if (p->num_tokens < 0 || p->hidden <= 0 || p->num_experts <= 0 || p->inter <= 0 ||
+        p->top_k <= 0 || p->top_k > p->num_experts)
+        return MOE_ERR_SHAPE;
+    if (p->top_k > kMaxTopK || p->num_experts > kMaxExperts)
+        return MOE_ERR_UNSUPPORTED;
+    if (p->hidden % 64 != 0 || p->inter % 64 != 0)
+        return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)p->num_tokens * p->top_k >= (1ll << 30))
+        return MOE_ERR_UNSUPPORTED;
+    if (p->path != MOE_PATH_AUTO && p->path != MOE_PATH_DIRECT && p->path != MOE_PATH_SORTED)
+        return MOE_ERR_UNSUPPORTED;
+    if (p->path == MOE_PATH_DIRECT && p->num_tokens * p->top_k > MOE_DIRECT_MAX_ROUTES)
+        return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+int check_routing(const moe_params_t *p, int bias_given)
+{
+    if (!p)
+        return MOE_ERR_NULL;
+    if (p->scoring != MOE_SCORING_SOFTMAX && p->scoring != MOE_SCORING_SIGMOID)
+        return MOE_ERR_UNSUPPORTED;
+    if (p->renormalize != 0 && p->renormalize != 1)
+        return MOE_ERR_UNSUPPORTED;
+    const int ng = p->num_expert_group, tg = p->topk_group;
+    if (ng < 1 || ng > kMaxGroups || tg < 1 || tg > ng || p->num_experts % ng != 0)
+        return MOE_ERR_UNSUPPORTED;
+    if (p->top_k > tg * (p->num_experts / ng))
+        return MOE_ERR_UNSUPPORTED;
+    if (p->scoring == MOE_SCORING_SOFTMAX && (bias_given || ng > 1))
+        return MOE_ERR_UNSUPPORTED;
+    if (!(p->routed_scaling_factor == p->routed_scaling_factor))  // NaN
+        return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+int check_shared(int32_t S)
+{
+    if (S < 0)
+        return MOE_ERR_SHAPE;
+    if (S > 0 && S % 64 != 0)
+        return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+void make_plan(const moe_params_t *p, int32_t S, Plan *pl)
+{
+    pl->T = p->num_tokens;
+    pl->H = p->hidden;
+    pl->E = p->num_experts;
+    pl->F = p->inter;
+    pl->k = p->top_k;
+    pl->S = S;
+    pl->P = pl->T * pl->k;
+    const int P = pl->P;
+    if (p->path == MOE_PATH_AUTO)
+        pl->path = (P <= MOE_DIRECT_MAX_ROUTES) ? MOE_PATH_DIRECT : MOE_PATH_SORTED;
+    else
+        pl->path = p->path;
+    pl->block_m = kSortedBlockM;
+    pl->slots = P + pl->E * (pl->block_m - 1);
+    pl->tiles_cap = P / pl->block_m + pl->E;
+
+    if (pl->path == MOE_PATH_DIRECT) {
+        pl->gate_up = {1, 1, 4};
+        pl->down = {2, 1, 4};
+    } else {
+        const int mt = rows_tier(P, pl->E);
+        pl->gate_up = {2, mt, 2};
+        pl->down = {4, mt, 2};
+    }
+    pl->shared_gate_up = {2, 4, 1};
+    pl->shared_down = {4, 4, 1};
+
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o = align256(o + bytes);
+        return at;
+    };
+    pl->off_ids = take((size_t)P * 4);
+    pl->off_weights = take((size_t)P * 4);
+    if (pl->path == MOE_PATH_SORTED) {
+        pl->off_sorted = take((size_t)pl->slots * 4);
+        pl->off_offsets = take((size_t)(pl->E + 1) * 4);
+        pl->off_tile_expert = take((size_t)pl->tiles_cap * 4);
+        pl->off_inverse = take((size_t)P * 4);
+        pl->off_n_tiles = take(4);
+        pl->off_h = take((size_t)pl->slots * pl->F * 2);
+    } else {
+        pl->off_sorted = pl->off_offsets = pl->off_tile_expert = pl->off_inverse = 0;
+        pl->off_n_tiles = 0;
+        pl->off_h = take((size_t)P * pl->F * 2);
+    }
+    pl->off_y = take((size_t)P * pl->H * 2);
+    if (S > 0) {
+        pl->off_hs = take((size_t)pl->T * S * 2);
+        pl->off_ys = take((size_t)pl->T * pl->H * 2);
+    } else {
+        pl->off_hs = pl->off_ys = 0;
+    }
+    pl->total = o;
+}
+
+}  // namespace moe

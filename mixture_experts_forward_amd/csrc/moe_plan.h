@@ -1,0 +1,44 @@
+// moe_plan.h -- host-only planning of a fused MoE call: argument checks, path choice, tile
+// choice and the workspace layout.  No HIP call is made here, so every check runs (and can be
+// tested) without a GPU.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+constexpr int kMaxTopK = 32;
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxGroups = 64;
+constexpr int kSortedBlockM = 16;  // row tile of the weight-streaming GEMMs
+
+struct TileChoice {
+    int nt, mt, ksplit;
+};
+
+struct Plan {
+    int path;           // MOE_PATH_DIRECT or MOE_PATH_SORTED (resolved)
+    int T, H, E, F, k, S, P;
+    int block_m;        // sorted path
+    int slots;          // rows of the padded sorted order
+    int tiles_cap;
+    TileChoice gate_up, down, shared_gate_up, shared_down;
+    // byte offsets into the workspace
+    size_t off_ids, off_weights, off_sorted, off_offsets, off_tile_expert, off_inverse,
+        off_n_tiles, off_h, off_y, off_hs, off_ys;
+    size_t total;
+};
+
+// Size checks common to every fused entry point (T, H, E, F, k, path).
+int check_dims(const moe_params_t *p);
+// Routing attribute checks (scoring, grouping, bias).
+int check_routing(const moe_params_t *p, int bias_given);
+int check_shared(int32_t shared_inter);
+
+// Fills *plan for a valid p (checks must have passed).  S = shared_inter (0 = none).
+void make_plan(const moe_params_t *p, int32_t S, Plan *plan);
+
+}  // namespace moe

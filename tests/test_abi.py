@@ -1,0 +1,129 @@
+"""The C-ABI library loads without a GPU, exports every function include/moe.h declares, and
+rejects invalid arguments on the host before touching the GPU (no compute call here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_forward_amd as moe
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "moe.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)
+    skip = {"if", "sizeof", "defined"}
+    return sorted({n for n in names if n not in skip})
+
+
+def test_library_exports_every_declared_function():
+    L = moe.lib()
+    names = _declared_functions()
+    assert "fused_moe_fwd" in names and "moe_route" in names and len(names) >= 9
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(moe.SIGNATURES), "binding and header disagree"
+
+
+def test_abi_version_and_status_strings():
+    assert moe.lib().moe_abi_version() == 1
+    for s in (0, -1, -2, -3, -4, -5):
+        assert moe.status_string(s) and moe.status_string(s) != "unknown status"
+    assert moe.status_string(7) == "unknown status"
+
+
+def _check(p, bias=0, S=0):
+    return moe.lib().moe_check_params(ctypes.byref(p), bias, S)
+
+
+def test_check_params_rules():
+    ok = moe.make_params(32, 2048, 128, 768, 8)
+    assert _check(ok) == 0
+    assert moe.lib().moe_check_params(None, 0, 0) == -1
+    assert _check(moe.make_params(-1, 2048, 128, 768, 8)) == -2
+    assert _check(moe.make_params(0, 2048, 128, 768, 8)) == 0          # T = 0 is valid
+    assert _check(moe.make_params(4, 0, 8, 64, 2)) == -2
+    assert _check(moe.make_params(4, 128, 8, 64, 9)) == -2              # k > E
+    assert _check(moe.make_params(4, 128, 64, 64, 33)) == -3            # k > 32
+    assert _check(moe.make_params(4, 128, 2048, 64, 2)) == -3           # E > 1024
+    assert _check(moe.make_params(4, 96, 8, 64, 2)) == -3               # H % 64
+    assert _check(moe.make_params(4, 128, 8, 80, 2)) == -3              # F % 64
+    assert _check(moe.make_params(4, 128, 8, 64, 2), bias=1) == -3      # softmax + bias
+    g = moe.make_params(4, 128, 8, 64, 2, "sigmoid", True, 3, 1)        # 8 % 3
+    assert _check(g) == -3
+    g = moe.make_params(4, 128, 8, 64, 2, "softmax", True, 2, 1)        # softmax + groups
+    assert _check(g) == -3
+    g = moe.make_params(4, 128, 8, 64, 5, "sigmoid", True, 4, 2)        # k > 2 groups * 2
+    assert _check(g) == -3
+    g = moe.make_params(4, 128, 8, 64, 4, "sigmoid", True, 4, 2)
+    assert _check(g, bias=1) == 0
+    assert _check(moe.make_params(9, 128, 8, 64, 8, path="direct")) == -3  # 72 routes > 64
+    assert _check(moe.make_params(8, 128, 8, 64, 8, path="direct")) == 0
+    assert _check(ok, S=-64) == -2
+    assert _check(ok, S=100) == -3
+    assert _check(ok, S=18432) == 0
+
+
+def test_workspace_bytes():
+    p = moe.make_params(32, 2048, 128, 768, 8)
+    n = moe.workspace_bytes(p)
+    P = 256
+    slots = P + 128 * 15
+    # routing + sorted lists + h [slots, F] bf16 + y [P, H] bf16, each 256-aligned
+    assert n >= slots * 768 * 2 + P * 2048 * 2
+    assert n % 256 == 0
+    assert moe.workspace_bytes(p, 18432) > n
+    assert moe.workspace_bytes(moe.make_params(0, 2048, 128, 768, 8)) == 0
+    small = moe.make_params(8, 2048, 128, 768, 8)
+    assert moe.workspace_bytes(small) < n                      # direct path: no sorted lists
+
+
+def test_entry_points_reject_before_launch():
+    """Invalid calls return their error code without any HIP call (runs without a GPU)."""
+    L = moe.lib()
+    p = moe.make_params(4, 128, 8, 64, 2)
+    fake = ctypes.c_void_p(4096)
+    assert L.fused_moe_fwd(None, fake, fake, fake, None, ctypes.byref(p), fake, None, None, fake,
+                           1 << 30, None) == -1
+    assert L.fused_moe_fwd(fake, fake, fake, fake, None, None, fake, None, None, fake, 1 << 30,
+                           None) == -1
+    bad = moe.make_params(4, 128, 8, 64, 9)
+    assert L.fused_moe_fwd(fake, fake, fake, fake, None, ctypes.byref(bad), fake, None, None,
+                           fake, 1 << 30, None) == -2
+    assert L.fused_moe_fwd(fake, fake, fake, fake, fake, ctypes.byref(p), fake, None, None, fake,
+                           1 << 30, None) == -3   # softmax with a bias
+    assert L.fused_moe_fwd(fake, fake, fake, fake, None, ctypes.byref(p), fake, None, None, fake,
+                           16, None) == -4        # workspace too small
+    odd = ctypes.c_void_p(4096 + 2)
+    assert L.fused_moe_fwd(odd, fake, fake, fake, None, ctypes.byref(p), fake, None, None, fake,
+                           1 << 30, None) == -3   # misaligned bf16 pointer
+    assert L.fused_moe_shared_fwd(fake, fake, fake, fake, None, None, None, 64, ctypes.byref(p),
+                                  fake, None, None, fake, 1 << 30, None) == -1
+    assert L.fused_moe_shared_fwd(fake, fake, fake, fake, None, fake, fake, 0, ctypes.byref(p),
+                                  fake, None, None, fake, 1 << 30, None) == -2
+    assert L.fused_moe_experts_fwd(fake, fake, fake, None, fake, ctypes.byref(p), fake, fake,
+                                   1 << 30, None) == -1
+    z = moe.make_params(0, 128, 8, 64, 2)
+    assert L.fused_moe_fwd(fake, fake, fake, fake, None, ctypes.byref(z), fake, None, None, None,
+                           0, None) == 0          # T = 0: nothing to do
+    assert L.moe_route(fake, None, None, fake, fake, None) == -1
+    assert L.moe_route(fake, fake, ctypes.byref(p), fake, fake, None) == -3
+    assert L.moe_route(None, None, ctypes.byref(p), fake, fake, None) == -1
+    assert L.moe_align_sort(fake, 4, 2, 0, 16, fake, fake, fake, fake, fake, None) == -2
+    assert L.moe_align_sort(fake, 4, 2, 2048, 16, fake, fake, fake, fake, fake, None) == -3
+    assert L.moe_align_sort(fake, 4, 2, 8, 0, fake, fake, fake, fake, fake, None) == -3
+    assert L.moe_align_sort(None, 4, 2, 8, 16, fake, fake, fake, fake, fake, None) == -1
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        moe.fused_moe_experts_fwd(x, torch.zeros(8, 128, 128, dtype=torch.bfloat16),
+                                  torch.zeros(8, 128, 64, dtype=torch.bfloat16),
+                                  torch.zeros(4, 2, dtype=torch.int32),
+                                  torch.zeros(4, 2, dtype=torch.float32))

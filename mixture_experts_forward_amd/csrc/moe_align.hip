@@ -1,4 +1,5 @@
-// moe_align.hip -- expert histogram, padded prefix sum and stable permutation of routes.
+// moe_align.hip -- expert histogram, padded prefix sum and stable permutation of routes, and the
+// fused routing + align kernel used for small batches.
 //
 // Computes the expert-contiguous route order of the TileOPs "MoE" page's MoEPermuteAlignFwd
 // (topk_ids [T,K] i32 -> per-expert prefix sums of the contiguous layout) together with the
@@ -13,14 +14,28 @@
 //      expert in earlier waves of the round (per-wave histograms packed as two 16-bit counters
 //      per word) + its rank among earlier lanes of its own wave (LDS broadcast compare).
 // Every slot of sorted_route_ids and tile_expert is written exactly once.
-#include "moe_device.h"
+//
+// k_route_align routes up to kFusedMaxRoutes routes with the same 16 waves first (one wave per
+// token, moe_route_dev.h), keeps the ids in LDS and sorts them without a second launch.
 #include "moe_internal.h"
+#include "moe_route_dev.h"
 
 namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxExperts = 1024;
+constexpr int kFusedMaxRoutes = 2048;
+constexpr int kFusedMaxExperts = 512;
+
+struct AlignSmem {
+    int count[kMaxExperts];
+    int base[kMaxExperts];
+    uint32_t hist[kWaves][kMaxExperts / 2];  // two 16-bit counters per word
+    alignas(16) int round_ids[kThreads];
+    int wave_total[kWaves];
+    int total;
+};
 
 __device__ __forceinline__ int wave_inclusive_scan(int v, int lane)
 {
@@ -33,53 +48,46 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane)
     return v;
 }
 
-__global__ __launch_bounds__(kThreads) void k_align_sort(
-    const int32_t *__restrict__ ids, int P, int E, int bm, int slots, int tiles_cap,
-    int32_t *__restrict__ sorted_ids, int32_t *__restrict__ offsets,
-    int32_t *__restrict__ tile_expert, int32_t *__restrict__ inverse,
-    int32_t *__restrict__ n_tiles)
+// The whole align/sort by one 1024-thread workgroup.  ids may point to global memory or LDS.
+__device__ void align_block(const int32_t *ids, int P, int E, int bm, int slots, int tiles_cap,
+                            int32_t *__restrict__ sorted_ids, int32_t *__restrict__ offsets,
+                            int32_t *__restrict__ tile_expert, int32_t *__restrict__ inverse,
+                            int32_t *__restrict__ n_tiles, AlignSmem &sm)
 {
-    __shared__ int s_count[kMaxExperts];
-    __shared__ int s_base[kMaxExperts];
-    __shared__ uint32_t s_hist[kWaves][kMaxExperts / 2];  // two 16-bit counters per word
-    __shared__ int s_round_ids[kThreads];
-    __shared__ int s_wave_total[kWaves];
-    __shared__ int s_total;
-
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = tid >> 6;
     const int half_words = (E + 1) / 2;
 
     if (tid < E)
-        s_count[tid] = 0;
+        sm.count[tid] = 0;
     for (int x = tid; x < kWaves * half_words; x += kThreads)
-        s_hist[x / half_words][x % half_words] = 0;
+        sm.hist[x / half_words][x % half_words] = 0;
     __syncthreads();
 
     // 1. histogram
     for (int r = tid; r < P; r += kThreads) {
         const int e = ids[r];
         if (e >= 0 && e < E)
-            atomicAdd(&s_count[e], 1);
+            atomicAdd(&sm.count[e], 1);
     }
     __syncthreads();
 
     // 2. exclusive scan of the padded counts (thread e owns expert e)
-    const int c = (tid < E) ? s_count[tid] : 0;
+    const int c = (tid < E) ? sm.count[tid] : 0;
     const int padded = (c + bm - 1) / bm * bm;
     int incl = wave_inclusive_scan(padded, lane);
     if (lane == 63)
-        s_wave_total[wv] = incl;
+        sm.wave_total[wv] = incl;
     __syncthreads();
     int before_wave = 0;
     for (int w = 0; w < wv; ++w)
-        before_wave += s_wave_total[w];
+        before_wave += sm.wave_total[w];
     incl += before_wave;
     const int excl = incl - padded;
     if (tid < E) {
         offsets[tid] = excl;
-        s_base[tid] = excl;
+        sm.base[tid] = excl;
         for (int s = excl + c; s < excl + padded; ++s)
             sorted_ids[s] = -1;
         for (int i = excl / bm; i < (excl + padded) / bm; ++i)
@@ -88,10 +96,10 @@ __global__ __launch_bounds__(kThreads) void k_align_sort(
     if (tid == E - 1) {
         offsets[E] = incl;
         *n_tiles = incl / bm;
-        s_total = incl;
+        sm.total = incl;
     }
     __syncthreads();
-    const int total = s_total;
+    const int total = sm.total;
     for (int s = total + tid; s < slots; s += kThreads)
         sorted_ids[s] = -1;
     for (int i = total / bm + tid; i < tiles_cap; i += kThreads)
@@ -104,11 +112,11 @@ __global__ __launch_bounds__(kThreads) void k_align_sort(
         const bool valid = (e >= 0 && e < E);
         if (!valid)
             e = -1;
-        s_round_ids[tid] = e;
+        sm.round_ids[tid] = e;
         __syncthreads();
         int rank = 0;
         if (valid) {
-            const int4 *w4 = reinterpret_cast<const int4 *>(&s_round_ids[wv * 64]);
+            const int4 *w4 = reinterpret_cast<const int4 *>(&sm.round_ids[wv * 64]);
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
                 const int4 v = w4[q];
@@ -117,14 +125,14 @@ __global__ __launch_bounds__(kThreads) void k_align_sort(
                 rank += (4 * q + 2 < lane && v.z == e);
                 rank += (4 * q + 3 < lane && v.w == e);
             }
-            atomicAdd(&s_hist[wv][e >> 1], 1u << ((e & 1) * 16));
+            atomicAdd(&sm.hist[wv][e >> 1], 1u << ((e & 1) * 16));
         }
         __syncthreads();
         if (valid) {
             int before = 0;
             for (int w = 0; w < wv; ++w)
-                before += (s_hist[w][e >> 1] >> ((e & 1) * 16)) & 0xffff;
-            const int pos = s_base[e] + before + rank;
+                before += (sm.hist[w][e >> 1] >> ((e & 1) * 16)) & 0xffff;
+            const int pos = sm.base[e] + before + rank;
             sorted_ids[pos] = r;
             inverse[r] = pos;
         } else if (r < P) {
@@ -134,14 +142,50 @@ __global__ __launch_bounds__(kThreads) void k_align_sort(
         if (tid < E) {
             int sum = 0;
             for (int w = 0; w < kWaves; ++w)
-                sum += (s_hist[w][tid >> 1] >> ((tid & 1) * 16)) & 0xffff;
-            s_base[tid] += sum;
+                sum += (sm.hist[w][tid >> 1] >> ((tid & 1) * 16)) & 0xffff;
+            sm.base[tid] += sum;
         }
         __syncthreads();
         for (int x = tid; x < kWaves * half_words; x += kThreads)
-            s_hist[x / half_words][x % half_words] = 0;
+            sm.hist[x / half_words][x % half_words] = 0;
         // the next round's first barrier orders this clear before its atomics
     }
+}
+
+__global__ __launch_bounds__(kThreads) void k_align_sort(
+    const int32_t *__restrict__ ids, int P, int E, int bm, int slots, int tiles_cap,
+    int32_t *__restrict__ sorted_ids, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ tile_expert, int32_t *__restrict__ inverse,
+    int32_t *__restrict__ n_tiles)
+{
+    __shared__ AlignSmem sm;
+    align_block(ids, P, E, bm, slots, tiles_cap, sorted_ids, offsets, tile_expert, inverse,
+                n_tiles, sm);
+}
+
+// Routing of all T tokens (wave w takes tokens w, w+16, ...) then align/sort of their ids,
+// which stay in LDS in between.  During routing the per-wave histogram area holds each wave's
+// E selection keys for the group scan (E <= 512 fits).
+template <int SLOTS>
+__global__ __launch_bounds__(kThreads) void k_route_align(
+    const float *__restrict__ gating, const float *__restrict__ bias, int T, int E, int k,
+    int sigmoid, int renormalize, int n_group, int topk_group, float rsf,
+    int32_t *__restrict__ ids_out, float *__restrict__ weights_out, int bm, int slots,
+    int tiles_cap, int32_t *__restrict__ sorted_ids, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ tile_expert, int32_t *__restrict__ inverse,
+    int32_t *__restrict__ n_tiles)
+{
+    __shared__ AlignSmem sm;
+    __shared__ int32_t s_ids[kFusedMaxRoutes];
+    const int wv = threadIdx.x >> 6;
+    float *keys = reinterpret_cast<float *>(&sm.hist[wv][0]);  // kMaxExperts/2 floats per wave
+    for (int t = wv; t < T; t += kWaves)
+        moe_route_dev::route_token<SLOTS>(gating, bias, t, E, k, sigmoid, renormalize, n_group,
+                                          topk_group, rsf, keys, threadIdx.x & 63, ids_out,
+                                          weights_out, s_ids);
+    __syncthreads();
+    align_block(s_ids, T * k, E, bm, slots, tiles_cap, sorted_ids, offsets, tile_expert,
+                inverse, n_tiles, sm);
 }
 
 }  // namespace
@@ -156,6 +200,35 @@ void launch_align_sort(const int32_t *ids, int P, int E, int block_m, int32_t *s
     const int tiles_cap = P / block_m + E;
     hipLaunchKernelGGL(k_align_sort, dim3(1), dim3(kThreads), 0, stream, ids, P, E, block_m,
                        slots, tiles_cap, sorted_ids, offsets, tile_expert, inverse, n_tiles);
+}
+
+bool route_align_fusable(int T, int E, int k)
+{
+    return T * k <= kFusedMaxRoutes && E <= kFusedMaxExperts;
+}
+
+void launch_route_align(const float *gating, const float *bias, int T, int E, int k, int sigmoid,
+                        int renormalize, int n_group, int topk_group, float rsf, int32_t *ids,
+                        float *weights, int block_m, int32_t *sorted_ids, int32_t *offsets,
+                        int32_t *tile_expert, int32_t *inverse, int32_t *n_tiles,
+                        hipStream_t stream)
+{
+    const int P = T * k;
+    const int slots = P + E * (block_m - 1);
+    const int tiles_cap = P / block_m + E;
+#define MOE_RA_CASE(S)                                                                           \
+    hipLaunchKernelGGL(k_route_align<S>, dim3(1), dim3(kThreads), 0, stream, gating, bias, T, E, \
+                       k, sigmoid, renormalize, n_group, topk_group, rsf, ids, weights, block_m, \
+                       slots, tiles_cap, sorted_ids, offsets, tile_expert, inverse, n_tiles)
+    if (E <= 64)
+        MOE_RA_CASE(1);
+    else if (E <= 128)
+        MOE_RA_CASE(2);
+    else if (E <= 256)
+        MOE_RA_CASE(4);
+    else
+        MOE_RA_CASE(8);
+#undef MOE_RA_CASE
 }
 
 }  // namespace moe

@@ -34,7 +34,7 @@ struct Ctx {
     hipStream_t stream;
 };
 
-// Workspace-resident sorted layout (sorted path) and the GEMM problems of a plan.
+// The GEMM problems of a plan (sorted layout, when used, lives in the workspace).
 moe::GemmProblem gate_up_problem(const moe::Plan &pl, const Ctx &c)
 {
     moe::GemmProblem g = {};
@@ -50,10 +50,22 @@ moe::GemmProblem gate_up_problem(const moe::Plan &pl, const Ctx &c)
     if (pl.path == MOE_PATH_SORTED) {
         g.sorted_ids = ws_at<int32_t>(c.ws, pl.off_sorted);
         g.offsets = ws_at<int32_t>(c.ws, pl.off_offsets);
-        g.num_groups = pl.E;
+        g.tile_expert = ws_at<int32_t>(c.ws, pl.off_tile_expert);
+        g.num_groups = pl.gate_up.kind == moe::KERNEL_TILED ? pl.tiles_cap : pl.E;
     } else {
         g.num_groups = pl.P;
     }
+    return g;
+}
+
+moe::GemmProblem down_problem(const moe::Plan &pl, const Ctx &c)
+{
+    moe::GemmProblem g = gate_up_problem(pl, c);
+    g.act = ws_at<uint16_t>(c.ws, pl.off_h);
+    g.weight = c.w_down;
+    g.out = ws_at<uint16_t>(c.ws, pl.off_y);
+    g.K = pl.F;
+    g.n_out = pl.H;
     return g;
 }
 
@@ -73,7 +85,16 @@ moe::GemmProblem shared_problem(const moe::Plan &pl, const Ctx &c, bool gate_up)
     return g;
 }
 
-moe::WsTile ws_tile(const moe::TileChoice &t) { return moe::WsTile{t.nt, t.mt, t.ksplit}; }
+moe::WsTile ws_tile(const moe::TileChoice &t) { return moe::WsTile{t.nt, t.mt, t.ksplit, t.stages}; }
+
+bool launch_gemm(bool gate_up, const moe::GemmProblem &g, moe::RowSource src,
+                 const moe::TileChoice &t, hipStream_t stream)
+{
+    if (t.kind == moe::KERNEL_TILED)
+        return moe::launch_tiled(gate_up, g, src, ws_tile(t), stream);
+    return gate_up ? moe::launch_gate_up(g, src, ws_tile(t), stream)
+                   : moe::launch_down(g, src, ws_tile(t), stream);
+}
 
 int run_stage(int stage, const moe::Plan &pl, const Ctx &c)
 {
@@ -89,27 +110,20 @@ int run_stage(int stage, const moe::Plan &pl, const Ctx &c)
                                    ws_at<int32_t>(c.ws, pl.off_n_tiles), c.stream);
         break;
     case MOE_STAGE_GATE_UP:
-        if (!moe::launch_gate_up(gate_up_problem(pl, c), src, ws_tile(pl.gate_up), c.stream))
+        if (!launch_gemm(true, gate_up_problem(pl, c), src, pl.gate_up, c.stream))
             return MOE_ERR_LAUNCH;
         break;
-    case MOE_STAGE_DOWN: {
-        moe::GemmProblem g = gate_up_problem(pl, c);
-        g.act = ws_at<uint16_t>(c.ws, pl.off_h);
-        g.weight = c.w_down;
-        g.out = ws_at<uint16_t>(c.ws, pl.off_y);
-        g.K = pl.F;
-        g.n_out = pl.H;
-        if (!moe::launch_down(g, src, ws_tile(pl.down), c.stream))
+    case MOE_STAGE_DOWN:
+        if (!launch_gemm(false, down_problem(pl, c), src, pl.down, c.stream))
             return MOE_ERR_LAUNCH;
         break;
-    }
     case MOE_STAGE_SHARED:
         if (pl.S <= 0)
             return MOE_ERR_UNSUPPORTED;
-        if (!moe::launch_gate_up(shared_problem(pl, c, true), moe::ROWS_DENSE,
-                                 ws_tile(pl.shared_gate_up), c.stream) ||
-            !moe::launch_down(shared_problem(pl, c, false), moe::ROWS_DENSE,
-                              ws_tile(pl.shared_down), c.stream))
+        if (!launch_gemm(true, shared_problem(pl, c, true), moe::ROWS_DENSE, pl.shared_gate_up,
+                         c.stream) ||
+            !launch_gemm(false, shared_problem(pl, c, false), moe::ROWS_DENSE, pl.shared_down,
+                         c.stream))
             return MOE_ERR_LAUNCH;
         break;
     case MOE_STAGE_COMBINE:
@@ -123,10 +137,11 @@ int run_stage(int stage, const moe::Plan &pl, const Ctx &c)
     return launch_status();
 }
 
-// Routed experts (+ shared expert) and the combine, with the routing already in ids/weights.
-int experts_impl(const moe::Plan &pl, const Ctx &c)
+// Routed experts (+ shared expert) and the combine, with the routing already in ids/weights
+// (and, if first_stage is past MOE_STAGE_ALIGN, the sorted layout already in the workspace).
+int experts_impl(const moe::Plan &pl, const Ctx &c, int first_stage = MOE_STAGE_ALIGN)
 {
-    for (int stage = MOE_STAGE_ALIGN; stage <= MOE_STAGE_COMBINE; ++stage) {
+    for (int stage = first_stage; stage <= MOE_STAGE_COMBINE; ++stage) {
         if (stage == MOE_STAGE_SHARED && pl.S == 0)
             continue;
         const int st = run_stage(stage, pl, c);
@@ -167,10 +182,22 @@ int fused_impl(const uint16_t *hidden, const float *gating, const uint16_t *w_ga
 
     int32_t *ids = ids_out ? ids_out : ws_at<int32_t>(ws, pl.off_ids);
     float *weights = weights_out ? weights_out : ws_at<float>(ws, pl.off_weights);
-    moe::launch_route(gating, bias, pl.T, pl.E, pl.k, p->scoring == MOE_SCORING_SIGMOID,
-                      p->renormalize, p->num_expert_group, p->topk_group,
-                      p->routed_scaling_factor, ids, weights, s);
     const Ctx c = {hidden, w_gate_up, w_down, s_gu, s_d, ids, weights, out, ws, s};
+    const int sigmoid = p->scoring == MOE_SCORING_SIGMOID;
+    if (pl.path == MOE_PATH_SORTED && moe::route_align_fusable(pl.T, pl.E, pl.k)) {
+        // small batch: routing and the sort in one launch, ids kept on chip in between
+        moe::launch_route_align(gating, bias, pl.T, pl.E, pl.k, sigmoid, p->renormalize,
+                                p->num_expert_group, p->topk_group, p->routed_scaling_factor,
+                                ids, weights, pl.block_m, ws_at<int32_t>(ws, pl.off_sorted),
+                                ws_at<int32_t>(ws, pl.off_offsets),
+                                ws_at<int32_t>(ws, pl.off_tile_expert),
+                                ws_at<int32_t>(ws, pl.off_inverse),
+                                ws_at<int32_t>(ws, pl.off_n_tiles), s);
+        return experts_impl(pl, c, MOE_STAGE_GATE_UP);
+    }
+    moe::launch_route(gating, bias, pl.T, pl.E, pl.k, sigmoid, p->renormalize,
+                      p->num_expert_group, p->topk_group, p->routed_scaling_factor, ids,
+                      weights, s);
     return experts_impl(pl, c);
 }
 

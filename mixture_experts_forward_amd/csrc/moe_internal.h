@@ -17,6 +17,14 @@ void launch_align_sort(const int32_t *ids, int P, int E, int block_m, int32_t *s
                        int32_t *offsets, int32_t *tile_expert, int32_t *inverse, int32_t *n_tiles,
                        hipStream_t stream);
 
+// Routing + align/sort in one single-workgroup launch (small batches only).
+bool route_align_fusable(int T, int E, int k);
+void launch_route_align(const float *gating, const float *bias, int T, int E, int k, int sigmoid,
+                        int renormalize, int n_group, int topk_group, float rsf, int32_t *ids,
+                        float *weights, int block_m, int32_t *sorted_ids, int32_t *offsets,
+                        int32_t *tile_expert, int32_t *inverse, int32_t *n_tiles,
+                        hipStream_t stream);
+
 // ---------------------------------------------------------------- expert GEMMs
 // Where a GEMM takes its rows from.
 enum RowSource {
@@ -32,24 +40,32 @@ struct GemmProblem {
     const int32_t *sorted_ids;  // ROWS_SORTED
     const int32_t *offsets;     // ROWS_SORTED: [E+1]
     const int32_t *topk_ids;    // ROWS_DIRECT: [P]
+    const int32_t *tile_expert; // row-tiled kernel, ROWS_SORTED: expert of each row tile
     int K;                      // reduction length
     int n_out;                  // output columns (F for gate-up, H for down)
     int top_k;                  // routes per token
-    int num_groups;             // experts (SORTED), routes (DIRECT), row blocks (DENSE)
+    int num_groups;             // weight-streaming: experts (SORTED), routes (DIRECT), row
+                                // blocks (DENSE); row-tiled: row tiles
     int P;                      // routes (DIRECT)
     int rows;                   // tokens (DENSE)
     int num_experts;            // E (valid expert ids are [0, E))
 };
 
-// Tile shape of one weight-streaming launch: NT 16-column tiles per workgroup (per half for
-// gate-up), MT 16-row tiles per pass, KSPLIT waves splitting the K loop.
+// Tile shape of one launch.
+//   weight-streaming kernel: NT 16-column tiles per workgroup (per half for gate-up), MT 16-row
+//     tiles per pass, KSPLIT waves splitting the K loop;
+//   row-tiled kernel: NT 16-column tiles per wave (4 waves), 16*MT rows per tile (ksplit unused);
+//   both: STAGES register buffers (STAGES-1 k-steps of 64 in flight per wave).
 struct WsTile {
-    int nt, mt, ksplit;
+    int nt, mt, ksplit, stages;
 };
 
 // false: no kernel is instantiated for this tile shape (nothing launched)
 bool launch_gate_up(const GemmProblem &g, RowSource src, WsTile tile, hipStream_t stream);
 bool launch_down(const GemmProblem &g, RowSource src, WsTile tile, hipStream_t stream);
+// Row-tiled kernel (ROWS_SORTED with block_m = 16*tile.mt, or ROWS_DENSE).
+bool launch_tiled(bool gate_up, const GemmProblem &g, RowSource src, WsTile tile,
+                  hipStream_t stream);
 
 // ---------------------------------------------------------------- combine
 // out[t] = bf16( sum_j w[t,j] * y[t*k+j] (+ ys[t]) ), routes with ids outside [0,E) skipped.

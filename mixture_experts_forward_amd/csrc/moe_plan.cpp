@@ -7,19 +7,6 @@ namespace {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Row tiles per pass from the expected routed rows per expert, T*k/E: a weight tile is
-// streamed once per pass, so one pass should cover a typical expert (the tile tiers of the
-// FlashInfer BF16-activation PR follow the same routed-rows-per-expert density).
-int rows_tier(int P, int E)
-{
-    const double mean = (double)P / (double)E;
-    if (mean <= 8.0)
-        return 1;
-    if (mean <= 24.0)
-        return 2;
-    return 4;
-}
-
 }  // namespace
 
 int check_dims(const moe_params_t *p)
@@ -85,20 +72,27 @@ void make_plan(const moe_params_t *p, int32_t S, Plan *pl)
         pl->path = (P <= MOE_DIRECT_MAX_ROUTES) ? MOE_PATH_DIRECT : MOE_PATH_SORTED;
     else
         pl->path = p->path;
-    pl->block_m = kSortedBlockM;
+    // Kernel and tile by routed rows per expert, T*k/E (density tiers, as the FlashInfer
+    // BF16-activation PR picks its route tiles); shapes measured on MI355X.  Few rows per
+    // expert (decode): the weight-streaming kernel, one 16-column tile per wave for gate-up,
+    // two for down, K split over four waves, 16-row passes.  More (batch, prefill, shared
+    // expert): the row-tiled kernel, activation tile shared through LDS, 64- or 128-row tiles.
+    const double mean_rows = (double)P / (double)pl->E;
+    if (pl->path == MOE_PATH_DIRECT || mean_rows <= 8.0) {
+        pl->gate_up = {KERNEL_WS, 1, 1, 4, 3};
+        pl->down = {KERNEL_WS, 2, 1, 4, 2};
+    } else if (mean_rows <= 64.0) {
+        pl->gate_up = {KERNEL_TILED, 1, 4, 1, 3};
+        pl->down = {KERNEL_TILED, 2, 4, 1, 3};
+    } else {
+        pl->gate_up = {KERNEL_TILED, 1, 8, 1, 2};
+        pl->down = {KERNEL_TILED, 2, 8, 1, 2};
+    }
+    pl->shared_gate_up = {KERNEL_TILED, 1, 8, 1, 2};
+    pl->shared_down = {KERNEL_TILED, 2, 8, 1, 2};
+    pl->block_m = pl->gate_up.kind == KERNEL_TILED ? 16 * pl->gate_up.mt : kSortedBlockM;
     pl->slots = P + pl->E * (pl->block_m - 1);
     pl->tiles_cap = P / pl->block_m + pl->E;
-
-    if (pl->path == MOE_PATH_DIRECT) {
-        pl->gate_up = {1, 1, 4};
-        pl->down = {2, 1, 4};
-    } else {
-        const int mt = rows_tier(P, pl->E);
-        pl->gate_up = {2, mt, 2};
-        pl->down = {4, mt, 2};
-    }
-    pl->shared_gate_up = {2, 4, 1};
-    pl->shared_down = {4, 4, 1};
 
     size_t o = 0;
     auto take = [&](size_t bytes) {

@@ -15,8 +15,11 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxGroups = 64;
 constexpr int kSortedBlockM = 16;  // row tile of the weight-streaming GEMMs
 
+enum KernelKind { KERNEL_WS = 0, KERNEL_TILED = 1 };
+
 struct TileChoice {
-    int nt, mt, ksplit;
+    int kind;  // KernelKind
+    int nt, mt, ksplit, stages;
 };
 
 struct Plan {

@@ -1,0 +1,187 @@
+// moe_route_dev.h -- per-token top-k / grouped top-k routing on one wave (gfx950, wave64).
+//
+// Computes what the TileOPs "MoE" page's FusedTopKFwd op computes (gating_output [T,E] f32,
+// top_k, renormalize, scoring_func, correction_bias [E] f32, num_expert_group, topk_group,
+// routed_scaling_factor):
+//   - selection keys in f32: the logit for softmax; f32(f32(sigmoid(g)) + bias) for sigmoid,
+//     the sigmoid evaluated in double and rounded once;
+//   - grouped top-k: a group scores the f32 sum of its two largest keys, the topk_group best
+//     groups stay eligible (ties to the lower group);
+//   - top-k by key over eligible experts, ties to the lower expert index, ids in descending
+//     key order;
+//   - weights: unbiased scores of the chosen experts in double, renormalised if asked, times
+//     the routed scaling factor, rounded to f32 once.
+//
+// Layout: lane l of a token's wave holds experts e = 64*i + l (i < SLOTS), so the row load is
+// coalesced.  Selection runs on 64-bit keys (order-preserving f32 bits << 32 | ~index): the
+// wave maximum is the best expert with the lower-index tie-break built in, so every step is
+// exact integer comparison and the result is bit-identical to any correct implementation.
+#pragma once
+
+#include "moe_device.h"
+
+namespace moe_route_dev {
+
+
+__device__ __forceinline__ uint32_t ordered_bits(float f)
+{
+    if (f == 0.0f)
+        f = 0.0f;  // -0 and +0 are the same key
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t select_key(float key, int idx)
+{
+    return ((uint64_t)ordered_bits(key) << 32) | (uint64_t)(0xffffffffu - (uint32_t)idx);
+}
+
+__device__ __forceinline__ int select_index(uint64_t key)
+{
+    return (int)(0xffffffffu - (uint32_t)key);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)v, off);
+        const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off);
+        const uint64_t o = ((uint64_t)hi << 32) | lo;
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        v += __shfl_xor(v, off);
+    return v;
+}
+
+// Routes token t with one wave (lane = lane index).  s_key: E floats of LDS owned by this wave
+// (used when n_group > 1).  ids_copy: optional second destination of the ids (LDS).
+template <int SLOTS>
+__device__ __forceinline__ void route_token(
+    const float *__restrict__ gating, const float *__restrict__ bias, int t, int E, int k,
+    int sigmoid, int renormalize, int n_group, int topk_group, float rsf, float *s_key, int lane,
+    int32_t *__restrict__ ids_out, float *__restrict__ weights_out, int32_t *ids_copy)
+{
+    const float *g = gating + (size_t)t * E;
+
+    float key[SLOTS];
+    uint32_t eligible = 0;  // bit i: slot i holds an eligible expert
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i) {
+        const int e = 64 * i + lane;
+        key[i] = 0.0f;
+        if (e < E) {
+            const float gv = g[e];
+            if (sigmoid) {
+                const float s = (float)(1.0 / (1.0 + exp(-(double)gv)));
+                key[i] = s + (bias ? bias[e] : 0.0f);
+            } else {
+                key[i] = gv;
+            }
+            eligible |= 1u << i;
+        }
+    }
+
+    if (n_group > 1) {
+        // group scores: lane gi < n_group scans its contiguous group of E/n_group experts
+        const int gs = E / n_group;
+#pragma unroll
+        for (int i = 0; i < SLOTS; ++i) {
+            const int e = 64 * i + lane;
+            if (e < E)
+                s_key[e] = key[i];
+        }
+        moe_wave_sync();
+        uint64_t gkey = 0;
+        if (lane < n_group) {
+            float b1 = -INFINITY, b2 = -INFINITY;
+            for (int e = lane * gs; e < (lane + 1) * gs; ++e) {
+                const float v = s_key[e];
+                if (v > b1) {
+                    b2 = b1;
+                    b1 = v;
+                } else if (v > b2) {
+                    b2 = v;
+                }
+            }
+            const float score = (gs == 1) ? b1 : b1 + b2;
+            gkey = select_key(score, lane);
+        }
+        uint64_t kept = 0;  // bit gi: group gi kept
+        for (int n = 0; n < topk_group; ++n) {
+            const uint64_t best = wave_max_u64(gkey);
+            const int gi = select_index(best);
+            kept |= 1ull << gi;
+            if (lane == gi)
+                gkey = 0;
+        }
+#pragma unroll
+        for (int i = 0; i < SLOTS; ++i) {
+            const int e = 64 * i + lane;
+            if (e < E && !((kept >> (e / gs)) & 1ull))
+                eligible &= ~(1u << i);
+        }
+    }
+
+    // top-k: k rounds of a wave-wide maximum over the remaining eligible experts
+    int my_id = -1;
+    int first_id = 0;  // wave-uniform: the best expert overall
+    for (int j = 0; j < k; ++j) {
+        uint64_t best = 0;
+#pragma unroll
+        for (int i = 0; i < SLOTS; ++i) {
+            if ((eligible >> i) & 1u) {
+                const uint64_t c = select_key(key[i], 64 * i + lane);
+                best = c > best ? c : best;
+            }
+        }
+        best = wave_max_u64(best);
+        const int e = select_index(best);
+        if ((e & 63) == lane)
+            eligible &= ~(1u << (e >> 6));
+        if (lane == j)
+            my_id = e;
+        if (j == 0)
+            first_id = e;
+    }
+
+    // weights: lane j < k owns route j
+    // softmax is never grouped, so the first chosen expert holds the row's largest logit
+    const double m = (double)g[first_id];
+    double s = 0.0;
+    if (lane < k) {
+        const double gv = (double)g[my_id];
+        s = sigmoid ? 1.0 / (1.0 + exp(-gv)) : exp(gv - m);
+    }
+    double denom = 1.0;
+    if (renormalize) {
+        denom = wave_sum_f64(s);
+    } else if (!sigmoid) {
+        // full softmax denominator over all experts
+        double z = 0.0;
+#pragma unroll
+        for (int i = 0; i < SLOTS; ++i) {
+            const int e = 64 * i + lane;
+            if (e < E)
+                z += exp((double)g[e] - m);
+        }
+        denom = wave_sum_f64(z);
+    }
+    if (lane < k) {
+        const double w = s / denom * (double)rsf;
+        ids_out[(size_t)t * k + lane] = my_id;
+        weights_out[(size_t)t * k + lane] = (float)w;
+        if (ids_copy)
+            ids_copy[(size_t)t * k + lane] = my_id;
+    }
+}
+
+
+}  // namespace moe_route_dev

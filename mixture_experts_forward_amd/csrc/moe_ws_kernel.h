@@ -1,0 +1,296 @@
+// moe_ws_kernel.h -- the weight-streaming grouped GEMM kernel of the MoE experts (gfx950).
+//
+// gate-up (TileOPs "MoE" page, MoEGroupedGemmFwd with activation=silu_and_mul on
+// w_gate_up [E, 2F, H]):  h[row, f] = silu(x_row . Wg[e,f,:]) * (x_row . Wu[e,f,:])
+//   with Wg = rows [0,F) and Wu = rows [F,2F) of the expert's w_gate_up.
+// down (MoEGroupedGemmFwd on w_down [E, H, F]):  y[row, c] = h_row . Wd[e,c,:]
+//
+// At the routed-rows-per-expert counts of decode and batch MoE these GEMMs are bound by
+// reading every touched expert's weights from HBM once, so the kernel is built around that
+// stream:
+//   - a workgroup owns one expert (or one route on the direct path, or a block of tokens for
+//     the shared expert) and NT 16-column tiles of the output; it reads each weight row it
+//     needs once per pass over its rows;
+//   - weight loads are non-temporal and each load instruction covers whole 128-byte lines (8
+//     lanes x 16 bytes per row, 8 rows per instruction), with STAGES-1 k-steps of 64 elements
+//     in flight per wave in registers;
+//   - every workgroup starts its K loop at a different k-step (rotated, wrapping around), so
+//     the concurrent requests of the whole grid spread over all HBM channels instead of all
+//     hitting the same offset of 4 KB rows at once;
+//   - each k-step is transposed through a per-wave LDS buffer (XOR-swizzled 16-byte slots,
+//     conflict-free on both sides) into the v_mfma_f32_16x16x32_bf16 operand layout; the
+//     weights are the A operand, so a lane ends with four consecutive output columns of one row;
+//   - the activation rows (L2-resident) are loaded straight into the B operand layout;
+//   - KSPLIT waves split the K loop of the same tile and are summed through LDS in a fixed
+//     order: more bytes in flight per tile, no second kernel, deterministic results.
+// The gate and up tiles of the same columns sit in the same lanes, so SiLU(gate)*up is applied
+// in registers and h is rounded to bf16 once; stores are 8 bytes (4 bf16) per lane.
+//
+// Row sources: ROWS_SORTED walks one expert's padded segment of the sorted route list (pad
+// rows hold route -1 and are neither read nor written); ROWS_DIRECT scans topk_ids (T*k <= 64):
+// the first route of an expert gathers all routes of that expert and later ones exit, so an
+// expert's weights are streamed once however many tokens chose it; ROWS_DENSE takes every
+// token (shared expert).
+#pragma once
+
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe_ws {
+
+using moe::GemmProblem;
+
+// index of the n-th (0-based) set bit of m, or -1
+__device__ __forceinline__ int nth_set_bit(uint64_t m, int n)
+{
+    for (int i = 0; i < n && m; ++i)
+        m &= m - 1;
+    return m ? (int)__builtin_ctzll(m) : -1;
+}
+
+__device__ __forceinline__ moe_u32x4 load_nt(const uint16_t *p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const moe_u32x4 *>(p));
+}
+
+__device__ __forceinline__ moe_u32x4 load_cached(const uint16_t *p)
+{
+    return *reinterpret_cast<const moe_u32x4 *>(p);
+}
+
+// LDS bytes of one workgroup: per-wave transpose buffers, reused for the K-split sum.
+template <int NW, int MT, int KSPLIT>
+struct WsSmem {
+    static constexpr int kTranspose = KSPLIT * NW * 16 * 8;            // 16-byte slots
+    static constexpr int kReduce = (KSPLIT > 1 ? KSPLIT - 1 : 0) * MT * NW * 64;  // f32x4
+    static constexpr int kSlots = kTranspose > kReduce ? kTranspose : kReduce;
+};
+
+template <bool GATE_UP, int SRC, int NT, int MT, int KSPLIT, int STAGES>
+__global__ __launch_bounds__(64 * KSPLIT) void k_ws_gemm(GemmProblem g)
+{
+    constexpr int NW = GATE_UP ? 2 * NT : NT;  // 16-row weight tiles per k-step
+    constexpr int ROWS = 16 * MT;              // rows per pass
+    using Smem = WsSmem<NW, MT, KSPLIT>;
+    __shared__ moe_u32x4 s_mem[Smem::kSlots];
+
+    const int lane = threadIdx.x & 63;
+    const int kw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index (uniform)
+    const int col0 = blockIdx.x * (16 * NT);
+    const int grp = blockIdx.y;
+    const int K = g.K;
+
+    // ---- which rows this workgroup owns
+    int expert = 0, seg_begin = 0, n_rows = 0;
+    uint64_t members = 0;
+    if (SRC == moe::ROWS_SORTED) {
+        expert = grp;
+        seg_begin = g.offsets[grp];
+        n_rows = g.offsets[grp + 1] - seg_begin;
+    } else if (SRC == moe::ROWS_DIRECT) {
+        const int e = g.topk_ids[grp];
+        if (e < 0 || e >= g.num_experts)
+            return;
+        const int mine = (lane < g.P) ? g.topk_ids[lane] : -1;
+        members = __ballot(mine == e);
+        if (members & ((1ull << grp) - 1))
+            return;  // an earlier route of this expert owns it
+        expert = e;
+        n_rows = __popcll(members);
+    } else {
+        seg_begin = grp * ROWS;
+        n_rows = min(ROWS, g.rows - seg_begin);
+    }
+    if (n_rows <= 0)
+        return;
+
+    // ---- weight loads: lane reads 16 bytes (chunk lane%8) of rows lane/8 and 8 + lane/8 of
+    //      each 16-row tile
+    const int w_rows = GATE_UP ? 2 * g.n_out : g.n_out;
+    const uint16_t *W = g.weight + (size_t)expert * w_rows * K;
+    const int lrow = lane >> 3, lchunk = lane & 7;
+    const uint16_t *wld[NW];
+    bool tile_ok[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int c = col0 + 16 * nt;
+        tile_ok[nt] = c < g.n_out;
+        const int row = (tile_ok[nt] ? c : 0) + lrow;
+        wld[nt] = W + (size_t)row * K + 8 * lchunk;
+        if (GATE_UP)
+            wld[NT + nt] = W + (size_t)(row + g.n_out) * K + 8 * lchunk;
+    }
+    // LDS transpose buffer of this wave: NW tiles x 16 rows x 8 slots; row r keeps chunk c in
+    // slot c ^ (r >> 1)
+    moe_u32x4 *tbuf = s_mem + kw * NW * 128;
+    const int wslot0 = lrow * 8 + (lchunk ^ (lrow >> 1));
+    const int wslot1 = (lrow + 8) * 8 + (lchunk ^ ((lrow + 8) >> 1));
+    const int rrow = lane & 15, rq = lane >> 4;
+    const int rslot0 = rrow * 8 + (rq ^ (rrow >> 1));        // chunks 0..3 -> k 0..31
+    const int rslot1 = rrow * 8 + ((rq + 4) ^ (rrow >> 1));  // chunks 4..7 -> k 32..63
+    const int xoff = 8 * rq;                                 // B operand: k = 8*(lane/16) (+32)
+
+    // ---- K range of this wave, visited from a rotated start
+    const int nks = K / 64;
+    const int per = (nks + KSPLIT - 1) / KSPLIT;
+    const int ks0 = kw * per;
+    const int nk = max(0, min(nks, ks0 + per) - ks0);
+    const int rot = nk > 0 ? (int)((blockIdx.x * 7u + blockIdx.y * 13u) % (unsigned)nk) : 0;
+
+    for (int pass0 = 0; pass0 < n_rows; pass0 += ROWS) {
+        // ---- row plan: activation row and output row of slot lane%16 of each m-tile
+        const uint16_t *arow[MT];
+        int dst[MT];
+        const int mt_active = min(MT, (n_rows - pass0 + 15) / 16);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int s = pass0 + 16 * mt + (lane & 15);
+            int src_row = -1, dst_row = -1;
+            if (s < n_rows) {
+                if (SRC == moe::ROWS_SORTED) {
+                    const int row = seg_begin + s;
+                    const int route = g.sorted_ids[row];
+                    if (route >= 0) {
+                        src_row = GATE_UP ? route / g.top_k : row;
+                        dst_row = GATE_UP ? row : route;
+                    }
+                } else if (SRC == moe::ROWS_DIRECT) {
+                    const int route = nth_set_bit(members, s);
+                    src_row = GATE_UP ? route / g.top_k : route;
+                    dst_row = route;
+                } else {
+                    src_row = dst_row = seg_begin + s;
+                }
+            }
+            // an unused slot reads row 0: its column of the result is never stored
+            arow[mt] = g.act + (size_t)(src_row < 0 ? 0 : src_row) * K + xoff;
+            dst[mt] = dst_row;
+        }
+
+        moe_f32x4 acc[MT][NW];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nw = 0; nw < NW; ++nw)
+                acc[mt][nw] = moe_f32x4{0.f, 0.f, 0.f, 0.f};
+
+        moe_u32x4 wraw[STAGES][NW][2], xv[STAGES][MT][2];
+        auto load = [&](int st, int i) {
+            const int ks = ks0 + (i + rot) % nk;
+            const int k = ks * 64;
+#pragma unroll
+            for (int nw = 0; nw < NW; ++nw) {
+                if (tile_ok[nw % NT]) {
+                    wraw[st][nw][0] = load_nt(wld[nw] + k);
+                    wraw[st][nw][1] = load_nt(wld[nw] + (size_t)8 * K + k);
+                }
+            }
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                if (mt < mt_active) {
+                    xv[st][mt][0] = load_cached(arow[mt] + k);
+                    xv[st][mt][1] = load_cached(arow[mt] + k + 32);
+                }
+            }
+        };
+        auto compute = [&](int st) {
+#pragma unroll
+            for (int nw = 0; nw < NW; ++nw) {
+                if (tile_ok[nw % NT]) {
+                    tbuf[nw * 128 + wslot0] = wraw[st][nw][0];
+                    tbuf[nw * 128 + wslot1] = wraw[st][nw][1];
+                }
+            }
+            moe_wave_sync();
+#pragma unroll
+            for (int nw = 0; nw < NW; ++nw) {
+                if (!tile_ok[nw % NT])
+                    continue;
+                const moe_u32x4 a0 = tbuf[nw * 128 + rslot0];
+                const moe_u32x4 a1 = tbuf[nw * 128 + rslot1];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    if (mt < mt_active) {
+                        acc[mt][nw] = moe_mfma_16x16x32(a0, xv[st][mt][0], acc[mt][nw]);
+                        acc[mt][nw] = moe_mfma_16x16x32(a1, xv[st][mt][1], acc[mt][nw]);
+                    }
+                }
+            }
+            moe_wave_sync();
+        };
+
+        // software pipeline: STAGES-1 k-steps in flight
+#pragma unroll
+        for (int st = 0; st < STAGES - 1; ++st)
+            if (st < nk)
+                load(st, st);
+        for (int i = 0; i < nk; i += STAGES) {
+#pragma unroll
+            for (int st = 0; st < STAGES; ++st) {
+                const int cur = i + st;
+                if (cur < nk) {
+                    const int nxt = cur + STAGES - 1;
+                    if (nxt < nk)
+                        load((st + STAGES - 1) % STAGES, nxt);
+                    compute(st);
+                }
+            }
+        }
+
+        // ---- fixed-order sum over the K-split waves (LDS reused once every wave is done)
+        if (KSPLIT > 1) {
+            moe_f32x4 *red = reinterpret_cast<moe_f32x4 *>(s_mem);
+            __syncthreads();
+            if (kw > 0) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int nw = 0; nw < NW; ++nw)
+                        red[(((kw - 1) * MT + mt) * NW + nw) * 64 + lane] = acc[mt][nw];
+            }
+            __syncthreads();
+            if (kw == 0) {
+#pragma unroll
+                for (int w = 0; w < KSPLIT - 1; ++w)
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                        for (int nw = 0; nw < NW; ++nw)
+                            acc[mt][nw] += red[((w * MT + mt) * NW + nw) * 64 + lane];
+            }
+            __syncthreads();
+        }
+
+        // ---- epilogue (wave 0): lane holds columns 4*(lane/16)+r of row lane%16
+        if (kw == 0) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                if (mt >= mt_active || dst[mt] < 0)
+                    continue;
+                uint16_t *orow = g.out + (size_t)dst[mt] * g.n_out;
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    if (!tile_ok[nt])
+                        continue;
+                    float v[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        if (GATE_UP) {
+                            const float gate = acc[mt][nt][r];
+                            const float up = acc[mt][NT + nt][r];
+                            v[r] = gate / (1.0f + __expf(-gate)) * up;
+                        } else {
+                            v[r] = acc[mt][nt][r];
+                        }
+                    }
+                    moe_u32x2 packed;
+                    packed.x = moe_pack_bf16x2(v[0], v[1]);
+                    packed.y = moe_pack_bf16x2(v[2], v[3]);
+                    *reinterpret_cast<moe_u32x2 *>(orow + col0 + 16 * nt + 4 * rq) = packed;
+                }
+            }
+        }
+    }
+}
+
+}  // namespace moe_ws

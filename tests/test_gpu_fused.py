@@ -96,6 +96,24 @@ def test_shared_expert_small(T, path):
     _check_pass(cfg, make_inputs(cfg, DEV, seed=9), path, what="shared T=%d %s" % (T, path))
 
 
+@pytest.mark.parametrize("T,E,k,H,F", [
+    (37, 16, 4, 256, 128),    # ~9 rows per expert: 64-row tiles, ragged tiles and tail
+    (300, 8, 4, 128, 192),    # ~150 rows per expert: 128-row tiles, several per expert
+    (129, 4, 2, 192, 64),     # ~65 rows per expert: 128-row tiles, one partial
+    (70, 16, 8, 320, 64),     # ~35 rows per expert: 64-row tiles, F a single column block
+])
+def test_row_tiled_sizes(T, E, k, H, F):
+    cfg = replace(CONFIGS["tiny"], T=T, E=E, k=k, H=H, F=F)
+    _check_pass(cfg, make_inputs(cfg, DEV, seed=T), "sorted", what="tiled T=%d E=%d" % (T, E))
+
+
+@pytest.mark.parametrize("T", [1, 31, 200])
+def test_shared_expert_rows(T):
+    """Dense shared-expert GEMMs over 1, a ragged 31 and 200 (two 128-row tiles) tokens."""
+    cfg = replace(CONFIGS["kimi-k2-shared"], T=T, H=192, E=16, F=64, S=320, k=2)
+    _check_pass(cfg, make_inputs(cfg, DEV, seed=T + 1), "auto", what="shared rows T=%d" % T)
+
+
 @pytest.mark.parametrize("path", ["direct", "sorted"])
 def test_experts_given_routing_with_padding_and_repeats(path):
     """fused_moe_experts_fwd with -1 routes, repeated ids of one token, and NaN weights in every

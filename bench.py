@@ -48,11 +48,28 @@ def parse():
     ap.add_argument("--rotate", type=int, default=0, help="input sets (0 = automatic)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="one device-to-device copy of BYTES before the timed loops (the "
+                         "known-size reference for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
+                    help="write profiles/<kernel>_<workload>_pmc.txt from rocprofv3 --pmc "
+                         "output directories (FETCH_SIZE run, WRITE_SIZE run[, MFMA run])")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="write profiles/kernel_trace_<workload>.md from a rocprofv3 "
+                         "--kernel-trace --stats output directory")
+    ap.add_argument("--pmc-commands", nargs="*", default=[],
+                    help="the rocprofv3 command lines that produced --summarize-pmc's inputs")
     return ap.parse_args()
 
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(args)
+        return
+    if args.summarize_trace:
+        summarize_trace(args)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d "
               "requested). Run with --gpus 1." % args.gpus, file=sys.stderr)
@@ -75,6 +92,13 @@ def main():
     log("workload %s, %d input sets of %.2f GB weights" % (cfg.name, R, wbytes / 1e9))
     sets = [make_inputs(cfg, dev, seed=42 + i) for i in range(R)]
     torch.cuda.synchronize()
+    if args.copy_calibration:
+        src = torch.ones(args.copy_calibration, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)      # one plain copy kernel of known size
+        torch.cuda.synchronize()
+        del src, dst
 
     S = cfg.S
     p = moe.make_params(cfg.T, cfg.H, cfg.E, cfg.F, cfg.k, cfg.scoring, cfg.renormalize,
@@ -252,11 +276,118 @@ def read_traffic(workload):
 
 
 def kernel_source_hash():
+    """Hash of the GEMM kernel sources: counter summaries taken on other sources are stale."""
     import hashlib
     h = hashlib.sha256()
-    src = os.path.join(ROOT, "mixture_experts_forward_amd", "csrc", "moe_gemm_ws.hip")
-    h.update(open(src, "rb").read())
+    csrc = os.path.join(ROOT, "mixture_experts_forward_amd", "csrc")
+    for name in ("moe_ws_kernel.h", "moe_tiled_kernel.h", "moe_device.h", "moe_plan.cpp"):
+        h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()[:16]
+
+
+def _read_counters(d):
+    """rocprofv3 --pmc CSV rows of directory d -> {dispatch_id: (kernel name, {counter: value})}"""
+    import csv
+    import glob
+    out = {}
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for row in csv.DictReader(open(path)):
+            did = int(row["Dispatch_Id"])
+            name, vals = out.setdefault(did, (row["Kernel_Name"], {}))
+            vals[row["Counter_Name"]] = vals.get(row["Counter_Name"], 0.0) + \
+                float(row["Counter_Value"])
+    return out
+
+
+def _is_dominant(name):
+    """The gate-up GEMM of the routed experts (weight-streaming or row-tiled kernel)."""
+    return (("k_ws_gemm<true" in name or "k_tiled_gemm<true" in name)
+            and "<true, 2," not in name)
+
+
+def _calibration_copy(disp):
+    """Dispatch id of the calibration copy: the last copy kernel before the first routing
+    kernel of the pass."""
+    ids = sorted(disp)
+    first_route = next(i for i in ids if "k_route" in disp[i][0])
+    copies = [i for i in ids if i < first_route and "copy" in disp[i][0].lower()]
+    return copies[-1]
+
+
+def summarize_trace(args):
+    """profiles/kernel_trace_<workload>.md from a rocprofv3 --kernel-trace --stats run of
+    bench.py: per-kernel call counts and durations of the pass's kernels."""
+    import csv
+    import glob
+    from moe_harness.workloads import BENCH_CONFIG, CONFIGS
+    cfg = CONFIGS[args.config or BENCH_CONFIG]
+    path = glob.glob(os.path.join(args.summarize_trace, "**", "*kernel_stats.csv"),
+                     recursive=True)[0]
+    lines = ["# Kernel trace: fused MoE forward, workload %s (T=%d, H=%d, E=%d, F=%d, top-%d%s)"
+             % (cfg.name, cfg.T, cfg.H, cfg.E, cfg.F, cfg.k,
+                ", shared S=%d" % cfg.S if cfg.S else ""), ""]
+    for c in args.pmc_commands:
+        lines += ["Command (from /tmp, repository at $R):", "", "    " + c, ""]
+    lines += ["Input-generation and copy kernels are omitted.", "",
+              "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for r in csv.DictReader(open(path)):
+        n = r["Name"]
+        if "at::native" in n or "rocclr" in n:
+            continue
+        short = n.replace("(anonymous namespace)::", "").replace("void ", "")
+        short = short.split("(")[0] if "(" in short else short
+        lines.append("| `%s` | %s | %.2f | %.2f | %.2f |" % (
+            short, r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3))
+    lines += ["", "Template arguments: k_ws_gemm<GATE_UP, SRC, NT, MT, KSPLIT, STAGES> (SRC 0 "
+              "sorted, 1 direct, 2 dense); k_tiled_gemm<GATE_UP, SRC, BM, NTW, STAGES>."]
+    out = os.path.join(PROFILE_DIR, "kernel_trace_%s.md" % cfg.name)
+    os.makedirs(PROFILE_DIR, exist_ok=True)
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_pmc(args):
+    """profiles/gate_up_<workload>_pmc.txt from rocprofv3 --pmc runs of bench.py
+    --copy-calibration (FETCH_SIZE run, WRITE_SIZE run, optional MFMA-busy run)."""
+    from moe_harness.workloads import BENCH_CONFIG, CONFIGS
+    cfg = CONFIGS[args.config or BENCH_CONFIG]
+    runs = [_read_counters(d) for d in args.summarize_pmc]
+    res = {}
+    lines = ["# HBM traffic and MFMA activity of the gate-up GEMM, workload %s" % cfg.name,
+             "# FETCH_SIZE / WRITE_SIZE are per-dispatch KiB; each is scaled by the reading of "
+             "the same counter for one plain device-to-device copy of known size in the same "
+             "run.", "#"]
+    for c in args.pmc_commands:
+        lines.append("command: %s" % c)
+    for counter, disp in zip(("FETCH_SIZE", "WRITE_SIZE"), runs[:2]):
+        dom = [v[counter] for i, (n, v) in disp.items() if _is_dominant(n) and counter in v]
+        names = sorted({n for n, v in disp.values() if _is_dominant(n)})
+        cal = disp[_calibration_copy(disp)][1][counter]
+        copy_bytes = args.copy_calibration
+        scale = copy_bytes / (cal * 1024.0)
+        res[counter] = sum(dom) / len(dom) * 1024.0 * scale
+        lines += ["%s_kib_per_dispatch: %.1f" % (counter.lower(), sum(dom) / len(dom)),
+                  "%s_dispatches: %d" % (counter.lower(), len(dom)),
+                  "%s_copy_kib: %.1f" % (counter.lower(), cal),
+                  "%s_scale: %.5f" % (counter.lower(), scale)]
+        res["kernels"] = names
+    if len(runs) > 2:
+        disp = runs[2]
+        busy = [v["SQ_VALU_MFMA_BUSY_CYCLES"] / (v["GRBM_GUI_ACTIVE"] * 1024.0)
+                for n, v in disp.values() if _is_dominant(n) and "GRBM_GUI_ACTIVE" in v]
+        if busy:
+            lines.append("mfma_busy_pct: %.2f" % (100.0 * sum(busy) / len(busy)))
+    lines += ["copy_bytes: %d" % args.copy_calibration,
+              "kernel: %s" % "; ".join(res["kernels"]),
+              "kernel_source_sha256: %s" % kernel_source_hash(),
+              "fetch_bytes_per_launch: %.0f" % res["FETCH_SIZE"],
+              "write_bytes_per_launch: %.0f" % res["WRITE_SIZE"],
+              "traffic_bytes_per_launch: %.0f" % (res["FETCH_SIZE"] + res["WRITE_SIZE"])]
+    path = os.path.join(PROFILE_DIR, "gate_up_%s_pmc.txt" % cfg.name)
+    os.makedirs(PROFILE_DIR, exist_ok=True)
+    open(path, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def cpu_baseline(cfg, d, seconds):

@@ -53,14 +53,16 @@ enum {
 enum { MOE_SCORING_SOFTMAX = 0, MOE_SCORING_SIGMOID = 1 };
 
 /* Path selection for fused_moe_fwd / fused_moe_shared_fwd / fused_moe_experts_fwd.
- * AUTO: DIRECT when T*k <= MOE_DIRECT_MAX_ROUTES, SORTED otherwise.
- * DIRECT: no sort; one workgroup per (route, column block) reads topk_ids straight away, the
- *   first route of each expert gathers every route of that expert (aiter MI308 decoding PR,
- *   "Changes": direct decoding from topk_ids over tokens x routes).  Requires
+ * AUTO: DIRECT when T*k <= MOE_DIRECT_MAX_ROUTES and T*k <= 8*E (a few routed rows per expert),
+ *   SORTED otherwise.
+ * DIRECT: no sort; the expert GEMMs read topk_ids straight away (aiter MI308 decoding PR,
+ *   "Changes": direct decoding from topk_ids).  For T*k <= 64 one workgroup per (route, column
+ *   block), the first route of each expert gathering every route of that expert; above that one
+ *   workgroup per (expert, column block) scanning all routes for its expert.  Requires
  *   T*k <= MOE_DIRECT_MAX_ROUTES, else MOE_ERR_UNSUPPORTED.
  * SORTED: align/sort first, then expert-contiguous grouped GEMMs. */
 enum { MOE_PATH_AUTO = 0, MOE_PATH_DIRECT = 1, MOE_PATH_SORTED = 2 };
-#define MOE_DIRECT_MAX_ROUTES 64
+#define MOE_DIRECT_MAX_ROUTES 512
 
 /* Attributes of the pass (TileOPs "MoE" page, FusedMoEFwd and FusedTopKFwd attributes).
  *   num_tokens T >= 0; hidden H; num_experts E; inter F (expert intermediate size); top_k k.

@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
 MOE_OK = 0
 SCORING = {"softmax": 0, "sigmoid": 1}
 PATHS = {"auto": 0, "direct": 1, "sorted": 2}
-DIRECT_MAX_ROUTES = 64
+DIRECT_MAX_ROUTES = 512
 
 
 class MoEError(RuntimeError):

@@ -1,5 +1,4 @@
-// moe_align.hip -- expert histogram, padded prefix sum and stable permutation of routes, and the
-// fused routing + align kernel used for small batches.
+// moe_align.hip -- expert histogram, padded prefix sum and stable permutation of routes.
 //
 // Computes the expert-contiguous route order of the TileOPs "MoE" page's MoEPermuteAlignFwd
 // (topk_ids [T,K] i32 -> per-expert prefix sums of the contiguous layout) together with the
@@ -14,19 +13,14 @@
 //      expert in earlier waves of the round (per-wave histograms packed as two 16-bit counters
 //      per word) + its rank among earlier lanes of its own wave (LDS broadcast compare).
 // Every slot of sorted_route_ids and tile_expert is written exactly once.
-//
-// k_route_align routes up to kFusedMaxRoutes routes with the same 16 waves first (one wave per
-// token, moe_route_dev.h), keeps the ids in LDS and sorts them without a second launch.
+#include "moe_device.h"
 #include "moe_internal.h"
-#include "moe_route_dev.h"
 
 namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxExperts = 1024;
-constexpr int kFusedMaxRoutes = 2048;
-constexpr int kFusedMaxExperts = 512;
 
 struct AlignSmem {
     int count[kMaxExperts];
@@ -48,11 +42,14 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane)
     return v;
 }
 
-// The whole align/sort by one 1024-thread workgroup.  ids may point to global memory or LDS.
-__device__ void align_block(const int32_t *ids, int P, int E, int bm, int slots, int tiles_cap,
-                            int32_t *__restrict__ sorted_ids, int32_t *__restrict__ offsets,
-                            int32_t *__restrict__ tile_expert, int32_t *__restrict__ inverse,
-                            int32_t *__restrict__ n_tiles, AlignSmem &sm)
+// The whole align/sort by one 1024-thread workgroup.
+__device__ __forceinline__ void align_block(const int32_t *__restrict__ ids, int P, int E, int bm,
+                                            int slots, int tiles_cap,
+                                            int32_t *__restrict__ sorted_ids,
+                                            int32_t *__restrict__ offsets,
+                                            int32_t *__restrict__ tile_expert,
+                                            int32_t *__restrict__ inverse,
+                                            int32_t *__restrict__ n_tiles, AlignSmem &sm)
 {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -163,31 +160,6 @@ __global__ __launch_bounds__(kThreads) void k_align_sort(
                 n_tiles, sm);
 }
 
-// Routing of all T tokens (wave w takes tokens w, w+16, ...) then align/sort of their ids,
-// which stay in LDS in between.  During routing the per-wave histogram area holds each wave's
-// E selection keys for the group scan (E <= 512 fits).
-template <int SLOTS>
-__global__ __launch_bounds__(kThreads) void k_route_align(
-    const float *__restrict__ gating, const float *__restrict__ bias, int T, int E, int k,
-    int sigmoid, int renormalize, int n_group, int topk_group, float rsf,
-    int32_t *__restrict__ ids_out, float *__restrict__ weights_out, int bm, int slots,
-    int tiles_cap, int32_t *__restrict__ sorted_ids, int32_t *__restrict__ offsets,
-    int32_t *__restrict__ tile_expert, int32_t *__restrict__ inverse,
-    int32_t *__restrict__ n_tiles)
-{
-    __shared__ AlignSmem sm;
-    __shared__ int32_t s_ids[kFusedMaxRoutes];
-    const int wv = threadIdx.x >> 6;
-    float *keys = reinterpret_cast<float *>(&sm.hist[wv][0]);  // kMaxExperts/2 floats per wave
-    for (int t = wv; t < T; t += kWaves)
-        moe_route_dev::route_token<SLOTS>(gating, bias, t, E, k, sigmoid, renormalize, n_group,
-                                          topk_group, rsf, keys, threadIdx.x & 63, ids_out,
-                                          weights_out, s_ids);
-    __syncthreads();
-    align_block(s_ids, T * k, E, bm, slots, tiles_cap, sorted_ids, offsets, tile_expert,
-                inverse, n_tiles, sm);
-}
-
 }  // namespace
 
 namespace moe {
@@ -200,35 +172,6 @@ void launch_align_sort(const int32_t *ids, int P, int E, int block_m, int32_t *s
     const int tiles_cap = P / block_m + E;
     hipLaunchKernelGGL(k_align_sort, dim3(1), dim3(kThreads), 0, stream, ids, P, E, block_m,
                        slots, tiles_cap, sorted_ids, offsets, tile_expert, inverse, n_tiles);
-}
-
-bool route_align_fusable(int T, int E, int k)
-{
-    return T * k <= kFusedMaxRoutes && E <= kFusedMaxExperts;
-}
-
-void launch_route_align(const float *gating, const float *bias, int T, int E, int k, int sigmoid,
-                        int renormalize, int n_group, int topk_group, float rsf, int32_t *ids,
-                        float *weights, int block_m, int32_t *sorted_ids, int32_t *offsets,
-                        int32_t *tile_expert, int32_t *inverse, int32_t *n_tiles,
-                        hipStream_t stream)
-{
-    const int P = T * k;
-    const int slots = P + E * (block_m - 1);
-    const int tiles_cap = P / block_m + E;
-#define MOE_RA_CASE(S)                                                                           \
-    hipLaunchKernelGGL(k_route_align<S>, dim3(1), dim3(kThreads), 0, stream, gating, bias, T, E, \
-                       k, sigmoid, renormalize, n_group, topk_group, rsf, ids, weights, block_m, \
-                       slots, tiles_cap, sorted_ids, offsets, tile_expert, inverse, n_tiles)
-    if (E <= 64)
-        MOE_RA_CASE(1);
-    else if (E <= 128)
-        MOE_RA_CASE(2);
-    else if (E <= 256)
-        MOE_RA_CASE(4);
-    else
-        MOE_RA_CASE(8);
-#undef MOE_RA_CASE
 }
 
 }  // namespace moe

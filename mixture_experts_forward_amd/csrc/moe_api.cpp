@@ -53,7 +53,7 @@ moe::GemmProblem gate_up_problem(const moe::Plan &pl, const Ctx &c)
         g.tile_expert = ws_at<int32_t>(c.ws, pl.off_tile_expert);
         g.num_groups = pl.gate_up.kind == moe::KERNEL_TILED ? pl.tiles_cap : pl.E;
     } else {
-        g.num_groups = pl.P;
+        g.num_groups = pl.P <= 64 ? pl.P : pl.E;  // per route (direct) or per expert (scan)
     }
     return g;
 }
@@ -98,7 +98,9 @@ bool launch_gemm(bool gate_up, const moe::GemmProblem &g, moe::RowSource src,
 
 int run_stage(int stage, const moe::Plan &pl, const Ctx &c)
 {
-    const moe::RowSource src = pl.path == MOE_PATH_SORTED ? moe::ROWS_SORTED : moe::ROWS_DIRECT;
+    const moe::RowSource src = pl.path == MOE_PATH_SORTED ? moe::ROWS_SORTED
+                               : pl.P <= 64                ? moe::ROWS_DIRECT
+                                                           : moe::ROWS_SCAN;
     switch (stage) {
     case MOE_STAGE_ALIGN:
         if (pl.path == MOE_PATH_SORTED)
@@ -184,17 +186,6 @@ int fused_impl(const uint16_t *hidden, const float *gating, const uint16_t *w_ga
     float *weights = weights_out ? weights_out : ws_at<float>(ws, pl.off_weights);
     const Ctx c = {hidden, w_gate_up, w_down, s_gu, s_d, ids, weights, out, ws, s};
     const int sigmoid = p->scoring == MOE_SCORING_SIGMOID;
-    if (pl.path == MOE_PATH_SORTED && moe::route_align_fusable(pl.T, pl.E, pl.k)) {
-        // small batch: routing and the sort in one launch, ids kept on chip in between
-        moe::launch_route_align(gating, bias, pl.T, pl.E, pl.k, sigmoid, p->renormalize,
-                                p->num_expert_group, p->topk_group, p->routed_scaling_factor,
-                                ids, weights, pl.block_m, ws_at<int32_t>(ws, pl.off_sorted),
-                                ws_at<int32_t>(ws, pl.off_offsets),
-                                ws_at<int32_t>(ws, pl.off_tile_expert),
-                                ws_at<int32_t>(ws, pl.off_inverse),
-                                ws_at<int32_t>(ws, pl.off_n_tiles), s);
-        return experts_impl(pl, c, MOE_STAGE_GATE_UP);
-    }
     moe::launch_route(gating, bias, pl.T, pl.E, pl.k, sigmoid, p->renormalize,
                       p->num_expert_group, p->topk_group, p->routed_scaling_factor, ids,
                       weights, s);

@@ -24,6 +24,7 @@ bool dispatch(const GemmProblem &g, moe::WsTile t, hipStream_t s)
     }
     MOE_WS_CASE(1, 1, 4, 3)
     MOE_WS_CASE(2, 1, 4, 2)
+    MOE_WS_CASE(2, 1, 2, 3)
 #undef MOE_WS_CASE
     return false;
 }
@@ -36,17 +37,27 @@ static bool launch_any(bool gate_up, const GemmProblem &g, RowSource src, WsTile
                        hipStream_t stream)
 {
     if (gate_up) {
-        if (src == ROWS_SORTED)
+        switch (src) {
+        case ROWS_SORTED:
             return dispatch<true, ROWS_SORTED>(g, tile, stream);
-        if (src == ROWS_DIRECT)
+        case ROWS_DIRECT:
             return dispatch<true, ROWS_DIRECT>(g, tile, stream);
-        return dispatch<true, ROWS_DENSE>(g, tile, stream);
+        case ROWS_SCAN:
+            return dispatch<true, ROWS_SCAN>(g, tile, stream);
+        default:
+            return dispatch<true, ROWS_DENSE>(g, tile, stream);
+        }
     }
-    if (src == ROWS_SORTED)
+    switch (src) {
+    case ROWS_SORTED:
         return dispatch<false, ROWS_SORTED>(g, tile, stream);
-    if (src == ROWS_DIRECT)
+    case ROWS_DIRECT:
         return dispatch<false, ROWS_DIRECT>(g, tile, stream);
-    return dispatch<false, ROWS_DENSE>(g, tile, stream);
+    case ROWS_SCAN:
+        return dispatch<false, ROWS_SCAN>(g, tile, stream);
+    default:
+        return dispatch<false, ROWS_DENSE>(g, tile, stream);
+    }
 }
 
 bool launch_gate_up(const GemmProblem &g, RowSource src, WsTile tile, hipStream_t stream)

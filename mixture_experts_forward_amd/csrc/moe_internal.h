@@ -17,21 +17,15 @@ void launch_align_sort(const int32_t *ids, int P, int E, int block_m, int32_t *s
                        int32_t *offsets, int32_t *tile_expert, int32_t *inverse, int32_t *n_tiles,
                        hipStream_t stream);
 
-// Routing + align/sort in one single-workgroup launch (small batches only).
-bool route_align_fusable(int T, int E, int k);
-void launch_route_align(const float *gating, const float *bias, int T, int E, int k, int sigmoid,
-                        int renormalize, int n_group, int topk_group, float rsf, int32_t *ids,
-                        float *weights, int block_m, int32_t *sorted_ids, int32_t *offsets,
-                        int32_t *tile_expert, int32_t *inverse, int32_t *n_tiles,
-                        hipStream_t stream);
-
 // ---------------------------------------------------------------- expert GEMMs
 // Where a GEMM takes its rows from.
 enum RowSource {
     ROWS_SORTED = 0,  // rows of one expert's padded segment of the sorted route list
-    ROWS_DIRECT = 1,  // routes of one expert found by scanning topk_ids (no sort)
+    ROWS_DIRECT = 1,  // route-major, no sort: the first route of an expert gathers its routes
     ROWS_DENSE = 2,   // every token, one weight matrix (shared expert)
+    ROWS_SCAN = 3,    // expert-major, no sort: the expert's routes found by scanning topk_ids
 };
+constexpr int kScanMaxRoutes = 512;  // ROWS_SCAN: routes scanned by one workgroup
 
 struct GemmProblem {
     const uint16_t *act;        // activation rows [*, K] bf16

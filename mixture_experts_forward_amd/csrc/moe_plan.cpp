@@ -68,8 +68,10 @@ void make_plan(const moe_params_t *p, int32_t S, Plan *pl)
     pl->S = S;
     pl->P = pl->T * pl->k;
     const int P = pl->P;
+    const double mean_rows = (double)P / (double)pl->E;
     if (p->path == MOE_PATH_AUTO)
-        pl->path = (P <= MOE_DIRECT_MAX_ROUTES) ? MOE_PATH_DIRECT : MOE_PATH_SORTED;
+        pl->path = (P <= MOE_DIRECT_MAX_ROUTES && mean_rows <= 8.0) ? MOE_PATH_DIRECT
+                                                                   : MOE_PATH_SORTED;
     else
         pl->path = p->path;
     // Kernel and tile by routed rows per expert, T*k/E (density tiers, as the FlashInfer
@@ -77,8 +79,10 @@ void make_plan(const moe_params_t *p, int32_t S, Plan *pl)
     // expert (decode): the weight-streaming kernel, one 16-column tile per wave for gate-up,
     // two for down, K split over four waves, 16-row passes.  More (batch, prefill, shared
     // expert): the row-tiled kernel, activation tile shared through LDS, 64- or 128-row tiles.
-    const double mean_rows = (double)P / (double)pl->E;
-    if (pl->path == MOE_PATH_DIRECT || mean_rows <= 8.0) {
+    if (pl->path == MOE_PATH_DIRECT) {
+        pl->gate_up = {KERNEL_WS, 1, 1, 4, 3};
+        pl->down = {KERNEL_WS, 2, 1, P <= 64 ? 4 : 2, P <= 64 ? 2 : 3};
+    } else if (mean_rows <= 8.0) {
         pl->gate_up = {KERNEL_WS, 1, 1, 4, 3};
         pl->down = {KERNEL_WS, 2, 1, 4, 2};
     } else if (mean_rows <= 64.0) {

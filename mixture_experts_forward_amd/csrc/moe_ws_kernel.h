@@ -27,10 +27,12 @@
 // in registers and h is rounded to bf16 once; stores are 8 bytes (4 bf16) per lane.
 //
 // Row sources: ROWS_SORTED walks one expert's padded segment of the sorted route list (pad
-// rows hold route -1 and are neither read nor written); ROWS_DIRECT scans topk_ids (T*k <= 64):
-// the first route of an expert gathers all routes of that expert and later ones exit, so an
-// expert's weights are streamed once however many tokens chose it; ROWS_DENSE takes every
-// token (shared expert).
+// rows hold route -1 and are neither read nor written).  Without a sort: ROWS_DIRECT (T*k <= 64)
+// runs one workgroup per route, the first route of an expert gathers all routes of that expert
+// and later ones exit; ROWS_SCAN (T*k <= 512) runs one workgroup per expert, which finds its
+// routes by scanning topk_ids with wave ballots.  Either way an expert's weights are streamed
+// once however many tokens chose it, and rows are taken in route order.  ROWS_DENSE takes
+// every token (shared expert).
 #pragma once
 
 #include "moe_device.h"
@@ -46,6 +48,21 @@ __device__ __forceinline__ int nth_set_bit(uint64_t m, int n)
     for (int i = 0; i < n && m; ++i)
         m &= m - 1;
     return m ? (int)__builtin_ctzll(m) : -1;
+}
+
+constexpr int kScanChunks = moe::kScanMaxRoutes / 64;
+
+// index of the n-th member of the route set given as kScanChunks 64-bit masks, or -1
+__device__ __forceinline__ int nth_member(const uint64_t (&masks)[kScanChunks], int n)
+{
+#pragma unroll
+    for (int c = 0; c < kScanChunks; ++c) {
+        const int pc = __popcll(masks[c]);
+        if (n < pc)
+            return 64 * c + nth_set_bit(masks[c], n);
+        n -= pc;
+    }
+    return -1;
 }
 
 __device__ __forceinline__ moe_u32x4 load_nt(const uint16_t *p)
@@ -83,7 +100,17 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_ws_gemm(GemmProblem g)
     // ---- which rows this workgroup owns
     int expert = 0, seg_begin = 0, n_rows = 0;
     uint64_t members = 0;
-    if (SRC == moe::ROWS_SORTED) {
+    uint64_t scan_masks[kScanChunks];
+    if (SRC == moe::ROWS_SCAN) {
+        expert = grp;
+#pragma unroll
+        for (int c = 0; c < kScanChunks; ++c) {
+            const int r = 64 * c + lane;
+            const int id = (r < g.P) ? g.topk_ids[r] : -1;
+            scan_masks[c] = __ballot(id == expert);
+            n_rows += __popcll(scan_masks[c]);
+        }
+    } else if (SRC == moe::ROWS_SORTED) {
         expert = grp;
         seg_begin = g.offsets[grp];
         n_rows = g.offsets[grp + 1] - seg_begin;
@@ -137,7 +164,31 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_ws_gemm(GemmProblem g)
     const int nk = max(0, min(nks, ks0 + per) - ks0);
     const int rot = nk > 0 ? (int)((blockIdx.x * 7u + blockIdx.y * 13u) % (unsigned)nk) : 0;
 
+    moe_u32x4 wraw[STAGES][NW][2];
+    auto load_w = [&](int st, int i) {
+        const int k = (ks0 + (i + rot) % nk) * 64;
+#pragma unroll
+        for (int nw = 0; nw < NW; ++nw) {
+            if (tile_ok[nw % NT]) {
+                wraw[st][nw][0] = load_nt(wld[nw] + k);
+                wraw[st][nw][1] = load_nt(wld[nw] + (size_t)8 * K + k);
+            }
+        }
+    };
+    // The first pass's weight prefetch is issued before its row plan: the plan's dependent
+    // loads (sorted ids or scan -> route -> token row) then overlap the weight latency.
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st)
+        if (st < nk)
+            load_w(st, st);
+
     for (int pass0 = 0; pass0 < n_rows; pass0 += ROWS) {
+        if (pass0 > 0) {
+#pragma unroll
+            for (int st = 0; st < STAGES - 1; ++st)
+                if (st < nk)
+                    load_w(st, st);
+        }
         // ---- row plan: activation row and output row of slot lane%16 of each m-tile
         const uint16_t *arow[MT];
         int dst[MT];
@@ -154,8 +205,9 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_ws_gemm(GemmProblem g)
                         src_row = GATE_UP ? route / g.top_k : row;
                         dst_row = GATE_UP ? row : route;
                     }
-                } else if (SRC == moe::ROWS_DIRECT) {
-                    const int route = nth_set_bit(members, s);
+                } else if (SRC == moe::ROWS_DIRECT || SRC == moe::ROWS_SCAN) {
+                    const int route = SRC == moe::ROWS_DIRECT ? nth_set_bit(members, s)
+                                                              : nth_member(scan_masks, s);
                     src_row = GATE_UP ? route / g.top_k : route;
                     dst_row = route;
                 } else {
@@ -174,17 +226,9 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_ws_gemm(GemmProblem g)
             for (int nw = 0; nw < NW; ++nw)
                 acc[mt][nw] = moe_f32x4{0.f, 0.f, 0.f, 0.f};
 
-        moe_u32x4 wraw[STAGES][NW][2], xv[STAGES][MT][2];
-        auto load = [&](int st, int i) {
-            const int ks = ks0 + (i + rot) % nk;
-            const int k = ks * 64;
-#pragma unroll
-            for (int nw = 0; nw < NW; ++nw) {
-                if (tile_ok[nw % NT]) {
-                    wraw[st][nw][0] = load_nt(wld[nw] + k);
-                    wraw[st][nw][1] = load_nt(wld[nw] + (size_t)8 * K + k);
-                }
-            }
+        moe_u32x4 xv[STAGES][MT][2];
+        auto load_x = [&](int st, int i) {
+            const int k = (ks0 + (i + rot) % nk) * 64;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 if (mt < mt_active) {
@@ -219,19 +263,21 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_ws_gemm(GemmProblem g)
             moe_wave_sync();
         };
 
-        // software pipeline: STAGES-1 k-steps in flight
+        // software pipeline: STAGES-1 k-steps in flight (their weights already requested)
 #pragma unroll
         for (int st = 0; st < STAGES - 1; ++st)
             if (st < nk)
-                load(st, st);
+                load_x(st, st);
         for (int i = 0; i < nk; i += STAGES) {
 #pragma unroll
             for (int st = 0; st < STAGES; ++st) {
                 const int cur = i + st;
                 if (cur < nk) {
                     const int nxt = cur + STAGES - 1;
-                    if (nxt < nk)
-                        load((st + STAGES - 1) % STAGES, nxt);
+                    if (nxt < nk) {
+                        load_w((st + STAGES - 1) % STAGES, nxt);
+                        load_x((st + STAGES - 1) % STAGES, nxt);
+                    }
                     compute(st);
                 }
             }

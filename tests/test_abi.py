@@ -61,25 +61,29 @@ def test_check_params_rules():
     assert _check(g) == -3
     g = moe.make_params(4, 128, 8, 64, 4, "sigmoid", True, 4, 2)
     assert _check(g, bias=1) == 0
-    assert _check(moe.make_params(9, 128, 8, 64, 8, path="direct")) == -3  # 72 routes > 64
-    assert _check(moe.make_params(8, 128, 8, 64, 8, path="direct")) == 0
+    assert _check(moe.make_params(65, 128, 8, 64, 8, path="direct")) == -3  # 520 routes > 512
+    assert _check(moe.make_params(64, 128, 8, 64, 8, path="direct")) == 0
     assert _check(ok, S=-64) == -2
     assert _check(ok, S=100) == -3
     assert _check(ok, S=18432) == 0
 
 
 def test_workspace_bytes():
+    # decode batch (2 routed rows per expert): direct path, h and y in route order
     p = moe.make_params(32, 2048, 128, 768, 8)
     n = moe.workspace_bytes(p)
     P = 256
-    slots = P + 128 * 15
-    # routing + sorted lists + h [slots, F] bf16 + y [P, H] bf16, each 256-aligned
-    assert n >= slots * 768 * 2 + P * 2048 * 2
+    assert n >= P * 768 * 2 + P * 2048 * 2
     assert n % 256 == 0
-    assert moe.workspace_bytes(p, 18432) > n
+    assert moe.workspace_bytes(p, 18432) >= n + 32 * 18432 * 2 + 32 * 2048 * 2
     assert moe.workspace_bytes(moe.make_params(0, 2048, 128, 768, 8)) == 0
-    small = moe.make_params(8, 2048, 128, 768, 8)
-    assert moe.workspace_bytes(small) < n                      # direct path: no sorted lists
+    # the same shape forced onto the sorted path also holds the sorted lists, padded to 16 rows
+    s = moe.workspace_bytes(moe.make_params(32, 2048, 128, 768, 8, path="sorted"))
+    slots = P + 128 * 15
+    assert s >= slots * 768 * 2 + P * 2048 * 2 and s > n
+    # prefill: 128-row tiles
+    q = moe.workspace_bytes(moe.make_params(4096, 7168, 256, 2048, 8))
+    assert q >= (32768 + 256 * 127) * 2048 * 2 + 32768 * 7168 * 2
 
 
 def test_entry_points_reject_before_launch():

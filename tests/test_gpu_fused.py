@@ -114,12 +114,14 @@ def test_shared_expert_rows(T):
     _check_pass(cfg, make_inputs(cfg, DEV, seed=T + 1), "auto", what="shared rows T=%d" % T)
 
 
-@pytest.mark.parametrize("path", ["direct", "sorted"])
-def test_experts_given_routing_with_padding_and_repeats(path):
+@pytest.mark.parametrize("T,path", [(7, "direct"), (7, "sorted"), (20, "direct"),
+                                    (20, "sorted"), (64, "direct")])
+def test_experts_given_routing_with_padding_and_repeats(T, path):
     """fused_moe_experts_fwd with -1 routes, repeated ids of one token, and NaN weights in every
     expert no route selects: a kernel that reads expert -1, an unselected expert or a skipped row
-    produces NaN and fails the check."""
-    cfg = replace(CONFIGS["tiny"], T=7, E=16, k=8, H=128, F=64)
+    produces NaN and fails the check.  T=7 takes the route-major direct path, T=20 and T=64 the
+    expert-major scan (160 and 512 routes)."""
+    cfg = replace(CONFIGS["tiny"], T=T, E=16, k=8, H=128, F=64)
     d = make_inputs(cfg, DEV, seed=11)
     ids = random_topk_ids(cfg.T, cfg.k, cfg.E, seed=3, pad_fraction=0.2, allow_repeats=True)
     ids[0, :] = -1                                # a token with no route at all

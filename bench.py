@@ -280,7 +280,8 @@ def kernel_source_hash():
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mixture_experts_forward_amd", "csrc")
-    for name in ("moe_ws_kernel.h", "moe_tiled_kernel.h", "moe_device.h", "moe_plan.cpp"):
+    for name in ("moe_ws_kernel.h", "moe_tiled_kernel.h", "moe_block_kernel.h", "moe_device.h",
+                 "moe_plan.cpp"):
         h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()[:16]
 

@@ -51,7 +51,7 @@ moe::GemmProblem gate_up_problem(const moe::Plan &pl, const Ctx &c)
         g.sorted_ids = ws_at<int32_t>(c.ws, pl.off_sorted);
         g.offsets = ws_at<int32_t>(c.ws, pl.off_offsets);
         g.tile_expert = ws_at<int32_t>(c.ws, pl.off_tile_expert);
-        g.num_groups = pl.gate_up.kind == moe::KERNEL_TILED ? pl.tiles_cap : pl.E;
+        g.num_groups = pl.gate_up.kind == moe::KERNEL_WS ? pl.E : pl.tiles_cap;
     } else {
         g.num_groups = pl.P <= 64 ? pl.P : pl.E;  // per route (direct) or per expert (scan)
     }
@@ -92,6 +92,8 @@ bool launch_gemm(bool gate_up, const moe::GemmProblem &g, moe::RowSource src,
 {
     if (t.kind == moe::KERNEL_TILED)
         return moe::launch_tiled(gate_up, g, src, ws_tile(t), stream);
+    if (t.kind == moe::KERNEL_BLOCK)
+        return moe::launch_block(gate_up, g, src, ws_tile(t), stream);
     return gate_up ? moe::launch_gate_up(g, src, ws_tile(t), stream)
                    : moe::launch_down(g, src, ws_tile(t), stream);
 }

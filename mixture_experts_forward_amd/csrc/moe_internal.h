@@ -49,6 +49,7 @@ struct GemmProblem {
 //   weight-streaming kernel: NT 16-column tiles per workgroup (per half for gate-up), MT 16-row
 //     tiles per pass, KSPLIT waves splitting the K loop;
 //   row-tiled kernel: NT 16-column tiles per wave (4 waves), 16*MT rows per tile (ksplit unused);
+//   block kernel: NT 16-row weight tiles per wave (2 x 2 waves), 128 rows per tile (MT = 8);
 //   both: STAGES register buffers (STAGES-1 k-steps of 64 in flight per wave).
 struct WsTile {
     int nt, mt, ksplit, stages;
@@ -59,6 +60,10 @@ bool launch_gate_up(const GemmProblem &g, RowSource src, WsTile tile, hipStream_
 bool launch_down(const GemmProblem &g, RowSource src, WsTile tile, hipStream_t stream);
 // Row-tiled kernel (ROWS_SORTED with block_m = 16*tile.mt, or ROWS_DENSE).
 bool launch_tiled(bool gate_up, const GemmProblem &g, RowSource src, WsTile tile,
+                  hipStream_t stream);
+// 128-row block kernel (ROWS_SORTED with block_m = 128, or ROWS_DENSE); tile.nt = TN 16-row
+// weight tiles per wave (2 x 2 waves), tile.stages register buffers.
+bool launch_block(bool gate_up, const GemmProblem &g, RowSource src, WsTile tile,
                   hipStream_t stream);
 
 // ---------------------------------------------------------------- combine

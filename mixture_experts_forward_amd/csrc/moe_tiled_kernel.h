@@ -128,8 +128,10 @@ __global__ __launch_bounds__(64 * kWaves) void k_tiled_gemm(GemmProblem g, int n
         xslot[i] = r * 8 + (lchunk ^ ((r >> 1) & 7));
     }
 
+    // K-loop start: the same for the row tiles of one column block (consecutive on one XCD,
+    // sharing its weight tile through L2), different across column blocks (HBM channels)
     const int nk = K / 64;
-    const int rot = (int)((nblk * 7u + mtile * 13u) % (unsigned)nk);
+    const int rot = (int)((nblk * 7u) % (unsigned)nk);
 
     moe_f32x4 acc[TM][NW];
 #pragma unroll
@@ -143,10 +145,8 @@ __global__ __launch_bounds__(64 * kWaves) void k_tiled_gemm(GemmProblem g, int n
         const int k = ((i + rot) % nk) * 64;
 #pragma unroll
         for (int nw = 0; nw < NW; ++nw) {
-            if (tile_ok[nw % NTW]) {
-                wraw[st][nw][0] = load_nt(wld[nw] + k);
-                wraw[st][nw][1] = load_nt(wld[nw] + (size_t)8 * K + k);
-            }
+            wraw[st][nw][0] = load_nt(wld[nw] + k);
+            wraw[st][nw][1] = load_nt(wld[nw] + (size_t)8 * K + k);
         }
 #pragma unroll
         for (int x = 0; x < XI; ++x)
@@ -159,10 +159,8 @@ __global__ __launch_bounds__(64 * kWaves) void k_tiled_gemm(GemmProblem g, int n
             xb[xslot[x]] = xraw[st][x];
 #pragma unroll
         for (int nw = 0; nw < NW; ++nw) {
-            if (tile_ok[nw % NTW]) {
-                tbuf[nw * 128 + wslot0] = wraw[st][nw][0];
-                tbuf[nw * 128 + wslot1] = wraw[st][nw][1];
-            }
+            tbuf[nw * 128 + wslot0] = wraw[st][nw][0];
+            tbuf[nw * 128 + wslot1] = wraw[st][nw][1];
         }
         __syncthreads();  // activation tile complete; also orders this wave's transpose buffer
         moe_u32x4 a[NW][2];
@@ -178,32 +176,34 @@ __global__ __launch_bounds__(64 * kWaves) void k_tiled_gemm(GemmProblem g, int n
             const moe_u32x4 b0 = xb[r * 8 + (rq ^ sw)];
             const moe_u32x4 b1 = xb[r * 8 + ((rq + 4) ^ sw)];
 #pragma unroll
-            for (int nw = 0; nw < NW; ++nw) {
-                if (tile_ok[nw % NTW]) {
-                    acc[mt][nw] = moe_mfma_16x16x32(a[nw][0], b0, acc[mt][nw]);
-                    acc[mt][nw] = moe_mfma_16x16x32(a[nw][1], b1, acc[mt][nw]);
-                }
-            }
+            for (int nw = 0; nw < NW; ++nw)
+                acc[mt][nw] = moe_mfma_16x16x32(a[nw][0], b0, acc[mt][nw]);
+#pragma unroll
+            for (int nw = 0; nw < NW; ++nw)
+                acc[mt][nw] = moe_mfma_16x16x32(a[nw][1], b1, acc[mt][nw]);
         }
         moe_wave_sync();  // this wave's transpose reads finish before its next writes
     };
 
+    // Software pipeline, STAGES-1 k-steps in flight.  The steady state is branch-free so that
+    // the compiler's wait counts stay exact: past the end, the prefetch wraps to an early
+    // k-step (in bounds, never consumed).  Weight tiles past the last column read row 0 of the
+    // expert (wld is clamped); they only feed columns that are never stored.
 #pragma unroll
     for (int st = 0; st < STAGES - 1; ++st)
-        if (st < nk)
-            load(st, st);
-    for (int i = 0; i < nk; i += STAGES) {
+        load(st, st);
+    int i = 0;
+    for (; i + STAGES <= nk; i += STAGES) {
 #pragma unroll
         for (int st = 0; st < STAGES; ++st) {
-            const int cur = i + st;
-            if (cur < nk) {
-                const int nxt = cur + STAGES - 1;
-                if (nxt < nk)
-                    load((st + STAGES - 1) % STAGES, nxt);
-                compute(st, cur);
-            }
+            load((st + STAGES - 1) % STAGES, i + st + STAGES - 1);
+            compute(st, i + st);
         }
     }
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st)
+        if (i + st < nk)
+            compute(st, i + st);
 
     // ---- epilogue: lane holds columns 4*(lane/16)+r of row mt*16 + lane%16
 #pragma unroll

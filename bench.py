@@ -232,7 +232,7 @@ def main():
         "rows_per_expert": loads[0],
         "staged_ms_per_step": round(staged_ms, 5),
         "stage_ms": {k: round(v, 5) for k, v in per_stage.items()},
-        "roofline": {"kernel": "gate_up (k_ws_gemm gate-up)", "bound": "hbm",
+        "roofline": {"kernel": "gate-up GEMM of the routed experts", "bound": "hbm",
                      "achieved": round(gu_gbs, 1), "peak": peak_gbs, "unit": "GB/s",
                      "frac": round(gu_gbs / peak_gbs, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": gu_bytes},
@@ -302,8 +302,8 @@ def _read_counters(d):
 
 def _is_dominant(name):
     """The gate-up GEMM of the routed experts (weight-streaming or row-tiled kernel)."""
-    return (("k_ws_gemm<true" in name or "k_tiled_gemm<true" in name)
-            and "<true, 2," not in name)
+    return (("k_ws_gemm<true" in name or "k_tiled_gemm<true" in name
+             or "k_block_gemm<true" in name) and "<true, 2," not in name)
 
 
 def _calibration_copy(disp):
@@ -341,7 +341,8 @@ def summarize_trace(args):
             short, r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
             float(r["MaxNs"]) / 1e3))
     lines += ["", "Template arguments: k_ws_gemm<GATE_UP, SRC, NT, MT, KSPLIT, STAGES> (SRC 0 "
-              "sorted, 1 direct, 2 dense); k_tiled_gemm<GATE_UP, SRC, BM, NTW, STAGES>."]
+              "sorted, 1 direct, 2 dense, 3 scan); k_tiled_gemm<GATE_UP, SRC, BM, NTW, STAGES>; "
+              "k_block_gemm<GATE_UP, SRC, TN, STAGES>."]
     out = os.path.join(PROFILE_DIR, "kernel_trace_%s.md" % cfg.name)
     os.makedirs(PROFILE_DIR, exist_ok=True)
     open(out, "w").write("\n".join(lines) + "\n")

@@ -9,17 +9,22 @@
 //     (or 4) MFMAs;
 //   - both operand tiles of a 64-element k-step (128 rows x 128 B activations, BW rows x 128 B
 //     weights) are loaded cooperatively, each wave instruction covering 8 rows x 128 B (whole
-//     lines; weights non-temporal), STAGES-1 k-steps ahead in registers, and written to a
-//     double-buffered, XOR-swizzled LDS tile -- one barrier per k-step;
+//     lines), STAGES-1 k-steps ahead in registers, and written to a double-buffered,
+//     XOR-swizzled LDS tile -- one barrier per k-step.  Weights use ordinary cached loads: the
+//     row tiles of one expert re-read them from L2 (non-temporal loads measured slower here);
 //   - for gate-up, a wave's weight rows are TN/2 gate tiles and the TN/2 up tiles of the same
 //     columns, so SiLU(gate)*up is applied in registers;
-//   - blocks are dealt round-robin to the 8 XCDs, so consecutive tile numbers on one XCD run
-//     together and share its L2; the row tiles of one column block are numbered consecutively
-//     and share its weight tile (numbering the column blocks of one row tile consecutively
-//     instead, to keep an activation tile in L2, measured slower on MI355X for both prefill
-//     experts and the dense shared expert).  Workgroups that share a weight tile start their
-//     K loop at the same k-step; different column blocks start at different k-steps, which
-//     spreads the concurrent requests over the HBM channels.
+//   - tiles are numbered so that workgroups sharing data are neighbours, and blocks are dealt
+//     round-robin to the 8 XCDs, each XCD taking a contiguous range of tile numbers per round
+//     (see k_block_gemm).  Sorted rows are numbered expert by expert -- column block by
+//     column block, the expert's row tiles within -- and all tiles of one expert start their K
+//     loop at the same k-step; dense rows number the row tiles of a column block
+//     consecutively, which start at the same k-step.  Different experts / column blocks start
+//     at different k-steps, spreading the requests over the HBM channels.
+//   - the same kernel runs on a plain grid (one tile per workgroup: sorted rows, where that
+//     measured faster) or a persistent one (one workgroup per resident slot, walking the
+//     tiles in rounds: dense rows, whose row tiles then run in step and share each weight
+//     k-slice through L2).
 #pragma once
 
 #include "moe_device.h"
@@ -33,15 +38,13 @@ constexpr int kWaves = 4;
 constexpr int kXcds = 8;
 constexpr int kBM = 128;
 
-__host__ __device__ inline int block_grid(int n_blocks, int m_tiles)
+// Grid of a launch: the resident workgroup slots (a multiple of 8), or fewer when the launch
+// has fewer tiles (total_cap: an upper bound of the tile count).
+inline int block_grid(int total_cap, int slots)
 {
-    const int b = n_blocks * m_tiles;
-    return (b + kXcds - 1) / kXcds * kXcds;
-}
-
-__device__ __forceinline__ moe_u32x4 load_nt(const uint16_t *p)
-{
-    return __builtin_nontemporal_load(reinterpret_cast<const moe_u32x4 *>(p));
+    const int cap = (total_cap + kXcds - 1) / kXcds * kXcds;
+    const int s = slots / kXcds * kXcds;
+    return cap < kXcds ? kXcds : (s < kXcds ? kXcds : (cap < s ? cap : s));
 }
 
 __device__ __forceinline__ moe_u32x4 load_cached(const uint16_t *p)
@@ -52,40 +55,53 @@ __device__ __forceinline__ moe_u32x4 load_cached(const uint16_t *p)
 // slot of 16-byte chunk c of row r in a swizzled 8-slot row
 __device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
 
+// Number of tiles of a launch: sorted rows -> the routing's row tiles (read from the layout)
+// x column blocks; dense rows -> m_tiles x column blocks.
+template <int SRC>
+__device__ __forceinline__ int block_total(const GemmProblem &g, int n_blocks, int m_tiles)
+{
+    if (SRC == moe::ROWS_SORTED)
+        return g.offsets[g.num_experts] / kBM * n_blocks;
+    return m_tiles * n_blocks;
+}
+
+// Tile number t -> (column block, row tile, expert).  Sorted rows: expert-major (an expert's
+// tiles are consecutive, column block by column block, its row tiles within); t / n_blocks
+// falls inside the expert's own row tiles, so tile_expert names it.  Dense rows: row tiles of
+// a column block consecutive.
+template <int SRC>
+__device__ __forceinline__ void block_decode(const GemmProblem &g, int t, int n_blocks,
+                                             int m_tiles, int &nblk, int &mtile, int &expert)
+{
+    if (SRC == moe::ROWS_SORTED) {
+        expert = g.tile_expert[t / n_blocks];
+        const int t0 = g.offsets[expert] / kBM;
+        const int te = g.offsets[expert + 1] / kBM - t0;
+        const int local = t - t0 * n_blocks;
+        nblk = local / te;
+        mtile = t0 + local % te;
+    } else {
+        nblk = t / m_tiles;
+        mtile = t % m_tiles;
+        expert = 0;
+    }
+}
+
+// One 128-row x BW-weight-row tile: K loop and epilogue.
 template <bool GATE_UP, int SRC, int TN, int STAGES>
-__global__ __launch_bounds__(64 * kWaves) void k_block_gemm(GemmProblem g, int n_blocks,
-                                                           int m_tiles)
+__device__ __forceinline__ void block_tile(const GemmProblem &g, int nblk, int mtile, int expert,
+                                           moe_u32x4 (*s_x)[kBM * 8],
+                                           moe_u32x4 (*s_w)[32 * TN * 8])
 {
     constexpr int BW = 32 * TN;        // weight rows per workgroup
     constexpr int XL = kBM / 32;       // activation loads per thread per k-step
     constexpr int WL = BW / 32;        // weight loads per thread per k-step
-    static_assert(!GATE_UP || TN % 2 == 0, "gate-up pairs gate and up tiles");
-    __shared__ moe_u32x4 s_x[2][kBM * 8];
-    __shared__ moe_u32x4 s_w[2][BW * 8];
-
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wv >> 1, wn = wv & 1;
-
-    // ---- tile of this workgroup (XCD-aware order)
-    const int per_xcd = block_grid(n_blocks, m_tiles) / kXcds;
-    const int logical = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-    if (logical >= n_blocks * m_tiles)
-        return;
-    const int nblk = logical / m_tiles;
-    const int mtile = logical % m_tiles;
     const int row0 = mtile * kBM;
-    int expert = 0, n_rows = kBM;
-    if (SRC == moe::ROWS_SORTED) {
-        expert = g.tile_expert[mtile];
-        if (expert < 0)
-            return;
-    } else {
-        n_rows = min(kBM, g.rows - row0);
-        if (n_rows <= 0)
-            return;
-    }
+    const int n_rows = SRC == moe::ROWS_SORTED ? kBM : min(kBM, g.rows - row0);
     const int K = g.K;
     // output columns of this workgroup: gate-up BW/2 (gate and up rows), down BW
     const int cols_per_wg = GATE_UP ? BW / 2 : BW;
@@ -138,10 +154,11 @@ __global__ __launch_bounds__(64 * kWaves) void k_block_gemm(GemmProblem g, int n
     }
     const int rr = lane & 15, rq = lane >> 4;
 
-    // K-loop start: the same for the row tiles of one column block (they then read each k-slice
-    // of the shared weight tile at about the same time), different across column blocks
+    // K-loop start: the same for workgroups that share tiles through L2 (they then read each
+    // k-slice at about the same time): per expert (sorted rows), else per column block
     const int nk = K / 64;
-    const int rot = (int)((nblk * 7u) % (unsigned)nk);
+    const unsigned rkey = SRC == moe::ROWS_SORTED ? expert : nblk;
+    const int rot = (int)((rkey * 7u) % (unsigned)nk);
 
     moe_f32x4 acc[4][TN];
 #pragma unroll
@@ -157,7 +174,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_block_gemm(GemmProblem g, int n
         const int k = ((i + rot) % nk) * 64;
 #pragma unroll
         for (int j = 0; j < WL; ++j)
-            wraw[st][j] = load_nt(wld[j] + k);
+            wraw[st][j] = load_cached(wld[j] + k);
 #pragma unroll
         for (int j = 0; j < XL; ++j)
             xraw[st][j] = load_cached(xld[j] + k);
@@ -251,6 +268,31 @@ __global__ __launch_bounds__(64 * kWaves) void k_block_gemm(GemmProblem g, int n
             packed.y = moe_pack_bf16x2(v[2], v[3]);
             *reinterpret_cast<moe_u32x2 *>(orow + col + 4 * rq) = packed;
         }
+    }
+}
+
+// Persistent grid (gridDim.x a multiple of 8): round r hands XCD x the tiles
+// [r*W + x*W/8, r*W + (x+1)*W/8), W = the slots in use.
+template <bool GATE_UP, int SRC, int TN, int STAGES>
+__global__ __launch_bounds__(64 * kWaves) void k_block_gemm(GemmProblem g, int n_blocks,
+                                                           int m_tiles)
+{
+    static_assert(!GATE_UP || TN % 2 == 0, "gate-up pairs gate and up tiles");
+    __shared__ moe_u32x4 s_x[2][kBM * 8];
+    __shared__ moe_u32x4 s_w[2][32 * TN * 8];
+
+    const int total = block_total<SRC>(g, n_blocks, m_tiles);
+    // fewer tiles than slots: spread them evenly over the XCDs
+    const int W = min((int)gridDim.x, (total + kXcds - 1) / kXcds * kXcds);
+    const int per = W / kXcds;
+    const int idx = blockIdx.x / kXcds;
+    if (idx >= per)
+        return;
+    for (int t = (blockIdx.x % kXcds) * per + idx; t < total; t += W) {
+        int nblk, mtile, expert;
+        block_decode<SRC>(g, t, n_blocks, m_tiles, nblk, mtile, expert);
+        block_tile<GATE_UP, SRC, TN, STAGES>(g, nblk, mtile, expert, s_x, s_w);
+        __syncthreads();  // the next tile's first LDS stores follow every wave's last reads
     }
 }
 

@@ -5,15 +5,42 @@ namespace {
 
 using moe::GemmProblem;
 
+// Workgroups of `kernel` resident on one CU (found once per instantiation).
+template <typename Kernel>
+int per_cu(Kernel kernel)
+{
+    static const int n = [&] {
+        int blocks = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, 64 * moe_block::kWaves,
+                                                         0) != hipSuccess || blocks < 1)
+            blocks = 1;
+        return blocks;
+    }();
+    return n;
+}
+
+int device_cus()
+{
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n < 1)
+        n = 256;
+    return n;
+}
+
 template <bool GATE_UP, int SRC, int TN, int STAGES>
 void launch_one(const GemmProblem &g, hipStream_t stream)
 {
+    const auto kernel = moe_block::k_block_gemm<GATE_UP, SRC, TN, STAGES>;
     const int cols = GATE_UP ? 16 * TN : 32 * TN;  // output columns per workgroup
     const int n_blocks = (g.n_out + cols - 1) / cols;
     const int m_tiles = g.num_groups;
-    hipLaunchKernelGGL((moe_block::k_block_gemm<GATE_UP, SRC, TN, STAGES>),
-                       dim3(moe_block::block_grid(n_blocks, m_tiles)),
-                       dim3(64 * moe_block::kWaves), 0, stream, g, n_blocks, m_tiles);
+    // sorted rows: one tile per workgroup; dense rows: one workgroup per resident slot
+    const int slots = SRC == moe::ROWS_DENSE ? per_cu(kernel) * device_cus() : (1 << 30);
+    const int grid = moe_block::block_grid(n_blocks * m_tiles, slots);
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * moe_block::kWaves), 0, stream, g, n_blocks,
+                       m_tiles);
 }
 
 // Instantiated shapes (TN 16-row weight tiles per wave, STAGES).

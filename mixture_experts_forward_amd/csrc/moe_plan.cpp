@@ -90,8 +90,8 @@ void make_plan(const moe_params_t *p, int32_t S, Plan *pl)
         pl->gate_up = {KERNEL_TILED, 1, 4, 1, 3};
         pl->down = {KERNEL_TILED, 2, 4, 1, 3};
     } else {
-        pl->gate_up = {KERNEL_BLOCK, 8, 8, 1, 2};
-        pl->down = {KERNEL_BLOCK, 8, 8, 1, 2};
+        pl->gate_up = {KERNEL_BLOCK, 4, 8, 1, 2};
+        pl->down = {KERNEL_BLOCK, 4, 8, 1, 2};
     }
     pl->shared_gate_up = {KERNEL_BLOCK, 4, 8, 1, 3};
     pl->shared_down = {KERNEL_BLOCK, 4, 8, 1, 3};

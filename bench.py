@@ -376,7 +376,8 @@ def summarize_pmc(args):
         res["kernels"] = names
     if len(runs) > 2:
         disp = runs[2]
-        busy = [v["SQ_VALU_MFMA_BUSY_CYCLES"] / (v["GRBM_GUI_ACTIVE"] * 1024.0)
+        # GRBM_GUI_ACTIVE is summed over the 8 XCDs; MFMA-busy cycles over the 1024 SIMDs
+        busy = [v["SQ_VALU_MFMA_BUSY_CYCLES"] / (v["GRBM_GUI_ACTIVE"] / 8.0 * 1024.0)
                 for n, v in disp.values() if _is_dominant(n) and "GRBM_GUI_ACTIVE" in v]
         if busy:
             lines.append("mfma_busy_pct: %.2f" % (100.0 * sum(busy) / len(busy)))

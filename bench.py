@@ -280,8 +280,8 @@ def kernel_source_hash():
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mixture_experts_forward_amd", "csrc")
-    for name in ("moe_ws_kernel.h", "moe_tiled_kernel.h", "moe_block_kernel.h", "moe_device.h",
-                 "moe_plan.cpp"):
+    for name in ("moe_ws_kernel.h", "moe_tiled_kernel.h", "moe_block_kernel.h",
+                 "moe_wide_kernel.h", "moe_device.h", "moe_plan.cpp"):
         h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()[:16]
 
@@ -303,7 +303,8 @@ def _read_counters(d):
 def _is_dominant(name):
     """The gate-up GEMM of the routed experts (weight-streaming or row-tiled kernel)."""
     return (("k_ws_gemm<true" in name or "k_tiled_gemm<true" in name
-             or "k_block_gemm<true" in name) and "<true, 2," not in name)
+             or "k_block_gemm<true" in name or "k_wide_gemm<true" in name)
+            and "<true, 2," not in name and "<true, 2>" not in name)
 
 
 def _calibration_copy(disp):
@@ -342,7 +343,7 @@ def summarize_trace(args):
             float(r["MaxNs"]) / 1e3))
     lines += ["", "Template arguments: k_ws_gemm<GATE_UP, SRC, NT, MT, KSPLIT, STAGES> (SRC 0 "
               "sorted, 1 direct, 2 dense, 3 scan); k_tiled_gemm<GATE_UP, SRC, BM, NTW, STAGES>; "
-              "k_block_gemm<GATE_UP, SRC, TN, STAGES>."]
+              "k_block_gemm<GATE_UP, SRC, TN, STAGES>; k_wide_gemm<GATE_UP, SRC>."]
     out = os.path.join(PROFILE_DIR, "kernel_trace_%s.md" % cfg.name)
     os.makedirs(PROFILE_DIR, exist_ok=True)
     open(out, "w").write("\n".join(lines) + "\n")

@@ -94,6 +94,8 @@ bool launch_gemm(bool gate_up, const moe::GemmProblem &g, moe::RowSource src,
         return moe::launch_tiled(gate_up, g, src, ws_tile(t), stream);
     if (t.kind == moe::KERNEL_BLOCK)
         return moe::launch_block(gate_up, g, src, ws_tile(t), stream);
+    if (t.kind == moe::KERNEL_WIDE)
+        return moe::launch_wide(gate_up, g, src, stream);
     return gate_up ? moe::launch_gate_up(g, src, ws_tile(t), stream)
                    : moe::launch_down(g, src, ws_tile(t), stream);
 }

@@ -1,0 +1,69 @@
+// moe_gemm_wide.hip -- launches of the 256 x 256 tile GEMM (moe_wide_kernel.h).
+#include "moe_wide_kernel.h"
+
+namespace {
+
+using moe::GemmProblem;
+
+// Workgroups of `kernel` resident on one CU (found once per instantiation).
+template <typename Kernel>
+int per_cu(Kernel kernel)
+{
+    static const int n = [&] {
+        int blocks = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, moe_wide::kThreads,
+                                                         0) != hipSuccess || blocks < 1)
+            blocks = 1;
+        return blocks;
+    }();
+    return n;
+}
+
+int device_cus()
+{
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n < 1)
+        n = 256;
+    return n;
+}
+
+template <bool GATE_UP, int SRC>
+void launch_one(const GemmProblem &g, hipStream_t stream)
+{
+    const auto kernel = moe_wide::k_wide_gemm<GATE_UP, SRC>;
+    const int cols = GATE_UP ? moe_wide::kBW / 2 : moe_wide::kBW;  // output columns per tile
+    const int n_blocks = (g.n_out + cols - 1) / cols;
+    const int m_tiles = g.num_groups;
+    // sorted rows: one tile per workgroup; dense rows: one workgroup per resident slot
+    const int slots = SRC == moe::ROWS_DENSE ? per_cu(kernel) * device_cus() : (1 << 30);
+    const int grid = moe_wide::wide_grid(n_blocks * m_tiles, slots);
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(moe_wide::kThreads), 0, stream, g, n_blocks,
+                       m_tiles);
+}
+
+}  // namespace
+
+namespace moe {
+
+bool launch_wide(bool gate_up, const GemmProblem &g, RowSource src, hipStream_t stream)
+{
+    if (src == ROWS_SORTED) {
+        if (gate_up)
+            launch_one<true, ROWS_SORTED>(g, stream);
+        else
+            launch_one<false, ROWS_SORTED>(g, stream);
+        return true;
+    }
+    if (src == ROWS_DENSE) {
+        if (gate_up)
+            launch_one<true, ROWS_DENSE>(g, stream);
+        else
+            launch_one<false, ROWS_DENSE>(g, stream);
+        return true;
+    }
+    return false;
+}
+
+}  // namespace moe

@@ -65,6 +65,8 @@ bool launch_tiled(bool gate_up, const GemmProblem &g, RowSource src, WsTile tile
 // weight tiles per wave (2 x 2 waves), tile.stages register buffers.
 bool launch_block(bool gate_up, const GemmProblem &g, RowSource src, WsTile tile,
                   hipStream_t stream);
+// 256 x 256 tile kernel (ROWS_SORTED with block_m = 256, or ROWS_DENSE with 256-row tiles).
+bool launch_wide(bool gate_up, const GemmProblem &g, RowSource src, hipStream_t stream);
 
 // ---------------------------------------------------------------- combine
 // out[t] = bf16( sum_j w[t,j] * y[t*k+j] (+ ys[t]) ), routes with ids outside [0,E) skipped.

@@ -78,8 +78,9 @@ void make_plan(const moe_params_t *p, int32_t S, Plan *pl)
     // BF16-activation PR picks its route tiles); shapes measured on MI355X.  Few rows per
     // expert (decode): the weight-streaming kernel, one 16-column tile per wave for gate-up,
     // two for down, K split over four waves, 16-row passes.  Tens of rows (batch): the
-    // row-tiled kernel, activation tile shared through LDS, 64-row tiles.  Hundreds (prefill)
-    // and the dense shared expert: the 128-row block kernel, both operands through LDS.
+    // row-tiled kernel, activation tile shared through LDS, 64-row tiles.  Hundreds (prefill):
+    // the 256 x 256 tile kernel, both operands loaded straight into LDS.  The dense shared
+    // expert: the 128-row block kernel.
     if (pl->path == MOE_PATH_DIRECT) {
         pl->gate_up = {KERNEL_WS, 1, 1, 4, 3};
         pl->down = {KERNEL_WS, 2, 1, P <= 64 ? 4 : 2, P <= 64 ? 2 : 3};
@@ -90,8 +91,8 @@ void make_plan(const moe_params_t *p, int32_t S, Plan *pl)
         pl->gate_up = {KERNEL_TILED, 1, 4, 1, 3};
         pl->down = {KERNEL_TILED, 2, 4, 1, 3};
     } else {
-        pl->gate_up = {KERNEL_BLOCK, 4, 8, 1, 2};
-        pl->down = {KERNEL_BLOCK, 4, 8, 1, 2};
+        pl->gate_up = {KERNEL_WIDE, 0, 16, 1, 2};
+        pl->down = {KERNEL_WIDE, 0, 16, 1, 2};
     }
     pl->shared_gate_up = {KERNEL_BLOCK, 4, 8, 1, 3};
     pl->shared_down = {KERNEL_BLOCK, 4, 8, 1, 3};

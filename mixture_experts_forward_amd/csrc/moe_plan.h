@@ -15,7 +15,7 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxGroups = 64;
 constexpr int kSortedBlockM = 16;  // row tile of the weight-streaming GEMMs
 
-enum KernelKind { KERNEL_WS = 0, KERNEL_TILED = 1, KERNEL_BLOCK = 2 };
+enum KernelKind { KERNEL_WS = 0, KERNEL_TILED = 1, KERNEL_BLOCK = 2, KERNEL_WIDE = 3 };
 
 struct TileChoice {
     int kind;  // KernelKind

@@ -1,0 +1,327 @@
+// moe_wide_kernel.h -- 256 x 256 tile GEMM of the MoE experts for prefill (hundreds of routed
+// rows per expert) and the dense shared expert.
+//
+// Same math as moe_ws_kernel.h (gate-up with the SiLU(gate)*up epilogue, or down).  Built so
+// that each weight byte and each activation byte fetched from beyond L2 feeds as many MFMAs as
+// one CU can hold:
+//   - a workgroup of 8 waves owns a 256-row tile and 256 weight rows (gate-up: 128 gate rows and
+//     the 128 up rows of the same columns); waves form a 4 x 2 grid, wave (wm, wn) computing the
+//     16-row tiles wm, wm+4, wm+8, wm+12 of the row tile against weight rows
+//     [128*wn, 128*wn + 128) -- 4 x 8 accumulators of v_mfma_f32_16x16x32_bf16;
+//   - both operand tiles of a 64-element k-step (256 rows x 128 B each, 64 KB) go from global
+//     memory straight into LDS with global_load_lds_dwordx4 -- each wave instruction covers
+//     8 whole 128-byte rows and no register holds them -- into the slot order
+//     slot(r, c) = 8r + (c ^ ((r >> 1) & 7)) that the MFMA operand reads take without bank
+//     conflicts: lane l of an instruction writes slot 8*(l/8) + l%8 of its 8 rows, so it
+//     fetches chunk (l%8) ^ swizzle(row) of its row;
+//   - two LDS stages (128 KB): the next k-step is in flight while the current one is
+//     multiplied; one barrier per k-step;
+//   - padding rows of an expert's segment form a suffix, so the 16-row tiles that hold only
+//     padding are known from their first row: their loads and MFMAs are skipped, and the
+//     interleaved row-tile assignment spreads the real rows evenly over the four SIMDs.  MFMA
+//     work thus follows the routed rows, not the 256-row padding;
+//   - tiles are numbered expert by expert (sorted rows) or row tiles of a column block
+//     consecutively (dense rows) and blocks are dealt round-robin to the 8 XCDs, each XCD
+//     taking a contiguous range of tile numbers; tiles sharing a weight or activation tile
+//     start their K loop at the same k-step, others at different ones (HBM channels).
+// A lane ends with four consecutive output columns of one row.
+#pragma once
+
+#include <type_traits>
+
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe_wide {
+
+using moe::GemmProblem;
+
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kXcds = 8;
+constexpr int kBM = 256;                       // rows per tile
+constexpr int kBW = 256;                       // weight rows per tile
+constexpr int kWM = 4, kWN = 2;                // wave grid
+constexpr int kMT = kBM / 16 / kWM;            // 16-row tiles per wave (4)
+constexpr int kNT = kBW / 16 / kWN;            // 16-row weight tiles per wave (8)
+constexpr int kXLoads = kBM / 8 / kWaves;      // activation DMA instructions per wave (4)
+constexpr int kWLoads = kBW / 8 / kWaves;      // weight DMA instructions per wave (4)
+constexpr int kStageSlots = (kBM + kBW) * 8;   // 16-byte slots per stage (64 KB)
+
+// Grid of a launch: resident slots (a multiple of 8), or fewer when there are fewer tiles
+// (total_cap: an upper bound of the tile count).
+inline int wide_grid(int total_cap, int slots)
+{
+    const int cap = (total_cap + kXcds - 1) / kXcds * kXcds;
+    const int s = slots / kXcds * kXcds;
+    return cap < kXcds ? kXcds : (s < kXcds ? kXcds : (cap < s ? cap : s));
+}
+
+// 16 bytes from global address g into LDS byte address lds_base + 16 * lane (the whole wave
+// writes 1 KB).  Issued as inline assembly so that the compiler's wait-count pass does not
+// drain it before every LDS read; the kernel waits for it explicitly (vmcnt) before the
+// barrier that publishes the stage.
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(g), "s"(lds_base)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ void wait_all_loads()
+{
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+__device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
+
+template <int SRC>
+__device__ __forceinline__ int wide_total(const GemmProblem &g, int n_blocks, int m_tiles)
+{
+    if (SRC == moe::ROWS_SORTED)
+        return g.offsets[g.num_experts] / kBM * n_blocks;
+    return m_tiles * n_blocks;
+}
+
+// Tile number t -> (column block, row tile, expert); see moe_block_kernel.h's block_decode.
+template <int SRC>
+__device__ __forceinline__ void wide_decode(const GemmProblem &g, int t, int n_blocks,
+                                            int m_tiles, int &nblk, int &mtile, int &expert)
+{
+    if (SRC == moe::ROWS_SORTED) {
+        expert = g.tile_expert[t / n_blocks];
+        const int t0 = g.offsets[expert] / kBM;
+        const int te = g.offsets[expert + 1] / kBM - t0;
+        const int local = t - t0 * n_blocks;
+        nblk = local / te;
+        mtile = t0 + local % te;
+    } else {
+        nblk = t / m_tiles;
+        mtile = t % m_tiles;
+        expert = 0;
+    }
+}
+
+// Number of leading real rows of the tile: sorted rows -> padding is a suffix of the expert's
+// segment (found by a binary search of the first -1); dense rows -> min(256, rows - row0).
+template <int SRC>
+__device__ __forceinline__ int wide_real_rows(const GemmProblem &g, int row0)
+{
+    if (SRC != moe::ROWS_SORTED)
+        return min(kBM, g.rows - row0);
+    int lo = 0, hi = kBM;  // sorted_ids[row0 + r] >= 0 exactly for r < answer
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (g.sorted_ids[row0 + mid] >= 0)
+            lo = mid + 1;
+        else
+            hi = mid;
+    }
+    return lo;
+}
+
+template <bool GATE_UP, int SRC>
+__device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mtile, int expert,
+                                          moe_u32x4 *smem)
+{
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wv / kWN, wn = wv % kWN;
+    const int row0 = mtile * kBM;
+    const int K = g.K;
+    const int n_real = __builtin_amdgcn_readfirstlane(wide_real_rows<SRC>(g, row0));
+
+    // output columns of this workgroup: gate-up kBW/2 (gate and up rows), down kBW
+    const int cols_per_wg = GATE_UP ? kBW / 2 : kBW;
+    const int col_wg = nblk * cols_per_wg;
+
+    // ---- DMA sources.  Instruction j of this wave covers tile rows wv*32 + 8j .. +7; lane l
+    // fetches chunk (l%8) ^ swizzle(row) of row wv*32 + 8j + l/8.
+    const int lrow = lane >> 3, lpos = lane & 7;
+    const int w_rows = GATE_UP ? 2 * g.n_out : g.n_out;
+    const uint16_t *W = g.weight + (size_t)expert * w_rows * K;
+    const uint16_t *wsrc[kWLoads];
+#pragma unroll
+    for (int j = 0; j < kWLoads; ++j) {
+        const int r = wv * (kBW / kWaves) + 8 * j + lrow;  // weight row within the tile
+        // gate-up: rows [0, kBW/2) are gate rows of the workgroup's columns, [kBW/2, kBW) the
+        // up rows of the same columns; rows past the last column read row 0 (never stored)
+        const int c = col_wg + (GATE_UP ? r % (kBW / 2) : r);
+        const bool ok = c < g.n_out;
+        const int src = (GATE_UP && r >= kBW / 2) ? c + g.n_out : c;
+        const int chunk = lpos ^ ((r >> 1) & 7);
+        wsrc[j] = W + (size_t)(ok ? src : 0) * K + 8 * chunk;
+    }
+    const uint16_t *xsrc[kXLoads];
+    bool xload[kXLoads];  // wave-uniform: the instruction's 8 rows hold a real row
+#pragma unroll
+    for (int j = 0; j < kXLoads; ++j) {
+        const int rfirst = wv * (kBM / kWaves) + 8 * j;
+        const int r = rfirst + lrow;
+        xload[j] = rfirst < n_real;
+        int src = 0;
+        if (r < n_real)
+            src = SRC == moe::ROWS_SORTED
+                      ? (GATE_UP ? g.sorted_ids[row0 + r] / g.top_k : row0 + r)
+                      : row0 + r;
+        const int chunk = lpos ^ ((r >> 1) & 7);
+        xsrc[j] = g.act + (size_t)src * K + 8 * chunk;
+    }
+    // LDS byte addresses of the two stages: activation rows first, then weight rows
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+    const uint32_t x_dst = lds0 + wv * (kBM / kWaves) * 128;
+    const uint32_t w_dst = lds0 + kBM * 128 + wv * (kBW / kWaves) * 128;
+    constexpr uint32_t kStageBytes = kStageSlots * 16;
+
+    // ---- operand rows of this wave
+    // weight tile n of wave wn: gate-up: n < kNT/2 -> gate rows 16*(kNT/2)*wn + 16*n of the gate
+    // half; n >= kNT/2 -> the matching up rows.  down: rows 16*kNT*wn + 16*n.
+    int wrow0[kNT];
+#pragma unroll
+    for (int n = 0; n < kNT; ++n) {
+        if (GATE_UP) {
+            const int hn = n % (kNT / 2);
+            const int base = 16 * (kNT / 2) * wn + 16 * hn;
+            wrow0[n] = (n < kNT / 2) ? base : kBW / 2 + base;
+        } else {
+            wrow0[n] = 16 * kNT * wn + 16 * n;
+        }
+    }
+    const int rr = lane & 15, rq = lane >> 4;
+    // real 16-row tiles of this wave: tiles wm + 4i for i < mt_real (wave-uniform)
+    int mt_real = 0;
+#pragma unroll
+    for (int i = 0; i < kMT; ++i)
+        mt_real += (16 * (wm + kWM * i) < n_real) ? 1 : 0;
+
+    const int nk = K / 64;
+    const unsigned rkey = SRC == moe::ROWS_SORTED ? expert : nblk;
+    const int rot = (int)((rkey * 7u) % (unsigned)nk);
+
+    moe_f32x4 acc[kMT][kNT];
+#pragma unroll
+    for (int m = 0; m < kMT; ++m)
+#pragma unroll
+        for (int n = 0; n < kNT; ++n)
+            acc[m][n] = moe_f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto issue = [&](int stage, int i) {
+        const int kb = ((i + rot) % nk) * 64;  // element offset of the k-step
+        const uint32_t so = stage * kStageBytes;
+#pragma unroll
+        for (int j = 0; j < kXLoads; ++j)
+            if (xload[j])
+                dma16(xsrc[j] + kb, x_dst + so + j * 1024);
+#pragma unroll
+        for (int j = 0; j < kWLoads; ++j)
+            dma16(wsrc[j] + kb, w_dst + so + j * 1024);
+    };
+
+    // Pipeline: stage i % 2 holds k-step i.  At the top of step i this wave's loads of k-step i
+    // are the only ones outstanding (vmcnt 0); the barrier then publishes every wave's part of
+    // the stage and also guarantees that every wave has finished reading stage (i+1) % 2 in
+    // step i-1, so k-step i+1 can be loaded into it while k-step i is multiplied.  The loop is
+    // instantiated per count MTR of real 16-row tiles of this wave, so the MFMA block has no
+    // branches (a wave with none still loads its share and meets every barrier).
+    auto k_loop = [&](auto mtr) {
+        constexpr int MTR = decltype(mtr)::value;
+        issue(0, 0);
+        for (int i = 0; i < nk; ++i) {
+            wait_all_loads();
+            __syncthreads();
+            if (i + 1 < nk)
+                issue((i + 1) & 1, i + 1);
+            if (MTR == 0)
+                continue;
+            const moe_u32x4 *xb = smem + (i & 1) * kStageSlots;
+            const moe_u32x4 *wb = xb + kBM * 8;
+            moe_u32x4 b[MTR > 0 ? MTR : 1][2];
+#pragma unroll
+            for (int m = 0; m < MTR; ++m) {
+                const int r = 16 * (wm + kWM * m) + rr;
+                b[m][0] = xb[swz(r, rq)];
+                b[m][1] = xb[swz(r, rq + 4)];
+            }
+#pragma unroll
+            for (int n = 0; n < kNT; ++n) {
+                const int r = wrow0[n] + rr;
+                const moe_u32x4 a0 = wb[swz(r, rq)];
+                const moe_u32x4 a1 = wb[swz(r, rq + 4)];
+#pragma unroll
+                for (int m = 0; m < MTR; ++m)
+                    acc[m][n] = moe_mfma_16x16x32(a0, b[m][0], acc[m][n]);
+#pragma unroll
+                for (int m = 0; m < MTR; ++m)
+                    acc[m][n] = moe_mfma_16x16x32(a1, b[m][1], acc[m][n]);
+            }
+        }
+    };
+    switch (mt_real) {
+    case 0: k_loop(std::integral_constant<int, 0>()); break;
+    case 1: k_loop(std::integral_constant<int, 1>()); break;
+    case 2: k_loop(std::integral_constant<int, 2>()); break;
+    case 3: k_loop(std::integral_constant<int, 3>()); break;
+    default: k_loop(std::integral_constant<int, 4>()); break;
+    }
+
+    // ---- epilogue: lane holds columns 4*(lane/16)+q of row 16*(wm + 4m) + lane%16
+#pragma unroll
+    for (int m = 0; m < kMT; ++m) {
+        if (m >= mt_real)
+            continue;
+        const int r = 16 * (wm + kWM * m) + rr;
+        if (r >= n_real)
+            continue;
+        const int dst = SRC == moe::ROWS_SORTED
+                            ? (GATE_UP ? row0 + r : g.sorted_ids[row0 + r])
+                            : row0 + r;
+        uint16_t *orow = g.out + (size_t)dst * g.n_out;
+        constexpr int NOUT = GATE_UP ? kNT / 2 : kNT;
+#pragma unroll
+        for (int n = 0; n < NOUT; ++n) {
+            const int col = GATE_UP ? col_wg + 16 * (kNT / 2) * wn + 16 * n
+                                    : col_wg + 16 * kNT * wn + 16 * n;
+            if (col >= g.n_out)
+                continue;
+            float v[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (GATE_UP) {
+                    const float gate = acc[m][n][q];
+                    const float up = acc[m][n + kNT / 2][q];
+                    v[q] = gate / (1.0f + __expf(-gate)) * up;
+                } else {
+                    v[q] = acc[m][n][q];
+                }
+            }
+            moe_u32x2 packed;
+            packed.x = moe_pack_bf16x2(v[0], v[1]);
+            packed.y = moe_pack_bf16x2(v[2], v[3]);
+            *reinterpret_cast<moe_u32x2 *>(orow + col + 4 * rq) = packed;
+        }
+    }
+}
+
+// Round r hands XCD x the tiles [r*W + x*W/8, r*W + (x+1)*W/8), W = the slots in use.
+template <bool GATE_UP, int SRC>
+__global__ __launch_bounds__(kThreads) void k_wide_gemm(GemmProblem g, int n_blocks, int m_tiles)
+{
+    __shared__ moe_u32x4 smem[2 * kStageSlots];
+
+    const int total = wide_total<SRC>(g, n_blocks, m_tiles);
+    const int W = min((int)gridDim.x, (total + kXcds - 1) / kXcds * kXcds);
+    const int per = W / kXcds;
+    const int idx = blockIdx.x / kXcds;
+    if (idx >= per)
+        return;
+    for (int t = (blockIdx.x % kXcds) * per + idx; t < total; t += W) {
+        int nblk, mtile, expert;
+        wide_decode<SRC>(g, t, n_blocks, m_tiles, nblk, mtile, expert);
+        wide_tile<GATE_UP, SRC>(g, nblk, mtile, expert, smem);
+        __syncthreads();  // the next tile's first loads follow every wave's last reads
+    }
+}
+
+}  // namespace moe_wide

@@ -5,22 +5,29 @@
 // inverse map of its MoEPostPermuteFwd (inverse_indices [T*K]): every expert's routes in
 // increasing route index r = t*k + j, each expert's segment padded up to block_m rows.
 //
-// One workgroup of 1024 threads (16 waves) does the whole job in LDS:
-//   1. histogram with LDS integer atomics (order-independent, so deterministic);
-//   2. block-wide exclusive scan of the padded counts -> expert_offsets, tile_expert, n_tiles,
-//      and the -1 fill of padding slots;
-//   3. rounds of 1024 routes: a route's row = its expert's running base + the count of the same
-//      expert in earlier waves of the round (per-wave histograms packed as two 16-bit counters
-//      per word) + its rank among earlier lanes of its own wave (LDS broadcast compare).
+// Rounds of 1024 routes (one workgroup of 16 waves) do the stable scatter: a route's row = its
+// expert's running base + the count of the same expert in earlier waves of the round (per-wave
+// histograms packed as two 16-bit counters per word) + its rank among earlier lanes of its own
+// wave (LDS broadcast compare).  Two drivers:
+//   - one workgroup for everything (the public moe_align_sort, and up to 1024 routes): LDS
+//     histogram with integer atomics (order-independent, so deterministic), block-wide scan of
+//     the padded counts (expert_offsets, tile_expert, n_tiles, the -1 fill of padding slots),
+//     then the rounds in order;
+//   - three launches over chunks of 1024 routes when a caller provides a count table of
+//     chunks x E ints (the fused pass): per-chunk histograms, one workgroup that turns them
+//     into every chunk's starting row per expert and lays out the padded segments, then all
+//     chunks' rounds at once.
 // Every slot of sorted_route_ids and tile_expert is written exactly once.
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "moe_plan.h"
 
 namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxExperts = 1024;
+static_assert(kThreads == moe::kAlignChunk, "a chunk of the chunked align is one workgroup");
 
 struct AlignSmem {
     int count[kMaxExperts];
@@ -42,35 +49,18 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane)
     return v;
 }
 
-// The whole align/sort by one 1024-thread workgroup.
-__device__ __forceinline__ void align_block(const int32_t *__restrict__ ids, int P, int E, int bm,
-                                            int slots, int tiles_cap,
+// Padded exclusive scan of sm.count[0..E) (thread e owns expert e): writes expert_offsets,
+// tile_expert, n_tiles and the -1 padding of sorted_ids; leaves each expert's first row in
+// sm.base.
+__device__ __forceinline__ void scan_layout(int E, int bm, int slots, int tiles_cap,
                                             int32_t *__restrict__ sorted_ids,
                                             int32_t *__restrict__ offsets,
                                             int32_t *__restrict__ tile_expert,
-                                            int32_t *__restrict__ inverse,
                                             int32_t *__restrict__ n_tiles, AlignSmem &sm)
 {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = tid >> 6;
-    const int half_words = (E + 1) / 2;
-
-    if (tid < E)
-        sm.count[tid] = 0;
-    for (int x = tid; x < kWaves * half_words; x += kThreads)
-        sm.hist[x / half_words][x % half_words] = 0;
-    __syncthreads();
-
-    // 1. histogram
-    for (int r = tid; r < P; r += kThreads) {
-        const int e = ids[r];
-        if (e >= 0 && e < E)
-            atomicAdd(&sm.count[e], 1);
-    }
-    __syncthreads();
-
-    // 2. exclusive scan of the padded counts (thread e owns expert e)
     const int c = (tid < E) ? sm.count[tid] : 0;
     const int padded = (c + bm - 1) / bm * bm;
     int incl = wave_inclusive_scan(padded, lane);
@@ -101,52 +91,156 @@ __device__ __forceinline__ void align_block(const int32_t *__restrict__ ids, int
         sorted_ids[s] = -1;
     for (int i = total / bm + tid; i < tiles_cap; i += kThreads)
         tile_expert[i] = -1;
+}
 
-    // 3. stable scatter, 1024 routes per round
-    for (int r0 = 0; r0 < P; r0 += kThreads) {
-        const int r = r0 + tid;
-        int e = (r < P) ? ids[r] : -1;
-        const bool valid = (e >= 0 && e < E);
-        if (!valid)
-            e = -1;
-        sm.round_ids[tid] = e;
-        __syncthreads();
-        int rank = 0;
-        if (valid) {
-            const int4 *w4 = reinterpret_cast<const int4 *>(&sm.round_ids[wv * 64]);
+// Stable scatter of routes [r0, r0 + 1024): route r of expert e goes to row sm.base[e] + (its
+// rank among this round's routes of e).  With advance, sm.base moves past the round's routes.
+// sm.hist must be zero on entry and is zero again on return.
+__device__ __forceinline__ void scatter_round(const int32_t *__restrict__ ids, int P, int E,
+                                              int r0, bool advance,
+                                              int32_t *__restrict__ sorted_ids,
+                                              int32_t *__restrict__ inverse, AlignSmem &sm)
+{
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = tid >> 6;
+    const int half_words = (E + 1) / 2;
+    const int r = r0 + tid;
+    int e = (r < P) ? ids[r] : -1;
+    const bool valid = (e >= 0 && e < E);
+    if (!valid)
+        e = -1;
+    sm.round_ids[tid] = e;
+    __syncthreads();
+    int rank = 0;
+    if (valid) {
+        const int4 *w4 = reinterpret_cast<const int4 *>(&sm.round_ids[wv * 64]);
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const int4 v = w4[q];
-                rank += (4 * q + 0 < lane && v.x == e);
-                rank += (4 * q + 1 < lane && v.y == e);
-                rank += (4 * q + 2 < lane && v.z == e);
-                rank += (4 * q + 3 < lane && v.w == e);
-            }
-            atomicAdd(&sm.hist[wv][e >> 1], 1u << ((e & 1) * 16));
+        for (int q = 0; q < 16; ++q) {
+            const int4 v = w4[q];
+            rank += (4 * q + 0 < lane && v.x == e);
+            rank += (4 * q + 1 < lane && v.y == e);
+            rank += (4 * q + 2 < lane && v.z == e);
+            rank += (4 * q + 3 < lane && v.w == e);
         }
-        __syncthreads();
-        if (valid) {
-            int before = 0;
-            for (int w = 0; w < wv; ++w)
-                before += (sm.hist[w][e >> 1] >> ((e & 1) * 16)) & 0xffff;
-            const int pos = sm.base[e] + before + rank;
-            sorted_ids[pos] = r;
-            inverse[r] = pos;
-        } else if (r < P) {
-            inverse[r] = -1;
-        }
-        __syncthreads();
-        if (tid < E) {
-            int sum = 0;
-            for (int w = 0; w < kWaves; ++w)
-                sum += (sm.hist[w][tid >> 1] >> ((tid & 1) * 16)) & 0xffff;
-            sm.base[tid] += sum;
-        }
-        __syncthreads();
-        for (int x = tid; x < kWaves * half_words; x += kThreads)
-            sm.hist[x / half_words][x % half_words] = 0;
-        // the next round's first barrier orders this clear before its atomics
+        atomicAdd(&sm.hist[wv][e >> 1], 1u << ((e & 1) * 16));
     }
+    __syncthreads();
+    if (valid) {
+        int before = 0;
+        for (int w = 0; w < wv; ++w)
+            before += (sm.hist[w][e >> 1] >> ((e & 1) * 16)) & 0xffff;
+        const int pos = sm.base[e] + before + rank;
+        sorted_ids[pos] = r;
+        inverse[r] = pos;
+    } else if (r < P) {
+        inverse[r] = -1;
+    }
+    __syncthreads();
+    if (advance && tid < E) {
+        int sum = 0;
+        for (int w = 0; w < kWaves; ++w)
+            sum += (sm.hist[w][tid >> 1] >> ((tid & 1) * 16)) & 0xffff;
+        sm.base[tid] += sum;
+    }
+    __syncthreads();
+    for (int x = tid; x < kWaves * half_words; x += kThreads)
+        sm.hist[x / half_words][x % half_words] = 0;
+    // the next round's first barrier orders this clear before its atomics
+}
+
+// The whole align/sort by one 1024-thread workgroup.
+__device__ __forceinline__ void align_block(const int32_t *__restrict__ ids, int P, int E, int bm,
+                                            int slots, int tiles_cap,
+                                            int32_t *__restrict__ sorted_ids,
+                                            int32_t *__restrict__ offsets,
+                                            int32_t *__restrict__ tile_expert,
+                                            int32_t *__restrict__ inverse,
+                                            int32_t *__restrict__ n_tiles, AlignSmem &sm)
+{
+    const int tid = threadIdx.x;
+    const int half_words = (E + 1) / 2;
+    if (tid < E)
+        sm.count[tid] = 0;
+    for (int x = tid; x < kWaves * half_words; x += kThreads)
+        sm.hist[x / half_words][x % half_words] = 0;
+    __syncthreads();
+    for (int r = tid; r < P; r += kThreads) {
+        const int e = ids[r];
+        if (e >= 0 && e < E)
+            atomicAdd(&sm.count[e], 1);
+    }
+    __syncthreads();
+    scan_layout(E, bm, slots, tiles_cap, sorted_ids, offsets, tile_expert, n_tiles, sm);
+    for (int r0 = 0; r0 < P; r0 += kThreads)
+        scatter_round(ids, P, E, r0, true, sorted_ids, inverse, sm);
+}
+
+// Chunked driver, launch 1: histogram of chunk b (routes [1024b, 1024b + 1024)) into
+// counts[b*E + e].
+__global__ __launch_bounds__(kThreads) void k_align_hist(const int32_t *__restrict__ ids, int P,
+                                                         int E, int32_t *__restrict__ counts)
+{
+    __shared__ int cnt[kMaxExperts];
+    const int tid = threadIdx.x;
+    if (tid < E)
+        cnt[tid] = 0;
+    __syncthreads();
+    const int r = blockIdx.x * kThreads + tid;
+    if (r < P) {
+        const int e = ids[r];
+        if (e >= 0 && e < E)
+            atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();
+    if (tid < E)
+        counts[blockIdx.x * E + tid] = cnt[tid];
+}
+
+// Chunked driver, launch 2 (one workgroup): totals, padded layout, and counts[b*E + e] turned
+// into the first row of chunk b's routes of expert e.
+__global__ __launch_bounds__(kThreads) void k_align_scan(int32_t *__restrict__ counts,
+                                                         int chunks, int E, int bm, int slots,
+                                                         int tiles_cap,
+                                                         int32_t *__restrict__ sorted_ids,
+                                                         int32_t *__restrict__ offsets,
+                                                         int32_t *__restrict__ tile_expert,
+                                                         int32_t *__restrict__ n_tiles)
+{
+    __shared__ AlignSmem sm;
+    const int tid = threadIdx.x;
+    if (tid < E) {
+        int run = 0;
+        for (int b = 0; b < chunks; ++b) {
+            const int c = counts[b * E + tid];
+            counts[b * E + tid] = run;
+            run += c;
+        }
+        sm.count[tid] = run;
+    }
+    __syncthreads();
+    scan_layout(E, bm, slots, tiles_cap, sorted_ids, offsets, tile_expert, n_tiles, sm);
+    if (tid < E)
+        for (int b = 0; b < chunks; ++b)
+            counts[b * E + tid] += sm.base[tid];
+}
+
+// Chunked driver, launch 3: the round of chunk b from its starting rows.
+__global__ __launch_bounds__(kThreads) void k_align_scatter(const int32_t *__restrict__ ids,
+                                                            int P, int E,
+                                                            const int32_t *__restrict__ counts,
+                                                            int32_t *__restrict__ sorted_ids,
+                                                            int32_t *__restrict__ inverse)
+{
+    __shared__ AlignSmem sm;
+    const int tid = threadIdx.x;
+    const int half_words = (E + 1) / 2;
+    if (tid < E)
+        sm.base[tid] = counts[blockIdx.x * E + tid];
+    for (int x = tid; x < kWaves * half_words; x += kThreads)
+        sm.hist[x / half_words][x % half_words] = 0;
+    __syncthreads();
+    scatter_round(ids, P, E, blockIdx.x * kThreads, false, sorted_ids, inverse, sm);
 }
 
 __global__ __launch_bounds__(kThreads) void k_align_sort(
@@ -166,12 +260,22 @@ namespace moe {
 
 void launch_align_sort(const int32_t *ids, int P, int E, int block_m, int32_t *sorted_ids,
                        int32_t *offsets, int32_t *tile_expert, int32_t *inverse, int32_t *n_tiles,
-                       hipStream_t stream)
+                       int32_t *scratch, hipStream_t stream)
 {
     const int slots = P + E * (block_m - 1);
     const int tiles_cap = P / block_m + E;
-    hipLaunchKernelGGL(k_align_sort, dim3(1), dim3(kThreads), 0, stream, ids, P, E, block_m,
-                       slots, tiles_cap, sorted_ids, offsets, tile_expert, inverse, n_tiles);
+    if (scratch == nullptr || P <= kThreads) {
+        hipLaunchKernelGGL(k_align_sort, dim3(1), dim3(kThreads), 0, stream, ids, P, E, block_m,
+                           slots, tiles_cap, sorted_ids, offsets, tile_expert, inverse, n_tiles);
+        return;
+    }
+    const int chunks = (P + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(k_align_hist, dim3(chunks), dim3(kThreads), 0, stream, ids, P, E,
+                       scratch);
+    hipLaunchKernelGGL(k_align_scan, dim3(1), dim3(kThreads), 0, stream, scratch, chunks, E,
+                       block_m, slots, tiles_cap, sorted_ids, offsets, tile_expert, n_tiles);
+    hipLaunchKernelGGL(k_align_scatter, dim3(chunks), dim3(kThreads), 0, stream, ids, P, E,
+                       scratch, sorted_ids, inverse);
 }
 
 }  // namespace moe

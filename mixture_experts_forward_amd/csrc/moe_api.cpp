@@ -113,7 +113,9 @@ int run_stage(int stage, const moe::Plan &pl, const Ctx &c)
                                    ws_at<int32_t>(c.ws, pl.off_offsets),
                                    ws_at<int32_t>(c.ws, pl.off_tile_expert),
                                    ws_at<int32_t>(c.ws, pl.off_inverse),
-                                   ws_at<int32_t>(c.ws, pl.off_n_tiles), c.stream);
+                                   ws_at<int32_t>(c.ws, pl.off_n_tiles),
+                                   pl.off_align ? ws_at<int32_t>(c.ws, pl.off_align) : nullptr,
+                                   c.stream);
         break;
     case MOE_STAGE_GATE_UP:
         if (!launch_gemm(true, gate_up_problem(pl, c), src, pl.gate_up, c.stream))
@@ -270,7 +272,8 @@ int moe_align_sort(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E, int
     if (((int64_t)T * k + (int64_t)E * (block_m - 1)) >= (1ll << 31))
         return MOE_ERR_UNSUPPORTED;
     moe::launch_align_sort(topk_ids, T * k, E, block_m, sorted_route_ids, expert_offsets,
-                           tile_expert, inverse_pos, n_tiles, static_cast<hipStream_t>(stream));
+                           tile_expert, inverse_pos, n_tiles, nullptr,
+                           static_cast<hipStream_t>(stream));
     return launch_status();
 }
 

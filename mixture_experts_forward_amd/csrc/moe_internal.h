@@ -13,9 +13,11 @@ void launch_route(const float *gating, const float *bias, int T, int E, int k, i
                   float *weights, hipStream_t stream);
 
 // ---------------------------------------------------------------- align / sort
+// scratch: NULL (one workgroup does everything) or align_scratch_ints(P, E) ints of device
+// memory (moe_plan.h) for the chunked three-launch form (used when P > 1024).
 void launch_align_sort(const int32_t *ids, int P, int E, int block_m, int32_t *sorted_ids,
                        int32_t *offsets, int32_t *tile_expert, int32_t *inverse, int32_t *n_tiles,
-                       hipStream_t stream);
+                       int32_t *scratch, hipStream_t stream);
 
 // ---------------------------------------------------------------- expert GEMMs
 // Where a GEMM takes its rows from.

@@ -80,7 +80,8 @@ void make_plan(const moe_params_t *p, int32_t S, Plan *pl)
     // two for down, K split over four waves, 16-row passes.  Tens of rows (batch): the
     // row-tiled kernel, activation tile shared through LDS, 64-row tiles.  Hundreds (prefill):
     // the 256 x 256 tile kernel, both operands loaded straight into LDS.  The dense shared
-    // expert: the 128-row block kernel.
+    // expert: the 256 x 256 tile kernel for gate-up, the 128-row block kernel for down (whose
+    // few, long-K tiles fill the GPU better at 128 x 128).
     if (pl->path == MOE_PATH_DIRECT) {
         pl->gate_up = {KERNEL_WS, 1, 1, 4, 3};
         pl->down = {KERNEL_WS, 2, 1, P <= 64 ? 4 : 2, P <= 64 ? 2 : 3};
@@ -94,7 +95,7 @@ void make_plan(const moe_params_t *p, int32_t S, Plan *pl)
         pl->gate_up = {KERNEL_WIDE, 0, 16, 1, 2};
         pl->down = {KERNEL_WIDE, 0, 16, 1, 2};
     }
-    pl->shared_gate_up = {KERNEL_BLOCK, 4, 8, 1, 3};
+    pl->shared_gate_up = {KERNEL_WIDE, 0, 16, 1, 2};
     pl->shared_down = {KERNEL_BLOCK, 4, 8, 1, 3};
     pl->block_m = pl->gate_up.kind == KERNEL_WS ? kSortedBlockM : 16 * pl->gate_up.mt;
     pl->slots = P + pl->E * (pl->block_m - 1);
@@ -114,10 +115,12 @@ void make_plan(const moe_params_t *p, int32_t S, Plan *pl)
         pl->off_tile_expert = take((size_t)pl->tiles_cap * 4);
         pl->off_inverse = take((size_t)P * 4);
         pl->off_n_tiles = take(4);
+        const size_t scratch = align_scratch_ints(P, pl->E);
+        pl->off_align = scratch ? take(scratch * 4) : 0;
         pl->off_h = take((size_t)pl->slots * pl->F * 2);
     } else {
         pl->off_sorted = pl->off_offsets = pl->off_tile_expert = pl->off_inverse = 0;
-        pl->off_n_tiles = 0;
+        pl->off_n_tiles = pl->off_align = 0;
         pl->off_h = take((size_t)P * pl->F * 2);
     }
     pl->off_y = take((size_t)P * pl->H * 2);

@@ -14,6 +14,14 @@ constexpr int kMaxTopK = 32;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxGroups = 64;
 constexpr int kSortedBlockM = 16;  // row tile of the weight-streaming GEMMs
+constexpr int kAlignChunk = 1024;   // routes per chunk of the chunked align/sort
+
+// Ints of device scratch the chunked align/sort needs for P routes and E experts (0: P fits one
+// workgroup, which needs none).
+inline size_t align_scratch_ints(int P, int E)
+{
+    return P > kAlignChunk ? (size_t)((P + kAlignChunk - 1) / kAlignChunk) * E : 0;
+}
 
 enum KernelKind { KERNEL_WS = 0, KERNEL_TILED = 1, KERNEL_BLOCK = 2, KERNEL_WIDE = 3 };
 
@@ -31,7 +39,7 @@ struct Plan {
     TileChoice gate_up, down, shared_gate_up, shared_down;
     // byte offsets into the workspace
     size_t off_ids, off_weights, off_sorted, off_offsets, off_tile_expert, off_inverse,
-        off_n_tiles, off_h, off_y, off_hs, off_ys;
+        off_n_tiles, off_align, off_h, off_y, off_hs, off_ys;
     size_t total;
 };
 

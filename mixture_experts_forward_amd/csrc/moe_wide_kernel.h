@@ -13,9 +13,14 @@
 //     8 whole 128-byte rows and no register holds them -- into the slot order
 //     slot(r, c) = 8r + (c ^ ((r >> 1) & 7)) that the MFMA operand reads take without bank
 //     conflicts: lane l of an instruction writes slot 8*(l/8) + l%8 of its 8 rows, so it
-//     fetches chunk (l%8) ^ swizzle(row) of its row;
-//   - two LDS stages (128 KB): the next k-step is in flight while the current one is
-//     multiplied; one barrier per k-step;
+//     fetches chunk (l%8) ^ swizzle(row) of its row (for 32-element k-steps: 4 slots per row,
+//     swizzle (r >> 1) & 3);
+//   - STAGES LDS stages of a KSTEP-element k-step; the launches use KSTEP = 64 with two
+//     stages (128 KB): the next k-step is in flight while the current one is multiplied, one
+//     barrier per k-step.  (32-element k-steps with three to five stages, more bytes in flight
+//     but twice the barriers, and register-staged loads instead of LDS DMA, all measured no
+//     faster on MI355X: the loads of one CU are bound by how many line requests it keeps in
+//     flight, not by the pipeline depth);
 //   - padding rows of an expert's segment form a suffix, so the 16-row tiles that hold only
 //     padding are known from their first row: their loads and MFMAs are skipped, and the
 //     interleaved row-tile assignment spreads the real rows evenly over the four SIMDs.  MFMA
@@ -44,9 +49,23 @@ constexpr int kBW = 256;                       // weight rows per tile
 constexpr int kWM = 4, kWN = 2;                // wave grid
 constexpr int kMT = kBM / 16 / kWM;            // 16-row tiles per wave (4)
 constexpr int kNT = kBW / 16 / kWN;            // 16-row weight tiles per wave (8)
-constexpr int kXLoads = kBM / 8 / kWaves;      // activation DMA instructions per wave (4)
-constexpr int kWLoads = kBW / 8 / kWaves;      // weight DMA instructions per wave (4)
-constexpr int kStageSlots = (kBM + kBW) * 8;   // 16-byte slots per stage (64 KB)
+
+// LDS shape of one pipeline stage holding a KSTEP-element k-step of both operands: rows of
+// KSTEP/8 16-byte slots, activation rows first.
+template <int KSTEP>
+struct Stage {
+    static constexpr int kSlots = KSTEP / 8;                    // 16-byte slots per row
+    static constexpr int kRowsPerLoad = 64 / kSlots;            // rows per wave DMA instruction
+    static constexpr int kXLoads = kBM / kWaves / kRowsPerLoad; // per wave
+    static constexpr int kWLoads = kBW / kWaves / kRowsPerLoad;
+    static constexpr int kBytes = (kBM + kBW) * KSTEP * 2;
+    // slot of chunk c of row r: XOR-swizzled so that the MFMA operand reads (16 rows x one
+    // chunk per 16 lanes) hit distinct banks
+    static __device__ __forceinline__ int slot(int r, int c)
+    {
+        return r * kSlots + (c ^ ((r >> 1) & (kSlots - 1)));
+    }
+};
 
 // Grid of a launch: resident slots (a multiple of 8), or fewer when there are fewer tiles
 // (total_cap: an upper bound of the tile count).
@@ -69,12 +88,33 @@ __device__ __forceinline__ void dma16(const void *g, uint32_t lds_base)
                  : "memory", "m0");
 }
 
-__device__ __forceinline__ void wait_all_loads()
+// Wait until at most n of this wave's vector-memory loads are outstanding (0 <= n <= 63).
+__device__ __forceinline__ void wait_loads(int n)
 {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#define MOE_WAIT_CASE(N)                                                                         \
+    case N:                                                                                      \
+        asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory");                                  \
+        break;
+    switch (n) {
+        MOE_WAIT_CASE(1) MOE_WAIT_CASE(2) MOE_WAIT_CASE(3) MOE_WAIT_CASE(4) MOE_WAIT_CASE(5)
+        MOE_WAIT_CASE(6) MOE_WAIT_CASE(7) MOE_WAIT_CASE(8) MOE_WAIT_CASE(9) MOE_WAIT_CASE(10)
+        MOE_WAIT_CASE(11) MOE_WAIT_CASE(12) MOE_WAIT_CASE(13) MOE_WAIT_CASE(14) MOE_WAIT_CASE(15)
+        MOE_WAIT_CASE(16) MOE_WAIT_CASE(17) MOE_WAIT_CASE(18) MOE_WAIT_CASE(19) MOE_WAIT_CASE(20)
+        MOE_WAIT_CASE(21) MOE_WAIT_CASE(22) MOE_WAIT_CASE(23) MOE_WAIT_CASE(24) MOE_WAIT_CASE(25)
+        MOE_WAIT_CASE(26) MOE_WAIT_CASE(27) MOE_WAIT_CASE(28) MOE_WAIT_CASE(29) MOE_WAIT_CASE(30)
+        MOE_WAIT_CASE(31) MOE_WAIT_CASE(32) MOE_WAIT_CASE(33) MOE_WAIT_CASE(34) MOE_WAIT_CASE(35)
+        MOE_WAIT_CASE(36) MOE_WAIT_CASE(37) MOE_WAIT_CASE(38) MOE_WAIT_CASE(39) MOE_WAIT_CASE(40)
+        MOE_WAIT_CASE(41) MOE_WAIT_CASE(42) MOE_WAIT_CASE(43) MOE_WAIT_CASE(44) MOE_WAIT_CASE(45)
+        MOE_WAIT_CASE(46) MOE_WAIT_CASE(47) MOE_WAIT_CASE(48) MOE_WAIT_CASE(49) MOE_WAIT_CASE(50)
+        MOE_WAIT_CASE(51) MOE_WAIT_CASE(52) MOE_WAIT_CASE(53) MOE_WAIT_CASE(54) MOE_WAIT_CASE(55)
+        MOE_WAIT_CASE(56) MOE_WAIT_CASE(57) MOE_WAIT_CASE(58) MOE_WAIT_CASE(59) MOE_WAIT_CASE(60)
+        MOE_WAIT_CASE(61) MOE_WAIT_CASE(62) MOE_WAIT_CASE(63)
+    default:
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        break;
+    }
+#undef MOE_WAIT_CASE
 }
-
-__device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
 
 template <int SRC>
 __device__ __forceinline__ int wide_total(const GemmProblem &g, int n_blocks, int m_tiles)
@@ -121,10 +161,13 @@ __device__ __forceinline__ int wide_real_rows(const GemmProblem &g, int row0)
     return lo;
 }
 
-template <bool GATE_UP, int SRC>
+template <bool GATE_UP, int SRC, int KSTEP, int STAGES>
 __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mtile, int expert,
                                           moe_u32x4 *smem)
 {
+    using St = Stage<KSTEP>;
+    constexpr int kSlots = St::kSlots, kRows = St::kRowsPerLoad;
+    constexpr int kXLoads = St::kXLoads, kWLoads = St::kWLoads;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -137,43 +180,46 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
     const int cols_per_wg = GATE_UP ? kBW / 2 : kBW;
     const int col_wg = nblk * cols_per_wg;
 
-    // ---- DMA sources.  Instruction j of this wave covers tile rows wv*32 + 8j .. +7; lane l
-    // fetches chunk (l%8) ^ swizzle(row) of row wv*32 + 8j + l/8.
-    const int lrow = lane >> 3, lpos = lane & 7;
+    // ---- DMA sources.  Instruction j of this wave covers kRows consecutive tile rows; lane l
+    // fetches chunk (l % kSlots) ^ swizzle(row) of row first + l / kSlots, which is the slot
+    // that lane writes (a wave instruction fills 1 KB of LDS, lane l at 16 * l).
+    const int lrow = lane / kSlots, lpos = lane % kSlots;
     const int w_rows = GATE_UP ? 2 * g.n_out : g.n_out;
     const uint16_t *W = g.weight + (size_t)expert * w_rows * K;
     const uint16_t *wsrc[kWLoads];
 #pragma unroll
     for (int j = 0; j < kWLoads; ++j) {
-        const int r = wv * (kBW / kWaves) + 8 * j + lrow;  // weight row within the tile
+        const int r = wv * (kBW / kWaves) + kRows * j + lrow;  // weight row within the tile
         // gate-up: rows [0, kBW/2) are gate rows of the workgroup's columns, [kBW/2, kBW) the
         // up rows of the same columns; rows past the last column read row 0 (never stored)
         const int c = col_wg + (GATE_UP ? r % (kBW / 2) : r);
         const bool ok = c < g.n_out;
         const int src = (GATE_UP && r >= kBW / 2) ? c + g.n_out : c;
-        const int chunk = lpos ^ ((r >> 1) & 7);
+        const int chunk = lpos ^ ((r >> 1) & (kSlots - 1));
         wsrc[j] = W + (size_t)(ok ? src : 0) * K + 8 * chunk;
     }
     const uint16_t *xsrc[kXLoads];
-    bool xload[kXLoads];  // wave-uniform: the instruction's 8 rows hold a real row
+    bool xload[kXLoads];  // wave-uniform: the instruction's rows hold a real row
+    int n_loads = kWLoads;
 #pragma unroll
     for (int j = 0; j < kXLoads; ++j) {
-        const int rfirst = wv * (kBM / kWaves) + 8 * j;
+        const int rfirst = wv * (kBM / kWaves) + kRows * j;
         const int r = rfirst + lrow;
         xload[j] = rfirst < n_real;
-        int src = 0;
+        n_loads += xload[j] ? 1 : 0;
+        int src = 0;  // padding rows of a loaded group read row 0 (never stored)
         if (r < n_real)
             src = SRC == moe::ROWS_SORTED
                       ? (GATE_UP ? g.sorted_ids[row0 + r] / g.top_k : row0 + r)
                       : row0 + r;
-        const int chunk = lpos ^ ((r >> 1) & 7);
+        const int chunk = lpos ^ ((r >> 1) & (kSlots - 1));
         xsrc[j] = g.act + (size_t)src * K + 8 * chunk;
     }
-    // LDS byte addresses of the two stages: activation rows first, then weight rows
+    // LDS byte addresses within a stage: activation rows first, then weight rows
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-    const uint32_t x_dst = lds0 + wv * (kBM / kWaves) * 128;
-    const uint32_t w_dst = lds0 + kBM * 128 + wv * (kBW / kWaves) * 128;
-    constexpr uint32_t kStageBytes = kStageSlots * 16;
+    const uint32_t x_dst = lds0 + wv * (kBM / kWaves) * (KSTEP * 2);
+    const uint32_t w_dst = lds0 + kBM * (KSTEP * 2) + wv * (kBW / kWaves) * (KSTEP * 2);
+    constexpr uint32_t kStageBytes = St::kBytes;
 
     // ---- operand rows of this wave
     // weight tile n of wave wn: gate-up: n < kNT/2 -> gate rows 16*(kNT/2)*wn + 16*n of the gate
@@ -196,7 +242,7 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
     for (int i = 0; i < kMT; ++i)
         mt_real += (16 * (wm + kWM * i) < n_real) ? 1 : 0;
 
-    const int nk = K / 64;
+    const int nk = K / KSTEP;
     const unsigned rkey = SRC == moe::ROWS_SORTED ? expert : nblk;
     const int rot = (int)((rkey * 7u) % (unsigned)nk);
 
@@ -208,7 +254,7 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
             acc[m][n] = moe_f32x4{0.f, 0.f, 0.f, 0.f};
 
     auto issue = [&](int stage, int i) {
-        const int kb = ((i + rot) % nk) * 64;  // element offset of the k-step
+        const int kb = ((i + rot) % nk) * KSTEP;  // element offset of the k-step
         const uint32_t so = stage * kStageBytes;
 #pragma unroll
         for (int j = 0; j < kXLoads; ++j)
@@ -219,42 +265,41 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
             dma16(wsrc[j] + kb, w_dst + so + j * 1024);
     };
 
-    // Pipeline: stage i % 2 holds k-step i.  At the top of step i this wave's loads of k-step i
-    // are the only ones outstanding (vmcnt 0); the barrier then publishes every wave's part of
-    // the stage and also guarantees that every wave has finished reading stage (i+1) % 2 in
-    // step i-1, so k-step i+1 can be loaded into it while k-step i is multiplied.  The loop is
+    // Pipeline: stage i % STAGES holds k-step i; k-steps i .. i+STAGES-2 are in flight at the
+    // top of step i.  Waiting until only the later ones (n_loads each) are outstanding leaves
+    // this wave's part of k-step i in LDS; the barrier then publishes every wave's part and
+    // also guarantees that every wave has finished reading stage (i-1) % STAGES in step i-1,
+    // so k-step i+STAGES-1 can be loaded into it while k-step i is multiplied.  The loop is
     // instantiated per count MTR of real 16-row tiles of this wave, so the MFMA block has no
     // branches (a wave with none still loads its share and meets every barrier).
     auto k_loop = [&](auto mtr) {
         constexpr int MTR = decltype(mtr)::value;
-        issue(0, 0);
+#pragma unroll
+        for (int s = 0; s < STAGES - 1; ++s)
+            if (s < nk)
+                issue(s, s);
         for (int i = 0; i < nk; ++i) {
-            wait_all_loads();
+            wait_loads(min(STAGES - 2, nk - 1 - i) * n_loads);
             __syncthreads();
-            if (i + 1 < nk)
-                issue((i + 1) & 1, i + 1);
+            if (i + STAGES - 1 < nk)
+                issue((i + STAGES - 1) % STAGES, i + STAGES - 1);
             if (MTR == 0)
                 continue;
-            const moe_u32x4 *xb = smem + (i & 1) * kStageSlots;
-            const moe_u32x4 *wb = xb + kBM * 8;
-            moe_u32x4 b[MTR > 0 ? MTR : 1][2];
+            const moe_u32x4 *xb = smem + (i % STAGES) * (kStageBytes / 16);
+            const moe_u32x4 *wb = xb + kBM * kSlots;
 #pragma unroll
-            for (int m = 0; m < MTR; ++m) {
-                const int r = 16 * (wm + kWM * m) + rr;
-                b[m][0] = xb[swz(r, rq)];
-                b[m][1] = xb[swz(r, rq + 4)];
-            }
-#pragma unroll
-            for (int n = 0; n < kNT; ++n) {
-                const int r = wrow0[n] + rr;
-                const moe_u32x4 a0 = wb[swz(r, rq)];
-                const moe_u32x4 a1 = wb[swz(r, rq + 4)];
+            for (int h = 0; h < KSTEP / 32; ++h) {
+                moe_u32x4 b[MTR > 0 ? MTR : 1];
 #pragma unroll
                 for (int m = 0; m < MTR; ++m)
-                    acc[m][n] = moe_mfma_16x16x32(a0, b[m][0], acc[m][n]);
+                    b[m] = xb[St::slot(16 * (wm + kWM * m) + rr, rq + 4 * h)];
 #pragma unroll
-                for (int m = 0; m < MTR; ++m)
-                    acc[m][n] = moe_mfma_16x16x32(a1, b[m][1], acc[m][n]);
+                for (int n = 0; n < kNT; ++n) {
+                    const moe_u32x4 a = wb[St::slot(wrow0[n] + rr, rq + 4 * h)];
+#pragma unroll
+                    for (int m = 0; m < MTR; ++m)
+                        acc[m][n] = moe_mfma_16x16x32(a, b[m], acc[m][n]);
+                }
             }
         }
     };
@@ -305,10 +350,10 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
 }
 
 // Round r hands XCD x the tiles [r*W + x*W/8, r*W + (x+1)*W/8), W = the slots in use.
-template <bool GATE_UP, int SRC>
+template <bool GATE_UP, int SRC, int KSTEP, int STAGES>
 __global__ __launch_bounds__(kThreads) void k_wide_gemm(GemmProblem g, int n_blocks, int m_tiles)
 {
-    __shared__ moe_u32x4 smem[2 * kStageSlots];
+    __shared__ moe_u32x4 smem[STAGES * Stage<KSTEP>::kBytes / 16];
 
     const int total = wide_total<SRC>(g, n_blocks, m_tiles);
     const int W = min((int)gridDim.x, (total + kXcds - 1) / kXcds * kXcds);
@@ -319,7 +364,7 @@ __global__ __launch_bounds__(kThreads) void k_wide_gemm(GemmProblem g, int n_blo
     for (int t = (blockIdx.x % kXcds) * per + idx; t < total; t += W) {
         int nblk, mtile, expert;
         wide_decode<SRC>(g, t, n_blocks, m_tiles, nblk, mtile, expert);
-        wide_tile<GATE_UP, SRC>(g, nblk, mtile, expert, smem);
+        wide_tile<GATE_UP, SRC, KSTEP, STAGES>(g, nblk, mtile, expert, smem);
         __syncthreads();  // the next tile's first loads follow every wave's last reads
     }
 }

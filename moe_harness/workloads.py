@@ -128,13 +128,20 @@ def make_inputs(cfg: MoEConfig, device="cpu", seed: int = 42, weights: bool = Tr
 
 
 def random_topk_ids(T: int, k: int, E: int, seed: int = 42, device="cpu",
-                    pad_fraction: float = 0.0, allow_repeats: bool = False) -> torch.Tensor:
+                    pad_fraction: float = 0.0, allow_repeats: bool = False,
+                    skew: float = 0.0) -> torch.Tensor:
     """Seeded synthetic topk_ids [T,k] int32 for the routing-given entry points: k distinct
     experts per token (or independent draws with ``allow_repeats``), a fraction of entries
-    replaced by -1 padding routes."""
+    replaced by -1 padding routes.  ``skew`` > 0 draws the k distinct experts with probability
+    proportional to (1 + popularity rank)^-skew, the ranks a seeded permutation of the experts
+    (a few hot experts and a long tail, as real routers produce)."""
     g = _gen("cpu", seed, 9)
     if allow_repeats:
         ids = torch.randint(0, E, (T, k), generator=g, dtype=torch.int64)
+    elif skew > 0.0:
+        probs = torch.empty(E, dtype=torch.float64)
+        probs[torch.randperm(E, generator=g)] = (1.0 + torch.arange(E, dtype=torch.float64)) ** -skew
+        ids = torch.multinomial(probs.expand(T, E), k, replacement=False, generator=g)
     else:
         ids = torch.argsort(torch.rand((T, E), generator=g), dim=1)[:, :k]
     if pad_fraction > 0.0:

@@ -115,12 +115,14 @@ def test_shared_expert_rows(T):
 
 
 @pytest.mark.parametrize("T,path", [(7, "direct"), (7, "sorted"), (20, "direct"),
-                                    (20, "sorted"), (64, "direct")])
+                                    (20, "sorted"), (64, "direct"), (200, "sorted"),
+                                    (600, "sorted")])
 def test_experts_given_routing_with_padding_and_repeats(T, path):
     """fused_moe_experts_fwd with -1 routes, repeated ids of one token, and NaN weights in every
     expert no route selects: a kernel that reads expert -1, an unselected expert or a skipped row
     produces NaN and fails the check.  T=7 takes the route-major direct path, T=20 and T=64 the
-    expert-major scan (160 and 512 routes)."""
+    expert-major scan (160 and 512 routes); T=200 and T=600 (1600 and 4800 routes, ~100 and
+    ~300 rows per expert) the chunked align and the 256-row tile GEMM."""
     cfg = replace(CONFIGS["tiny"], T=T, E=16, k=8, H=128, F=64)
     d = make_inputs(cfg, DEV, seed=11)
     ids = random_topk_ids(cfg.T, cfg.k, cfg.E, seed=3, pad_fraction=0.2, allow_repeats=True)
@@ -145,6 +147,28 @@ def test_experts_given_routing_with_padding_and_repeats(T, path):
                             to_u16(d["w_down"]), ids.cpu().numpy(), w.cpu().numpy())
     assert_output_close(out, ref, "padding/repeats " + path)
     assert torch.all(out[0] == 0)
+
+
+@pytest.mark.parametrize("T,E,k,H,F,skew", [
+    (700, 16, 4, 128, 128, 1.5),   # ~1000 rows on the hottest expert: four 256-row tiles
+    (64, 32, 8, 256, 64, 2.0),     # 512 routes, ~16 per expert on average: 64-row tiles
+    (150, 128, 4, 128, 64, 1.2),   # 600 routes, ~5 per expert: weight-streaming, chunked align
+])
+def test_skewed_routing_sorted(T, E, k, H, F, skew):
+    """Zipf-like routing (a few hot experts, a long tail of cold or unused ones) through the
+    sorted path, every token compared with the oracle."""
+    cfg = replace(CONFIGS["tiny"], T=T, E=E, k=k, H=H, F=F)
+    d = make_inputs(cfg, DEV, seed=T + E)
+    ids = random_topk_ids(T, k, E, seed=5, skew=skew).to(DEV)
+    w = random_topk_weights(T, k, seed=5).to(DEV)
+    out = moe.fused_moe_experts_fwd(d["hidden_states"], d["w_gate_up"], d["w_down"], ids, w,
+                                    path="sorted")
+    torch.cuda.synchronize()
+    _, ref = oracle.experts(to_u16(d["hidden_states"]), to_u16(d["w_gate_up"]),
+                            to_u16(d["w_down"]), ids.cpu().numpy(), w.cpu().numpy())
+    rel = assert_output_close(out, ref, "skewed T=%d E=%d" % (T, E))
+    print("skewed T=%d E=%d: max expert load %d, rel-L2 %.2e" % (
+        T, E, int(torch.bincount(ids.flatten().long().cpu()).max()), rel), flush=True)
 
 
 def test_empty_tokens_is_a_no_op():

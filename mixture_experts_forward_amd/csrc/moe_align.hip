@@ -15,7 +15,7 @@
 //     then the rounds in order;
 //   - three launches over chunks of 1024 routes when a caller provides a count table of
 //     chunks x E ints (the fused pass): per-chunk histograms, one workgroup that turns them
-//     into every chunk's starting row per expert and lays out the padded segments, then all
+//     into per-chunk prefix counts per expert and lays out the padded segments, then all
 //     chunks' rounds at once.
 // Every slot of sorted_route_ids and tile_expert is written exactly once.
 #include "moe_device.h"
@@ -51,7 +51,7 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane)
 
 // Padded exclusive scan of sm.count[0..E) (thread e owns expert e): writes expert_offsets,
 // tile_expert, n_tiles and the -1 padding of sorted_ids; leaves each expert's first row in
-// sm.base.
+// sm.base (sm.count unchanged).
 __device__ __forceinline__ void scan_layout(int E, int bm, int slots, int tiles_cap,
                                             int32_t *__restrict__ sorted_ids,
                                             int32_t *__restrict__ offsets,
@@ -75,10 +75,6 @@ __device__ __forceinline__ void scan_layout(int E, int bm, int slots, int tiles_
     if (tid < E) {
         offsets[tid] = excl;
         sm.base[tid] = excl;
-        for (int s = excl + c; s < excl + padded; ++s)
-            sorted_ids[s] = -1;
-        for (int i = excl / bm; i < (excl + padded) / bm; ++i)
-            tile_expert[i] = tid;
     }
     if (tid == E - 1) {
         offsets[E] = incl;
@@ -86,6 +82,15 @@ __device__ __forceinline__ void scan_layout(int E, int bm, int slots, int tiles_
         sm.total = incl;
     }
     __syncthreads();
+    // padding rows and tile table of expert e, by wave e % 16 (lanes share the slots)
+    for (int e = wv; e < E; e += kWaves) {
+        const int b = sm.base[e], ce = sm.count[e];
+        const int pe = (ce + bm - 1) / bm * bm;
+        for (int s = b + ce + lane; s < b + pe; s += 64)
+            sorted_ids[s] = -1;
+        for (int i = b / bm + lane; i < (b + pe) / bm; i += 64)
+            tile_expert[i] = e;
+    }
     const int total = sm.total;
     for (int s = total + tid; s < slots; s += kThreads)
         sorted_ids[s] = -1;
@@ -197,8 +202,9 @@ __global__ __launch_bounds__(kThreads) void k_align_hist(const int32_t *__restri
         counts[blockIdx.x * E + tid] = cnt[tid];
 }
 
-// Chunked driver, launch 2 (one workgroup): totals, padded layout, and counts[b*E + e] turned
-// into the first row of chunk b's routes of expert e.
+// Chunked driver, launch 2 (one workgroup): per-expert totals and the padded layout;
+// counts[b*E + e] becomes the number of expert e's routes in chunks before b.  The counts are
+// read 16 chunks at a time so that their loads overlap.
 __global__ __launch_bounds__(kThreads) void k_align_scan(int32_t *__restrict__ counts,
                                                          int chunks, int E, int bm, int slots,
                                                          int tiles_cap,
@@ -207,28 +213,35 @@ __global__ __launch_bounds__(kThreads) void k_align_scan(int32_t *__restrict__ c
                                                          int32_t *__restrict__ tile_expert,
                                                          int32_t *__restrict__ n_tiles)
 {
+    constexpr int kBatch = 16;
     __shared__ AlignSmem sm;
     const int tid = threadIdx.x;
     if (tid < E) {
         int run = 0;
-        for (int b = 0; b < chunks; ++b) {
-            const int c = counts[b * E + tid];
-            counts[b * E + tid] = run;
-            run += c;
+        for (int b0 = 0; b0 < chunks; b0 += kBatch) {
+            int c[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u)
+                c[u] = (b0 + u < chunks) ? counts[(b0 + u) * E + tid] : 0;
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                if (b0 + u < chunks)
+                    counts[(b0 + u) * E + tid] = run;
+                run += c[u];
+            }
         }
         sm.count[tid] = run;
     }
     __syncthreads();
     scan_layout(E, bm, slots, tiles_cap, sorted_ids, offsets, tile_expert, n_tiles, sm);
-    if (tid < E)
-        for (int b = 0; b < chunks; ++b)
-            counts[b * E + tid] += sm.base[tid];
 }
 
-// Chunked driver, launch 3: the round of chunk b from its starting rows.
+// Chunked driver, launch 3: the round of chunk b, its routes of expert e starting at row
+// expert_offsets[e] + (routes of e in earlier chunks).
 __global__ __launch_bounds__(kThreads) void k_align_scatter(const int32_t *__restrict__ ids,
                                                             int P, int E,
                                                             const int32_t *__restrict__ counts,
+                                                            const int32_t *__restrict__ offsets,
                                                             int32_t *__restrict__ sorted_ids,
                                                             int32_t *__restrict__ inverse)
 {
@@ -236,7 +249,7 @@ __global__ __launch_bounds__(kThreads) void k_align_scatter(const int32_t *__res
     const int tid = threadIdx.x;
     const int half_words = (E + 1) / 2;
     if (tid < E)
-        sm.base[tid] = counts[blockIdx.x * E + tid];
+        sm.base[tid] = offsets[tid] + counts[blockIdx.x * E + tid];
     for (int x = tid; x < kWaves * half_words; x += kThreads)
         sm.hist[x / half_words][x % half_words] = 0;
     __syncthreads();
@@ -275,7 +288,7 @@ void launch_align_sort(const int32_t *ids, int P, int E, int block_m, int32_t *s
     hipLaunchKernelGGL(k_align_scan, dim3(1), dim3(kThreads), 0, stream, scratch, chunks, E,
                        block_m, slots, tiles_cap, sorted_ids, offsets, tile_expert, n_tiles);
     hipLaunchKernelGGL(k_align_scatter, dim3(chunks), dim3(kThreads), 0, stream, ids, P, E,
-                       scratch, sorted_ids, inverse);
+                       scratch, offsets, sorted_ids, inverse);
 }
 
 }  // namespace moe

@@ -180,6 +180,46 @@ def main():
     log("staged: %.4f ms/step; per stage (ms): %s" % (
         staged_ms, ", ".join("%s %.4f" % (k, v) for k, v in per_stage.items())))
 
+    # ---- loop 3: the same fused calls replayed from HIP graphs (one graph per input set):
+    # the pass without host launch overhead
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for j in range(R):
+            fused_step(j)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for j in range(R):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fused_step(j)
+        graphs.append(g)
+    for i in range(args.warmup):
+        graphs[i % R].replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        graphs[i % R].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph_ms = e0.elapsed_time(e1) / args.steps
+    del graphs
+    # ---- loop 4: one input set over and over (weights partly cache-resident)
+    for i in range(args.warmup):
+        fused_step(0)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        fused_step(0)
+    e1.record()
+    torch.cuda.synchronize()
+    warm_ms = e0.elapsed_time(e1) / args.steps
+    log("graph replay: %.4f ms/step; warm (one input set): %.4f ms/step" % (graph_ms, warm_ms))
+    ctx = context_numbers(torch, dev)
+    log("context: device copy %.0f GB/s, torch bf16 matmul %.0f TFLOP/s" % (
+        ctx["device_copy_gbps"], ctx["torch_matmul_bf16_tflops"]))
+
     # ---- roofline of the pass and of the dominant kernel, from the realized routing
     touched = []
     loads = []
@@ -203,6 +243,9 @@ def main():
 
     ms = fused_ms
     base = BASELINE_MS.get(cfg.name)
+    t_hbm = pass_bytes / perfmodel.HBM_PEAK_BYTES_PER_S
+    t_mfma = pass_flops / perfmodel.BF16_MFMA_PEAK_FLOP_PER_S
+    floor_ms = max(t_hbm, t_mfma) * 1e3
     line = {
         "metric": "fused-MoE fwd ms; achieved TB/s (decode) / TFLOP/s (prefill) vs roofline",
         "value": round(ms, 5),
@@ -230,6 +273,10 @@ def main():
         "flops": pass_flops,
         "touched_experts": touched_mean,
         "rows_per_expert": loads[0],
+        "binding_roofline": {"bound": "hbm" if t_hbm >= t_mfma else "mfma",
+                             "floor_ms": round(floor_ms, 5), "frac": round(floor_ms / ms, 4)},
+        "graph_ms_per_step": round(graph_ms, 5),
+        "warm_ms_per_step": round(warm_ms, 5),
         "staged_ms_per_step": round(staged_ms, 5),
         "stage_ms": {k: round(v, 5) for k, v in per_stage.items()},
         "roofline": {"kernel": "gate-up GEMM of the routed experts", "bound": "hbm",
@@ -238,8 +285,40 @@ def main():
                      "algorithmic_bytes_per_launch": gu_bytes},
         "cpu_baseline": cpu,
         "baseline_context": base,
+        "context": ctx,
     }
     print(json.dumps(line), flush=True)
+
+
+def context_numbers(torch, dev):
+    """What this GPU reaches outside the library, for context: a 1 GiB device-to-device copy
+    (read + write bytes per second) and a torch bf16 8192^3 matmul."""
+    n = 1 << 30
+    a = torch.ones(n, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2.0 * n * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    m = 8192
+    x = torch.randn((m, m), dtype=torch.bfloat16, device=dev)
+    y = torch.randn((m, m), dtype=torch.bfloat16, device=dev)
+    z = torch.matmul(x, y)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        z = torch.matmul(x, y)
+    e1.record()
+    torch.cuda.synchronize()
+    tflops = 2.0 * m ** 3 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del x, y, z
+    return {"device_copy_gbps": round(copy_gbps, 1), "torch_matmul_bf16_tflops": round(tflops, 1)}
 
 
 # The pages' own figure for this exact workload (another, unnamed GPU): context only.

@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default=None)
     ap.add_argument("--rotate", type=int, default=0, help="input sets (0 = automatic)")
+    ap.add_argument("--path", default="auto", choices=["auto", "direct", "sorted"],
+                    help="the library's path choice (auto: its own rule)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -102,7 +104,7 @@ def main():
 
     S = cfg.S
     p = moe.make_params(cfg.T, cfg.H, cfg.E, cfg.F, cfg.k, cfg.scoring, cfg.renormalize,
-                        cfg.num_expert_group, cfg.topk_group, cfg.rsf)
+                        cfg.num_expert_group, cfg.topk_group, cfg.rsf, path=args.path)
     ws = torch.empty(max(256, moe.workspace_bytes(p, S)), dtype=torch.uint8, device=dev)
     out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
     ids = [torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev) for _ in range(R)]
@@ -114,13 +116,13 @@ def main():
             moe.fused_moe_shared_fwd(d["hidden_states"], d["gating_output"], d["w_gate_up"],
                                      d["w_down"], d["shared_w_gate_up"], d["shared_w_down"],
                                      cfg.k, d["correction_bias"], cfg.scoring, cfg.renormalize,
-                                     cfg.num_expert_group, cfg.topk_group, cfg.rsf, out=out,
-                                     workspace=ws)
+                                     cfg.num_expert_group, cfg.topk_group, cfg.rsf,
+                                     path=args.path, out=out, workspace=ws)
         else:
             moe.fused_moe_fwd(d["hidden_states"], d["gating_output"], d["w_gate_up"],
                               d["w_down"], cfg.k, d["correction_bias"], cfg.scoring,
                               cfg.renormalize, cfg.num_expert_group, cfg.topk_group, cfg.rsf,
-                              out=out, workspace=ws)
+                              path=args.path, out=out, workspace=ws)
 
     stages = [moe.STAGE_ALIGN, moe.STAGE_GATE_UP, moe.STAGE_DOWN]
     if S > 0:
@@ -263,7 +265,7 @@ def main():
                    "top_k": cfg.k, "scoring": cfg.scoring, "renormalize": cfg.renormalize,
                    "num_expert_group": cfg.num_expert_group, "topk_group": cfg.topk_group,
                    "routed_scaling_factor": cfg.rsf, "correction_bias": cfg.bias,
-                   "shared_inter": cfg.S, "parallelism": "single GPU"},
+                   "shared_inter": cfg.S, "path": args.path, "parallelism": "single GPU"},
         "achieved_tbps": round(pass_bytes / (ms * 1e-3) / 1e12, 4),
         "achieved_tflops": round(pass_flops / (ms * 1e-3) / 1e12, 3),
         "hbm_roofline_frac": round(pass_bytes / (ms * 1e-3) / perfmodel.HBM_PEAK_BYTES_PER_S, 4),

@@ -82,8 +82,11 @@ def main():
 
     import mixture_experts_forward_amd as moe
     from moe_harness import perfmodel
-    from moe_harness.workloads import BENCH_CONFIG, CONFIGS, make_inputs
+    from moe_harness.workloads import BENCH_CONFIG, CONFIGS, MASKED_CONFIGS, make_inputs
 
+    if args.config in MASKED_CONFIGS:
+        bench_masked(args, MASKED_CONFIGS[args.config])
+        return
     cfg = CONFIGS[args.config or BENCH_CONFIG]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -207,6 +210,15 @@ def main():
     torch.cuda.synchronize()
     graph_ms = e0.elapsed_time(e1) / args.steps
     del graphs
+    # ---- loop 3b: per-step events around single fused calls, for the median
+    step_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(args.steps)]
+    for i in range(args.steps):
+        step_evs[i][0].record()
+        fused_step(i)
+        step_evs[i][1].record()
+    torch.cuda.synchronize()
+    median_ms = float(np.median([a.elapsed_time(b) for a, b in step_evs]))
     # ---- loop 4: one input set over and over (weights partly cache-resident)
     for i in range(args.warmup):
         fused_step(0)
@@ -217,7 +229,8 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     warm_ms = e0.elapsed_time(e1) / args.steps
-    log("graph replay: %.4f ms/step; warm (one input set): %.4f ms/step" % (graph_ms, warm_ms))
+    log("graph replay: %.4f ms/step; median single call %.4f ms; warm (one input set): "
+        "%.4f ms/step" % (graph_ms, median_ms, warm_ms))
     ctx = context_numbers(torch, dev)
     log("context: device copy %.0f GB/s, torch bf16 matmul %.0f TFLOP/s" % (
         ctx["device_copy_gbps"], ctx["torch_matmul_bf16_tflops"]))
@@ -278,6 +291,7 @@ def main():
         "binding_roofline": {"bound": "hbm" if t_hbm >= t_mfma else "mfma",
                              "floor_ms": round(floor_ms, 5), "frac": round(floor_ms / ms, 4)},
         "graph_ms_per_step": round(graph_ms, 5),
+        "median_ms_single_call": round(median_ms, 5),
         "warm_ms_per_step": round(warm_ms, 5),
         "staged_ms_per_step": round(staged_ms, 5),
         "stage_ms": {k: round(v, 5) for k, v in per_stage.items()},
@@ -290,6 +304,115 @@ def main():
         "context": ctx,
     }
     print(json.dumps(line), flush=True)
+
+
+def bench_masked(args, cfg):
+    """The masked-layout expert MLPs of one expert-parallel shard (fused_moe_masked_fwd): the
+    whole call, and its stages with events between them; the roofline object is the gate-up
+    GEMM's (the page's MoEGroupedGemmFwd on the same shapes)."""
+    import numpy as np
+    import torch
+
+    import mixture_experts_forward_amd as moe
+    from moe_harness import perfmodel
+    from moe_harness.workloads import make_masked_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    moe.lib()
+    wbytes = cfg.E * 6.0 * cfg.H * cfg.F
+    R = args.rotate or max(1, min(8, math.ceil(16 * LLC_BYTES / wbytes)))
+    sets = [make_masked_inputs(cfg, dev, seed=42 + i) for i in range(R)]
+    ws = torch.empty(max(256, moe.masked_workspace_bytes(cfg.E, cfg.max_m, cfg.H, cfg.F)),
+                     dtype=torch.uint8, device=dev)
+    out = torch.zeros((cfg.E, cfg.max_m, cfg.H), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def step(i):
+        d = sets[i % R]
+        moe.fused_moe_masked_fwd(d["a"], d["masked_m"], d["w_gate_up"], d["w_down"], out=out,
+                                 workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    stages = [moe.STAGE_ALIGN, moe.STAGE_GATE_UP, moe.STAGE_DOWN]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        d = sets[i % R]
+        evs[i][0].record()
+        for n, st in enumerate(stages):
+            moe.fused_moe_masked_stage(st, d["a"], d["masked_m"], d["w_gate_up"], d["w_down"],
+                                       out, ws)
+            evs[i][n + 1].record()
+    torch.cuda.synchronize()
+    per = {moe.STAGE_NAMES[st]: sum(e[n].elapsed_time(e[n + 1]) for e in evs) / args.steps
+           for n, st in enumerate(stages)}
+    log("masked %s: %.4f ms/call; stages (ms): %s" % (
+        cfg.name, ms, ", ".join("%s %.4f" % kv for kv in per.items())))
+    rows = float(np.mean([int(sd["masked_m"].clamp(0, cfg.max_m).sum()) for sd in sets]))
+    pass_bytes = wbytes + 4.0 * rows * cfg.H + 4.0 * cfg.E
+    pass_flops = 2.0 * rows * 3 * cfg.H * cfg.F
+    gu_bytes = cfg.E * 4.0 * cfg.H * cfg.F + 2.0 * rows * cfg.H + 2.0 * rows * cfg.F
+    gu_gbs = gu_bytes / (per["gate_up"] * 1e-3) / 1e9
+    peak_gbs = perfmodel.HBM_PEAK_BYTES_PER_S / 1e9
+    t_hbm = pass_bytes / perfmodel.HBM_PEAK_BYTES_PER_S
+    t_mfma = pass_flops / perfmodel.BF16_MFMA_PEAK_FLOP_PER_S
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_masked(cfg, sets[0], args.cpu_seconds)
+    line = {
+        "metric": "masked expert-MLP ms (one expert-parallel shard); achieved TB/s vs roofline",
+        "value": round(ms, 5), "unit": "ms", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; %d rotating input sets)" % R,
+        "config": {"workload": cfg.name, "E": cfg.E, "max_m": cfg.max_m, "H": cfg.H,
+                   "F": cfg.F, "rows_in_use_mean": rows, "parallelism": "single GPU"},
+        "achieved_tbps": round(pass_bytes / (ms * 1e-3) / 1e12, 4),
+        "achieved_tflops": round(pass_flops / (ms * 1e-3) / 1e12, 3),
+        "binding_roofline": {"bound": "hbm" if t_hbm >= t_mfma else "mfma",
+                             "floor_ms": round(max(t_hbm, t_mfma) * 1e3, 5),
+                             "frac": round(max(t_hbm, t_mfma) * 1e3 / ms, 4)},
+        "stage_ms": {k: round(v, 5) for k, v in per.items()},
+        "roofline": {"kernel": "gate-up GEMM of the masked rows", "bound": "hbm",
+                     "achieved": round(gu_gbs, 1), "peak": peak_gbs, "unit": "GB/s",
+                     "frac": round(gu_gbs / peak_gbs, 4), "traffic": read_traffic(cfg.name),
+                     "algorithmic_bytes_per_launch": gu_bytes},
+        "cpu_baseline": cpu,
+        "baseline_context": {"gate_up_ms": 0.4851, "source": "TileOPs MoE page, "
+                             "MoEGroupedGemmFwd ds-v3-ep8-masked bf16 (the gate-up GEMM alone)",
+                             "hardware": "not named on the page"},
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_masked(cfg, d, seconds):
+    """The oracle's masked MLP on the host for a sample of the experts, scaled to all E."""
+    import numpy as np
+    import oracle
+    from moe_harness.workloads import to_u16
+    a, m = to_u16(d["a"]), d["masked_m"].cpu().numpy()
+    wgu, wd = to_u16(d["w_gate_up"]), to_u16(d["w_down"])
+    t0 = time.perf_counter()
+    oracle.masked_mlp(a[:1], m[:1], wgu[:1], wd[:1])
+    one = max(time.perf_counter() - t0, 1e-6)
+    n = int(max(1, min(cfg.E, seconds / one)))
+    t0 = time.perf_counter()
+    oracle.masked_mlp(a[:n], m[:n], wgu[:n], wd[:n])
+    dt = time.perf_counter() - t0
+    per_call = dt / n * cfg.E
+    log("cpu oracle: %d of %d experts in %.2f s on %d threads -> %.1f ms per call" % (
+        n, cfg.E, dt, oracle.max_threads(), per_call * 1e3))
+    return {"value": round(per_call * 1e3, 3), "unit": "ms", "cores": oracle.max_threads(),
+            "kind": "oracle", "sample": "%d of %d experts, scaled to all" % (n, cfg.E)}
 
 
 def context_numbers(torch, dev):

@@ -228,6 +228,38 @@ int fused_moe_experts_stage(int stage, const uint16_t *hidden_states, const uint
                             const moe_params_t *p, uint16_t *out, void *workspace,
                             size_t workspace_bytes, void *stream);
 
+/* ---------------------------------------------------------------------------------------
+ * Masked layout: the expert MLPs of one expert-parallel shard (TileOPs "MoE" page,
+ * MoEGroupedGemmFwd with a: [E, layout.max_m, K] and layout_metadata [E] i32, workload
+ * ds-v3-ep8-masked; MoEPrePermuteFwd's num_local_experts).  Local expert e owns the row block
+ * a[e, 0:max_m, :] whose first masked_m[e] rows are the tokens routed to it (placed there by the
+ * exchange between GPUs); the remaining rows of the block are ignored.
+ *   a          [E, max_m, H] bf16.
+ *   masked_m   [E] int32, device: rows in use per expert; clamped to [0, max_m] on the device.
+ *   w_gate_up  [E, 2F, H] bf16 (rows [0,F) gate, [F,2F) up); w_down [E, H, F] bf16.
+ *   out        [E, max_m, H] bf16: row i of expert e is written for i < masked_m[e] with
+ *              bf16( bf16(SiLU(gate) * up) W_down^T ); the other rows are not touched.  There
+ *              are no route weights: weighting and summing a token's rows belongs to the caller
+ *              after the return exchange.
+ *   E in 1..1024, max_m >= 0 (0: nothing is enqueued), H % 64 == 0, F % 64 == 0,
+ *   E * max_m < 2^30.
+ * Workspace: fused_moe_masked_workspace_bytes(E, max_m, H, F) bytes (0 when nothing is to do).
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (E < 1, max_m < 0, H < 1 or F < 1),
+ * MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH. */
+size_t fused_moe_masked_workspace_bytes(int32_t E, int32_t max_m, int32_t H, int32_t F);
+int fused_moe_masked_fwd(const uint16_t *a, const int32_t *masked_m, const uint16_t *w_gate_up,
+                         const uint16_t *w_down, int32_t E, int32_t max_m, int32_t H, int32_t F,
+                         uint16_t *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/* fused_moe_masked_stage -- one step of fused_moe_masked_fwd with the same arguments:
+ * MOE_STAGE_ALIGN (the expert-contiguous layout of the rows in use, into the workspace),
+ * MOE_STAGE_GATE_UP (-> h in the workspace), MOE_STAGE_DOWN (-> out).  The three in that order
+ * enqueue exactly the kernels of fused_moe_masked_fwd.  Other stages: MOE_ERR_UNSUPPORTED. */
+int fused_moe_masked_stage(int stage, const uint16_t *a, const int32_t *masked_m,
+                           const uint16_t *w_gate_up, const uint16_t *w_down, int32_t E,
+                           int32_t max_m, int32_t H, int32_t F, uint16_t *out, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -12,6 +12,7 @@ Entry points (same names as the C ABI):
   fused_moe_fwd(hidden_states, gating_output, w_gate_up, w_down, top_k, ...) -> out
   fused_moe_shared_fwd(..., shared_w_gate_up, shared_w_down)  -> out
   fused_moe_experts_fwd(hidden_states, w_gate_up, w_down, topk_ids, topk_weights) -> out
+  fused_moe_masked_fwd(a, masked_m, w_gate_up, w_down)        -> out [E, max_m, H]
 """
 import ctypes
 import os
@@ -61,6 +62,11 @@ SIGNATURES = {
     "fused_moe_experts_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "fused_moe_experts_stage": (ctypes.c_int, [ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _I32,
                                                _P, _P, _P, _SZ, _P]),
+    "fused_moe_masked_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
+    "fused_moe_masked_fwd": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _SZ,
+                                            _P]),
+    "fused_moe_masked_stage": (ctypes.c_int, [ctypes.c_int, _P, _P, _P, _P, _I32, _I32, _I32,
+                                              _I32, _P, _P, _SZ, _P]),
 }
 
 # stages of fused_moe_experts_stage, in the order fused_moe_experts_fwd runs them
@@ -282,3 +288,53 @@ def fused_moe_experts_stage(stage, params, hidden_states, w_gate_up, w_down, top
             ctypes.byref(params), _ptr(out), _ptr(workspace), workspace.numel(), _stream(dev))
     if st != MOE_OK:
         raise MoEError(st, "fused_moe_experts_stage(%s)" % STAGE_NAMES.get(stage, stage))
+
+
+def masked_workspace_bytes(E, max_m, H, F):
+    return int(lib().fused_moe_masked_workspace_bytes(int(E), int(max_m), int(H), int(F)))
+
+
+def _masked_args(a, masked_m, w_gate_up, w_down, out, workspace):
+    E, max_m, H = a.shape
+    F = w_down.shape[2]
+    dev = a.device
+    _check(a, "a", torch.bfloat16, (E, max_m, H))
+    _check(masked_m, "masked_m", torch.int32, (E,), dev)
+    _check(w_gate_up, "w_gate_up", torch.bfloat16, (E, 2 * F, H), dev)
+    _check(w_down, "w_down", torch.bfloat16, (E, H, F), dev)
+    if out is None:
+        out = torch.zeros((E, max_m, H), dtype=torch.bfloat16, device=dev)
+    _check(out, "out", torch.bfloat16, (E, max_m, H), dev)
+    n = masked_workspace_bytes(E, max_m, H, F)
+    if workspace is None:
+        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+    return E, max_m, H, F, out, workspace
+
+
+def fused_moe_masked_fwd(a, masked_m, w_gate_up, w_down, out=None, workspace=None):
+    """Expert MLPs of one expert-parallel shard on the masked layout a [E, max_m, H]: rows
+    i < masked_m[e] of expert e -> out [E, max_m, H].  Rows past masked_m are left as they are
+    in ``out`` (zeros when out is allocated here)."""
+    E, max_m, H, F, out, workspace = _masked_args(a, masked_m, w_gate_up, w_down, out, workspace)
+    dev = a.device
+    with torch.cuda.device(dev):
+        st = lib().fused_moe_masked_fwd(_ptr(a), _ptr(masked_m), _ptr(w_gate_up), _ptr(w_down),
+                                        E, max_m, H, F, _ptr(out), _ptr(workspace),
+                                        workspace.numel(), _stream(dev))
+    if st != MOE_OK:
+        raise MoEError(st, "fused_moe_masked_fwd")
+    return out
+
+
+def fused_moe_masked_stage(stage, a, masked_m, w_gate_up, w_down, out, workspace):
+    """One stage (STAGE_ALIGN, STAGE_GATE_UP or STAGE_DOWN) of fused_moe_masked_fwd on the
+    caller's workspace (at least masked_workspace_bytes bytes, kept across the stages)."""
+    E, max_m, H = a.shape
+    F = w_down.shape[2]
+    dev = a.device
+    with torch.cuda.device(dev):
+        st = lib().fused_moe_masked_stage(int(stage), _ptr(a), _ptr(masked_m), _ptr(w_gate_up),
+                                          _ptr(w_down), E, max_m, H, F, _ptr(out),
+                                          _ptr(workspace), workspace.numel(), _stream(dev))
+    if st != MOE_OK:
+        raise MoEError(st, "fused_moe_masked_stage(%s)" % STAGE_NAMES.get(stage, stage))

@@ -378,3 +378,111 @@ int fused_moe_experts_stage(int stage, const uint16_t *hidden_states, const uint
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- masked layout
+
+namespace {
+
+// The masked rows as a routed problem: E * max_m single-route tokens, sorted path.
+int masked_plan(int32_t E, int32_t max_m, int32_t H, int32_t F, moe::Plan *pl)
+{
+    if (E < 1 || max_m < 0 || H < 1 || F < 1)
+        return MOE_ERR_SHAPE;
+    if ((int64_t)E * max_m >= (1ll << 30))
+        return MOE_ERR_UNSUPPORTED;
+    moe_params_t p = {};
+    p.num_tokens = E * max_m;
+    p.hidden = H;
+    p.num_experts = E;
+    p.inter = F;
+    p.top_k = 1;
+    p.scoring = MOE_SCORING_SOFTMAX;
+    p.renormalize = 0;
+    p.num_expert_group = 1;
+    p.topk_group = 1;
+    p.routed_scaling_factor = 1.0f;
+    p.path = MOE_PATH_SORTED;
+    const int st = moe::check_dims(&p);
+    if (st != MOE_OK)
+        return st;
+    if (max_m > 0)
+        moe::make_plan(&p, 0, pl);
+    return MOE_OK;
+}
+
+// The routed plan's workspace up to (not including) its expert-output rows: the masked pass
+// writes those rows straight to out.
+size_t masked_bytes(const moe::Plan &pl) { return pl.off_y; }
+
+int masked_run(int first, int last, const uint16_t *a, const int32_t *masked_m,
+               const uint16_t *w_gate_up, const uint16_t *w_down, int32_t E, int32_t max_m,
+               int32_t H, int32_t F, uint16_t *out, void *ws, size_t ws_bytes, void *stream)
+{
+    moe::Plan pl;
+    int st = masked_plan(E, max_m, H, F, &pl);
+    if (st != MOE_OK)
+        return st;
+    if (max_m == 0)
+        return MOE_OK;
+    const bool align = first <= MOE_STAGE_ALIGN, gate_up = first <= MOE_STAGE_GATE_UP &&
+                                                           last >= MOE_STAGE_GATE_UP;
+    const bool down = last >= MOE_STAGE_DOWN;
+    if (!ws || (align && !masked_m) || (gate_up && (!a || !w_gate_up)) ||
+        (down && (!w_down || !out)))
+        return MOE_ERR_NULL;
+    if (ws_bytes < masked_bytes(pl))
+        return MOE_ERR_WORKSPACE;
+    if (!aligned16(ws) || (a && !aligned16(a)) || (w_gate_up && !aligned16(w_gate_up)) ||
+        (w_down && !aligned16(w_down)) || (out && !aligned16(out)))
+        return MOE_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int32_t *ids = ws_at<int32_t>(ws, pl.off_ids);
+    const Ctx c = {a, w_gate_up, w_down, nullptr, nullptr, ids, nullptr, out, ws, s};
+    if (align) {
+        moe::launch_masked_ids(masked_m, E, max_m, ids, s);
+        if ((st = run_stage(MOE_STAGE_ALIGN, pl, c)) != MOE_OK)
+            return st;
+    }
+    if (gate_up && (st = run_stage(MOE_STAGE_GATE_UP, pl, c)) != MOE_OK)
+        return st;
+    if (down) {
+        moe::GemmProblem g = down_problem(pl, c);
+        g.out = out;  // row q of the flattened blocks is written in place
+        if (!launch_gemm(false, g, moe::ROWS_SORTED, pl.down, s))
+            return MOE_ERR_LAUNCH;
+    }
+    return launch_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fused_moe_masked_workspace_bytes(int32_t E, int32_t max_m, int32_t H, int32_t F)
+{
+    moe::Plan pl;
+    if (masked_plan(E, max_m, H, F, &pl) != MOE_OK || max_m == 0)
+        return 0;
+    return masked_bytes(pl);
+}
+
+int fused_moe_masked_fwd(const uint16_t *a, const int32_t *masked_m, const uint16_t *w_gate_up,
+                         const uint16_t *w_down, int32_t E, int32_t max_m, int32_t H, int32_t F,
+                         uint16_t *out, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return masked_run(MOE_STAGE_ALIGN, MOE_STAGE_DOWN, a, masked_m, w_gate_up, w_down, E, max_m,
+                      H, F, out, workspace, workspace_bytes, stream);
+}
+
+int fused_moe_masked_stage(int stage, const uint16_t *a, const int32_t *masked_m,
+                           const uint16_t *w_gate_up, const uint16_t *w_down, int32_t E,
+                           int32_t max_m, int32_t H, int32_t F, uint16_t *out, void *workspace,
+                           size_t workspace_bytes, void *stream)
+{
+    if (stage != MOE_STAGE_ALIGN && stage != MOE_STAGE_GATE_UP && stage != MOE_STAGE_DOWN)
+        return MOE_ERR_UNSUPPORTED;
+    return masked_run(stage, stage, a, masked_m, w_gate_up, w_down, E, max_m, H, F, out,
+                      workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -70,6 +70,11 @@ bool launch_block(bool gate_up, const GemmProblem &g, RowSource src, WsTile tile
 // 256 x 256 tile kernel (ROWS_SORTED with block_m = 256, or ROWS_DENSE with 256-row tiles).
 bool launch_wide(bool gate_up, const GemmProblem &g, RowSource src, hipStream_t stream);
 
+// ---------------------------------------------------------------- masked layout
+// ids[e * max_m + i] = e for i < clamp(masked_m[e], 0, max_m), else -1.
+void launch_masked_ids(const int32_t *masked_m, int E, int max_m, int32_t *ids,
+                       hipStream_t stream);
+
 // ---------------------------------------------------------------- combine
 // out[t] = bf16( sum_j w[t,j] * y[t*k+j] (+ ys[t]) ), routes with ids outside [0,E) skipped.
 void launch_combine(const uint16_t *y, const int32_t *ids, const float *weights,

@@ -33,6 +33,7 @@ STREAM_W_DOWN = 5
 STREAM_SHARED_GATE_UP = 6
 STREAM_SHARED_DOWN = 7
 STREAM_SKEW = 8
+STREAM_MASKED_COUNTS = 11
 
 
 @dataclass(frozen=True)
@@ -65,6 +66,40 @@ CONFIGS = {
     "kimi-k2-shared": MoEConfig("kimi-k2-shared", T=512, H=7168, E=384, F=2048, k=8,
                                 scoring="sigmoid", rsf=2.827, bias=True, S=18432),
 }
+
+
+@dataclass(frozen=True)
+class MaskedConfig:
+    """Masked-layout workload of one expert-parallel shard: E local experts, row blocks of
+    max_m, rows in use per expert drawn uniformly from [lo, max_m]."""
+    name: str
+    E: int
+    max_m: int
+    H: int
+    F: int
+    lo: int
+
+
+# TileOPs "MoE" page, MoEGroupedGemmFwd ds-v3-ep8-masked: a [32, 128, 7168], b [32, 4096, 7168];
+# its TFLOP/s figure implies about 96 rows in use per expert, the mean of counts in [64, 128]
+MASKED_CONFIGS = {
+    "ds-v3-ep8-masked": MaskedConfig("ds-v3-ep8-masked", E=32, max_m=128, H=7168, F=2048, lo=64),
+}
+
+
+def make_masked_inputs(cfg: MaskedConfig, device="cpu", seed: int = 42) -> dict:
+    """a [E,max_m,H] bf16, masked_m [E] int32, w_gate_up [E,2F,H] and w_down [E,H,F] bf16."""
+    E, m, H, F = cfg.E, cfg.max_m, cfg.H, cfg.F
+    g = _gen("cpu", seed, STREAM_MASKED_COUNTS)
+    counts = torch.randint(cfg.lo, m + 1, (E,), generator=g, dtype=torch.int32)
+    return {
+        "a": _normal((E, m, H), 1.0, torch.bfloat16, device, seed, STREAM_HIDDEN),
+        "masked_m": counts.to(device),
+        "w_gate_up": _normal((E, 2 * F, H), H ** -0.5, torch.bfloat16, device, seed,
+                             STREAM_W_GATE_UP),
+        "w_down": _normal((E, H, F), F ** -0.5, torch.bfloat16, device, seed, STREAM_W_DOWN),
+    }
+
 
 # the configuration the benchmark times by default: Qwen3-30B-style decode, 32 tokens
 BENCH_CONFIG = "qwen3-30b-decode"

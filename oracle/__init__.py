@@ -13,6 +13,7 @@ Functions (each follows the passage cited in ``moe_oracle.c``):
   experts(x, w_gate_up, w_down, topk_ids, topk_weights, shared_w_gate_up=None,
           shared_w_down=None, tokens=None, num_threads=0) -> (acc float64 [n,H], out uint16 [n,H])
   forward(...) = route + experts, the whole pass
+  masked_mlp(a, masked_m, w_gate_up, w_down) -> (acc float64 [E,max_m,H], out uint16 [E,max_m,H])
   double_to_bf16(values) -> uint16 (one rounding, nearest-even)
 """
 import ctypes
@@ -153,6 +154,23 @@ def forward(x, gating, w_gate_up, w_down, bias=None, k=2, scoring="softmax", ren
     acc, out = experts(x, w_gate_up, w_down, ids, w, shared_w_gate_up, shared_w_down, tokens,
                        num_threads)
     return {"topk_ids": ids, "topk_weights": w, "acc": acc, "out": out}
+
+
+def masked_mlp(a, masked_m, w_gate_up, w_down, num_threads=0):
+    """The expert MLPs of the masked layout (TileOPs "MoE" page, MoEGroupedGemmFwd with
+    a: [E, layout.max_m, K] and layout_metadata [E]): row i of expert e, for
+    i < clamp(masked_m[e], 0, max_m), is that expert's SwiGLU MLP of a[e, i]; other rows are 0.
+    It is the routed experts' computation with every row a token routed to its block's expert
+    with weight 1 (and -1, no route, for rows past masked_m)."""
+    a = np.asarray(a)
+    E, max_m, H = a.shape
+    m = np.clip(np.asarray(masked_m, dtype=np.int64), 0, max_m)
+    ids = np.where(np.arange(max_m)[None, :] < m[:, None],
+                   np.arange(E)[:, None], -1).astype(np.int32).reshape(E * max_m, 1)
+    w = np.ones((E * max_m, 1), dtype=np.float32)
+    acc, out = experts(a.reshape(E * max_m, H), w_gate_up, w_down, ids, w,
+                       num_threads=num_threads)
+    return acc.reshape(E, max_m, H), out.reshape(E, max_m, H)
 
 
 def double_to_bf16(values):

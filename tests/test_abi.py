@@ -131,3 +131,31 @@ def test_binding_rejects_cpu_tensors():
                                   torch.zeros(8, 128, 64, dtype=torch.bfloat16),
                                   torch.zeros(4, 2, dtype=torch.int32),
                                   torch.zeros(4, 2, dtype=torch.float32))
+
+
+def test_masked_entry_points_reject_before_launch():
+    L = moe.lib()
+    ws_need = L.fused_moe_masked_workspace_bytes(32, 128, 7168, 2048)
+    assert ws_need > 0
+    assert L.fused_moe_masked_workspace_bytes(32, 0, 7168, 2048) == 0   # nothing to do
+    assert L.fused_moe_masked_workspace_bytes(0, 128, 7168, 2048) == 0
+    assert L.fused_moe_masked_workspace_bytes(4, 8, 96, 64) == 0        # H % 64
+    # larger row blocks need more workspace (sorted layout and h grow with E * max_m)
+    assert L.fused_moe_masked_workspace_bytes(32, 256, 7168, 2048) > ws_need
+    fake = ctypes.c_void_p(1 << 20)   # aligned, never dereferenced: checks come first
+    args = lambda E, m, H, F, ws, n: (fake, fake, fake, fake, E, m, H, F, fake, ws, n, None)
+    assert L.fused_moe_masked_fwd(*args(0, 8, 128, 64, fake, 1 << 30)) == -2
+    assert L.fused_moe_masked_fwd(*args(4, -1, 128, 64, fake, 1 << 30)) == -2
+    assert L.fused_moe_masked_fwd(*args(4, 8, 96, 64, fake, 1 << 30)) == -3
+    assert L.fused_moe_masked_fwd(*args(2048, 8, 128, 64, fake, 1 << 30)) == -3   # E > 1024
+    assert L.fused_moe_masked_fwd(*args(4, 8, 128, 64, None, 1 << 30)) == -1
+    n = L.fused_moe_masked_workspace_bytes(4, 8, 128, 64)
+    assert L.fused_moe_masked_fwd(*args(4, 8, 128, 64, fake, n - 1)) == -4
+    assert L.fused_moe_masked_fwd(*args(4, 0, 128, 64, None, 0)) == 0   # max_m = 0: no-op
+    assert L.fused_moe_masked_fwd(fake, None, fake, fake, 4, 8, 128, 64, fake, fake, n,
+                                  None) == -1                            # masked_m missing
+    assert L.fused_moe_masked_stage(5, fake, fake, fake, fake, 4, 8, 128, 64, fake, fake, n,
+                                    None) == -3                          # no combine stage
+    # a stage checks only what it reads: the down stage needs no activations or masked_m
+    assert L.fused_moe_masked_stage(3, None, None, None, fake, 4, 8, 128, 64, None, fake, n,
+                                    None) == -1                          # but out is needed

@@ -14,6 +14,8 @@ Functions (each follows the passage cited in ``moe_oracle.c``):
           shared_w_down=None, tokens=None, num_threads=0) -> (acc float64 [n,H], out uint16 [n,H])
   forward(...) = route + experts, the whole pass
   masked_mlp(a, masked_m, w_gate_up, w_down) -> (acc float64 [E,max_m,H], out uint16 [E,max_m,H])
+  fp8_e4m3_decode(codes) -> float64 values of OCP e4m3 codes
+  grouped_gemm_fp8(a, a_scale, b, b_scale, masked_m) -> (acc float64 [E,max_m,N], out uint16)
   double_to_bf16(values) -> uint16 (one rounding, nearest-even)
 """
 import ctypes
@@ -49,6 +51,10 @@ def _load():
     lib.oracle_experts.restype = _I
     lib.oracle_double_to_bf16.argtypes = [ctypes.c_double]
     lib.oracle_double_to_bf16.restype = ctypes.c_uint16
+    lib.oracle_fp8_e4m3_to_double.argtypes = [ctypes.c_uint8]
+    lib.oracle_fp8_e4m3_to_double.restype = ctypes.c_double
+    lib.oracle_grouped_gemm_fp8.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P]
+    lib.oracle_grouped_gemm_fp8.restype = _I
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = _I
     _lib = lib
@@ -171,6 +177,33 @@ def masked_mlp(a, masked_m, w_gate_up, w_down, num_threads=0):
     acc, out = experts(a.reshape(E * max_m, H), w_gate_up, w_down, ids, w,
                        num_threads=num_threads)
     return acc.reshape(E, max_m, H), out.reshape(E, max_m, H)
+
+
+def fp8_e4m3_decode(codes):
+    """OCP e4m3 codes (uint8 array) -> float64 values, one call per code into the C decoder."""
+    c = np.asarray(codes, dtype=np.uint8)
+    f = _load().oracle_fp8_e4m3_to_double
+    return np.array([f(int(v)) for v in c.ravel()], dtype=np.float64).reshape(c.shape)
+
+
+def grouped_gemm_fp8(a, a_scale, b, b_scale, masked_m):
+    """MoEGroupedGemmFP8Fwd on the masked layout: a uint8 [E,max_m,K] e4m3, a_scale float32
+    [E,max_m,K/128], b uint8 [E,N,K] e4m3, b_scale float32 [E,N/128,K/128], masked_m int32 [E].
+    Rows past masked_m are 0 in the result."""
+    a = _c(a, np.uint8)
+    b = _c(b, np.uint8)
+    sa = _c(a_scale, np.float32)
+    sb = _c(b_scale, np.float32)
+    m = _c(masked_m, np.int32)
+    E, max_m, K = a.shape
+    N = b.shape[1]
+    out = np.zeros((E, max_m, N), dtype=np.uint16)
+    acc = np.zeros((E, max_m, N), dtype=np.float64)
+    rc = _load().oracle_grouped_gemm_fp8(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(m), E,
+                                         max_m, N, K, _ptr(out), _ptr(acc))
+    if rc != 0:
+        raise ValueError("oracle_grouped_gemm_fp8 rejected its arguments (%d)" % rc)
+    return acc, out
 
 
 def double_to_bf16(values):

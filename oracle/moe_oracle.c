@@ -11,6 +11,8 @@
  *   route     gating logits -> top-k expert ids and f32 route weights
  *   align     stable counting sort of the routes by expert, each expert padded to block_m rows
  *   experts   out[t] = RNE_bf16( sum_j w[t,j] * SwiGLU_{id[t,j]}(x[t]) + SharedSwiGLU(x[t]) )
+ *   fp8 grouped GEMM (MoEGroupedGemmFP8Fwd, masked layout, e4m3 operands with f32 scales per
+ *             1 x 128 activation block and per 128 x 128 weight block)
  *
  * Precision: every floating-point quantity is double; results are rounded exactly once at the
  * end (route weights to f32, outputs to bf16 with round-to-nearest-even).  The only f32
@@ -380,6 +382,65 @@ int oracle_experts(const uint16_t *x, const uint16_t *w_gate_up, const uint16_t 
         free(xd); free(a); free(acc);
     }
     return status;
+}
+
+/* ---------------------------------------------------------------- fp8 grouped GEMM */
+
+/* OCP FP8 E4M3 ("e4m3fn") code -> double, from the format's definition: 1 sign bit, 4 exponent
+ * bits with bias 7, 3 mantissa bits; exponent field 0 encodes subnormals m/8 * 2^-6; there are
+ * no infinities, and S.1111.111 is NaN, so the largest finite magnitude is 1.75 * 2^8 = 448.
+ * (TileOPs "MoE" page, MoEGroupedGemmFP8Fwd: dtype=fp8e4m3.) */
+double oracle_fp8_e4m3_to_double(uint8_t code)
+{
+    const int sign = code >> 7, e = (code >> 3) & 15, m = code & 7;
+    if (e == 15 && m == 7)
+        return NAN;
+    const double mag = e == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -mag : mag;
+}
+
+/* The grouped GEMM of the masked layout with block scales (TileOPs "MoE" page,
+ * MoEGroupedGemmFP8Fwd: a [E, layout.max_m, K] e4m3 with a_scale [E, layout.max_m,
+ * ceil_div(K, 128)] f32; b [E, N, K] e4m3 with b_scale [E, ceil_div(N, 128), ceil_div(K, 128)]
+ * f32; layout_metadata [E] i32 = rows in use per expert):
+ *   out[e, m, n] = RNE_bf16( sum_kb a_scale[e, m, kb] * b_scale[e, n / 128, kb]
+ *                            * sum_{k in block kb} a[e, m, k] * b[e, n, k] )
+ * for m < clamp(masked_m[e], 0, max_m); other rows are left as they are.  Reading: the scale
+ * of a block multiplies the exact product sum of that block's decoded codes (the dequantised
+ * operands' dot product), and the output is bf16.  Everything in double, one rounding. */
+int oracle_grouped_gemm_fp8(const uint8_t *a, const float *a_scale, const uint8_t *b,
+                            const float *b_scale, const int32_t *masked_m, int E, int max_m,
+                            int N, int K, uint16_t *out, double *acc_out)
+{
+    if (E < 1 || max_m < 0 || N < 1 || K < 1)
+        return -1;
+    const int KB = (K + 127) / 128, NB = (N + 127) / 128;
+    for (int e = 0; e < E; ++e) {
+        int rows = masked_m[e];
+        rows = rows < 0 ? 0 : (rows > max_m ? max_m : rows);
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic)
+#endif
+        for (int mn = 0; mn < rows * N; ++mn) {
+            const int m = mn / N, n = mn % N;
+            const uint8_t *ar = a + ((size_t)e * max_m + m) * K;
+            const uint8_t *br = b + ((size_t)e * N + n) * K;
+            double total = 0.0;
+            for (int kb = 0; kb < KB; ++kb) {
+                double block = 0.0;
+                for (int k = kb * 128; k < K && k < kb * 128 + 128; ++k)
+                    block += oracle_fp8_e4m3_to_double(ar[k]) * oracle_fp8_e4m3_to_double(br[k]);
+                const double sa = a_scale[((size_t)e * max_m + m) * KB + kb];
+                const double sb = b_scale[((size_t)e * NB + n / 128) * KB + kb];
+                total += sa * sb * block;
+            }
+            const size_t o = ((size_t)e * max_m + m) * N + n;
+            out[o] = oracle_double_to_bf16(total);
+            if (acc_out)
+                acc_out[o] = total;
+        }
+    }
+    return 0;
 }
 
 int oracle_max_threads(void)

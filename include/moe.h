@@ -260,6 +260,26 @@ int fused_moe_masked_stage(int stage, const uint16_t *a, const int32_t *masked_m
                            int32_t max_m, int32_t H, int32_t F, uint16_t *out, void *workspace,
                            size_t workspace_bytes, void *stream);
 
+/* ---------------------------------------------------------------------------------------
+ * moe_grouped_gemm_fp8 -- block-scaled FP8 grouped GEMM of the masked layout (TileOPs "MoE"
+ * page, MoEGroupedGemmFP8Fwd: a [E, layout.max_m, K] and b [E, N, K] in fp8e4m3, a_scale
+ * [E, layout.max_m, ceil_div(K, 128)] f32, b_scale [E, ceil_div(N, 128), ceil_div(K, 128)] f32,
+ * layout_metadata [E] i32):
+ *   out[e, m, n] = bf16( sum_kb a_scale[e,m,kb] * b_scale[e,n/128,kb]
+ *                        * sum_{k in block kb} a[e,m,k] * b[e,n,k] )   for m < masked_m[e].
+ *   a        [E, max_m, K] uint8: OCP e4m3 codes (S.EEEE.MMM, bias 7, no infinities).
+ *   a_scale  [E, max_m, K/128] f32; b [E, N, K] uint8 e4m3; b_scale [E, ceil(N/128), K/128] f32.
+ *   masked_m [E] int32, device: rows in use per expert, clamped to [0, max_m] on the device.
+ *   out      [E, max_m, N] bf16: rows m < masked_m[e] written, the other rows untouched.
+ * Products of a block are summed exactly (MFMA, f32), scaled in f32 and accumulated in f32;
+ * NaN codes (S.1111.111) propagate.  Needs E >= 1, max_m >= 0 (0: nothing is enqueued),
+ * N % 64 == 0, K % 128 == 0, 16-byte aligned a, b, out and 4-byte aligned scales.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (E < 1, max_m < 0, N < 1, K < 1), MOE_ERR_UNSUPPORTED
+ * (N % 64, K % 128, E * max_m >= 2^30, alignment), MOE_ERR_LAUNCH. */
+int moe_grouped_gemm_fp8(const uint8_t *a, const float *a_scale, const uint8_t *b,
+                         const float *b_scale, const int32_t *masked_m, int32_t E, int32_t max_m,
+                         int32_t N, int32_t K, uint16_t *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

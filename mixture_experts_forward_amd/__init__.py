@@ -13,6 +13,7 @@ Entry points (same names as the C ABI):
   fused_moe_shared_fwd(..., shared_w_gate_up, shared_w_down)  -> out
   fused_moe_experts_fwd(hidden_states, w_gate_up, w_down, topk_ids, topk_weights) -> out
   fused_moe_masked_fwd(a, masked_m, w_gate_up, w_down)        -> out [E, max_m, H]
+  moe_grouped_gemm_fp8(a, a_scale, b, b_scale, masked_m)      -> out [E, max_m, N] bf16
 """
 import ctypes
 import os
@@ -67,6 +68,8 @@ SIGNATURES = {
                                             _P]),
     "fused_moe_masked_stage": (ctypes.c_int, [ctypes.c_int, _P, _P, _P, _P, _I32, _I32, _I32,
                                               _I32, _P, _P, _SZ, _P]),
+    "moe_grouped_gemm_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P,
+                                            _P]),
 }
 
 # stages of fused_moe_experts_stage, in the order fused_moe_experts_fwd runs them
@@ -338,3 +341,30 @@ def fused_moe_masked_stage(stage, a, masked_m, w_gate_up, w_down, out, workspace
                                           _ptr(workspace), workspace.numel(), _stream(dev))
     if st != MOE_OK:
         raise MoEError(st, "fused_moe_masked_stage(%s)" % STAGE_NAMES.get(stage, stage))
+
+
+def moe_grouped_gemm_fp8(a, a_scale, b, b_scale, masked_m, out=None):
+    """Block-scaled FP8 grouped GEMM of the masked layout: a [E,max_m,K] and b [E,N,K] e4m3
+    (torch.float8_e4m3fn or uint8 codes), a_scale [E,max_m,K/128] and b_scale
+    [E,ceil(N/128),K/128] f32, masked_m [E] int32 -> out [E,max_m,N] bf16 (rows past masked_m
+    left as they are; zeros when out is allocated here)."""
+    E, max_m, K = a.shape
+    N = b.shape[1]
+    dev = a.device
+    codes = lambda t: t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t
+    a8, b8 = codes(a), codes(b)
+    _check(a8, "a", torch.uint8, (E, max_m, K))
+    _check(b8, "b", torch.uint8, (E, N, K), dev)
+    _check(a_scale, "a_scale", torch.float32, (E, max_m, (K + 127) // 128), dev)
+    _check(b_scale, "b_scale", torch.float32, (E, (N + 127) // 128, (K + 127) // 128), dev)
+    _check(masked_m, "masked_m", torch.int32, (E,), dev)
+    if out is None:
+        out = torch.zeros((E, max_m, N), dtype=torch.bfloat16, device=dev)
+    _check(out, "out", torch.bfloat16, (E, max_m, N), dev)
+    with torch.cuda.device(dev):
+        st = lib().moe_grouped_gemm_fp8(_ptr(a8), _ptr(a_scale), _ptr(b8), _ptr(b_scale),
+                                        _ptr(masked_m), E, max_m, N, K, _ptr(out),
+                                        _stream(dev))
+    if st != MOE_OK:
+        raise MoEError(st, "moe_grouped_gemm_fp8")
+    return out

@@ -485,4 +485,25 @@ int fused_moe_masked_stage(int stage, const uint16_t *a, const int32_t *masked_m
                       workspace, workspace_bytes, stream);
 }
 
+int moe_grouped_gemm_fp8(const uint8_t *a, const float *a_scale, const uint8_t *b,
+                         const float *b_scale, const int32_t *masked_m, int32_t E, int32_t max_m,
+                         int32_t N, int32_t K, uint16_t *out, void *stream)
+{
+    if (E < 1 || max_m < 0 || N < 1 || K < 1)
+        return MOE_ERR_SHAPE;
+    if (N % 64 != 0 || K % 128 != 0 || (int64_t)E * max_m >= (1ll << 30) ||
+        (int64_t)E * N >= (1ll << 30))
+        return MOE_ERR_UNSUPPORTED;
+    if (max_m == 0)
+        return MOE_OK;
+    if (!a || !a_scale || !b || !b_scale || !masked_m || !out)
+        return MOE_ERR_NULL;
+    if (!aligned16(a) || !aligned16(b) || !aligned16(out) || ((uintptr_t)a_scale & 3u) ||
+        ((uintptr_t)b_scale & 3u))
+        return MOE_ERR_UNSUPPORTED;
+    moe::launch_fp8_gemm(a, a_scale, b, b_scale, masked_m, E, max_m, N, K, out,
+                         static_cast<hipStream_t>(stream));
+    return launch_status();
+}
+
 }  // extern "C"

@@ -1,0 +1,244 @@
+// moe_fp8_kernel.h -- block-scaled FP8 grouped GEMM of the masked layout (TileOPs "MoE" page,
+// MoEGroupedGemmFP8Fwd: a [E, layout.max_m, K] e4m3 with a_scale [E, layout.max_m, K/128] f32,
+// b [E, N, K] e4m3 with b_scale [E, N/128, K/128] f32, layout_metadata [E] = rows in use):
+//
+//   out[e, m, n] = bf16( sum_kb a_scale[e, m, kb] * b_scale[e, n/128, kb]
+//                        * sum_{k in block kb} a[e, m, k] * b[e, n, k] ),  m < masked_m[e]
+//
+// Built like the row-tiled bf16 kernel, for the decode and small-batch shapes the page lists
+// (64 to 256 rows per expert; weight-bandwidth bound):
+//   - a workgroup (4 waves) owns a BM-row tile of one expert's block and 4 * NTW 16-column
+//     tiles of the output; wave w owns NTW of them and streams its own weight rows with
+//     non-temporal 16-byte loads covering whole 128-byte lines (8 lanes per row), STAGES-1
+//     k-steps ahead, through a per-wave swizzled LDS transpose into the MFMA A operand;
+//   - a k-step is 128 elements: one 128-byte line per row, one scale block, and one
+//     v_mfma_scale_f32_16x16x128_f8f6f4 (e4m3 x e4m3, hardware block scales left at 1.0) per
+//     pair of 16-row tiles.  A lane's four results share one output row and one 128-column
+//     weight block, so the block's partial sum is scaled by a_scale * b_scale (f32) and added to
+//     the f32 accumulator;
+//   - the tile's activation rows of a k-step are loaded once per workgroup into a
+//     double-buffered swizzled LDS tile read by all four waves (one barrier per k-step);
+//   - tiles are numbered expert by expert, column block by column block, the row tiles of a
+//     column block innermost; blocks are dealt round-robin to the 8 XCDs, each XCD taking a
+//     contiguous range, so an expert's activation tile and each weight tile are shared through
+//     one L2, and every tile of an expert starts its K loop at the same k-step.
+// A lane ends with four consecutive output columns of one row.
+#pragma once
+
+#include "moe_device.h"
+
+namespace moe_fp8 {
+
+struct Fp8Problem {
+    const uint8_t *a;         // [E, max_m, K] e4m3
+    const float *a_scale;     // [E, max_m, KB]
+    const uint8_t *b;         // [E, N, K] e4m3
+    const float *b_scale;     // [E, NB, KB]
+    const int32_t *masked_m;  // [E]
+    uint16_t *out;            // [E, max_m, N] bf16
+    int E, max_m, N, K, KB, NB;
+};
+
+constexpr int kWaves = 4;
+constexpr int kXcds = 8;
+
+typedef int moe_i32x8 __attribute__((ext_vector_type(8)));
+
+__host__ __device__ inline int fp8_grid(int tiles)
+{
+    return (tiles + kXcds - 1) / kXcds * kXcds;
+}
+
+__device__ __forceinline__ moe_u32x4 load_nt16(const uint8_t *p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const moe_u32x4 *>(p));
+}
+
+__device__ __forceinline__ moe_u32x4 load16(const uint8_t *p)
+{
+    return *reinterpret_cast<const moe_u32x4 *>(p);
+}
+
+// 32 bytes of one operand row for the 16x16x128 MFMA: chunks c and c + 4 of the 128-byte row
+// segment (the same pair for both operands, so each lane group covers the same 32 k-values).
+__device__ __forceinline__ moe_i32x8 join(moe_u32x4 lo, moe_u32x4 hi)
+{
+    return moe_i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+__device__ __forceinline__ moe_f32x4 mfma_fp8_block(moe_i32x8 a, moe_i32x8 b)
+{
+    // format selectors 0/0: both operands OCP e4m3; block scales 127 (E8M0) = 1.0
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, moe_f32x4{0.f, 0.f, 0.f, 0.f},
+                                                            0, 0, 0, 127, 0, 127);
+}
+
+template <int BM, int NTW, int STAGES>
+__global__ __launch_bounds__(64 * kWaves) void k_fp8_gemm(Fp8Problem p, int n_blocks, int m_tiles)
+{
+    constexpr int TM = BM / 16;                  // 16-row MFMA tiles of the row tile
+    constexpr int XI = BM / (8 * kWaves);        // activation load instructions per wave
+    static_assert(BM % (8 * kWaves) == 0, "BM must be a multiple of 32");
+    __shared__ moe_u32x4 s_x[2][BM * 8];          // activation tile, 16-byte slots
+    __shared__ moe_u32x4 s_t[kWaves][NTW * 128];  // per-wave weight transpose buffers
+
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+    // ---- tile: expert-major, column blocks, row tiles innermost; XCD-contiguous ranges
+    const int per_expert = n_blocks * m_tiles;
+    const int total = p.E * per_expert;
+    const int per_xcd = fp8_grid(total) / kXcds;
+    const int t = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    if (t >= total)
+        return;
+    const int expert = t / per_expert;
+    const int rem = t - expert * per_expert;
+    const int nblk = rem / m_tiles;
+    const int row0 = (rem - nblk * m_tiles) * BM;
+    const int rows_used = min(max(p.masked_m[expert], 0), p.max_m);
+    const int n_rows = min(BM, rows_used - row0);
+    if (n_rows <= 0)
+        return;
+    const int K = p.K, KB = p.KB;
+    const int col0 = nblk * (16 * NTW * kWaves) + wv * (16 * NTW);
+
+    // ---- weight rows of this wave: lane reads chunk lane%8 of rows lane/8 and 8 + lane/8
+    const uint8_t *B = p.b + (size_t)expert * p.N * K;
+    const int lrow = lane >> 3, lchunk = lane & 7;
+    const uint8_t *wld[NTW];
+    bool tile_ok[NTW];
+    int sb_base[NTW];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+        const int c = col0 + 16 * nt;
+        tile_ok[nt] = c < p.N;
+        const int cc = tile_ok[nt] ? c : 0;
+        wld[nt] = B + (size_t)(cc + lrow) * K + 16 * lchunk;
+        sb_base[nt] = (expert * p.NB + cc / 128) * KB;
+    }
+    moe_u32x4 *tbuf = s_t[wv];
+    const int wslot0 = lrow * 8 + (lchunk ^ (lrow >> 1));
+    const int wslot1 = (lrow + 8) * 8 + (lchunk ^ ((lrow + 8) >> 1));
+    const int rr = lane & 15, rq = lane >> 4;
+    const int rslot0 = rr * 8 + (rq ^ (rr >> 1));
+    const int rslot1 = rr * 8 + ((rq + 4) ^ (rr >> 1));
+
+    // ---- activation rows this lane loads: tile rows wv*BM/4 + 8*i + lane/8, chunk lane%8;
+    // rows past the rows in use read the tile's first row (their results are never stored)
+    const uint8_t *A = p.a + (size_t)expert * p.max_m * K;
+    const uint8_t *xld[XI];
+    int xslot[XI];
+#pragma unroll
+    for (int i = 0; i < XI; ++i) {
+        const int r = wv * (BM / kWaves) + 8 * i + lrow;
+        const int src = row0 + (r < n_rows ? r : 0);
+        xld[i] = A + (size_t)src * K + 16 * lchunk;
+        xslot[i] = r * 8 + (lchunk ^ ((r >> 1) & 7));
+    }
+    // a_scale rows of this lane's results: row 16*mt + lane%16 of the tile
+    int sa_base[TM];
+#pragma unroll
+    for (int mt = 0; mt < TM; ++mt) {
+        const int r = 16 * mt + rr;
+        sa_base[mt] = (expert * p.max_m + row0 + (r < n_rows ? r : 0)) * KB;
+    }
+
+    const int rot = (int)((expert * 7u) % (unsigned)KB);
+
+    moe_f32x4 acc[TM][NTW];
+#pragma unroll
+    for (int mt = 0; mt < TM; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt)
+            acc[mt][nt] = moe_f32x4{0.f, 0.f, 0.f, 0.f};
+
+    moe_u32x4 wraw[STAGES][NTW][2], xraw[STAGES][XI];
+    float sa[STAGES][TM], sb[STAGES][NTW];
+    auto load = [&](int st, int i) {
+        const int kb = (i + rot) % KB;
+        const int k = kb * 128;
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+            wraw[st][nt][0] = load_nt16(wld[nt] + k);
+            wraw[st][nt][1] = load_nt16(wld[nt] + (size_t)8 * K + k);
+            sb[st][nt] = p.b_scale[sb_base[nt] + kb];
+        }
+#pragma unroll
+        for (int x = 0; x < XI; ++x)
+            xraw[st][x] = load16(xld[x] + k);
+#pragma unroll
+        for (int mt = 0; mt < TM; ++mt)
+            sa[st][mt] = p.a_scale[sa_base[mt] + kb];
+    };
+    auto compute = [&](int st, int i) {
+        moe_u32x4 *xb = s_x[i & 1];
+#pragma unroll
+        for (int x = 0; x < XI; ++x)
+            xb[xslot[x]] = xraw[st][x];
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+            tbuf[nt * 128 + wslot0] = wraw[st][nt][0];
+            tbuf[nt * 128 + wslot1] = wraw[st][nt][1];
+        }
+        __syncthreads();  // activation tile complete; also orders this wave's transpose buffer
+        moe_i32x8 a[NTW];
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt)
+            a[nt] = join(tbuf[nt * 128 + rslot0], tbuf[nt * 128 + rslot1]);
+#pragma unroll
+        for (int mt = 0; mt < TM; ++mt) {
+            const int r = mt * 16 + rr;
+            const int sw = (r >> 1) & 7;
+            const moe_i32x8 bx = join(xb[r * 8 + (rq ^ sw)], xb[r * 8 + ((rq + 4) ^ sw)]);
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) {
+                const moe_f32x4 part = mfma_fp8_block(a[nt], bx);
+                const float s = sa[st][mt] * sb[st][nt];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    acc[mt][nt][q] = fmaf(part[q], s, acc[mt][nt][q]);
+            }
+        }
+        moe_wave_sync();  // this wave's transpose reads finish before its next writes
+    };
+
+    // Software pipeline, STAGES-1 k-steps in flight; branch-free steady state (the prefetch past
+    // the end wraps to an early k-step: in bounds, never consumed).
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st)
+        load(st, st);
+    int i = 0;
+    for (; i + STAGES <= KB; i += STAGES) {
+#pragma unroll
+        for (int st = 0; st < STAGES; ++st) {
+            load((st + STAGES - 1) % STAGES, i + st + STAGES - 1);
+            compute(st, i + st);
+        }
+    }
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st)
+        if (i + st < KB)
+            compute(st, i + st);
+
+    // ---- epilogue: lane holds columns 4*(lane/16)+q of row 16*mt + lane%16
+#pragma unroll
+    for (int mt = 0; mt < TM; ++mt) {
+        const int r = mt * 16 + rr;
+        if (r >= n_rows)
+            continue;
+        uint16_t *orow = p.out + ((size_t)expert * p.max_m + row0 + r) * p.N;
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+            if (!tile_ok[nt])
+                continue;
+            moe_u32x2 packed;
+            packed.x = moe_pack_bf16x2(acc[mt][nt][0], acc[mt][nt][1]);
+            packed.y = moe_pack_bf16x2(acc[mt][nt][2], acc[mt][nt][3]);
+            *reinterpret_cast<moe_u32x2 *>(orow + col0 + 16 * nt + 4 * rq) = packed;
+        }
+    }
+}
+
+}  // namespace moe_fp8

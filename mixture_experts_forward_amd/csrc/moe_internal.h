@@ -75,6 +75,12 @@ bool launch_wide(bool gate_up, const GemmProblem &g, RowSource src, hipStream_t 
 void launch_masked_ids(const int32_t *masked_m, int E, int max_m, int32_t *ids,
                        hipStream_t stream);
 
+// ---------------------------------------------------------------- fp8 grouped GEMM
+// out[e, m, n] for m < masked_m[e] (moe_fp8_kernel.h); K % 128 == 0, N % 64 == 0.
+void launch_fp8_gemm(const uint8_t *a, const float *a_scale, const uint8_t *b,
+                     const float *b_scale, const int32_t *masked_m, int E, int max_m, int N,
+                     int K, uint16_t *out, hipStream_t stream);
+
 // ---------------------------------------------------------------- combine
 // out[t] = bf16( sum_j w[t,j] * y[t*k+j] (+ ys[t]) ), routes with ids outside [0,E) skipped.
 void launch_combine(const uint16_t *y, const int32_t *ids, const float *weights,

@@ -34,6 +34,7 @@ STREAM_SHARED_GATE_UP = 6
 STREAM_SHARED_DOWN = 7
 STREAM_SKEW = 8
 STREAM_MASKED_COUNTS = 11
+STREAM_FP8 = 12
 
 
 @dataclass(frozen=True)
@@ -98,6 +99,56 @@ def make_masked_inputs(cfg: MaskedConfig, device="cpu", seed: int = 42) -> dict:
         "w_gate_up": _normal((E, 2 * F, H), H ** -0.5, torch.bfloat16, device, seed,
                              STREAM_W_GATE_UP),
         "w_down": _normal((E, H, F), F ** -0.5, torch.bfloat16, device, seed, STREAM_W_DOWN),
+    }
+
+
+def random_e4m3_codes(shape, generator, device="cpu") -> torch.Tensor:
+    """Seeded OCP e4m3 codes (uint8): random sign, exponent field 3..11 (magnitudes 2^-4 to
+    ~2^4.9, as block-quantised values occupy), random mantissa; never a NaN code."""
+    sign = torch.randint(0, 2, shape, generator=generator, dtype=torch.int32)
+    exp = torch.randint(3, 12, shape, generator=generator, dtype=torch.int32)
+    man = torch.randint(0, 8, shape, generator=generator, dtype=torch.int32)
+    return ((sign << 7) | (exp << 3) | man).to(torch.uint8).to(device)
+
+
+@dataclass(frozen=True)
+class Fp8Config:
+    """Masked-layout FP8 grouped GEMM workload: E experts, row blocks of max_m (rows in use
+    drawn from [lo, max_m]), N output columns, K reduction."""
+    name: str
+    E: int
+    max_m: int
+    N: int
+    K: int
+    lo: int
+
+
+# TileOPs "MoE" page, MoEGroupedGemmFP8Fwd workloads (T = tokens of the step)
+FP8_CONFIGS = {
+    "ds-v3-dec-b64-up": Fp8Config("ds-v3-dec-b64-up", E=32, max_m=64, N=4096, K=7168, lo=64),
+    "ds-v3-dec-b64-down": Fp8Config("ds-v3-dec-b64-down", E=32, max_m=64, N=7168, K=2048,
+                                    lo=64),
+    "ds-v3-dec-b256-up": Fp8Config("ds-v3-dec-b256-up", E=32, max_m=256, N=4096, K=7168,
+                                   lo=256),
+    "ds-v3-e8-up-masked": Fp8Config("ds-v3-e8-up-masked", E=8, max_m=128, N=4096, K=7168,
+                                    lo=96),
+}
+
+
+def make_fp8_inputs(cfg: Fp8Config, device="cpu", seed: int = 42) -> dict:
+    """a [E,max_m,K] / b [E,N,K] e4m3 codes (uint8), a_scale [E,max_m,K/128] and
+    b_scale [E,ceil(N/128),K/128] f32 (positive, 2^-7 and 2^-9 times U[0.5, 1.5]),
+    masked_m [E] int32 in [lo, max_m]."""
+    E, m, N, K = cfg.E, cfg.max_m, cfg.N, cfg.K
+    g = _gen("cpu", seed, STREAM_FP8)
+    KB, NB = (K + 127) // 128, (N + 127) // 128
+    return {
+        "a": random_e4m3_codes((E, m, K), g, device),
+        "a_scale": ((torch.rand((E, m, KB), generator=g) + 0.5) * 2.0 ** -7).to(device),
+        "b": random_e4m3_codes((E, N, K), g, device),
+        "b_scale": ((torch.rand((E, NB, KB), generator=g) + 0.5) * 2.0 ** -9).to(device),
+        "masked_m": torch.randint(cfg.lo, m + 1, (E,), generator=g,
+                                  dtype=torch.int32).to(device),
     }
 
 

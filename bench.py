@@ -82,10 +82,14 @@ def main():
 
     import mixture_experts_forward_amd as moe
     from moe_harness import perfmodel
-    from moe_harness.workloads import BENCH_CONFIG, CONFIGS, MASKED_CONFIGS, make_inputs
+    from moe_harness.workloads import (BENCH_CONFIG, CONFIGS, FP8_CONFIGS, MASKED_CONFIGS,
+                                       make_inputs)
 
     if args.config in MASKED_CONFIGS:
         bench_masked(args, MASKED_CONFIGS[args.config])
+        return
+    if args.config in FP8_CONFIGS:
+        bench_fp8(args, FP8_CONFIGS[args.config])
         return
     cfg = CONFIGS[args.config or BENCH_CONFIG]
     dev = torch.device("cuda:0")
@@ -390,6 +394,95 @@ def bench_masked(args, cfg):
         "baseline_context": {"gate_up_ms": 0.4851, "source": "TileOPs MoE page, "
                              "MoEGroupedGemmFwd ds-v3-ep8-masked bf16 (the gate-up GEMM alone)",
                              "hardware": "not named on the page"},
+    }
+    print(json.dumps(line), flush=True)
+
+
+# The pages' figures for the FP8 grouped GEMM workloads (TileOPs "MoE" page,
+# MoEGroupedGemmFP8Fwd; GPU not named): context only.
+FP8_BASELINE_MS = {"ds-v3-dec-b64-up": 0.2266, "ds-v3-dec-b64-down": 0.1157,
+                   "ds-v3-dec-b256-up": 0.2420, "ds-v3-e8-up-masked": 0.0743}
+
+
+def bench_fp8(args, cfg):
+    """The block-scaled FP8 grouped GEMM of the masked layout (moe_grouped_gemm_fp8): one
+    launch per step, against the 8 TB/s roofline of its bytes (e4m3 operands, f32 scales, bf16
+    output) and the 5.0 PFLOP/s dense FP8 MFMA peak."""
+    import numpy as np
+    import torch
+
+    import mixture_experts_forward_amd as moe
+    from moe_harness import perfmodel
+    from moe_harness.workloads import make_fp8_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    moe.lib()
+    KB, NB = cfg.K // 128, (cfg.N + 127) // 128
+    wbytes = cfg.E * (cfg.N * cfg.K + NB * KB * 4.0)
+    R = args.rotate or max(1, min(8, math.ceil(16 * LLC_BYTES / wbytes)))
+    sets = [make_fp8_inputs(cfg, dev, seed=42 + i) for i in range(R)]
+    out = torch.zeros((cfg.E, cfg.max_m, cfg.N), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def step(i):
+        d = sets[i % R]
+        moe.moe_grouped_gemm_fp8(d["a"], d["a_scale"], d["b"], d["b_scale"], d["masked_m"],
+                                 out=out)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    rows = float(np.mean([int(sd["masked_m"].clamp(0, cfg.max_m).sum()) for sd in sets]))
+    nbytes = wbytes + rows * (cfg.K + KB * 4.0 + 2.0 * cfg.N) + 4.0 * cfg.E
+    flops = 2.0 * rows * cfg.N * cfg.K
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    peak_gbs = perfmodel.HBM_PEAK_BYTES_PER_S / 1e9
+    t_hbm, t_mfma = nbytes / perfmodel.HBM_PEAK_BYTES_PER_S, flops / 5.0e15
+    log("fp8 %s: %.4f ms/call, %.0f GB/s, %.1f TFLOP/s" % (cfg.name, ms, gbs,
+                                                          flops / (ms * 1e-3) / 1e12))
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        h = {k: v.cpu().numpy() for k, v in sets[0].items()}
+        cols = 128
+        t0 = time.perf_counter()
+        oracle.grouped_gemm_fp8(h["a"][:1], h["a_scale"][:1], h["b"][:1, :cols],
+                                h["b_scale"][:1, :1], h["masked_m"][:1])
+        dt = time.perf_counter() - t0
+        scale = cfg.E * (cfg.N / cols) * rows / cfg.E / max(1, int(h["masked_m"][0]))
+        cpu = {"value": round(dt * scale * 1e3, 3), "unit": "ms", "cores": oracle.max_threads(),
+               "kind": "oracle", "sample": "expert 0, first %d output columns, scaled to all "
+               "experts, columns and rows in use" % cols}
+        log("cpu oracle: sample %.2f s -> %.1f ms per call" % (dt, cpu["value"]))
+    base = FP8_BASELINE_MS.get(cfg.name)
+    line = {
+        "metric": "FP8 grouped GEMM ms (masked layout, block scales); achieved TB/s vs roofline",
+        "value": round(ms, 5), "unit": "ms", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3",
+        "data": "synthetic (seeded e4m3 codes and scales; %d rotating input sets)" % R,
+        "config": {"workload": cfg.name, "E": cfg.E, "max_m": cfg.max_m, "N": cfg.N,
+                   "K": cfg.K, "rows_in_use_mean": rows, "parallelism": "single GPU"},
+        "achieved_tbps": round(gbs / 1e3, 4),
+        "achieved_tflops": round(flops / (ms * 1e-3) / 1e12, 3),
+        "binding_roofline": {"bound": "hbm" if t_hbm >= t_mfma else "mfma",
+                             "floor_ms": round(max(t_hbm, t_mfma) * 1e3, 5),
+                             "frac": round(max(t_hbm, t_mfma) * 1e3 / ms, 4)},
+        "roofline": {"kernel": "k_fp8_gemm", "bound": "hbm", "achieved": round(gbs, 1),
+                     "peak": peak_gbs, "unit": "GB/s", "frac": round(gbs / peak_gbs, 4),
+                     "traffic": read_traffic(cfg.name), "algorithmic_bytes_per_launch": nbytes},
+        "cpu_baseline": cpu,
+        "baseline_context": ({"ms": base, "source": "TileOPs MoE page, MoEGroupedGemmFP8Fwd "
+                              "%s fp8e4m3" % cfg.name, "hardware": "not named on the page"}
+                             if base else None),
     }
     print(json.dumps(line), flush=True)
 

@@ -23,9 +23,19 @@
 //     contiguous range, so an expert's activation tile and each weight tile are shared through
 //     one L2, and every tile of an expert starts its K loop at the same k-step.
 // A lane ends with four consecutive output columns of one row.
+//
+// k_fp8_wide is the same computation on the 256 x 256 tile of moe_wide_kernel.h, for blocks of
+// ~128 rows and more: 8 waves, both operands loaded straight into LDS (a 128-element FP8 k-step
+// is the 128-byte row segment that kernel's load path and swizzle are built for), 16-row tiles
+// without rows in use skipped, so each weight byte is requested once per 256 rows.  It needs
+// K % 512 == 0 and a 16-byte aligned a_scale (activation scales are staged 4 blocks at a
+// time).  The block sums of one weight tile are scaled while the next tile's MFMAs run.
 #pragma once
 
+#include <type_traits>
+
 #include "moe_device.h"
+#include "moe_wide_kernel.h"
 
 namespace moe_fp8 {
 
@@ -237,6 +247,207 @@ __global__ __launch_bounds__(64 * kWaves) void k_fp8_gemm(Fp8Problem p, int n_bl
             packed.x = moe_pack_bf16x2(acc[mt][nt][0], acc[mt][nt][1]);
             packed.y = moe_pack_bf16x2(acc[mt][nt][2], acc[mt][nt][3]);
             *reinterpret_cast<moe_u32x2 *>(orow + col0 + 16 * nt + 4 * rq) = packed;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- 256 x 256 tile form
+
+// Grid of a launch: tiles rounded up to a multiple of 8.
+__host__ __device__ inline int fp8_wide_grid(int tiles)
+{
+    return (tiles + kXcds - 1) / kXcds * kXcds;
+}
+
+// NT: 16-row weight tiles per wave (8: 256 output columns per workgroup, 4: 128 -- twice the
+// workgroups, for launches that would not fill the GPU).
+template <int NT>
+__global__ __launch_bounds__(moe_wide::kThreads) void k_fp8_wide(Fp8Problem p, int n_blocks,
+                                                                  int m_tiles)
+{
+    // moe_wide's tile constants (this namespace's kWaves is the 4-wave kernel's)
+    using moe_wide::kBM;
+    using moe_wide::kMT;
+    using moe_wide::kWM;
+    using moe_wide::kWN;
+    using moe_wide::kXcds;
+    using moe_wide::kThreads;
+    using moe_wide::Stage;
+    using moe_wide::dma16;
+    using moe_wide::wait_loads;
+    using St = Stage<64>;                 // 128-byte rows: 128 e4m3 codes (slot order)
+    constexpr int BW = 32 * NT;           // output columns (weight rows) per workgroup
+    constexpr int WLoads = BW / 64;       // weight DMA instructions per wave
+    constexpr int kStage = (kBM + BW) * 128;
+    constexpr int kG = 4;               // k-steps per group of staged activation scales
+    __shared__ moe_u32x4 smem[2 * kStage / 16];
+    __shared__ float s_scale[2][kBM * kG];  // a_scale of the tile rows, two groups
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wv / kWN, wn = wv % kWN;
+
+    // ---- tile: expert-major, column blocks, row tiles innermost; XCD-contiguous ranges
+    const int per_expert = n_blocks * m_tiles;
+    const int total = p.E * per_expert;
+    const int W = min((int)gridDim.x, fp8_wide_grid(total));
+    const int per = W / kXcds;
+    const int idx = blockIdx.x / kXcds;
+    if (idx >= per)
+        return;
+    const int t = (blockIdx.x % kXcds) * per + idx;
+    if (t >= total)
+        return;
+    const int expert = t / per_expert;
+    const int rem = t - expert * per_expert;
+    const int nblk = rem / m_tiles;
+    const int row0 = (rem - nblk * m_tiles) * kBM;
+    const int rows_used = min(max(p.masked_m[expert], 0), p.max_m);
+    const int n_real = __builtin_amdgcn_readfirstlane(min(kBM, rows_used - row0));
+    if (n_real <= 0)
+        return;
+    const int K = p.K, KB = p.KB;
+    const int col_wg = nblk * BW;
+
+    // ---- DMA sources (see moe_wide_kernel.h): instruction j of this wave covers tile rows
+    // wv*32 + 8j .. +7, lane l fetching chunk (l%8) ^ swizzle(row) of row wv*32 + 8j + l/8
+    const int lrow = lane >> 3, lpos = lane & 7;
+    const uint8_t *B = p.b + (size_t)expert * p.N * K;
+    const uint8_t *A = p.a + ((size_t)expert * p.max_m + row0) * K;
+    const uint8_t *wsrc[WLoads];
+#pragma unroll
+    for (int j = 0; j < WLoads; ++j) {
+        const int r = wv * (BW / moe_wide::kWaves) + 8 * j + lrow;
+        const int c = col_wg + r;
+        wsrc[j] = B + (size_t)(c < p.N ? c : 0) * K + 16 * (lpos ^ ((r >> 1) & 7));
+    }
+    const uint8_t *xsrc[St::kXLoads];
+    bool xload[St::kXLoads];
+#pragma unroll
+    for (int j = 0; j < St::kXLoads; ++j) {
+        const int rfirst = wv * (kBM / moe_wide::kWaves) + 8 * j;
+        const int r = rfirst + lrow;
+        xload[j] = rfirst < n_real;
+        xsrc[j] = A + (size_t)(r < n_real ? r : 0) * K + 16 * (lpos ^ ((r >> 1) & 7));
+    }
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+    const uint32_t x_dst = lds0 + wv * (kBM / moe_wide::kWaves) * 128;
+    const uint32_t w_dst = lds0 + kBM * 128 + wv * (BW / moe_wide::kWaves) * 128;
+
+    const int rr = lane & 15, rq = lane >> 4;
+    int mt_real = 0;
+#pragma unroll
+    for (int i = 0; i < kMT; ++i)
+        mt_real += (16 * (wm + kWM * i) < n_real) ? 1 : 0;
+    // scales: a_scale of the tile's rows is staged in LDS kG k-steps at a time -- waves 0..3
+    // each copy 64 rows x kG consecutive blocks (16 bytes a row, one load instruction; rows past
+    // the rows in use copy row 0) -- instead of one strided load per row per k-step.  b_scale:
+    // the block of this wave's 128 columns, one uniform load per k-step.
+    const float *sa_src = p.a_scale +
+                          ((size_t)expert * p.max_m + row0 +
+                           (64 * (wv & 3) + lane < n_real ? 64 * (wv & 3) + lane : 0)) * KB;
+    const uint32_t sa_dst = (uint32_t)(uintptr_t)&s_scale[0][0] + (wv & 3) * 64 * 16;
+    const int wcol = col_wg + 16 * NT * wn;  // this wave's columns: one 128-column block
+    const int sb_base = (expert * p.NB + (wcol < p.N ? wcol : 0) / 128) * KB;
+    // the K loop starts at a multiple of kG blocks (KB % kG == 0), so groups stay aligned
+    const int rot = (int)((expert * 7u) % (unsigned)(KB / kG)) * kG;
+
+    moe_f32x4 acc[kMT][NT];
+#pragma unroll
+    for (int m = 0; m < kMT; ++m)
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+            acc[m][n] = moe_f32x4{0.f, 0.f, 0.f, 0.f};
+
+    float sb[2];
+    auto issue = [&](int stage, int i) {
+        const int kb = (i + rot) % KB;
+        const int k = kb * 128;
+        const uint32_t so = stage * kStage;
+#pragma unroll
+        for (int j = 0; j < St::kXLoads; ++j)
+            if (xload[j])
+                dma16(xsrc[j] + k, x_dst + so + j * 1024);
+#pragma unroll
+        for (int j = 0; j < WLoads; ++j)
+            dma16(wsrc[j] + k, w_dst + so + j * 1024);
+        if (i % kG == 0 && wv < 4)  // a new group: a_scale[rows][kb .. kb + kG)
+            dma16(sa_src + kb, sa_dst + ((i / kG) & 1) * (kBM * kG * 4));
+        sb[stage] = p.b_scale[sb_base + kb];
+    };
+
+    // Two LDS stages as in moe_wide_kernel.h: at the top of step i this wave's loads of k-step
+    // i (operands and scales) are the only ones outstanding; the barrier publishes the stage
+    // and frees the other one for k-step i+1.  Instantiated per count of real 16-row tiles.
+    auto k_loop = [&](auto mtr) {
+        constexpr int MTR = decltype(mtr)::value;
+        issue(0, 0);
+        for (int i = 0; i < KB; ++i) {
+            wait_loads(0);
+            __syncthreads();
+            if (i + 1 < KB)
+                issue((i + 1) & 1, i + 1);
+            if (MTR == 0)
+                continue;
+            const moe_u32x4 *xb = smem + (i & 1) * (kStage / 16);
+            const moe_u32x4 *wb = xb + kBM * 8;
+            moe_i32x8 bx[MTR > 0 ? MTR : 1];
+            float s[MTR > 0 ? MTR : 1];
+            const float *sa = s_scale[(i / kG) & 1];
+#pragma unroll
+            for (int m = 0; m < MTR; ++m) {
+                const int r = 16 * (wm + kWM * m) + rr;
+                bx[m] = join(xb[St::slot(r, rq)], xb[St::slot(r, rq + 4)]);
+                s[m] = sa[r * kG + i % kG] * sb[i & 1];
+            }
+            // The block sums of weight tile n are scaled into the accumulators while the MFMAs
+            // of tile n+1 run (two sets of partials), so no FMA waits on the MFMA just issued.
+            moe_f32x4 part[2][MTR > 0 ? MTR : 1];
+#pragma unroll
+            for (int n = 0; n <= NT; ++n) {
+                if (n < NT) {
+                    const int r = 16 * NT * wn + 16 * n + rr;
+                    const moe_i32x8 aw = join(wb[St::slot(r, rq)], wb[St::slot(r, rq + 4)]);
+#pragma unroll
+                    for (int m = 0; m < MTR; ++m)
+                        part[n & 1][m] = mfma_fp8_block(aw, bx[m]);
+                }
+                if (n > 0) {
+#pragma unroll
+                    for (int m = 0; m < MTR; ++m)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            acc[m][n - 1][q] =
+                                fmaf(part[(n - 1) & 1][m][q], s[m], acc[m][n - 1][q]);
+                }
+            }
+        }
+    };
+    switch (mt_real) {
+    case 0: k_loop(std::integral_constant<int, 0>()); break;
+    case 1: k_loop(std::integral_constant<int, 1>()); break;
+    case 2: k_loop(std::integral_constant<int, 2>()); break;
+    case 3: k_loop(std::integral_constant<int, 3>()); break;
+    default: k_loop(std::integral_constant<int, 4>()); break;
+    }
+
+    // ---- epilogue: lane holds columns 4*(lane/16)+q of row 16*(wm + 4m) + lane%16
+#pragma unroll
+    for (int m = 0; m < kMT; ++m) {
+        const int r = 16 * (wm + kWM * m) + rr;
+        if (m >= mt_real || r >= n_real)
+            continue;
+        uint16_t *orow = p.out + ((size_t)expert * p.max_m + row0 + r) * p.N;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            const int col = wcol + 16 * n + 4 * rq;
+            if (col >= p.N)
+                continue;
+            moe_u32x2 packed;
+            packed.x = moe_pack_bf16x2(acc[m][n][0], acc[m][n][1]);
+            packed.y = moe_pack_bf16x2(acc[m][n][2], acc[m][n][3]);
+            *reinterpret_cast<moe_u32x2 *>(orow + col) = packed;
         }
     }
 }

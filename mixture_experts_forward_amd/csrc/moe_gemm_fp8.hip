@@ -1,4 +1,8 @@
-// moe_gemm_fp8.hip -- launches of the block-scaled FP8 grouped GEMM (moe_fp8_kernel.h).
+// moe_gemm_fp8.hip -- launches of the block-scaled FP8 grouped GEMM (moe_fp8_kernel.h): the
+// 64-row form for blocks of up to 64 rows, else the 256-row tile form (256 or, when that gives
+// fewer than two workgroups per CU, 128 columns per workgroup); the 64-row form also when K is
+// not a multiple of 512 or a_scale is not 16-byte aligned.  Tile shapes measured on MI355X on
+// the page's decode shapes.
 #include "moe_fp8_kernel.h"
 #include "moe_internal.h"
 
@@ -12,6 +16,25 @@ void launch_one(const moe_fp8::Fp8Problem &p, hipStream_t stream)
     const int tiles = p.E * n_blocks * m_tiles;
     hipLaunchKernelGGL((moe_fp8::k_fp8_gemm<BM, NTW, STAGES>), dim3(moe_fp8::fp8_grid(tiles)),
                        dim3(64 * moe_fp8::kWaves), 0, stream, p, n_blocks, m_tiles);
+}
+
+template <int NT>
+void launch_fp8_wide(const moe_fp8::Fp8Problem &p, int m_tiles, hipStream_t stream)
+{
+    const int n_blocks = (p.N + 32 * NT - 1) / (32 * NT);
+    hipLaunchKernelGGL(moe_fp8::k_fp8_wide<NT>,
+                       dim3(moe_fp8::fp8_wide_grid(p.E * n_blocks * m_tiles)),
+                       dim3(moe_wide::kThreads), 0, stream, p, n_blocks, m_tiles);
+}
+
+int device_cus()
+{
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n < 1)
+        n = 256;
+    return n;
 }
 
 }  // namespace
@@ -35,7 +58,18 @@ void launch_fp8_gemm(const uint8_t *a, const float *a_scale, const uint8_t *b,
     p.K = K;
     p.KB = K / 128;
     p.NB = (N + 127) / 128;
-    launch_one<64, 1, 3>(p, stream);
+    // Blocks of up to 64 rows: the 64-row form (one row tile).  Taller blocks: the 256-row
+    // form, which needs 4-block scale groups and 16-byte aligned activation scales.
+    if (max_m <= 64 || p.KB % 4 != 0 || ((uintptr_t)a_scale & 15u) != 0) {
+        launch_one<64, 4, 2>(p, stream);
+        return;
+    }
+    const int m_tiles = (max_m + moe_wide::kBM - 1) / moe_wide::kBM;
+    const int wide_tiles = E * m_tiles * ((N + 255) / 256);
+    if (wide_tiles >= 2 * device_cus())
+        launch_fp8_wide<8>(p, m_tiles, stream);
+    else
+        launch_fp8_wide<4>(p, m_tiles, stream);
 }
 
 }  // namespace moe

@@ -52,6 +52,8 @@ def _host(d):
     (4, 64, 256, 512, None),                   # one 64-row tile per expert
     (2, 130, 128, 256, [130, 65]),             # three row tiles, a partial last one
     (5, 16, 64, 128, [-1, 99, 16, 0, 3]),      # one k-block; counts clamped to [0, max_m]
+    (3, 200, 256, 1024, [200, 7, 130]),        # 256-row form, 128 columns per workgroup
+    (512, 65, 256, 512, None),                 # 256-row form, 256 columns per workgroup
 ])
 def test_fp8_small_matches_oracle(E, max_m, N, K, counts):
     d = make_fp8_inputs(Fp8Config("t", E, max_m, N, K, 0), DEV, seed=E + max_m)

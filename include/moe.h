@@ -242,7 +242,7 @@ int fused_moe_experts_stage(int stage, const uint16_t *hidden_states, const uint
  *              are no route weights: weighting and summing a token's rows belongs to the caller
  *              after the return exchange.
  *   E in 1..1024, max_m >= 0 (0: nothing is enqueued), H % 64 == 0, F % 64 == 0,
- *   E * max_m < 2^30.
+ *   E * max_m < 2^30; a, the weights, out and the workspace 16-byte aligned.
  * Workspace: fused_moe_masked_workspace_bytes(E, max_m, H, F) bytes (0 when nothing is to do).
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (E < 1, max_m < 0, H < 1 or F < 1),
  * MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH. */

@@ -6,6 +6,7 @@
 
 typedef __bf16 moe_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float moe_f32x4 __attribute__((ext_vector_type(4)));
+typedef float moe_f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t moe_u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t moe_u32x2 __attribute__((ext_vector_type(2)));
 
@@ -38,6 +39,15 @@ __device__ __forceinline__ uint32_t moe_pack_bf16x2(float lo, float hi)
 __device__ __forceinline__ moe_f32x4 moe_mfma_16x16x32(moe_u32x4 a, moe_u32x4 b, moe_f32x4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(moe_bf16x8, a),
+                                                   __builtin_bit_cast(moe_bf16x8, b), c, 0, 0, 0);
+}
+
+// D(32x32, f32) += A(32x16, bf16) * B(16x32, bf16) on one wave: twice the work of the 16x16x32
+// form in the same issue time on gfx950.  Lane l supplies A[l%32][8*(l/32) .. +8] and
+// B[8*(l/32) .. +8][l%32] and holds D[8*(r/4) + 4*(l/32) + r%4][l%32], r = 0..15.
+__device__ __forceinline__ moe_f32x16 moe_mfma_32x32x16(moe_u32x4 a, moe_u32x4 b, moe_f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(moe_bf16x8, a),
                                                    __builtin_bit_cast(moe_bf16x8, b), c, 0, 0, 0);
 }
 

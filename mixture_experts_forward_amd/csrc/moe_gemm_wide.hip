@@ -32,7 +32,7 @@ int device_cus()
 template <bool GATE_UP, int SRC>
 void launch_one(const GemmProblem &g, hipStream_t stream)
 {
-    const auto kernel = moe_wide::k_wide_gemm<GATE_UP, SRC, 64, 2>;
+    const auto kernel = moe_wide::k_wide_gemm<GATE_UP, SRC, 3>;
     const int cols = GATE_UP ? moe_wide::kBW / 2 : moe_wide::kBW;  // output columns per tile
     const int n_blocks = (g.n_out + cols - 1) / cols;
     const int m_tiles = g.num_groups;

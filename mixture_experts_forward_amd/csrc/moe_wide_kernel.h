@@ -6,30 +6,31 @@
 // one CU can hold:
 //   - a workgroup of 8 waves owns a 256-row tile and 256 weight rows (gate-up: 128 gate rows and
 //     the 128 up rows of the same columns); waves form a 4 x 2 grid, wave (wm, wn) computing the
-//     16-row tiles wm, wm+4, wm+8, wm+12 of the row tile against weight rows
-//     [128*wn, 128*wn + 128) -- 4 x 8 accumulators of v_mfma_f32_16x16x32_bf16;
-//   - both operand tiles of a 64-element k-step (256 rows x 128 B each, 64 KB) go from global
-//     memory straight into LDS with global_load_lds_dwordx4 -- each wave instruction covers
-//     8 whole 128-byte rows and no register holds them -- into the slot order
+//     32-row tiles wm and wm+4 of the row tile against weight rows [128*wn, 128*wn + 128) --
+//     2 x 4 accumulators of v_mfma_f32_32x32x16_bf16, which does twice the work of the
+//     16x16x32 form per issue slot on gfx950 (measured 2.25 vs 1.29 PFLOP/s);
+//   - each operand's 64-element k-step (256 rows x 128 B, 32 KB) goes from global memory
+//     straight into LDS with global_load_lds_dwordx4 -- each wave instruction covers 8 whole
+//     128-byte rows and no register holds them -- into the slot order
 //     slot(r, c) = 8r + (c ^ ((r >> 1) & 7)) that the MFMA operand reads take without bank
 //     conflicts: lane l of an instruction writes slot 8*(l/8) + l%8 of its 8 rows, so it
-//     fetches chunk (l%8) ^ swizzle(row) of its row (for 32-element k-steps: 4 slots per row,
-//     swizzle (r >> 1) & 3);
-//   - STAGES LDS stages of a KSTEP-element k-step; the launches use KSTEP = 64 with two
-//     stages (128 KB): the next k-step is in flight while the current one is multiplied, one
-//     barrier per k-step.  (32-element k-steps with three to five stages, more bytes in flight
-//     but twice the barriers, and register-staged loads instead of LDS DMA, all measured no
-//     faster on MI355X: the loads of one CU are bound by how many line requests it keeps in
-//     flight, not by the pipeline depth);
-//   - padding rows of an expert's segment form a suffix, so the 16-row tiles that hold only
+//     fetches chunk (l%8) ^ swizzle(row) of its row;
+//   - the operands run separate pipelines: the weight rows (from HBM) WS - 1 k-steps ahead in
+//     WS stages, the activation rows (mostly L2 hits: every column block of an expert reads
+//     them) one k-step ahead in two; WS = 3 fills the 160 KB of LDS and keeps two k-steps of
+//     weights in flight per CU.  One barrier per k-step;
+//   - padding rows of an expert's segment form a suffix, so the 32-row tiles that hold only
 //     padding are known from their first row: their loads and MFMAs are skipped, and the
-//     interleaved row-tile assignment spreads the real rows evenly over the four SIMDs.  MFMA
-//     work thus follows the routed rows, not the 256-row padding;
+//     interleaved row-tile assignment spreads the real rows over the four SIMDs.  MFMA work
+//     thus follows the routed rows, not the 256-row padding;
+//   - the bf16 output tile is staged in LDS (XOR-swizzled 16-byte chunks) and stored as whole
+//     rows;
 //   - tiles are numbered expert by expert (sorted rows) or row tiles of a column block
 //     consecutively (dense rows) and blocks are dealt round-robin to the 8 XCDs, each XCD
 //     taking a contiguous range of tile numbers; tiles sharing a weight or activation tile
-//     start their K loop at the same k-step, others at different ones (HBM channels).
-// A lane ends with four consecutive output columns of one row.
+//     start their K loop at the same k-step (they stay in step and share the lines in L2),
+//     others at different ones (HBM channels).
+// The shared pieces (Stage, dma16, wait_loads, the tile numbering) also serve moe_fp8_kernel.h.
 #pragma once
 
 #include <type_traits>
@@ -161,11 +162,25 @@ __device__ __forceinline__ int wide_real_rows(const GemmProblem &g, int row0)
     return lo;
 }
 
-template <bool GATE_UP, int SRC, int KSTEP, int STAGES>
+// The bf16 tile: 32 x 32 x 16 MFMAs (twice the work per issue of 16 x 16 x 32 on gfx950), a wave
+// computing 2 row tiles x 4 weight tiles of 32.
+constexpr int kMT32 = kBM / 32 / kWM;     // 32-row tiles per wave (2)
+constexpr int kNT32 = kBW / 32 / kWN;     // 32-row weight tiles per wave (4)
+constexpr int kStep = 64;                 // elements per k-step (128-byte rows)
+constexpr int kHalf = kBM * kStep * 2;    // LDS bytes of one operand's k-step (32 KB)
+// The weight rows come from HBM and the activation rows mostly from L2, so the two operands
+// run separate pipelines: activations one k-step ahead (two stages), weights WS - 1 k-steps
+// ahead (WS stages; WS = 3 takes all 160 KB of LDS).
+constexpr int kXStages = 2;
+template <int WS>
+constexpr int wide_lds_bytes() { return (kXStages + WS) * kHalf; }
+static_assert(kBM == kBW, "both operands' k-steps take kHalf bytes");
+
+template <bool GATE_UP, int SRC, int WS>
 __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mtile, int expert,
                                           moe_u32x4 *smem)
 {
-    using St = Stage<KSTEP>;
+    using St = Stage<kStep>;
     constexpr int kSlots = St::kSlots, kRows = St::kRowsPerLoad;
     constexpr int kXLoads = St::kXLoads, kWLoads = St::kWLoads;
     const int tid = threadIdx.x;
@@ -200,13 +215,11 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
     }
     const uint16_t *xsrc[kXLoads];
     bool xload[kXLoads];  // wave-uniform: the instruction's rows hold a real row
-    int n_loads = kWLoads;
 #pragma unroll
     for (int j = 0; j < kXLoads; ++j) {
         const int rfirst = wv * (kBM / kWaves) + kRows * j;
         const int r = rfirst + lrow;
         xload[j] = rfirst < n_real;
-        n_loads += xload[j] ? 1 : 0;
         int src = 0;  // padding rows of a loaded group read row 0 (never stored)
         if (r < n_real)
             src = SRC == moe::ROWS_SORTED
@@ -215,90 +228,98 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
         const int chunk = lpos ^ ((r >> 1) & (kSlots - 1));
         xsrc[j] = g.act + (size_t)src * K + 8 * chunk;
     }
-    // LDS byte addresses within a stage: activation rows first, then weight rows
+    // LDS byte addresses: the activation stages, then the weight stages
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-    const uint32_t x_dst = lds0 + wv * (kBM / kWaves) * (KSTEP * 2);
-    const uint32_t w_dst = lds0 + kBM * (KSTEP * 2) + wv * (kBW / kWaves) * (KSTEP * 2);
-    constexpr uint32_t kStageBytes = St::kBytes;
+    const uint32_t x_dst = lds0 + wv * (kBM / kWaves) * (kStep * 2);
+    const uint32_t w_dst = lds0 + kXStages * kHalf + wv * (kBW / kWaves) * (kStep * 2);
 
     // ---- operand rows of this wave
-    // weight tile n of wave wn: gate-up: n < kNT/2 -> gate rows 16*(kNT/2)*wn + 16*n of the gate
-    // half; n >= kNT/2 -> the matching up rows.  down: rows 16*kNT*wn + 16*n.
-    int wrow0[kNT];
+    // weight tile n of wave wn: gate-up: n < kNT32/2 -> gate rows 32*(kNT32/2)*wn + 32*n of the
+    // gate half; n >= kNT32/2 -> the matching up rows.  down: rows 32*kNT32*wn + 32*n.
+    int wrow0[kNT32];
 #pragma unroll
-    for (int n = 0; n < kNT; ++n) {
+    for (int n = 0; n < kNT32; ++n) {
         if (GATE_UP) {
-            const int hn = n % (kNT / 2);
-            const int base = 16 * (kNT / 2) * wn + 16 * hn;
-            wrow0[n] = (n < kNT / 2) ? base : kBW / 2 + base;
+            const int hn = n % (kNT32 / 2);
+            const int base = 32 * (kNT32 / 2) * wn + 32 * hn;
+            wrow0[n] = (n < kNT32 / 2) ? base : kBW / 2 + base;
         } else {
-            wrow0[n] = 16 * kNT * wn + 16 * n;
+            wrow0[n] = 32 * kNT32 * wn + 32 * n;
         }
     }
-    const int rr = lane & 15, rq = lane >> 4;
-    // real 16-row tiles of this wave: tiles wm + 4i for i < mt_real (wave-uniform)
+    const int rr = lane & 31, rq = lane >> 5;
+    // real 32-row tiles of this wave: tiles wm + 4i for i < mt_real (wave-uniform)
     int mt_real = 0;
 #pragma unroll
-    for (int i = 0; i < kMT; ++i)
-        mt_real += (16 * (wm + kWM * i) < n_real) ? 1 : 0;
+    for (int i = 0; i < kMT32; ++i)
+        mt_real += (32 * (wm + kWM * i) < n_real) ? 1 : 0;
 
-    const int nk = K / KSTEP;
+    const int nk = K / kStep;
     const unsigned rkey = SRC == moe::ROWS_SORTED ? expert : nblk;
     const int rot = (int)((rkey * 7u) % (unsigned)nk);
 
-    moe_f32x4 acc[kMT][kNT];
+    moe_f32x16 acc[kMT32][kNT32];
 #pragma unroll
-    for (int m = 0; m < kMT; ++m)
+    for (int m = 0; m < kMT32; ++m)
 #pragma unroll
-        for (int n = 0; n < kNT; ++n)
-            acc[m][n] = moe_f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int n = 0; n < kNT32; ++n)
+            acc[m][n] = moe_f32x16{};
 
-    auto issue = [&](int stage, int i) {
-        const int kb = ((i + rot) % nk) * KSTEP;  // element offset of the k-step
-        const uint32_t so = stage * kStageBytes;
+    auto issue_x = [&](int i) {
+        const int kb = ((i + rot) % nk) * kStep;  // element offset of k-step i
+        const uint32_t so = (i % kXStages) * kHalf;
 #pragma unroll
         for (int j = 0; j < kXLoads; ++j)
             if (xload[j])
                 dma16(xsrc[j] + kb, x_dst + so + j * 1024);
+    };
+    auto issue_w = [&](int i) {
+        const int kb = ((i + rot) % nk) * kStep;
+        const uint32_t so = (i % WS) * kHalf;
 #pragma unroll
         for (int j = 0; j < kWLoads; ++j)
             dma16(wsrc[j] + kb, w_dst + so + j * 1024);
     };
 
-    // Pipeline: stage i % STAGES holds k-step i; k-steps i .. i+STAGES-2 are in flight at the
-    // top of step i.  Waiting until only the later ones (n_loads each) are outstanding leaves
-    // this wave's part of k-step i in LDS; the barrier then publishes every wave's part and
-    // also guarantees that every wave has finished reading stage (i-1) % STAGES in step i-1,
-    // so k-step i+STAGES-1 can be loaded into it while k-step i is multiplied.  The loop is
-    // instantiated per count MTR of real 16-row tiles of this wave, so the MFMA block has no
+    // Pipeline, A = WS - 1 weight k-steps ahead.  Issue order: x(0) w(0) .. w(A-1), then in step
+    // i x(i+1) w(i+A).  At the top of step i this wave's outstanding loads are therefore (oldest
+    // first) ... x(i) w(i+1) .. w(i+A-1): waiting until only those weight steps are left leaves
+    // its parts of x(i) and w(i) in LDS, and the barrier publishes every wave's parts.  The
+    // barrier also guarantees that every wave has finished step i-1, whose stages x(i+1) and
+    // w(i+A) then overwrite.  The loop is
+    // instantiated per count MTR of real 32-row tiles of this wave, so the MFMA block has no
     // branches (a wave with none still loads its share and meets every barrier).
     auto k_loop = [&](auto mtr) {
         constexpr int MTR = decltype(mtr)::value;
+        constexpr int A = WS - 1;
+        issue_x(0);
 #pragma unroll
-        for (int s = 0; s < STAGES - 1; ++s)
+        for (int s = 0; s < A; ++s)
             if (s < nk)
-                issue(s, s);
+                issue_w(s);
         for (int i = 0; i < nk; ++i) {
-            wait_loads(min(STAGES - 2, nk - 1 - i) * n_loads);
+            wait_loads(min(A - 1, nk - 1 - i) * kWLoads);
             __syncthreads();
-            if (i + STAGES - 1 < nk)
-                issue((i + STAGES - 1) % STAGES, i + STAGES - 1);
+            if (i + 1 < nk)
+                issue_x(i + 1);
+            if (i + A < nk)
+                issue_w(i + A);
             if (MTR == 0)
                 continue;
-            const moe_u32x4 *xb = smem + (i % STAGES) * (kStageBytes / 16);
-            const moe_u32x4 *wb = xb + kBM * kSlots;
+            const moe_u32x4 *xb = smem + (i % kXStages) * (kHalf / 16);
+            const moe_u32x4 *wb = smem + (kXStages + i % WS) * (kHalf / 16);
 #pragma unroll
-            for (int h = 0; h < KSTEP / 32; ++h) {
+            for (int h = 0; h < kStep / 16; ++h) {
                 moe_u32x4 b[MTR > 0 ? MTR : 1];
 #pragma unroll
                 for (int m = 0; m < MTR; ++m)
-                    b[m] = xb[St::slot(16 * (wm + kWM * m) + rr, rq + 4 * h)];
+                    b[m] = xb[St::slot(32 * (wm + kWM * m) + rr, 2 * h + rq)];
 #pragma unroll
-                for (int n = 0; n < kNT; ++n) {
-                    const moe_u32x4 a = wb[St::slot(wrow0[n] + rr, rq + 4 * h)];
+                for (int n = 0; n < kNT32; ++n) {
+                    const moe_u32x4 a = wb[St::slot(wrow0[n] + rr, 2 * h + rq)];
 #pragma unroll
                     for (int m = 0; m < MTR; ++m)
-                        acc[m][n] = moe_mfma_16x16x32(a, b[m], acc[m][n]);
+                        acc[m][n] = moe_mfma_32x32x16(a, b[m], acc[m][n]);
                 }
             }
         }
@@ -306,54 +327,70 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
     switch (mt_real) {
     case 0: k_loop(std::integral_constant<int, 0>()); break;
     case 1: k_loop(std::integral_constant<int, 1>()); break;
-    case 2: k_loop(std::integral_constant<int, 2>()); break;
-    case 3: k_loop(std::integral_constant<int, 3>()); break;
-    default: k_loop(std::integral_constant<int, 4>()); break;
+    default: k_loop(std::integral_constant<int, 2>()); break;
     }
 
-    // ---- epilogue: lane holds columns 4*(lane/16)+q of row 16*(wm + 4m) + lane%16
+    // ---- epilogue.  For weight tile n, register 4q' + q holds column 8q' + 4*(lane/32) + q of
+    // the tile, row 32*(wm + 4m) + lane%32.  The bf16 tile (kBM rows x TC columns) goes through
+    // LDS so that global stores write whole rows: 16-byte chunk c of row r sits at chunk
+    // position c ^ (r % CPR) of the row (the 8-byte writes of 32 rows at one column then
+    // spread over the banks; the 16-byte reads of one row stay conflict-free).
+    constexpr int TC = GATE_UP ? kBW / 2 : kBW;  // output columns of the tile
+    constexpr int CPR = TC / 8;                  // 16-byte chunks per row
+    static_assert(kBM * TC * 2 <= wide_lds_bytes<2>(), "output tile fits in LDS");
+    __syncthreads();  // every wave is done with the last k-step's operands
+    uint16_t *otile = reinterpret_cast<uint16_t *>(smem);
+    auto opos = [](int r, int c) { return r * CPR + (c ^ (r & (CPR - 1))); };
 #pragma unroll
-    for (int m = 0; m < kMT; ++m) {
+    for (int m = 0; m < kMT32; ++m) {
         if (m >= mt_real)
             continue;
-        const int r = 16 * (wm + kWM * m) + rr;
-        if (r >= n_real)
-            continue;
-        const int dst = SRC == moe::ROWS_SORTED
-                            ? (GATE_UP ? row0 + r : g.sorted_ids[row0 + r])
-                            : row0 + r;
-        uint16_t *orow = g.out + (size_t)dst * g.n_out;
-        constexpr int NOUT = GATE_UP ? kNT / 2 : kNT;
+        const int r = 32 * (wm + kWM * m) + rr;
+        constexpr int NOUT = GATE_UP ? kNT32 / 2 : kNT32;
 #pragma unroll
         for (int n = 0; n < NOUT; ++n) {
-            const int col = GATE_UP ? col_wg + 16 * (kNT / 2) * wn + 16 * n
-                                    : col_wg + 16 * kNT * wn + 16 * n;
-            if (col >= g.n_out)
-                continue;
-            float v[4];
+            const int lc0 = (GATE_UP ? 32 * (kNT32 / 2) * wn : 32 * kNT32 * wn) + 32 * n;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if (GATE_UP) {
-                    const float gate = acc[m][n][q];
-                    const float up = acc[m][n + kNT / 2][q];
-                    v[q] = gate / (1.0f + __expf(-gate)) * up;
-                } else {
-                    v[q] = acc[m][n][q];
+            for (int q4 = 0; q4 < 4; ++q4) {
+                float v[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (GATE_UP) {
+                        const float gate = acc[m][n][4 * q4 + q];
+                        const float up = acc[m][n + kNT32 / 2][4 * q4 + q];
+                        v[q] = gate / (1.0f + __expf(-gate)) * up;
+                    } else {
+                        v[q] = acc[m][n][4 * q4 + q];
+                    }
                 }
+                moe_u32x2 packed;
+                packed.x = moe_pack_bf16x2(v[0], v[1]);
+                packed.y = moe_pack_bf16x2(v[2], v[3]);
+                const int lc = lc0 + 8 * q4;  // first column of the 16-byte chunk
+                *reinterpret_cast<moe_u32x2 *>(otile + 8 * opos(r, lc / 8) + 4 * rq) = packed;
             }
-            moe_u32x2 packed;
-            packed.x = moe_pack_bf16x2(v[0], v[1]);
-            packed.y = moe_pack_bf16x2(v[2], v[3]);
-            *reinterpret_cast<moe_u32x2 *>(orow + col + 4 * rq) = packed;
+        }
+    }
+    __syncthreads();
+    // thread t stores chunk t % CPR of rows t / CPR, t / CPR + kThreads / CPR, ...
+    const int oc = tid % CPR;
+    const int col = col_wg + 8 * oc;
+    if (col < g.n_out) {
+        for (int r = tid / CPR; r < n_real; r += kThreads / CPR) {
+            const int dst = SRC == moe::ROWS_SORTED
+                                ? (GATE_UP ? row0 + r : g.sorted_ids[row0 + r])
+                                : row0 + r;
+            *reinterpret_cast<moe_u32x4 *>(g.out + (size_t)dst * g.n_out + col) =
+                *reinterpret_cast<const moe_u32x4 *>(otile + 8 * opos(r, oc));
         }
     }
 }
 
 // Round r hands XCD x the tiles [r*W + x*W/8, r*W + (x+1)*W/8), W = the slots in use.
-template <bool GATE_UP, int SRC, int KSTEP, int STAGES>
+template <bool GATE_UP, int SRC, int WS>
 __global__ __launch_bounds__(kThreads) void k_wide_gemm(GemmProblem g, int n_blocks, int m_tiles)
 {
-    __shared__ moe_u32x4 smem[STAGES * Stage<KSTEP>::kBytes / 16];
+    __shared__ moe_u32x4 smem[wide_lds_bytes<WS>() / 16];
 
     const int total = wide_total<SRC>(g, n_blocks, m_tiles);
     const int W = min((int)gridDim.x, (total + kXcds - 1) / kXcds * kXcds);
@@ -364,7 +401,7 @@ __global__ __launch_bounds__(kThreads) void k_wide_gemm(GemmProblem g, int n_blo
     for (int t = (blockIdx.x % kXcds) * per + idx; t < total; t += W) {
         int nblk, mtile, expert;
         wide_decode<SRC>(g, t, n_blocks, m_tiles, nblk, mtile, expert);
-        wide_tile<GATE_UP, SRC, KSTEP, STAGES>(g, nblk, mtile, expert, smem);
+        wide_tile<GATE_UP, SRC, WS>(g, nblk, mtile, expert, smem);
         __syncthreads();  // the next tile's first loads follow every wave's last reads
     }
 }

@@ -252,9 +252,15 @@ def main():
                                              cfg.S, cfg.bias)
     pass_flops = perfmodel.flops(cfg.T, cfg.k, cfg.H, cfg.F, cfg.S)
     gu_bytes = touched_mean * 4.0 * cfg.H * cfg.F + 2.0 * cfg.T * cfg.H + 2.0 * P * cfg.F
+    gu_flops = 2.0 * P * 2 * cfg.F * cfg.H
     gu_ms = per_stage["gate_up"]
     gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
+    gu_tflops = gu_flops / (gu_ms * 1e-3) / 1e12
     peak_gbs = perfmodel.HBM_PEAK_BYTES_PER_S / 1e9
+    peak_tflops = perfmodel.BF16_MFMA_PEAK_FLOP_PER_S / 1e12
+    # the gate-up kernel's own bound: its bytes at 8 TB/s or its FLOPs at the bf16 MFMA peak
+    gu_mfma_bound = gu_flops / perfmodel.BF16_MFMA_PEAK_FLOP_PER_S > \
+        gu_bytes / perfmodel.HBM_PEAK_BYTES_PER_S
     traffic = read_traffic(cfg.name)
 
     # ---- CPU baseline: the oracle on this host
@@ -299,10 +305,16 @@ def main():
         "warm_ms_per_step": round(warm_ms, 5),
         "staged_ms_per_step": round(staged_ms, 5),
         "stage_ms": {k: round(v, 5) for k, v in per_stage.items()},
-        "roofline": {"kernel": "gate-up GEMM of the routed experts", "bound": "hbm",
-                     "achieved": round(gu_gbs, 1), "peak": peak_gbs, "unit": "GB/s",
-                     "frac": round(gu_gbs / peak_gbs, 4), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": gu_bytes},
+        "roofline": ({"kernel": "gate-up GEMM of the routed experts", "bound": "mfma",
+                      "achieved": round(gu_tflops, 1), "peak": peak_tflops, "unit": "TFLOP/s",
+                      "frac": round(gu_tflops / peak_tflops, 4), "traffic": traffic,
+                      "algorithmic_flops_per_launch": gu_flops,
+                      "algorithmic_bytes_per_launch": gu_bytes}
+                     if gu_mfma_bound else
+                     {"kernel": "gate-up GEMM of the routed experts", "bound": "hbm",
+                      "achieved": round(gu_gbs, 1), "peak": peak_gbs, "unit": "GB/s",
+                      "frac": round(gu_gbs / peak_gbs, 4), "traffic": traffic,
+                      "algorithmic_bytes_per_launch": gu_bytes}),
         "cpu_baseline": cpu,
         "baseline_context": base,
         "context": ctx,

@@ -117,6 +117,30 @@ __device__ __forceinline__ void wait_loads(int n)
 #undef MOE_WAIT_CASE
 }
 
+// Workgroup barrier of a k-loop whose stages are filled by dma16: waits until at most n
+// (0 <= n <= 63) of this wave's vector-memory loads are outstanding and its LDS reads are
+// done, then s_barrier.  After it every wave's DMA of the awaited k-steps has landed in LDS and
+// every wave has finished reading the previous stage.  __syncthreads() is not used here: its
+// release fence also waits for every outstanding load (vmcnt(0)), which would drain the loads
+// of later k-steps at each step.  The "memory" clobber keeps LDS accesses on their side.
+__device__ __forceinline__ void step_barrier(int n)
+{
+#define MOE_BAR_CASE(N)                                                                          \
+    case N:                                                                                      \
+        asm volatile("s_waitcnt vmcnt(" #N ") lgkmcnt(0)\n\ts_barrier" ::: "memory");          \
+        break;
+    switch (n) {
+        MOE_BAR_CASE(1) MOE_BAR_CASE(2) MOE_BAR_CASE(3) MOE_BAR_CASE(4) MOE_BAR_CASE(5)
+        MOE_BAR_CASE(6) MOE_BAR_CASE(7) MOE_BAR_CASE(8) MOE_BAR_CASE(9) MOE_BAR_CASE(10)
+        MOE_BAR_CASE(11) MOE_BAR_CASE(12) MOE_BAR_CASE(13) MOE_BAR_CASE(14) MOE_BAR_CASE(15)
+        MOE_BAR_CASE(16)
+    default:
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        break;
+    }
+#undef MOE_BAR_CASE
+}
+
 template <int SRC>
 __device__ __forceinline__ int wide_total(const GemmProblem &g, int n_blocks, int m_tiles)
 {
@@ -298,8 +322,7 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
             if (s < nk)
                 issue_w(s);
         for (int i = 0; i < nk; ++i) {
-            wait_loads(min(A - 1, nk - 1 - i) * kWLoads);
-            __syncthreads();
+            step_barrier(min(A - 1, nk - 1 - i) * kWLoads);
             if (i + 1 < nk)
                 issue_x(i + 1);
             if (i + A < nk)
@@ -308,19 +331,29 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
                 continue;
             const moe_u32x4 *xb = smem + (i % kXStages) * (kHalf / 16);
             const moe_u32x4 *wb = smem + (kXStages + i % WS) * (kHalf / 16);
-#pragma unroll
-            for (int h = 0; h < kStep / 16; ++h) {
-                moe_u32x4 b[MTR > 0 ? MTR : 1];
+            // operands of 16-element sub-step h; those of h + 1 are read while the MFMAs of h
+            // run, so the LDS latency hides behind 8 MFMAs instead of stalling them
+            moe_u32x4 a[2][kNT32], b[2][MTR > 0 ? MTR : 1];
+            auto read = [&](int buf, int h) {
 #pragma unroll
                 for (int m = 0; m < MTR; ++m)
-                    b[m] = xb[St::slot(32 * (wm + kWM * m) + rr, 2 * h + rq)];
+                    b[buf][m] = xb[St::slot(32 * (wm + kWM * m) + rr, 2 * h + rq)];
 #pragma unroll
-                for (int n = 0; n < kNT32; ++n) {
-                    const moe_u32x4 a = wb[St::slot(wrow0[n] + rr, 2 * h + rq)];
+                for (int n = 0; n < kNT32; ++n)
+                    a[buf][n] = wb[St::slot(wrow0[n] + rr, 2 * h + rq)];
+            };
+            read(0, 0);
+#pragma unroll
+            for (int h = 0; h < kStep / 16; ++h) {
+                if (h + 1 < kStep / 16)
+                    read((h + 1) & 1, h + 1);
+                __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of these MFMAs
+#pragma unroll
+                for (int n = 0; n < kNT32; ++n)
 #pragma unroll
                     for (int m = 0; m < MTR; ++m)
-                        acc[m][n] = moe_mfma_32x32x16(a, b[m], acc[m][n]);
-                }
+                        acc[m][n] = moe_mfma_32x32x16(a[h & 1][n], b[h & 1][m], acc[m][n]);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     };

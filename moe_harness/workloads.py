@@ -66,6 +66,12 @@ CONFIGS = {
                                        topk_group=4, rsf=2.5, bias=True),
     "kimi-k2-shared": MoEConfig("kimi-k2-shared", T=512, H=7168, E=384, F=2048, k=8,
                                 scoring="sigmoid", rsf=2.827, bias=True, S=18432),
+    # DeepSeek-V3 routing and dimensions at 16384 tokens: about 500 routed rows per expert, so
+    # about 500 FLOP per weight byte, above the MI355X ridge (2.5 PFLOP/s / 8 TB/s = 312): the
+    # expert GEMMs are MFMA-bound here, unlike at 4096 tokens
+    "ds-v3-prefill-16k": MoEConfig("ds-v3-prefill-16k", T=16384, H=7168, E=256, F=2048, k=8,
+                                   scoring="sigmoid", num_expert_group=8, topk_group=4,
+                                   rsf=2.5, bias=True),
 }
 
 

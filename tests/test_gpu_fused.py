@@ -82,6 +82,15 @@ def test_ds_v3_grouped_prefill_sampled():
 
 
 @pytest.mark.slow
+def test_ds_v3_prefill_16k_sampled():
+    cfg = CONFIGS["ds-v3-prefill-16k"]
+    d = make_inputs(cfg, DEV)
+    _check_pass(cfg, d, "auto", sample_tokens(cfg.T, 8), cfg.name)
+    del d
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.slow
 def test_kimi_k2_shared_sampled():
     cfg = CONFIGS["kimi-k2-shared"]
     d = make_inputs(cfg, DEV)

@@ -15,7 +15,10 @@ Functions (each follows the passage cited in ``moe_oracle.c``):
   forward(...) = route + experts, the whole pass
   masked_mlp(a, masked_m, w_gate_up, w_down) -> (acc float64 [E,max_m,H], out uint16 [E,max_m,H])
   fp8_e4m3_decode(codes) -> float64 values of OCP e4m3 codes
+  fp8_e4m3_encode(values) -> uint8 codes (nearest, ties to even, saturating at 448)
+  quant_fp8_1x128(x) -> (codes uint8 [M,K], scales float32 [M,ceil(K/128)])
   grouped_gemm_fp8(a, a_scale, b, b_scale, masked_m) -> (acc float64 [E,max_m,N], out uint16)
+  grouped_gemm_fp8_contiguous(a, a_scale, b, b_scale, offsets) -> (acc [P,N], out uint16 [P,N])
   double_to_bf16(values) -> uint16 (one rounding, nearest-even)
 """
 import ctypes
@@ -54,6 +57,10 @@ def _load():
     lib.oracle_fp8_e4m3_to_double.argtypes = [ctypes.c_uint8]
     lib.oracle_fp8_e4m3_to_double.restype = ctypes.c_double
     lib.oracle_grouped_gemm_fp8.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P]
+    lib.oracle_fp8_e4m3_encode.restype = ctypes.c_uint8
+    lib.oracle_fp8_e4m3_encode.argtypes = [ctypes.c_double]
+    lib.oracle_quant_fp8_1x128.argtypes = [_P, _I, _I, _P, _P]
+    lib.oracle_grouped_gemm_fp8_contig.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P]
     lib.oracle_grouped_gemm_fp8.restype = _I
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = _I
@@ -203,6 +210,49 @@ def grouped_gemm_fp8(a, a_scale, b, b_scale, masked_m):
                                          max_m, N, K, _ptr(out), _ptr(acc))
     if rc != 0:
         raise ValueError("oracle_grouped_gemm_fp8 rejected its arguments (%d)" % rc)
+    return acc, out
+
+
+def fp8_e4m3_encode(values):
+    """float values -> OCP e4m3 codes (uint8): nearest finite value, ties to the even code,
+    saturating at +-448; one call per value into the C encoder."""
+    v = np.asarray(values, dtype=np.float64)
+    f = _load().oracle_fp8_e4m3_encode
+    return np.array([f(float(x)) for x in v.ravel()], dtype=np.uint8).reshape(v.shape)
+
+
+def quant_fp8_1x128(x):
+    """bf16 activations (uint16 bits [M,K]) -> (e4m3 codes uint8 [M,K], f32 scales
+    [M,ceil(K/128)]): per 1 x 128 group s = fl32(amax / 448) (1 for an all-zero group), code =
+    the e4m3 nearest to fl32(x / s)."""
+    x = _c(x, np.uint16)
+    M, K = x.shape
+    q = np.zeros((M, K), dtype=np.uint8)
+    s = np.zeros((M, (K + 127) // 128), dtype=np.float32)
+    rc = _load().oracle_quant_fp8_1x128(_ptr(x), M, K, _ptr(q), _ptr(s))
+    if rc != 0:
+        raise ValueError("oracle_quant_fp8_1x128 rejected its arguments (%d)" % rc)
+    return q, s
+
+
+def grouped_gemm_fp8_contiguous(a, a_scale, b, b_scale, offsets):
+    """The block-scaled FP8 grouped GEMM on the contiguous layout: a uint8 [P,K] e4m3 with
+    a_scale float32 [P,K/128]; b uint8 [E,N,K] e4m3 with b_scale float32 [E,N/128,K/128];
+    offsets int32 [E+1], expert e owning rows [offsets[e], offsets[e+1]).  Rows outside every
+    range are 0 in the result."""
+    a = _c(a, np.uint8)
+    b = _c(b, np.uint8)
+    sa = _c(a_scale, np.float32)
+    sb = _c(b_scale, np.float32)
+    off = _c(offsets, np.int32)
+    P, K = a.shape
+    E, N = b.shape[0], b.shape[1]
+    out = np.zeros((P, N), dtype=np.uint16)
+    acc = np.zeros((P, N), dtype=np.float64)
+    rc = _load().oracle_grouped_gemm_fp8_contig(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(off),
+                                                E, P, N, K, _ptr(out), _ptr(acc))
+    if rc != 0:
+        raise ValueError("oracle_grouped_gemm_fp8_contig rejected its arguments (%d)" % rc)
     return acc, out
 
 

@@ -12,12 +12,15 @@
  *   align     stable counting sort of the routes by expert, each expert padded to block_m rows
  *   experts   out[t] = RNE_bf16( sum_j w[t,j] * SwiGLU_{id[t,j]}(x[t]) + SharedSwiGLU(x[t]) )
  *   fp8 grouped GEMM (MoEGroupedGemmFP8Fwd, masked layout, e4m3 operands with f32 scales per
- *             1 x 128 activation block and per 128 x 128 weight block)
+ *             1 x 128 activation block and per 128 x 128 weight block; and the same GEMM on
+ *             the contiguous layout of the page's bf16 grouped GEMMs)
+ *   fp8 quant bf16 activations -> e4m3 codes with one f32 scale per 1 x 128 group
  *
  * Precision: every floating-point quantity is double; results are rounded exactly once at the
  * end (route weights to f32, outputs to bf16 with round-to-nearest-even).  The only f32
- * arithmetic is the selection key of sigmoid scoring (score rounded to f32 plus the f32 bias),
- * which is where the selection is defined in f32 on both sides.
+ * arithmetic is the selection key of sigmoid scoring (score rounded to f32 plus the f32 bias)
+ * and the two divisions of the fp8 quantiser (group scale and quotient), which is where those
+ * integer decisions are defined in f32 on both sides.
  *
  * Readings of the pages that this file adopts where they are silent are listed in the
  * comments of the function that applies them.
@@ -438,6 +441,105 @@ int oracle_grouped_gemm_fp8(const uint8_t *a, const float *a_scale, const uint8_
             out[o] = oracle_double_to_bf16(total);
             if (acc_out)
                 acc_out[o] = total;
+        }
+    }
+    return 0;
+}
+
+/* double -> OCP e4m3 code: the finite e4m3 value nearest to v, ties to the code with an even
+ * mantissa (round to nearest even), magnitudes beyond the largest finite value 448 saturate to
+ * it (the format has no infinity; its one NaN pattern per sign is never produced).  Written from
+ * the definition: the 127 non-negative finite codes are scanned for the nearest value.  NaN in
+ * gives the NaN code 0x7F.  The sign of v (also of -0.0) is kept. */
+uint8_t oracle_fp8_e4m3_encode(double v)
+{
+    if (v != v)
+        return 0x7F;
+    const int neg = signbit(v) ? 1 : 0;
+    const double a = fabs(v);
+    int best = 0;
+    double best_d = INFINITY;
+    for (int c = 0; c <= 0x7E; ++c) {
+        const double d = fabs(oracle_fp8_e4m3_to_double((uint8_t)c) - a);
+        /* strictly nearer, or as near and even (codes ascend with value, so a tie is between c-1
+         * and c, and the even one of the two wins) */
+        if (d < best_d || (d == best_d && (c & 1) == 0)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return (uint8_t)(best | (neg << 7));
+}
+
+/* Per-token 1 x 128 group quantisation of bf16 activations to e4m3 with one f32 scale per group
+ * (the a / a_scale pair of TileOPs "MoE" page, MoEGroupedGemmFP8Fwd: a_scale
+ * [..., ceil_div(K, 128)] f32).  The pages give the scale's shape, not its rule; reading: the
+ * group's scale is s = fl32(amax / 448) with amax the largest |x| of the group (s = 1 for an
+ * all-zero group), and each value's code is the e4m3 nearest to fl32(x / s) (both divisions in
+ * f32, as a quantised code is decided in the kernel's precision).  x [M, K] bf16 bits,
+ * q [M, K] codes, scale [M, ceil(K / 128)]; the last group of a row may be partial. */
+int oracle_quant_fp8_1x128(const uint16_t *x, int M, int K, uint8_t *q, float *scale)
+{
+    if (M < 0 || K < 1)
+        return -1;
+    const int G = (K + 127) / 128;
+    for (int r = 0; r < M; ++r) {
+        for (int g = 0; g < G; ++g) {
+            const int k0 = 128 * g, k1 = k0 + 128 < K ? k0 + 128 : K;
+            float amax = 0.0f;
+            for (int k = k0; k < k1; ++k) {
+                const float v = fabsf((float)bf16_to_double(x[(size_t)r * K + k]));
+                amax = v > amax ? v : amax;
+            }
+            volatile float s = amax / 448.0f;
+            if (amax == 0.0f)
+                s = 1.0f;
+            scale[(size_t)r * G + g] = s;
+            for (int k = k0; k < k1; ++k) {
+                volatile float t = (float)bf16_to_double(x[(size_t)r * K + k]) / s;
+                q[(size_t)r * K + k] = oracle_fp8_e4m3_encode((double)t);
+            }
+        }
+    }
+    return 0;
+}
+
+/* The same block-scaled grouped GEMM on the contiguous layout (TileOPs "MoE" page,
+ * layout=contiguous(packing=tight, metadata_kind=physical_psum)): the rows of all experts are
+ * stacked in a [P, K], expert e owning rows [offsets[e], offsets[e+1]) (offsets [E+1], the
+ * prefix sums of the rows per expert); a_scale [P, ceil(K/128)] f32.  Row r of expert e:
+ *   out[r, n] = RNE_bf16( sum_kb a_scale[r, kb] * b_scale[e, n / 128, kb]
+ *                         * sum_{k in block kb} a[r, k] * b[e, n, k] ).
+ * Rows outside every expert's range are left as they are.  Everything in double. */
+int oracle_grouped_gemm_fp8_contig(const uint8_t *a, const float *a_scale, const uint8_t *b,
+                                   const float *b_scale, const int32_t *offsets, int E, int P,
+                                   int N, int K, uint16_t *out, double *acc_out)
+{
+    if (E < 1 || P < 0 || N < 1 || K < 1)
+        return -1;
+    const int KB = (K + 127) / 128, NB = (N + 127) / 128;
+    for (int e = 0; e < E; ++e) {
+        int r0 = offsets[e], r1 = offsets[e + 1];
+        r0 = r0 < 0 ? 0 : (r0 > P ? P : r0);
+        r1 = r1 < r0 ? r0 : (r1 > P ? P : r1);
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic)
+#endif
+        for (int rn = 0; rn < (r1 - r0) * N; ++rn) {
+            const int r = r0 + rn / N, n = rn % N;
+            const uint8_t *ar = a + (size_t)r * K;
+            const uint8_t *br = b + ((size_t)e * N + n) * K;
+            double total = 0.0;
+            for (int kb = 0; kb < KB; ++kb) {
+                double block = 0.0;
+                for (int k = kb * 128; k < K && k < kb * 128 + 128; ++k)
+                    block += oracle_fp8_e4m3_to_double(ar[k]) * oracle_fp8_e4m3_to_double(br[k]);
+                total += (double)a_scale[(size_t)r * KB + kb] *
+                         (double)b_scale[((size_t)e * NB + n / 128) * KB + kb] * block;
+            }
+            out[(size_t)r * N + n] = oracle_double_to_bf16(total);
+            if (acc_out)
+                acc_out[(size_t)r * N + n] = total;
         }
     }
     return 0;

@@ -14,6 +14,8 @@ Entry points (same names as the C ABI):
   fused_moe_experts_fwd(hidden_states, w_gate_up, w_down, topk_ids, topk_weights) -> out
   fused_moe_masked_fwd(a, masked_m, w_gate_up, w_down)        -> out [E, max_m, H]
   moe_grouped_gemm_fp8(a, a_scale, b, b_scale, masked_m)      -> out [E, max_m, N] bf16
+  moe_grouped_gemm_fp8_contiguous(a, a_scale, b, b_scale, expert_offsets) -> out [P, N] bf16
+  moe_quant_fp8(x)                                            -> (q [M, K] e4m3, scale [M, K/128])
 """
 import ctypes
 import os
@@ -70,6 +72,9 @@ SIGNATURES = {
                                               _I32, _P, _P, _SZ, _P]),
     "moe_grouped_gemm_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P,
                                             _P]),
+    "moe_grouped_gemm_fp8_contiguous": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32,
+                                                       _I32, _P, _P]),
+    "moe_quant_fp8": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _P]),
 }
 
 # stages of fused_moe_experts_stage, in the order fused_moe_experts_fwd runs them
@@ -368,3 +373,49 @@ def moe_grouped_gemm_fp8(a, a_scale, b, b_scale, masked_m, out=None):
     if st != MOE_OK:
         raise MoEError(st, "moe_grouped_gemm_fp8")
     return out
+
+
+def moe_grouped_gemm_fp8_contiguous(a, a_scale, b, b_scale, expert_offsets, out=None):
+    """Block-scaled FP8 grouped GEMM of the contiguous layout: a [P,K] e4m3 (torch.float8_e4m3fn
+    or uint8 codes) with a_scale [P,K/128] f32, b [E,N,K] e4m3 with b_scale [E,ceil(N/128),K/128]
+    f32, expert_offsets [E+1] int32 (expert e owns rows [offsets[e], offsets[e+1])) -> out [P,N]
+    bf16 (rows of no expert left as they are; zeros when out is allocated here)."""
+    P, K = a.shape
+    E, N = b.shape[0], b.shape[1]
+    dev = a.device
+    codes = lambda t: t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t
+    a8, b8 = codes(a), codes(b)
+    _check(a8, "a", torch.uint8, (P, K))
+    _check(b8, "b", torch.uint8, (E, N, K), dev)
+    _check(a_scale, "a_scale", torch.float32, (P, (K + 127) // 128), dev)
+    _check(b_scale, "b_scale", torch.float32, (E, (N + 127) // 128, (K + 127) // 128), dev)
+    _check(expert_offsets, "expert_offsets", torch.int32, (E + 1,), dev)
+    if out is None:
+        out = torch.zeros((P, N), dtype=torch.bfloat16, device=dev)
+    _check(out, "out", torch.bfloat16, (P, N), dev)
+    with torch.cuda.device(dev):
+        st = lib().moe_grouped_gemm_fp8_contiguous(_ptr(a8), _ptr(a_scale), _ptr(b8),
+                                                   _ptr(b_scale), _ptr(expert_offsets), E, P, N,
+                                                   K, _ptr(out), _stream(dev))
+    if st != MOE_OK:
+        raise MoEError(st, "moe_grouped_gemm_fp8_contiguous")
+    return out
+
+
+def moe_quant_fp8(x, q=None, scale=None):
+    """bf16 x [M,K] -> (q [M,K] uint8 e4m3 codes, scale [M,ceil(K/128)] f32): per 1 x 128 group
+    scale = amax / 448 (1 for an all-zero group), codes nearest to x / scale, ties to even."""
+    M, K = x.shape
+    dev = x.device
+    _check(x, "x", torch.bfloat16, (M, K))
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = torch.empty((M, (K + 127) // 128), dtype=torch.float32, device=dev)
+    _check(q, "q", torch.uint8, (M, K), dev)
+    _check(scale, "scale", torch.float32, (M, (K + 127) // 128), dev)
+    with torch.cuda.device(dev):
+        st = lib().moe_quant_fp8(_ptr(x), M, K, _ptr(q), _ptr(scale), _stream(dev))
+    if st != MOE_OK:
+        raise MoEError(st, "moe_quant_fp8")
+    return q, scale

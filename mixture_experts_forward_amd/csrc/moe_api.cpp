@@ -506,4 +506,43 @@ int moe_grouped_gemm_fp8(const uint8_t *a, const float *a_scale, const uint8_t *
     return launch_status();
 }
 
+int moe_grouped_gemm_fp8_contiguous(const uint8_t *a, const float *a_scale, const uint8_t *b,
+                                    const float *b_scale, const int32_t *expert_offsets,
+                                    int32_t E, int32_t P, int32_t N, int32_t K, uint16_t *out,
+                                    void *stream)
+{
+    if (E < 1 || P < 0 || N < 1 || K < 1)
+        return MOE_ERR_SHAPE;
+    if (N % 64 != 0 || K % 128 != 0 || E > 1024 || P >= (1 << 30) ||
+        (int64_t)E * N >= (1ll << 30))
+        return MOE_ERR_UNSUPPORTED;
+    if (P == 0)
+        return MOE_OK;
+    if (!a || !a_scale || !b || !b_scale || !expert_offsets || !out)
+        return MOE_ERR_NULL;
+    if (!aligned16(a) || !aligned16(b) || !aligned16(out) || ((uintptr_t)a_scale & 3u) ||
+        ((uintptr_t)b_scale & 3u) || ((uintptr_t)expert_offsets & 3u))
+        return MOE_ERR_UNSUPPORTED;
+    moe::launch_fp8_gemm_contig(a, a_scale, b, b_scale, expert_offsets, E, P, N, K, out,
+                                static_cast<hipStream_t>(stream));
+    return launch_status();
+}
+
+int moe_quant_fp8(const uint16_t *x, int32_t M, int32_t K, uint8_t *q, float *scale,
+                  void *stream)
+{
+    if (M < 0 || K < 1)
+        return MOE_ERR_SHAPE;
+    if (K % 8 != 0 || (int64_t)M * ((K + 127) / 128) >= (1ll << 34))
+        return MOE_ERR_UNSUPPORTED;
+    if (M == 0)
+        return MOE_OK;
+    if (!x || !q || !scale)
+        return MOE_ERR_NULL;
+    if (!aligned16(x) || ((uintptr_t)q & 7u) || ((uintptr_t)scale & 3u))
+        return MOE_ERR_UNSUPPORTED;
+    moe::launch_quant_fp8(x, M, K, q, scale, static_cast<hipStream_t>(stream));
+    return launch_status();
+}
+
 }  // extern "C"

@@ -5,6 +5,9 @@
 //   out[e, m, n] = bf16( sum_kb a_scale[e, m, kb] * b_scale[e, n/128, kb]
 //                        * sum_{k in block kb} a[e, m, k] * b[e, n, k] ),  m < masked_m[e]
 //
+// and of the contiguous layout of the page's grouped GEMMs (a [P, K], expert e owning rows
+// [offsets[e], offsets[e+1])), the same sum per row.
+//
 // Built like the row-tiled bf16 kernel, for the decode and small-batch shapes the page lists
 // (64 to 256 rows per expert; weight-bandwidth bound):
 //   - a workgroup (4 waves) owns a BM-row tile of one expert's block and 4 * NTW 16-column
@@ -39,14 +42,19 @@
 
 namespace moe_fp8 {
 
+// Masked layout (offsets == nullptr): expert e's rows are a[e, 0 .. masked_m[e]) of
+// a [E, max_m, K].  Contiguous layout: a [P, K], expert e's rows are [offsets[e], offsets[e+1])
+// (the TileOPs page's layout=contiguous with physical prefix-sum metadata); a_scale and out
+// follow a's rows.
 struct Fp8Problem {
-    const uint8_t *a;         // [E, max_m, K] e4m3
-    const float *a_scale;     // [E, max_m, KB]
+    const uint8_t *a;         // [E, max_m, K] or [P, K] e4m3
+    const float *a_scale;     // [E, max_m, KB] or [P, KB]
     const uint8_t *b;         // [E, N, K] e4m3
     const float *b_scale;     // [E, NB, KB]
-    const int32_t *masked_m;  // [E]
-    uint16_t *out;            // [E, max_m, N] bf16
-    int E, max_m, N, K, KB, NB;
+    const int32_t *masked_m;  // [E] (masked layout)
+    const int32_t *offsets;   // [E + 1] (contiguous layout), else nullptr
+    uint16_t *out;            // [E, max_m, N] or [P, N] bf16
+    int E, max_m, P, N, K, KB, NB;
 };
 
 constexpr int kWaves = 4;
@@ -57,6 +65,89 @@ typedef int moe_i32x8 __attribute__((ext_vector_type(8)));
 __host__ __device__ inline int fp8_grid(int tiles)
 {
     return (tiles + kXcds - 1) / kXcds * kXcds;
+}
+
+// One tile of a launch: its expert, column block, the a/out row of its first row, its rows.
+struct Fp8Tile {
+    int expert, nblk, rbase, n_rows;
+};
+
+// Rows of expert e in the contiguous layout: [r0, r1) of offsets, clamped to [0, P].
+__device__ __forceinline__ void contig_rows(const Fp8Problem &p, int e, int &r0, int &r1)
+{
+    r0 = min(max(p.offsets[e], 0), p.P);
+    r1 = min(max(p.offsets[e + 1], r0), p.P);
+}
+
+// Tile of this workgroup.  Tiles are numbered expert by expert, column blocks, then the BM-row
+// tiles of the expert innermost, and blocks are dealt to the 8 XCDs (blockIdx % 8) as
+// contiguous ranges of tile numbers.  Masked layout: m_tiles row tiles per expert (tiles past
+// its rows in use are empty).  Contiguous layout: ceil(rows / BM) per expert; every wave sums
+// them over the experts itself (lane l a run of ceil(E/64) experts, then a wave prefix sum),
+// which gives the tile count and, by a ballot, the expert of tile t.  Wave-uniform; false: no
+// tile for this workgroup.
+template <int BM>
+__device__ __forceinline__ bool fp8_locate(const Fp8Problem &p, int n_blocks, int m_tiles,
+                                           Fp8Tile &o)
+{
+    const int idx = blockIdx.x / kXcds;
+    if (p.offsets == nullptr) {
+        const int per_expert = n_blocks * m_tiles;
+        const int total = p.E * per_expert;
+        const int per = fp8_grid(total) / kXcds;
+        const int t = (blockIdx.x % kXcds) * per + idx;
+        if (idx >= per || t >= total)
+            return false;
+        o.expert = t / per_expert;
+        const int rem = t - o.expert * per_expert;
+        o.nblk = rem / m_tiles;
+        const int row0 = (rem - o.nblk * m_tiles) * BM;
+        const int rows_used = min(max(p.masked_m[o.expert], 0), p.max_m);
+        o.n_rows = min(BM, rows_used - row0);
+        o.rbase = o.expert * p.max_m + row0;
+        return o.n_rows > 0;
+    }
+    const int lane = threadIdx.x & 63;
+    const int run = (p.E + 63) / 64;
+    const int e0 = min(p.E, lane * run), e1 = min(p.E, e0 + run);
+    int mine = 0;
+    for (int e = e0; e < e1; ++e) {
+        int r0, r1;
+        contig_rows(p, e, r0, r1);
+        mine += (r1 - r0 + BM - 1) / BM * n_blocks;
+    }
+    int incl = mine;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(incl, d);
+        if (lane >= d)
+            incl += v;
+    }
+    const int total = __shfl(incl, 63);
+    const int per = fp8_grid(total) / kXcds;
+    const int t = (blockIdx.x % kXcds) * per + idx;
+    if (idx >= per || t >= total)
+        return false;
+    const unsigned long long hit = __ballot(t >= incl - mine && t < incl);
+    const int owner = __ffsll((long long)hit) - 1;
+    int e = __shfl(e0, owner), cum = __shfl(incl - mine, owner);
+    const int e_end = __shfl(e1, owner);
+    int r0 = 0, r1 = 0;
+    for (; e < e_end; ++e) {
+        contig_rows(p, e, r0, r1);
+        const int te = (r1 - r0 + BM - 1) / BM * n_blocks;
+        if (t < cum + te)
+            break;
+        cum += te;
+    }
+    const int mt_e = (r1 - r0 + BM - 1) / BM;
+    const int rem = t - cum;
+    o.expert = e;
+    o.nblk = rem / mt_e;
+    const int row0 = (rem - o.nblk * mt_e) * BM;
+    o.n_rows = min(BM, r1 - r0 - row0);
+    o.rbase = r0 + row0;
+    return o.n_rows > 0;
 }
 
 __device__ __forceinline__ moe_u32x4 load_nt16(const uint8_t *p)
@@ -97,20 +188,11 @@ __global__ __launch_bounds__(64 * kWaves) void k_fp8_gemm(Fp8Problem p, int n_bl
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
     // ---- tile: expert-major, column blocks, row tiles innermost; XCD-contiguous ranges
-    const int per_expert = n_blocks * m_tiles;
-    const int total = p.E * per_expert;
-    const int per_xcd = fp8_grid(total) / kXcds;
-    const int t = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-    if (t >= total)
+    Fp8Tile tile;
+    if (!fp8_locate<BM>(p, n_blocks, m_tiles, tile))
         return;
-    const int expert = t / per_expert;
-    const int rem = t - expert * per_expert;
-    const int nblk = rem / m_tiles;
-    const int row0 = (rem - nblk * m_tiles) * BM;
-    const int rows_used = min(max(p.masked_m[expert], 0), p.max_m);
-    const int n_rows = min(BM, rows_used - row0);
-    if (n_rows <= 0)
-        return;
+    const int expert = tile.expert, nblk = tile.nblk, rbase = tile.rbase;
+    const int n_rows = tile.n_rows;
     const int K = p.K, KB = p.KB;
     const int col0 = nblk * (16 * NTW * kWaves) + wv * (16 * NTW);
 
@@ -137,13 +219,13 @@ __global__ __launch_bounds__(64 * kWaves) void k_fp8_gemm(Fp8Problem p, int n_bl
 
     // ---- activation rows this lane loads: tile rows wv*BM/4 + 8*i + lane/8, chunk lane%8;
     // rows past the rows in use read the tile's first row (their results are never stored)
-    const uint8_t *A = p.a + (size_t)expert * p.max_m * K;
+    const uint8_t *A = p.a + (size_t)rbase * K;
     const uint8_t *xld[XI];
     int xslot[XI];
 #pragma unroll
     for (int i = 0; i < XI; ++i) {
         const int r = wv * (BM / kWaves) + 8 * i + lrow;
-        const int src = row0 + (r < n_rows ? r : 0);
+        const int src = r < n_rows ? r : 0;
         xld[i] = A + (size_t)src * K + 16 * lchunk;
         xslot[i] = r * 8 + (lchunk ^ ((r >> 1) & 7));
     }
@@ -152,7 +234,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_fp8_gemm(Fp8Problem p, int n_bl
 #pragma unroll
     for (int mt = 0; mt < TM; ++mt) {
         const int r = 16 * mt + rr;
-        sa_base[mt] = (expert * p.max_m + row0 + (r < n_rows ? r : 0)) * KB;
+        sa_base[mt] = (rbase + (r < n_rows ? r : 0)) * KB;
     }
 
     const int rot = (int)((expert * 7u) % (unsigned)KB);
@@ -238,7 +320,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_fp8_gemm(Fp8Problem p, int n_bl
         const int r = mt * 16 + rr;
         if (r >= n_rows)
             continue;
-        uint16_t *orow = p.out + ((size_t)expert * p.max_m + row0 + r) * p.N;
+        uint16_t *orow = p.out + ((size_t)rbase + r) * p.N;
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) {
             if (!tile_ok[nt])
@@ -289,24 +371,11 @@ __global__ __launch_bounds__(moe_wide::kThreads) void k_fp8_wide(Fp8Problem p, i
     const int wm = wv / kWN, wn = wv % kWN;
 
     // ---- tile: expert-major, column blocks, row tiles innermost; XCD-contiguous ranges
-    const int per_expert = n_blocks * m_tiles;
-    const int total = p.E * per_expert;
-    const int W = min((int)gridDim.x, fp8_wide_grid(total));
-    const int per = W / kXcds;
-    const int idx = blockIdx.x / kXcds;
-    if (idx >= per)
+    Fp8Tile tile;
+    if (!fp8_locate<kBM>(p, n_blocks, m_tiles, tile))
         return;
-    const int t = (blockIdx.x % kXcds) * per + idx;
-    if (t >= total)
-        return;
-    const int expert = t / per_expert;
-    const int rem = t - expert * per_expert;
-    const int nblk = rem / m_tiles;
-    const int row0 = (rem - nblk * m_tiles) * kBM;
-    const int rows_used = min(max(p.masked_m[expert], 0), p.max_m);
-    const int n_real = __builtin_amdgcn_readfirstlane(min(kBM, rows_used - row0));
-    if (n_real <= 0)
-        return;
+    const int expert = tile.expert, nblk = tile.nblk, rbase = tile.rbase;
+    const int n_real = __builtin_amdgcn_readfirstlane(tile.n_rows);
     const int K = p.K, KB = p.KB;
     const int col_wg = nblk * BW;
 
@@ -314,7 +383,7 @@ __global__ __launch_bounds__(moe_wide::kThreads) void k_fp8_wide(Fp8Problem p, i
     // wv*32 + 8j .. +7, lane l fetching chunk (l%8) ^ swizzle(row) of row wv*32 + 8j + l/8
     const int lrow = lane >> 3, lpos = lane & 7;
     const uint8_t *B = p.b + (size_t)expert * p.N * K;
-    const uint8_t *A = p.a + ((size_t)expert * p.max_m + row0) * K;
+    const uint8_t *A = p.a + (size_t)rbase * K;
     const uint8_t *wsrc[WLoads];
 #pragma unroll
     for (int j = 0; j < WLoads; ++j) {
@@ -345,7 +414,7 @@ __global__ __launch_bounds__(moe_wide::kThreads) void k_fp8_wide(Fp8Problem p, i
     // the rows in use copy row 0) -- instead of one strided load per row per k-step.  b_scale:
     // the block of this wave's 128 columns, one uniform load per k-step.
     const float *sa_src = p.a_scale +
-                          ((size_t)expert * p.max_m + row0 +
+                          ((size_t)rbase +
                            (64 * (wv & 3) + lane < n_real ? 64 * (wv & 3) + lane : 0)) * KB;
     const uint32_t sa_dst = (uint32_t)(uintptr_t)&s_scale[0][0] + (wv & 3) * 64 * 16;
     const int wcol = col_wg + 16 * NT * wn;  // this wave's columns: one 128-column block
@@ -438,7 +507,7 @@ __global__ __launch_bounds__(moe_wide::kThreads) void k_fp8_wide(Fp8Problem p, i
         const int r = 16 * (wm + kWM * m) + rr;
         if (m >= mt_real || r >= n_real)
             continue;
-        uint16_t *orow = p.out + ((size_t)expert * p.max_m + row0 + r) * p.N;
+        uint16_t *orow = p.out + ((size_t)rbase + r) * p.N;
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
             const int col = wcol + 16 * n + 4 * rq;

@@ -8,12 +8,21 @@
 
 namespace {
 
+// Tiles of a launch: masked layout, E * m_tiles per column block; contiguous layout, at most
+// ceil(P / BM) + E per column block (the kernel counts the real ones itself).
+int tile_bound(const moe_fp8::Fp8Problem &p, int BM, int n_blocks, int m_tiles)
+{
+    if (p.offsets == nullptr)
+        return p.E * n_blocks * m_tiles;
+    return ((p.P + BM - 1) / BM + p.E) * n_blocks;
+}
+
 template <int BM, int NTW, int STAGES>
 void launch_one(const moe_fp8::Fp8Problem &p, hipStream_t stream)
 {
     const int n_blocks = (p.N + 64 * NTW - 1) / (64 * NTW);
     const int m_tiles = (p.max_m + BM - 1) / BM;
-    const int tiles = p.E * n_blocks * m_tiles;
+    const int tiles = tile_bound(p, BM, n_blocks, m_tiles);
     hipLaunchKernelGGL((moe_fp8::k_fp8_gemm<BM, NTW, STAGES>), dim3(moe_fp8::fp8_grid(tiles)),
                        dim3(64 * moe_fp8::kWaves), 0, stream, p, n_blocks, m_tiles);
 }
@@ -23,7 +32,7 @@ void launch_fp8_wide(const moe_fp8::Fp8Problem &p, int m_tiles, hipStream_t stre
 {
     const int n_blocks = (p.N + 32 * NT - 1) / (32 * NT);
     hipLaunchKernelGGL(moe_fp8::k_fp8_wide<NT>,
-                       dim3(moe_fp8::fp8_wide_grid(p.E * n_blocks * m_tiles)),
+                       dim3(moe_fp8::fp8_wide_grid(tile_bound(p, moe_wide::kBM, n_blocks, m_tiles))),
                        dim3(moe_wide::kThreads), 0, stream, p, n_blocks, m_tiles);
 }
 
@@ -51,9 +60,11 @@ void launch_fp8_gemm(const uint8_t *a, const float *a_scale, const uint8_t *b,
     p.b = b;
     p.b_scale = b_scale;
     p.masked_m = masked_m;
+    p.offsets = nullptr;
     p.out = out;
     p.E = E;
     p.max_m = max_m;
+    p.P = 0;
     p.N = N;
     p.K = K;
     p.KB = K / 128;
@@ -70,6 +81,38 @@ void launch_fp8_gemm(const uint8_t *a, const float *a_scale, const uint8_t *b,
         launch_fp8_wide<8>(p, m_tiles, stream);
     else
         launch_fp8_wide<4>(p, m_tiles, stream);
+}
+
+void launch_fp8_gemm_contig(const uint8_t *a, const float *a_scale, const uint8_t *b,
+                            const float *b_scale, const int32_t *offsets, int E, int P, int N,
+                            int K, uint16_t *out, hipStream_t stream)
+{
+    moe_fp8::Fp8Problem p;
+    p.a = a;
+    p.a_scale = a_scale;
+    p.b = b;
+    p.b_scale = b_scale;
+    p.masked_m = nullptr;
+    p.offsets = offsets;
+    p.out = out;
+    p.E = E;
+    p.max_m = 0;
+    p.P = P;
+    p.N = N;
+    p.K = K;
+    p.KB = K / 128;
+    p.NB = (N + 127) / 128;
+    // the mean rows per expert picks the tile form, as max_m does for the masked layout
+    const int mean_rows = (P + E - 1) / E;
+    if (mean_rows <= 64 || p.KB % 4 != 0 || ((uintptr_t)a_scale & 15u) != 0) {
+        launch_one<64, 4, 2>(p, stream);
+        return;
+    }
+    const int wide_tiles = ((P + moe_wide::kBM - 1) / moe_wide::kBM) * ((N + 255) / 256);
+    if (wide_tiles >= 2 * device_cus())
+        launch_fp8_wide<8>(p, 0, stream);
+    else
+        launch_fp8_wide<4>(p, 0, stream);
 }
 
 }  // namespace moe

@@ -80,6 +80,15 @@ void launch_masked_ids(const int32_t *masked_m, int E, int max_m, int32_t *ids,
 void launch_fp8_gemm(const uint8_t *a, const float *a_scale, const uint8_t *b,
                      const float *b_scale, const int32_t *masked_m, int E, int max_m, int N,
                      int K, uint16_t *out, hipStream_t stream);
+// the same GEMM on the contiguous layout: a [P, K], expert e owning rows [offsets[e], offsets[e+1])
+void launch_fp8_gemm_contig(const uint8_t *a, const float *a_scale, const uint8_t *b,
+                            const float *b_scale, const int32_t *offsets, int E, int P, int N,
+                            int K, uint16_t *out, hipStream_t stream);
+
+// ---------------------------------------------------------------- fp8 activation quantiser
+// x [M, K] bf16 -> q [M, K] e4m3 codes, scale [M, ceil(K/128)] f32 (moe_quant.hip); K % 8 == 0.
+void launch_quant_fp8(const uint16_t *x, int M, int K, uint8_t *q, float *scale,
+                      hipStream_t stream);
 
 // ---------------------------------------------------------------- combine
 // out[t] = bf16( sum_j w[t,j] * y[t*k+j] (+ ys[t]) ), routes with ids outside [0,E) skipped.

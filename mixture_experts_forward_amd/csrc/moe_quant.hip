@@ -1,0 +1,105 @@
+// moe_quant.hip -- bf16 activations -> OCP e4m3 codes with one f32 scale per 1 x 128 group, the
+// a / a_scale operand pair of the block-scaled FP8 grouped GEMM (TileOPs "MoE" page,
+// MoEGroupedGemmFP8Fwd: a_scale [.., ceil_div(K, 128)] f32).
+//
+// Per group: s = amax / 448 (448 = the largest finite e4m3 magnitude; s = 1 for an all-zero
+// group), code = e4m3 nearest to x / s, ties to the even code.  Both divisions are IEEE f32.
+// 16 lanes own one group (8 consecutive elements each: one 16-byte load, one 8-byte store); the
+// group's amax is a 16-lane butterfly of maxima.  HBM-bound: 2 bytes in, 1 + 4/128 out per
+// element.
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// f32 -> e4m3 code, round to nearest even, magnitudes from 448 up saturate to 448 (0x7E), NaN
+// -> 0x7F.  Normal range (|v| >= 2^-6): the e4m3 code is the f32 exponent rebiased (127 -> 7)
+// and the top 3 mantissa bits, plus one when the 20 dropped bits are above half or exactly
+// half with an odd code (a carry out of the mantissa steps the exponent, which is the next
+// e4m3 value).  Below 2^-6 the codes are the subnormals m * 2^-9: m = rint(|v| * 512) (exact
+// scaling, rint rounds half to even; m = 8 is the code of 2^-6).
+__device__ __forceinline__ uint32_t e4m3_code(float v)
+{
+    const uint32_t bits = __float_as_uint(v);
+    const uint32_t sign = (bits >> 24) & 0x80u;
+    const float a = fabsf(v);
+    uint32_t code;
+    if (!(a < 448.0f)) {
+        code = a != a ? 0x7Fu : 0x7Eu;
+    } else if (a < 0.015625f) {
+        code = (uint32_t)rintf(a * 512.0f);
+    } else {
+        const uint32_t ab = __float_as_uint(a);
+        const uint32_t base = ((((ab >> 23) - 127u + 7u)) << 3) | ((ab >> 20) & 7u);
+        const uint32_t rest = ab & 0xFFFFFu;
+        code = base + ((rest > 0x80000u || (rest == 0x80000u && (base & 1u))) ? 1u : 0u);
+    }
+    return code | sign;
+}
+
+__global__ __launch_bounds__(kThreads) void k_quant_fp8(const uint16_t *__restrict__ x, int M,
+                                                        int K, uint8_t *__restrict__ q,
+                                                        float *__restrict__ scale)
+{
+    const int G = (K + 127) / 128;
+    const long long gid = (long long)blockIdx.x * (kThreads / 16) + threadIdx.x / 16;
+    if (gid >= (long long)M * G)  // whole 16-lane groups leave together
+        return;
+    const int row = (int)(gid / G), g = (int)(gid % G);
+    const int sub = threadIdx.x & 15;
+    const int k = 128 * g + 8 * sub;  // first of this lane's 8 elements
+    const bool in = k < K;            // K % 8 == 0: a lane's 8 are all in or all out
+    float v[8];
+    if (in) {
+        const moe_u32x4 raw = *reinterpret_cast<const moe_u32x4 *>(x + (size_t)row * K + k);
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            v[i] = 0.0f;
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1)
+        amax = fmaxf(amax, __shfl_xor(amax, d, 16));
+    const float s = amax == 0.0f ? 1.0f : amax / 448.0f;
+    if (sub == 0)
+        scale[(size_t)row * G + g] = s;
+    if (!in)
+        return;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        lo |= e4m3_code(v[i] / s) << (8 * i);
+        hi |= e4m3_code(v[4 + i] / s) << (8 * i);
+    }
+    moe_u32x2 packed;
+    packed.x = lo;
+    packed.y = hi;
+    *reinterpret_cast<moe_u32x2 *>(q + (size_t)row * K + k) = packed;
+}
+
+}  // namespace
+
+namespace moe {
+
+void launch_quant_fp8(const uint16_t *x, int M, int K, uint8_t *q, float *scale,
+                      hipStream_t stream)
+{
+    const long long groups = (long long)M * ((K + 127) / 128);
+    const long long blocks = (groups + kThreads / 16 - 1) / (kThreads / 16);
+    hipLaunchKernelGGL(k_quant_fp8, dim3((unsigned)blocks), dim3(kThreads), 0, stream, x, M, K,
+                       q, scale);
+}
+
+}  // namespace moe

@@ -159,3 +159,26 @@ def test_masked_entry_points_reject_before_launch():
     # a stage checks only what it reads: the down stage needs no activations or masked_m
     assert L.fused_moe_masked_stage(3, None, None, None, fake, 4, 8, 128, 64, None, fake, n,
                                     None) == -1                          # but out is needed
+
+
+def test_fp8_contiguous_and_quant_reject_before_launch():
+    L = moe.lib()
+    fake = ctypes.c_void_p(1 << 20)   # aligned, never dereferenced: checks come first
+    odd = ctypes.c_void_p((1 << 20) + 4)
+    g = lambda E, P, N, K, a=fake, off=fake: L.moe_grouped_gemm_fp8_contiguous(
+        a, fake, fake, fake, off, E, P, N, K, fake, None)
+    assert g(0, 16, 128, 128) == -2
+    assert g(4, -1, 128, 128) == -2
+    assert g(4, 16, 96, 128) == -3                 # N % 64
+    assert g(4, 16, 128, 200) == -3                # K % 128
+    assert g(2048, 16, 128, 128) == -3             # E > 1024
+    assert g(4, 16, 128, 128, a=odd) == -3         # a not 16-byte aligned
+    assert g(4, 16, 128, 128, off=None) == -1
+    assert g(4, 0, 128, 128, a=None, off=None) == 0   # P = 0: nothing to do
+    q = lambda M, K, x=fake, qq=fake: L.moe_quant_fp8(x, M, K, qq, fake, None)
+    assert q(-1, 128) == -2
+    assert q(4, 0) == -2
+    assert q(4, 100) == -3                         # K % 8
+    assert q(4, 128, qq=ctypes.c_void_p((1 << 20) + 4)) == -3   # q not 8-byte aligned
+    assert q(4, 128, x=None) == -1
+    assert q(0, 128, x=None) == 0                  # M = 0: nothing to do

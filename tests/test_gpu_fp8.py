@@ -1,4 +1,6 @@
-"""GPU parity of the block-scaled FP8 grouped GEMM (moe_grouped_gemm_fp8) against the oracle.
+"""GPU parity of the block-scaled FP8 grouped GEMMs (moe_grouped_gemm_fp8 on the masked layout,
+moe_grouped_gemm_fp8_contiguous on the contiguous one) and of the 1 x 128 activation quantiser
+(moe_quant_fp8, bit-exact codes and scales) against the oracle.
 
 Bound per element: one bf16 step of the result plus the accumulation error,
 |got - ref| <= 2^-7 |ref| + 2^-12 A, where A = sum_kb sa*sb*sum_k |a_k b_k| (the oracle on
@@ -98,3 +100,97 @@ def test_fp8_nan_code_poisons_only_its_row():
     assert torch.all(torch.isnan(out[1, 7]))
     out[1, 7] = 0
     assert torch.all(torch.isfinite(out))
+
+
+def _contig_inputs(E, counts, N, K, seed, extra_rows=3):
+    """a [P,K] e4m3 rows (the experts' rows stacked, then extra rows of no expert), offsets."""
+    g = torch.Generator().manual_seed(seed)
+    off = torch.zeros(E + 1, dtype=torch.int32)
+    off[1:] = torch.cumsum(torch.tensor(counts, dtype=torch.int32), 0)
+    P = int(off[-1]) + extra_rows
+    d = make_fp8_inputs(Fp8Config("c", E, 1, N, K, 0), DEV, seed=seed)
+    from moe_harness.workloads import random_e4m3_codes
+    d["a"] = random_e4m3_codes((P, K), g, DEV)
+    d["a_scale"] = ((torch.rand((P, (K + 127) // 128), generator=g) + 0.5) * 2.0 ** -7).to(DEV)
+    d["offsets"] = off.to(DEV)
+    del d["masked_m"]
+    return d, P
+
+
+@pytest.mark.parametrize("E,counts,N,K", [
+    (4, [5, 0, 37, 64], 192, 384),            # 64-row form: ragged, an empty expert
+    (3, [130, 1, 64], 128, 256),              # 64-row form: several row tiles of one expert
+    (3, [300, 77, 256], 256, 1024),           # 256-row form (mean rows > 64), partial tiles
+    (2, [0, 0], 64, 128),                     # no rows at all
+])
+def test_fp8_contiguous_matches_oracle(E, counts, N, K):
+    d, P = _contig_inputs(E, counts, N, K, seed=E * 7 + N)
+    out = torch.full((P, N), SENTINEL, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    moe.moe_grouped_gemm_fp8_contiguous(d["a"], d["a_scale"], d["b"], d["b_scale"],
+                                        d["offsets"], out=out)
+    torch.cuda.synchronize()
+    h = _host(d)
+    args = (h["a"], h["a_scale"], h["b"], h["b_scale"], h["offsets"])
+    _, ref = oracle.grouped_gemm_fp8_contiguous(*args)
+    A, _ = oracle.grouped_gemm_fp8_contiguous(h["a"] & 0x7F, h["a_scale"], h["b"] & 0x7F,
+                                              h["b_scale"], h["offsets"])
+    got = to_u16(out)
+    used = np.arange(P) < int(h["offsets"][-1])
+    assert np.all(got[~used] == SENTINEL), "a row of no expert was written"
+    _close(got[used], ref[used], A[used], "fp8 contiguous E=%d N=%d K=%d" % (E, N, K))
+
+
+def test_fp8_contiguous_equals_masked_layout():
+    """The same rows through both layouts give the same bits (both pick the 256-row form here:
+    max_m 96 and mean rows 82 are above 64; same expert order, same sums per row)."""
+    E, max_m, N, K = 3, 96, 256, 512
+    counts = [96, 80, 70]
+    d = make_fp8_inputs(Fp8Config("t", E, max_m, N, K, 0), DEV, seed=3)
+    d["masked_m"] = torch.tensor(counts, dtype=torch.int32, device=DEV)
+    masked = to_u16(_run(d))
+    rows = torch.cat([d["a"][e, :c] for e, c in enumerate(counts)])
+    srows = torch.cat([d["a_scale"][e, :c] for e, c in enumerate(counts)])
+    off = torch.tensor([0, 96, 176, 246], dtype=torch.int32, device=DEV)
+    got = to_u16(moe.moe_grouped_gemm_fp8_contiguous(rows, srows, d["b"], d["b_scale"], off))
+    want = np.concatenate([masked[e, :c] for e, c in enumerate(counts)])
+    assert np.array_equal(got, want)
+
+
+def _bf16_rows(M, K, seed):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn((M, K), generator=g)
+    x[1] = 0.0                                          # an all-zero row
+    x[2] *= 2.0 ** -12                                  # codes in the subnormal range
+    x[3, :64] *= 1e4                                    # one large value per group dominates
+    return x.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("M,K", [(5, 128), (7, 200), (33, 7168), (4, 2048 + 8)])
+def test_quant_fp8_bit_exact(M, K):
+    x = _bf16_rows(M, K, seed=M + K)
+    q, s = moe.moe_quant_fp8(x.to(DEV))
+    torch.cuda.synchronize()
+    rq, rs = oracle.quant_fp8_1x128(to_u16(x))
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32)), "scales differ"
+    got = q.cpu().numpy()
+    bad = np.argwhere(got != rq)
+    assert bad.size == 0, "codes differ at %s: got %s want %s" % (
+        bad[:4].tolist(), got[tuple(bad[:4].T)], rq[tuple(bad[:4].T)])
+
+
+def test_quant_then_contiguous_gemm_matches_oracle_chain():
+    """bf16 rows -> quantiser -> contiguous GEMM, against the oracle's quantiser and GEMM."""
+    E, counts, N, K = 3, [40, 0, 90], 128, 512
+    P = sum(counts)
+    x = _bf16_rows(P, K, seed=9)
+    d, _ = _contig_inputs(E, counts, N, K, seed=5, extra_rows=0)
+    q, s = moe.moe_quant_fp8(x.to(DEV))
+    got = to_u16(moe.moe_grouped_gemm_fp8_contiguous(q, s, d["b"], d["b_scale"], d["offsets"]))
+    torch.cuda.synchronize()
+    rq, rs = oracle.quant_fp8_1x128(to_u16(x))
+    h = _host(d)
+    _, ref = oracle.grouped_gemm_fp8_contiguous(rq, rs, h["b"], h["b_scale"], h["offsets"])
+    A, _ = oracle.grouped_gemm_fp8_contiguous(rq & 0x7F, rs, h["b"] & 0x7F, h["b_scale"],
+                                              h["offsets"])
+    _close(got, ref, A, "quant + contiguous fp8")
+

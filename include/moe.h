@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 /* status codes */
 enum {
@@ -51,6 +51,12 @@ enum {
 };
 
 enum { MOE_SCORING_SOFTMAX = 0, MOE_SCORING_SIGMOID = 1 };
+
+/* Element type of hidden_states, the expert weights, the shared expert's weights and out (and of
+ * the intermediate h and expert-output rows): bf16 or IEEE f16 (TileOPs "MoE" page, FusedMoEFwd
+ * qwen3-235b-decode: dtype=bf16, f16).  Passed as 16-bit patterns in uint16_t either way; the
+ * MFMA products accumulate in f32 and every rounding to the type is to nearest even. */
+enum { MOE_DTYPE_BF16 = 0, MOE_DTYPE_F16 = 1 };
 
 /* Path selection for fused_moe_fwd / fused_moe_shared_fwd / fused_moe_experts_fwd.
  * AUTO: DIRECT when T*k <= MOE_DIRECT_MAX_ROUTES and T*k <= 8*E (a few routed rows per expert),
@@ -72,6 +78,7 @@ enum { MOE_PATH_AUTO = 0, MOE_PATH_DIRECT = 1, MOE_PATH_SORTED = 2 };
  *   num_expert_group, topk_group: DeepSeek-style grouped top-k; (1, 1) = ungrouped.
  *   routed_scaling_factor: multiplies every routed weight (after renormalisation); 1 = none.
  *   path: MOE_PATH_*.
+ *   dtype: MOE_DTYPE_* (0, the zero-initialised default, is bf16).
  * Supported: 1 <= k <= 32, k <= E <= 1024, E % num_expert_group == 0,
  *   1 <= topk_group <= num_expert_group <= 64, k <= topk_group * E / num_expert_group,
  *   H % 64 == 0 and F % 64 == 0; softmax only with no correction_bias and no grouping.
@@ -88,6 +95,7 @@ typedef struct moe_params {
     int32_t topk_group;
     float routed_scaling_factor;
     int32_t path;
+    int32_t dtype;
 } moe_params_t;
 
 /* MOE_ABI_VERSION of the loaded library. */

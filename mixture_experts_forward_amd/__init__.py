@@ -43,7 +43,7 @@ class MoEParams(ctypes.Structure):
                 ("top_k", ctypes.c_int32), ("scoring", ctypes.c_int32),
                 ("renormalize", ctypes.c_int32), ("num_expert_group", ctypes.c_int32),
                 ("topk_group", ctypes.c_int32), ("routed_scaling_factor", ctypes.c_float),
-                ("path", ctypes.c_int32)]
+                ("path", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
 _lib = None
@@ -125,11 +125,22 @@ def _check(t, name, dtype, shape, device=None):
         raise ValueError("%s must be contiguous" % name)
 
 
+# element type of the pass (MOE_DTYPE_*): torch dtype -> code
+DTYPES = {torch.bfloat16: 0, torch.float16: 1}
+
+
 def make_params(T, H, E, F, k, scoring="softmax", renormalize=True, num_expert_group=1,
-                topk_group=1, routed_scaling_factor=1.0, path="auto"):
+                topk_group=1, routed_scaling_factor=1.0, path="auto", dtype=torch.bfloat16):
     return MoEParams(int(T), int(H), int(E), int(F), int(k), SCORING[scoring],
                      int(bool(renormalize)), int(num_expert_group), int(topk_group),
-                     float(routed_scaling_factor), PATHS[path])
+                     float(routed_scaling_factor), PATHS[path], DTYPES[dtype])
+
+
+def _pass_dtype(hidden_states):
+    """the pass's element type, taken from hidden_states (bf16 or f16)"""
+    if hidden_states.dtype not in DTYPES:
+        raise ValueError("hidden_states must be bfloat16 or float16, got %s" % hidden_states.dtype)
+    return hidden_states.dtype
 
 
 def workspace_bytes(params, shared_inter=0):
@@ -194,22 +205,23 @@ def _fused(hidden_states, gating_output, w_gate_up, w_down, top_k, correction_bi
     E, F2, _ = w_gate_up.shape
     F = F2 // 2
     dev = hidden_states.device
-    _check(hidden_states, "hidden_states", torch.bfloat16, (T, H))
+    dt = _pass_dtype(hidden_states)
+    _check(hidden_states, "hidden_states", dt, (T, H))
     _check(gating_output, "gating_output", torch.float32, (T, E), dev)
-    _check(w_gate_up, "w_gate_up", torch.bfloat16, (E, 2 * F, H), dev)
-    _check(w_down, "w_down", torch.bfloat16, (E, H, F), dev)
+    _check(w_gate_up, "w_gate_up", dt, (E, 2 * F, H), dev)
+    _check(w_down, "w_down", dt, (E, H, F), dev)
     if correction_bias is not None:
         _check(correction_bias, "correction_bias", torch.float32, (E,), dev)
     S = 0
     if shared_w_gate_up is not None:
         S = shared_w_gate_up.shape[0] // 2
-        _check(shared_w_gate_up, "shared_w_gate_up", torch.bfloat16, (2 * S, H), dev)
-        _check(shared_w_down, "shared_w_down", torch.bfloat16, (H, S), dev)
+        _check(shared_w_gate_up, "shared_w_gate_up", dt, (2 * S, H), dev)
+        _check(shared_w_down, "shared_w_down", dt, (H, S), dev)
     p = make_params(T, H, E, F, top_k, scoring, renormalize, num_expert_group, topk_group,
-                    routed_scaling_factor, path)
+                    routed_scaling_factor, path, dt)
     if out is None:
-        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    _check(out, "out", torch.bfloat16, (T, H), dev)
+        out = torch.empty((T, H), dtype=dt, device=dev)
+    _check(out, "out", dt, (T, H), dev)
     ids = torch.empty((T, top_k), dtype=torch.int32, device=dev) if return_routing else None
     w = torch.empty((T, top_k), dtype=torch.float32, device=dev) if return_routing else None
     with torch.cuda.device(dev):
@@ -261,15 +273,16 @@ def fused_moe_experts_fwd(hidden_states, w_gate_up, w_down, topk_ids, topk_weigh
     F = F2 // 2
     k = topk_ids.shape[1]
     dev = hidden_states.device
-    _check(hidden_states, "hidden_states", torch.bfloat16, (T, H))
-    _check(w_gate_up, "w_gate_up", torch.bfloat16, (E, 2 * F, H), dev)
-    _check(w_down, "w_down", torch.bfloat16, (E, H, F), dev)
+    dt = _pass_dtype(hidden_states)
+    _check(hidden_states, "hidden_states", dt, (T, H))
+    _check(w_gate_up, "w_gate_up", dt, (E, 2 * F, H), dev)
+    _check(w_down, "w_down", dt, (E, H, F), dev)
     _check(topk_ids, "topk_ids", torch.int32, (T, k), dev)
     _check(topk_weights, "topk_weights", torch.float32, (T, k), dev)
-    p = make_params(T, H, E, F, k, path=path)
+    p = make_params(T, H, E, F, k, path=path, dtype=dt)
     if out is None:
-        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    _check(out, "out", torch.bfloat16, (T, H), dev)
+        out = torch.empty((T, H), dtype=dt, device=dev)
+    _check(out, "out", dt, (T, H), dev)
     with torch.cuda.device(dev):
         ws, nbytes = _workspace(p, 0, dev, workspace)
         st = lib().fused_moe_experts_fwd(_ptr(hidden_states), _ptr(w_gate_up), _ptr(w_down),

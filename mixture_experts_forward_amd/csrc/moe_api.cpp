@@ -47,6 +47,7 @@ moe::GemmProblem gate_up_problem(const moe::Plan &pl, const Ctx &c)
     g.top_k = pl.k;
     g.P = pl.P;
     g.num_experts = pl.E;
+    g.dtype = pl.dtype;
     if (pl.path == MOE_PATH_SORTED) {
         g.sorted_ids = ws_at<int32_t>(c.ws, pl.off_sorted);
         g.offsets = ws_at<int32_t>(c.ws, pl.off_offsets);
@@ -81,6 +82,7 @@ moe::GemmProblem shared_problem(const moe::Plan &pl, const Ctx &c, bool gate_up)
     g.top_k = 1;
     g.rows = pl.T;
     g.num_experts = 1;
+    g.dtype = pl.dtype;
     g.num_groups = (pl.T + 16 * t.mt - 1) / (16 * t.mt);
     return g;
 }
@@ -137,7 +139,7 @@ int run_stage(int stage, const moe::Plan &pl, const Ctx &c)
     case MOE_STAGE_COMBINE:
         moe::launch_combine(ws_at<uint16_t>(c.ws, pl.off_y), c.ids, c.weights,
                             pl.S > 0 ? ws_at<uint16_t>(c.ws, pl.off_ys) : nullptr, c.out, pl.T,
-                            pl.H, pl.k, pl.E, c.stream);
+                            pl.H, pl.k, pl.E, pl.dtype, c.stream);
         break;
     default:
         return MOE_ERR_UNSUPPORTED;

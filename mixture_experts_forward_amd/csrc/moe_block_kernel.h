@@ -88,7 +88,7 @@ __device__ __forceinline__ void block_decode(const GemmProblem &g, int t, int n_
 }
 
 // One 128-row x BW-weight-row tile: K loop and epilogue.
-template <bool GATE_UP, int SRC, int TN, int STAGES>
+template <bool GATE_UP, int SRC, int TN, int STAGES, int DT>
 __device__ __forceinline__ void block_tile(const GemmProblem &g, int nblk, int mtile, int expert,
                                            moe_u32x4 (*s_x)[kBM * 8],
                                            moe_u32x4 (*s_w)[32 * TN * 8])
@@ -204,10 +204,10 @@ __device__ __forceinline__ void block_tile(const GemmProblem &g, int nblk, int m
             // the two halves of k are issued TN MFMAs apart: no back-to-back dependency
 #pragma unroll
             for (int n = 0; n < TN; ++n)
-                acc[m][n] = moe_mfma_16x16x32(a[n][0], b0, acc[m][n]);
+                acc[m][n] = moe_mma16<DT>(a[n][0], b0, acc[m][n]);
 #pragma unroll
             for (int n = 0; n < TN; ++n)
-                acc[m][n] = moe_mfma_16x16x32(a[n][1], b1, acc[m][n]);
+                acc[m][n] = moe_mma16<DT>(a[n][1], b1, acc[m][n]);
         }
     };
 
@@ -264,8 +264,8 @@ __device__ __forceinline__ void block_tile(const GemmProblem &g, int nblk, int m
                 }
             }
             moe_u32x2 packed;
-            packed.x = moe_pack_bf16x2(v[0], v[1]);
-            packed.y = moe_pack_bf16x2(v[2], v[3]);
+            packed.x = moe_pack2<DT>(v[0], v[1]);
+            packed.y = moe_pack2<DT>(v[2], v[3]);
             *reinterpret_cast<moe_u32x2 *>(orow + col + 4 * rq) = packed;
         }
     }
@@ -273,7 +273,7 @@ __device__ __forceinline__ void block_tile(const GemmProblem &g, int nblk, int m
 
 // Persistent grid (gridDim.x a multiple of 8): round r hands XCD x the tiles
 // [r*W + x*W/8, r*W + (x+1)*W/8), W = the slots in use.
-template <bool GATE_UP, int SRC, int TN, int STAGES>
+template <bool GATE_UP, int SRC, int TN, int STAGES, int DT>
 __global__ __launch_bounds__(64 * kWaves) void k_block_gemm(GemmProblem g, int n_blocks,
                                                            int m_tiles)
 {
@@ -291,7 +291,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_block_gemm(GemmProblem g, int n
     for (int t = (blockIdx.x % kXcds) * per + idx; t < total; t += W) {
         int nblk, mtile, expert;
         block_decode<SRC>(g, t, n_blocks, m_tiles, nblk, mtile, expert);
-        block_tile<GATE_UP, SRC, TN, STAGES>(g, nblk, mtile, expert, s_x, s_w);
+        block_tile<GATE_UP, SRC, TN, STAGES, DT>(g, nblk, mtile, expert, s_x, s_w);
         __syncthreads();  // the next tile's first LDS stores follow every wave's last reads
     }
 }

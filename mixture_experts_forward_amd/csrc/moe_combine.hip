@@ -1,6 +1,7 @@
 // moe_combine.hip -- deterministic weighted combine of the expert output rows.
 //
 // out[t, c] = bf16( sum_{j<k} w[t,j] * y[t*k + j, c]  (+ ys[t, c]) ), j ascending, f32 sums
+// (f16 in and out for the f16 pass)
 // (TileOPs "MoE" page, MoEPostPermuteFwd: expert_output, topk_weights [T,K] f32; the shared
 // expert of FusedMoESharedExpertFwd is added with weight one).  Routes whose id is outside
 // [0, E) are skipped.  The expert GEMMs write y indexed by route, so a token's k rows are
@@ -14,6 +15,7 @@ namespace {
 
 constexpr int kThreads = 256;
 
+template <int DT>
 __global__ __launch_bounds__(kThreads) void k_combine(
     const uint16_t *__restrict__ y, const int32_t *__restrict__ ids,
     const float *__restrict__ weights, const uint16_t *__restrict__ ys, uint16_t *__restrict__ out,
@@ -33,22 +35,22 @@ __global__ __launch_bounds__(kThreads) void k_combine(
         const moe_u32x4 v = *reinterpret_cast<const moe_u32x4 *>(y + r * H + c);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            acc[2 * q] += w * moe_bf16_to_f32(v[q] & 0xffffu);
-            acc[2 * q + 1] += w * moe_bf16_to_f32(v[q] >> 16);
+            acc[2 * q] += w * moe_to_f32<DT>(v[q]);
+            acc[2 * q + 1] += w * moe_to_f32<DT>(v[q] >> 16);
         }
     }
     if (ys) {
         const moe_u32x4 v = *reinterpret_cast<const moe_u32x4 *>(ys + (size_t)t * H + c);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            acc[2 * q] += moe_bf16_to_f32(v[q] & 0xffffu);
-            acc[2 * q + 1] += moe_bf16_to_f32(v[q] >> 16);
+            acc[2 * q] += moe_to_f32<DT>(v[q]);
+            acc[2 * q + 1] += moe_to_f32<DT>(v[q] >> 16);
         }
     }
     moe_u32x4 o;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-        o[q] = moe_pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+        o[q] = moe_pack2<DT>(acc[2 * q], acc[2 * q + 1]);
     *reinterpret_cast<moe_u32x4 *>(out + (size_t)t * H + c) = o;
 }
 
@@ -57,12 +59,16 @@ __global__ __launch_bounds__(kThreads) void k_combine(
 namespace moe {
 
 void launch_combine(const uint16_t *y, const int32_t *ids, const float *weights,
-                    const uint16_t *ys, uint16_t *out, int T, int H, int k, int E,
+                    const uint16_t *ys, uint16_t *out, int T, int H, int k, int E, int dtype,
                     hipStream_t stream)
 {
     const dim3 grid(T, (H / 8 + kThreads - 1) / kThreads);
-    hipLaunchKernelGGL(k_combine, grid, dim3(kThreads), 0, stream, y, ids, weights, ys, out, H,
-                       k, E);
+    if (dtype == 1)
+        hipLaunchKernelGGL(k_combine<1>, grid, dim3(kThreads), 0, stream, y, ids, weights, ys,
+                           out, H, k, E);
+    else
+        hipLaunchKernelGGL(k_combine<0>, grid, dim3(kThreads), 0, stream, y, ids, weights, ys,
+                           out, H, k, E);
 }
 
 }  // namespace moe

@@ -51,6 +51,53 @@ __device__ __forceinline__ moe_f32x16 moe_mfma_32x32x16(moe_u32x4 a, moe_u32x4 b
                                                    __builtin_bit_cast(moe_bf16x8, b), c, 0, 0, 0);
 }
 
+// Element type of the pass's activations, weights and outputs: DT 0 = bf16, 1 = f16 (both
+// 16-bit patterns in uint16_t).  The MFMA forms of the two types share lane layouts.
+typedef _Float16 moe_f16x8 __attribute__((ext_vector_type(8)));
+
+template <int DT>
+__device__ __forceinline__ moe_f32x4 moe_mma16(moe_u32x4 a, moe_u32x4 b, moe_f32x4 c)
+{
+    if constexpr (DT == 1)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(moe_f16x8, a),
+                                                      __builtin_bit_cast(moe_f16x8, b), c, 0, 0,
+                                                      0);
+    else
+        return moe_mfma_16x16x32(a, b, c);
+}
+
+template <int DT>
+__device__ __forceinline__ moe_f32x16 moe_mma32(moe_u32x4 a, moe_u32x4 b, moe_f32x16 c)
+{
+    if constexpr (DT == 1)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(moe_f16x8, a),
+                                                      __builtin_bit_cast(moe_f16x8, b), c, 0, 0,
+                                                      0);
+    else
+        return moe_mfma_32x32x16(a, b, c);
+}
+
+// two f32 -> one word of two 16-bit values (lo in the low half), round to nearest even
+template <int DT>
+__device__ __forceinline__ uint32_t moe_pack2(float lo, float hi)
+{
+    if constexpr (DT == 1)
+        return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+    else
+        return moe_pack_bf16x2(lo, hi);
+}
+
+// 16-bit pattern (low half of b) -> f32, exact
+template <int DT>
+__device__ __forceinline__ float moe_to_f32(uint32_t b)
+{
+    if constexpr (DT == 1)
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(b & 0xffffu));
+    else
+        return moe_bf16_to_f32(b & 0xffffu);
+}
+
 // Ordering a wave's LDS traffic without a workgroup barrier.
 __device__ __forceinline__ void moe_wave_sync()
 {

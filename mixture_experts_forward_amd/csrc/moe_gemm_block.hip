@@ -29,10 +29,10 @@ int device_cus()
     return n;
 }
 
-template <bool GATE_UP, int SRC, int TN, int STAGES>
-void launch_one(const GemmProblem &g, hipStream_t stream)
+template <bool GATE_UP, int SRC, int TN, int STAGES, int DT>
+void launch_typed(const GemmProblem &g, hipStream_t stream)
 {
-    const auto kernel = moe_block::k_block_gemm<GATE_UP, SRC, TN, STAGES>;
+    const auto kernel = moe_block::k_block_gemm<GATE_UP, SRC, TN, STAGES, DT>;
     const int cols = GATE_UP ? 16 * TN : 32 * TN;  // output columns per workgroup
     const int n_blocks = (g.n_out + cols - 1) / cols;
     const int m_tiles = g.num_groups;
@@ -41,6 +41,15 @@ void launch_one(const GemmProblem &g, hipStream_t stream)
     const int grid = moe_block::block_grid(n_blocks * m_tiles, slots);
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * moe_block::kWaves), 0, stream, g, n_blocks,
                        m_tiles);
+}
+
+template <bool GATE_UP, int SRC, int TN, int STAGES>
+void launch_one(const GemmProblem &g, hipStream_t stream)
+{
+    if (g.dtype == 1)
+        launch_typed<GATE_UP, SRC, TN, STAGES, 1>(g, stream);
+    else
+        launch_typed<GATE_UP, SRC, TN, STAGES, 0>(g, stream);
 }
 
 // Instantiated shapes (TN 16-row weight tiles per wave, STAGES).

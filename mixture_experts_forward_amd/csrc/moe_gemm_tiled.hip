@@ -12,8 +12,14 @@ void launch_one(const GemmProblem &g, hipStream_t stream)
                          (16 * NTW * moe_tiled::kWaves);
     const int m_tiles = g.num_groups;
     const int blocks = moe_tiled::tiled_grid(n_blocks, m_tiles);
-    hipLaunchKernelGGL((moe_tiled::k_tiled_gemm<GATE_UP, SRC, BM, NTW, STAGES>), dim3(blocks),
-                       dim3(64 * moe_tiled::kWaves), 0, stream, g, n_blocks, m_tiles);
+    if (g.dtype == 1)
+        hipLaunchKernelGGL((moe_tiled::k_tiled_gemm<GATE_UP, SRC, BM, NTW, STAGES, 1>),
+                           dim3(blocks), dim3(64 * moe_tiled::kWaves), 0, stream, g, n_blocks,
+                           m_tiles);
+    else
+        hipLaunchKernelGGL((moe_tiled::k_tiled_gemm<GATE_UP, SRC, BM, NTW, STAGES, 0>),
+                           dim3(blocks), dim3(64 * moe_tiled::kWaves), 0, stream, g, n_blocks,
+                           m_tiles);
 }
 
 // Instantiated tile shapes (BM rows, NTW 16-column tiles per wave, STAGES).

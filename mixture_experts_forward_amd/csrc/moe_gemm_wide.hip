@@ -29,10 +29,10 @@ int device_cus()
     return n;
 }
 
-template <bool GATE_UP, int SRC>
-void launch_one(const GemmProblem &g, hipStream_t stream)
+template <bool GATE_UP, int SRC, int DT>
+void launch_typed(const GemmProblem &g, hipStream_t stream)
 {
-    const auto kernel = moe_wide::k_wide_gemm<GATE_UP, SRC, 3>;
+    const auto kernel = moe_wide::k_wide_gemm<GATE_UP, SRC, 3, DT>;
     const int cols = GATE_UP ? moe_wide::kBW / 2 : moe_wide::kBW;  // output columns per tile
     const int n_blocks = (g.n_out + cols - 1) / cols;
     const int m_tiles = g.num_groups;
@@ -41,6 +41,15 @@ void launch_one(const GemmProblem &g, hipStream_t stream)
     const int grid = moe_wide::wide_grid(n_blocks * m_tiles, slots);
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(moe_wide::kThreads), 0, stream, g, n_blocks,
                        m_tiles);
+}
+
+template <bool GATE_UP, int SRC>
+void launch_one(const GemmProblem &g, hipStream_t stream)
+{
+    if (g.dtype == 1)
+        launch_typed<GATE_UP, SRC, 1>(g, stream);
+    else
+        launch_typed<GATE_UP, SRC, 0>(g, stream);
 }
 
 }  // namespace

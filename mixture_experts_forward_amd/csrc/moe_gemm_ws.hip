@@ -9,8 +9,12 @@ template <bool GATE_UP, int SRC, int NT, int MT, int KSPLIT, int STAGES>
 void launch_one(const GemmProblem &g, hipStream_t stream)
 {
     const dim3 grid((g.n_out + 16 * NT - 1) / (16 * NT), g.num_groups);
-    hipLaunchKernelGGL((moe_ws::k_ws_gemm<GATE_UP, SRC, NT, MT, KSPLIT, STAGES>), grid,
-                       dim3(64 * KSPLIT), 0, stream, g);
+    if (g.dtype == 1)
+        hipLaunchKernelGGL((moe_ws::k_ws_gemm<GATE_UP, SRC, NT, MT, KSPLIT, STAGES, 1>), grid,
+                           dim3(64 * KSPLIT), 0, stream, g);
+    else
+        hipLaunchKernelGGL((moe_ws::k_ws_gemm<GATE_UP, SRC, NT, MT, KSPLIT, STAGES, 0>), grid,
+                           dim3(64 * KSPLIT), 0, stream, g);
 }
 
 // Instantiated tile shapes.  Every shape the host plan may pick must be listed here.

@@ -45,6 +45,7 @@ struct GemmProblem {
     int P;                      // routes (DIRECT)
     int rows;                   // tokens (DENSE)
     int num_experts;            // E (valid expert ids are [0, E))
+    int dtype;                  // element type of act, weight, out: 0 bf16, 1 f16
 };
 
 // Tile shape of one launch.
@@ -93,7 +94,7 @@ void launch_quant_fp8(const uint16_t *x, int M, int K, uint8_t *q, float *scale,
 // ---------------------------------------------------------------- combine
 // out[t] = bf16( sum_j w[t,j] * y[t*k+j] (+ ys[t]) ), routes with ids outside [0,E) skipped.
 void launch_combine(const uint16_t *y, const int32_t *ids, const float *weights,
-                    const uint16_t *ys, uint16_t *out, int T, int H, int k, int E,
+                    const uint16_t *ys, uint16_t *out, int T, int H, int k, int E, int dtype,
                     hipStream_t stream);
 
 }  // namespace moe

@@ -26,6 +26,8 @@ int check_dims(const moe_params_t *p)
         return MOE_ERR_UNSUPPORTED;
     if (p->path == MOE_PATH_DIRECT && p->num_tokens * p->top_k > MOE_DIRECT_MAX_ROUTES)
         return MOE_ERR_UNSUPPORTED;
+    if (p->dtype != MOE_DTYPE_BF16 && p->dtype != MOE_DTYPE_F16)
+        return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 
@@ -67,6 +69,7 @@ void make_plan(const moe_params_t *p, int32_t S, Plan *pl)
     pl->k = p->top_k;
     pl->S = S;
     pl->P = pl->T * pl->k;
+    pl->dtype = p->dtype;
     const int P = pl->P;
     const double mean_rows = (double)P / (double)pl->E;
     if (p->path == MOE_PATH_AUTO)

@@ -33,6 +33,7 @@ struct TileChoice {
 struct Plan {
     int path;           // MOE_PATH_DIRECT or MOE_PATH_SORTED (resolved)
     int T, H, E, F, k, S, P;
+    int dtype;          // MOE_DTYPE_*
     int block_m;        // sorted path
     int slots;          // rows of the padded sorted order
     int tiles_cap;

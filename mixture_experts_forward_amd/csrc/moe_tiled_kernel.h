@@ -49,7 +49,7 @@ __host__ __device__ inline int tiled_grid(int n_blocks, int m_tiles)
     return (b + kXcds - 1) / kXcds * kXcds;
 }
 
-template <bool GATE_UP, int SRC, int BM, int NTW, int STAGES>
+template <bool GATE_UP, int SRC, int BM, int NTW, int STAGES, int DT>
 __global__ __launch_bounds__(64 * kWaves) void k_tiled_gemm(GemmProblem g, int n_blocks,
                                                            int m_tiles)
 {
@@ -177,10 +177,10 @@ __global__ __launch_bounds__(64 * kWaves) void k_tiled_gemm(GemmProblem g, int n
             const moe_u32x4 b1 = xb[r * 8 + ((rq + 4) ^ sw)];
 #pragma unroll
             for (int nw = 0; nw < NW; ++nw)
-                acc[mt][nw] = moe_mfma_16x16x32(a[nw][0], b0, acc[mt][nw]);
+                acc[mt][nw] = moe_mma16<DT>(a[nw][0], b0, acc[mt][nw]);
 #pragma unroll
             for (int nw = 0; nw < NW; ++nw)
-                acc[mt][nw] = moe_mfma_16x16x32(a[nw][1], b1, acc[mt][nw]);
+                acc[mt][nw] = moe_mma16<DT>(a[nw][1], b1, acc[mt][nw]);
         }
         moe_wave_sync();  // this wave's transpose reads finish before its next writes
     };
@@ -236,8 +236,8 @@ __global__ __launch_bounds__(64 * kWaves) void k_tiled_gemm(GemmProblem g, int n
                 }
             }
             moe_u32x2 packed;
-            packed.x = moe_pack_bf16x2(v[0], v[1]);
-            packed.y = moe_pack_bf16x2(v[2], v[3]);
+            packed.x = moe_pack2<DT>(v[0], v[1]);
+            packed.y = moe_pack2<DT>(v[2], v[3]);
             *reinterpret_cast<moe_u32x2 *>(orow + col0 + 16 * nt + 4 * rq) = packed;
         }
     }

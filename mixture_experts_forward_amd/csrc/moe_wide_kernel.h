@@ -200,7 +200,7 @@ template <int WS>
 constexpr int wide_lds_bytes() { return (kXStages + WS) * kHalf; }
 static_assert(kBM == kBW, "both operands' k-steps take kHalf bytes");
 
-template <bool GATE_UP, int SRC, int WS>
+template <bool GATE_UP, int SRC, int WS, int DT>
 __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mtile, int expert,
                                           moe_u32x4 *smem)
 {
@@ -352,7 +352,7 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
                 for (int n = 0; n < kNT32; ++n)
 #pragma unroll
                     for (int m = 0; m < MTR; ++m)
-                        acc[m][n] = moe_mfma_32x32x16(a[h & 1][n], b[h & 1][m], acc[m][n]);
+                        acc[m][n] = moe_mma32<DT>(a[h & 1][n], b[h & 1][m], acc[m][n]);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -397,8 +397,8 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
                     }
                 }
                 moe_u32x2 packed;
-                packed.x = moe_pack_bf16x2(v[0], v[1]);
-                packed.y = moe_pack_bf16x2(v[2], v[3]);
+                packed.x = moe_pack2<DT>(v[0], v[1]);
+                packed.y = moe_pack2<DT>(v[2], v[3]);
                 const int lc = lc0 + 8 * q4;  // first column of the 16-byte chunk
                 *reinterpret_cast<moe_u32x2 *>(otile + 8 * opos(r, lc / 8) + 4 * rq) = packed;
             }
@@ -420,7 +420,7 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
 }
 
 // Round r hands XCD x the tiles [r*W + x*W/8, r*W + (x+1)*W/8), W = the slots in use.
-template <bool GATE_UP, int SRC, int WS>
+template <bool GATE_UP, int SRC, int WS, int DT>
 __global__ __launch_bounds__(kThreads) void k_wide_gemm(GemmProblem g, int n_blocks, int m_tiles)
 {
     __shared__ moe_u32x4 smem[wide_lds_bytes<WS>() / 16];
@@ -434,7 +434,7 @@ __global__ __launch_bounds__(kThreads) void k_wide_gemm(GemmProblem g, int n_blo
     for (int t = (blockIdx.x % kXcds) * per + idx; t < total; t += W) {
         int nblk, mtile, expert;
         wide_decode<SRC>(g, t, n_blocks, m_tiles, nblk, mtile, expert);
-        wide_tile<GATE_UP, SRC, WS>(g, nblk, mtile, expert, smem);
+        wide_tile<GATE_UP, SRC, WS, DT>(g, nblk, mtile, expert, smem);
         __syncthreads();  // the next tile's first loads follow every wave's last reads
     }
 }

@@ -83,7 +83,7 @@ struct WsSmem {
     static constexpr int kSlots = kTranspose > kReduce ? kTranspose : kReduce;
 };
 
-template <bool GATE_UP, int SRC, int NT, int MT, int KSPLIT, int STAGES>
+template <bool GATE_UP, int SRC, int NT, int MT, int KSPLIT, int STAGES, int DT>
 __global__ __launch_bounds__(64 * KSPLIT) void k_ws_gemm(GemmProblem g)
 {
     constexpr int NW = GATE_UP ? 2 * NT : NT;  // 16-row weight tiles per k-step
@@ -255,8 +255,8 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_ws_gemm(GemmProblem g)
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
                     if (mt < mt_active) {
-                        acc[mt][nw] = moe_mfma_16x16x32(a0, xv[st][mt][0], acc[mt][nw]);
-                        acc[mt][nw] = moe_mfma_16x16x32(a1, xv[st][mt][1], acc[mt][nw]);
+                        acc[mt][nw] = moe_mma16<DT>(a0, xv[st][mt][0], acc[mt][nw]);
+                        acc[mt][nw] = moe_mma16<DT>(a1, xv[st][mt][1], acc[mt][nw]);
                     }
                 }
             }
@@ -330,8 +330,8 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_ws_gemm(GemmProblem g)
                         }
                     }
                     moe_u32x2 packed;
-                    packed.x = moe_pack_bf16x2(v[0], v[1]);
-                    packed.y = moe_pack_bf16x2(v[2], v[3]);
+                    packed.x = moe_pack2<DT>(v[0], v[1]);
+                    packed.y = moe_pack2<DT>(v[2], v[3]);
                     *reinterpret_cast<moe_u32x2 *>(orow + col0 + 16 * nt + 4 * rq) = packed;
                 }
             }

@@ -192,29 +192,31 @@ def _normal(shape, std: float, dtype, device, seed: int, stream: int) -> torch.T
 
 
 def make_inputs(cfg: MoEConfig, device="cpu", seed: int = 42, weights: bool = True,
-                num_tokens: Optional[int] = None) -> dict:
+                num_tokens: Optional[int] = None, dtype=torch.bfloat16) -> dict:
     """Seeded synthetic tensors for ``cfg`` on ``device``.
 
     Returns a dict with hidden_states [T,H] bf16, gating_output [T,E] f32, correction_bias [E]
     f32 or None, w_gate_up [E,2F,H] bf16, w_down [E,H,F] bf16 and, for S > 0,
     shared_w_gate_up [2S,H] / shared_w_down [H,S] bf16.  ``num_tokens`` overrides T (token
-    sweeps); weights do not depend on it.  ``weights=False`` skips the weight tensors."""
+    sweeps); weights do not depend on it.  ``weights=False`` skips the weight tensors.
+    ``dtype`` (bf16 or f16) is the element type of the activations and weights; the same f32
+    draws are rounded to it."""
     T = cfg.T if num_tokens is None else int(num_tokens)
     H, E, F, S = cfg.H, cfg.E, cfg.F, cfg.S
     d = {
-        "hidden_states": _normal((T, H), 1.0, torch.bfloat16, device, seed, STREAM_HIDDEN),
+        "hidden_states": _normal((T, H), 1.0, dtype, device, seed, STREAM_HIDDEN),
         "gating_output": _normal((T, E), 1.0, torch.float32, device, seed, STREAM_GATING),
         "correction_bias": (_normal((E,), 0.1, torch.float32, device, seed, STREAM_BIAS)
                             if cfg.bias else None),
     }
     if weights:
-        d["w_gate_up"] = _normal((E, 2 * F, H), H ** -0.5, torch.bfloat16, device, seed,
+        d["w_gate_up"] = _normal((E, 2 * F, H), H ** -0.5, dtype, device, seed,
                                  STREAM_W_GATE_UP)
-        d["w_down"] = _normal((E, H, F), F ** -0.5, torch.bfloat16, device, seed, STREAM_W_DOWN)
+        d["w_down"] = _normal((E, H, F), F ** -0.5, dtype, device, seed, STREAM_W_DOWN)
         if S > 0:
-            d["shared_w_gate_up"] = _normal((2 * S, H), H ** -0.5, torch.bfloat16, device, seed,
+            d["shared_w_gate_up"] = _normal((2 * S, H), H ** -0.5, dtype, device, seed,
                                             STREAM_SHARED_GATE_UP)
-            d["shared_w_down"] = _normal((H, S), S ** -0.5, torch.bfloat16, device, seed,
+            d["shared_w_down"] = _normal((H, S), S ** -0.5, dtype, device, seed,
                                          STREAM_SHARED_DOWN)
     return d
 

@@ -11,7 +11,8 @@ Functions (each follows the passage cited in ``moe_oracle.c``):
       -> (topk_ids int32 [T,k], topk_weights float32 [T,k])
   align_sort(topk_ids, num_experts, block_m) -> dict of int32 arrays
   experts(x, w_gate_up, w_down, topk_ids, topk_weights, shared_w_gate_up=None,
-          shared_w_down=None, tokens=None, num_threads=0) -> (acc float64 [n,H], out uint16 [n,H])
+          shared_w_down=None, tokens=None, num_threads=0, dtype="bf16")
+      -> (acc float64 [n,H], out uint16 [n,H]); dtype "bf16" or "f16" (IEEE binary16)
   forward(...) = route + experts, the whole pass
   masked_mlp(a, masked_m, w_gate_up, w_down) -> (acc float64 [E,max_m,H], out uint16 [E,max_m,H])
   fp8_e4m3_decode(codes) -> float64 values of OCP e4m3 codes
@@ -20,6 +21,7 @@ Functions (each follows the passage cited in ``moe_oracle.c``):
   grouped_gemm_fp8(a, a_scale, b, b_scale, masked_m) -> (acc float64 [E,max_m,N], out uint16)
   grouped_gemm_fp8_contiguous(a, a_scale, b, b_scale, offsets) -> (acc [P,N], out uint16 [P,N])
   double_to_bf16(values) -> uint16 (one rounding, nearest-even)
+  double_to_f16(values) -> uint16 binary16 bits (one rounding, nearest-even)
 """
 import ctypes
 import os
@@ -49,6 +51,10 @@ def _load():
     lib.oracle_route.restype = _I
     lib.oracle_align_sort.argtypes = [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P]
     lib.oracle_align_sort.restype = _I
+    lib.oracle_experts_dt.argtypes = [_I, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _I,
+                                      _P, _P, _I]
+    lib.oracle_double_to_f16.restype = ctypes.c_uint16
+    lib.oracle_double_to_f16.argtypes = [ctypes.c_double]
     lib.oracle_experts.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _I,
                                    _P, _P, _I]
     lib.oracle_experts.restype = _I
@@ -118,12 +124,16 @@ def align_sort(topk_ids, num_experts, block_m):
             "tile_expert": tile_expert, "inverse_pos": inverse, "n_tiles": int(n_tiles[0])}
 
 
+DTYPE_CODES = {"bf16": 0, "f16": 1}
+
+
 def experts(x, w_gate_up, w_down, topk_ids, topk_weights, shared_w_gate_up=None,
-            shared_w_down=None, tokens=None, num_threads=0):
-    """x [T,H] u16; w_gate_up [E,2F,H] u16; w_down [E,H,F] u16; ids/weights [T,k].
+            shared_w_down=None, tokens=None, num_threads=0, dtype="bf16"):
+    """x [T,H] u16; w_gate_up [E,2F,H] u16; w_down [E,H,F] u16; ids/weights [T,k].  The 16-bit
+    patterns are bf16 or IEEE f16 (dtype "bf16" / "f16"); the output is in the same type.
 
     tokens: optional list of token indices to evaluate (rows of the result follow it).
-    Returns (acc float64 [n,H] before rounding, out uint16 [n,H] bf16 bits)."""
+    Returns (acc float64 [n,H] before rounding, out uint16 [n,H] bits)."""
     x = _c(x, np.uint16)
     w_gate_up = _c(w_gate_up, np.uint16)
     w_down = _c(w_down, np.uint16)
@@ -151,9 +161,9 @@ def experts(x, w_gate_up, w_down, topk_ids, topk_weights, shared_w_gate_up=None,
         n = tok.size
     acc = np.empty((n, H), np.float64)
     out = np.empty((n, H), np.uint16)
-    st = _load().oracle_experts(_ptr(x), _ptr(w_gate_up), _ptr(w_down), _ptr(ids), _ptr(w),
-                                _ptr(sgu), _ptr(sd), S, H, E, F, k, _ptr(tok), n, _ptr(acc),
-                                _ptr(out), int(num_threads))
+    st = _load().oracle_experts_dt(DTYPE_CODES[dtype], _ptr(x), _ptr(w_gate_up), _ptr(w_down),
+                                   _ptr(ids), _ptr(w), _ptr(sgu), _ptr(sd), S, H, E, F, k,
+                                   _ptr(tok), n, _ptr(acc), _ptr(out), int(num_threads))
     if st != 0:
         raise ValueError("oracle_experts failed (status %d)" % st)
     return acc, out
@@ -161,11 +171,11 @@ def experts(x, w_gate_up, w_down, topk_ids, topk_weights, shared_w_gate_up=None,
 
 def forward(x, gating, w_gate_up, w_down, bias=None, k=2, scoring="softmax", renormalize=True,
             num_expert_group=1, topk_group=1, rsf=1.0, shared_w_gate_up=None,
-            shared_w_down=None, tokens=None, num_threads=0):
+            shared_w_down=None, tokens=None, num_threads=0, dtype="bf16"):
     """The whole pass: route every token, then evaluate the experts for ``tokens``."""
     ids, w = route(gating, bias, k, scoring, renormalize, num_expert_group, topk_group, rsf)
     acc, out = experts(x, w_gate_up, w_down, ids, w, shared_w_gate_up, shared_w_down, tokens,
-                       num_threads)
+                       num_threads, dtype)
     return {"topk_ids": ids, "topk_weights": w, "acc": acc, "out": out}
 
 
@@ -254,6 +264,15 @@ def grouped_gemm_fp8_contiguous(a, a_scale, b, b_scale, offsets):
     if rc != 0:
         raise ValueError("oracle_grouped_gemm_fp8_contig rejected its arguments (%d)" % rc)
     return acc, out
+
+
+def double_to_f16(values):
+    """float64 values -> IEEE binary16 bit patterns (uint16), one rounding to nearest even,
+    overflow to infinity."""
+    lib = _load()
+    v = np.asarray(values, np.float64)
+    flat = np.array([lib.oracle_double_to_f16(float(a)) for a in v.ravel()], np.uint16)
+    return flat.reshape(v.shape)
 
 
 def double_to_bf16(values):

@@ -311,7 +311,56 @@ int oracle_align_sort(const int32_t *topk_ids, int T, int k, int E, int block_m,
  * default.  The token loop is the only parallel loop; each token is computed by one thread in
  * a fixed order, so results do not depend on the thread count.
  */
-static void swiglu_mlp_accumulate(const double *x, const uint16_t *w_gu, const uint16_t *w_d,
+/* IEEE binary16 bit pattern -> double (exact): 1 sign, 5 exponent bits (bias 15), 10 fraction
+ * bits; exponent 0 encodes subnormals f/1024 * 2^-14; exponent 31 is inf (f = 0) or NaN. */
+static double f16_to_double(uint16_t b)
+{
+    const int sign = b >> 15, e = (b >> 10) & 31, f = b & 1023;
+    double mag;
+    if (e == 31)
+        mag = f ? NAN : INFINITY;
+    else if (e == 0)
+        mag = ldexp((double)f, -24);
+    else
+        mag = ldexp(1.0 + (double)f / 1024.0, e - 15);
+    return sign ? -mag : mag;
+}
+
+/* double -> binary16 bit pattern, one rounding, round-to-nearest-even: the value is rounded to a
+ * multiple of its binade's quantum (2^(E-10) for 2^E <= |v| < 2^(E+1), E >= -14; 2^-24 below
+ * 2^-14), then encoded; a result past the largest finite 65504 is infinity. */
+uint16_t oracle_double_to_f16(double v)
+{
+    if (v != v)
+        return 0x7E00;
+    const uint16_t sign = signbit(v) ? 0x8000 : 0;
+    const double a = fabs(v);
+    if (a == 0.0)
+        return sign;
+    int ex;
+    frexp(a, &ex);                 /* a in [2^(ex-1), 2^ex) */
+    const int E = ex - 1;
+    const double q = E < -14 ? ldexp(1.0, -24) : ldexp(1.0, E - 10);
+    const double r = nearbyint(a / q) * q;
+    if (r > 65504.0)
+        return sign | 0x7C00;
+    if (r < ldexp(1.0, -14))
+        return sign | (uint16_t)(r / ldexp(1.0, -24));
+    int er;
+    const double m = frexp(r, &er); /* r = m 2^er, m in [0.5, 1) */
+    const int e_field = er - 1 + 15;
+    const int frac = (int)((2.0 * m - 1.0) * 1024.0);
+    return sign | (uint16_t)(e_field << 10) | (uint16_t)frac;
+}
+
+/* element type of the expert pass: 0 bf16, 1 f16 (both as 16-bit patterns) */
+static double elem_to_double(uint16_t b, int dtype)
+{
+    return dtype == 1 ? f16_to_double(b) : bf16_to_double(b);
+}
+
+static void swiglu_mlp_accumulate(int dtype, const double *x, const uint16_t *w_gu,
+                                  const uint16_t *w_d,
                                   int H, int F, double weight, double *a, double *acc)
 {
     for (int f = 0; f < F; ++f) {
@@ -319,8 +368,8 @@ static void swiglu_mlp_accumulate(const double *x, const uint16_t *w_gu, const u
         const uint16_t *wu = w_gu + (size_t)(F + f) * H;
         double u = 0.0, v = 0.0;
         for (int h = 0; h < H; ++h) {
-            u += x[h] * bf16_to_double(wg[h]);
-            v += x[h] * bf16_to_double(wu[h]);
+            u += x[h] * elem_to_double(wg[h], dtype);
+            v += x[h] * elem_to_double(wu[h], dtype);
         }
         a[f] = u / (1.0 + exp(-u)) * v;
     }
@@ -328,17 +377,22 @@ static void swiglu_mlp_accumulate(const double *x, const uint16_t *w_gu, const u
         const uint16_t *wd = w_d + (size_t)h * F;
         double y = 0.0;
         for (int f = 0; f < F; ++f)
-            y += a[f] * bf16_to_double(wd[f]);
+            y += a[f] * elem_to_double(wd[f], dtype);
         acc[h] += weight * y;
     }
 }
 
-int oracle_experts(const uint16_t *x, const uint16_t *w_gate_up, const uint16_t *w_down,
-                   const int32_t *topk_ids, const float *topk_weights,
-                   const uint16_t *shared_w_gate_up, const uint16_t *shared_w_down, int S,
-                   int H, int E, int F, int k, const int32_t *token_list, int n_tokens,
-                   double *acc_out, uint16_t *out_bf16, int num_threads)
+/* The experts and combine for element type dtype (0 bf16, 1 f16 -- the TileOPs "MoE" page's
+ * FusedMoEFwd qwen3-235b-decode row runs both): inputs decoded exactly, everything in double,
+ * the output rounded once to the same type (nearest even). */
+int oracle_experts_dt(int dtype, const uint16_t *x, const uint16_t *w_gate_up,
+                      const uint16_t *w_down, const int32_t *topk_ids, const float *topk_weights,
+                      const uint16_t *shared_w_gate_up, const uint16_t *shared_w_down, int S,
+                      int H, int E, int F, int k, const int32_t *token_list, int n_tokens,
+                      double *acc_out, uint16_t *out_bits, int num_threads)
 {
+    if (dtype != 0 && dtype != 1)
+        return -3;
     if (H <= 0 || E <= 0 || F <= 0 || k <= 0 || n_tokens < 0 || S < 0)
         return -2;
     if (S > 0 && (!shared_w_gate_up || !shared_w_down))
@@ -365,26 +419,39 @@ int oracle_experts(const uint16_t *x, const uint16_t *w_gate_up, const uint16_t 
             continue;
         }
         for (int h = 0; h < H; ++h)
-            xd[h] = bf16_to_double(x[(size_t)t * H + h]);
+            xd[h] = elem_to_double(x[(size_t)t * H + h], dtype);
         for (int j = 0; j < k; ++j) {
             const int e = topk_ids[(size_t)t * k + j];
             if (e < 0 || e >= E)
                 continue;
-            swiglu_mlp_accumulate(xd, w_gate_up + (size_t)e * 2 * F * H,
+            swiglu_mlp_accumulate(dtype, xd, w_gate_up + (size_t)e * 2 * F * H,
                                   w_down + (size_t)e * H * F, H, F,
                                   (double)topk_weights[(size_t)t * k + j], a, acc);
         }
         if (S > 0)
-            swiglu_mlp_accumulate(xd, shared_w_gate_up, shared_w_down, H, S, 1.0, a, acc);
+            swiglu_mlp_accumulate(dtype, xd, shared_w_gate_up, shared_w_down, H, S, 1.0, a, acc);
         for (int h = 0; h < H; ++h) {
             if (acc_out)
                 acc_out[(size_t)i * H + h] = acc[h];
-            if (out_bf16)
-                out_bf16[(size_t)i * H + h] = oracle_double_to_bf16(acc[h]);
+            if (out_bits)
+                out_bits[(size_t)i * H + h] =
+                    dtype == 1 ? oracle_double_to_f16(acc[h]) : oracle_double_to_bf16(acc[h]);
         }
         free(xd); free(a); free(acc);
     }
     return status;
+}
+
+/* The bf16 pass (the element type of every FusedMoEFwd workload but one). */
+int oracle_experts(const uint16_t *x, const uint16_t *w_gate_up, const uint16_t *w_down,
+                   const int32_t *topk_ids, const float *topk_weights,
+                   const uint16_t *shared_w_gate_up, const uint16_t *shared_w_down, int S,
+                   int H, int E, int F, int k, const int32_t *token_list, int n_tokens,
+                   double *acc_out, uint16_t *out_bf16, int num_threads)
+{
+    return oracle_experts_dt(0, x, w_gate_up, w_down, topk_ids, topk_weights, shared_w_gate_up,
+                             shared_w_down, S, H, E, F, k, token_list, n_tokens, acc_out,
+                             out_bf16, num_threads);
 }
 
 /* ---------------------------------------------------------------- fp8 grouped GEMM */

@@ -3,7 +3,8 @@ the output tolerance.
 
 Output tolerance (bf16 output of a pass whose GPU side rounds h and the expert output rows to
 bf16 and accumulates in f32): relative L2 error <= 2e-2 over the compared elements, and every
-element within 5e-2 + 2e-2 * |ref| of the oracle's bf16 output.  Route weights: 1e-6 absolute.
+element within 5e-2 + 2e-2 * |ref| of the oracle's bf16 output.  The f16 pass keeps the same
+bound (its roundings of h and the rows are 8x finer).  Route weights: 1e-6 absolute.
 Route ids, sort results: bit-exact."""
 import numpy as np
 import torch
@@ -21,10 +22,25 @@ def bf16_to_np(t):
     return oracle.bf16_bits_to_float(to_u16(t)).astype(np.float64)
 
 
-def assert_output_close(got_bf16, ref_bits, what=""):
-    """got: GPU bf16 tensor [n,H] (or numpy float64); ref_bits: oracle uint16 [n,H]."""
-    g = got_bf16 if isinstance(got_bf16, np.ndarray) else bf16_to_np(got_bf16)
-    r = oracle.bf16_bits_to_float(ref_bits).astype(np.float64)
+def bits_to_np(bits, dtype="bf16"):
+    """16-bit patterns -> float64 values of type dtype ("bf16" or "f16")"""
+    if dtype == "f16":
+        return np.asarray(bits, np.uint16).view(np.float16).astype(np.float64)
+    return oracle.bf16_bits_to_float(bits).astype(np.float64)
+
+
+def oracle_dtype(t):
+    """the oracle's name of a torch tensor's 16-bit element type"""
+    return "f16" if t.dtype == torch.float16 else "bf16"
+
+
+def assert_output_close(got_bf16, ref_bits, what="", dtype=None):
+    """got: GPU bf16 or f16 tensor [n,H] (or numpy float64); ref_bits: oracle uint16 [n,H] of
+    the same type (dtype: "bf16"/"f16", default the tensor's own)."""
+    if dtype is None:
+        dtype = "bf16" if isinstance(got_bf16, np.ndarray) else oracle_dtype(got_bf16)
+    g = got_bf16 if isinstance(got_bf16, np.ndarray) else bits_to_np(to_u16(got_bf16), dtype)
+    r = bits_to_np(ref_bits, dtype)
     assert g.shape == r.shape, (g.shape, r.shape)
     assert np.all(np.isfinite(g)), "%s: non-finite output" % what
     err = g - r
@@ -68,7 +84,8 @@ def oracle_experts_sampled(d, ids, w, tokens, with_shared=False):
     if with_shared:
         sgu = to_u16(d["shared_w_gate_up"])
         sd = to_u16(d["shared_w_down"])
-    return oracle.experts(x, wgu, wd, local_ids, w[tokens], sgu, sd)
+    return oracle.experts(x, wgu, wd, local_ids, w[tokens], sgu, sd,
+                          dtype=oracle_dtype(d["hidden_states"]))
 
 
 def sample_tokens(T, n, seed=0):

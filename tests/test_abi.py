@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert moe.lib().moe_abi_version() == 1
+    assert moe.lib().moe_abi_version() == 2
     for s in (0, -1, -2, -3, -4, -5):
         assert moe.status_string(s) and moe.status_string(s) != "unknown status"
     assert moe.status_string(7) == "unknown status"
@@ -52,6 +52,10 @@ def test_check_params_rules():
     assert _check(moe.make_params(4, 128, 2048, 64, 2)) == -3           # E > 1024
     assert _check(moe.make_params(4, 96, 8, 64, 2)) == -3               # H % 64
     assert _check(moe.make_params(4, 128, 8, 80, 2)) == -3              # F % 64
+    bad_dtype = moe.make_params(4, 128, 8, 64, 2)
+    bad_dtype.dtype = 2
+    assert _check(bad_dtype) == -3                                      # unknown element type
+    assert _check(moe.make_params(4, 128, 8, 64, 2, dtype=__import__("torch").float16)) == 0
     assert _check(moe.make_params(4, 128, 8, 64, 2), bias=1) == -3      # softmax + bias
     g = moe.make_params(4, 128, 8, 64, 2, "sigmoid", True, 3, 1)        # 8 % 3
     assert _check(g) == -3

@@ -56,7 +56,10 @@ def test_qwen3_30b_decode_all_tokens():
     _check_pass(cfg, make_inputs(cfg, DEV), "auto", what=cfg.name)
 
 
-@pytest.mark.parametrize("T", [1, 2, 3, 5, 8, 9, 17, 63, 100])
+# odd and boundary token counts from 1 to 256 (the aiter decoding PR's served counts include
+# 3, 5-7 and 9-15); both paths where the direct path applies
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 6, 7, 8, 9, 11, 13, 15, 17, 31, 33, 63, 65, 100, 127,
+                               129, 255, 256])
 def test_decode_token_sweep(T):
     cfg = CONFIGS["qwen3-30b-decode"]
     d = make_inputs(cfg, DEV, seed=100 + T, num_tokens=T)

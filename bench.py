@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default=None)
+    ap.add_argument("--dtype", default="bf16", choices=["bf16", "f16"],
+                    help="element type of the fused pass (activations, weights, output)")
     ap.add_argument("--rotate", type=int, default=0, help="input sets (0 = automatic)")
     ap.add_argument("--path", default="auto", choices=["auto", "direct", "sorted"],
                     help="the library's path choice (auto: its own rule)")
@@ -99,7 +101,8 @@ def main():
     wbytes = cfg.E * 6.0 * cfg.H * cfg.F + 6.0 * cfg.H * cfg.S
     R = args.rotate or max(1, min(8, math.ceil(16 * LLC_BYTES / wbytes)))
     log("workload %s, %d input sets of %.2f GB weights" % (cfg.name, R, wbytes / 1e9))
-    sets = [make_inputs(cfg, dev, seed=42 + i) for i in range(R)]
+    tdt = torch.float16 if args.dtype == "f16" else torch.bfloat16
+    sets = [make_inputs(cfg, dev, seed=42 + i, dtype=tdt) for i in range(R)]
     torch.cuda.synchronize()
     if args.copy_calibration:
         src = torch.ones(args.copy_calibration, dtype=torch.uint8, device=dev)
@@ -111,9 +114,10 @@ def main():
 
     S = cfg.S
     p = moe.make_params(cfg.T, cfg.H, cfg.E, cfg.F, cfg.k, cfg.scoring, cfg.renormalize,
-                        cfg.num_expert_group, cfg.topk_group, cfg.rsf, path=args.path)
+                        cfg.num_expert_group, cfg.topk_group, cfg.rsf, path=args.path,
+                        dtype=tdt)
     ws = torch.empty(max(256, moe.workspace_bytes(p, S)), dtype=torch.uint8, device=dev)
-    out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((cfg.T, cfg.H), dtype=tdt, device=dev)
     ids = [torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev) for _ in range(R)]
     wts = [torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev) for _ in range(R)]
 
@@ -264,10 +268,11 @@ def main():
     traffic = read_traffic(cfg.name)
 
     # ---- CPU baseline: the oracle on this host
-    cpu = None if args.no_cpu_baseline else cpu_baseline(cfg, sets[0], args.cpu_seconds)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(cfg, sets[0], args.cpu_seconds,
+                                                         args.dtype)
 
     ms = fused_ms
-    base = BASELINE_MS.get(cfg.name)
+    base = BASELINE_MS.get(cfg.name if args.dtype == "bf16" else cfg.name + ":" + args.dtype)
     t_hbm = pass_bytes / perfmodel.HBM_PEAK_BYTES_PER_S
     t_mfma = pass_flops / perfmodel.BF16_MFMA_PEAK_FLOP_PER_S
     floor_ms = max(t_hbm, t_mfma) * 1e3
@@ -282,7 +287,7 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": round(ms / base["ms"], 4) if base else None,
-        "dtype": "bf16",
+        "dtype": args.dtype,
         "data": "synthetic (seeded; %d rotating input sets)" % R,
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "F": cfg.F,
                    "top_k": cfg.k, "scoring": cfg.scoring, "renormalize": cfg.renormalize,
@@ -557,6 +562,8 @@ BASELINE_MS = {
                          "qwen3-30b-decode-b32 bf16", "hardware": "not named on the page"},
     "qwen3-235b-batch": {"ms": 1.2042, "source": "TileOPs MoE page, FusedMoEFwd "
                          "qwen3-235b-decode bf16", "hardware": "not named on the page"},
+    "qwen3-235b-batch:f16": {"ms": 1.2004, "source": "TileOPs MoE page, FusedMoEFwd "
+                             "qwen3-235b-decode f16", "hardware": "not named on the page"},
     "ds-v3-grouped-prefill": {"ms": 7.1078, "source": "TileOPs MoE page, FusedMoEFwd "
                               "ds-v3-grouped-prefill bf16", "hardware": "not named on the page"},
     "kimi-k2-shared": {"ms": 5.0723, "source": "TileOPs MoE page, FusedMoESharedExpertFwd "
@@ -639,20 +646,22 @@ def summarize_trace(args):
                 ", shared S=%d" % cfg.S if cfg.S else ""), ""]
     for c in args.pmc_commands:
         lines += ["Command (from /tmp, repository at $R):", "", "    " + c, ""]
-    lines += ["Input-generation and copy kernels are omitted.", "",
+    lines += ["Input-generation and copy kernels, and the library GEMM of the bench's context "
+              "matmul, are omitted.", "",
               "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
     for r in csv.DictReader(open(path)):
         n = r["Name"]
-        if "at::native" in n or "rocclr" in n:
+        if "at::native" in n or "rocclr" in n or n.startswith("Cijk_"):
             continue
         short = n.replace("(anonymous namespace)::", "").replace("void ", "")
         short = short.split("(")[0] if "(" in short else short
         lines.append("| `%s` | %s | %.2f | %.2f | %.2f |" % (
             short, r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
             float(r["MaxNs"]) / 1e3))
-    lines += ["", "Template arguments: k_ws_gemm<GATE_UP, SRC, NT, MT, KSPLIT, STAGES> (SRC 0 "
-              "sorted, 1 direct, 2 dense, 3 scan); k_tiled_gemm<GATE_UP, SRC, BM, NTW, STAGES>; "
-              "k_block_gemm<GATE_UP, SRC, TN, STAGES>; k_wide_gemm<GATE_UP, SRC>."]
+    lines += ["", "Template arguments: k_ws_gemm<GATE_UP, SRC, NT, MT, KSPLIT, STAGES, DT> (SRC 0 "
+              "sorted, 1 direct, 2 dense, 3 scan; DT 0 bf16, 1 f16); k_tiled_gemm<GATE_UP, SRC, "
+              "BM, NTW, STAGES, DT>; k_block_gemm<GATE_UP, SRC, TN, STAGES, DT>; "
+              "k_wide_gemm<GATE_UP, SRC, WS, DT> (WS weight stages); k_combine<DT>."]
     out = os.path.join(PROFILE_DIR, "kernel_trace_%s.md" % cfg.name)
     os.makedirs(PROFILE_DIR, exist_ok=True)
     open(out, "w").write("\n".join(lines) + "\n")
@@ -703,7 +712,7 @@ def summarize_pmc(args):
     print("\n".join(lines))
 
 
-def cpu_baseline(cfg, d, seconds):
+def cpu_baseline(cfg, d, seconds, dtype="bf16"):
     """The oracle, as it stands, on this host: route every token, evaluate the experts of a
     sample of tokens; the time is scaled to one whole forward of T tokens."""
     import numpy as np
@@ -731,12 +740,12 @@ def cpu_baseline(cfg, d, seconds):
     threads = oracle.max_threads()
     # calibrate on one token, then size the sample to about `seconds`
     t0 = time.perf_counter()
-    oracle.experts(x, wgu, wd, lids, w, sgu, sd, tokens=[0])
+    oracle.experts(x, wgu, wd, lids, w, sgu, sd, tokens=[0], dtype=dtype)
     one = max(time.perf_counter() - t0, 1e-6)
     n = int(max(1, min(cfg.T, seconds * max(1, threads) / one)))
     tokens = np.linspace(0, cfg.T - 1, n).round().astype(np.int32)
     t0 = time.perf_counter()
-    oracle.experts(x, wgu, wd, lids, w, sgu, sd, tokens=tokens)
+    oracle.experts(x, wgu, wd, lids, w, sgu, sd, tokens=tokens, dtype=dtype)
     exp_s = time.perf_counter() - t0
     per_forward_ms = (route_s + exp_s * cfg.T / n) * 1e3
     log("cpu oracle: %d of %d tokens in %.2f s on %d threads -> %.1f ms per forward"

@@ -265,7 +265,8 @@ def main():
     # the gate-up kernel's own bound: its bytes at 8 TB/s or its FLOPs at the bf16 MFMA peak
     gu_mfma_bound = gu_flops / perfmodel.BF16_MFMA_PEAK_FLOP_PER_S > \
         gu_bytes / perfmodel.HBM_PEAK_BYTES_PER_S
-    traffic = read_traffic(cfg.name)
+    # the committed counter summaries are of the bf16 kernels
+    traffic = read_traffic(cfg.name) if args.dtype == "bf16" else None
 
     # ---- CPU baseline: the oracle on this host
     cpu = None if args.no_cpu_baseline else cpu_baseline(cfg, sets[0], args.cpu_seconds,

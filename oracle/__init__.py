@@ -22,6 +22,8 @@ Functions (each follows the passage cited in ``moe_oracle.c``):
   grouped_gemm_fp8_contiguous(a, a_scale, b, b_scale, offsets) -> (acc [P,N], out uint16 [P,N])
   double_to_bf16(values) -> uint16 (one rounding, nearest-even)
   double_to_f16(values) -> uint16 binary16 bits (one rounding, nearest-even)
+  mxfp4_dequant(q, scale) -> float64 weights of MXFP4 codes and E8M0 block scales
+  mxfp4_to_bf16(q, scale) -> the same values as bf16 bits (exact)
 """
 import ctypes
 import os
@@ -53,6 +55,11 @@ def _load():
     lib.oracle_align_sort.restype = _I
     lib.oracle_experts_dt.argtypes = [_I, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _I,
                                       _P, _P, _I]
+    lib.oracle_mxfp4_dequant.argtypes = [_P, _P, _I, _I, _P]
+    lib.oracle_e2m1_to_double.restype = ctypes.c_double
+    lib.oracle_e2m1_to_double.argtypes = [ctypes.c_uint8]
+    lib.oracle_e8m0_to_double.restype = ctypes.c_double
+    lib.oracle_e8m0_to_double.argtypes = [ctypes.c_uint8]
     lib.oracle_double_to_f16.restype = ctypes.c_uint16
     lib.oracle_double_to_f16.argtypes = [ctypes.c_double]
     lib.oracle_experts.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _I,
@@ -264,6 +271,27 @@ def grouped_gemm_fp8_contiguous(a, a_scale, b, b_scale, offsets):
     if rc != 0:
         raise ValueError("oracle_grouped_gemm_fp8_contig rejected its arguments (%d)" % rc)
     return acc, out
+
+
+def mxfp4_dequant(q, scale):
+    """MXFP4 weights -> float64: q uint8 [..., K/2] (two e2m1 codes per byte, element 2i in the
+    low nibble), scale uint8 [..., K/32] (E8M0) -> [..., K]."""
+    q = _c(q, np.uint8)
+    s = _c(scale, np.uint8)
+    K = q.shape[-1] * 2
+    rows = int(np.prod(q.shape[:-1])) if q.ndim > 1 else 1
+    out = np.empty(q.shape[:-1] + (K,), dtype=np.float64)
+    rc = _load().oracle_mxfp4_dequant(_ptr(q), _ptr(s), rows, K, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_mxfp4_dequant rejected its arguments (%d)" % rc)
+    return out
+
+
+def mxfp4_to_bf16(q, scale):
+    """MXFP4 weights -> the bf16 bit patterns of the same values: exact for scales up to 252
+    (an e2m1 value has at most two significant bits; 6 * 2^125 is below the bf16 maximum), the
+    largest codes overflowing to infinity from scale 253 up."""
+    return double_to_bf16(mxfp4_dequant(q, scale))
 
 
 def double_to_f16(values):

@@ -15,6 +15,7 @@
  *             1 x 128 activation block and per 128 x 128 weight block; and the same GEMM on
  *             the contiguous layout of the page's bf16 grouped GEMMs)
  *   fp8 quant bf16 activations -> e4m3 codes with one f32 scale per 1 x 128 group
+ *   mxfp4     dequantisation of MXFP4 expert weights (e2m1 codes, E8M0 block scales)
  *
  * Precision: every floating-point quantity is double; results are rounded exactly once at the
  * end (route weights to f32, outputs to bf16 with round-to-nearest-even).  The only f32
@@ -609,6 +610,42 @@ int oracle_grouped_gemm_fp8_contig(const uint8_t *a, const float *a_scale, const
                 acc_out[(size_t)r * N + n] = total;
         }
     }
+    return 0;
+}
+
+/* ---------------------------------------------------------------- MXFP4 weights */
+
+/* OCP MX e2m1 code (4 bits) -> double: 1 sign bit, 2 exponent bits with bias 1, 1 mantissa bit;
+ * exponent 0 encodes the subnormal m * 0.5; no infinities or NaN.  Magnitudes 0, 0.5, 1, 1.5,
+ * 2, 3, 4, 6. */
+double oracle_e2m1_to_double(uint8_t code)
+{
+    const int sign = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+    const double mag = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return sign ? -mag : mag;
+}
+
+/* OCP MX E8M0 scale byte -> double: 2^(s - 127); 255 is NaN. */
+double oracle_e8m0_to_double(uint8_t s)
+{
+    return s == 255 ? NAN : ldexp(1.0, (int)s - 127);
+}
+
+/* MXFP4 weights -> double (the FlashInfer BF16-activation PR's 4-bit expert weights with 16-bit
+ * activations, in the OCP MX layout): rows of K elements, two e2m1 codes per byte (element 2i
+ * in the low nibble of byte i, reading of the packing order), one E8M0 scale per 32 consecutive
+ * elements.  q [rows, K/2], scale [rows, K/32], out [rows, K]; K % 32 == 0. */
+int oracle_mxfp4_dequant(const uint8_t *q, const uint8_t *scale, int rows, int K, double *out)
+{
+    if (rows < 0 || K < 32 || K % 32 != 0)
+        return -1;
+    for (int r = 0; r < rows; ++r)
+        for (int k = 0; k < K; ++k) {
+            const uint8_t byte = q[(size_t)r * (K / 2) + k / 2];
+            const uint8_t code = (k & 1) ? (byte >> 4) : (byte & 15);
+            out[(size_t)r * K + k] = oracle_e2m1_to_double(code) *
+                                     oracle_e8m0_to_double(scale[(size_t)r * (K / 32) + k / 32]);
+        }
     return 0;
 }
 

@@ -237,6 +237,31 @@ int fused_moe_experts_stage(int stage, const uint16_t *hidden_states, const uint
                             size_t workspace_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------------------
+ * fused_moe_mxfp4_fwd -- fused_moe_fwd with MXFP4 expert weights and bf16 activations (W4A16;
+ * FlashInfer BF16-activation PR: 4-bit expert weights with BF16 activations, here in the OCP MX
+ * format that gfx950 converts natively).  Weights in MXFP4: blocks of 32 consecutive elements
+ * along the reduction dimension share one E8M0 scale; each element is an e2m1 code.
+ *   w_gate_up_q      [E, 2F, H/2] uint8: two e2m1 codes per byte, element 2i in the low
+ *                    nibble of byte i (e2m1: sign, 2 exponent bits with bias 1, 1 mantissa
+ *                    bit: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6).
+ *   w_gate_up_scale  [E, 2F, H/32] uint8: E8M0 scales, 2^(s-127); 255 is NaN.
+ *   w_down_q         [E, H, F/2] uint8; w_down_scale [E, H, F/32] uint8.
+ * Expert weight (e, n, k) = e2m1(code) * 2^(scale - 127); everything else as fused_moe_fwd
+ * (rows [0,F) of w_gate_up are gate, [F,2F) up).  For scales up to 252 the dequantised
+ * weights are exact in bf16, so the sums are those of the bf16 pass on those weights.  Needs p->dtype == MOE_DTYPE_BF16,
+ * H % 128 == 0 and F % 128 == 0; 16-byte aligned hidden_states, the code tensors, out and the
+ * workspace.  No shared expert.
+ * Workspace: fused_moe_mxfp4_workspace_bytes(p) bytes.
+ * Errors: as fused_moe_fwd. */
+size_t fused_moe_mxfp4_workspace_bytes(const moe_params_t *p);
+int fused_moe_mxfp4_fwd(const uint16_t *hidden_states, const float *gating_output,
+                        const uint8_t *w_gate_up_q, const uint8_t *w_gate_up_scale,
+                        const uint8_t *w_down_q, const uint8_t *w_down_scale,
+                        const float *correction_bias, const moe_params_t *p, uint16_t *out,
+                        int32_t *topk_ids_out, float *topk_weights_out, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------
  * Masked layout: the expert MLPs of one expert-parallel shard (TileOPs "MoE" page,
  * MoEGroupedGemmFwd with a: [E, layout.max_m, K] and layout_metadata [E] i32, workload
  * ds-v3-ep8-masked; MoEPrePermuteFwd's num_local_experts).  Local expert e owns the row block

@@ -16,6 +16,8 @@ Entry points (same names as the C ABI):
   moe_grouped_gemm_fp8(a, a_scale, b, b_scale, masked_m)      -> out [E, max_m, N] bf16
   moe_grouped_gemm_fp8_contiguous(a, a_scale, b, b_scale, expert_offsets) -> out [P, N] bf16
   moe_quant_fp8(x)                                            -> (q [M, K] e4m3, scale [M, K/128])
+  fused_moe_mxfp4_fwd(hidden, gating, w_gate_up_q, w_gate_up_scale, w_down_q, w_down_scale,
+                      top_k, ...)                             -> out [T, H] bf16 (MXFP4 weights)
 """
 import ctypes
 import os
@@ -60,6 +62,9 @@ SIGNATURES = {
     "moe_align_sort": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P]),
     "fused_moe_workspace_bytes": (_SZ, [_P, _I32]),
     "fused_moe_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "fused_moe_mxfp4_workspace_bytes": (_SZ, [_P]),
+    "fused_moe_mxfp4_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                           _SZ, _P]),
     "fused_moe_shared_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P,
                                             _P, _SZ, _P]),
     "fused_moe_experts_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -432,3 +437,47 @@ def moe_quant_fp8(x, q=None, scale=None):
     if st != MOE_OK:
         raise MoEError(st, "moe_quant_fp8")
     return q, scale
+
+
+def fused_moe_mxfp4_fwd(hidden_states, gating_output, w_gate_up_q, w_gate_up_scale, w_down_q,
+                        w_down_scale, top_k, correction_bias=None, scoring="softmax",
+                        renormalize=True, num_expert_group=1, topk_group=1,
+                        routed_scaling_factor=1.0, path="auto", out=None, workspace=None,
+                        return_routing=False):
+    """The fused pass with MXFP4 expert weights (uint8 e2m1 code pairs [E,2F,H/2] / [E,H,F/2],
+    uint8 E8M0 scales [E,2F,H/32] / [E,H,F/32]) and bf16 activations."""
+    T, H = hidden_states.shape
+    E, F2, _ = w_gate_up_q.shape
+    F = F2 // 2
+    dev = hidden_states.device
+    _check(hidden_states, "hidden_states", torch.bfloat16, (T, H))
+    _check(gating_output, "gating_output", torch.float32, (T, E), dev)
+    _check(w_gate_up_q, "w_gate_up_q", torch.uint8, (E, 2 * F, H // 2), dev)
+    _check(w_gate_up_scale, "w_gate_up_scale", torch.uint8, (E, 2 * F, H // 32), dev)
+    _check(w_down_q, "w_down_q", torch.uint8, (E, H, F // 2), dev)
+    _check(w_down_scale, "w_down_scale", torch.uint8, (E, H, F // 32), dev)
+    if correction_bias is not None:
+        _check(correction_bias, "correction_bias", torch.float32, (E,), dev)
+    p = make_params(T, H, E, F, top_k, scoring, renormalize, num_expert_group, topk_group,
+                    routed_scaling_factor, path)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _check(out, "out", torch.bfloat16, (T, H), dev)
+    ids = torch.empty((T, top_k), dtype=torch.int32, device=dev) if return_routing else None
+    w = torch.empty((T, top_k), dtype=torch.float32, device=dev) if return_routing else None
+    with torch.cuda.device(dev):
+        n = int(lib().fused_moe_mxfp4_workspace_bytes(ctypes.byref(p)))
+        if workspace is None:
+            workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+        elif workspace.dtype != torch.uint8 or workspace.numel() < n:
+            raise ValueError("workspace must be a uint8 tensor with >= %d bytes" % n)
+        st = lib().fused_moe_mxfp4_fwd(
+            _ptr(hidden_states), _ptr(gating_output), _ptr(w_gate_up_q), _ptr(w_gate_up_scale),
+            _ptr(w_down_q), _ptr(w_down_scale), _ptr(correction_bias), ctypes.byref(p),
+            _ptr(out), _ptr(ids), _ptr(w), _ptr(workspace), workspace.numel(), _stream(dev))
+    if st != MOE_OK:
+        raise MoEError(st, "fused_moe_mxfp4_fwd")
+    if return_routing:
+        return out, ids, w
+    return out
+

@@ -32,6 +32,8 @@ struct Ctx {
     uint16_t *out;
     void *ws;
     hipStream_t stream;
+    // MXFP4 expert weights (codes, scales), when the plan uses them
+    const uint8_t *gu_q = nullptr, *gu_s = nullptr, *d_q = nullptr, *d_s = nullptr;
 };
 
 // The GEMM problems of a plan (sorted layout, when used, lives in the workspace).
@@ -48,11 +50,15 @@ moe::GemmProblem gate_up_problem(const moe::Plan &pl, const Ctx &c)
     g.P = pl.P;
     g.num_experts = pl.E;
     g.dtype = pl.dtype;
+    g.wq = c.gu_q;
+    g.wscale = c.gu_s;
     if (pl.path == MOE_PATH_SORTED) {
         g.sorted_ids = ws_at<int32_t>(c.ws, pl.off_sorted);
         g.offsets = ws_at<int32_t>(c.ws, pl.off_offsets);
         g.tile_expert = ws_at<int32_t>(c.ws, pl.off_tile_expert);
-        g.num_groups = pl.gate_up.kind == moe::KERNEL_WS ? pl.E : pl.tiles_cap;
+        const bool per_expert =
+            pl.gate_up.kind == moe::KERNEL_WS || pl.gate_up.kind == moe::KERNEL_MX;
+        g.num_groups = per_expert ? pl.E : pl.tiles_cap;
     } else {
         g.num_groups = pl.P <= 64 ? pl.P : pl.E;  // per route (direct) or per expert (scan)
     }
@@ -64,6 +70,8 @@ moe::GemmProblem down_problem(const moe::Plan &pl, const Ctx &c)
     moe::GemmProblem g = gate_up_problem(pl, c);
     g.act = ws_at<uint16_t>(c.ws, pl.off_h);
     g.weight = c.w_down;
+    g.wq = c.d_q;
+    g.wscale = c.d_s;
     g.out = ws_at<uint16_t>(c.ws, pl.off_y);
     g.K = pl.F;
     g.n_out = pl.H;
@@ -98,6 +106,8 @@ bool launch_gemm(bool gate_up, const moe::GemmProblem &g, moe::RowSource src,
         return moe::launch_block(gate_up, g, src, ws_tile(t), stream);
     if (t.kind == moe::KERNEL_WIDE)
         return moe::launch_wide(gate_up, g, src, stream);
+    if (t.kind == moe::KERNEL_MX)
+        return moe::launch_mx(gate_up, g, src, ws_tile(t), stream);
     return gate_up ? moe::launch_gate_up(g, src, ws_tile(t), stream)
                    : moe::launch_down(g, src, ws_tile(t), stream);
 }
@@ -158,6 +168,18 @@ int experts_impl(const moe::Plan &pl, const Ctx &c, int first_stage = MOE_STAGE_
         if (st != MOE_OK)
             return st;
     }
+    return MOE_OK;
+}
+
+// MXFP4 weights (the plan of the bf16 pass with the MXFP4 GEMM for both expert GEMMs):
+// bf16 activations, H and F multiples of 128 (whole 128-element k-steps)
+int mx_check(const moe_params_t *p)
+{
+    int st = moe::check_dims(p);
+    if (st != MOE_OK)
+        return st;
+    if (p->dtype != MOE_DTYPE_BF16 || p->hidden % 128 != 0 || p->inter % 128 != 0)
+        return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 
@@ -314,6 +336,53 @@ int fused_moe_shared_fwd(const uint16_t *hidden_states, const float *gating_outp
     return fused_impl(hidden_states, gating_output, w_gate_up, w_down, correction_bias,
                       shared_w_gate_up, shared_w_down, shared_inter, p, out, topk_ids_out,
                       topk_weights_out, workspace, workspace_bytes, stream);
+}
+
+size_t fused_moe_mxfp4_workspace_bytes(const moe_params_t *p)
+{
+    if (mx_check(p) != MOE_OK || p->num_tokens == 0)
+        return 0;
+    moe::Plan pl;
+    moe::make_plan(p, 0, &pl, moe::WEIGHTS_MXFP4);
+    return pl.total;
+}
+
+int fused_moe_mxfp4_fwd(const uint16_t *hidden_states, const float *gating_output,
+                        const uint8_t *w_gate_up_q, const uint8_t *w_gate_up_scale,
+                        const uint8_t *w_down_q, const uint8_t *w_down_scale,
+                        const float *correction_bias, const moe_params_t *p, uint16_t *out,
+                        int32_t *topk_ids_out, float *topk_weights_out, void *workspace,
+                        size_t workspace_bytes, void *stream)
+{
+    int st = mx_check(p);
+    if (st != MOE_OK)
+        return st;
+    if ((st = moe::check_routing(p, correction_bias != nullptr)) != MOE_OK)
+        return st;
+    if (p->num_tokens == 0)
+        return MOE_OK;
+    if (!hidden_states || !gating_output || !w_gate_up_q || !w_gate_up_scale || !w_down_q ||
+        !w_down_scale || !out || !workspace)
+        return MOE_ERR_NULL;
+    moe::Plan pl;
+    moe::make_plan(p, 0, &pl, moe::WEIGHTS_MXFP4);
+    if (workspace_bytes < pl.total)
+        return MOE_ERR_WORKSPACE;
+    if (!aligned16(hidden_states) || !aligned16(w_gate_up_q) || !aligned16(w_down_q) ||
+        !aligned16(out) || !aligned16(workspace))
+        return MOE_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int32_t *ids = topk_ids_out ? topk_ids_out : ws_at<int32_t>(workspace, pl.off_ids);
+    float *weights = topk_weights_out ? topk_weights_out : ws_at<float>(workspace, pl.off_weights);
+    Ctx c = {hidden_states, nullptr, nullptr, nullptr, nullptr, ids, weights, out, workspace, s};
+    c.gu_q = w_gate_up_q;
+    c.gu_s = w_gate_up_scale;
+    c.d_q = w_down_q;
+    c.d_s = w_down_scale;
+    moe::launch_route(gating_output, correction_bias, pl.T, pl.E, pl.k,
+                      p->scoring == MOE_SCORING_SIGMOID, p->renormalize, p->num_expert_group,
+                      p->topk_group, p->routed_scaling_factor, ids, weights, s);
+    return experts_impl(pl, c);
 }
 
 int fused_moe_experts_fwd(const uint16_t *hidden_states, const uint16_t *w_gate_up,

@@ -46,6 +46,8 @@ struct GemmProblem {
     int rows;                   // tokens (DENSE)
     int num_experts;            // E (valid expert ids are [0, E))
     int dtype;                  // element type of act, weight, out: 0 bf16, 1 f16
+    const uint8_t *wq;          // MXFP4 weights: [experts][n_weight_rows][K/2] e2m1 pairs
+    const uint8_t *wscale;      // MXFP4 weights: [experts][n_weight_rows][K/32] E8M0
 };
 
 // Tile shape of one launch.
@@ -75,6 +77,12 @@ bool launch_wide(bool gate_up, const GemmProblem &g, RowSource src, hipStream_t 
 // ids[e * max_m + i] = e for i < clamp(masked_m[e], 0, max_m), else -1.
 void launch_masked_ids(const int32_t *masked_m, int E, int max_m, int32_t *ids,
                        hipStream_t stream);
+
+// ---------------------------------------------------------------- MXFP4-weight GEMM
+// The weight-streaming GEMM with MXFP4 weights (g.wq, g.wscale) and bf16 activations
+// (moe_mx_kernel.h); SORTED, DIRECT or SCAN rows; K % 128 == 0.
+bool launch_mx(bool gate_up, const GemmProblem &g, RowSource src, WsTile tile,
+               hipStream_t stream);
 
 // ---------------------------------------------------------------- fp8 grouped GEMM
 // out[e, m, n] for m < masked_m[e] (moe_fp8_kernel.h); K % 128 == 0, N % 64 == 0.

@@ -60,7 +60,7 @@ int check_shared(int32_t S)
     return MOE_OK;
 }
 
-void make_plan(const moe_params_t *p, int32_t S, Plan *pl)
+void make_plan(const moe_params_t *p, int32_t S, Plan *pl, int wfmt)
 {
     pl->T = p->num_tokens;
     pl->H = p->hidden;
@@ -98,9 +98,16 @@ void make_plan(const moe_params_t *p, int32_t S, Plan *pl)
         pl->gate_up = {KERNEL_WIDE, 0, 16, 1, 2};
         pl->down = {KERNEL_WIDE, 0, 16, 1, 2};
     }
+    if (wfmt == WEIGHTS_MXFP4) {
+        // MXFP4 weights (W4A16): the weight-streaming form at every row count, 16-row passes
+        pl->gate_up = {KERNEL_MX, 1, 1, 4, 3};
+        pl->down = {KERNEL_MX, 2, 1, pl->path == MOE_PATH_DIRECT && P <= 64 ? 4 : 2, 3};
+    }
     pl->shared_gate_up = {KERNEL_WIDE, 0, 16, 1, 2};
     pl->shared_down = {KERNEL_BLOCK, 4, 8, 1, 3};
-    pl->block_m = pl->gate_up.kind == KERNEL_WS ? kSortedBlockM : 16 * pl->gate_up.mt;
+    pl->block_m = (pl->gate_up.kind == KERNEL_WS || pl->gate_up.kind == KERNEL_MX)
+                      ? kSortedBlockM
+                      : 16 * pl->gate_up.mt;
     pl->slots = P + pl->E * (pl->block_m - 1);
     pl->tiles_cap = P / pl->block_m + pl->E;
 

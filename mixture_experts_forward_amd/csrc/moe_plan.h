@@ -23,7 +23,10 @@ inline size_t align_scratch_ints(int P, int E)
     return P > kAlignChunk ? (size_t)((P + kAlignChunk - 1) / kAlignChunk) * E : 0;
 }
 
-enum KernelKind { KERNEL_WS = 0, KERNEL_TILED = 1, KERNEL_BLOCK = 2, KERNEL_WIDE = 3 };
+enum KernelKind { KERNEL_WS = 0, KERNEL_TILED = 1, KERNEL_BLOCK = 2, KERNEL_WIDE = 3, KERNEL_MX = 4 };
+
+// Weight format of the routed experts: 16-bit (bf16 / f16) or MXFP4.
+enum WeightFormat { WEIGHTS_16BIT = 0, WEIGHTS_MXFP4 = 1 };
 
 struct TileChoice {
     int kind;  // KernelKind
@@ -51,6 +54,6 @@ int check_routing(const moe_params_t *p, int bias_given);
 int check_shared(int32_t shared_inter);
 
 // Fills *plan for a valid p (checks must have passed).  S = shared_inter (0 = none).
-void make_plan(const moe_params_t *p, int32_t S, Plan *plan);
+void make_plan(const moe_params_t *p, int32_t S, Plan *plan, int wfmt = WEIGHTS_16BIT);
 
 }  // namespace moe

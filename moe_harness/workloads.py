@@ -23,6 +23,8 @@ different streams, so a test draws once and hands the same bytes to both sides.
 from dataclasses import dataclass, replace
 from typing import Optional
 
+import math
+
 import torch
 
 STREAM_HIDDEN = 1
@@ -35,6 +37,7 @@ STREAM_SHARED_DOWN = 7
 STREAM_SKEW = 8
 STREAM_MASKED_COUNTS = 11
 STREAM_FP8 = 12
+STREAM_MXFP4 = 13
 
 
 @dataclass(frozen=True)
@@ -253,3 +256,34 @@ def random_topk_weights(T: int, k: int, seed: int = 42, device="cpu") -> torch.T
 def to_u16(t: torch.Tensor):
     """bf16 tensor (any device) -> numpy uint16 bit patterns on the host."""
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view("uint16")
+
+
+def mxfp4_scale_byte(fan_in: int) -> int:
+    """E8M0 scale byte that gives MXFP4 weights of uniformly random e2m1 codes (RMS magnitude
+    sqrt(68.5/8) ~ 2.93) a standard deviation of about 1/sqrt(fan_in), like the bf16 weights."""
+    return int(round(127 + math.log2(1.0 / (math.sqrt(fan_in) * math.sqrt(68.5 / 8)))))
+
+
+def make_mxfp4_weights(cfg: MoEConfig, device="cpu", seed: int = 42) -> dict:
+    """MXFP4 expert weights of cfg's shape: w_gate_up_q [E,2F,H/2] and w_down_q [E,H,F/2] uint8
+    (two uniformly random e2m1 codes per byte), w_gate_up_scale [E,2F,H/32] and w_down_scale
+    [E,H,F/32] uint8 E8M0 scales drawn from {s0-1, s0, s0+1}, s0 = mxfp4_scale_byte(fan_in)."""
+    E, H, F = cfg.E, cfg.H, cfg.F
+    g = _gen(device, seed, STREAM_MXFP4)
+
+    def codes(shape):
+        return torch.randint(0, 256, shape, generator=g, device=device, dtype=torch.int32).to(
+            torch.uint8)
+
+    def scales(shape, fan_in):
+        s0 = mxfp4_scale_byte(fan_in)
+        return torch.randint(s0 - 1, s0 + 2, shape, generator=g, device=device,
+                             dtype=torch.int32).to(torch.uint8)
+
+    return {
+        "w_gate_up_q": codes((E, 2 * F, H // 2)),
+        "w_gate_up_scale": scales((E, 2 * F, H // 32), H),
+        "w_down_q": codes((E, H, F // 2)),
+        "w_down_scale": scales((E, H, F // 32), F),
+    }
+

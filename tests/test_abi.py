@@ -186,3 +186,22 @@ def test_fp8_contiguous_and_quant_reject_before_launch():
     assert q(4, 128, qq=ctypes.c_void_p((1 << 20) + 4)) == -3   # q not 8-byte aligned
     assert q(4, 128, x=None) == -1
     assert q(0, 128, x=None) == 0                  # M = 0: nothing to do
+
+
+def test_mxfp4_entry_points_reject_before_launch():
+    L = moe.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    ok = moe.make_params(32, 2048, 128, 768, 8)
+    n = L.fused_moe_mxfp4_workspace_bytes(ctypes.byref(ok))
+    assert n > 0
+    call = lambda p, ws, nb, hidden=fake: L.fused_moe_mxfp4_fwd(
+        hidden, fake, fake, fake, fake, fake, None, ctypes.byref(p), fake, None, None, ws, nb,
+        None)
+    assert call(moe.make_params(32, 2048, 128, 768, 8), fake, n - 1) == -4
+    assert call(moe.make_params(32, 2048, 128, 768, 8), fake, n, hidden=None) == -1
+    assert call(moe.make_params(32, 2112, 128, 768, 8), fake, 1 << 30) == -3     # H % 128
+    assert call(moe.make_params(32, 2048, 128, 704, 8), fake, 1 << 30) == -3     # F % 128
+    f16 = moe.make_params(32, 2048, 128, 768, 8, dtype=__import__("torch").float16)
+    assert call(f16, fake, 1 << 30) == -3                                        # bf16 only
+    assert L.fused_moe_mxfp4_workspace_bytes(ctypes.byref(f16)) == 0
+    assert call(moe.make_params(0, 2048, 128, 768, 8), None, 0) == 0             # T = 0

@@ -1,0 +1,83 @@
+"""GPU parity of the fused pass with MXFP4 expert weights (fused_moe_mxfp4_fwd: e2m1 codes with
+E8M0 scales per 32 elements, bf16 activations) against the oracle: the routed experts'
+computation on the dequantised weights (exact in bf16 at these scales), with the bf16 pass's
+tolerance (tests/parity.py).  Covers the direct path (route and scan workgroups), the sorted
+path, several 16-row passes per expert and full qwen3-30b decode dimensions on sampled
+tokens."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_forward_amd as moe
+import oracle
+from moe_harness.workloads import CONFIGS, make_inputs, make_mxfp4_weights, to_u16
+from parity import WEIGHT_ATOL, assert_output_close, oracle_route, sample_tokens
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _oracle_mx(d, mx, ids, w, tokens):
+    """oracle output for `tokens` from the dequantised weights of the experts they use"""
+    E = mx["w_gate_up_q"].shape[0]
+    sub = ids[tokens]
+    used = np.unique(sub[(sub >= 0) & (sub < E)])
+    remap = np.full(E, -1, np.int64)
+    remap[used] = np.arange(used.size)
+    local = np.where((sub >= 0) & (sub < E), remap[np.clip(sub, 0, E - 1)], -1).astype(np.int32)
+    sel = torch.as_tensor(used, device=DEV, dtype=torch.long)
+    host = {k: v.index_select(0, sel).cpu().numpy() for k, v in mx.items()}
+    wgu = oracle.mxfp4_to_bf16(host["w_gate_up_q"], host["w_gate_up_scale"])
+    wd = oracle.mxfp4_to_bf16(host["w_down_q"], host["w_down_scale"])
+    x = to_u16(d["hidden_states"][torch.as_tensor(tokens, device=DEV)])
+    return oracle.experts(x, wgu, wd, local, np.asarray(w, np.float32)[tokens])
+
+
+def _check(cfg, d, mx, path, tokens=None, what=""):
+    out, ids, w = moe.fused_moe_mxfp4_fwd(
+        d["hidden_states"], d["gating_output"], mx["w_gate_up_q"], mx["w_gate_up_scale"],
+        mx["w_down_q"], mx["w_down_scale"], cfg.k, d.get("correction_bias"), cfg.scoring,
+        cfg.renormalize, cfg.num_expert_group, cfg.topk_group, cfg.rsf, path=path,
+        return_routing=True)
+    torch.cuda.synchronize()
+    rid, rw = oracle_route(d, cfg)
+    assert np.array_equal(ids.cpu().numpy(), rid), "%s: routing ids differ" % what
+    assert np.max(np.abs(w.cpu().numpy().astype(np.float64) - rw)) <= WEIGHT_ATOL
+    tokens = np.arange(cfg.T) if tokens is None else np.asarray(tokens)
+    _, ref = _oracle_mx(d, mx, rid, rw, tokens)
+    rel = assert_output_close(out[torch.as_tensor(tokens, device=DEV)], ref, what)
+    print("%s: rel-L2 %.2e" % (what, rel), flush=True)
+
+
+@pytest.mark.parametrize("T,path", [(4, "auto"), (4, "direct"), (4, "sorted"), (40, "direct"),
+                                    (40, "sorted"), (1, "direct")])
+def test_mxfp4_small(T, path):
+    cfg = replace(CONFIGS["tiny"], T=T, H=256, E=8, F=128, k=2)
+    d = make_inputs(cfg, DEV, seed=T, weights=False)
+    mx = make_mxfp4_weights(cfg, DEV, seed=T)
+    _check(cfg, d, mx, path, what="mxfp4 T=%d %s" % (T, path))
+
+
+def test_mxfp4_several_passes_per_expert():
+    # about 64 rows per expert: four 16-row passes, each streaming the weights again
+    cfg = replace(CONFIGS["tiny"], T=128, H=256, E=4, F=256, k=2)
+    d = make_inputs(cfg, DEV, seed=5, weights=False)
+    mx = make_mxfp4_weights(cfg, DEV, seed=5)
+    _check(cfg, d, mx, "sorted", what="mxfp4 multi-pass")
+
+
+@pytest.mark.parametrize("T,path", [(1, "direct"), (32, "direct"), (32, "sorted")])
+def test_mxfp4_qwen3_30b_decode_sampled(T, path):
+    cfg = replace(CONFIGS["qwen3-30b-decode"], T=T)
+    d = make_inputs(cfg, DEV, seed=300 + T, weights=False)
+    mx = make_mxfp4_weights(cfg, DEV, seed=7)
+    _check(cfg, d, mx, path, sample_tokens(T, 3), "mxfp4 qwen3-30b T=%d %s" % (T, path))
+
+
+def test_mxfp4_grouped_sigmoid_routing():
+    cfg = replace(CONFIGS["ds-v3-grouped-prefill"], T=24, H=256, E=32, F=128)
+    d = make_inputs(cfg, DEV, seed=9, weights=False)
+    mx = make_mxfp4_weights(cfg, DEV, seed=9)
+    _check(cfg, d, mx, "auto", what="mxfp4 grouped sigmoid")

@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--config", default=None)
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "f16"],
                     help="element type of the fused pass (activations, weights, output)")
+    ap.add_argument("--weights", default="16bit", choices=["16bit", "mxfp4"],
+                    help="expert weight format: the pass's element type, or MXFP4 (bf16 "
+                         "activations)")
     ap.add_argument("--rotate", type=int, default=0, help="input sets (0 = automatic)")
     ap.add_argument("--path", default="auto", choices=["auto", "direct", "sorted"],
                     help="the library's path choice (auto: its own rule)")
@@ -85,7 +88,7 @@ def main():
     import mixture_experts_forward_amd as moe
     from moe_harness import perfmodel
     from moe_harness.workloads import (BENCH_CONFIG, CONFIGS, FP8_CONFIGS, MASKED_CONFIGS,
-                                       make_inputs)
+                                       make_inputs, make_mxfp4_weights)
 
     if args.config in MASKED_CONFIGS:
         bench_masked(args, MASKED_CONFIGS[args.config])
@@ -98,11 +101,24 @@ def main():
     torch.cuda.set_device(dev)
     moe.lib()
 
-    wbytes = cfg.E * 6.0 * cfg.H * cfg.F + 6.0 * cfg.H * cfg.S
+    mx = args.weights == "mxfp4"
+    if mx and (cfg.S > 0 or args.dtype != "bf16"):
+        sys.exit("--weights mxfp4 takes bf16 activations and no shared expert")
+    # bytes per routed expert's weights: 16-bit, or MXFP4 (half a byte per element plus one
+    # scale byte per 32)
+    wfac = 17.0 / 32.0 / 2.0 if mx else 1.0
+    wbytes = cfg.E * 6.0 * cfg.H * cfg.F * wfac + 6.0 * cfg.H * cfg.S
     R = args.rotate or max(1, min(8, math.ceil(16 * LLC_BYTES / wbytes)))
     log("workload %s, %d input sets of %.2f GB weights" % (cfg.name, R, wbytes / 1e9))
     tdt = torch.float16 if args.dtype == "f16" else torch.bfloat16
-    sets = [make_inputs(cfg, dev, seed=42 + i, dtype=tdt) for i in range(R)]
+    if mx:
+        sets = []
+        for i in range(R):
+            d = make_inputs(cfg, dev, seed=42 + i, weights=False)
+            d.update(make_mxfp4_weights(cfg, dev, seed=42 + i))
+            sets.append(d)
+    else:
+        sets = [make_inputs(cfg, dev, seed=42 + i, dtype=tdt) for i in range(R)]
     torch.cuda.synchronize()
     if args.copy_calibration:
         src = torch.ones(args.copy_calibration, dtype=torch.uint8, device=dev)
@@ -116,14 +132,21 @@ def main():
     p = moe.make_params(cfg.T, cfg.H, cfg.E, cfg.F, cfg.k, cfg.scoring, cfg.renormalize,
                         cfg.num_expert_group, cfg.topk_group, cfg.rsf, path=args.path,
                         dtype=tdt)
-    ws = torch.empty(max(256, moe.workspace_bytes(p, S)), dtype=torch.uint8, device=dev)
+    ws_need = moe.mxfp4_workspace_bytes(p) if mx else moe.workspace_bytes(p, S)
+    ws = torch.empty(max(256, ws_need), dtype=torch.uint8, device=dev)
     out = torch.empty((cfg.T, cfg.H), dtype=tdt, device=dev)
     ids = [torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev) for _ in range(R)]
     wts = [torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev) for _ in range(R)]
 
     def fused_step(i):
         d = sets[i % R]
-        if S > 0:
+        if mx:
+            moe.fused_moe_mxfp4_fwd(d["hidden_states"], d["gating_output"], d["w_gate_up_q"],
+                                    d["w_gate_up_scale"], d["w_down_q"], d["w_down_scale"],
+                                    cfg.k, d["correction_bias"], cfg.scoring, cfg.renormalize,
+                                    cfg.num_expert_group, cfg.topk_group, cfg.rsf,
+                                    path=args.path, out=out, workspace=ws)
+        elif S > 0:
             moe.fused_moe_shared_fwd(d["hidden_states"], d["gating_output"], d["w_gate_up"],
                                      d["w_down"], d["shared_w_gate_up"], d["shared_w_down"],
                                      cfg.k, d["correction_bias"], cfg.scoring, cfg.renormalize,
@@ -154,9 +177,12 @@ def main():
         if events is not None:
             events[1].record()
         for n, s in enumerate(stages):
-            moe.fused_moe_experts_stage(s, p, d["hidden_states"], d["w_gate_up"], d["w_down"],
-                                        ids[j], wts[j], out, ws, d.get("shared_w_gate_up"),
-                                        d.get("shared_w_down"))
+            if mx:
+                moe.fused_moe_mxfp4_stage(s, p, d["hidden_states"], d, ids[j], wts[j], out, ws)
+            else:
+                moe.fused_moe_experts_stage(s, p, d["hidden_states"], d["w_gate_up"],
+                                            d["w_down"], ids[j], wts[j], out, ws,
+                                            d.get("shared_w_gate_up"), d.get("shared_w_down"))
             if events is not None:
                 events[n + 2].record()
 
@@ -254,8 +280,10 @@ def main():
     P = cfg.T * cfg.k
     pass_bytes = perfmodel.algorithmic_bytes(cfg.T, cfg.H, cfg.E, cfg.F, cfg.k, touched_mean,
                                              cfg.S, cfg.bias)
+    # MXFP4: the touched experts' weights shrink to 17/64 of their bf16 bytes
+    pass_bytes -= touched_mean * 6.0 * cfg.H * cfg.F * (1.0 - wfac)
     pass_flops = perfmodel.flops(cfg.T, cfg.k, cfg.H, cfg.F, cfg.S)
-    gu_bytes = touched_mean * 4.0 * cfg.H * cfg.F + 2.0 * cfg.T * cfg.H + 2.0 * P * cfg.F
+    gu_bytes = touched_mean * 4.0 * cfg.H * cfg.F * wfac + 2.0 * cfg.T * cfg.H + 2.0 * P * cfg.F
     gu_flops = 2.0 * P * 2 * cfg.F * cfg.H
     gu_ms = per_stage["gate_up"]
     gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
@@ -265,15 +293,16 @@ def main():
     # the gate-up kernel's own bound: its bytes at 8 TB/s or its FLOPs at the bf16 MFMA peak
     gu_mfma_bound = gu_flops / perfmodel.BF16_MFMA_PEAK_FLOP_PER_S > \
         gu_bytes / perfmodel.HBM_PEAK_BYTES_PER_S
-    # the committed counter summaries are of the bf16 kernels
-    traffic = read_traffic(cfg.name) if args.dtype == "bf16" else None
+    # the committed counter summaries are of the bf16 kernels with bf16 weights
+    traffic = read_traffic(cfg.name) if args.dtype == "bf16" and not mx else None
 
     # ---- CPU baseline: the oracle on this host
     cpu = None if args.no_cpu_baseline else cpu_baseline(cfg, sets[0], args.cpu_seconds,
                                                          args.dtype)
+    base = None if mx else BASELINE_MS.get(
+        cfg.name if args.dtype == "bf16" else cfg.name + ":" + args.dtype)
 
     ms = fused_ms
-    base = BASELINE_MS.get(cfg.name if args.dtype == "bf16" else cfg.name + ":" + args.dtype)
     t_hbm = pass_bytes / perfmodel.HBM_PEAK_BYTES_PER_S
     t_mfma = pass_flops / perfmodel.BF16_MFMA_PEAK_FLOP_PER_S
     floor_ms = max(t_hbm, t_mfma) * 1e3
@@ -294,7 +323,8 @@ def main():
                    "top_k": cfg.k, "scoring": cfg.scoring, "renormalize": cfg.renormalize,
                    "num_expert_group": cfg.num_expert_group, "topk_group": cfg.topk_group,
                    "routed_scaling_factor": cfg.rsf, "correction_bias": cfg.bias,
-                   "shared_inter": cfg.S, "path": args.path, "parallelism": "single GPU"},
+                   "shared_inter": cfg.S, "path": args.path, "weights": args.weights,
+                   "parallelism": "single GPU"},
         "achieved_tbps": round(pass_bytes / (ms * 1e-3) / 1e12, 4),
         "achieved_tflops": round(pass_flops / (ms * 1e-3) / 1e12, 3),
         "hbm_roofline_frac": round(pass_bytes / (ms * 1e-3) / perfmodel.HBM_PEAK_BYTES_PER_S, 4),
@@ -565,6 +595,16 @@ BASELINE_MS = {
                          "qwen3-235b-decode bf16", "hardware": "not named on the page"},
     "qwen3-235b-batch:f16": {"ms": 1.2004, "source": "TileOPs MoE page, FusedMoEFwd "
                              "qwen3-235b-decode f16", "hardware": "not named on the page"},
+    "qwen3-30b-decode-b1": {"ms": 0.0396, "source": "TileOPs MoE page, FusedMoEFwd "
+                            "qwen3-30b-decode-b1 bf16", "hardware": "not named on the page"},
+    "qwen3-235b-prefill": {"ms": 2.5018, "source": "TileOPs MoE page, FusedMoEFwd "
+                           "qwen3-235b-prefill bf16", "hardware": "not named on the page"},
+    "ds-v3-grouped-decode": {"ms": 3.7285, "source": "TileOPs MoE page, FusedMoEFwd "
+                             "ds-v3-grouped-decode bf16", "hardware": "not named on the page"},
+    "kimi-k2-decode": {"ms": 3.6029, "source": "TileOPs MoE page, FusedMoEFwd kimi-k2-decode "
+                       "bf16", "hardware": "not named on the page"},
+    "kimi-k2-prefill": {"ms": 6.9423, "source": "TileOPs MoE page, FusedMoEFwd kimi-k2-prefill "
+                        "bf16", "hardware": "not named on the page"},
     "ds-v3-grouped-prefill": {"ms": 7.1078, "source": "TileOPs MoE page, FusedMoEFwd "
                               "ds-v3-grouped-prefill bf16", "hardware": "not named on the page"},
     "kimi-k2-shared": {"ms": 5.0723, "source": "TileOPs MoE page, FusedMoESharedExpertFwd "
@@ -730,9 +770,18 @@ def cpu_baseline(cfg, d, seconds, dtype="bf16"):
     route_s = time.perf_counter() - t0
     import torch
     used = np.unique(ids)
-    sel = torch.as_tensor(used, device=d["w_gate_up"].device)
-    wgu = to_u16(d["w_gate_up"].index_select(0, sel))
-    wd = to_u16(d["w_down"].index_select(0, sel))
+    if "w_gate_up_q" in d:  # MXFP4 weights: the oracle dequantises the used experts first
+        sel = torch.as_tensor(used, device=d["w_gate_up_q"].device)
+        host = {k: d[k].index_select(0, sel).cpu().numpy() for k in
+                ("w_gate_up_q", "w_gate_up_scale", "w_down_q", "w_down_scale")}
+        t0 = time.perf_counter()
+        wgu = oracle.mxfp4_to_bf16(host["w_gate_up_q"], host["w_gate_up_scale"])
+        wd = oracle.mxfp4_to_bf16(host["w_down_q"], host["w_down_scale"])
+        route_s += time.perf_counter() - t0
+    else:
+        sel = torch.as_tensor(used, device=d["w_gate_up"].device)
+        wgu = to_u16(d["w_gate_up"].index_select(0, sel))
+        wd = to_u16(d["w_down"].index_select(0, sel))
     remap = np.full(cfg.E, -1, np.int64)
     remap[used] = np.arange(used.size)
     lids = remap[ids].astype(np.int32)

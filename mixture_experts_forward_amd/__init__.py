@@ -63,6 +63,8 @@ SIGNATURES = {
     "fused_moe_workspace_bytes": (_SZ, [_P, _I32]),
     "fused_moe_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "fused_moe_mxfp4_workspace_bytes": (_SZ, [_P]),
+    "fused_moe_mxfp4_stage": (ctypes.c_int, [_I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
+                                             _P]),
     "fused_moe_mxfp4_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                            _SZ, _P]),
     "fused_moe_shared_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P,
@@ -480,4 +482,24 @@ def fused_moe_mxfp4_fwd(hidden_states, gating_output, w_gate_up_q, w_gate_up_sca
     if return_routing:
         return out, ids, w
     return out
+
+
+def fused_moe_mxfp4_stage(stage, params, hidden_states, mx, topk_ids, topk_weights, out,
+                          workspace):
+    """One stage of the MXFP4 expert part (see include/moe.h): ``mx`` holds w_gate_up_q,
+    w_gate_up_scale, w_down_q, w_down_scale; ``params`` a MoEParams; the workspace at least
+    fused_moe_mxfp4_workspace_bytes(params) bytes.  Tensors are assumed checked by the caller."""
+    dev = hidden_states.device
+    with torch.cuda.device(dev):
+        st = lib().fused_moe_mxfp4_stage(
+            int(stage), _ptr(hidden_states), _ptr(mx["w_gate_up_q"]),
+            _ptr(mx["w_gate_up_scale"]), _ptr(mx["w_down_q"]), _ptr(mx["w_down_scale"]),
+            _ptr(topk_ids), _ptr(topk_weights), ctypes.byref(params), _ptr(out),
+            _ptr(workspace), workspace.numel(), _stream(dev))
+    if st != MOE_OK:
+        raise MoEError(st, "fused_moe_mxfp4_stage(%s)" % STAGE_NAMES.get(stage, stage))
+
+
+def mxfp4_workspace_bytes(params):
+    return int(lib().fused_moe_mxfp4_workspace_bytes(ctypes.byref(params)))
 

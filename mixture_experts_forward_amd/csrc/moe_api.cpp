@@ -448,6 +448,41 @@ int fused_moe_experts_stage(int stage, const uint16_t *hidden_states, const uint
     return run_stage(stage, pl, c);
 }
 
+int fused_moe_mxfp4_stage(int stage, const uint16_t *hidden_states, const uint8_t *w_gate_up_q,
+                          const uint8_t *w_gate_up_scale, const uint8_t *w_down_q,
+                          const uint8_t *w_down_scale, const int32_t *topk_ids,
+                          const float *topk_weights, const moe_params_t *p, uint16_t *out,
+                          void *workspace, size_t workspace_bytes, void *stream)
+{
+    int st = mx_check(p);
+    if (st != MOE_OK)
+        return st;
+    if (stage < MOE_STAGE_ALIGN || stage > MOE_STAGE_COMBINE || stage == MOE_STAGE_SHARED)
+        return MOE_ERR_UNSUPPORTED;
+    if (p->num_tokens == 0)
+        return MOE_OK;
+    if (!workspace || !topk_ids || (stage == MOE_STAGE_GATE_UP && !hidden_states) ||
+        (stage == MOE_STAGE_GATE_UP && (!w_gate_up_q || !w_gate_up_scale)) ||
+        (stage == MOE_STAGE_DOWN && (!w_down_q || !w_down_scale)) ||
+        (stage == MOE_STAGE_COMBINE && (!topk_weights || !out)))
+        return MOE_ERR_NULL;
+    moe::Plan pl;
+    moe::make_plan(p, 0, &pl, moe::WEIGHTS_MXFP4);
+    if (workspace_bytes < pl.total)
+        return MOE_ERR_WORKSPACE;
+    if (!aligned16(workspace) || (hidden_states && !aligned16(hidden_states)) ||
+        (w_gate_up_q && !aligned16(w_gate_up_q)) || (w_down_q && !aligned16(w_down_q)) ||
+        (out && !aligned16(out)))
+        return MOE_ERR_UNSUPPORTED;
+    Ctx c = {hidden_states, nullptr, nullptr, nullptr, nullptr, topk_ids, topk_weights, out,
+             workspace, static_cast<hipStream_t>(stream)};
+    c.gu_q = w_gate_up_q;
+    c.gu_s = w_gate_up_scale;
+    c.d_q = w_down_q;
+    c.d_s = w_down_scale;
+    return run_stage(stage, pl, c);
+}
+
 }  // extern "C"
 
 // ---------------------------------------------------------------- masked layout

@@ -100,8 +100,8 @@ void make_plan(const moe_params_t *p, int32_t S, Plan *pl, int wfmt)
     }
     if (wfmt == WEIGHTS_MXFP4) {
         // MXFP4 weights (W4A16): the weight-streaming form at every row count, 16-row passes
-        pl->gate_up = {KERNEL_MX, 1, 1, 4, 3};
-        pl->down = {KERNEL_MX, 2, 1, pl->path == MOE_PATH_DIRECT && P <= 64 ? 4 : 2, 3};
+        pl->gate_up = {KERNEL_MX, 1, 1, 2, 3};
+        pl->down = {KERNEL_MX, 2, 1, 2, 3};
     }
     pl->shared_gate_up = {KERNEL_WIDE, 0, 16, 1, 2};
     pl->shared_down = {KERNEL_BLOCK, 4, 8, 1, 3};

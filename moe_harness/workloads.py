@@ -69,6 +69,17 @@ CONFIGS = {
                                        topk_group=4, rsf=2.5, bias=True),
     "kimi-k2-shared": MoEConfig("kimi-k2-shared", T=512, H=7168, E=384, F=2048, k=8,
                                 scoring="sigmoid", rsf=2.827, bias=True, S=18432),
+    # further TileOPs FusedMoEFwd rows (the page's Kimi-K2 rows without the shared expert list
+    # E = 256)
+    "qwen3-30b-decode-b1": MoEConfig("qwen3-30b-decode-b1", T=1, H=2048, E=128, F=768, k=8),
+    "qwen3-235b-prefill": MoEConfig("qwen3-235b-prefill", T=4096, H=4096, E=128, F=1536, k=8),
+    "ds-v3-grouped-decode": MoEConfig("ds-v3-grouped-decode", T=512, H=7168, E=256, F=2048,
+                                      k=8, scoring="sigmoid", num_expert_group=8,
+                                      topk_group=4, rsf=2.5, bias=True),
+    "kimi-k2-decode": MoEConfig("kimi-k2-decode", T=512, H=7168, E=256, F=2048, k=8,
+                                scoring="sigmoid", rsf=2.827, bias=True),
+    "kimi-k2-prefill": MoEConfig("kimi-k2-prefill", T=4096, H=7168, E=256, F=2048, k=8,
+                                 scoring="sigmoid", rsf=2.827, bias=True),
     # DeepSeek-V3 routing and dimensions at 16384 tokens: about 500 routed rows per expert, so
     # about 500 FLOP per weight byte, above the MI355X ridge (2.5 PFLOP/s / 8 TB/s = 312): the
     # expert GEMMs are MFMA-bound here, unlike at 4096 tokens

@@ -22,6 +22,8 @@ Functions (each follows the passage cited in ``moe_oracle.c``):
   grouped_gemm_fp8_contiguous(a, a_scale, b, b_scale, offsets) -> (acc [P,N], out uint16 [P,N])
   double_to_bf16(values) -> uint16 (one rounding, nearest-even)
   double_to_f16(values) -> uint16 binary16 bits (one rounding, nearest-even)
+  fp8_forward(x, gating, w_gate_up, w_gate_up_scale, w_down, w_down_scale, ...)
+      -> the FP8 pass (1 x 128 activation groups, 128 x 128 weight blocks) for ``tokens``
   mxfp4_dequant(q, scale) -> float64 weights of MXFP4 codes and E8M0 block scales
   mxfp4_to_bf16(q, scale) -> the same values as bf16 bits (exact)
 """
@@ -271,6 +273,47 @@ def grouped_gemm_fp8_contiguous(a, a_scale, b, b_scale, offsets):
     if rc != 0:
         raise ValueError("oracle_grouped_gemm_fp8_contig rejected its arguments (%d)" % rc)
     return acc, out
+
+
+def fp8_forward(x, gating, w_gate_up, w_gate_up_scale, w_down, w_down_scale, bias=None, k=2,
+                scoring="softmax", renormalize=True, num_expert_group=1, topk_group=1, rsf=1.0,
+                tokens=None):
+    """The MoE pass with FP8 expert weights (e4m3 codes with f32 scales per 128 x 128 block),
+    step by step: route; each routed x row quantised per 1 x 128 group (quant_fp8_1x128); per
+    expert the gate-up block-scaled GEMM (grouped_gemm_fp8_contiguous), rounded to bf16; h =
+    bf16(SiLU(gate) * up) (reading: h is stored in bf16 before it is quantised, as the 16-bit
+    passes store it) quantised the same way; the down GEMM; out[t] = bf16(sum_j w_j y_j) from the
+    unrounded down sums.  x [T,H] bf16 bits; returns (topk_ids, topk_weights, out [n,H] bf16
+    bits) for ``tokens`` (default all)."""
+    x = _c(x, np.uint16)
+    T, H = x.shape
+    E, F2 = w_gate_up.shape[0], w_gate_up.shape[1]
+    F = F2 // 2
+    ids, w = route(gating, bias, k, scoring, renormalize, num_expert_group, topk_group, rsf)
+    tok = np.arange(T) if tokens is None else np.asarray(tokens, np.int64)
+    routes = [(int(t), j) for t in tok for j in range(k) if 0 <= ids[t, j] < E]
+    order = sorted(range(len(routes)), key=lambda i: (ids[routes[i][0], routes[i][1]], i))
+    routes = [routes[i] for i in order]
+    counts = np.bincount([ids[t, j] for t, j in routes], minlength=E) if routes else \
+        np.zeros(E, np.int64)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    rows = np.array([x[t] for t, j in routes], np.uint16).reshape(len(routes), H)
+    xq, xs = quant_fp8_1x128(rows) if routes else (np.zeros((0, H), np.uint8),
+                                                     np.zeros((0, H // 128), np.float32))
+    _, gu = grouped_gemm_fp8_contiguous(xq, xs, w_gate_up, w_gate_up_scale, offsets)
+    g = bf16_bits_to_float(gu[:, :F]).astype(np.float64)
+    u = bf16_bits_to_float(gu[:, F:]).astype(np.float64)
+    h = double_to_bf16(g / (1.0 + np.exp(-g)) * u) if routes else np.zeros((0, F), np.uint16)
+    hq, hs = quant_fp8_1x128(h) if routes else (np.zeros((0, F), np.uint8),
+                                                  np.zeros((0, F // 128), np.float32))
+    y, _ = grouped_gemm_fp8_contiguous(hq, hs, w_down, w_down_scale, offsets)
+    acc = np.zeros((len(tok), H))
+    row_of = {(t, j): r for r, (t, j) in enumerate(routes)}  # the sum runs in route order j
+    for i, t in enumerate(tok.tolist()):
+        for j in range(k):
+            if (t, j) in row_of:
+                acc[i] += float(w[t, j]) * y[row_of[(t, j)]]
+    return ids, w, double_to_bf16(acc)
 
 
 def mxfp4_dequant(q, scale):

@@ -273,6 +273,29 @@ int fused_moe_mxfp4_stage(int stage, const uint16_t *hidden_states, const uint8_
                           void *workspace, size_t workspace_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------------------
+ * fused_moe_fp8_fwd -- fused_moe_fwd with FP8 expert weights: OCP e4m3 codes with f32 scales
+ * per 128 x 128 weight block (TileOPs "MoE" page, MoEGroupedGemmFP8Fwd's b / b_scale), and the
+ * bf16 activations quantised per 1 x 128 group on the way in (moe_quant_fp8's rule).
+ *   w_gate_up        [E, 2F, H] uint8 e4m3 (rows [0,F) gate, [F,2F) up);
+ *   w_gate_up_scale  [E, 2F/128, H/128] f32;
+ *   w_down           [E, H, F] uint8 e4m3; w_down_scale [E, H/128, F/128] f32.
+ * The pass: route; the routes in expert order (align with block_m 1); each route's x row
+ * quantised (moe_quant_fp8) in that order; the gate-up GEMM as moe_grouped_gemm_fp8_contiguous
+ * (bf16 gate and up); h = bf16(SiLU(gate) * up) quantised the same way; the down GEMM (bf16
+ * rows); the weighted combine of fused_moe_fwd.  Needs p->dtype == MOE_DTYPE_BF16,
+ * H % 128 == 0, F % 128 == 0, no shared expert; 16-byte aligned hidden_states, weights, out
+ * and workspace, 4-byte aligned scales.
+ * Workspace: fused_moe_fp8_workspace_bytes(p) bytes.
+ * Errors: as fused_moe_fwd. */
+size_t fused_moe_fp8_workspace_bytes(const moe_params_t *p);
+int fused_moe_fp8_fwd(const uint16_t *hidden_states, const float *gating_output,
+                      const uint8_t *w_gate_up, const float *w_gate_up_scale,
+                      const uint8_t *w_down, const float *w_down_scale,
+                      const float *correction_bias, const moe_params_t *p, uint16_t *out,
+                      int32_t *topk_ids_out, float *topk_weights_out, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------
  * Masked layout: the expert MLPs of one expert-parallel shard (TileOPs "MoE" page,
  * MoEGroupedGemmFwd with a: [E, layout.max_m, K] and layout_metadata [E] i32, workload
  * ds-v3-ep8-masked; MoEPrePermuteFwd's num_local_experts).  Local expert e owns the row block

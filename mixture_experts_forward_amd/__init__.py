@@ -18,6 +18,8 @@ Entry points (same names as the C ABI):
   moe_quant_fp8(x)                                            -> (q [M, K] e4m3, scale [M, K/128])
   fused_moe_mxfp4_fwd(hidden, gating, w_gate_up_q, w_gate_up_scale, w_down_q, w_down_scale,
                       top_k, ...)                             -> out [T, H] bf16 (MXFP4 weights)
+  fused_moe_fp8_fwd(hidden, gating, w_gate_up, w_gate_up_scale, w_down, w_down_scale, top_k, ...)
+                                                              -> out [T, H] bf16 (FP8 weights)
 """
 import ctypes
 import os
@@ -63,6 +65,9 @@ SIGNATURES = {
     "fused_moe_workspace_bytes": (_SZ, [_P, _I32]),
     "fused_moe_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "fused_moe_mxfp4_workspace_bytes": (_SZ, [_P]),
+    "fused_moe_fp8_workspace_bytes": (_SZ, [_P]),
+    "fused_moe_fp8_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
+                                         _P]),
     "fused_moe_mxfp4_stage": (ctypes.c_int, [_I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
                                              _P]),
     "fused_moe_mxfp4_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -502,4 +507,50 @@ def fused_moe_mxfp4_stage(stage, params, hidden_states, mx, topk_ids, topk_weigh
 
 def mxfp4_workspace_bytes(params):
     return int(lib().fused_moe_mxfp4_workspace_bytes(ctypes.byref(params)))
+
+
+def fused_moe_fp8_fwd(hidden_states, gating_output, w_gate_up, w_gate_up_scale, w_down,
+                      w_down_scale, top_k, correction_bias=None, scoring="softmax",
+                      renormalize=True, num_expert_group=1, topk_group=1,
+                      routed_scaling_factor=1.0, out=None, workspace=None,
+                      return_routing=False):
+    """The fused pass with FP8 expert weights: w_gate_up [E,2F,H] / w_down [E,H,F] e4m3
+    (torch.float8_e4m3fn or uint8 codes) with f32 scales [E,2F/128,H/128] / [E,H/128,F/128];
+    bf16 activations quantised per 1 x 128 group on the way in."""
+    T, H = hidden_states.shape
+    codes = lambda t: t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t
+    wgu, wd = codes(w_gate_up), codes(w_down)
+    E, F2, _ = wgu.shape
+    F = F2 // 2
+    dev = hidden_states.device
+    _check(hidden_states, "hidden_states", torch.bfloat16, (T, H))
+    _check(gating_output, "gating_output", torch.float32, (T, E), dev)
+    _check(wgu, "w_gate_up", torch.uint8, (E, 2 * F, H), dev)
+    _check(w_gate_up_scale, "w_gate_up_scale", torch.float32, (E, 2 * F // 128, H // 128), dev)
+    _check(wd, "w_down", torch.uint8, (E, H, F), dev)
+    _check(w_down_scale, "w_down_scale", torch.float32, (E, H // 128, F // 128), dev)
+    if correction_bias is not None:
+        _check(correction_bias, "correction_bias", torch.float32, (E,), dev)
+    p = make_params(T, H, E, F, top_k, scoring, renormalize, num_expert_group, topk_group,
+                    routed_scaling_factor)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _check(out, "out", torch.bfloat16, (T, H), dev)
+    ids = torch.empty((T, top_k), dtype=torch.int32, device=dev) if return_routing else None
+    w = torch.empty((T, top_k), dtype=torch.float32, device=dev) if return_routing else None
+    with torch.cuda.device(dev):
+        n = int(lib().fused_moe_fp8_workspace_bytes(ctypes.byref(p)))
+        if workspace is None:
+            workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+        elif workspace.dtype != torch.uint8 or workspace.numel() < n:
+            raise ValueError("workspace must be a uint8 tensor with >= %d bytes" % n)
+        st = lib().fused_moe_fp8_fwd(
+            _ptr(hidden_states), _ptr(gating_output), _ptr(wgu), _ptr(w_gate_up_scale), _ptr(wd),
+            _ptr(w_down_scale), _ptr(correction_bias), ctypes.byref(p), _ptr(out), _ptr(ids),
+            _ptr(w), _ptr(workspace), workspace.numel(), _stream(dev))
+    if st != MOE_OK:
+        raise MoEError(st, "fused_moe_fp8_fwd")
+    if return_routing:
+        return out, ids, w
+    return out
 

@@ -385,6 +385,57 @@ int fused_moe_mxfp4_fwd(const uint16_t *hidden_states, const float *gating_outpu
     return experts_impl(pl, c);
 }
 
+// ---- the FP8 pass: routed rows quantised per 1 x 128 group, block-scaled FP8 expert GEMMs on
+// the contiguous (tight, expert-ordered) layout
+struct Fp8Pass {
+    int T, H, E, F, k, P;
+    size_t off_ids, off_weights, off_sorted, off_offsets, off_tile_expert, off_inverse,
+        off_n_tiles, off_align, off_aq, off_as, off_gu, off_hq, off_hs, off_y, total;
+};
+
+int fp8_check(const moe_params_t *p)
+{
+    int st = moe::check_dims(p);
+    if (st != MOE_OK)
+        return st;
+    if (p->dtype != MOE_DTYPE_BF16 || p->hidden % 128 != 0 || p->inter % 128 != 0)
+        return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+void fp8_plan(const moe_params_t *p, Fp8Pass *f)
+{
+    f->T = p->num_tokens;
+    f->H = p->hidden;
+    f->E = p->num_experts;
+    f->F = p->inter;
+    f->k = p->top_k;
+    f->P = f->T * f->k;
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o = (o + bytes + 255) / 256 * 256;
+        return at;
+    };
+    const size_t P = f->P;
+    f->off_ids = take(P * 4);
+    f->off_weights = take(P * 4);
+    f->off_sorted = take(P * 4);                      // block_m 1: no padding slots
+    f->off_offsets = take((size_t)(f->E + 1) * 4);
+    f->off_tile_expert = take((P + f->E) * 4);
+    f->off_inverse = take(P * 4);
+    f->off_n_tiles = take(4);
+    const size_t scratch = moe::align_scratch_ints(f->P, f->E);
+    f->off_align = scratch ? take(scratch * 4) : 0;
+    f->off_aq = take(P * f->H);
+    f->off_as = take(P * (f->H / 128) * 4);
+    f->off_gu = take(P * 2 * f->F * 2);
+    f->off_hq = take(P * f->F);
+    f->off_hs = take(P * (f->F / 128) * 4);
+    f->off_y = take(P * f->H * 2);
+    f->total = o;
+}
+
 int fused_moe_experts_fwd(const uint16_t *hidden_states, const uint16_t *w_gate_up,
                           const uint16_t *w_down, const int32_t *topk_ids,
                           const float *topk_weights, const moe_params_t *p, uint16_t *out,
@@ -481,6 +532,72 @@ int fused_moe_mxfp4_stage(int stage, const uint16_t *hidden_states, const uint8_
     c.d_q = w_down_q;
     c.d_s = w_down_scale;
     return run_stage(stage, pl, c);
+}
+
+size_t fused_moe_fp8_workspace_bytes(const moe_params_t *p)
+{
+    if (fp8_check(p) != MOE_OK || p->num_tokens == 0)
+        return 0;
+    Fp8Pass f;
+    fp8_plan(p, &f);
+    return f.total;
+}
+
+int fused_moe_fp8_fwd(const uint16_t *hidden_states, const float *gating_output,
+                      const uint8_t *w_gate_up, const float *w_gate_up_scale,
+                      const uint8_t *w_down, const float *w_down_scale,
+                      const float *correction_bias, const moe_params_t *p, uint16_t *out,
+                      int32_t *topk_ids_out, float *topk_weights_out, void *workspace,
+                      size_t workspace_bytes, void *stream)
+{
+    int st = fp8_check(p);
+    if (st != MOE_OK)
+        return st;
+    if ((st = moe::check_routing(p, correction_bias != nullptr)) != MOE_OK)
+        return st;
+    if (p->num_tokens == 0)
+        return MOE_OK;
+    if (!hidden_states || !gating_output || !w_gate_up || !w_gate_up_scale || !w_down ||
+        !w_down_scale || !out || !workspace)
+        return MOE_ERR_NULL;
+    Fp8Pass f;
+    fp8_plan(p, &f);
+    if (workspace_bytes < f.total)
+        return MOE_ERR_WORKSPACE;
+    if (!aligned16(hidden_states) || !aligned16(w_gate_up) || !aligned16(w_down) ||
+        !aligned16(out) || !aligned16(workspace) || ((uintptr_t)w_gate_up_scale & 3u) ||
+        ((uintptr_t)w_down_scale & 3u))
+        return MOE_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void *ws = workspace;
+    int32_t *ids = topk_ids_out ? topk_ids_out : ws_at<int32_t>(ws, f.off_ids);
+    float *weights = topk_weights_out ? topk_weights_out : ws_at<float>(ws, f.off_weights);
+    int32_t *sorted = ws_at<int32_t>(ws, f.off_sorted);
+    int32_t *offsets = ws_at<int32_t>(ws, f.off_offsets);
+    int32_t *inverse = ws_at<int32_t>(ws, f.off_inverse);
+    uint8_t *aq = ws_at<uint8_t>(ws, f.off_aq);
+    float *as = ws_at<float>(ws, f.off_as);
+    uint16_t *gu = ws_at<uint16_t>(ws, f.off_gu);
+    uint8_t *hq = ws_at<uint8_t>(ws, f.off_hq);
+    float *hs = ws_at<float>(ws, f.off_hs);
+    uint16_t *y = ws_at<uint16_t>(ws, f.off_y);
+    moe::launch_route(gating_output, correction_bias, f.T, f.E, f.k,
+                      p->scoring == MOE_SCORING_SIGMOID, p->renormalize, p->num_expert_group,
+                      p->topk_group, p->routed_scaling_factor, ids, weights, s);
+    // expert order, tight (block 1): rows [offsets[e], offsets[e+1]) are expert e's routes
+    moe::launch_align_sort(ids, f.P, f.E, 1, sorted, offsets,
+                           ws_at<int32_t>(ws, f.off_tile_expert), inverse,
+                           ws_at<int32_t>(ws, f.off_n_tiles),
+                           f.off_align ? ws_at<int32_t>(ws, f.off_align) : nullptr, s);
+    // x rows of the routes in expert order, quantised
+    moe::launch_quant_fp8_gather(hidden_states, sorted, f.k, f.P, f.H, aq, as, s);
+    moe::launch_fp8_gemm_contig(aq, as, w_gate_up, w_gate_up_scale, offsets, f.E, f.P, 2 * f.F,
+                                f.H, gu, s);
+    moe::launch_quant_fp8_swiglu(gu, f.P, f.F, hq, hs, s);
+    moe::launch_fp8_gemm_contig(hq, hs, w_down, w_down_scale, offsets, f.E, f.P, f.H, f.F, y, s);
+    moe::launch_combine(y, ids, weights, nullptr, out, f.T, f.H, f.k, f.E, MOE_DTYPE_BF16, s,
+                        inverse);
+    return launch_status();
 }
 
 }  // extern "C"

@@ -5,7 +5,8 @@
 // (TileOPs "MoE" page, MoEPostPermuteFwd: expert_output, topk_weights [T,K] f32; the shared
 // expert of FusedMoESharedExpertFwd is added with weight one).  Routes whose id is outside
 // [0, E) are skipped.  The expert GEMMs write y indexed by route, so a token's k rows are
-// contiguous and each 16-byte load covers eight columns.  Every output row is written, so the
+// contiguous and each 16-byte load covers eight columns (the FP8 pass, whose rows stay in expert
+// order, passes the row of each route instead).  Every output row is written, so the
 // output needs no clear beforehand (the aiter MI308 decoding PR drops its output clear for the
 // same reason).
 #include "moe_device.h"
@@ -19,7 +20,7 @@ template <int DT>
 __global__ __launch_bounds__(kThreads) void k_combine(
     const uint16_t *__restrict__ y, const int32_t *__restrict__ ids,
     const float *__restrict__ weights, const uint16_t *__restrict__ ys, uint16_t *__restrict__ out,
-    int H, int k, int E)
+    int H, int k, int E, const int32_t *__restrict__ row_of_route)
 {
     const int t = blockIdx.x;
     const int c = (blockIdx.y * kThreads + threadIdx.x) * 8;
@@ -32,7 +33,8 @@ __global__ __launch_bounds__(kThreads) void k_combine(
         if (e < 0 || e >= E)
             continue;
         const float w = weights[r];
-        const moe_u32x4 v = *reinterpret_cast<const moe_u32x4 *>(y + r * H + c);
+        const size_t yr = row_of_route ? (size_t)row_of_route[r] : r;
+        const moe_u32x4 v = *reinterpret_cast<const moe_u32x4 *>(y + yr * H + c);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             acc[2 * q] += w * moe_to_f32<DT>(v[q]);
@@ -60,15 +62,15 @@ namespace moe {
 
 void launch_combine(const uint16_t *y, const int32_t *ids, const float *weights,
                     const uint16_t *ys, uint16_t *out, int T, int H, int k, int E, int dtype,
-                    hipStream_t stream)
+                    hipStream_t stream, const int32_t *row_of_route)
 {
     const dim3 grid(T, (H / 8 + kThreads - 1) / kThreads);
     if (dtype == 1)
         hipLaunchKernelGGL(k_combine<1>, grid, dim3(kThreads), 0, stream, y, ids, weights, ys,
-                           out, H, k, E);
+                           out, H, k, E, row_of_route);
     else
         hipLaunchKernelGGL(k_combine<0>, grid, dim3(kThreads), 0, stream, y, ids, weights, ys,
-                           out, H, k, E);
+                           out, H, k, E, row_of_route);
 }
 
 }  // namespace moe

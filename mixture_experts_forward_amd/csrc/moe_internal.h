@@ -98,11 +98,17 @@ void launch_fp8_gemm_contig(const uint8_t *a, const float *a_scale, const uint8_
 // x [M, K] bf16 -> q [M, K] e4m3 codes, scale [M, ceil(K/128)] f32 (moe_quant.hip); K % 8 == 0.
 void launch_quant_fp8(const uint16_t *x, int M, int K, uint8_t *q, float *scale,
                       hipStream_t stream);
+// the same of rows row_src[r] / div of x (row_src[r] < 0: zero row)
+void launch_quant_fp8_gather(const uint16_t *x, const int32_t *row_src, int div, int M, int K,
+                             uint8_t *q, float *scale, hipStream_t stream);
+// the same of h = bf16(SiLU(gu[r, k]) * gu[r, K + k]) for gate-up rows gu [M, 2K]
+void launch_quant_fp8_swiglu(const uint16_t *gu, int M, int K, uint8_t *q, float *scale,
+                             hipStream_t stream);
 
 // ---------------------------------------------------------------- combine
 // out[t] = bf16( sum_j w[t,j] * y[t*k+j] (+ ys[t]) ), routes with ids outside [0,E) skipped.
 void launch_combine(const uint16_t *y, const int32_t *ids, const float *weights,
                     const uint16_t *ys, uint16_t *out, int T, int H, int k, int E, int dtype,
-                    hipStream_t stream);
+                    hipStream_t stream, const int32_t *row_of_route = nullptr);
 
 }  // namespace moe

@@ -298,3 +298,22 @@ def make_mxfp4_weights(cfg: MoEConfig, device="cpu", seed: int = 42) -> dict:
         "w_down_scale": scales((E, H, F // 32), F),
     }
 
+
+def make_fp8_weights(cfg: MoEConfig, device="cpu", seed: int = 42) -> dict:
+    """FP8 expert weights of cfg's shape: w_gate_up [E,2F,H] and w_down [E,H,F] e4m3 codes
+    (uint8; random_e4m3_codes) with f32 scales per 128 x 128 block [E,2F/128,H/128] and
+    [E,H/128,F/128], chosen so the dequantised weights have a standard deviation of about
+    1/sqrt(fan_in) (the codes' RMS magnitude is about 9): 1/(9 sqrt(fan_in)) x U[0.5, 1.5]."""
+    E, H, F = cfg.E, cfg.H, cfg.F
+    g = _gen("cpu", seed, STREAM_FP8 + 100)
+
+    def scales(shape, fan_in):
+        return ((torch.rand(shape, generator=g) + 0.5) / (9.0 * math.sqrt(fan_in))).to(device)
+
+    return {
+        "w_gate_up": random_e4m3_codes((E, 2 * F, H), g, device),
+        "w_gate_up_scale": scales((E, 2 * F // 128, H // 128), H),
+        "w_down": random_e4m3_codes((E, H, F), g, device),
+        "w_down_scale": scales((E, H // 128, F // 128), F),
+    }
+

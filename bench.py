@@ -47,9 +47,10 @@ def parse():
     ap.add_argument("--config", default=None)
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "f16"],
                     help="element type of the fused pass (activations, weights, output)")
-    ap.add_argument("--weights", default="16bit", choices=["16bit", "mxfp4"],
-                    help="expert weight format: the pass's element type, or MXFP4 (bf16 "
-                         "activations)")
+    ap.add_argument("--weights", default="16bit", choices=["16bit", "mxfp4", "fp8"],
+                    help="expert weight format: the pass's element type, MXFP4 (bf16 "
+                         "activations), or FP8 e4m3 with 128x128 block scales (activations "
+                         "quantised per 1x128 group)")
     ap.add_argument("--rotate", type=int, default=0, help="input sets (0 = automatic)")
     ap.add_argument("--path", default="auto", choices=["auto", "direct", "sorted"],
                     help="the library's path choice (auto: its own rule)")
@@ -88,7 +89,7 @@ def main():
     import mixture_experts_forward_amd as moe
     from moe_harness import perfmodel
     from moe_harness.workloads import (BENCH_CONFIG, CONFIGS, FP8_CONFIGS, MASKED_CONFIGS,
-                                       make_inputs, make_mxfp4_weights)
+                                       make_fp8_weights, make_inputs, make_mxfp4_weights)
 
     if args.config in MASKED_CONFIGS:
         bench_masked(args, MASKED_CONFIGS[args.config])
@@ -102,20 +103,21 @@ def main():
     moe.lib()
 
     mx = args.weights == "mxfp4"
-    if mx and (cfg.S > 0 or args.dtype != "bf16"):
-        sys.exit("--weights mxfp4 takes bf16 activations and no shared expert")
-    # bytes per routed expert's weights: 16-bit, or MXFP4 (half a byte per element plus one
-    # scale byte per 32)
-    wfac = 17.0 / 32.0 / 2.0 if mx else 1.0
+    f8 = args.weights == "fp8"
+    if (mx or f8) and (cfg.S > 0 or args.dtype != "bf16"):
+        sys.exit("--weights %s takes bf16 activations and no shared expert" % args.weights)
+    # bytes per routed expert's weights relative to 16-bit: MXFP4 half a byte per element plus
+    # one scale byte per 32; FP8 one byte plus 4 bytes per 128 x 128 block
+    wfac = 17.0 / 32.0 / 2.0 if mx else ((1.0 + 4.0 / 16384.0) / 2.0 if f8 else 1.0)
     wbytes = cfg.E * 6.0 * cfg.H * cfg.F * wfac + 6.0 * cfg.H * cfg.S
     R = args.rotate or max(1, min(8, math.ceil(16 * LLC_BYTES / wbytes)))
     log("workload %s, %d input sets of %.2f GB weights" % (cfg.name, R, wbytes / 1e9))
     tdt = torch.float16 if args.dtype == "f16" else torch.bfloat16
-    if mx:
+    if mx or f8:
         sets = []
         for i in range(R):
             d = make_inputs(cfg, dev, seed=42 + i, weights=False)
-            d.update(make_mxfp4_weights(cfg, dev, seed=42 + i))
+            d.update((make_mxfp4_weights if mx else make_fp8_weights)(cfg, dev, seed=42 + i))
             sets.append(d)
     else:
         sets = [make_inputs(cfg, dev, seed=42 + i, dtype=tdt) for i in range(R)]
@@ -132,7 +134,8 @@ def main():
     p = moe.make_params(cfg.T, cfg.H, cfg.E, cfg.F, cfg.k, cfg.scoring, cfg.renormalize,
                         cfg.num_expert_group, cfg.topk_group, cfg.rsf, path=args.path,
                         dtype=tdt)
-    ws_need = moe.mxfp4_workspace_bytes(p) if mx else moe.workspace_bytes(p, S)
+    ws_need = (moe.mxfp4_workspace_bytes(p) if mx else
+               moe.fp8_workspace_bytes(p) if f8 else moe.workspace_bytes(p, S))
     ws = torch.empty(max(256, ws_need), dtype=torch.uint8, device=dev)
     out = torch.empty((cfg.T, cfg.H), dtype=tdt, device=dev)
     ids = [torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev) for _ in range(R)]
@@ -140,7 +143,13 @@ def main():
 
     def fused_step(i):
         d = sets[i % R]
-        if mx:
+        if f8:
+            moe.fused_moe_fp8_fwd(d["hidden_states"], d["gating_output"], d["w_gate_up"],
+                                  d["w_gate_up_scale"], d["w_down"], d["w_down_scale"], cfg.k,
+                                  d["correction_bias"], cfg.scoring, cfg.renormalize,
+                                  cfg.num_expert_group, cfg.topk_group, cfg.rsf, out=out,
+                                  workspace=ws)
+        elif mx:
             moe.fused_moe_mxfp4_fwd(d["hidden_states"], d["gating_output"], d["w_gate_up_q"],
                                     d["w_gate_up_scale"], d["w_down_q"], d["w_down_scale"],
                                     cfg.k, d["correction_bias"], cfg.scoring, cfg.renormalize,
@@ -177,7 +186,9 @@ def main():
         if events is not None:
             events[1].record()
         for n, s in enumerate(stages):
-            if mx:
+            if f8:
+                moe.fused_moe_fp8_stage(s, p, d["hidden_states"], d, ids[j], wts[j], out, ws)
+            elif mx:
                 moe.fused_moe_mxfp4_stage(s, p, d["hidden_states"], d, ids[j], wts[j], out, ws)
             else:
                 moe.fused_moe_experts_stage(s, p, d["hidden_states"], d["w_gate_up"],
@@ -294,12 +305,16 @@ def main():
     gu_mfma_bound = gu_flops / perfmodel.BF16_MFMA_PEAK_FLOP_PER_S > \
         gu_bytes / perfmodel.HBM_PEAK_BYTES_PER_S
     # the committed counter summaries are of the bf16 kernels with bf16 weights
-    traffic = read_traffic(cfg.name) if args.dtype == "bf16" and not mx else None
+    traffic = read_traffic(cfg.name) if args.dtype == "bf16" and args.weights == "16bit" else None
 
     # ---- CPU baseline: the oracle on this host
-    cpu = None if args.no_cpu_baseline else cpu_baseline(cfg, sets[0], args.cpu_seconds,
-                                                         args.dtype)
-    base = None if mx else BASELINE_MS.get(
+    if args.no_cpu_baseline:
+        cpu = None
+    elif f8:
+        cpu = cpu_baseline_fp8(cfg, sets[0], args.cpu_seconds)
+    else:
+        cpu = cpu_baseline(cfg, sets[0], args.cpu_seconds, args.dtype)
+    base = None if args.weights != "16bit" else BASELINE_MS.get(
         cfg.name if args.dtype == "bf16" else cfg.name + ":" + args.dtype)
 
     ms = fused_ms
@@ -317,7 +332,7 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": round(ms / base["ms"], 4) if base else None,
-        "dtype": args.dtype,
+        "dtype": "fp8e4m3" if f8 else args.dtype,
         "data": "synthetic (seeded; %d rotating input sets)" % R,
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "F": cfg.F,
                    "top_k": cfg.k, "scoring": cfg.scoring, "renormalize": cfg.renormalize,
@@ -753,6 +768,69 @@ def summarize_pmc(args):
     print("\n".join(lines))
 
 
+def _cpu_baseline_mx(cfg, d, seconds, x, ids, w, route_s):
+    """MXFP4 weights: per sampled token, the oracle dequantises that token's experts
+    (oracle.mxfp4_to_bf16) and evaluates them; scaled to one whole forward."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    def one_token(t):
+        sel = torch.as_tensor(ids[t], device=d["w_gate_up_q"].device, dtype=torch.long)
+        host = {k: d[k].index_select(0, sel).cpu().numpy() for k in
+                ("w_gate_up_q", "w_gate_up_scale", "w_down_q", "w_down_scale")}
+        t0 = time.perf_counter()
+        wgu = oracle.mxfp4_to_bf16(host["w_gate_up_q"], host["w_gate_up_scale"])
+        wd = oracle.mxfp4_to_bf16(host["w_down_q"], host["w_down_scale"])
+        oracle.experts(x[t:t + 1], wgu, wd, np.arange(cfg.k, dtype=np.int32)[None, :],
+                       w[t:t + 1])
+        return time.perf_counter() - t0
+
+    one = max(one_token(0), 1e-6)
+    n = int(max(1, min(cfg.T, seconds / one)))
+    tokens = np.linspace(0, cfg.T - 1, n).round().astype(np.int64)
+    dt = sum(one_token(int(t)) for t in tokens)
+    per_forward_ms = (route_s + dt * cfg.T / n) * 1e3
+    log("cpu oracle (mxfp4 weights): %d of %d tokens in %.2f s -> %.1f ms per forward"
+        % (n, cfg.T, dt, per_forward_ms))
+    return {"value": round(per_forward_ms, 2), "unit": "ms", "cores": oracle.max_threads(),
+            "kind": "oracle", "sample": "routing of all %d tokens + per sampled token the "
+            "dequantisation and evaluation of its experts, %d of %d tokens, scaled to all"
+            % (cfg.T, n, cfg.T)}
+
+
+def cpu_baseline_fp8(cfg, d, seconds):
+    """The oracle's FP8 pass (oracle.fp8_forward) on this host for a sample of tokens, scaled
+    to one whole forward of T tokens (its routing runs on every token either way)."""
+    import numpy as np
+
+    import oracle
+    from moe_harness.workloads import to_u16
+
+    h = {k: d[k].cpu().numpy() for k in ("w_gate_up", "w_gate_up_scale", "w_down",
+                                         "w_down_scale", "gating_output")}
+    b = None if d["correction_bias"] is None else d["correction_bias"].cpu().numpy()
+    x = to_u16(d["hidden_states"])
+    args = (x, h["gating_output"], h["w_gate_up"], h["w_gate_up_scale"], h["w_down"],
+            h["w_down_scale"], b, cfg.k, cfg.scoring, cfg.renormalize, cfg.num_expert_group,
+            cfg.topk_group, float(np.float32(cfg.rsf)))
+    t0 = time.perf_counter()
+    oracle.fp8_forward(*args, tokens=[0])
+    one = max(time.perf_counter() - t0, 1e-6)
+    n = int(max(1, min(cfg.T, seconds / one)))
+    tokens = np.linspace(0, cfg.T - 1, n).round().astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.fp8_forward(*args, tokens=tokens)
+    dt = time.perf_counter() - t0
+    per_forward_ms = dt * cfg.T / n * 1e3
+    log("cpu oracle (fp8 pass): %d of %d tokens in %.2f s -> %.1f ms per forward"
+        % (n, cfg.T, dt, per_forward_ms))
+    return {"value": round(per_forward_ms, 2), "unit": "ms", "cores": oracle.max_threads(),
+            "kind": "oracle", "sample": "fp8 pass of %d of %d tokens (evenly spaced; routing of "
+            "all tokens each call), scaled to all" % (n, cfg.T)}
+
+
 def cpu_baseline(cfg, d, seconds, dtype="bf16"):
     """The oracle, as it stands, on this host: route every token, evaluate the experts of a
     sample of tokens; the time is scaled to one whole forward of T tokens."""
@@ -770,14 +848,8 @@ def cpu_baseline(cfg, d, seconds, dtype="bf16"):
     route_s = time.perf_counter() - t0
     import torch
     used = np.unique(ids)
-    if "w_gate_up_q" in d:  # MXFP4 weights: the oracle dequantises the used experts first
-        sel = torch.as_tensor(used, device=d["w_gate_up_q"].device)
-        host = {k: d[k].index_select(0, sel).cpu().numpy() for k in
-                ("w_gate_up_q", "w_gate_up_scale", "w_down_q", "w_down_scale")}
-        t0 = time.perf_counter()
-        wgu = oracle.mxfp4_to_bf16(host["w_gate_up_q"], host["w_gate_up_scale"])
-        wd = oracle.mxfp4_to_bf16(host["w_down_q"], host["w_down_scale"])
-        route_s += time.perf_counter() - t0
+    if "w_gate_up_q" in d:  # MXFP4 weights: the oracle dequantises a token's experts, then runs
+        return _cpu_baseline_mx(cfg, d, seconds, x, ids, w, route_s)
     else:
         sel = torch.as_tensor(used, device=d["w_gate_up"].device)
         wgu = to_u16(d["w_gate_up"].index_select(0, sel))

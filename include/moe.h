@@ -295,6 +295,17 @@ int fused_moe_fp8_fwd(const uint16_t *hidden_states, const float *gating_output,
                       int32_t *topk_ids_out, float *topk_weights_out, void *workspace,
                       size_t workspace_bytes, void *stream);
 
+/* fused_moe_fp8_stage -- one step of fused_moe_fp8_fwd's expert part with the routing given:
+ * MOE_STAGE_ALIGN (expert order and the quantised routed x rows), MOE_STAGE_GATE_UP,
+ * MOE_STAGE_DOWN (h quantised, then the down GEMM), MOE_STAGE_COMBINE, in that order, enqueue
+ * exactly the expert kernels of the fused call.  A stage checks only the pointers it reads.
+ * MOE_STAGE_SHARED: MOE_ERR_UNSUPPORTED. */
+int fused_moe_fp8_stage(int stage, const uint16_t *hidden_states, const uint8_t *w_gate_up,
+                        const float *w_gate_up_scale, const uint8_t *w_down,
+                        const float *w_down_scale, const int32_t *topk_ids,
+                        const float *topk_weights, const moe_params_t *p, uint16_t *out,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
 /* ---------------------------------------------------------------------------------------
  * Masked layout: the expert MLPs of one expert-parallel shard (TileOPs "MoE" page,
  * MoEGroupedGemmFwd with a: [E, layout.max_m, K] and layout_metadata [E] i32, workload

@@ -66,6 +66,8 @@ SIGNATURES = {
     "fused_moe_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "fused_moe_mxfp4_workspace_bytes": (_SZ, [_P]),
     "fused_moe_fp8_workspace_bytes": (_SZ, [_P]),
+    "fused_moe_fp8_stage": (ctypes.c_int, [_I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
+                                           _P]),
     "fused_moe_fp8_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
                                          _P]),
     "fused_moe_mxfp4_stage": (ctypes.c_int, [_I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
@@ -553,4 +555,23 @@ def fused_moe_fp8_fwd(hidden_states, gating_output, w_gate_up, w_gate_up_scale, 
     if return_routing:
         return out, ids, w
     return out
+
+
+def fused_moe_fp8_stage(stage, params, hidden_states, fw, topk_ids, topk_weights, out,
+                        workspace):
+    """One stage of the FP8 pass's expert part (see include/moe.h): ``fw`` holds w_gate_up,
+    w_gate_up_scale, w_down, w_down_scale (uint8 codes); ``params`` a MoEParams; the workspace
+    at least fp8_workspace_bytes(params) bytes.  Tensors are assumed checked by the caller."""
+    dev = hidden_states.device
+    with torch.cuda.device(dev):
+        st = lib().fused_moe_fp8_stage(
+            int(stage), _ptr(hidden_states), _ptr(fw["w_gate_up"]), _ptr(fw["w_gate_up_scale"]),
+            _ptr(fw["w_down"]), _ptr(fw["w_down_scale"]), _ptr(topk_ids), _ptr(topk_weights),
+            ctypes.byref(params), _ptr(out), _ptr(workspace), workspace.numel(), _stream(dev))
+    if st != MOE_OK:
+        raise MoEError(st, "fused_moe_fp8_stage(%s)" % STAGE_NAMES.get(stage, stage))
+
+
+def fp8_workspace_bytes(params):
+    return int(lib().fused_moe_fp8_workspace_bytes(ctypes.byref(params)))
 

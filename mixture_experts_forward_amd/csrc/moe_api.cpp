@@ -393,7 +393,8 @@ struct Fp8Pass {
         off_n_tiles, off_align, off_aq, off_as, off_gu, off_hq, off_hs, off_y, total;
 };
 
-int fp8_check(const moe_params_t *p)
+// One stage of the FP8 pass's expert part (the routing in ids / weights).
+static int fp8_check(const moe_params_t *p)
 {
     int st = moe::check_dims(p);
     if (st != MOE_OK)
@@ -403,7 +404,7 @@ int fp8_check(const moe_params_t *p)
     return MOE_OK;
 }
 
-void fp8_plan(const moe_params_t *p, Fp8Pass *f)
+static void fp8_plan(const moe_params_t *p, Fp8Pass *f)
 {
     f->T = p->num_tokens;
     f->H = p->hidden;
@@ -434,6 +435,45 @@ void fp8_plan(const moe_params_t *p, Fp8Pass *f)
     f->off_hs = take(P * (f->F / 128) * 4);
     f->off_y = take(P * f->H * 2);
     f->total = o;
+}
+
+static void fp8_stage(int stage, const Fp8Pass &f, const uint16_t *hidden, const uint8_t *w_gu,
+               const float *s_gu, const uint8_t *w_d, const float *s_d, const int32_t *ids,
+               const float *weights, uint16_t *out, void *ws, hipStream_t s)
+{
+    int32_t *sorted = ws_at<int32_t>(ws, f.off_sorted);
+    int32_t *offsets = ws_at<int32_t>(ws, f.off_offsets);
+    int32_t *inverse = ws_at<int32_t>(ws, f.off_inverse);
+    uint8_t *aq = ws_at<uint8_t>(ws, f.off_aq);
+    float *as = ws_at<float>(ws, f.off_as);
+    uint16_t *gu = ws_at<uint16_t>(ws, f.off_gu);
+    uint8_t *hq = ws_at<uint8_t>(ws, f.off_hq);
+    float *hs = ws_at<float>(ws, f.off_hs);
+    uint16_t *y = ws_at<uint16_t>(ws, f.off_y);
+    switch (stage) {
+    case MOE_STAGE_ALIGN:
+        // expert order, tight (block 1): rows [offsets[e], offsets[e+1]) are expert e's routes;
+        // then the routes' x rows in that order, quantised
+        moe::launch_align_sort(ids, f.P, f.E, 1, sorted, offsets,
+                               ws_at<int32_t>(ws, f.off_tile_expert), inverse,
+                               ws_at<int32_t>(ws, f.off_n_tiles),
+                               f.off_align ? ws_at<int32_t>(ws, f.off_align) : nullptr, s);
+        moe::launch_quant_fp8_gather(hidden, sorted, f.k, f.P, f.H, aq, as, s);
+        break;
+    case MOE_STAGE_GATE_UP:
+        moe::launch_fp8_gemm_contig(aq, as, w_gu, s_gu, offsets, f.E, f.P, 2 * f.F, f.H, gu, s);
+        break;
+    case MOE_STAGE_DOWN:
+        moe::launch_quant_fp8_swiglu(gu, f.P, f.F, hq, hs, s);
+        moe::launch_fp8_gemm_contig(hq, hs, w_d, s_d, offsets, f.E, f.P, f.H, f.F, y, s);
+        break;
+    case MOE_STAGE_COMBINE:
+        moe::launch_combine(y, ids, weights, nullptr, out, f.T, f.H, f.k, f.E, MOE_DTYPE_BF16, s,
+                            inverse);
+        break;
+    default:
+        break;
+    }
 }
 
 int fused_moe_experts_fwd(const uint16_t *hidden_states, const uint16_t *w_gate_up,
@@ -572,31 +612,44 @@ int fused_moe_fp8_fwd(const uint16_t *hidden_states, const float *gating_output,
     void *ws = workspace;
     int32_t *ids = topk_ids_out ? topk_ids_out : ws_at<int32_t>(ws, f.off_ids);
     float *weights = topk_weights_out ? topk_weights_out : ws_at<float>(ws, f.off_weights);
-    int32_t *sorted = ws_at<int32_t>(ws, f.off_sorted);
-    int32_t *offsets = ws_at<int32_t>(ws, f.off_offsets);
-    int32_t *inverse = ws_at<int32_t>(ws, f.off_inverse);
-    uint8_t *aq = ws_at<uint8_t>(ws, f.off_aq);
-    float *as = ws_at<float>(ws, f.off_as);
-    uint16_t *gu = ws_at<uint16_t>(ws, f.off_gu);
-    uint8_t *hq = ws_at<uint8_t>(ws, f.off_hq);
-    float *hs = ws_at<float>(ws, f.off_hs);
-    uint16_t *y = ws_at<uint16_t>(ws, f.off_y);
     moe::launch_route(gating_output, correction_bias, f.T, f.E, f.k,
                       p->scoring == MOE_SCORING_SIGMOID, p->renormalize, p->num_expert_group,
                       p->topk_group, p->routed_scaling_factor, ids, weights, s);
-    // expert order, tight (block 1): rows [offsets[e], offsets[e+1]) are expert e's routes
-    moe::launch_align_sort(ids, f.P, f.E, 1, sorted, offsets,
-                           ws_at<int32_t>(ws, f.off_tile_expert), inverse,
-                           ws_at<int32_t>(ws, f.off_n_tiles),
-                           f.off_align ? ws_at<int32_t>(ws, f.off_align) : nullptr, s);
-    // x rows of the routes in expert order, quantised
-    moe::launch_quant_fp8_gather(hidden_states, sorted, f.k, f.P, f.H, aq, as, s);
-    moe::launch_fp8_gemm_contig(aq, as, w_gate_up, w_gate_up_scale, offsets, f.E, f.P, 2 * f.F,
-                                f.H, gu, s);
-    moe::launch_quant_fp8_swiglu(gu, f.P, f.F, hq, hs, s);
-    moe::launch_fp8_gemm_contig(hq, hs, w_down, w_down_scale, offsets, f.E, f.P, f.H, f.F, y, s);
-    moe::launch_combine(y, ids, weights, nullptr, out, f.T, f.H, f.k, f.E, MOE_DTYPE_BF16, s,
-                        inverse);
+    for (int stage : {MOE_STAGE_ALIGN, MOE_STAGE_GATE_UP, MOE_STAGE_DOWN, MOE_STAGE_COMBINE})
+        fp8_stage(stage, f, hidden_states, w_gate_up, w_gate_up_scale, w_down, w_down_scale, ids,
+                  weights, out, ws, s);
+    return launch_status();
+}
+
+int fused_moe_fp8_stage(int stage, const uint16_t *hidden_states, const uint8_t *w_gate_up,
+                        const float *w_gate_up_scale, const uint8_t *w_down,
+                        const float *w_down_scale, const int32_t *topk_ids,
+                        const float *topk_weights, const moe_params_t *p, uint16_t *out,
+                        void *workspace, size_t workspace_bytes, void *stream)
+{
+    int st = fp8_check(p);
+    if (st != MOE_OK)
+        return st;
+    if (stage < MOE_STAGE_ALIGN || stage > MOE_STAGE_COMBINE || stage == MOE_STAGE_SHARED)
+        return MOE_ERR_UNSUPPORTED;
+    if (p->num_tokens == 0)
+        return MOE_OK;
+    if (!workspace || !topk_ids || (stage == MOE_STAGE_ALIGN && !hidden_states) ||
+        (stage == MOE_STAGE_GATE_UP && (!w_gate_up || !w_gate_up_scale)) ||
+        (stage == MOE_STAGE_DOWN && (!w_down || !w_down_scale)) ||
+        (stage == MOE_STAGE_COMBINE && (!topk_weights || !out)))
+        return MOE_ERR_NULL;
+    Fp8Pass f;
+    fp8_plan(p, &f);
+    if (workspace_bytes < f.total)
+        return MOE_ERR_WORKSPACE;
+    if (!aligned16(workspace) || (hidden_states && !aligned16(hidden_states)) ||
+        (w_gate_up && !aligned16(w_gate_up)) || (w_down && !aligned16(w_down)) ||
+        (out && !aligned16(out)) || ((uintptr_t)w_gate_up_scale & 3u) ||
+        ((uintptr_t)w_down_scale & 3u))
+        return MOE_ERR_UNSUPPORTED;
+    fp8_stage(stage, f, hidden_states, w_gate_up, w_gate_up_scale, w_down, w_down_scale,
+              topk_ids, topk_weights, out, workspace, static_cast<hipStream_t>(stream));
     return launch_status();
 }
 

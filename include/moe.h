@@ -352,9 +352,10 @@ int fused_moe_masked_stage(int stage, const uint16_t *a, const int32_t *masked_m
  * A block's products are summed by the MFMA (whose internal sum carries about 15 fraction bits
  * relative to the sum of the products' magnitudes, not a full f32 sum), scaled in f32 and
  * accumulated in f32; NaN codes (S.1111.111) propagate.  Needs E >= 1, max_m >= 0 (0: nothing is enqueued),
- * N % 64 == 0, K % 128 == 0, 16-byte aligned a, b, out and 4-byte aligned scales.
+ * N % 64 == 0, K % 128 == 0, E * ceil(max_m/64) * ceil(N/256) < 2^30, 16-byte aligned a, b,
+ * out and 4-byte aligned scales.
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (E < 1, max_m < 0, N < 1, K < 1), MOE_ERR_UNSUPPORTED
- * (N % 64, K % 128, E * max_m >= 2^30, alignment), MOE_ERR_LAUNCH. */
+ * (N % 64, K % 128, E * max_m >= 2^30, the tile count, alignment), MOE_ERR_LAUNCH. */
 int moe_grouped_gemm_fp8(const uint8_t *a, const float *a_scale, const uint8_t *b,
                          const float *b_scale, const int32_t *masked_m, int32_t E, int32_t max_m,
                          int32_t N, int32_t K, uint16_t *out, void *stream);
@@ -371,8 +372,8 @@ int moe_grouped_gemm_fp8(const uint8_t *a, const float *a_scale, const uint8_t *
  *                   (each clamped to [0, P] on the device; a decreasing pair gives no rows).
  *   out             [P, N] bf16: rows of some expert written, the others untouched.
  * Same arithmetic as moe_grouped_gemm_fp8.  Needs E in 1..1024, 0 <= P < 2^30 (0: nothing is
- * enqueued), N % 64 == 0, K % 128 == 0, 16-byte aligned a, b, out and 4-byte aligned scales
- * and offsets.
+ * enqueued), (ceil(P/64) + E) * ceil(N/256) < 2^30, N % 64 == 0, K % 128 == 0, 16-byte aligned
+ * a, b, out and 4-byte aligned scales and offsets.
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (E < 1, P < 0, N < 1, K < 1), MOE_ERR_UNSUPPORTED,
  * MOE_ERR_LAUNCH. */
 int moe_grouped_gemm_fp8_contiguous(const uint8_t *a, const float *a_scale, const uint8_t *b,

@@ -767,8 +767,10 @@ int moe_grouped_gemm_fp8(const uint8_t *a, const float *a_scale, const uint8_t *
 {
     if (E < 1 || max_m < 0 || N < 1 || K < 1)
         return MOE_ERR_SHAPE;
+    // the launch covers E * ceil(max_m / 64) row tiles per 256-column block
     if (N % 64 != 0 || K % 128 != 0 || (int64_t)E * max_m >= (1ll << 30) ||
-        (int64_t)E * N >= (1ll << 30))
+        (int64_t)E * N >= (1ll << 30) ||
+        (int64_t)E * ((max_m + 63) / 64) * ((N + 255) / 256) >= (1ll << 30))
         return MOE_ERR_UNSUPPORTED;
     if (max_m == 0)
         return MOE_OK;
@@ -789,8 +791,10 @@ int moe_grouped_gemm_fp8_contiguous(const uint8_t *a, const float *a_scale, cons
 {
     if (E < 1 || P < 0 || N < 1 || K < 1)
         return MOE_ERR_SHAPE;
+    // the launch covers at most (ceil(P / 64) + E) row tiles per 256-column block
     if (N % 64 != 0 || K % 128 != 0 || E > 1024 || P >= (1 << 30) ||
-        (int64_t)E * N >= (1ll << 30))
+        (int64_t)E * N >= (1ll << 30) ||
+        ((int64_t)(P + 63) / 64 + E) * ((N + 255) / 256) >= (1ll << 30))
         return MOE_ERR_UNSUPPORTED;
     if (P == 0)
         return MOE_OK;

@@ -179,6 +179,7 @@ def test_fp8_contiguous_and_quant_reject_before_launch():
     assert g(4, 16, 128, 128, a=odd) == -3         # a not 16-byte aligned
     assert g(4, 16, 128, 128, off=None) == -1
     assert g(4, 0, 128, 128, a=None, off=None) == 0   # P = 0: nothing to do
+    assert g(4, (1 << 30) - 64, 1 << 16, 128) == -3    # tile count past the launch bound
     q = lambda M, K, x=fake, qq=fake: L.moe_quant_fp8(x, M, K, qq, fake, None)
     assert q(-1, 128) == -2
     assert q(4, 0) == -2

@@ -277,8 +277,9 @@ def main():
     log("graph replay: %.4f ms/step; median single call %.4f ms; warm (one input set): "
         "%.4f ms/step" % (graph_ms, median_ms, warm_ms))
     ctx = context_numbers(torch, dev)
-    log("context: device copy %.0f GB/s, torch bf16 matmul %.0f TFLOP/s" % (
-        ctx["device_copy_gbps"], ctx["torch_matmul_bf16_tflops"]))
+    log("context: streaming read %.0f GB/s, device copy %.0f GB/s, torch bf16 matmul %.0f "
+        "TFLOP/s" % (ctx["stream_read_gbps"], ctx["device_copy_gbps"],
+                     ctx["torch_matmul_bf16_tflops"]))
 
     # ---- roofline of the pass and of the dominant kernel, from the realized routing
     touched = []
@@ -365,7 +366,10 @@ def main():
                      {"kernel": "gate-up GEMM of the routed experts", "bound": "hbm",
                       "achieved": round(gu_gbs, 1), "peak": peak_gbs, "unit": "GB/s",
                       "frac": round(gu_gbs / peak_gbs, 4), "traffic": traffic,
-                      "algorithmic_bytes_per_launch": gu_bytes}),
+                      "algorithmic_bytes_per_launch": gu_bytes,
+                      # the same rate against what a plain streaming read reaches here
+                      "stream_read_gbps": ctx["stream_read_gbps"],
+                      "frac_of_stream_read": round(gu_gbs / ctx["stream_read_gbps"], 4)}),
         "cpu_baseline": cpu,
         "baseline_context": base,
         "context": ctx,
@@ -571,9 +575,29 @@ def cpu_baseline_masked(cfg, d, seconds):
             "kind": "oracle", "sample": "%d of %d experts, scaled to all" % (n, cfg.E)}
 
 
+def stream_read_gbps(torch, dev, nbytes=4 << 30, reps=5):
+    """The library's streaming-read kernel (moe_stream_read) over a buffer 16x the last-level
+    cache: the HBM read rate this GPU's CUs reach on a plain sequential stream."""
+    import mixture_experts_forward_amd as moe
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device=dev).fill_(1)
+    sink = moe.moe_stream_read(buf)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        moe.moe_stream_read(buf, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf, sink
+    return gbps
+
+
 def context_numbers(torch, dev):
-    """What this GPU reaches outside the library, for context: a 1 GiB device-to-device copy
-    (read + write bytes per second) and a torch bf16 8192^3 matmul."""
+    """What this GPU reaches, for context: the library's streaming-read kernel over 4 GiB (the
+    practical HBM read ceiling), a 1 GiB device-to-device copy (read + write bytes per second)
+    and a torch bf16 8192^3 matmul."""
+    read_gbps = stream_read_gbps(torch, dev)
     n = 1 << 30
     a = torch.ones(n, dtype=torch.uint8, device=dev)
     b = torch.empty_like(a)
@@ -599,7 +623,8 @@ def context_numbers(torch, dev):
     torch.cuda.synchronize()
     tflops = 2.0 * m ** 3 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12
     del x, y, z
-    return {"device_copy_gbps": round(copy_gbps, 1), "torch_matmul_bf16_tflops": round(tflops, 1)}
+    return {"stream_read_gbps": round(read_gbps, 1), "device_copy_gbps": round(copy_gbps, 1),
+            "torch_matmul_bf16_tflops": round(tflops, 1)}
 
 
 # The pages' own figure for this exact workload (another, unnamed GPU): context only.

@@ -395,6 +395,23 @@ int moe_grouped_gemm_fp8_contiguous(const uint8_t *a, const float *a_scale, cons
 int moe_quant_fp8(const uint16_t *x, int32_t M, int32_t K, uint8_t *q, float *scale,
                   void *stream);
 
+/* ---- measurement: the HBM streaming-read ceiling
+ *
+ * Not a step of the pass: the plain sequential read that the expert GEMMs' weight streams are
+ * measured against (a roofline is reported against the published HBM peak; this is the rate
+ * the same CUs reach on a pure read, so it gives the achievable share of that peak).
+ *
+ * moe_stream_read_sink_words() is the number of uint32 words moe_stream_read writes to sink
+ * (G = one per CU of the current device).  moe_stream_read enqueues one read of bytes bytes of
+ * buf (device memory, 16-byte aligned, bytes a multiple of 16) with 16-byte non-temporal loads
+ * by G 512-thread workgroups sweeping the buffer in 8 KB blocks (block q read by workgroup
+ * q % G); sink[b] receives the xor of the 32-bit words workgroup b read (so the loads cannot be
+ * elided).  bytes = 0: nothing is enqueued.
+ * Errors: MOE_ERR_NULL (buf or sink NULL with bytes > 0), MOE_ERR_UNSUPPORTED (alignment, bytes
+ * % 16), MOE_ERR_LAUNCH. */
+int moe_stream_read_sink_words(void);
+int moe_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

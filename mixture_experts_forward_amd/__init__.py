@@ -20,6 +20,8 @@ Entry points (same names as the C ABI):
                       top_k, ...)                             -> out [T, H] bf16 (MXFP4 weights)
   fused_moe_fp8_fwd(hidden, gating, w_gate_up, w_gate_up_scale, w_down, w_down_scale, top_k, ...)
                                                               -> out [T, H] bf16 (FP8 weights)
+  moe_stream_read(buf)                                        -> sink (measurement: one HBM
+                                                                 streaming read of buf)
 """
 import ctypes
 import os
@@ -89,6 +91,8 @@ SIGNATURES = {
     "moe_grouped_gemm_fp8_contiguous": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32,
                                                        _I32, _P, _P]),
     "moe_quant_fp8": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _P]),
+    "moe_stream_read_sink_words": (ctypes.c_int, []),
+    "moe_stream_read": (ctypes.c_int, [_P, ctypes.c_size_t, _P, _P]),
 }
 
 # stages of fused_moe_experts_stage, in the order fused_moe_experts_fwd runs them
@@ -575,3 +579,18 @@ def fused_moe_fp8_stage(stage, params, hidden_states, fw, topk_ids, topk_weights
 def fp8_workspace_bytes(params):
     return int(lib().fused_moe_fp8_workspace_bytes(ctypes.byref(params)))
 
+
+def moe_stream_read(buf, sink=None):
+    """One streaming read of the bytes of the device tensor buf (the HBM read ceiling the
+    expert GEMMs' weight streams are compared with).  Returns the int32 sink tensor (one word
+    per CU) that the kernel writes."""
+    dev = buf.device
+    if sink is None:
+        sink = torch.empty(int(lib().moe_stream_read_sink_words()), dtype=torch.int32,
+                           device=dev)
+    nbytes = buf.numel() * buf.element_size()
+    with torch.cuda.device(dev):
+        st = lib().moe_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(dev))
+    if st != MOE_OK:
+        raise MoEError(st, "moe_stream_read")
+    return sink

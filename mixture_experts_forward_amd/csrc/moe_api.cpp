@@ -825,4 +825,19 @@ int moe_quant_fp8(const uint16_t *x, int32_t M, int32_t K, uint8_t *q, float *sc
     return launch_status();
 }
 
+int moe_stream_read_sink_words(void) { return moe::stream_read_grid(); }
+
+int moe_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream)
+{
+    if (bytes == 0)
+        return MOE_OK;
+    if (!buf || !sink)
+        return MOE_ERR_NULL;
+    if (!aligned16(buf) || bytes % 16 != 0)
+        return MOE_ERR_UNSUPPORTED;
+    moe::launch_stream_read(buf, bytes, sink, moe::stream_read_grid(),
+                            static_cast<hipStream_t>(stream));
+    return launch_status();
+}
+
 }  // extern "C"

@@ -111,4 +111,11 @@ void launch_combine(const uint16_t *y, const int32_t *ids, const float *weights,
                     const uint16_t *ys, uint16_t *out, int T, int H, int k, int E, int dtype,
                     hipStream_t stream, const int32_t *row_of_route = nullptr);
 
+// ---------------------------------------------------------------- measurement
+// Workgroups of the streaming-read kernel (one per CU of the current device).
+int stream_read_grid();
+// Reads bytes (a multiple of 16) of buf once; writes one word per workgroup to sink[grid].
+void launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, int grid,
+                        hipStream_t stream);
+
 }  // namespace moe

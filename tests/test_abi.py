@@ -206,3 +206,15 @@ def test_mxfp4_entry_points_reject_before_launch():
     assert call(f16, fake, 1 << 30) == -3                                        # bf16 only
     assert L.fused_moe_mxfp4_workspace_bytes(ctypes.byref(f16)) == 0
     assert call(moe.make_params(0, 2048, 128, 768, 8), None, 0) == 0             # T = 0
+
+
+def test_stream_read_rejects_before_launch():
+    """The streaming-read measurement validates its arguments before any HIP call."""
+    L = moe.lib()
+    fake = ctypes.c_void_p(4096)
+    assert L.moe_stream_read(None, 0, None, None) == 0                   # nothing to read
+    assert L.moe_stream_read(None, 1024, fake, None) == -1
+    assert L.moe_stream_read(fake, 1024, None, None) == -1
+    assert L.moe_stream_read(ctypes.c_void_p(4096 + 8), 1024, fake, None) == -3  # alignment
+    assert L.moe_stream_read(fake, 1000, fake, None) == -3                # bytes % 16
+

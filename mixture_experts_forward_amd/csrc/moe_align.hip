@@ -35,6 +35,7 @@ struct AlignSmem {
     uint32_t hist[kWaves][kMaxExperts / 2];  // two 16-bit counters per word
     alignas(16) int round_ids[kThreads];
     int wave_total[kWaves];
+    int wave_cost[kWaves];
     int total;
 };
 
@@ -52,11 +53,65 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane)
 // Padded exclusive scan of sm.count[0..E) (thread e owns expert e): writes expert_offsets,
 // tile_expert, n_tiles and the -1 padding of sorted_ids; leaves each expert's first row in
 // sm.base (sm.count unchanged).
+__device__ __forceinline__ void write_schedule(int E, int bm, int c, int excl_rows,
+                                               moe::TileSchedule *__restrict__ sched,
+                                               AlignSmem &sm);
+
+// The per-XCD tile ranges of the layout (moe::TileSchedule): thread e < E holds expert e's
+// routed rows c and its first padded row excl_rows; sm.total is the padded row count.  Each
+// expert's cost (its row tiles' 5*bm/4 + their rows) is scanned; range boundary p (1..7) falls
+// in the expert whose cost interval holds p/8 of the total, at the matching fraction of its row
+// tiles.  Also zeroes the counters.
+__device__ __forceinline__ void write_schedule(int E, int bm, int c, int excl_rows,
+                                               moe::TileSchedule *__restrict__ sched,
+                                               AlignSmem &sm)
+{
+    constexpr int P = moe::kSchedParts;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = tid >> 6;
+    const int te = (c + bm - 1) / bm;  // row tiles of expert tid (0 past E)
+    const int cost = te * (5 * bm / 4) + c;
+    int incl = wave_inclusive_scan(cost, lane);
+    if (lane == 63)
+        sm.wave_cost[wv] = incl;
+    __syncthreads();
+    int before = 0, total = 0;
+    for (int w = 0; w < kWaves; ++w) {
+        before += w < wv ? sm.wave_cost[w] : 0;
+        total += sm.wave_cost[w];
+    }
+    incl += before;
+    const int excl = incl - cost;
+    const float row_tiles = (float)(sm.total / bm);
+    if (tid <= P)
+        sched->queue[tid] = 0;
+    if (total == 0) {
+        if (tid <= P)
+            sched->bounds[tid] = 0.0f;
+        return;
+    }
+    if (tid == 0) {
+        sched->bounds[0] = 0.0f;
+        sched->bounds[P] = row_tiles;
+    }
+    if (tid < E && cost > 0) {
+        for (int p = 1; p < P; ++p) {
+            const double target = (double)total * p / P;
+            if ((double)excl < target && target <= (double)incl) {
+                const double f = (target - excl) / cost;
+                sched->bounds[p] = (float)(excl_rows / bm + f * te);
+            }
+        }
+    }
+}
+
 __device__ __forceinline__ void scan_layout(int E, int bm, int slots, int tiles_cap,
                                             int32_t *__restrict__ sorted_ids,
                                             int32_t *__restrict__ offsets,
                                             int32_t *__restrict__ tile_expert,
-                                            int32_t *__restrict__ n_tiles, AlignSmem &sm)
+                                            int32_t *__restrict__ n_tiles,
+                                            moe::TileSchedule *__restrict__ sched, AlignSmem &sm)
 {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -82,6 +137,8 @@ __device__ __forceinline__ void scan_layout(int E, int bm, int slots, int tiles_
         sm.total = incl;
     }
     __syncthreads();
+    if (sched)
+        write_schedule(E, bm, c, excl, sched, sm);
     // padding rows and tile table of expert e, by wave e % 16 (lanes share the slots)
     for (int e = wv; e < E; e += kWaves) {
         const int b = sm.base[e], ce = sm.count[e];
@@ -161,7 +218,8 @@ __device__ __forceinline__ void align_block(const int32_t *__restrict__ ids, int
                                             int32_t *__restrict__ offsets,
                                             int32_t *__restrict__ tile_expert,
                                             int32_t *__restrict__ inverse,
-                                            int32_t *__restrict__ n_tiles, AlignSmem &sm)
+                                            int32_t *__restrict__ n_tiles,
+                                            moe::TileSchedule *__restrict__ sched, AlignSmem &sm)
 {
     const int tid = threadIdx.x;
     const int half_words = (E + 1) / 2;
@@ -176,7 +234,7 @@ __device__ __forceinline__ void align_block(const int32_t *__restrict__ ids, int
             atomicAdd(&sm.count[e], 1);
     }
     __syncthreads();
-    scan_layout(E, bm, slots, tiles_cap, sorted_ids, offsets, tile_expert, n_tiles, sm);
+    scan_layout(E, bm, slots, tiles_cap, sorted_ids, offsets, tile_expert, n_tiles, sched, sm);
     for (int r0 = 0; r0 < P; r0 += kThreads)
         scatter_round(ids, P, E, r0, true, sorted_ids, inverse, sm);
 }
@@ -211,7 +269,8 @@ __global__ __launch_bounds__(kThreads) void k_align_scan(int32_t *__restrict__ c
                                                          int32_t *__restrict__ sorted_ids,
                                                          int32_t *__restrict__ offsets,
                                                          int32_t *__restrict__ tile_expert,
-                                                         int32_t *__restrict__ n_tiles)
+                                                         int32_t *__restrict__ n_tiles,
+                                                         moe::TileSchedule *__restrict__ sched)
 {
     constexpr int kBatch = 16;
     __shared__ AlignSmem sm;
@@ -233,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void k_align_scan(int32_t *__restrict__ c
         sm.count[tid] = run;
     }
     __syncthreads();
-    scan_layout(E, bm, slots, tiles_cap, sorted_ids, offsets, tile_expert, n_tiles, sm);
+    scan_layout(E, bm, slots, tiles_cap, sorted_ids, offsets, tile_expert, n_tiles, sched, sm);
 }
 
 // Chunked driver, launch 3: the round of chunk b, its routes of expert e starting at row
@@ -260,11 +319,11 @@ __global__ __launch_bounds__(kThreads) void k_align_sort(
     const int32_t *__restrict__ ids, int P, int E, int bm, int slots, int tiles_cap,
     int32_t *__restrict__ sorted_ids, int32_t *__restrict__ offsets,
     int32_t *__restrict__ tile_expert, int32_t *__restrict__ inverse,
-    int32_t *__restrict__ n_tiles)
+    int32_t *__restrict__ n_tiles, moe::TileSchedule *__restrict__ sched)
 {
     __shared__ AlignSmem sm;
     align_block(ids, P, E, bm, slots, tiles_cap, sorted_ids, offsets, tile_expert, inverse,
-                n_tiles, sm);
+                n_tiles, sched, sm);
 }
 
 }  // namespace
@@ -273,20 +332,22 @@ namespace moe {
 
 void launch_align_sort(const int32_t *ids, int P, int E, int block_m, int32_t *sorted_ids,
                        int32_t *offsets, int32_t *tile_expert, int32_t *inverse, int32_t *n_tiles,
-                       int32_t *scratch, hipStream_t stream)
+                       int32_t *scratch, hipStream_t stream, TileSchedule *sched)
 {
     const int slots = P + E * (block_m - 1);
     const int tiles_cap = P / block_m + E;
     if (scratch == nullptr || P <= kThreads) {
         hipLaunchKernelGGL(k_align_sort, dim3(1), dim3(kThreads), 0, stream, ids, P, E, block_m,
-                           slots, tiles_cap, sorted_ids, offsets, tile_expert, inverse, n_tiles);
+                           slots, tiles_cap, sorted_ids, offsets, tile_expert, inverse, n_tiles,
+                           sched);
         return;
     }
     const int chunks = (P + kThreads - 1) / kThreads;
     hipLaunchKernelGGL(k_align_hist, dim3(chunks), dim3(kThreads), 0, stream, ids, P, E,
                        scratch);
     hipLaunchKernelGGL(k_align_scan, dim3(1), dim3(kThreads), 0, stream, scratch, chunks, E,
-                       block_m, slots, tiles_cap, sorted_ids, offsets, tile_expert, n_tiles);
+                       block_m, slots, tiles_cap, sorted_ids, offsets, tile_expert, n_tiles,
+                       sched);
     hipLaunchKernelGGL(k_align_scatter, dim3(chunks), dim3(kThreads), 0, stream, ids, P, E,
                        scratch, offsets, sorted_ids, inverse);
 }

@@ -13,6 +13,9 @@ namespace {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// the plan reserves 2 * 4 * 9 bytes for the sorted path's tile schedule
+static_assert(sizeof(moe::TileSchedule) <= 2 * 4 * 9, "tile schedule fits its workspace slot");
+
 int launch_status()
 {
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
@@ -56,6 +59,7 @@ moe::GemmProblem gate_up_problem(const moe::Plan &pl, const Ctx &c)
         g.sorted_ids = ws_at<int32_t>(c.ws, pl.off_sorted);
         g.offsets = ws_at<int32_t>(c.ws, pl.off_offsets);
         g.tile_expert = ws_at<int32_t>(c.ws, pl.off_tile_expert);
+        g.sched = pl.off_sched ? ws_at<moe::TileSchedule>(c.ws, pl.off_sched) : nullptr;
         const bool per_expert =
             pl.gate_up.kind == moe::KERNEL_WS || pl.gate_up.kind == moe::KERNEL_MX;
         g.num_groups = per_expert ? pl.E : pl.tiles_cap;
@@ -127,7 +131,9 @@ int run_stage(int stage, const moe::Plan &pl, const Ctx &c)
                                    ws_at<int32_t>(c.ws, pl.off_inverse),
                                    ws_at<int32_t>(c.ws, pl.off_n_tiles),
                                    pl.off_align ? ws_at<int32_t>(c.ws, pl.off_align) : nullptr,
-                                   c.stream);
+                                   c.stream,
+                                   pl.off_sched ? ws_at<moe::TileSchedule>(c.ws, pl.off_sched)
+                                                : nullptr);
         break;
     case MOE_STAGE_GATE_UP:
         if (!launch_gemm(true, gate_up_problem(pl, c), src, pl.gate_up, c.stream))

@@ -36,8 +36,10 @@ void launch_typed(const GemmProblem &g, hipStream_t stream)
     const int cols = GATE_UP ? moe_wide::kBW / 2 : moe_wide::kBW;  // output columns per tile
     const int n_blocks = (g.n_out + cols - 1) / cols;
     const int m_tiles = g.num_groups;
-    // sorted rows: one tile per workgroup; dense rows: one workgroup per resident slot
-    const int slots = SRC == moe::ROWS_DENSE ? per_cu(kernel) * device_cus() : (1 << 30);
+    // dense rows, and sorted rows with a schedule: one workgroup per resident slot; sorted rows
+    // without one: one tile per workgroup
+    const bool persistent = SRC == moe::ROWS_DENSE || g.sched != nullptr;
+    const int slots = persistent ? per_cu(kernel) * device_cus() : (1 << 30);
     const int grid = moe_wide::wide_grid(n_blocks * m_tiles, slots);
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(moe_wide::kThreads), 0, stream, g, n_blocks,
                        m_tiles);

@@ -13,11 +13,27 @@ void launch_route(const float *gating, const float *bias, int T, int E, int k, i
                   float *weights, hipStream_t stream);
 
 // ---------------------------------------------------------------- align / sort
+// Work schedule of a grouped GEMM over the sorted layout, written by the align step.  The
+// layout's tiles (expert by expert, each expert's block_m-row tiles x the GEMM's column blocks)
+// are split into kSchedParts contiguous ranges of about equal estimated cost (a row tile of r
+// routed rows costs 5*block_m/4 + r: a fixed weight stream plus MFMA work per row), one range
+// per XCD.  bounds[p] is the start of range p in row-tile units (a GEMM with n column blocks
+// starts range p at tile round(bounds[p] * n)); bounds[0] = 0, bounds[kSchedParts] = the row
+// tile count.  queue[p] counts the tiles handed out of range p and queue[kSchedParts] the
+// workgroups that have finished; all of queue is zero between launches (the align step zeroes
+// it, and the last workgroup of a launch that uses it zeroes it again).
+constexpr int kSchedParts = 8;
+struct TileSchedule {
+    float bounds[kSchedParts + 1];
+    int32_t queue[kSchedParts + 1];
+};
+
 // scratch: NULL (one workgroup does everything) or align_scratch_ints(P, E) ints of device
-// memory (moe_plan.h) for the chunked three-launch form (used when P > 1024).
+// memory (moe_plan.h) for the chunked three-launch form (used when P > 1024).  sched: NULL or
+// the TileSchedule to write.
 void launch_align_sort(const int32_t *ids, int P, int E, int block_m, int32_t *sorted_ids,
                        int32_t *offsets, int32_t *tile_expert, int32_t *inverse, int32_t *n_tiles,
-                       int32_t *scratch, hipStream_t stream);
+                       int32_t *scratch, hipStream_t stream, TileSchedule *sched = nullptr);
 
 // ---------------------------------------------------------------- expert GEMMs
 // Where a GEMM takes its rows from.
@@ -48,6 +64,8 @@ struct GemmProblem {
     int dtype;                  // element type of act, weight, out: 0 bf16, 1 f16
     const uint8_t *wq;          // MXFP4 weights: [experts][n_weight_rows][K/2] e2m1 pairs
     const uint8_t *wscale;      // MXFP4 weights: [experts][n_weight_rows][K/32] E8M0
+    TileSchedule *sched;        // 256 x 256 tile kernel, ROWS_SORTED: per-XCD tile ranges and
+                                // their counters (NULL: tiles dealt statically)
 };
 
 // Tile shape of one launch.

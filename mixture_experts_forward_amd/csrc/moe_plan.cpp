@@ -125,11 +125,14 @@ void make_plan(const moe_params_t *p, int32_t S, Plan *pl, int wfmt)
         pl->off_tile_expert = take((size_t)pl->tiles_cap * 4);
         pl->off_inverse = take((size_t)P * 4);
         pl->off_n_tiles = take(4);
+        // per-XCD tile ranges of the 256 x 256 tile kernel (moe_internal.h's TileSchedule)
+        pl->off_sched = pl->gate_up.kind == KERNEL_WIDE ? take(2 * 4 * 9) : 0;
         const size_t scratch = align_scratch_ints(P, pl->E);
         pl->off_align = scratch ? take(scratch * 4) : 0;
         pl->off_h = take((size_t)pl->slots * pl->F * 2);
     } else {
         pl->off_sorted = pl->off_offsets = pl->off_tile_expert = pl->off_inverse = 0;
+        pl->off_sched = 0;
         pl->off_n_tiles = pl->off_align = 0;
         pl->off_h = take((size_t)P * pl->F * 2);
     }

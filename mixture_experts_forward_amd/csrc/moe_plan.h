@@ -43,7 +43,7 @@ struct Plan {
     TileChoice gate_up, down, shared_gate_up, shared_down;
     // byte offsets into the workspace
     size_t off_ids, off_weights, off_sorted, off_offsets, off_tile_expert, off_inverse,
-        off_n_tiles, off_align, off_h, off_y, off_hs, off_ys;
+        off_n_tiles, off_sched, off_align, off_h, off_y, off_hs, off_ys;
     size_t total;
 };
 

@@ -419,6 +419,73 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
     }
 }
 
+// Tile t of the schedule's range p (p = 0..8: the range starts, in tiles of a GEMM with
+// n_blocks column blocks; range 8's start is the tile count).
+__device__ __forceinline__ int sched_bound(const moe::TileSchedule *sched, int p, int n_blocks,
+                                           int total)
+{
+    if (p <= 0)
+        return 0;
+    if (p >= moe::kSchedParts)
+        return total;
+    const int b = __float2int_rn(sched->bounds[p] * (float)n_blocks);
+    return min(max(b, 0), total);
+}
+
+// Sorted rows with a schedule: a persistent workgroup on XCD x (= blockIdx % 8) takes the next
+// tile of range x from its counter (one atomic per tile; tiles of one expert stay on one XCD
+// and share its L2), and once range x is used up, the next tiles of ranges x+1, x+2, ...  The
+// workgroup leaves when every range is used up; the last one to leave zeroes the counters for
+// the next launch.  No workgroup ever waits for another.
+template <bool GATE_UP, int SRC, int WS, int DT>
+__device__ __forceinline__ void wide_queue_loop(const GemmProblem &g, int n_blocks, int total,
+                                                moe_u32x4 *smem)
+{
+    constexpr int P = moe::kSchedParts;
+    // thread 0 passes the tile number through the first word of the (idle) stage memory
+    volatile int *s_next = reinterpret_cast<volatile int *>(smem);
+    moe::TileSchedule *sched = g.sched;
+    const int home = blockIdx.x % kXcds;
+    int tried = 0;  // ranges found used up (thread 0's state)
+    while (true) {
+        if (threadIdx.x == 0) {
+            int t = -1;
+            while (tried < P) {
+                const int p = (home + tried) % P;
+                const int lo = sched_bound(sched, p, n_blocks, total);
+                const int hi = sched_bound(sched, p + 1, n_blocks, total);
+                if (lo < hi) {
+                    const int n = atomicAdd(&sched->queue[p], 1);
+                    if (n < hi - lo) {
+                        t = lo + n;
+                        break;
+                    }
+                }
+                ++tried;
+            }
+            *s_next = t;
+        }
+        __syncthreads();
+        const int t = *s_next;
+        __syncthreads();  // every wave has read it before the tile's loads overwrite the stage
+        if (t < 0)
+            break;
+        int nblk, mtile, expert;
+        wide_decode<SRC>(g, t, n_blocks, 0, nblk, mtile, expert);
+        wide_tile<GATE_UP, SRC, WS, DT>(g, nblk, mtile, expert, smem);
+        __syncthreads();  // the next tile's first loads follow every wave's last reads
+    }
+    if (threadIdx.x == 0) {
+        // thread 0's counter updates are complete (their results were used); the last
+        // workgroup out sees every other one's and zeroes the counters
+        __threadfence();
+        if (atomicAdd(&sched->queue[P], 1) == (int)gridDim.x - 1) {
+            for (int p = 0; p <= P; ++p)
+                atomicExch(&sched->queue[p], 0);
+        }
+    }
+}
+
 // Round r hands XCD x the tiles [r*W + x*W/8, r*W + (x+1)*W/8), W = the slots in use.
 template <bool GATE_UP, int SRC, int WS, int DT>
 __global__ __launch_bounds__(kThreads) void k_wide_gemm(GemmProblem g, int n_blocks, int m_tiles)
@@ -426,6 +493,10 @@ __global__ __launch_bounds__(kThreads) void k_wide_gemm(GemmProblem g, int n_blo
     __shared__ moe_u32x4 smem[wide_lds_bytes<WS>() / 16];
 
     const int total = wide_total<SRC>(g, n_blocks, m_tiles);
+    if (SRC == moe::ROWS_SORTED && g.sched != nullptr) {
+        wide_queue_loop<GATE_UP, SRC, WS, DT>(g, n_blocks, total, smem);
+        return;
+    }
     const int W = min((int)gridDim.x, (total + kXcds - 1) / kXcds * kXcds);
     const int per = W / kXcds;
     const int idx = blockIdx.x / kXcds;

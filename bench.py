@@ -664,7 +664,7 @@ def read_traffic(workload):
         if ":" in line:
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256") != kernel_source_hash():
+    if vals.get("kernel_source_sha256") != kernel_source_hash(vals.get("kernel", "")):
         return None
     try:
         return float(vals["traffic_bytes_per_launch"])
@@ -672,13 +672,28 @@ def read_traffic(workload):
         return None
 
 
-def kernel_source_hash():
-    """Hash of the GEMM kernel sources: counter summaries taken on other sources are stale."""
+# kernel family (as it appears in a kernel name) -> its source files
+KERNEL_FAMILY_SOURCES = {
+    "k_ws_gemm": ("moe_ws_kernel.h", "moe_gemm_ws.hip"),
+    "k_tiled_gemm": ("moe_tiled_kernel.h", "moe_gemm_tiled.hip"),
+    "k_block_gemm": ("moe_block_kernel.h", "moe_gemm_block.hip"),
+    "k_wide_gemm": ("moe_wide_kernel.h", "moe_gemm_wide.hip"),
+}
+
+
+def kernel_source_hash(kernel_names):
+    """Hash of the sources of the kernel family named in kernel_names (the summary's 'kernel'
+    line; its template arguments record the tile shape the plan chose) and the shared device
+    helpers: a counter summary taken on other sources of that kernel is stale.  Changes to
+    other kernels leave it valid."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mixture_experts_forward_amd", "csrc")
-    for name in ("moe_ws_kernel.h", "moe_tiled_kernel.h", "moe_block_kernel.h",
-                 "moe_wide_kernel.h", "moe_device.h", "moe_plan.cpp"):
+    names = []
+    for fam, files in KERNEL_FAMILY_SOURCES.items():
+        if fam in kernel_names:
+            names += files
+    for name in names + ["moe_device.h"]:
         h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()[:16]
 
@@ -727,12 +742,12 @@ def summarize_trace(args):
                 ", shared S=%d" % cfg.S if cfg.S else ""), ""]
     for c in args.pmc_commands:
         lines += ["Command (from /tmp, repository at $R):", "", "    " + c, ""]
-    lines += ["Input-generation and copy kernels, and the library GEMM of the bench's context "
-              "matmul, are omitted.", "",
+    lines += ["Input-generation and copy kernels, and the bench's context measurements (the "
+              "streaming-read kernel and the library GEMM of its matmul), are omitted.", "",
               "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
     for r in csv.DictReader(open(path)):
         n = r["Name"]
-        if "at::native" in n or "rocclr" in n or n.startswith("Cijk_"):
+        if "at::native" in n or "rocclr" in n or n.startswith("Cijk_") or "k_stream_read" in n:
             continue
         short = n.replace("(anonymous namespace)::", "").replace("void ", "")
         short = short.split("(")[0] if "(" in short else short
@@ -783,7 +798,7 @@ def summarize_pmc(args):
             lines.append("mfma_busy_pct: %.2f" % (100.0 * sum(busy) / len(busy)))
     lines += ["copy_bytes: %d" % args.copy_calibration,
               "kernel: %s" % "; ".join(res["kernels"]),
-              "kernel_source_sha256: %s" % kernel_source_hash(),
+              "kernel_source_sha256: %s" % kernel_source_hash("; ".join(res["kernels"])),
               "fetch_bytes_per_launch: %.0f" % res["FETCH_SIZE"],
               "write_bytes_per_launch: %.0f" % res["WRITE_SIZE"],
               "traffic_bytes_per_launch: %.0f" % (res["FETCH_SIZE"] + res["WRITE_SIZE"])]

@@ -96,6 +96,10 @@ moe::GemmProblem shared_problem(const moe::Plan &pl, const Ctx &c, bool gate_up)
     g.num_experts = 1;
     g.dtype = pl.dtype;
     g.num_groups = (pl.T + 16 * t.mt - 1) / (16 * t.mt);
+    if (pl.off_partial) {
+        g.partial = ws_at<float>(c.ws, pl.off_partial);
+        g.partial_bytes = pl.partial_bytes;
+    }
     return g;
 }
 

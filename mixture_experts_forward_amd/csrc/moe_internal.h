@@ -66,7 +66,15 @@ struct GemmProblem {
     const uint8_t *wscale;      // MXFP4 weights: [experts][n_weight_rows][K/32] E8M0
     TileSchedule *sched;        // 256 x 256 tile kernel, ROWS_SORTED: per-XCD tile ranges and
                                 // their counters (NULL: tiles dealt statically)
+    float *partial;             // 256 x 256 tile kernel, ROWS_DENSE: f32 partial tiles of the
+                                // K-split tiles (NULL: no split)
+    size_t partial_bytes;       // bytes at partial
+    int split_tiles;            // set by the launcher: tiles split along K ...
+    int split_parts;            // ... into this many parts each
 };
+
+// f32 partial tile of the K-split 256 x 256 kernel: 256 activation rows x 256 weight rows.
+constexpr size_t kWidePartialBytes = 256u * 256u * 4u;
 
 // Tile shape of one launch.
 //   weight-streaming kernel: NT 16-column tiles per workgroup (per half for gate-up), MT 16-row

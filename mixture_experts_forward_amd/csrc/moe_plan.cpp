@@ -104,7 +104,7 @@ void make_plan(const moe_params_t *p, int32_t S, Plan *pl, int wfmt)
         pl->down = {KERNEL_MX, 2, 1, 2, 3};
     }
     pl->shared_gate_up = {KERNEL_WIDE, 0, 16, 1, 2};
-    pl->shared_down = {KERNEL_BLOCK, 4, 8, 1, 3};
+    pl->shared_down = {KERNEL_WIDE, 0, 16, 1, 2};
     pl->block_m = (pl->gate_up.kind == KERNEL_WS || pl->gate_up.kind == KERNEL_MX)
                       ? kSortedBlockM
                       : 16 * pl->gate_up.mt;
@@ -140,8 +140,14 @@ void make_plan(const moe_params_t *p, int32_t S, Plan *pl, int wfmt)
     if (S > 0) {
         pl->off_hs = take((size_t)pl->T * S * 2);
         pl->off_ys = take((size_t)pl->T * pl->H * 2);
+        // f32 partial tiles of the shared expert's K-split 256 x 256 tiles: at most one per
+        // workgroup slot (kMaxSplitSlots slots of 256 x 256 f32)
+        pl->partial_bytes = (size_t)kMaxSplitSlots * 256 * 256 * 4;
+        pl->off_partial = take(pl->partial_bytes);
     } else {
         pl->off_hs = pl->off_ys = 0;
+        pl->off_partial = 0;
+        pl->partial_bytes = 0;
     }
     pl->total = o;
 }

@@ -15,6 +15,9 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxGroups = 64;
 constexpr int kSortedBlockM = 16;  // row tile of the weight-streaming GEMMs
 constexpr int kAlignChunk = 1024;   // routes per chunk of the chunked align/sort
+// Workgroup slots (CUs x resident workgroups) whose K-split partial tiles the shared expert's
+// workspace holds; on a device with more, the split uses fewer parts.
+constexpr int kMaxSplitSlots = 256;
 
 // Ints of device scratch the chunked align/sort needs for P routes and E experts (0: P fits one
 // workgroup, which needs none).
@@ -43,7 +46,8 @@ struct Plan {
     TileChoice gate_up, down, shared_gate_up, shared_down;
     // byte offsets into the workspace
     size_t off_ids, off_weights, off_sorted, off_offsets, off_tile_expert, off_inverse,
-        off_n_tiles, off_sched, off_align, off_h, off_y, off_hs, off_ys;
+        off_n_tiles, off_sched, off_align, off_h, off_y, off_hs, off_ys, off_partial;
+    size_t partial_bytes;  // bytes at off_partial (shared expert's K-split tiles)
     size_t total;
 };
 

@@ -200,9 +200,14 @@ template <int WS>
 constexpr int wide_lds_bytes() { return (kXStages + WS) * kHalf; }
 static_assert(kBM == kBW, "both operands' k-steps take kHalf bytes");
 
+// One 256 x 256 tile over k-steps [kbeg, kbeg + kcnt) of the K loop (visited from a rotated
+// start).  part == NULL: the whole K range, written as bf16 (gate-up: SiLU(gate)*up).  Else the
+// f32 accumulators of this K range go to part as [256 activation rows][256 weight rows] (rows
+// past the tile's real rows are not written), for k_wide_reduce to sum.
 template <bool GATE_UP, int SRC, int WS, int DT>
 __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mtile, int expert,
-                                          moe_u32x4 *smem)
+                                          moe_u32x4 *smem, int kbeg = 0, int kcnt = -1,
+                                          float *part = nullptr)
 {
     using St = Stage<kStep>;
     constexpr int kSlots = St::kSlots, kRows = St::kRowsPerLoad;
@@ -278,7 +283,7 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
     for (int i = 0; i < kMT32; ++i)
         mt_real += (32 * (wm + kWM * i) < n_real) ? 1 : 0;
 
-    const int nk = K / kStep;
+    const int nk = kcnt < 0 ? K / kStep : kcnt;
     const unsigned rkey = SRC == moe::ROWS_SORTED ? expert : nblk;
     const int rot = (int)((rkey * 7u) % (unsigned)nk);
 
@@ -290,7 +295,7 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
             acc[m][n] = moe_f32x16{};
 
     auto issue_x = [&](int i) {
-        const int kb = ((i + rot) % nk) * kStep;  // element offset of k-step i
+        const int kb = (kbeg + (i + rot) % nk) * kStep;  // element offset of k-step i
         const uint32_t so = (i % kXStages) * kHalf;
 #pragma unroll
         for (int j = 0; j < kXLoads; ++j)
@@ -298,7 +303,7 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
                 dma16(xsrc[j] + kb, x_dst + so + j * 1024);
     };
     auto issue_w = [&](int i) {
-        const int kb = ((i + rot) % nk) * kStep;
+        const int kb = (kbeg + (i + rot) % nk) * kStep;
         const uint32_t so = (i % WS) * kHalf;
 #pragma unroll
         for (int j = 0; j < kWLoads; ++j)
@@ -368,6 +373,31 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
     // LDS so that global stores write whole rows: 16-byte chunk c of row r sits at chunk
     // position c ^ (r % CPR) of the row (the 8-byte writes of 32 rows at one column then
     // spread over the banks; the 16-byte reads of one row stay conflict-free).
+    if (part != nullptr) {
+        // register 4q' + q of weight tile n: weight row wrow0[n] + 8q' + 4*(lane/32) + q of the
+        // tile, activation row 32*(wm + 4m) + lane%32; four consecutive f32 per store
+#pragma unroll
+        for (int m = 0; m < kMT32; ++m) {
+            if (m >= mt_real)
+                continue;
+            const int r = 32 * (wm + kWM * m) + rr;
+            if (r >= n_real)
+                continue;
+#pragma unroll
+            for (int n = 0; n < kNT32; ++n)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    moe_f32x4 v;
+                    v.x = acc[m][n][4 * q4 + 0];
+                    v.y = acc[m][n][4 * q4 + 1];
+                    v.z = acc[m][n][4 * q4 + 2];
+                    v.w = acc[m][n][4 * q4 + 3];
+                    *reinterpret_cast<moe_f32x4 *>(
+                        part + (size_t)r * kBW + wrow0[n] + 8 * q4 + 4 * rq) = v;
+                }
+        }
+        return;
+    }
     constexpr int TC = GATE_UP ? kBW / 2 : kBW;  // output columns of the tile
     constexpr int CPR = TC / 8;                  // 16-byte chunks per row
     static_assert(kBM * TC * 2 <= wide_lds_bytes<2>(), "output tile fits in LDS");
@@ -486,6 +516,92 @@ __device__ __forceinline__ void wide_queue_loop(const GemmProblem &g, int n_bloc
     }
 }
 
+// K split of the dense tiles (the shared expert at a few hundred tokens has too few 256 x 256
+// tiles for a whole number of rounds over the CUs): the launch's units are its first
+// total - n_split tiles whole, then each of the last n_split tiles as q_split parts of its K
+// loop, part j covering k-steps [j*nk/q_split, (j+1)*nk/q_split).  Units are dealt like tiles
+// (XCD-contiguous ranges per round); part j of split tile s writes f32 partial (s*q_split + j).
+__host__ __device__ inline int wide_split_units(int total, int n_split, int q_split)
+{
+    return total - n_split + n_split * q_split;
+}
+
+template <bool GATE_UP, int SRC, int WS, int DT>
+__device__ __forceinline__ void wide_split_loop(const GemmProblem &g, int n_blocks, int m_tiles,
+                                                int total, moe_u32x4 *smem)
+{
+    const int n_split = g.split_tiles, q_split = g.split_parts;
+    const int whole = total - n_split;
+    const int units = wide_split_units(total, n_split, q_split);
+    const int W = min((int)gridDim.x, (units + kXcds - 1) / kXcds * kXcds);
+    const int per = W / kXcds;
+    const int idx = blockIdx.x / kXcds;
+    if (idx >= per)
+        return;
+    const int nk = g.K / kStep;
+    for (int u = (blockIdx.x % kXcds) * per + idx; u < units; u += W) {
+        int t = u, kbeg = 0, kcnt = -1;
+        float *part = nullptr;
+        if (u >= whole) {
+            const int s = (u - whole) / q_split, j = (u - whole) % q_split;
+            t = whole + s;
+            kbeg = j * nk / q_split;
+            kcnt = (j + 1) * nk / q_split - kbeg;
+            part = g.partial + (size_t)(s * q_split + j) * (kBM * kBW);
+        }
+        int nblk, mtile, expert;
+        wide_decode<SRC>(g, t, n_blocks, m_tiles, nblk, mtile, expert);
+        wide_tile<GATE_UP, SRC, WS, DT>(g, nblk, mtile, expert, smem, kbeg, kcnt, part);
+        __syncthreads();  // the next unit's first loads follow every wave's last reads
+    }
+}
+
+// Sum of the K parts of the split tiles, in part order, and the tile epilogue: gate-up ->
+// SiLU(gate)*up, down -> the sum; rounded once to the element type.  One thread per 8 output
+// columns of one activation row of one split tile.
+template <bool GATE_UP, int DT>
+__global__ __launch_bounds__(256) void k_wide_reduce(GemmProblem g, int n_blocks, int m_tiles,
+                                                     int total)
+{
+    constexpr int TC = GATE_UP ? kBW / 2 : kBW;  // output columns of a tile
+    constexpr int C8 = TC / 8;
+    const int n_split = g.split_tiles, q_split = g.split_parts;
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= n_split * kBM * C8)
+        return;
+    const int s = i / (kBM * C8), r = (i / C8) % kBM, c8 = i % C8;
+    const int t = total - n_split + s;
+    const int nblk = t / m_tiles, mtile = t % m_tiles;
+    const int row = mtile * kBM + r;
+    const int col = nblk * TC + 8 * c8;
+    if (row >= g.rows || col >= g.n_out)
+        return;
+    float a[8] = {}, b[8] = {};
+    for (int j = 0; j < q_split; ++j) {
+        const float *p = g.partial + (size_t)(s * q_split + j) * (kBM * kBW) + (size_t)r * kBW;
+        const moe_f32x4 a0 = *reinterpret_cast<const moe_f32x4 *>(p + 8 * c8);
+        const moe_f32x4 a1 = *reinterpret_cast<const moe_f32x4 *>(p + 8 * c8 + 4);
+        a[0] += a0.x; a[1] += a0.y; a[2] += a0.z; a[3] += a0.w;
+        a[4] += a1.x; a[5] += a1.y; a[6] += a1.z; a[7] += a1.w;
+        if (GATE_UP) {  // the up rows of the same columns: weight rows 128 + c
+            const moe_f32x4 b0 = *reinterpret_cast<const moe_f32x4 *>(p + TC + 8 * c8);
+            const moe_f32x4 b1 = *reinterpret_cast<const moe_f32x4 *>(p + TC + 8 * c8 + 4);
+            b[0] += b0.x; b[1] += b0.y; b[2] += b0.z; b[3] += b0.w;
+            b[4] += b1.x; b[5] += b1.y; b[6] += b1.z; b[7] += b1.w;
+        }
+    }
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        v[e] = GATE_UP ? a[e] / (1.0f + __expf(-a[e])) * b[e] : a[e];
+    moe_u32x4 o;
+    o.x = moe_pack2<DT>(v[0], v[1]);
+    o.y = moe_pack2<DT>(v[2], v[3]);
+    o.z = moe_pack2<DT>(v[4], v[5]);
+    o.w = moe_pack2<DT>(v[6], v[7]);
+    *reinterpret_cast<moe_u32x4 *>(g.out + (size_t)row * g.n_out + col) = o;
+}
+
 // Round r hands XCD x the tiles [r*W + x*W/8, r*W + (x+1)*W/8), W = the slots in use.
 template <bool GATE_UP, int SRC, int WS, int DT>
 __global__ __launch_bounds__(kThreads) void k_wide_gemm(GemmProblem g, int n_blocks, int m_tiles)
@@ -495,6 +611,10 @@ __global__ __launch_bounds__(kThreads) void k_wide_gemm(GemmProblem g, int n_blo
     const int total = wide_total<SRC>(g, n_blocks, m_tiles);
     if (SRC == moe::ROWS_SORTED && g.sched != nullptr) {
         wide_queue_loop<GATE_UP, SRC, WS, DT>(g, n_blocks, total, smem);
+        return;
+    }
+    if (SRC != moe::ROWS_SORTED && g.partial != nullptr) {
+        wide_split_loop<GATE_UP, SRC, WS, DT>(g, n_blocks, m_tiles, total, smem);
         return;
     }
     const int W = min((int)gridDim.x, (total + kXcds - 1) / kXcds * kXcds);

@@ -757,7 +757,8 @@ def summarize_trace(args):
     lines += ["", "Template arguments: k_ws_gemm<GATE_UP, SRC, NT, MT, KSPLIT, STAGES, DT> (SRC 0 "
               "sorted, 1 direct, 2 dense, 3 scan; DT 0 bf16, 1 f16); k_tiled_gemm<GATE_UP, SRC, "
               "BM, NTW, STAGES, DT>; k_block_gemm<GATE_UP, SRC, TN, STAGES, DT>; "
-              "k_wide_gemm<GATE_UP, SRC, WS, DT> (WS weight stages); k_combine<DT>."]
+              "k_wide_gemm<GATE_UP, SRC, WS, DT> (WS weight stages); k_wide_reduce<GATE_UP, DT> (sum "
+              "of the K-split dense tiles' parts); k_combine<DT>."]
     out = os.path.join(PROFILE_DIR, "kernel_trace_%s.md" % cfg.name)
     os.makedirs(PROFILE_DIR, exist_ok=True)
     open(out, "w").write("\n".join(lines) + "\n")

@@ -20,9 +20,11 @@
  *     keep graph addresses stable; invocation-local scratch, no module-global arena).
  *   - All arguments are validated on the host before anything is enqueued: a call that returns
  *     an error has launched nothing.  The library never falls back silently to another path.
- *   - Results are bitwise deterministic for identical inputs: no floating-point atomics; the
- *     only atomics are integer counters in the align step, whose results do not depend on
- *     their order.
+ *   - Results are bitwise deterministic for identical inputs: no floating-point atomics.  The
+ *     only atomics are integer counters: the align step's histograms, whose results do not
+ *     depend on their order, and the tile counters of the 256 x 256 tile GEMM on the sorted
+ *     layout (workspace), which decide only which workgroup computes a tile, never how.  Calls
+ *     that share one workspace must therefore not overlap (as for any workspace contents).
  *   - Inputs are assumed finite.  T = 0 returns MOE_OK and enqueues nothing (pointers may then
  *     be NULL); moe_align_sort is the exception: with T = 0 it still writes its (empty) layout.
  *   - Route ids outside [0, E) (the -1 padding routes of the aiter MI308 decoding PR,

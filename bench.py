@@ -305,6 +305,32 @@ def main():
     # the gate-up kernel's own bound: its bytes at 8 TB/s or its FLOPs at the bf16 MFMA peak
     gu_mfma_bound = gu_flops / perfmodel.BF16_MFMA_PEAK_FLOP_PER_S > \
         gu_bytes / perfmodel.HBM_PEAK_BYTES_PER_S
+    # algorithmic bytes of each HBM-bound stage (what it must read and write once) and its rate
+    # against the 8 TB/s peak: touched experts' weights, the activation / intermediate rows it
+    # reads and the rows it writes (16-bit elements; MXFP4 / FP8 weights scaled by wfac)
+    eb = 2.0  # bytes per 16-bit element
+    stage_bytes = {
+        "route": 4.0 * cfg.T * cfg.E + (4.0 * cfg.E if cfg.bias else 0.0) + 8.0 * P,
+        "gate_up": gu_bytes,
+        "down": touched_mean * 2.0 * cfg.H * cfg.F * wfac + eb * P * cfg.F + eb * P * cfg.H,
+        "combine": eb * P * cfg.H + 8.0 * P + eb * cfg.T * cfg.H * (2.0 if S > 0 else 1.0),
+    }
+    if S > 0:
+        stage_bytes["shared"] = (6.0 * cfg.H * S * eb / 2.0 + eb * cfg.T * cfg.H
+                                 + 2.0 * eb * cfg.T * S + eb * cfg.T * cfg.H)
+    stage_flops = {"gate_up": gu_flops, "down": 2.0 * P * cfg.H * cfg.F,
+                   "shared": 2.0 * cfg.T * 3.0 * cfg.H * S}
+    stage_roofline = {}
+    for name, b in stage_bytes.items():
+        t = per_stage.get(name)
+        if t:
+            gbs = b / (t * 1e-3) / 1e9
+            stage_roofline[name] = {"algorithmic_bytes": b, "achieved_gbps": round(gbs, 1),
+                                    "frac_of_hbm_peak": round(gbs / peak_gbs, 4)}
+            if stage_flops.get(name):
+                tf = stage_flops[name] / (t * 1e-3) / 1e12
+                stage_roofline[name].update(achieved_tflops=round(tf, 1),
+                                            frac_of_mfma_peak=round(tf / peak_tflops, 4))
     # the committed counter summaries are of the bf16 kernels with bf16 weights
     traffic = read_traffic(cfg.name) if args.dtype == "bf16" and args.weights == "16bit" else None
 
@@ -357,6 +383,7 @@ def main():
         "warm_ms_per_step": round(warm_ms, 5),
         "staged_ms_per_step": round(staged_ms, 5),
         "stage_ms": {k: round(v, 5) for k, v in per_stage.items()},
+        "stage_roofline": stage_roofline,
         "roofline": ({"kernel": "gate-up GEMM of the routed experts", "bound": "mfma",
                       "achieved": round(gu_tflops, 1), "peak": peak_tflops, "unit": "TFLOP/s",
                       "frac": round(gu_tflops / peak_tflops, 4), "traffic": traffic,

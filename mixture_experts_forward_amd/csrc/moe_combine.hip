@@ -27,18 +27,36 @@ __global__ __launch_bounds__(kThreads) void k_combine(
     if (c >= H)
         return;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-        const size_t r = (size_t)t * k + j;
-        const int e = ids[r];
-        if (e < 0 || e >= E)
-            continue;
-        const float w = weights[r];
-        const size_t yr = row_of_route ? (size_t)row_of_route[r] : r;
-        const moe_u32x4 v = *reinterpret_cast<const moe_u32x4 *>(y + yr * H + c);
+    // routes in groups of kGroup: the group's row loads are all issued before any is summed, so
+    // their latencies overlap; the sums still run in j order
+    constexpr int kGroup = 8;
+    for (int j0 = 0; j0 < k; j0 += kGroup) {
+        moe_u32x4 v[kGroup];
+        float w[kGroup];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            acc[2 * q] += w * moe_to_f32<DT>(v[q]);
-            acc[2 * q + 1] += w * moe_to_f32<DT>(v[q] >> 16);
+        for (int u = 0; u < kGroup; ++u) {
+            const int j = j0 + u;
+            w[u] = 0.0f;
+            v[u] = moe_u32x4{0u, 0u, 0u, 0u};
+            if (j < k) {
+                const size_t r = (size_t)t * k + j;
+                const int e = ids[r];
+                if (e >= 0 && e < E) {
+                    w[u] = weights[r];
+                    const size_t yr = row_of_route ? (size_t)row_of_route[r] : r;
+                    v[u] = *reinterpret_cast<const moe_u32x4 *>(y + yr * H + c);
+                }
+            }
+        }
+        // a skipped route adds 0 * 0 = +0, which leaves the sum as it is (the sum starts at +0
+        // and never becomes -0)
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[2 * q] += w[u] * moe_to_f32<DT>(v[u][q]);
+                acc[2 * q + 1] += w[u] * moe_to_f32<DT>(v[u][q] >> 16);
+            }
         }
     }
     if (ys) {

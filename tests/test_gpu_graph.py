@@ -28,13 +28,22 @@ def _call(cfg, d, out, ws):
                              out=out, workspace=ws)
 
 
+# reduced dimensions that keep each workload's kernel choice: the weight-streaming kernel
+# (decode), the row-tiled kernel (batch), and the 256 x 256 kernel on the sorted layout with
+# its per-XCD tile counters and, with a shared expert, its K-split dense tiles
+_DIMS = {"kimi-k2-shared": dict(H=1024, E=64, F=256, S=512),
+         "ds-v3-grouped-prefill": dict(H=512, E=16, F=256, num_expert_group=4, topk_group=2),
+         "kimi-k2-wide": dict(H=512, E=16, F=256, S=640)}
+
+
 @pytest.mark.parametrize("name,T", [("qwen3-30b-decode", 32), ("qwen3-30b-decode", 4),
                                     ("qwen3-235b-batch", 160),
-                                    ("kimi-k2-shared", 40)])
+                                    ("kimi-k2-shared", 40),
+                                    ("ds-v3-grouped-prefill", 512),
+                                    ("kimi-k2-wide", 300)])
 def test_graph_replays_match_eager(name, T):
-    cfg = replace(CONFIGS[name], T=T)
-    if name == "kimi-k2-shared":
-        cfg = replace(cfg, H=1024, E=64, F=256, S=512)
+    base = CONFIGS["kimi-k2-shared" if name == "kimi-k2-wide" else name]
+    cfg = replace(base, T=T, **_DIMS.get(name, {}))
     d = make_inputs(cfg, DEV, num_tokens=T)
     other = make_inputs(cfg, DEV, num_tokens=T, seed=7)
     p = moe.make_params(cfg.T, cfg.H, cfg.E, cfg.F, cfg.k, cfg.scoring, cfg.renormalize,

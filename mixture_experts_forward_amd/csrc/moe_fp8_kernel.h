@@ -333,6 +333,151 @@ __global__ __launch_bounds__(64 * kWaves) void k_fp8_gemm(Fp8Problem p, int n_bl
     }
 }
 
+// ---------------------------------------------------------------- weight-streaming form
+// A few rows per expert (decode): a workgroup owns one expert and NT 16-column tiles of the
+// output; its KSPLIT waves split the K loop and are summed through LDS in a fixed order, and the
+// expert's rows go through in 16-row passes (one pass at decode).  An e4m3 k-step of a weight
+// row is one 128-byte line; lane l loads bytes [16q, 16q + 16) and [64 + 16q, 80 + 16q) of row
+// l%16 (q = l/16), the two chunks join() pairs, straight into the MFMA A operand -- no LDS
+// transpose -- with non-temporal loads STAGES-1 k-steps ahead, and its activation row likewise
+// into B; a wave's two load instructions cover the tile's 16 whole lines.  Scales and
+// accumulation as k_fp8_gemm.
+template <int NT, int KSPLIT, int STAGES>
+__global__ __launch_bounds__(64 * KSPLIT) void k_fp8_ws(Fp8Problem p)
+{
+    __shared__ moe_f32x4 s_red[(KSPLIT > 1 ? KSPLIT - 1 : 1) * NT * 64];
+    const int lane = threadIdx.x & 63;
+    const int kw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int expert = blockIdx.y;
+    const int col0 = blockIdx.x * (16 * NT);
+    int r0, r1;
+    if (p.offsets != nullptr) {
+        contig_rows(p, expert, r0, r1);
+    } else {
+        r0 = expert * p.max_m;
+        r1 = r0 + min(max(p.masked_m[expert], 0), p.max_m);
+    }
+    const int n_rows = r1 - r0;
+    if (n_rows <= 0)
+        return;
+    const int K = p.K, KB = p.KB;
+    const int rr = lane & 15, rq = lane >> 4;
+
+    const uint8_t *B = p.b + (size_t)expert * p.N * K;
+    const uint8_t *wrow[NT];
+    bool tile_ok[NT];
+    int sb_base[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int c = col0 + 16 * nt;
+        tile_ok[nt] = c < p.N;
+        const int cc = tile_ok[nt] ? c : 0;
+        wrow[nt] = B + (size_t)(cc + rr) * K + 16 * rq;
+        sb_base[nt] = (expert * p.NB + cc / 128) * KB;
+    }
+    // K blocks of this wave, visited from a rotated start
+    const int per = (KB + KSPLIT - 1) / KSPLIT;
+    const int kb0 = kw * per;
+    const int nk = max(0, min(KB, kb0 + per) - kb0);
+    const int rot = nk > 0 ? (int)((blockIdx.x * 7u + blockIdx.y * 13u) % (unsigned)nk) : 0;
+
+    for (int pass0 = 0; pass0 < n_rows; pass0 += 16) {
+        // B operand column lane%16: row pass0 + lane%16 of the expert's rows (past its rows:
+        // its first row, whose results are never stored)
+        const int r = pass0 + rr;
+        const bool rok = r < n_rows;
+        const size_t arow_i = (size_t)r0 + (rok ? r : 0);
+        const uint8_t *arow = p.a + arow_i * K + 16 * rq;
+        const float *asc = p.a_scale + arow_i * KB;
+
+        moe_f32x4 acc[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+            acc[nt] = moe_f32x4{0.f, 0.f, 0.f, 0.f};
+        moe_u32x4 w[STAGES][NT][2], x[STAGES][2];
+        float sa[STAGES], sb[STAGES][NT];
+        auto load = [&](int st, int i) {
+            const int kb = kb0 + (i + rot) % nk;
+            const int k = kb * 128;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                if (tile_ok[nt]) {
+                    w[st][nt][0] = load_nt16(wrow[nt] + k);
+                    w[st][nt][1] = load_nt16(wrow[nt] + k + 64);
+                    sb[st][nt] = p.b_scale[sb_base[nt] + kb];
+                }
+            }
+            x[st][0] = load16(arow + k);
+            x[st][1] = load16(arow + k + 64);
+            sa[st] = asc[kb];
+        };
+        auto compute = [&](int st) {
+            const moe_i32x8 bx = join(x[st][0], x[st][1]);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                if (!tile_ok[nt])
+                    continue;
+                const moe_f32x4 part = mfma_fp8_block(join(w[st][nt][0], w[st][nt][1]), bx);
+                const float s = sa[st] * sb[st][nt];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    acc[nt][q] = fmaf(part[q], s, acc[nt][q]);
+            }
+        };
+        // software pipeline: STAGES-1 k-steps in flight
+#pragma unroll
+        for (int st = 0; st < STAGES - 1; ++st)
+            if (st < nk)
+                load(st, st);
+        for (int i = 0; i < nk; i += STAGES) {
+#pragma unroll
+            for (int st = 0; st < STAGES; ++st) {
+                const int cur = i + st;
+                if (cur < nk) {
+                    const int nxt = cur + STAGES - 1;
+                    if (nxt < nk)
+                        load((st + STAGES - 1) % STAGES, nxt);
+                    compute(st);
+                }
+            }
+        }
+
+        // ---- fixed-order sum over the K-split waves
+        if (KSPLIT > 1) {
+            __syncthreads();
+            if (kw > 0) {
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    s_red[((kw - 1) * NT + nt) * 64 + lane] = acc[nt];
+            }
+            __syncthreads();
+            if (kw == 0) {
+#pragma unroll
+                for (int v = 0; v < KSPLIT - 1; ++v)
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt)
+                        acc[nt] += s_red[(v * NT + nt) * 64 + lane];
+            }
+        }
+
+        // ---- epilogue (wave 0): lane holds columns 4*(lane/16)+q of row pass0 + lane%16
+        if (kw == 0 && rok) {
+            uint16_t *orow = p.out + ((size_t)r0 + r) * p.N;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                if (!tile_ok[nt])
+                    continue;
+                moe_u32x2 packed;
+                packed.x = moe_pack_bf16x2(acc[nt][0], acc[nt][1]);
+                packed.y = moe_pack_bf16x2(acc[nt][2], acc[nt][3]);
+                *reinterpret_cast<moe_u32x2 *>(orow + col0 + 16 * nt + 4 * rq) = packed;
+            }
+        }
+        if (KSPLIT > 1)
+            __syncthreads();  // the next pass reuses s_red
+    }
+}
+
 // ---------------------------------------------------------------- 256 x 256 tile form
 
 // Grid of a launch: tiles rounded up to a multiple of 8.

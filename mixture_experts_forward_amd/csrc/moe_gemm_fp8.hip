@@ -1,5 +1,6 @@
 // moe_gemm_fp8.hip -- launches of the block-scaled FP8 grouped GEMM (moe_fp8_kernel.h): the
-// 64-row form for blocks of up to 64 rows, else the 256-row tile form (256 or, when that gives
+// weight-streaming form for a few rows per expert (decode), the 64-row form for blocks of up to
+// 64 rows, else the 256-row tile form (256 or, when that gives
 // fewer than two workgroups per CU, 128 columns per workgroup); the 64-row form also when K is
 // not a multiple of 512 or a_scale is not 16-byte aligned.  Tile shapes measured on MI355X on
 // the page's decode shapes.
@@ -36,6 +37,17 @@ void launch_fp8_wide(const moe_fp8::Fp8Problem &p, int m_tiles, hipStream_t stre
                        dim3(moe_wide::kThreads), 0, stream, p, n_blocks, m_tiles);
 }
 
+// The weight-streaming form: one workgroup per (32 output columns, expert); K split over four
+// waves (two when K has fewer than 16 blocks).
+void launch_fp8_ws(const moe_fp8::Fp8Problem &p, hipStream_t stream)
+{
+    const dim3 grid((p.N + 31) / 32, p.E);
+    if (p.KB >= 16)
+        hipLaunchKernelGGL((moe_fp8::k_fp8_ws<2, 4, 3>), grid, dim3(64 * 4), 0, stream, p);
+    else
+        hipLaunchKernelGGL((moe_fp8::k_fp8_ws<2, 2, 3>), grid, dim3(64 * 2), 0, stream, p);
+}
+
 int device_cus()
 {
     int dev = 0, n = 0;
@@ -69,8 +81,13 @@ void launch_fp8_gemm(const uint8_t *a, const float *a_scale, const uint8_t *b,
     p.K = K;
     p.KB = K / 128;
     p.NB = (N + 127) / 128;
-    // Blocks of up to 64 rows: the 64-row form (one row tile).  Taller blocks: the 256-row
-    // form, which needs 4-block scale groups and 16-byte aligned activation scales.
+    // Blocks of up to 16 rows (decode): the weight-streaming form.  Up to 64 rows: the 64-row
+    // form (one row tile).  Taller blocks: the 256-row form, which needs 4-block scale groups
+    // and 16-byte aligned activation scales.
+    if (max_m <= 16) {
+        launch_fp8_ws(p, stream);
+        return;
+    }
     if (max_m <= 64 || p.KB % 4 != 0 || ((uintptr_t)a_scale & 15u) != 0) {
         launch_one<64, 4, 2>(p, stream);
         return;
@@ -104,6 +121,10 @@ void launch_fp8_gemm_contig(const uint8_t *a, const float *a_scale, const uint8_
     p.NB = (N + 127) / 128;
     // the mean rows per expert picks the tile form, as max_m does for the masked layout
     const int mean_rows = (P + E - 1) / E;
+    if (mean_rows <= 8) {
+        launch_fp8_ws(p, stream);
+        return;
+    }
     if (mean_rows <= 64 || p.KB % 4 != 0 || ((uintptr_t)a_scale & 15u) != 0) {
         launch_one<64, 4, 2>(p, stream);
         return;

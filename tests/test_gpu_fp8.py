@@ -53,6 +53,8 @@ def _host(d):
     (3, 37, 192, 384, [37, 0, 20]),           # ragged rows, an empty expert, N past 128
     (4, 64, 256, 512, None),                   # one 64-row tile per expert
     (2, 130, 128, 256, [130, 65]),             # three row tiles, a partial last one
+    (4, 16, 256, 2048, [16, 0, 1, 9]),         # weight-streaming form (decode): 4-way K split
+    (3, 12, 192, 384, [12, 5, 0]),             # weight-streaming form: 2-way K split, N % 32
     (5, 16, 64, 128, [-1, 99, 16, 0, 3]),      # one k-block; counts clamped to [0, max_m]
     (3, 200, 256, 1024, [200, 7, 130]),        # 256-row form, 128 columns per workgroup
     (512, 65, 256, 512, None),                 # 256-row form, 256 columns per workgroup
@@ -121,6 +123,9 @@ def _contig_inputs(E, counts, N, K, seed, extra_rows=3):
     (4, [5, 0, 37, 64], 192, 384),            # 64-row form: ragged, an empty expert
     (3, [130, 1, 64], 128, 256),              # 64-row form: several row tiles of one expert
     (3, [300, 77, 256], 256, 1024),           # 256-row form (mean rows > 64), partial tiles
+    (6, [1, 0, 3, 17, 2, 5], 192, 384),       # weight-streaming form (mean rows <= 8): a
+                                              # 17-row expert takes two 16-row passes
+    (8, [2, 1, 0, 4, 3, 1, 2, 2], 256, 2048),  # weight-streaming form, 4-way K split
     (2, [0, 0], 64, 128),                     # no rows at all
 ])
 def test_fp8_contiguous_matches_oracle(E, counts, N, K):

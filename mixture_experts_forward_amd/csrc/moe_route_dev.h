@@ -41,16 +41,39 @@ __device__ __forceinline__ int select_index(uint64_t key)
     return (int)(0xffffffffu - (uint32_t)key);
 }
 
+// v of the lane that DPP control CTRL selects within this lane's row of 16 (every lane of the
+// row has a source under the controls used here)
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v)
+{
+    const uint32_t lo =
+        (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xf, 0xf, false);
+    const uint32_t hi =
+        (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xf, 0xf, false);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ uint64_t lane_u64(uint64_t v, int l)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Maximum over the 64 lanes, returned to every lane.  Within each row of 16 lanes four DPP
+// exchanges (lane ^ 1, lane ^ 2, then the mirror images within 8 and within 16 lanes) leave the
+// row's maximum in all its lanes; the four rows' maxima are then read as scalars.  DPP moves
+// run on the VALU, not through the LDS crossbar that a general lane shuffle takes.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const uint32_t lo = __shfl_xor((uint32_t)v, off);
-        const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off);
-        const uint64_t o = ((uint64_t)hi << 32) | lo;
-        v = o > v ? o : v;
-    }
-    return v;
+    v = max_u64(v, dpp_u64<0xB1>(v));   // quad_perm [1,0,3,2]
+    v = max_u64(v, dpp_u64<0x4E>(v));   // quad_perm [2,3,0,1]
+    v = max_u64(v, dpp_u64<0x141>(v));  // row_half_mirror
+    v = max_u64(v, dpp_u64<0x140>(v));  // row_mirror
+    return max_u64(max_u64(lane_u64(v, 0), lane_u64(v, 16)),
+                   max_u64(lane_u64(v, 32), lane_u64(v, 48)));
 }
 
 __device__ __forceinline__ double wave_sum_f64(double v)

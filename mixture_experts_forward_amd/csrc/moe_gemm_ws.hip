@@ -5,16 +5,34 @@ namespace {
 
 using moe::GemmProblem;
 
-template <bool GATE_UP, int SRC, int NT, int MT, int KSPLIT, int STAGES>
-void launch_one(const GemmProblem &g, hipStream_t stream)
+template <bool GATE_UP, int SRC, int NT, int MT, int KSPLIT, int STAGES, int SEGK>
+void launch_seg(const GemmProblem &g, hipStream_t stream)
 {
     const dim3 grid((g.n_out + 16 * NT - 1) / (16 * NT), g.num_groups);
     if (g.dtype == 1)
-        hipLaunchKernelGGL((moe_ws::k_ws_gemm<GATE_UP, SRC, NT, MT, KSPLIT, STAGES, 1>), grid,
-                           dim3(64 * KSPLIT), 0, stream, g);
+        hipLaunchKernelGGL((moe_ws::k_ws_gemm<GATE_UP, SRC, NT, MT, KSPLIT, STAGES, 1, SEGK>),
+                           grid, dim3(64 * KSPLIT), 0, stream, g);
     else
-        hipLaunchKernelGGL((moe_ws::k_ws_gemm<GATE_UP, SRC, NT, MT, KSPLIT, STAGES, 0>), grid,
-                           dim3(64 * KSPLIT), 0, stream, g);
+        hipLaunchKernelGGL((moe_ws::k_ws_gemm<GATE_UP, SRC, NT, MT, KSPLIT, STAGES, 0, SEGK>),
+                           grid, dim3(64 * KSPLIT), 0, stream, g);
+}
+
+// Weight rows a multiple of 4 KB apart stream faster in 256-byte row segments (two k-steps per
+// load, one segment in flight: as many bytes ahead as two k-steps of the one-k-step form).
+// The form needs every wave's K range to hold whole segments.  Its first compute waits for a
+// whole segment, so it pays only on grids of several workgroups per resident slot (MI355X,
+// qwen3-30b gate-up: 6144 workgroups 108 -> 106.5 us; one token, 384 workgroups: 19.3 -> 20.6).
+constexpr long long kSeg2MinWorkgroups = 2048;
+template <bool GATE_UP, int SRC, int NT, int MT, int KSPLIT, int STAGES>
+void launch_one(const GemmProblem &g, hipStream_t stream)
+{
+    const long long wgs = (long long)((g.n_out + 16 * NT - 1) / (16 * NT)) * g.num_groups;
+    const bool seg2 = STAGES == 3 && (g.K * 2) % 4096 == 0 && (g.K / 64) % (2 * KSPLIT) == 0 &&
+                      wgs >= kSeg2MinWorkgroups;
+    if (seg2)
+        launch_seg<GATE_UP, SRC, NT, MT, KSPLIT, 2, 2>(g, stream);
+    else
+        launch_seg<GATE_UP, SRC, NT, MT, KSPLIT, STAGES, 1>(g, stream);
 }
 
 // Instantiated tile shapes.  Every shape the host plan may pick must be listed here.

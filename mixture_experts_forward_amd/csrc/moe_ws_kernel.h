@@ -11,9 +11,12 @@
 //   - a workgroup owns one expert (or one route on the direct path, or a block of tokens for
 //     the shared expert) and NT 16-column tiles of the output; it reads each weight row it
 //     needs once per pass over its rows;
-//   - weight loads are non-temporal and each load instruction covers whole 128-byte lines (8
-//     lanes x 16 bytes per row, 8 rows per instruction), with STAGES-1 k-steps of 64 elements
-//     in flight per wave in registers;
+//   - weight loads are non-temporal and each load instruction covers whole 128-byte lines, with
+//     STAGES-1 segments of SEGK k-steps (64 elements each) in flight per wave in registers.  A
+//     load instruction reads 8/SEGK rows x 128*SEGK bytes: with SEGK = 1, 8 rows x one k-step;
+//     with SEGK = 2, 4 rows x 256 bytes.  Rows a power-of-two multiple of 4 KB apart read at the
+//     same offset map onto few HBM channels, so on such strides the longer row segments stream
+//     faster (MI355X, 4 KB rows: 6.8 -> 7.1 TB/s for a pure read of the same bytes);
 //   - every workgroup starts its K loop at a different k-step (rotated, wrapping around), so
 //     the concurrent requests of the whole grid spread over all HBM channels instead of all
 //     hitting the same offset of 4 KB rows at once;
@@ -76,25 +79,31 @@ __device__ __forceinline__ moe_u32x4 load_cached(const uint16_t *p)
 }
 
 // LDS bytes of one workgroup: per-wave transpose buffers, reused for the K-split sum.
-template <int NW, int MT, int KSPLIT>
+template <int NW, int MT, int KSPLIT, int SEGK>
 struct WsSmem {
-    static constexpr int kTranspose = KSPLIT * NW * 16 * 8;            // 16-byte slots
+    static constexpr int kTranspose = KSPLIT * NW * 16 * 8 * SEGK;     // 16-byte slots
     static constexpr int kReduce = (KSPLIT > 1 ? KSPLIT - 1 : 0) * MT * NW * 64;  // f32x4
     static constexpr int kSlots = kTranspose > kReduce ? kTranspose : kReduce;
 };
 
-template <bool GATE_UP, int SRC, int NT, int MT, int KSPLIT, int STAGES, int DT>
-__global__ __launch_bounds__(64 * KSPLIT) void k_ws_gemm(GemmProblem g)
+// One workgroup's tile: column block bx, row group by.
+// SEGK: k-steps per weight load segment (1 or 2); the K range of every wave must hold a whole
+// number of segments (the launcher checks K).
+template <bool GATE_UP, int SRC, int NT, int MT, int KSPLIT, int STAGES, int DT, int SEGK>
+__device__ __forceinline__ void ws_body(const GemmProblem &g, int bx, int by, moe_u32x4 *s_mem)
 {
     constexpr int NW = GATE_UP ? 2 * NT : NT;  // 16-row weight tiles per k-step
     constexpr int ROWS = 16 * MT;              // rows per pass
-    using Smem = WsSmem<NW, MT, KSPLIT>;
-    __shared__ moe_u32x4 s_mem[Smem::kSlots];
+    constexpr int RPI = 8 / SEGK;              // weight rows per load instruction
+    constexpr int LPR = 8 * SEGK;              // lanes per row of an instruction = row slots
+    constexpr int NLD = 2 * SEGK;              // load instructions per 16-row tile and segment
+    constexpr int TS = 16 * LPR;               // transpose slots per 16-row tile
+    static_assert(SEGK == 1 || SEGK == 2, "segments of one or two k-steps");
 
     const int lane = threadIdx.x & 63;
     const int kw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index (uniform)
-    const int col0 = blockIdx.x * (16 * NT);
-    const int grp = blockIdx.y;
+    const int col0 = bx * (16 * NT);
+    const int grp = by;
     const int K = g.K;
 
     // ---- which rows this workgroup owns
@@ -131,11 +140,11 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_ws_gemm(GemmProblem g)
     if (n_rows <= 0)
         return;
 
-    // ---- weight loads: lane reads 16 bytes (chunk lane%8) of rows lane/8 and 8 + lane/8 of
-    //      each 16-row tile
+    // ---- weight loads: instruction j of a segment reads 16 bytes (chunk lane % LPR) of row
+    //      RPI*j + lane / LPR of each 16-row tile
     const int w_rows = GATE_UP ? 2 * g.n_out : g.n_out;
     const uint16_t *W = g.weight + (size_t)expert * w_rows * K;
-    const int lrow = lane >> 3, lchunk = lane & 7;
+    const int lrow = lane / LPR, lchunk = lane % LPR;
     const uint16_t *wld[NW];
     bool tile_ok[NT];
 #pragma unroll
@@ -147,31 +156,44 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_ws_gemm(GemmProblem g)
         if (GATE_UP)
             wld[NT + nt] = W + (size_t)(row + g.n_out) * K + 8 * lchunk;
     }
-    // LDS transpose buffer of this wave: NW tiles x 16 rows x 8 slots; row r keeps chunk c in
-    // slot c ^ (r >> 1)
-    moe_u32x4 *tbuf = s_mem + kw * NW * 128;
-    const int wslot0 = lrow * 8 + (lchunk ^ (lrow >> 1));
-    const int wslot1 = (lrow + 8) * 8 + (lchunk ^ ((lrow + 8) >> 1));
+    // LDS transpose buffer of this wave: NW tiles x 16 rows x LPR slots; row r keeps chunk c
+    // (elements 8c .. 8c+7 of the segment) in slot c ^ swz(r): the 16 rows read at one chunk
+    // position, and the LPR chunks of a row written by one instruction, hit distinct banks
+    auto swz = [](int r) { return SEGK == 1 ? (r >> 1) : (r & 15); };
+    moe_u32x4 *tbuf = s_mem + kw * NW * TS;
+    int wslot[NLD];
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+        const int r = RPI * j + lrow;
+        wslot[j] = r * LPR + (lchunk ^ swz(r));
+    }
     const int rrow = lane & 15, rq = lane >> 4;
-    const int rslot0 = rrow * 8 + (rq ^ (rrow >> 1));        // chunks 0..3 -> k 0..31
-    const int rslot1 = rrow * 8 + ((rq + 4) ^ (rrow >> 1));  // chunks 4..7 -> k 32..63
-    const int xoff = 8 * rq;                                 // B operand: k = 8*(lane/16) (+32)
+    int rslot0[SEGK], rslot1[SEGK];
+#pragma unroll
+    for (int h = 0; h < SEGK; ++h) {
+        rslot0[h] = rrow * LPR + ((8 * h + rq) ^ swz(rrow));      // k-step h, k 0..31
+        rslot1[h] = rrow * LPR + ((8 * h + rq + 4) ^ swz(rrow));  // k-step h, k 32..63
+    }
+    const int xoff = 8 * rq;  // B operand: k = 8*(lane/16) (+32)
 
-    // ---- K range of this wave, visited from a rotated start
+    // ---- K range of this wave (nk k-steps, nseg segments), visited from a rotated start
     const int nks = K / 64;
     const int per = (nks + KSPLIT - 1) / KSPLIT;
     const int ks0 = kw * per;
     const int nk = max(0, min(nks, ks0 + per) - ks0);
-    const int rot = nk > 0 ? (int)((blockIdx.x * 7u + blockIdx.y * 13u) % (unsigned)nk) : 0;
+    const int nseg = nk / SEGK;
+    const int rot =
+        nseg > 0 ? (int)((bx * 7u + by * 13u) % (unsigned)nseg) : 0;
 
-    moe_u32x4 wraw[STAGES][NW][2];
+    moe_u32x4 wraw[STAGES][NW][NLD];
     auto load_w = [&](int st, int i) {
-        const int k = (ks0 + (i + rot) % nk) * 64;
+        const int k = (ks0 + ((i + rot) % nseg) * SEGK) * 64;
 #pragma unroll
         for (int nw = 0; nw < NW; ++nw) {
             if (tile_ok[nw % NT]) {
-                wraw[st][nw][0] = load_nt(wld[nw] + k);
-                wraw[st][nw][1] = load_nt(wld[nw] + (size_t)8 * K + k);
+#pragma unroll
+                for (int j = 0; j < NLD; ++j)
+                    wraw[st][nw][j] = load_nt(wld[nw] + (size_t)(RPI * j) * K + k);
             }
         }
     };
@@ -179,14 +201,14 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_ws_gemm(GemmProblem g)
     // loads (sorted ids or scan -> route -> token row) then overlap the weight latency.
 #pragma unroll
     for (int st = 0; st < STAGES - 1; ++st)
-        if (st < nk)
+        if (st < nseg)
             load_w(st, st);
 
     for (int pass0 = 0; pass0 < n_rows; pass0 += ROWS) {
         if (pass0 > 0) {
 #pragma unroll
             for (int st = 0; st < STAGES - 1; ++st)
-                if (st < nk)
+                if (st < nseg)
                     load_w(st, st);
         }
         // ---- row plan: activation row and output row of slot lane%16 of each m-tile
@@ -226,14 +248,17 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_ws_gemm(GemmProblem g)
             for (int nw = 0; nw < NW; ++nw)
                 acc[mt][nw] = moe_f32x4{0.f, 0.f, 0.f, 0.f};
 
-        moe_u32x4 xv[STAGES][MT][2];
+        moe_u32x4 xv[STAGES][SEGK][MT][2];
         auto load_x = [&](int st, int i) {
-            const int k = (ks0 + (i + rot) % nk) * 64;
+            const int k0 = (ks0 + ((i + rot) % nseg) * SEGK) * 64;
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                if (mt < mt_active) {
-                    xv[st][mt][0] = load_cached(arow[mt] + k);
-                    xv[st][mt][1] = load_cached(arow[mt] + k + 32);
+            for (int h = 0; h < SEGK; ++h) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    if (mt < mt_active) {
+                        xv[st][h][mt][0] = load_cached(arow[mt] + k0 + 64 * h);
+                        xv[st][h][mt][1] = load_cached(arow[mt] + k0 + 64 * h + 32);
+                    }
                 }
             }
         };
@@ -241,40 +266,44 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_ws_gemm(GemmProblem g)
 #pragma unroll
             for (int nw = 0; nw < NW; ++nw) {
                 if (tile_ok[nw % NT]) {
-                    tbuf[nw * 128 + wslot0] = wraw[st][nw][0];
-                    tbuf[nw * 128 + wslot1] = wraw[st][nw][1];
+#pragma unroll
+                    for (int j = 0; j < NLD; ++j)
+                        tbuf[nw * TS + wslot[j]] = wraw[st][nw][j];
                 }
             }
             moe_wave_sync();
 #pragma unroll
-            for (int nw = 0; nw < NW; ++nw) {
-                if (!tile_ok[nw % NT])
-                    continue;
-                const moe_u32x4 a0 = tbuf[nw * 128 + rslot0];
-                const moe_u32x4 a1 = tbuf[nw * 128 + rslot1];
+            for (int h = 0; h < SEGK; ++h) {
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    if (mt < mt_active) {
-                        acc[mt][nw] = moe_mma16<DT>(a0, xv[st][mt][0], acc[mt][nw]);
-                        acc[mt][nw] = moe_mma16<DT>(a1, xv[st][mt][1], acc[mt][nw]);
+                for (int nw = 0; nw < NW; ++nw) {
+                    if (!tile_ok[nw % NT])
+                        continue;
+                    const moe_u32x4 a0 = tbuf[nw * TS + rslot0[h]];
+                    const moe_u32x4 a1 = tbuf[nw * TS + rslot1[h]];
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) {
+                        if (mt < mt_active) {
+                            acc[mt][nw] = moe_mma16<DT>(a0, xv[st][h][mt][0], acc[mt][nw]);
+                            acc[mt][nw] = moe_mma16<DT>(a1, xv[st][h][mt][1], acc[mt][nw]);
+                        }
                     }
                 }
             }
             moe_wave_sync();
         };
 
-        // software pipeline: STAGES-1 k-steps in flight (their weights already requested)
+        // software pipeline: STAGES-1 segments in flight (their weights already requested)
 #pragma unroll
         for (int st = 0; st < STAGES - 1; ++st)
-            if (st < nk)
+            if (st < nseg)
                 load_x(st, st);
-        for (int i = 0; i < nk; i += STAGES) {
+        for (int i = 0; i < nseg; i += STAGES) {
 #pragma unroll
             for (int st = 0; st < STAGES; ++st) {
                 const int cur = i + st;
-                if (cur < nk) {
+                if (cur < nseg) {
                     const int nxt = cur + STAGES - 1;
-                    if (nxt < nk) {
+                    if (nxt < nseg) {
                         load_w((st + STAGES - 1) % STAGES, nxt);
                         load_x((st + STAGES - 1) % STAGES, nxt);
                     }
@@ -337,6 +366,15 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_ws_gemm(GemmProblem g)
             }
         }
     }
+}
+
+template <bool GATE_UP, int SRC, int NT, int MT, int KSPLIT, int STAGES, int DT, int SEGK = 1>
+__global__ __launch_bounds__(64 * KSPLIT)
+__attribute__((amdgpu_waves_per_eu(SEGK == 2 ? 3 : 1))) void k_ws_gemm(GemmProblem g)
+{
+    constexpr int NW = GATE_UP ? 2 * NT : NT;
+    __shared__ moe_u32x4 s_mem[WsSmem<NW, MT, KSPLIT, SEGK>::kSlots];
+    ws_body<GATE_UP, SRC, NT, MT, KSPLIT, STAGES, DT, SEGK>(g, blockIdx.x, blockIdx.y, s_mem);
 }
 
 }  // namespace moe_ws

@@ -69,6 +69,17 @@ def test_decode_token_sweep(T):
         _check_pass(c, d, p, what="T=%d %s" % (T, p))
 
 
+@pytest.mark.parametrize("T", [24, 100])
+def test_qwen3_235b_dims_decode(T):
+    """8 KB gate-up weight rows on the weight-streaming kernel (two-k-step row segments): the
+    direct path (24 tokens) and the sorted path at ~6 rows per expert (100 tokens)."""
+    cfg = replace(CONFIGS["qwen3-235b-batch"], T=T)
+    d = make_inputs(cfg, DEV, seed=300 + T, num_tokens=T)
+    paths = ["sorted"] + (["direct"] if T * cfg.k <= moe.DIRECT_MAX_ROUTES else [])
+    for p in paths:
+        _check_pass(cfg, d, p, sample_tokens(T, 10), "qwen3-235b dims T=%d %s" % (T, p))
+
+
 def test_qwen3_235b_batch_sampled():
     cfg = CONFIGS["qwen3-235b-batch"]
     d = make_inputs(cfg, DEV)

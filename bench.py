@@ -781,8 +781,9 @@ def summarize_trace(args):
         lines.append("| `%s` | %s | %.2f | %.2f | %.2f |" % (
             short, r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
             float(r["MaxNs"]) / 1e3))
-    lines += ["", "Template arguments: k_ws_gemm<GATE_UP, SRC, NT, MT, KSPLIT, STAGES, DT> (SRC 0 "
-              "sorted, 1 direct, 2 dense, 3 scan; DT 0 bf16, 1 f16); k_tiled_gemm<GATE_UP, SRC, "
+    lines += ["", "Template arguments: k_ws_gemm<GATE_UP, SRC, NT, MT, KSPLIT, STAGES, DT, SEGK> "
+              "(SRC 0 sorted, 1 direct, 2 dense, 3 scan; DT 0 bf16, 1 f16; SEGK k-steps per weight "
+              "load segment, STAGES counting segments); k_tiled_gemm<GATE_UP, SRC, "
               "BM, NTW, STAGES, DT>; k_block_gemm<GATE_UP, SRC, TN, STAGES, DT>; "
               "k_wide_gemm<GATE_UP, SRC, WS, DT> (WS weight stages); k_wide_reduce<GATE_UP, DT> (sum "
               "of the K-split dense tiles' parts); k_combine<DT>."]

@@ -33,6 +33,7 @@ bool dispatch(const GemmProblem &g, moe::WsTile t, hipStream_t s)
     }
     MOE_TILED_CASE(64, 1, 3)
     MOE_TILED_CASE(64, 2, 3)
+    MOE_TILED_CASE(64, 2, 2)
     MOE_TILED_CASE(128, 1, 2)
     MOE_TILED_CASE(128, 2, 2)
 #undef MOE_TILED_CASE

@@ -342,10 +342,17 @@ __global__ __launch_bounds__(64 * kWaves) void k_fp8_gemm(Fp8Problem p, int n_bl
 // transpose -- with non-temporal loads STAGES-1 k-steps ahead, and its activation row likewise
 // into B; a wave's two load instructions cover the tile's 16 whole lines.  Scales and
 // accumulation as k_fp8_gemm.
-template <int NT, int KSPLIT, int STAGES>
-__global__ __launch_bounds__(64 * KSPLIT) void k_fp8_ws(Fp8Problem p)
+// SEG = 2 (weight rows a multiple of 2 KB apart): a load instruction reads 4 rows x 256 bytes
+// (two k-steps) instead, the layout that streams fastest on such strides, and a per-wave
+// XOR-swizzled LDS transpose (16 rows x 16 chunks) hands the same A operand to the MFMA;
+// STAGES then counts two-k-step segments.  Every wave's K range must hold whole segments.
+template <int NT, int KSPLIT, int STAGES, int SEG = 1>
+__global__ __launch_bounds__(64 * KSPLIT)
+void k_fp8_ws(Fp8Problem p)
 {
+    static_assert(SEG == 1 || SEG == 2, "one- or two-k-step segments");
     __shared__ moe_f32x4 s_red[(KSPLIT > 1 ? KSPLIT - 1 : 1) * NT * 64];
+    __shared__ moe_u32x4 s_t[SEG > 1 ? KSPLIT * NT * 256 : 1];
     const int lane = threadIdx.x & 63;
     const int kw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int expert = blockIdx.y;
@@ -372,14 +379,32 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_fp8_ws(Fp8Problem p)
         const int c = col0 + 16 * nt;
         tile_ok[nt] = c < p.N;
         const int cc = tile_ok[nt] ? c : 0;
-        wrow[nt] = B + (size_t)(cc + rr) * K + 16 * rq;
+        wrow[nt] = SEG == 1 ? B + (size_t)(cc + rr) * K + 16 * rq
+                            : B + (size_t)(cc + (lane >> 4)) * K + 16 * (lane & 15);
         sb_base[nt] = (expert * p.NB + cc / 128) * KB;
     }
-    // K blocks of this wave, visited from a rotated start
+    // K blocks of this wave (nseg segments of SEG blocks), visited from a rotated start
     const int per = (KB + KSPLIT - 1) / KSPLIT;
     const int kb0 = kw * per;
     const int nk = max(0, min(KB, kb0 + per) - kb0);
-    const int rot = nk > 0 ? (int)((blockIdx.x * 7u + blockIdx.y * 13u) % (unsigned)nk) : 0;
+    const int nseg = nk / SEG;
+    const int rot =
+        nseg > 0 ? (int)((blockIdx.x * 7u + blockIdx.y * 13u) % (unsigned)nseg) : 0;
+    // SEG = 2 transpose buffer of this wave: row r keeps 16-byte chunk c in slot c ^ r; a lane
+    // of instruction j writes chunk lane%16 of row 4j + lane/16, and reads chunks 8h + rq and
+    // 8h + 4 + rq (bytes 16rq and 64 + 16rq of k-step h) of row rr
+    moe_u32x4 *tb = s_t + (SEG > 1 ? kw * NT * 256 : 0);
+    int wslot[2 * SEG], rslot[SEG][2];
+#pragma unroll
+    for (int j = 0; j < 2 * SEG; ++j) {
+        const int r = 4 * j + (lane >> 4);
+        wslot[j] = r * 16 + ((lane & 15) ^ r);
+    }
+#pragma unroll
+    for (int h = 0; h < SEG; ++h) {
+        rslot[h][0] = rr * 16 + ((8 * h + rq) ^ rr);
+        rslot[h][1] = rr * 16 + ((8 * h + 4 + rq) ^ rr);
+    }
 
     for (int pass0 = 0; pass0 < n_rows; pass0 += 16) {
         // B operand column lane%16: row pass0 + lane%16 of the expert's rows (past its rows:
@@ -394,48 +419,76 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_fp8_ws(Fp8Problem p)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
             acc[nt] = moe_f32x4{0.f, 0.f, 0.f, 0.f};
-        moe_u32x4 w[STAGES][NT][2], x[STAGES][2];
-        float sa[STAGES], sb[STAGES][NT];
+        moe_u32x4 w[STAGES][NT][2 * SEG], x[STAGES][SEG][2];
+        float sa[STAGES][SEG], sb[STAGES][SEG][NT];
         auto load = [&](int st, int i) {
-            const int kb = kb0 + (i + rot) % nk;
+            const int kb = kb0 + ((i + rot) % nseg) * SEG;  // first K block of segment i
             const int k = kb * 128;
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 if (tile_ok[nt]) {
-                    w[st][nt][0] = load_nt16(wrow[nt] + k);
-                    w[st][nt][1] = load_nt16(wrow[nt] + k + 64);
-                    sb[st][nt] = p.b_scale[sb_base[nt] + kb];
+                    if (SEG == 1) {
+                        w[st][nt][0] = load_nt16(wrow[nt] + k);
+                        w[st][nt][1] = load_nt16(wrow[nt] + k + 64);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 2 * SEG; ++j)
+                            w[st][nt][j] = load_nt16(wrow[nt] + (size_t)(4 * j) * K + k);
+                    }
+#pragma unroll
+                    for (int h = 0; h < SEG; ++h)
+                        sb[st][h][nt] = p.b_scale[sb_base[nt] + kb + h];
                 }
             }
-            x[st][0] = load16(arow + k);
-            x[st][1] = load16(arow + k + 64);
-            sa[st] = asc[kb];
-        };
-        auto compute = [&](int st) {
-            const moe_i32x8 bx = join(x[st][0], x[st][1]);
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                if (!tile_ok[nt])
-                    continue;
-                const moe_f32x4 part = mfma_fp8_block(join(w[st][nt][0], w[st][nt][1]), bx);
-                const float s = sa[st] * sb[st][nt];
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    acc[nt][q] = fmaf(part[q], s, acc[nt][q]);
+            for (int h = 0; h < SEG; ++h) {
+                x[st][h][0] = load16(arow + k + 128 * h);
+                x[st][h][1] = load16(arow + k + 128 * h + 64);
+                sa[st][h] = asc[kb + h];
             }
         };
-        // software pipeline: STAGES-1 k-steps in flight
+        auto compute = [&](int st) {
+            if (SEG > 1) {
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    if (tile_ok[nt])
+#pragma unroll
+                        for (int j = 0; j < 2 * SEG; ++j)
+                            tb[nt * 256 + wslot[j]] = w[st][nt][j];
+                moe_wave_sync();
+            }
+#pragma unroll
+            for (int h = 0; h < SEG; ++h) {
+                const moe_i32x8 bx = join(x[st][h][0], x[st][h][1]);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    if (!tile_ok[nt])
+                        continue;
+                    const moe_i32x8 a = SEG == 1 ? join(w[st][nt][0], w[st][nt][1])
+                                                 : join(tb[nt * 256 + rslot[h][0]],
+                                                        tb[nt * 256 + rslot[h][1]]);
+                    const moe_f32x4 part = mfma_fp8_block(a, bx);
+                    const float s = sa[st][h] * sb[st][h][nt];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        acc[nt][q] = fmaf(part[q], s, acc[nt][q]);
+                }
+            }
+            if (SEG > 1)
+                moe_wave_sync();  // this wave's transpose reads finish before its next writes
+        };
+        // software pipeline: STAGES-1 segments in flight
 #pragma unroll
         for (int st = 0; st < STAGES - 1; ++st)
-            if (st < nk)
+            if (st < nseg)
                 load(st, st);
-        for (int i = 0; i < nk; i += STAGES) {
+        for (int i = 0; i < nseg; i += STAGES) {
 #pragma unroll
             for (int st = 0; st < STAGES; ++st) {
                 const int cur = i + st;
-                if (cur < nk) {
+                if (cur < nseg) {
                     const int nxt = cur + STAGES - 1;
-                    if (nxt < nk)
+                    if (nxt < nseg)
                         load((st + STAGES - 1) % STAGES, nxt);
                     compute(st);
                 }

@@ -42,7 +42,11 @@ void launch_fp8_wide(const moe_fp8::Fp8Problem &p, int m_tiles, hipStream_t stre
 void launch_fp8_ws(const moe_fp8::Fp8Problem &p, hipStream_t stream)
 {
     const dim3 grid((p.N + 31) / 32, p.E);
-    if (p.KB >= 16)
+    // weight rows a multiple of 2 KB apart: 4 rows x 256 bytes per load (whole segments per wave)
+    const bool seg2 = p.K % 2048 == 0 && p.KB % 8 == 0;
+    if (p.KB >= 16 && seg2)
+        hipLaunchKernelGGL((moe_fp8::k_fp8_ws<2, 4, 2, 2>), grid, dim3(64 * 4), 0, stream, p);
+    else if (p.KB >= 16)
         hipLaunchKernelGGL((moe_fp8::k_fp8_ws<2, 4, 3>), grid, dim3(64 * 4), 0, stream, p);
     else
         hipLaunchKernelGGL((moe_fp8::k_fp8_ws<2, 2, 3>), grid, dim3(64 * 2), 0, stream, p);

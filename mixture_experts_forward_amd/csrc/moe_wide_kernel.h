@@ -443,8 +443,11 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
             const int dst = SRC == moe::ROWS_SORTED
                                 ? (GATE_UP ? row0 + r : g.sorted_ids[row0 + r])
                                 : row0 + r;
-            *reinterpret_cast<moe_u32x4 *>(g.out + (size_t)dst * g.n_out + col) =
-                *reinterpret_cast<const moe_u32x4 *>(otile + 8 * opos(r, oc));
+            // output rows are read once, by a later launch: non-temporal, so they do not evict
+            // the operands this launch's other tiles still share through L2
+            __builtin_nontemporal_store(
+                *reinterpret_cast<const moe_u32x4 *>(otile + 8 * opos(r, oc)),
+                reinterpret_cast<moe_u32x4 *>(g.out + (size_t)dst * g.n_out + col));
         }
     }
 }

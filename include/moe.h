@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 /* status codes */
 enum {
@@ -146,11 +146,26 @@ int moe_route(const float *gating_output, const float *correction_bias, const mo
  *                     tile, -1 past the last tile.
  *   inverse_pos       [T*k] int32, device, written: row of route r, -1 for skipped routes.
  *   n_tiles           [1] int32, device, written: number of tiles (expert_offsets[E]/block_m).
+ *   workspace         device scratch of at least moe_align_sort_workspace_bytes(T, k, E,
+ *                     block_m) bytes, 4-byte aligned, owned by the caller; contents on entry
+ *                     are ignored and on return unspecified (the sort/workspace buffers that
+ *                     the FlashInfer BF16-activation MoE PR preallocates).  May be NULL when
+ *                     that size is 0.
+ * Up to 1024 routes one workgroup does everything; above that the workspace holds a
+ * chunks x E table of per-chunk expert counts (chunks of 1024 routes) and the sort runs as
+ * three launches: per-chunk histograms, one workgroup for the padded layout, then every
+ * chunk's stable scatter at once.  The outputs are the same either way.
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (T < 0, k < 1, E < 1), MOE_ERR_UNSUPPORTED
- * (E > 1024, block_m outside 1..1024, T*k >= 2^30), MOE_ERR_LAUNCH. */
+ * (E > 1024, block_m outside 1..1024, T*k >= 2^30, a misaligned workspace),
+ * MOE_ERR_WORKSPACE (workspace_bytes below the size query), MOE_ERR_LAUNCH. */
 int moe_align_sort(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E, int32_t block_m,
                    int32_t *sorted_route_ids, int32_t *expert_offsets, int32_t *tile_expert,
-                   int32_t *inverse_pos, int32_t *n_tiles, void *stream);
+                   int32_t *inverse_pos, int32_t *n_tiles, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace moe_align_sort needs for T*k routes and E experts: 0 up to 1024 routes,
+ * else 4 * ceil(T*k / 1024) * E.  Returns 0 for arguments moe_align_sort would reject. */
+size_t moe_align_sort_workspace_bytes(int32_t T, int32_t k, int32_t E, int32_t block_m);
 
 /* ---------------------------------------------------------------------------------------
  * Workspace of the fused entry points: device memory the caller allocates (256-byte aligned)

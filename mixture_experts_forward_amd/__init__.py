@@ -8,7 +8,8 @@ the library is missing, importing a function raises instead of falling back to a
 
 Entry points (same names as the C ABI):
   moe_route(gating_output, top_k, ...)                        -> (topk_ids, topk_weights)
-  moe_align_sort(topk_ids, num_experts, block_m)              -> dict of int32 tensors
+  moe_align_sort(topk_ids, num_experts, block_m[, workspace]) -> dict of int32 tensors
+  moe_align_sort_workspace_bytes(T, k, num_experts, block_m) -> bytes
   fused_moe_fwd(hidden_states, gating_output, w_gate_up, w_down, top_k, ...) -> out
   fused_moe_shared_fwd(..., shared_w_gate_up, shared_w_down)  -> out
   fused_moe_experts_fwd(hidden_states, w_gate_up, w_down, topk_ids, topk_weights) -> out
@@ -63,7 +64,9 @@ SIGNATURES = {
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_check_params": (ctypes.c_int, [_P, ctypes.c_int, _I32]),
     "moe_route": (ctypes.c_int, [_P, _P, _P, _P, _P, _P]),
-    "moe_align_sort": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P]),
+    "moe_align_sort": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ,
+                                      _P]),
+    "moe_align_sort_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
     "fused_moe_workspace_bytes": (_SZ, [_P, _I32]),
     "fused_moe_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "fused_moe_mxfp4_workspace_bytes": (_SZ, [_P]),
@@ -193,7 +196,9 @@ def moe_route(gating_output, top_k, correction_bias=None, scoring="softmax", ren
     return ids, w
 
 
-def moe_align_sort(topk_ids, num_experts, block_m):
+def moe_align_sort(topk_ids, num_experts, block_m, workspace=None):
+    """Sorted layout of the routes (dict of int32 tensors).  workspace: a uint8 device tensor of
+    at least moe_align_sort_workspace_bytes bytes, or None to allocate one."""
     T, k = topk_ids.shape
     dev = topk_ids.device
     _check(topk_ids, "topk_ids", torch.int32, (T, k))
@@ -206,14 +211,23 @@ def moe_align_sort(topk_ids, num_experts, block_m):
         "inverse_pos": torch.empty(P, dtype=torch.int32, device=dev),
         "n_tiles": torch.empty(1, dtype=torch.int32, device=dev),
     }
+    need = lib().moe_align_sort_workspace_bytes(T, k, E, int(block_m))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     with torch.cuda.device(dev):
         st = lib().moe_align_sort(_ptr(topk_ids), T, k, E, int(block_m),
                                   _ptr(out["sorted_route_ids"]), _ptr(out["expert_offsets"]),
                                   _ptr(out["tile_expert"]), _ptr(out["inverse_pos"]),
-                                  _ptr(out["n_tiles"]), _stream(dev))
+                                  _ptr(out["n_tiles"]), _ptr(workspace), workspace.numel(),
+                                  _stream(dev))
     if st != MOE_OK:
         raise MoEError(st, "moe_align_sort")
     return out
+
+
+def moe_align_sort_workspace_bytes(T, k, num_experts, block_m):
+    return int(lib().moe_align_sort_workspace_bytes(int(T), int(k), int(num_experts),
+                                                    int(block_m)))
 
 
 def _fused(hidden_states, gating_output, w_gate_up, w_down, top_k, correction_bias, scoring,

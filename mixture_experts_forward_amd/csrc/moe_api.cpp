@@ -110,8 +110,6 @@ bool launch_gemm(bool gate_up, const moe::GemmProblem &g, moe::RowSource src,
 {
     if (t.kind == moe::KERNEL_TILED)
         return moe::launch_tiled(gate_up, g, src, ws_tile(t), stream);
-    if (t.kind == moe::KERNEL_BLOCK)
-        return moe::launch_block(gate_up, g, src, ws_tile(t), stream);
     if (t.kind == moe::KERNEL_WIDE)
         return moe::launch_wide(gate_up, g, src, stream);
     if (t.kind == moe::KERNEL_MX)
@@ -292,21 +290,52 @@ int moe_route(const float *gating_output, const float *correction_bias, const mo
     return launch_status();
 }
 
-int moe_align_sort(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E, int32_t block_m,
-                   int32_t *sorted_route_ids, int32_t *expert_offsets, int32_t *tile_expert,
-                   int32_t *inverse_pos, int32_t *n_tiles, void *stream)
+namespace {
+
+// moe_align_sort's argument checks shared with its workspace query
+int align_args(int32_t T, int32_t k, int32_t E, int32_t block_m)
 {
     if (T < 0 || k < 1 || E < 1)
         return MOE_ERR_SHAPE;
     if (E > moe::kMaxExperts || block_m < 1 || block_m > 1024 || (int64_t)T * k >= (1ll << 30))
         return MOE_ERR_UNSUPPORTED;
+    if (((int64_t)T * k + (int64_t)E * (block_m - 1)) >= (1ll << 31))
+        return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+}  // namespace
+
+size_t moe_align_sort_workspace_bytes(int32_t T, int32_t k, int32_t E, int32_t block_m)
+{
+    if (align_args(T, k, E, block_m) != MOE_OK)
+        return 0;
+    return moe::align_scratch_ints(T * k, E) * 4;
+}
+
+int moe_align_sort(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E, int32_t block_m,
+                   int32_t *sorted_route_ids, int32_t *expert_offsets, int32_t *tile_expert,
+                   int32_t *inverse_pos, int32_t *n_tiles, void *workspace,
+                   size_t workspace_bytes, void *stream)
+{
+    int st = align_args(T, k, E, block_m);
+    if (st != MOE_OK)
+        return st;
     if (!sorted_route_ids || !expert_offsets || !tile_expert || !n_tiles ||
         (T > 0 && (!topk_ids || !inverse_pos)))
         return MOE_ERR_NULL;
-    if (((int64_t)T * k + (int64_t)E * (block_m - 1)) >= (1ll << 31))
-        return MOE_ERR_UNSUPPORTED;
+    const size_t need = moe::align_scratch_ints(T * k, E) * 4;
+    if (need > 0) {
+        if (workspace_bytes < need)
+            return MOE_ERR_WORKSPACE;
+        if (!workspace)
+            return MOE_ERR_NULL;
+        if (((uintptr_t)workspace & 3u) != 0)
+            return MOE_ERR_UNSUPPORTED;
+    }
     moe::launch_align_sort(topk_ids, T * k, E, block_m, sorted_route_ids, expert_offsets,
-                           tile_expert, inverse_pos, n_tiles, nullptr,
+                           tile_expert, inverse_pos, n_tiles,
+                           need > 0 ? static_cast<int32_t *>(workspace) : nullptr,
                            static_cast<hipStream_t>(stream));
     return launch_status();
 }

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert moe.lib().moe_abi_version() == 2
+    assert moe.lib().moe_abi_version() == 3
     for s in (0, -1, -2, -3, -4, -5):
         assert moe.status_string(s) and moe.status_string(s) != "unknown status"
     assert moe.status_string(7) == "unknown status"
@@ -85,9 +85,9 @@ def test_workspace_bytes():
     s = moe.workspace_bytes(moe.make_params(32, 2048, 128, 768, 8, path="sorted"))
     slots = P + 128 * 15
     assert s >= slots * 768 * 2 + P * 2048 * 2 and s > n
-    # prefill: 128-row tiles
+    # prefill: 256-row tiles
     q = moe.workspace_bytes(moe.make_params(4096, 7168, 256, 2048, 8))
-    assert q >= (32768 + 256 * 127) * 2048 * 2 + 32768 * 7168 * 2
+    assert q >= (32768 + 256 * 255) * 2048 * 2 + 32768 * 7168 * 2
 
 
 def test_entry_points_reject_before_launch():
@@ -121,10 +121,31 @@ def test_entry_points_reject_before_launch():
     assert L.moe_route(fake, None, None, fake, fake, None) == -1
     assert L.moe_route(fake, fake, ctypes.byref(p), fake, fake, None) == -3
     assert L.moe_route(None, None, ctypes.byref(p), fake, fake, None) == -1
-    assert L.moe_align_sort(fake, 4, 2, 0, 16, fake, fake, fake, fake, fake, None) == -2
-    assert L.moe_align_sort(fake, 4, 2, 2048, 16, fake, fake, fake, fake, fake, None) == -3
-    assert L.moe_align_sort(fake, 4, 2, 8, 0, fake, fake, fake, fake, fake, None) == -3
-    assert L.moe_align_sort(None, 4, 2, 8, 16, fake, fake, fake, fake, fake, None) == -1
+    assert L.moe_align_sort(fake, 4, 2, 0, 16, fake, fake, fake, fake, fake, None, 0,
+                            None) == -2
+    assert L.moe_align_sort(fake, 4, 2, 2048, 16, fake, fake, fake, fake, fake, None, 0,
+                            None) == -3
+    assert L.moe_align_sort(fake, 4, 2, 8, 0, fake, fake, fake, fake, fake, None, 0, None) == -3
+    assert L.moe_align_sort(None, 4, 2, 8, 16, fake, fake, fake, fake, fake, None, 0,
+                            None) == -1
+
+
+def test_align_sort_workspace_checks():
+    """The align workspace: 0 bytes up to 1024 routes, a chunks x E count table above; a short
+    or missing workspace is rejected before anything is launched."""
+    L = moe.lib()
+    fake = ctypes.c_void_p(1 << 20)   # aligned, never dereferenced: checks come first
+    q = L.moe_align_sort_workspace_bytes
+    assert q(128, 8, 128, 16) == 0                      # 1024 routes: one workgroup
+    assert q(129, 8, 128, 16) == 2 * 128 * 4            # 1032 routes: two chunks
+    assert q(4096, 8, 256, 256) == 32 * 256 * 4         # DeepSeek-V3 prefill: 32 chunks
+    assert q(4096, 8, 0, 16) == 0 and q(4, 2, 8, 0) == 0 and q(-1, 2, 8, 16) == 0
+    need = q(4096, 8, 256, 256)
+    args = (fake, 4096, 8, 256, 256, fake, fake, fake, fake, fake)
+    assert L.moe_align_sort(*args, fake, need - 4, None) == -4        # too small
+    assert L.moe_align_sort(*args, None, 0, None) == -4               # none given
+    assert L.moe_align_sort(*args, None, need, None) == -1            # size without a buffer
+    assert L.moe_align_sort(*args, ctypes.c_void_p((1 << 20) + 2), need, None) == -3
 
 
 def test_binding_rejects_cpu_tensors():

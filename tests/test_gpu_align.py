@@ -28,6 +28,8 @@ def _ids(T, k, E, seed, pad=0.0, repeats=False, skew=False):
     (32, 8, 128, 16, 0.0, False, False),
     (512, 8, 128, 16, 0.0, False, False),
     (4096, 8, 256, 128, 0.0, False, False),
+    (4096, 8, 256, 256, 0.0, False, True),  # DeepSeek-V3 prefill size, chunked, skewed
+    (1025, 1, 16, 16, 0.0, False, False),    # two chunks, the second holding one route
     (4096, 8, 256, 16, 0.05, False, False),
     (512, 8, 384, 16, 0.0, False, False),
     (1000, 6, 1024, 1, 0.1, True, False),
@@ -59,9 +61,24 @@ def test_align_sort_overwrites_poisoned_outputs():
         moe._ptr(ids_dev), 64, 8, 32, 16,
         moe._ptr(got["sorted_route_ids"]), moe._ptr(got["expert_offsets"]),
         moe._ptr(got["tile_expert"]), moe._ptr(got["inverse_pos"]), moe._ptr(got["n_tiles"]),
-        moe._stream(torch.device(DEV)))
+        None, 0, moe._stream(torch.device(DEV)))
     assert st == 0
     torch.cuda.synchronize()
     ref = oracle.align_sort(ids, 32, 16)
     for key in ("sorted_route_ids", "expert_offsets", "tile_expert", "inverse_pos"):
         assert np.array_equal(got[key].cpu().numpy(), ref[key]), key
+
+
+def test_align_sort_chunked_poisoned_workspace():
+    """32768 routes through the public call with a workspace that holds stale values: the
+    chunked form writes every count it reads, and every output matches the oracle."""
+    ids = _ids(4096, 8, 256, seed=11, pad=0.02)
+    need = moe.moe_align_sort_workspace_bytes(4096, 8, 256, 256)
+    ws = torch.full((need // 4,), 0x3c3c3c3c, dtype=torch.int32, device=DEV).view(torch.uint8)
+    ref = oracle.align_sort(ids, 256, 256)
+    for _ in range(2):
+        got = moe.moe_align_sort(torch.from_numpy(ids).to(DEV), 256, 256, workspace=ws)
+        torch.cuda.synchronize()
+        for key in ("sorted_route_ids", "expert_offsets", "tile_expert", "inverse_pos"):
+            assert np.array_equal(got[key].cpu().numpy(), ref[key]), key
+        assert int(got["n_tiles"].item()) == ref["n_tiles"]

@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(os.path.dirname(HERE), "_build", "moe")
 LIB = os.path.join(HERE, "libmoe_mi355x.so")
 SOURCES = ["moe_plan.cpp", "moe_api.cpp", "moe_route.hip", "moe_align.hip", "moe_gemm_ws.hip",
-           "moe_gemm_tiled.hip", "moe_gemm_block.hip",
+           "moe_gemm_tiled.hip",
            "moe_gemm_wide.hip", "moe_combine.hip", "moe_masked.hip",
            "moe_gemm_fp8.hip", "moe_quant.hip", "moe_gemm_mx.hip", "moe_stream_read.hip"]
 ARCH = "gfx950"

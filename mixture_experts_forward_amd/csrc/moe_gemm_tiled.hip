@@ -34,8 +34,6 @@ bool dispatch(const GemmProblem &g, moe::WsTile t, hipStream_t s)
     MOE_TILED_CASE(64, 1, 3)
     MOE_TILED_CASE(64, 2, 3)
     MOE_TILED_CASE(64, 2, 2)
-    MOE_TILED_CASE(128, 1, 2)
-    MOE_TILED_CASE(128, 2, 2)
 #undef MOE_TILED_CASE
     return false;
 }
@@ -47,13 +45,10 @@ namespace moe {
 bool launch_tiled(bool gate_up, const GemmProblem &g, RowSource src, WsTile tile,
                   hipStream_t stream)
 {
-    if (src == ROWS_DIRECT)
+    if (src != ROWS_SORTED)
         return false;
-    if (gate_up)
-        return src == ROWS_SORTED ? dispatch<true, ROWS_SORTED>(g, tile, stream)
-                                  : dispatch<true, ROWS_DENSE>(g, tile, stream);
-    return src == ROWS_SORTED ? dispatch<false, ROWS_SORTED>(g, tile, stream)
-                              : dispatch<false, ROWS_DENSE>(g, tile, stream);
+    return gate_up ? dispatch<true, ROWS_SORTED>(g, tile, stream)
+                   : dispatch<false, ROWS_SORTED>(g, tile, stream);
 }
 
 }  // namespace moe

@@ -67,7 +67,7 @@ static bool launch_any(bool gate_up, const GemmProblem &g, RowSource src, WsTile
         case ROWS_SCAN:
             return dispatch<true, ROWS_SCAN>(g, tile, stream);
         default:
-            return dispatch<true, ROWS_DENSE>(g, tile, stream);
+            return false;
         }
     }
     switch (src) {
@@ -78,7 +78,7 @@ static bool launch_any(bool gate_up, const GemmProblem &g, RowSource src, WsTile
     case ROWS_SCAN:
         return dispatch<false, ROWS_SCAN>(g, tile, stream);
     default:
-        return dispatch<false, ROWS_DENSE>(g, tile, stream);
+        return false;
     }
 }
 

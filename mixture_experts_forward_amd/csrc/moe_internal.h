@@ -80,7 +80,6 @@ constexpr size_t kWidePartialBytes = 256u * 256u * 4u;
 //   weight-streaming kernel: NT 16-column tiles per workgroup (per half for gate-up), MT 16-row
 //     tiles per pass, KSPLIT waves splitting the K loop;
 //   row-tiled kernel: NT 16-column tiles per wave (4 waves), 16*MT rows per tile (ksplit unused);
-//   block kernel: NT 16-row weight tiles per wave (2 x 2 waves), 128 rows per tile (MT = 8);
 //   both: STAGES register buffers (STAGES-1 k-steps of 64 in flight per wave).
 struct WsTile {
     int nt, mt, ksplit, stages;
@@ -89,12 +88,8 @@ struct WsTile {
 // false: no kernel is instantiated for this tile shape (nothing launched)
 bool launch_gate_up(const GemmProblem &g, RowSource src, WsTile tile, hipStream_t stream);
 bool launch_down(const GemmProblem &g, RowSource src, WsTile tile, hipStream_t stream);
-// Row-tiled kernel (ROWS_SORTED with block_m = 16*tile.mt, or ROWS_DENSE).
+// Row-tiled kernel (ROWS_SORTED with block_m = 16*tile.mt).
 bool launch_tiled(bool gate_up, const GemmProblem &g, RowSource src, WsTile tile,
-                  hipStream_t stream);
-// 128-row block kernel (ROWS_SORTED with block_m = 128, or ROWS_DENSE); tile.nt = TN 16-row
-// weight tiles per wave (2 x 2 waves), tile.stages register buffers.
-bool launch_block(bool gate_up, const GemmProblem &g, RowSource src, WsTile tile,
                   hipStream_t stream);
 // 256 x 256 tile kernel (ROWS_SORTED with block_m = 256, or ROWS_DENSE with 256-row tiles).
 bool launch_wide(bool gate_up, const GemmProblem &g, RowSource src, hipStream_t stream);

@@ -83,8 +83,8 @@ void make_plan(const moe_params_t *p, int32_t S, Plan *pl, int wfmt)
     // two for down, K split over four waves, 16-row passes.  Tens of rows (batch): the
     // row-tiled kernel, activation tile shared through LDS, 64-row tiles.  Hundreds (prefill):
     // the 256 x 256 tile kernel, both operands loaded straight into LDS.  The dense shared
-    // expert: the 256 x 256 tile kernel for gate-up, the 128-row block kernel for down (whose
-    // few, long-K tiles fill the GPU better at 128 x 128).
+    // expert: the 256 x 256 tile kernel for both GEMMs, the tiles past the last whole round
+    // over the CUs split along K.
     if (pl->path == MOE_PATH_DIRECT) {
         pl->gate_up = {KERNEL_WS, 1, 1, 4, 3};
         pl->down = {KERNEL_WS, 2, 1, P <= 64 ? 4 : 2, P <= 64 ? 2 : 3};

@@ -149,7 +149,9 @@ __device__ __forceinline__ int wide_total(const GemmProblem &g, int n_blocks, in
     return m_tiles * n_blocks;
 }
 
-// Tile number t -> (column block, row tile, expert); see moe_block_kernel.h's block_decode.
+// Tile number t -> (column block, row tile, expert).  Sorted rows: tiles are numbered expert by
+// expert; within an expert, column block by column block with the expert's row tiles
+// innermost.  Dense rows: column block by column block, row tiles innermost.
 template <int SRC>
 __device__ __forceinline__ void wide_decode(const GemmProblem &g, int t, int n_blocks,
                                             int m_tiles, int &nblk, int &mtile, int &expert)

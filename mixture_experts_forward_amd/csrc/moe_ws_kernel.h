@@ -34,8 +34,8 @@
 // runs one workgroup per route, the first route of an expert gathers all routes of that expert
 // and later ones exit; ROWS_SCAN (T*k <= 512) runs one workgroup per expert, which finds its
 // routes by scanning topk_ids with wave ballots.  Either way an expert's weights are streamed
-// once however many tokens chose it, and rows are taken in route order.  ROWS_DENSE takes
-// every token (shared expert).
+// once however many tokens chose it, and rows are taken in route order.  (The dense shared
+// expert runs on the 256 x 256 tile kernel; no dense form of this kernel is instantiated.)
 #pragma once
 
 #include "moe_device.h"

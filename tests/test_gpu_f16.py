@@ -61,7 +61,7 @@ def test_f16_qwen3_235b_decode_sampled():
 
 def test_f16_wide_tiles_and_shared_expert():
     # hundreds of rows per expert (the 256 x 256 tile kernel) plus a shared expert (dense
-    # 256 x 256 gate-up, 128-row block down)
+    # 256 x 256 tiles for gate-up and down)
     cfg = replace(CONFIGS["kimi-k2-shared"], T=384, H=256, E=4, F=128, S=192, k=2)
     d = make_inputs(cfg, DEV, seed=7, dtype=F16)
     _check_pass(cfg, d, "sorted", sample_tokens(cfg.T, 48), "wide + shared f16")

@@ -5,8 +5,9 @@
 
 A step is one whole fused MoE forward (routing, align/sort, gate-up GEMM + SiLU*up, down GEMM,
 shared expert if the workload has one, weighted combine) over one batch of seeded synthetic
-inputs already resident in HBM.  The default workload is the Qwen3-30B-style decode layer
-(T=32 tokens, H=2048, E=128 experts, F=768, top-8 softmax routing).
+inputs already resident in HBM.  The default workload is the DeepSeek-V3-style grouped prefill
+(T=4096 tokens, H=7168, E=256 experts, F=2048, top-8 sigmoid routing with a correction bias,
+8 groups / top-4, routed scaling 2.5), the largest single-GPU workload.
 
 To keep the expert weights cold (the weights are what the pass streams), the inputs come in R
 rotating sets -- separate weights, hidden states and gating per set -- with R chosen so the
@@ -54,6 +55,11 @@ def parse():
     ap.add_argument("--rotate", type=int, default=0, help="input sets (0 = automatic)")
     ap.add_argument("--path", default="auto", choices=["auto", "direct", "sorted"],
                     help="the library's path choice (auto: its own rule)")
+    ap.add_argument("--skew", default=None, metavar="ALPHA|auto",
+                    help="skewed routing (aiter MI308 decoding PR, 'Skewed routing'): add "
+                         "-alpha*log(1+rank) to the router scores; 'auto' takes the alpha that "
+                         "gives the workload's most popular expert twice the mean load.  The "
+                         "line then also times the same pass on the unskewed scores")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -89,7 +95,8 @@ def main():
     import mixture_experts_forward_amd as moe
     from moe_harness import perfmodel
     from moe_harness.workloads import (BENCH_CONFIG, CONFIGS, FP8_CONFIGS, MASKED_CONFIGS,
-                                       make_fp8_weights, make_inputs, make_mxfp4_weights)
+                                       make_fp8_weights, make_inputs, make_mxfp4_weights,
+                                       skew_alpha, skew_gating)
 
     if args.config in MASKED_CONFIGS:
         bench_masked(args, MASKED_CONFIGS[args.config])
@@ -121,6 +128,13 @@ def main():
             sets.append(d)
     else:
         sets = [make_inputs(cfg, dev, seed=42 + i, dtype=tdt) for i in range(R)]
+    alpha = None
+    if args.skew is not None:
+        alpha = skew_alpha(cfg) if args.skew == "auto" else float(args.skew)
+        for d in sets:
+            d["gating_uniform"] = d["gating_output"]
+            d["gating_output"] = skew_gating(d["gating_output"], alpha)
+        log("skewed routing: alpha %.4f" % alpha)
     torch.cuda.synchronize()
     if args.copy_calibration:
         src = torch.ones(args.copy_calibration, dtype=torch.uint8, device=dev)
@@ -212,6 +226,27 @@ def main():
     fused_ms = e0.elapsed_time(e1) / args.steps
     log("fused: %.4f ms/step (device), %.4f ms/step (wall)" % (fused_ms,
                                                                  wall * 1e3 / args.steps))
+    skew_cmp = None
+    if alpha is not None:
+        # the same loop on the unskewed scores of the same input sets
+        for d in sets:
+            d["gating_output"], d["gating_uniform"] = d["gating_uniform"], d["gating_output"]
+        for i in range(args.warmup):
+            fused_step(i)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(args.steps):
+            fused_step(i)
+        e1.record()
+        torch.cuda.synchronize()
+        uniform_ms = e0.elapsed_time(e1) / args.steps
+        for d in sets:
+            d["gating_output"], d["gating_uniform"] = d["gating_uniform"], d["gating_output"]
+        skew_cmp = {"alpha": alpha, "skewed_ms": round(fused_ms, 5),
+                    "unskewed_ms": round(uniform_ms, 5),
+                    "skewed_over_unskewed": round(fused_ms / uniform_ms, 4)}
+        log("unskewed scores: %.4f ms/step; skewed / unskewed %.3f" % (uniform_ms,
+                                                                       fused_ms / uniform_ms))
 
     # ---- loop 2: staged calls with events between the stages
     for i in range(args.warmup):
@@ -358,7 +393,8 @@ def main():
         "ms_per_step": round(ms, 5),
         "higher_is_better": False,
         "scaling": "weak",
-        "vs_baseline": round(ms / base["ms"], 4) if base else None,
+        # the pages' figures come from other GPUs: context (baseline_context), not a target
+        "vs_baseline": None,
         "dtype": "fp8e4m3" if f8 else args.dtype,
         "data": "synthetic (seeded; %d rotating input sets)" % R,
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "F": cfg.F,
@@ -366,7 +402,7 @@ def main():
                    "num_expert_group": cfg.num_expert_group, "topk_group": cfg.topk_group,
                    "routed_scaling_factor": cfg.rsf, "correction_bias": cfg.bias,
                    "shared_inter": cfg.S, "path": args.path, "weights": args.weights,
-                   "parallelism": "single GPU"},
+                   "skew_alpha": alpha, "parallelism": "single GPU"},
         "achieved_tbps": round(pass_bytes / (ms * 1e-3) / 1e12, 4),
         "achieved_tflops": round(pass_flops / (ms * 1e-3) / 1e12, 3),
         "hbm_roofline_frac": round(pass_bytes / (ms * 1e-3) / perfmodel.HBM_PEAK_BYTES_PER_S, 4),
@@ -401,6 +437,8 @@ def main():
         "baseline_context": base,
         "context": ctx,
     }
+    if skew_cmp is not None:
+        line["skew"] = skew_cmp
     print(json.dumps(line), flush=True)
 
 

@@ -23,7 +23,9 @@ different streams, so a test draws once and hands the same bytes to both sides.
 from dataclasses import dataclass, replace
 from typing import Optional
 
+import json
 import math
+import os
 
 import torch
 
@@ -172,8 +174,9 @@ def make_fp8_inputs(cfg: Fp8Config, device="cpu", seed: int = 42) -> dict:
     }
 
 
-# the configuration the benchmark times by default: Qwen3-30B-style decode, 32 tokens
-BENCH_CONFIG = "qwen3-30b-decode"
+# the configuration the benchmark times by default: the DeepSeek-V3-style grouped prefill
+# (4096 tokens, 256 experts of 7168 x 2048), the largest of the single-GPU workloads
+BENCH_CONFIG = "ds-v3-grouped-prefill"
 
 
 def _gen(device, seed: int, stream: int) -> torch.Generator:
@@ -233,6 +236,41 @@ def make_inputs(cfg: MoEConfig, device="cpu", seed: int = 42, weights: bool = Tr
             d["shared_w_down"] = _normal((H, S), S ** -0.5, dtype, device, seed,
                                          STREAM_SHARED_DOWN)
     return d
+
+
+def skew_bias(E: int, alpha: float, seed: int = 42) -> torch.Tensor:
+    """Per-expert router-score bias of the skewed-routing workload (aiter MI308 decoding PR,
+    Performance, "Skewed routing"): -alpha * log(1 + rank[e]), the ranks a fixed seeded random
+    permutation of the experts (rank 0 the most popular).  float64 [E] on the host."""
+    g = _gen("cpu", seed, STREAM_SKEW)
+    rank = torch.empty(E, dtype=torch.float64)
+    rank[torch.randperm(E, generator=g)] = torch.arange(E, dtype=torch.float64)
+    return -float(alpha) * torch.log1p(rank)
+
+
+def skew_gating(gating: torch.Tensor, alpha: float, seed: int = 42) -> torch.Tensor:
+    """gating_output [T,E] f32 with the skew bias added to every token's scores (the sum in
+    float64, rounded to f32 once), on gating's device."""
+    if alpha == 0.0:
+        return gating.clone()
+    b = skew_bias(gating.shape[1], alpha, seed).to(gating.device)
+    return (gating.double() + b).to(torch.float32)
+
+
+SKEW_ALPHA_FILE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                               "tests", "golden", "skew_alpha.json")
+
+
+def skew_alpha(cfg: MoEConfig) -> float:
+    """The skew strength that gives cfg's routing a most popular expert at twice the mean load
+    (tests/golden/skew_alpha.json, written by tests/golden/skew_alpha.py with the oracle's
+    routing); 0 for routings already above that."""
+    with open(SKEW_ALPHA_FILE) as f:
+        table = json.load(f)
+    for entry in table.values():
+        if cfg.name in entry["workloads"]:
+            return float(entry["alpha"])
+    raise KeyError("no skew alpha recorded for workload %s" % cfg.name)
 
 
 def random_topk_ids(T: int, k: int, E: int, seed: int = 42, device="cpu",

@@ -95,3 +95,34 @@ def sample_tokens(T, n, seed=0):
     r = np.random.default_rng(seed)
     mid = r.choice(np.arange(1, T - 1), size=n - 2, replace=False)
     return np.sort(np.concatenate([[0, T - 1], mid]))
+
+
+def routing_tokens(ids, E, block_m, n=64, seed=0):
+    """At least n distinct tokens (if T allows) chosen from the realized routing ids [T,k] so
+    that the compared outputs cover the tiles the sorted path forms: tokens of the heaviest
+    expert's first route, its last route and up to 8 routes of its last (ragged) block_m-row
+    tile; an equal share of tokens from each eighth of the expert-sorted route order (the
+    tiles are numbered expert by expert, and the 8 XCDs take contiguous ranges of them); the
+    first and the last token; random tokens to make up n."""
+    ids = np.asarray(ids)
+    T, k = ids.shape
+    flat = ids.ravel()
+    routes = np.nonzero((flat >= 0) & (flat < E))[0]
+    rng = np.random.default_rng(seed)
+    pick = {0, T - 1}
+    if routes.size:
+        order = routes[np.argsort(flat[routes], kind="stable")]
+        counts = np.bincount(flat[routes], minlength=E)
+        heavy = routes[flat[routes] == int(np.argmax(counts))]     # route order
+        tail = heavy[(heavy.size - 1) // block_m * block_m:]
+        pick.update(int(r) // k for r in rng.choice(tail, size=min(8, tail.size), replace=False))
+        pick.update((int(heavy[0]) // k, int(heavy[-1]) // k))
+        per = max(1, (n - len(pick)) // 8)
+        for p in range(8):
+            seg = order[p * order.size // 8:(p + 1) * order.size // 8]
+            if seg.size:
+                pick.update(int(r) // k for r in rng.choice(seg, size=min(per, seg.size),
+                                                           replace=False))
+    while len(pick) < min(n, T):
+        pick.add(int(rng.integers(T)))
+    return np.array(sorted(pick))

@@ -14,7 +14,7 @@ import mixture_experts_forward_amd as moe
 import oracle
 from moe_harness.workloads import CONFIGS, make_inputs, random_topk_ids, random_topk_weights, to_u16
 from parity import (WEIGHT_ATOL, assert_output_close, oracle_experts_sampled, oracle_route,
-                    sample_tokens)
+                    routing_tokens, sample_tokens)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -33,12 +33,15 @@ def _fused(cfg, d, path="auto", **kw):
 
 
 def _check_pass(cfg, d, path, tokens=None, what=""):
+    """tokens: None (every token), an array, or a function of the realized routing ids."""
     out, ids, w = _fused(cfg, d, path)
     rid, rw = oracle_route(d, cfg)
     assert np.array_equal(ids, rid), "%s: routing ids differ" % what
     assert np.max(np.abs(w.astype(np.float64) - rw)) <= WEIGHT_ATOL
     if tokens is None:
         tokens = np.arange(cfg.T)
+    elif callable(tokens):
+        tokens = tokens(rid)
     _, ref = oracle_experts_sampled(d, rid, rw, tokens, with_shared=cfg.S > 0)
     rel = assert_output_close(out[torch.as_tensor(tokens, device=DEV)], ref, what)
     print("%s: rel-L2 %.2e" % (what, rel), flush=True)
@@ -80,17 +83,20 @@ def test_qwen3_235b_dims_decode(T):
         _check_pass(cfg, d, p, sample_tokens(T, 10), "qwen3-235b dims T=%d %s" % (T, p))
 
 
-def test_qwen3_235b_batch_sampled():
+def test_qwen3_235b_batch_all_tokens():
     cfg = CONFIGS["qwen3-235b-batch"]
     d = make_inputs(cfg, DEV)
-    _check_pass(cfg, d, "auto", sample_tokens(cfg.T, 12), cfg.name)
+    _check_pass(cfg, d, "auto", None, cfg.name)
 
 
 @pytest.mark.slow
 def test_ds_v3_grouped_prefill_sampled():
+    """The benchmark's launch configuration at full size: 64+ tokens chosen from the realized
+    routing (the heaviest expert's ragged last 256-row tile, every eighth of the sorted route
+    order, i.e. every XCD's tile range)."""
     cfg = CONFIGS["ds-v3-grouped-prefill"]
     d = make_inputs(cfg, DEV)
-    _check_pass(cfg, d, "auto", sample_tokens(cfg.T, 8), cfg.name)
+    _check_pass(cfg, d, "auto", lambda ids: routing_tokens(ids, cfg.E, 256, n=64), cfg.name)
     del d
     torch.cuda.empty_cache()
 
@@ -99,7 +105,7 @@ def test_ds_v3_grouped_prefill_sampled():
 def test_ds_v3_prefill_16k_sampled():
     cfg = CONFIGS["ds-v3-prefill-16k"]
     d = make_inputs(cfg, DEV)
-    _check_pass(cfg, d, "auto", sample_tokens(cfg.T, 8), cfg.name)
+    _check_pass(cfg, d, "auto", lambda ids: routing_tokens(ids, cfg.E, 256, n=32), cfg.name)
     del d
     torch.cuda.empty_cache()
 
@@ -108,7 +114,7 @@ def test_ds_v3_prefill_16k_sampled():
 def test_kimi_k2_shared_sampled():
     cfg = CONFIGS["kimi-k2-shared"]
     d = make_inputs(cfg, DEV)
-    _check_pass(cfg, d, "auto", sample_tokens(cfg.T, 8), cfg.name)
+    _check_pass(cfg, d, "auto", lambda ids: routing_tokens(ids, cfg.E, 64, n=96), cfg.name)
     del d
     torch.cuda.empty_cache()
 
@@ -121,8 +127,8 @@ def test_shared_expert_small(T, path):
 
 @pytest.mark.parametrize("T,E,k,H,F", [
     (37, 16, 4, 256, 128),    # ~9 rows per expert: 64-row tiles, ragged tiles and tail
-    (300, 8, 4, 128, 192),    # ~150 rows per expert: 128-row tiles, several per expert
-    (129, 4, 2, 192, 64),     # ~65 rows per expert: 128-row tiles, one partial
+    (300, 8, 4, 128, 192),    # ~150 rows per expert: 256 x 256 tiles, part-full row groups
+    (129, 4, 2, 192, 64),     # ~65 rows per expert: 256 x 256 tiles, F one partial column block
     (70, 16, 8, 320, 64),     # ~35 rows per expert: 64-row tiles, F a single column block
 ])
 def test_row_tiled_sizes(T, E, k, H, F):
@@ -132,7 +138,8 @@ def test_row_tiled_sizes(T, E, k, H, F):
 
 @pytest.mark.parametrize("T", [1, 31, 200])
 def test_shared_expert_rows(T):
-    """Dense shared-expert GEMMs over 1, a ragged 31 and 200 (two 128-row tiles) tokens."""
+    """Dense shared-expert GEMMs (256 x 256 tiles, K-split tail) over 1, a ragged 31 and 200
+    tokens."""
     cfg = replace(CONFIGS["kimi-k2-shared"], T=T, H=192, E=16, F=64, S=320, k=2)
     _check_pass(cfg, make_inputs(cfg, DEV, seed=T + 1), "auto", what="shared rows T=%d" % T)
 
@@ -178,8 +185,10 @@ def test_experts_given_routing_with_padding_and_repeats(T, path):
     (150, 128, 4, 128, 64, 1.2),   # 600 routes, ~5 per expert: weight-streaming, chunked align
 ])
 def test_skewed_routing_sorted(T, E, k, H, F, skew):
-    """Zipf-like routing (a few hot experts, a long tail of cold or unused ones) through the
-    sorted path, every token compared with the oracle."""
+    """Given Zipf-like routing ids (experts drawn with probability proportional to
+    (1 + rank)^-skew: a few very hot experts, a long tail of cold or unused ones) through the
+    sorted path, every token compared with the oracle.  This stresses hot experts harder than
+    the router-score skew of tests/test_gpu_skew.py."""
     cfg = replace(CONFIGS["tiny"], T=T, E=E, k=k, H=H, F=F)
     d = make_inputs(cfg, DEV, seed=T + E)
     ids = random_topk_ids(T, k, E, seed=5, skew=skew).to(DEV)

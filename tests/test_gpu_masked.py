@@ -12,8 +12,9 @@ import torch
 
 import mixture_experts_forward_amd as moe
 import oracle
-from moe_harness.workloads import CONFIGS, make_inputs, to_u16
-from parity import assert_output_close, oracle_route
+from moe_harness.workloads import (CONFIGS, MASKED_CONFIGS, make_inputs, make_masked_inputs,
+                                   to_u16)
+from parity import assert_output_close, oracle_experts_sampled, oracle_route, routing_tokens
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -102,3 +103,56 @@ def test_ep_shards_sum_to_unsharded_pass():
     torch.cuda.synchronize()
     rel = float(torch.linalg.norm(total - full.float()) / torch.linalg.norm(full.float()))
     assert rel < 2e-2, rel
+
+
+@pytest.mark.slow
+def test_ep8_shard_masked_real_shape():
+    """One EP8 shard of DeepSeek-V3 at its real shape (32 local experts, H 7168, F 2048, row
+    blocks of 128 with 64..128 rows in use; the benchmark's ds-v3-ep8-masked): every row of six
+    experts -- the fullest, the emptiest and four others -- against the oracle, and rows past
+    masked_m untouched."""
+    cfg = MASKED_CONFIGS["ds-v3-ep8-masked"]
+    d = make_masked_inputs(cfg, DEV)
+    out = torch.full((cfg.E, cfg.max_m, cfg.H), SENTINEL, dtype=torch.int16,
+                     device=DEV).view(torch.bfloat16)
+    moe.fused_moe_masked_fwd(d["a"], d["masked_m"], d["w_gate_up"], d["w_down"], out=out)
+    torch.cuda.synchronize()
+    counts = d["masked_m"].cpu().numpy()
+    r = np.random.default_rng(1)
+    pick = {int(np.argmax(counts)), int(np.argmin(counts))}
+    while len(pick) < 6:
+        pick.add(int(r.integers(cfg.E)))
+    pick = np.array(sorted(pick))
+    sel = torch.as_tensor(pick, device=DEV)
+    _, ref = oracle.masked_mlp(to_u16(d["a"].index_select(0, sel)), counts[pick],
+                               to_u16(d["w_gate_up"].index_select(0, sel)),
+                               to_u16(d["w_down"].index_select(0, sel)))
+    got = out.index_select(0, sel)
+    used = np.arange(cfg.max_m)[None, :] < counts[pick][:, None]
+    assert np.all(to_u16(got)[~used] == SENTINEL), "a row past masked_m was written"
+    rel = assert_output_close(got[torch.from_numpy(used).to(DEV)], ref[used], "ep8 masked")
+    print("ep8 masked experts %s: rel-L2 %.2e" % (pick.tolist(), rel), flush=True)
+
+
+@pytest.mark.slow
+def test_ep8_shard_routed_real_shape():
+    """The routed pass on shard 0 of 8 at DeepSeek-V3's real shape: 4096 tokens routed over all
+    256 experts (sigmoid + bias, 8 groups / top-4, rsf 2.5), the 32 local experts' weights only,
+    the other shards' routes -1; 64+ tokens chosen from the local routing compared with the
+    oracle on the same local ids."""
+    cfg = CONFIGS["ds-v3-grouped-prefill"]
+    d = make_inputs(cfg, DEV, weights=False)
+    ids, w = oracle_route(d, cfg)
+    n_local = 32
+    loc = np.where((ids >= 0) & (ids < n_local), ids, -1).astype(np.int32)
+    local = replace(cfg, E=n_local)
+    dl = make_inputs(local, DEV)                 # 32 experts of the real shape
+    dl["hidden_states"] = d["hidden_states"]
+    out = moe.fused_moe_experts_fwd(dl["hidden_states"], dl["w_gate_up"], dl["w_down"],
+                                    torch.from_numpy(loc).to(DEV), torch.from_numpy(w).to(DEV))
+    torch.cuda.synchronize()
+    tokens = routing_tokens(loc, n_local, 256, n=64)
+    _, ref = oracle_experts_sampled(dl, loc, w, tokens)
+    rel = assert_output_close(out[torch.as_tensor(tokens, device=DEV)], ref, "ep8 routed shard")
+    print("ep8 routed shard: %d local routes, rel-L2 %.2e" % (int((loc >= 0).sum()), rel),
+          flush=True)

@@ -196,6 +196,25 @@ int fused_moe_fwd(const uint16_t *hidden_states, const float *gating_output,
                   int32_t *topk_ids_out, float *topk_weights_out, void *workspace,
                   size_t workspace_bytes, void *stream);
 
+/* fused_moe_fwd_noalloc -- fused_moe_fwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments without the workspace, which instead is a fixed array of
+ * MOE_NOALLOC_SCRATCH_BYTES (128 MiB) of device memory inside the library, one per GPU, held
+ * until the process ends.  The call allocates nothing; its first call on a device (with that
+ * device current, and the stream on it) looks up the array's device address.  Every call on a
+ * GPU uses that GPU's one array, so calls that can overlap on one GPU (other streams, other
+ * threads) race and give undefined results; calls in one stream's order are fine.  Results
+ * are bit-identical to fused_moe_fwd's.
+ * Errors: as fused_moe_fwd; MOE_ERR_WORKSPACE when fused_moe_workspace_bytes(p, 0) exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES (checked before anything is enqueued; the Qwen3 decode and batch
+ * workloads fit, 4096-token DeepSeek-V3 prefill does not); MOE_ERR_LAUNCH if the array's
+ * address cannot be looked up. */
+#define MOE_NOALLOC_SCRATCH_BYTES (128u << 20)
+int fused_moe_fwd_noalloc(const uint16_t *hidden_states, const float *gating_output,
+                          const uint16_t *w_gate_up, const uint16_t *w_down,
+                          const float *correction_bias, const moe_params_t *p, uint16_t *out,
+                          int32_t *topk_ids_out, float *topk_weights_out, void *stream);
+
 /* fused_moe_shared_fwd -- fused_moe_fwd plus a shared expert added unweighted (TileOPs "MoE"
  * page, FusedMoESharedExpertFwd: shared_w_gate_up [2S,H], shared_w_down [H,S]).
  *   shared_w_gate_up [2S,H] bf16 (rows [0,S) gate, [S,2S) up); shared_w_down [H,S] bf16;

@@ -11,6 +11,7 @@ Entry points (same names as the C ABI):
   moe_align_sort(topk_ids, num_experts, block_m[, workspace]) -> dict of int32 tensors
   moe_align_sort_workspace_bytes(T, k, num_experts, block_m) -> bytes
   fused_moe_fwd(hidden_states, gating_output, w_gate_up, w_down, top_k, ...) -> out
+  fused_moe_fwd_noalloc(same as fused_moe_fwd, no workspace)  -> out (library-held scratch)
   fused_moe_shared_fwd(..., shared_w_gate_up, shared_w_down)  -> out
   fused_moe_experts_fwd(hidden_states, w_gate_up, w_down, topk_ids, topk_weights) -> out
   fused_moe_masked_fwd(a, masked_m, w_gate_up, w_down)        -> out [E, max_m, H]
@@ -69,6 +70,7 @@ SIGNATURES = {
     "moe_align_sort_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
     "fused_moe_workspace_bytes": (_SZ, [_P, _I32]),
     "fused_moe_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "fused_moe_fwd_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "fused_moe_mxfp4_workspace_bytes": (_SZ, [_P]),
     "fused_moe_fp8_workspace_bytes": (_SZ, [_P]),
     "fused_moe_fp8_stage": (ctypes.c_int, [_I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
@@ -284,6 +286,45 @@ def fused_moe_fwd(hidden_states, gating_output, w_gate_up, w_down, top_k, correc
     return _fused(hidden_states, gating_output, w_gate_up, w_down, top_k, correction_bias,
                   scoring, renormalize, num_expert_group, topk_group, routed_scaling_factor,
                   None, None, path, out, workspace, return_routing)
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20
+
+
+def fused_moe_fwd_noalloc(hidden_states, gating_output, w_gate_up, w_down, top_k,
+                          correction_bias=None, scoring="softmax", renormalize=True,
+                          num_expert_group=1, topk_group=1, routed_scaling_factor=1.0,
+                          path="auto", out=None, topk_ids_out=None, topk_weights_out=None):
+    """fused_moe_fwd without a workspace: the library's own fixed scratch array is used (see
+    include/moe.h).  out / topk_ids_out / topk_weights_out may be given (preallocated)."""
+    T, H = hidden_states.shape
+    E, F2, _ = w_gate_up.shape
+    F = F2 // 2
+    dev = hidden_states.device
+    dt = _pass_dtype(hidden_states)
+    _check(hidden_states, "hidden_states", dt, (T, H))
+    _check(gating_output, "gating_output", torch.float32, (T, E), dev)
+    _check(w_gate_up, "w_gate_up", dt, (E, 2 * F, H), dev)
+    _check(w_down, "w_down", dt, (E, H, F), dev)
+    if correction_bias is not None:
+        _check(correction_bias, "correction_bias", torch.float32, (E,), dev)
+    p = make_params(T, H, E, F, top_k, scoring, renormalize, num_expert_group, topk_group,
+                    routed_scaling_factor, path, dt)
+    if out is None:
+        out = torch.empty((T, H), dtype=dt, device=dev)
+    _check(out, "out", dt, (T, H), dev)
+    if topk_ids_out is not None:
+        _check(topk_ids_out, "topk_ids_out", torch.int32, (T, top_k), dev)
+    if topk_weights_out is not None:
+        _check(topk_weights_out, "topk_weights_out", torch.float32, (T, top_k), dev)
+    with torch.cuda.device(dev):
+        st = lib().fused_moe_fwd_noalloc(
+            _ptr(hidden_states), _ptr(gating_output), _ptr(w_gate_up), _ptr(w_down),
+            _ptr(correction_bias), ctypes.byref(p), _ptr(out), _ptr(topk_ids_out),
+            _ptr(topk_weights_out), _stream(dev))
+    if st != MOE_OK:
+        raise MoEError(st, "fused_moe_fwd_noalloc")
+    return out
 
 
 def fused_moe_shared_fwd(hidden_states, gating_output, w_gate_up, w_down, shared_w_gate_up,

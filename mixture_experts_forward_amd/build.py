@@ -19,7 +19,8 @@ LIB = os.path.join(HERE, "libmoe_mi355x.so")
 SOURCES = ["moe_plan.cpp", "moe_api.cpp", "moe_route.hip", "moe_align.hip", "moe_gemm_ws.hip",
            "moe_gemm_tiled.hip",
            "moe_gemm_wide.hip", "moe_combine.hip", "moe_masked.hip",
-           "moe_gemm_fp8.hip", "moe_quant.hip", "moe_gemm_mx.hip", "moe_stream_read.hip"]
+           "moe_gemm_fp8.hip", "moe_quant.hip", "moe_gemm_mx.hip", "moe_stream_read.hip",
+           "moe_noalloc.hip"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH, "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

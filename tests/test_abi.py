@@ -239,3 +239,22 @@ def test_stream_read_rejects_before_launch():
     assert L.moe_stream_read(ctypes.c_void_p(4096 + 8), 1024, fake, None) == -3  # alignment
     assert L.moe_stream_read(fake, 1000, fake, None) == -3                # bytes % 16
 
+
+
+def test_noalloc_checks_before_touching_the_gpu():
+    """fused_moe_fwd_noalloc rejects a pass whose workspace exceeds its fixed array, and passes
+    fused_moe_fwd's own argument errors through, before any HIP call."""
+    L = moe.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    big = moe.make_params(4096, 7168, 256, 2048, 8, "sigmoid")
+    assert moe.workspace_bytes(big) > moe.NOALLOC_SCRATCH_BYTES
+    assert L.fused_moe_fwd_noalloc(fake, fake, fake, fake, fake, ctypes.byref(big), fake, None,
+                                   None, None) == -4
+    assert L.fused_moe_fwd_noalloc(fake, fake, fake, fake, None, None, fake, None, None,
+                                   None) == -1
+    bad = moe.make_params(4, 128, 8, 64, 9)
+    assert L.fused_moe_fwd_noalloc(fake, fake, fake, fake, None, ctypes.byref(bad), fake, None,
+                                   None, None) == -2
+    z = moe.make_params(0, 128, 8, 64, 2)
+    assert L.fused_moe_fwd_noalloc(None, None, None, None, None, ctypes.byref(z), None, None,
+                                   None, None) == 0

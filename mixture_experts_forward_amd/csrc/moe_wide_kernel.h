@@ -172,20 +172,18 @@ __device__ __forceinline__ void wide_decode(const GemmProblem &g, int t, int n_b
 
 // Number of leading real rows of the tile: sorted rows -> padding is a suffix of the expert's
 // segment (found by a binary search of the first -1); dense rows -> min(256, rows - row0).
+// Every lane of the wave calls it: lane l reads the ids of rows 4l .. 4l+3 (one 16-byte load;
+// row0 is a multiple of 256 and the padded layout holds whole 256-row tiles), and four ballots
+// count the rows that hold a route -- one load latency instead of a dependent search.
 template <int SRC>
 __device__ __forceinline__ int wide_real_rows(const GemmProblem &g, int row0)
 {
     if (SRC != moe::ROWS_SORTED)
         return min(kBM, g.rows - row0);
-    int lo = 0, hi = kBM;  // sorted_ids[row0 + r] >= 0 exactly for r < answer
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (g.sorted_ids[row0 + mid] >= 0)
-            lo = mid + 1;
-        else
-            hi = mid;
-    }
-    return lo;
+    const int lane = threadIdx.x & 63;
+    const moe_u32x4 v = *reinterpret_cast<const moe_u32x4 *>(g.sorted_ids + row0 + 4 * lane);
+    return __popcll(__ballot((int)v.x >= 0)) + __popcll(__ballot((int)v.y >= 0)) +
+           __popcll(__ballot((int)v.z >= 0)) + __popcll(__ballot((int)v.w >= 0));
 }
 
 // The bf16 tile: 32 x 32 x 16 MFMAs (twice the work per issue of 16 x 16 x 32 on gfx950), a wave
@@ -201,15 +199,30 @@ constexpr int kXStages = 2;
 template <int WS>
 constexpr int wide_lds_bytes() { return (kXStages + WS) * kHalf; }
 static_assert(kBM == kBW, "both operands' k-steps take kHalf bytes");
+// Tiles of at most kSmallRows real rows run a deeper pipeline: kSmallStages stages of a
+// 64-row activation k-step (kSmallX bytes) and a 256-row weight k-step.
+#ifndef MOE_WIDE_SMALL_ROWS
+#define MOE_WIDE_SMALL_ROWS 64
+#endif
+constexpr int kSmallRows = MOE_WIDE_SMALL_ROWS;
+constexpr int kSmallStages = 4;
+constexpr int kSmallX = 64 * kStep * 2;
+static_assert(kSmallRows <= 64, "the small pipeline's activation stage holds 64 rows");
+static_assert(kSmallStages * (kSmallX + kHalf) <= wide_lds_bytes<3>(),
+              "the small pipeline fits the LDS of the three-stage kernel");
 
 // One 256 x 256 tile over k-steps [kbeg, kbeg + kcnt) of the K loop (visited from a rotated
 // start).  part == NULL: the whole K range, written as bf16 (gate-up: SiLU(gate)*up).  Else the
 // f32 accumulators of this K range go to part as [256 activation rows][256 weight rows] (rows
 // past the tile's real rows are not written), for k_wide_reduce to sum.
-template <bool GATE_UP, int SRC, int WS, int DT>
+struct NoHook {
+    __device__ void operator()() const {}
+};
+
+template <bool GATE_UP, int SRC, int WS, int DT, typename Hook = NoHook>
 __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mtile, int expert,
                                           moe_u32x4 *smem, int kbeg = 0, int kcnt = -1,
-                                          float *part = nullptr)
+                                          float *part = nullptr, Hook hook = Hook())
 {
     using St = Stage<kStep>;
     constexpr int kSlots = St::kSlots, kRows = St::kRowsPerLoad;
@@ -286,6 +299,9 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
         mt_real += (32 * (wm + kWM * i) < n_real) ? 1 : 0;
 
     const int nk = kcnt < 0 ? K / kStep : kcnt;
+    // every wave calls hook() once, after issuing the loads of k-step hook_at (three k-steps
+    // before the tile's last)
+    const int hook_at = nk > 3 ? nk - 3 : 0;
     const unsigned rkey = SRC == moe::ROWS_SORTED ? expert : nblk;
     const int rot = (int)((rkey * 7u) % (unsigned)nk);
 
@@ -334,6 +350,8 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
                 issue_x(i + 1);
             if (i + A < nk)
                 issue_w(i + A);
+            if (i == hook_at)
+                hook();
             if (MTR == 0)
                 continue;
             const moe_u32x4 *xb = smem + (i % kXStages) * (kHalf / 16);
@@ -364,10 +382,87 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
             }
         }
     };
-    switch (mt_real) {
-    case 0: k_loop(std::integral_constant<int, 0>()); break;
-    case 1: k_loop(std::integral_constant<int, 1>()); break;
-    default: k_loop(std::integral_constant<int, 2>()); break;
+    // Tiles of at most kSmallRows real rows (the few-row experts of prefill, an expert's ragged
+    // last tile) are bound by their weight stream, not by MFMAs.  Their activation rows fit
+    // 8 KB stages, so the LDS holds four stages of both operands and the weights run three
+    // k-steps ahead instead of two: 96 KB of weights in flight per CU, which lets these tiles
+    // draw more than an even share of HBM while tiles of fuller experts on other CUs are busy
+    // with MFMAs.  Each wave fetches 8 of the 64 activation rows and its 32 weight rows per
+    // k-step; both operands of a k-step are issued together, so one wait covers them.
+    auto k_loop_small = [&](auto mtr) {
+        constexpr int MTR = decltype(mtr)::value;   // 0 or 1 (rows < 64: tile m = 0 only)
+        constexpr int SA = kSmallStages - 1;        // k-steps ahead
+        static_assert(kSmallStages * (kSmallX + kHalf) <= wide_lds_bytes<WS>(),
+                      "the small pipeline fits this kernel's LDS");
+        const int srow = 8 * wv + lrow;             // this lane's activation row of the tile
+        const bool sxl = 8 * wv < n_real;           // wave-uniform: its 8 rows hold a real row
+        int ssrc = 0;
+        if (srow < n_real)
+            ssrc = SRC == moe::ROWS_SORTED
+                       ? (GATE_UP ? g.sorted_ids[row0 + srow] / g.top_k : row0 + srow)
+                       : row0 + srow;
+        const uint16_t *sx = g.act + (size_t)ssrc * K + 8 * (lpos ^ ((srow >> 1) & (kSlots - 1)));
+        const uint32_t sx_dst = lds0 + wv * 1024;
+        const uint32_t sw_dst = lds0 + kSmallStages * kSmallX + wv * (kBW / kWaves) * (kStep * 2);
+        const int per_step = kWLoads + (sxl ? 1 : 0);
+        auto issue = [&](int i) {
+            const int kb = (kbeg + (i + rot) % nk) * kStep;
+            const int st = i % kSmallStages;
+            if (sxl)
+                dma16(sx + kb, sx_dst + st * kSmallX);
+#pragma unroll
+            for (int j = 0; j < kWLoads; ++j)
+                dma16(wsrc[j] + kb, sw_dst + st * kHalf + j * 1024);
+        };
+#pragma unroll
+        for (int s = 0; s < SA; ++s)
+            if (s < nk)
+                issue(s);
+        for (int i = 0; i < nk; ++i) {
+            // at most the loads of steps i+1 .. i+SA-1 may still be in flight: this wave's part
+            // of step i has landed; the barrier publishes every wave's part and guarantees that
+            // every wave is done with step i-1, whose stage step i+SA overwrites
+            step_barrier(min(SA - 1, nk - 1 - i) * per_step);
+            if (i + SA < nk)
+                issue(i + SA);
+            if (i == hook_at)
+                hook();
+            if (MTR == 0)
+                continue;
+            const int st = i % kSmallStages;
+            const moe_u32x4 *xb = smem + st * (kSmallX / 16);
+            const moe_u32x4 *wb = smem + (kSmallStages * kSmallX + st * kHalf) / 16;
+            moe_u32x4 a[2][kNT32], b[2];
+            auto read = [&](int buf, int h) {
+                b[buf] = xb[St::slot(32 * wm + rr, 2 * h + rq)];
+#pragma unroll
+                for (int n = 0; n < kNT32; ++n)
+                    a[buf][n] = wb[St::slot(wrow0[n] + rr, 2 * h + rq)];
+            };
+            read(0, 0);
+#pragma unroll
+            for (int h = 0; h < kStep / 16; ++h) {
+                if (h + 1 < kStep / 16)
+                    read((h + 1) & 1, h + 1);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int n = 0; n < kNT32; ++n)
+                    acc[0][n] = moe_mma32<DT>(a[h & 1][n], b[h & 1], acc[0][n]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
+    if (n_real <= kSmallRows) {
+        if (mt_real == 0)
+            k_loop_small(std::integral_constant<int, 0>());
+        else
+            k_loop_small(std::integral_constant<int, 1>());
+    } else {
+        switch (mt_real) {
+        case 0: k_loop(std::integral_constant<int, 0>()); break;
+        case 1: k_loop(std::integral_constant<int, 1>()); break;
+        default: k_loop(std::integral_constant<int, 2>()); break;
+        }
     }
 
     // ---- epilogue.  For weight tile n, register 4q' + q holds column 8q' + 4*(lane/32) + q of
@@ -402,9 +497,19 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
     }
     constexpr int TC = GATE_UP ? kBW / 2 : kBW;  // output columns of the tile
     constexpr int CPR = TC / 8;                  // 16-byte chunks per row
+    constexpr int RSTEP = kThreads / CPR;        // rows stored per pass of the workgroup
     static_assert(kBM * TC * 2 <= wide_lds_bytes<2>(), "output tile fits in LDS");
+    // The down GEMM on sorted rows writes each row to its route's row.  Those 256 lookups are
+    // issued together (one per thread) before the staging and kept in LDS past the output tile,
+    // so the store loop does not wait on a lookup before each store.
+    constexpr bool kRouteDst = SRC == moe::ROWS_SORTED && !GATE_UP;
+    static_assert(kBM * TC * 2 + kBM * 4 <= wide_lds_bytes<WS>(), "lookups fit beside the tile");
+    int my_dst = -1;
+    if (kRouteDst && tid < kBM && tid < n_real)
+        my_dst = g.sorted_ids[row0 + tid];
     __syncthreads();  // every wave is done with the last k-step's operands
     uint16_t *otile = reinterpret_cast<uint16_t *>(smem);
+    int *s_dst = reinterpret_cast<int *>(smem) + kBM * TC * 2 / 4;
     auto opos = [](int r, int c) { return r * CPR + (c ^ (r & (CPR - 1))); };
 #pragma unroll
     for (int m = 0; m < kMT32; ++m) {
@@ -436,15 +541,15 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
             }
         }
     }
+    if (kRouteDst && tid < kBM)
+        s_dst[tid] = my_dst;
     __syncthreads();
-    // thread t stores chunk t % CPR of rows t / CPR, t / CPR + kThreads / CPR, ...
+    // thread t stores chunk t % CPR of rows t / CPR, t / CPR + RSTEP, ...
     const int oc = tid % CPR;
     const int col = col_wg + 8 * oc;
     if (col < g.n_out) {
-        for (int r = tid / CPR; r < n_real; r += kThreads / CPR) {
-            const int dst = SRC == moe::ROWS_SORTED
-                                ? (GATE_UP ? row0 + r : g.sorted_ids[row0 + r])
-                                : row0 + r;
+        for (int r = tid / CPR; r < n_real; r += RSTEP) {
+            const int dst = kRouteDst ? s_dst[r] : row0 + r;
             // output rows are read once, by a later launch: non-temporal, so they do not evict
             // the operands this launch's other tiles still share through L2
             __builtin_nontemporal_store(
@@ -481,34 +586,51 @@ __device__ __forceinline__ void wide_queue_loop(const GemmProblem &g, int n_bloc
     volatile int *s_next = reinterpret_cast<volatile int *>(smem);
     moe::TileSchedule *sched = g.sched;
     const int home = blockIdx.x % kXcds;
-    int tried = 0;  // ranges found used up (thread 0's state)
-    while (true) {
-        if (threadIdx.x == 0) {
-            int t = -1;
-            while (tried < P) {
-                const int p = (home + tried) % P;
-                const int lo = sched_bound(sched, p, n_blocks, total);
-                const int hi = sched_bound(sched, p + 1, n_blocks, total);
-                if (lo < hi) {
-                    const int n = atomicAdd(&sched->queue[p], 1);
-                    if (n < hi - lo) {
-                        t = lo + n;
-                        break;
-                    }
-                }
-                ++tried;
+    // thread 0's state: ranges found used up, the bounds [lo, hi) of the range it takes from,
+    // and the counter value of a take issued during the current tile (-1: none)
+    int tried = 0, lo = 0, hi = 0, pend = -1;
+    auto range = [&]() {
+        const int p = (home + tried) % P;
+        lo = sched_bound(sched, p, n_blocks, total);
+        hi = sched_bound(sched, p + 1, n_blocks, total);
+    };
+    auto next_tile = [&]() -> int {
+        while (tried < P) {
+            if (lo < hi) {
+                const int n = pend >= 0 ? pend : atomicAdd(&sched->queue[(home + tried) % P], 1);
+                pend = -1;
+                if (n < hi - lo)
+                    return lo + n;
             }
-            *s_next = t;
+            pend = -1;
+            if (++tried < P)
+                range();
         }
-        __syncthreads();
-        const int t = *s_next;
-        __syncthreads();  // every wave has read it before the tile's loads overwrite the stage
-        if (t < 0)
-            break;
+        return -1;
+    };
+    if (threadIdx.x == 0) {
+        range();
+        *s_next = next_tile();
+    }
+    __syncthreads();
+    int t = *s_next;
+    __syncthreads();  // every wave has read it before the tile's loads overwrite the stage
+    while (t >= 0) {
         int nblk, mtile, expert;
         wide_decode<SRC>(g, t, n_blocks, 0, nblk, mtile, expert);
-        wide_tile<GATE_UP, SRC, WS, DT>(g, nblk, mtile, expert, smem);
-        __syncthreads();  // the next tile's first loads follow every wave's last reads
+        // Three k-steps before the tile ends, thread 0 takes the next tile number from its
+        // range's counter; the round trip overlaps the tile's last k-steps and the result is
+        // first read after the tile (the take needs no load: the bounds are in registers).
+        wide_tile<GATE_UP, SRC, WS, DT>(g, nblk, mtile, expert, smem, 0, -1, nullptr, [&]() {
+            if (threadIdx.x == 0 && tried < P && lo < hi)
+                pend = atomicAdd(&sched->queue[(home + tried) % P], 1);
+        });
+        __syncthreads();  // every wave is done with the tile's LDS
+        if (threadIdx.x == 0)
+            *s_next = next_tile();
+        __syncthreads();
+        t = *s_next;
+        __syncthreads();  // every wave has read it before the next tile's loads overwrite it
     }
     if (threadIdx.x == 0) {
         // thread 0's counter updates are complete (their results were used); the last

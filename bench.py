@@ -741,9 +741,11 @@ def read_traffic(workload):
 KERNEL_FAMILY_SOURCES = {
     "k_ws_gemm": ("moe_ws_kernel.h", "moe_gemm_ws.hip"),
     "k_tiled_gemm": ("moe_tiled_kernel.h", "moe_gemm_tiled.hip"),
-    "k_block_gemm": ("moe_block_kernel.h", "moe_gemm_block.hip"),
     "k_wide_gemm": ("moe_wide_kernel.h", "moe_gemm_wide.hip"),
 }
+
+# GEMM roles with a counter summary each: profiles/<role>_<workload>_pmc.txt
+PMC_ROLES = ("gate_up", "down", "shared_gate_up", "shared_down")
 
 
 def kernel_source_hash(kernel_names):
@@ -777,11 +779,22 @@ def _read_counters(d):
     return out
 
 
+def _role(name):
+    """GEMM role of a kernel name: gate_up / down of the routed experts (any row source but
+    dense), shared_gate_up / shared_down (dense rows, SRC 2), or None for other kernels."""
+    for fam in KERNEL_FAMILY_SOURCES:
+        key = fam + "<"
+        if key in name:
+            args = name.split(key, 1)[1].split(">", 1)[0].split(",")
+            gate_up = args[0].strip() == "true"
+            dense = args[1].strip() == "2"
+            return ("shared_" if dense else "") + ("gate_up" if gate_up else "down")
+    return None
+
+
 def _is_dominant(name):
-    """The gate-up GEMM of the routed experts (weight-streaming or row-tiled kernel)."""
-    return (("k_ws_gemm<true" in name or "k_tiled_gemm<true" in name
-             or "k_block_gemm<true" in name or "k_wide_gemm<true" in name)
-            and "<true, 2," not in name and "<true, 2>" not in name)
+    """The gate-up GEMM of the routed experts."""
+    return _role(name) == "gate_up"
 
 
 def _calibration_copy(disp):
@@ -822,7 +835,7 @@ def summarize_trace(args):
     lines += ["", "Template arguments: k_ws_gemm<GATE_UP, SRC, NT, MT, KSPLIT, STAGES, DT, SEGK> "
               "(SRC 0 sorted, 1 direct, 2 dense, 3 scan; DT 0 bf16, 1 f16; SEGK k-steps per weight "
               "load segment, STAGES counting segments); k_tiled_gemm<GATE_UP, SRC, "
-              "BM, NTW, STAGES, DT>; k_block_gemm<GATE_UP, SRC, TN, STAGES, DT>; "
+              "BM, NTW, STAGES, DT>; "
               "k_wide_gemm<GATE_UP, SRC, WS, DT> (WS weight stages); k_wide_reduce<GATE_UP, DT> (sum "
               "of the K-split dense tiles' parts); k_combine<DT>."]
     out = os.path.join(PROFILE_DIR, "kernel_trace_%s.md" % cfg.name)
@@ -832,47 +845,55 @@ def summarize_trace(args):
 
 
 def summarize_pmc(args):
-    """profiles/gate_up_<workload>_pmc.txt from rocprofv3 --pmc runs of bench.py
+    """profiles/<role>_<workload>_pmc.txt for each expert GEMM role present (routed gate-up and
+    down, the shared expert's gate-up and down) from rocprofv3 --pmc runs of bench.py
     --copy-calibration (FETCH_SIZE run, WRITE_SIZE run, optional MFMA-busy run)."""
     from moe_harness.workloads import BENCH_CONFIG, CONFIGS
     cfg = CONFIGS[args.config or BENCH_CONFIG]
     runs = [_read_counters(d) for d in args.summarize_pmc]
-    res = {}
-    lines = ["# HBM traffic and MFMA activity of the gate-up GEMM, workload %s" % cfg.name,
-             "# FETCH_SIZE / WRITE_SIZE are per-dispatch KiB; each is scaled by the reading of "
-             "the same counter for one plain device-to-device copy of known size in the same "
-             "run.", "#"]
-    for c in args.pmc_commands:
-        lines.append("command: %s" % c)
-    for counter, disp in zip(("FETCH_SIZE", "WRITE_SIZE"), runs[:2]):
-        dom = [v[counter] for i, (n, v) in disp.items() if _is_dominant(n) and counter in v]
-        names = sorted({n for n, v in disp.values() if _is_dominant(n)})
-        cal = disp[_calibration_copy(disp)][1][counter]
-        copy_bytes = args.copy_calibration
-        scale = copy_bytes / (cal * 1024.0)
-        res[counter] = sum(dom) / len(dom) * 1024.0 * scale
-        lines += ["%s_kib_per_dispatch: %.1f" % (counter.lower(), sum(dom) / len(dom)),
-                  "%s_dispatches: %d" % (counter.lower(), len(dom)),
-                  "%s_copy_kib: %.1f" % (counter.lower(), cal),
-                  "%s_scale: %.5f" % (counter.lower(), scale)]
-        res["kernels"] = names
-    if len(runs) > 2:
-        disp = runs[2]
-        # GRBM_GUI_ACTIVE is summed over the 8 XCDs; MFMA-busy cycles over the 1024 SIMDs
-        busy = [v["SQ_VALU_MFMA_BUSY_CYCLES"] / (v["GRBM_GUI_ACTIVE"] / 8.0 * 1024.0)
-                for n, v in disp.values() if _is_dominant(n) and "GRBM_GUI_ACTIVE" in v]
-        if busy:
-            lines.append("mfma_busy_pct: %.2f" % (100.0 * sum(busy) / len(busy)))
-    lines += ["copy_bytes: %d" % args.copy_calibration,
-              "kernel: %s" % "; ".join(res["kernels"]),
-              "kernel_source_sha256: %s" % kernel_source_hash("; ".join(res["kernels"])),
-              "fetch_bytes_per_launch: %.0f" % res["FETCH_SIZE"],
-              "write_bytes_per_launch: %.0f" % res["WRITE_SIZE"],
-              "traffic_bytes_per_launch: %.0f" % (res["FETCH_SIZE"] + res["WRITE_SIZE"])]
-    path = os.path.join(PROFILE_DIR, "gate_up_%s_pmc.txt" % cfg.name)
-    os.makedirs(PROFILE_DIR, exist_ok=True)
-    open(path, "w").write("\n".join(lines) + "\n")
-    print("\n".join(lines))
+    titles = {"gate_up": "the gate-up GEMM of the routed experts",
+              "down": "the down GEMM of the routed experts",
+              "shared_gate_up": "the shared expert's gate-up GEMM",
+              "shared_down": "the shared expert's down GEMM"}
+    for role in PMC_ROLES:
+        if not any(_role(n) == role for n, _ in runs[0].values()):
+            continue
+        res = {}
+        lines = ["# HBM traffic and MFMA activity of %s, workload %s" % (titles[role], cfg.name),
+                 "# FETCH_SIZE / WRITE_SIZE are per-dispatch KiB; each is scaled by the reading of "
+                 "the same counter for one plain device-to-device copy of known size in the same "
+                 "run.", "#"]
+        for c in args.pmc_commands:
+            lines.append("command: %s" % c)
+        for counter, disp in zip(("FETCH_SIZE", "WRITE_SIZE"), runs[:2]):
+            dom = [v[counter] for i, (n, v) in disp.items() if _role(n) == role and counter in v]
+            names = sorted({n for n, v in disp.values() if _role(n) == role})
+            cal = disp[_calibration_copy(disp)][1][counter]
+            copy_bytes = args.copy_calibration
+            scale = copy_bytes / (cal * 1024.0)
+            res[counter] = sum(dom) / len(dom) * 1024.0 * scale
+            lines += ["%s_kib_per_dispatch: %.1f" % (counter.lower(), sum(dom) / len(dom)),
+                      "%s_dispatches: %d" % (counter.lower(), len(dom)),
+                      "%s_copy_kib: %.1f" % (counter.lower(), cal),
+                      "%s_scale: %.5f" % (counter.lower(), scale)]
+            res["kernels"] = names
+        if len(runs) > 2:
+            disp = runs[2]
+            # GRBM_GUI_ACTIVE is summed over the 8 XCDs; MFMA-busy cycles over the 1024 SIMDs
+            busy = [v["SQ_VALU_MFMA_BUSY_CYCLES"] / (v["GRBM_GUI_ACTIVE"] / 8.0 * 1024.0)
+                    for n, v in disp.values() if _role(n) == role and "GRBM_GUI_ACTIVE" in v]
+            if busy:
+                lines.append("mfma_busy_pct: %.2f" % (100.0 * sum(busy) / len(busy)))
+        lines += ["copy_bytes: %d" % args.copy_calibration,
+                  "kernel: %s" % "; ".join(res["kernels"]),
+                  "kernel_source_sha256: %s" % kernel_source_hash("; ".join(res["kernels"])),
+                  "fetch_bytes_per_launch: %.0f" % res["FETCH_SIZE"],
+                  "write_bytes_per_launch: %.0f" % res["WRITE_SIZE"],
+                  "traffic_bytes_per_launch: %.0f" % (res["FETCH_SIZE"] + res["WRITE_SIZE"])]
+        path = os.path.join(PROFILE_DIR, "%s_%s_pmc.txt" % (role, cfg.name))
+        os.makedirs(PROFILE_DIR, exist_ok=True)
+        open(path, "w").write("\n".join(lines) + "\n")
+        print("\n".join(lines))
 
 
 def _cpu_baseline_mx(cfg, d, seconds, x, ids, w, route_s):

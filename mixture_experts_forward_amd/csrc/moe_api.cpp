@@ -114,6 +114,8 @@ bool launch_gemm(bool gate_up, const moe::GemmProblem &g, moe::RowSource src,
         return moe::launch_wide(gate_up, g, src, stream);
     if (t.kind == moe::KERNEL_MX)
         return moe::launch_mx(gate_up, g, src, ws_tile(t), stream);
+    if (t.kind == moe::KERNEL_MX_TILED)
+        return moe::launch_mx_tiled(gate_up, g, src, ws_tile(t), stream);
     return gate_up ? moe::launch_gate_up(g, src, ws_tile(t), stream)
                    : moe::launch_down(g, src, ws_tile(t), stream);
 }

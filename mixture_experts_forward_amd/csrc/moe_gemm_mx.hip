@@ -50,9 +50,36 @@ bool by_source(const GemmProblem &g, moe::RowSource src, moe::WsTile t, hipStrea
     }
 }
 
+template <bool GATE_UP, int NTW, int STAGES>
+void launch_tiled_one(const GemmProblem &g, hipStream_t stream)
+{
+    const int n_blocks = (g.n_out + 16 * NTW * 4 - 1) / (16 * NTW * 4);
+    const int m_tiles = g.num_groups;
+    const int blocks = moe_tiled::tiled_grid(n_blocks, m_tiles);
+    hipLaunchKernelGGL((moe_mx::k_mx_tiled<GATE_UP, NTW, STAGES>), dim3(blocks), dim3(256), 0,
+                       stream, g, n_blocks, m_tiles);
+}
+
 }  // namespace
 
 namespace moe {
+
+bool launch_mx_tiled(bool gate_up, const GemmProblem &g, RowSource src, WsTile t,
+                     hipStream_t stream)
+{
+    if (src != ROWS_SORTED || t.mt != 4)
+        return false;
+#define MOE_MXT_CASE(G_, NTW_, ST_)                                                              \
+    if (gate_up == G_ && t.nt == NTW_ && t.stages == ST_) {                                      \
+        launch_tiled_one<G_, NTW_, ST_>(g, stream);                                              \
+        return true;                                                                             \
+    }
+    MOE_MXT_CASE(true, 1, 3)
+    MOE_MXT_CASE(false, 2, 3)
+#undef MOE_MXT_CASE
+    return false;
+}
+
 
 bool launch_mx(bool gate_up, const GemmProblem &g, RowSource src, WsTile tile,
                hipStream_t stream)

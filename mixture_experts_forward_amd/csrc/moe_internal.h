@@ -104,6 +104,10 @@ void launch_masked_ids(const int32_t *masked_m, int E, int max_m, int32_t *ids,
 // (moe_mx_kernel.h); SORTED, DIRECT or SCAN rows; K % 128 == 0.
 bool launch_mx(bool gate_up, const GemmProblem &g, RowSource src, WsTile tile,
                hipStream_t stream);
+// The row-tiled MXFP4-weight GEMM (ROWS_SORTED with block_m = 64; tile.mt = 4, tile.nt
+// 16-column tiles per wave, tile.stages).
+bool launch_mx_tiled(bool gate_up, const GemmProblem &g, RowSource src, WsTile tile,
+                     hipStream_t stream);
 
 // ---------------------------------------------------------------- fp8 grouped GEMM
 // out[e, m, n] for m < masked_m[e] (moe_fp8_kernel.h); K % 128 == 0, N % 64 == 0.

@@ -22,6 +22,7 @@
 
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "moe_tiled_kernel.h"
 #include "moe_ws_kernel.h"
 
 namespace moe_mx {
@@ -240,6 +241,198 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_mx_gemm(GemmProblem g)
         }
         if (KSPLIT > 1)
             __syncthreads();  // s_red is reused by the next pass
+    }
+}
+
+// Row-tiled form, for tens to hundreds of routed rows per expert: the 16-row passes above stream
+// an expert's weights once per pass; here a workgroup (4 waves) owns a 64-row tile of one
+// expert's segment of the sorted layout (block_m 64) and 4 * NTW 16-column tiles, so each
+// weight byte feeds 64 rows.
+//   - each wave streams its own NTW (gate-up: NTW gate and NTW up) 16-row weight tiles exactly
+//     as k_mx_gemm does: per 128-element k-step and tile one 16-byte load of codes and one scale
+//     byte per lane, STAGES-1 k-steps ahead in registers, dequantised straight into the four
+//     MFMA A operands (the same permuted k order: MFMA j takes elements 32p + 8j .. + 7 from
+//     lane group p);
+//   - the tile's 64 activation rows of a k-step (16 KB) are loaded once per workgroup (each wave
+//     a quarter: 4 rows x 256 bytes per instruction) into a double-buffered LDS tile whose
+//     16-byte chunk c of row r sits at position c ^ (r & 15), so that the B-operand reads (chunk
+//     4p + j of 16 different rows) and the row-wise writes are free of bank conflicts; one
+//     barrier per k-step;
+//   - the 16-row MFMA tiles past the tile's last routed row are skipped;
+//   - tile numbering and the rotated K start as the bf16 row-tiled kernel (row tiles of one
+//     column block consecutive on one XCD).
+template <bool GATE_UP, int NTW, int STAGES>
+__global__ __launch_bounds__(256) void k_mx_tiled(GemmProblem g, int n_blocks, int m_tiles)
+{
+    constexpr int kW = 4;                        // waves
+    constexpr int BM = 64, TM = BM / 16;         // rows per tile, 16-row MFMA tiles
+    constexpr int NW = GATE_UP ? 2 * NTW : NTW;  // 16-row weight tiles per wave per k-step
+    constexpr int XI = BM / kW / 4;              // activation load instructions per wave
+    __shared__ moe_u32x4 s_x[2][BM * 16];        // 64 rows x 16 chunks of 16 bytes
+
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+    const int nb_total = moe_tiled::tiled_grid(n_blocks, m_tiles);
+    const int per_xcd = nb_total / moe_tiled::kXcds;
+    const int logical = (blockIdx.x % moe_tiled::kXcds) * per_xcd + blockIdx.x / moe_tiled::kXcds;
+    if (logical >= n_blocks * m_tiles)
+        return;
+    const int nblk = logical / m_tiles;
+    const int mtile = logical % m_tiles;
+    const int row0 = mtile * BM;
+    const int expert = g.tile_expert[mtile];
+    if (expert < 0)
+        return;  // past the last tile of this routing
+    const int K = g.K;
+    const int col0 = nblk * (16 * NTW * kW) + wv * (16 * NTW);
+
+    // routed rows of the tile (padding is a suffix of the expert's segment): one id per lane
+    const int my_route = g.sorted_ids[row0 + lane];
+    const int n_real = __popcll(__ballot(my_route >= 0));
+    const int mt_active = (n_real + 15) / 16;
+
+    // ---- weights: lane owns row lane%16 of each tile, block lane/16 of each k-step
+    const int r16 = lane & 15, p = lane >> 4;
+    const int w_rows = GATE_UP ? 2 * g.n_out : g.n_out;
+    const size_t qrow = (size_t)K / 2, srow = (size_t)K / 32;  // bytes per weight row
+    const uint8_t *Wq = g.wq + (size_t)expert * w_rows * qrow;
+    const uint8_t *Ws = g.wscale + (size_t)expert * w_rows * srow;
+    const uint8_t *wq[NW];
+    const uint8_t *wsc[NW];
+    bool tile_ok[NTW];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+        const int c = col0 + 16 * nt;
+        tile_ok[nt] = c < g.n_out;
+        const int row = (tile_ok[nt] ? c : 0) + r16;  // past the last column: row 0, never stored
+        wq[nt] = Wq + row * qrow + 16 * p;
+        wsc[nt] = Ws + row * srow + p;
+        if (GATE_UP) {
+            wq[NTW + nt] = Wq + (row + g.n_out) * qrow + 16 * p;
+            wsc[NTW + nt] = Ws + (row + g.n_out) * srow + p;
+        }
+    }
+
+    // ---- activations: instruction i of this wave loads chunk lane%16 of tile row
+    //      16*wv + 4*i + lane/16
+    const uint16_t *xld[XI];
+    int xslot[XI];
+#pragma unroll
+    for (int i = 0; i < XI; ++i) {
+        const int r = (BM / kW) * wv + 4 * i + (lane >> 4);
+        const int route = g.sorted_ids[row0 + r];
+        const int src = route < 0 ? 0 : (GATE_UP ? route / g.top_k : row0 + r);  // 0: unused
+        xld[i] = g.act + (size_t)src * K + 8 * (lane & 15);
+        xslot[i] = r * 16 + ((lane & 15) ^ (r & 15));
+    }
+
+    const int nk = K / 128;
+    const int rot = (int)((nblk * 7u) % (unsigned)nk);
+
+    moe_f32x4 acc[TM][NW];
+#pragma unroll
+    for (int mt = 0; mt < TM; ++mt)
+#pragma unroll
+        for (int nw = 0; nw < NW; ++nw)
+            acc[mt][nw] = moe_f32x4{0.f, 0.f, 0.f, 0.f};
+
+    moe_u32x4 wraw[STAGES][NW], xraw[STAGES][XI];
+    uint32_t sraw[STAGES][NW];
+    auto load = [&](int st, int i) {
+        const int k = ((i + rot) % nk) * 128;
+#pragma unroll
+        for (int nw = 0; nw < NW; ++nw) {
+            wraw[st][nw] = __builtin_nontemporal_load(
+                reinterpret_cast<const moe_u32x4 *>(wq[nw] + k / 2));
+            sraw[st][nw] = wsc[nw][k / 32];
+        }
+#pragma unroll
+        for (int x = 0; x < XI; ++x)
+            xraw[st][x] = moe_ws::load_cached(xld[x] + k);
+    };
+    auto compute = [&](int st, int i) {
+        moe_u32x4 *xb = s_x[i & 1];
+#pragma unroll
+        for (int x = 0; x < XI; ++x)
+            xb[xslot[x]] = xraw[st][x];
+        __syncthreads();  // the activation tile of this k-step is complete
+        moe_u32x4 a[NW][4];
+#pragma unroll
+        for (int nw = 0; nw < NW; ++nw) {
+            const float sc = e8m0_to_f32(sraw[st][nw]);
+            const moe_u32x4 q = wraw[st][nw];
+            a[nw][0] = dequant8(q.x, sc);
+            a[nw][1] = dequant8(q.y, sc);
+            a[nw][2] = dequant8(q.z, sc);
+            a[nw][3] = dequant8(q.w, sc);
+        }
+#pragma unroll
+        for (int mt = 0; mt < TM; ++mt) {
+            if (mt >= mt_active)
+                break;
+            const int r = mt * 16 + r16;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const moe_u32x4 b = xb[r * 16 + ((4 * p + j) ^ r16)];
+#pragma unroll
+                for (int nw = 0; nw < NW; ++nw)
+                    acc[mt][nw] = moe_mma16<0>(a[nw][j], b, acc[mt][nw]);
+            }
+        }
+    };
+
+    // Software pipeline, STAGES-1 k-steps in flight; the steady state is branch-free (past the
+    // end the prefetch wraps to an early k-step, in bounds and never consumed).  The barrier in
+    // compute() of step i also guarantees every wave has finished step i-1's reads of the
+    // buffer that step i+1 overwrites.
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st)
+        load(st, st);
+    int i = 0;
+    for (; i + STAGES <= nk; i += STAGES) {
+#pragma unroll
+        for (int st = 0; st < STAGES; ++st) {
+            load((st + STAGES - 1) % STAGES, i + st + STAGES - 1);
+            compute(st, i + st);
+        }
+    }
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st)
+        if (i + st < nk)
+            compute(st, i + st);
+
+    // ---- epilogue: lane holds columns 4*(lane/16)+q of row mt*16 + lane%16
+#pragma unroll
+    for (int mt = 0; mt < TM; ++mt) {
+        if (mt >= mt_active)
+            break;
+        const int r = mt * 16 + r16;
+        const int route = g.sorted_ids[row0 + r];
+        if (route < 0)
+            continue;
+        const int dst = GATE_UP ? row0 + r : route;
+        uint16_t *orow = g.out + (size_t)dst * g.n_out;
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+            if (!tile_ok[nt])
+                continue;
+            float v[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (GATE_UP) {
+                    const float gate = acc[mt][nt][q];
+                    const float up = acc[mt][NTW + nt][q];
+                    v[q] = gate / (1.0f + __expf(-gate)) * up;
+                } else {
+                    v[q] = acc[mt][nt][q];
+                }
+            }
+            moe_u32x2 packed;
+            packed.x = moe_pack_bf16x2(v[0], v[1]);
+            packed.y = moe_pack_bf16x2(v[2], v[3]);
+            *reinterpret_cast<moe_u32x2 *>(orow + col0 + 16 * nt + 4 * p) = packed;
+        }
     }
 }
 

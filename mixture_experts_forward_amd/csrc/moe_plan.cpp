@@ -103,9 +103,16 @@ void make_plan(const moe_params_t *p, int32_t S, Plan *pl, int wfmt)
         pl->down = {KERNEL_WIDE, 0, 16, 1, 2};
     }
     if (wfmt == WEIGHTS_MXFP4) {
-        // MXFP4 weights (W4A16): the weight-streaming form at every row count, 16-row passes
-        pl->gate_up = {KERNEL_MX, 1, 1, 2, 3};
-        pl->down = {KERNEL_MX, 2, 1, 2, 3};
+        // MXFP4 weights (W4A16): the weight-streaming form with 16-row passes up to 8 routed
+        // rows per expert, the row-tiled form (64-row tiles, each weight byte feeding 64 rows)
+        // above
+        if (pl->path == MOE_PATH_DIRECT || mean_rows <= 8.0) {
+            pl->gate_up = {KERNEL_MX, 1, 1, 2, 3};
+            pl->down = {KERNEL_MX, 2, 1, 2, 3};
+        } else {
+            pl->gate_up = {KERNEL_MX_TILED, 1, 4, 1, 3};
+            pl->down = {KERNEL_MX_TILED, 2, 4, 1, 3};
+        }
     }
     pl->shared_gate_up = {KERNEL_WIDE, 0, 16, 1, 2};
     pl->shared_down = {KERNEL_WIDE, 0, 16, 1, 2};

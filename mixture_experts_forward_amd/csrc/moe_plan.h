@@ -26,7 +26,13 @@ inline size_t align_scratch_ints(int P, int E)
     return P > kAlignChunk ? (size_t)((P + kAlignChunk - 1) / kAlignChunk) * E : 0;
 }
 
-enum KernelKind { KERNEL_WS = 0, KERNEL_TILED = 1, KERNEL_WIDE = 3, KERNEL_MX = 4 };
+enum KernelKind {
+    KERNEL_WS = 0,
+    KERNEL_TILED = 1,
+    KERNEL_WIDE = 3,
+    KERNEL_MX = 4,
+    KERNEL_MX_TILED = 5
+};
 
 // Weight format of the routed experts: 16-bit (bf16 / f16) or MXFP4.
 enum WeightFormat { WEIGHTS_16BIT = 0, WEIGHTS_MXFP4 = 1 };

@@ -69,6 +69,9 @@ def _load():
     lib.oracle_experts.restype = _I
     lib.oracle_double_to_bf16.argtypes = [ctypes.c_double]
     lib.oracle_double_to_bf16.restype = ctypes.c_uint16
+    for name in ("oracle_double_to_bf16_n", "oracle_double_to_f16_n"):
+        getattr(lib, name).argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        getattr(lib, name).restype = None
     lib.oracle_fp8_e4m3_to_double.argtypes = [ctypes.c_uint8]
     lib.oracle_fp8_e4m3_to_double.restype = ctypes.c_double
     lib.oracle_grouped_gemm_fp8.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P]
@@ -340,17 +343,17 @@ def mxfp4_to_bf16(q, scale):
 def double_to_f16(values):
     """float64 values -> IEEE binary16 bit patterns (uint16), one rounding to nearest even,
     overflow to infinity."""
-    lib = _load()
-    v = np.asarray(values, np.float64)
-    flat = np.array([lib.oracle_double_to_f16(float(a)) for a in v.ravel()], np.uint16)
-    return flat.reshape(v.shape)
+    v = np.ascontiguousarray(values, np.float64)
+    out = np.empty(v.shape, np.uint16)
+    _load().oracle_double_to_f16_n(_ptr(v), v.size, _ptr(out))
+    return out
 
 
 def double_to_bf16(values):
-    lib = _load()
-    v = np.asarray(values, np.float64)
-    flat = np.array([lib.oracle_double_to_bf16(float(a)) for a in v.ravel()], np.uint16)
-    return flat.reshape(v.shape)
+    v = np.ascontiguousarray(values, np.float64)
+    out = np.empty(v.shape, np.uint16)
+    _load().oracle_double_to_bf16_n(_ptr(v), v.size, _ptr(out))
+    return out
 
 
 def bf16_bits_to_float(bits):

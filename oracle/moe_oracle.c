@@ -657,3 +657,16 @@ int oracle_max_threads(void)
     return 1;
 #endif
 }
+
+/* The roundings above applied to n values (the Python wrappers' array form). */
+void oracle_double_to_bf16_n(const double *v, size_t n, uint16_t *out)
+{
+    for (size_t i = 0; i < n; ++i)
+        out[i] = oracle_double_to_bf16(v[i]);
+}
+
+void oracle_double_to_f16_n(const double *v, size_t n, uint16_t *out)
+{
+    for (size_t i = 0; i < n; ++i)
+        out[i] = oracle_double_to_f16(v[i]);
+}

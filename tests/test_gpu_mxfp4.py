@@ -2,7 +2,8 @@
 E8M0 scales per 32 elements, bf16 activations) against the oracle: the routed experts'
 computation on the dequantised weights (exact in bf16 at these scales), with the bf16 pass's
 tolerance (tests/parity.py).  Covers the direct path (route and scan workgroups), the sorted
-path, several 16-row passes per expert and full qwen3-30b decode dimensions on sampled
+path with 16-row passes (a few rows per expert) and with 64-row tiles (tens of rows per expert
+and more: the row-tiled form), full qwen3-30b decode and qwen3-235b batch dimensions on sampled
 tokens."""
 from dataclasses import replace
 
@@ -60,8 +61,8 @@ def test_mxfp4_small(T, path):
     _check(cfg, d, mx, path, what="mxfp4 T=%d %s" % (T, path))
 
 
-def test_mxfp4_several_passes_per_expert():
-    # about 64 rows per expert: four 16-row passes, each streaming the weights again
+def test_mxfp4_several_tiles_per_expert():
+    # about 64 rows per expert: the row-tiled form, one or two 64-row tiles per expert
     cfg = replace(CONFIGS["tiny"], T=128, H=256, E=4, F=256, k=2)
     d = make_inputs(cfg, DEV, seed=5, weights=False)
     mx = make_mxfp4_weights(cfg, DEV, seed=5)
@@ -81,3 +82,34 @@ def test_mxfp4_grouped_sigmoid_routing():
     d = make_inputs(cfg, DEV, seed=9, weights=False)
     mx = make_mxfp4_weights(cfg, DEV, seed=9)
     _check(cfg, d, mx, "auto", what="mxfp4 grouped sigmoid")
+
+
+@pytest.mark.parametrize("T,E,k,H,F", [
+    (300, 8, 4, 256, 256),     # ~150 rows per expert: three 64-row tiles, a ragged last one
+    (70, 16, 8, 384, 128),     # ~35 rows per expert: one partial tile each, 3 k-steps
+    (33, 4, 2, 128, 128),      # 16-17 rows: one 16-row MFMA tile and a one-row one
+])
+def test_mxfp4_row_tiled_sizes(T, E, k, H, F):
+    cfg = replace(CONFIGS["tiny"], T=T, E=E, k=k, H=H, F=F)
+    d = make_inputs(cfg, DEV, seed=T + 1, weights=False)
+    mx = make_mxfp4_weights(cfg, DEV, seed=T + 1)
+    _check(cfg, d, mx, "auto", what="mxfp4 tiled T=%d E=%d" % (T, E))
+
+
+def test_mxfp4_qwen3_235b_batch_sampled():
+    """Qwen3-235B batch (512 tokens, 32 routed rows per expert on average): row-tiled.  Every
+    token's routing is compared; the outputs of 3 tokens (the oracle dequantises each expert
+    they use on the host, about a second per expert at these dimensions)."""
+    cfg = CONFIGS["qwen3-235b-batch"]
+    d = make_inputs(cfg, DEV, seed=11, weights=False)
+    mx = make_mxfp4_weights(cfg, DEV, seed=11)
+    _check(cfg, d, mx, "auto", sample_tokens(cfg.T, 3), "mxfp4 qwen3-235b batch")
+
+
+def test_mxfp4_skewed_grouped_routing():
+    """DeepSeek-V3 routing on reduced dimensions: hundreds of rows on the hottest experts,
+    a few on the coldest, one 64-row tile to many per expert."""
+    cfg = replace(CONFIGS["ds-v3-grouped-prefill"], T=1024, H=256, F=128)
+    d = make_inputs(cfg, DEV, seed=12, weights=False)
+    mx = make_mxfp4_weights(cfg, DEV, seed=12)
+    _check(cfg, d, mx, "auto", sample_tokens(cfg.T, 96), "mxfp4 ds-v3 routing")

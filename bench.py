@@ -162,7 +162,7 @@ def main():
                                   d["w_gate_up_scale"], d["w_down"], d["w_down_scale"], cfg.k,
                                   d["correction_bias"], cfg.scoring, cfg.renormalize,
                                   cfg.num_expert_group, cfg.topk_group, cfg.rsf, out=out,
-                                  workspace=ws)
+                                  workspace=ws, path=args.path)
         elif mx:
             moe.fused_moe_mxfp4_fwd(d["hidden_states"], d["gating_output"], d["w_gate_up_q"],
                                     d["w_gate_up_scale"], d["w_down_q"], d["w_down_scale"],

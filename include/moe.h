@@ -321,7 +321,12 @@ int fused_moe_mxfp4_stage(int stage, const uint16_t *hidden_states, const uint8_
  * rows); the weighted combine of fused_moe_fwd.  Needs p->dtype == MOE_DTYPE_BF16,
  * H % 128 == 0, F % 128 == 0, no shared expert; 16-byte aligned hidden_states, weights, out
  * and workspace, 4-byte aligned scales.
- * Workspace: fused_moe_fp8_workspace_bytes(p) bytes.
+ * p->path: MOE_PATH_DIRECT computes the same values with no align and no quantiser launches:
+ * each GEMM reads the routes from topk_ids and quantises its own rows by the same rule (the
+ * decoding form for a few tokens).  It needs T*k <= 64 and H, F multiples of 256 small enough
+ * for one workgroup's LDS to hold 16 quantised rows (K up to 9472), else MOE_ERR_UNSUPPORTED.
+ * AUTO takes it when it is allowed and T*k <= 8*E; SORTED never.
+ * Workspace: fused_moe_fp8_workspace_bytes(p) bytes (depends on the path taken).
  * Errors: as fused_moe_fwd. */
 size_t fused_moe_fp8_workspace_bytes(const moe_params_t *p);
 int fused_moe_fp8_fwd(const uint16_t *hidden_states, const float *gating_output,
@@ -332,9 +337,10 @@ int fused_moe_fp8_fwd(const uint16_t *hidden_states, const float *gating_output,
                       size_t workspace_bytes, void *stream);
 
 /* fused_moe_fp8_stage -- one step of fused_moe_fp8_fwd's expert part with the routing given:
- * MOE_STAGE_ALIGN (expert order and the quantised routed x rows), MOE_STAGE_GATE_UP,
- * MOE_STAGE_DOWN (h quantised, then the down GEMM), MOE_STAGE_COMBINE, in that order, enqueue
- * exactly the expert kernels of the fused call.  A stage checks only the pointers it reads.
+ * MOE_STAGE_ALIGN (expert order and the quantised routed x rows; direct path: nothing),
+ * MOE_STAGE_GATE_UP, MOE_STAGE_DOWN (h quantised, then the down GEMM), MOE_STAGE_COMBINE, in
+ * that order, enqueue exactly the expert kernels of the fused call.  A stage checks only the
+ * pointers it reads (hidden_states: ALIGN on the sorted path, GATE_UP on the direct one).
  * MOE_STAGE_SHARED: MOE_ERR_UNSUPPORTED. */
 int fused_moe_fp8_stage(int stage, const uint16_t *hidden_states, const uint8_t *w_gate_up,
                         const float *w_gate_up_scale, const uint8_t *w_down,

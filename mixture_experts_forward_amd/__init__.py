@@ -574,10 +574,11 @@ def fused_moe_fp8_fwd(hidden_states, gating_output, w_gate_up, w_gate_up_scale, 
                       w_down_scale, top_k, correction_bias=None, scoring="softmax",
                       renormalize=True, num_expert_group=1, topk_group=1,
                       routed_scaling_factor=1.0, out=None, workspace=None,
-                      return_routing=False):
+                      return_routing=False, path="auto"):
     """The fused pass with FP8 expert weights: w_gate_up [E,2F,H] / w_down [E,H,F] e4m3
     (torch.float8_e4m3fn or uint8 codes) with f32 scales [E,2F/128,H/128] / [E,H/128,F/128];
-    bf16 activations quantised per 1 x 128 group on the way in."""
+    bf16 activations quantised per 1 x 128 group on the way in.  path: "direct" (T*k <= 64:
+    no align and no quantiser launches), "sorted", or "auto"."""
     T, H = hidden_states.shape
     codes = lambda t: t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t
     wgu, wd = codes(w_gate_up), codes(w_down)
@@ -593,7 +594,7 @@ def fused_moe_fp8_fwd(hidden_states, gating_output, w_gate_up, w_gate_up_scale, 
     if correction_bias is not None:
         _check(correction_bias, "correction_bias", torch.float32, (E,), dev)
     p = make_params(T, H, E, F, top_k, scoring, renormalize, num_expert_group, topk_group,
-                    routed_scaling_factor)
+                    routed_scaling_factor, path)
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     _check(out, "out", torch.bfloat16, (T, H), dev)

@@ -441,19 +441,31 @@ int fused_moe_mxfp4_fwd(const uint16_t *hidden_states, const float *gating_outpu
 
 // ---- the FP8 pass: routed rows quantised per 1 x 128 group, block-scaled FP8 expert GEMMs on
 // the contiguous (tight, expert-ordered) layout
+// The direct form (T * k <= 64 routes, one launch per GEMM straight from topk_ids) or the
+// sorted one (align, quantisers, contiguous GEMMs).
 struct Fp8Pass {
     int T, H, E, F, k, P;
+    bool direct;
     size_t off_ids, off_weights, off_sorted, off_offsets, off_tile_expert, off_inverse,
-        off_n_tiles, off_align, off_aq, off_as, off_gu, off_hq, off_hs, off_y, total;
+        off_n_tiles, off_align, off_aq, off_as, off_gu, off_hq, off_hs, off_h, off_y, total;
 };
 
-// One stage of the FP8 pass's expert part (the routing in ids / weights).
+constexpr int kFp8DirectMaxRoutes = 64;
+
+static bool fp8_direct_fits(const moe_params_t *p)
+{
+    return p->num_tokens * p->top_k <= kFp8DirectMaxRoutes &&
+           moe::fp8_direct_shape_ok(p->hidden) && moe::fp8_direct_shape_ok(p->inter);
+}
+
 static int fp8_check(const moe_params_t *p)
 {
     int st = moe::check_dims(p);
     if (st != MOE_OK)
         return st;
     if (p->dtype != MOE_DTYPE_BF16 || p->hidden % 128 != 0 || p->inter % 128 != 0)
+        return MOE_ERR_UNSUPPORTED;
+    if (p->path == MOE_PATH_DIRECT && p->num_tokens > 0 && !fp8_direct_fits(p))
         return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
@@ -466,6 +478,9 @@ static void fp8_plan(const moe_params_t *p, Fp8Pass *f)
     f->F = p->inter;
     f->k = p->top_k;
     f->P = f->T * f->k;
+    // AUTO: direct while the routes are few, both absolutely and per expert
+    f->direct = p->path == MOE_PATH_DIRECT ||
+                (p->path == MOE_PATH_AUTO && fp8_direct_fits(p) && f->P <= 8 * f->E);
     size_t o = 0;
     auto take = [&](size_t bytes) {
         const size_t at = o;
@@ -475,6 +490,16 @@ static void fp8_plan(const moe_params_t *p, Fp8Pass *f)
     const size_t P = f->P;
     f->off_ids = take(P * 4);
     f->off_weights = take(P * 4);
+    if (f->direct) {
+        f->off_sorted = f->off_offsets = f->off_tile_expert = f->off_inverse = 0;
+        f->off_n_tiles = f->off_align = f->off_aq = f->off_as = f->off_gu = 0;
+        f->off_hq = f->off_hs = 0;
+        f->off_h = take(P * f->F * 2);
+        f->off_y = take(P * f->H * 2);
+        f->total = o;
+        return;
+    }
+    f->off_h = 0;
     f->off_sorted = take(P * 4);                      // block_m 1: no padding slots
     f->off_offsets = take((size_t)(f->E + 1) * 4);
     f->off_tile_expert = take((P + f->E) * 4);
@@ -491,10 +516,30 @@ static void fp8_plan(const moe_params_t *p, Fp8Pass *f)
     f->total = o;
 }
 
+// One stage of the FP8 pass's expert part (the routing in ids / weights).
 static void fp8_stage(int stage, const Fp8Pass &f, const uint16_t *hidden, const uint8_t *w_gu,
                const float *s_gu, const uint8_t *w_d, const float *s_d, const int32_t *ids,
                const float *weights, uint16_t *out, void *ws, hipStream_t s)
 {
+    if (f.direct) {
+        uint16_t *h = ws_at<uint16_t>(ws, f.off_h);
+        uint16_t *y = ws_at<uint16_t>(ws, f.off_y);
+        switch (stage) {
+        case MOE_STAGE_GATE_UP:
+            moe::launch_fp8_direct(true, hidden, ids, f.P, f.k, f.E, w_gu, s_gu, f.F, f.H, h, s);
+            break;
+        case MOE_STAGE_DOWN:
+            moe::launch_fp8_direct(false, h, ids, f.P, f.k, f.E, w_d, s_d, f.H, f.F, y, s);
+            break;
+        case MOE_STAGE_COMBINE:  // y row of route (t, j) is t * k + j
+            moe::launch_combine(y, ids, weights, nullptr, out, f.T, f.H, f.k, f.E,
+                                MOE_DTYPE_BF16, s);
+            break;
+        default:  // MOE_STAGE_ALIGN: nothing to do
+            break;
+        }
+        return;
+    }
     int32_t *sorted = ws_at<int32_t>(ws, f.off_sorted);
     int32_t *offsets = ws_at<int32_t>(ws, f.off_offsets);
     int32_t *inverse = ws_at<int32_t>(ws, f.off_inverse);
@@ -690,13 +735,14 @@ int fused_moe_fp8_stage(int stage, const uint16_t *hidden_states, const uint8_t 
         return MOE_ERR_UNSUPPORTED;
     if (p->num_tokens == 0)
         return MOE_OK;
-    if (!workspace || !topk_ids || (stage == MOE_STAGE_ALIGN && !hidden_states) ||
+    Fp8Pass f;
+    fp8_plan(p, &f);
+    const int x_stage = f.direct ? MOE_STAGE_GATE_UP : MOE_STAGE_ALIGN;
+    if (!workspace || !topk_ids || (stage == x_stage && !hidden_states) ||
         (stage == MOE_STAGE_GATE_UP && (!w_gate_up || !w_gate_up_scale)) ||
         (stage == MOE_STAGE_DOWN && (!w_down || !w_down_scale)) ||
         (stage == MOE_STAGE_COMBINE && (!topk_weights || !out)))
         return MOE_ERR_NULL;
-    Fp8Pass f;
-    fp8_plan(p, &f);
     if (workspace_bytes < f.total)
         return MOE_ERR_WORKSPACE;
     if (!aligned16(workspace) || (hidden_states && !aligned16(hidden_states)) ||

@@ -38,7 +38,9 @@
 #include <type_traits>
 
 #include "moe_device.h"
+#include "moe_fp8_quant.h"
 #include "moe_wide_kernel.h"
+#include "moe_ws_kernel.h"
 
 namespace moe_fp8 {
 
@@ -716,6 +718,289 @@ __global__ __launch_bounds__(moe_wide::kThreads) void k_fp8_wide(Fp8Problem p, i
             packed.y = moe_pack_bf16x2(acc[m][n][2], acc[m][n][3]);
             *reinterpret_cast<moe_u32x2 *>(orow + col) = packed;
         }
+    }
+}
+
+// ---------------------------------------------------------------- direct form (a few tokens)
+// The FP8 pass for T * k <= 64 routes without the align and quantiser launches (aiter MI308
+// decoding PR, "Changes": direct decoding from topk_ids): one workgroup per (column block,
+// route); the first route of an expert gathers every route of that expert (the others leave),
+// so an expert's weights are streamed once.  The workgroup quantises its rows itself, per
+// 1 x 128 group exactly as k_quant_fp8 does (16 lanes per group, s = amax / 448, the same
+// encoder), into an LDS copy of the rows (RL per pass, row r's 16-byte chunk c at position
+// c ^ r, so the B-operand reads of several rows at one chunk hit distinct banks) with their
+// scales.  RL (1..16) is the most rows an expert can hold in one pass: min(16, T) when every
+// token's experts are distinct, so at decode sizes the LDS copy is a few rows and several
+// workgroups share a CU; an expert with more rows takes more passes.  The MFMA's B columns
+// past RL read row 0, and their results are never stored.
+// Weights, block scaling and the K split are k_fp8_ws's.
+//   gate-up: rows are x[route / k]; the workgroup's NT gate tiles and the NT up tiles of the
+//     same columns; out h[route] = bf16(SiLU(g) * u) with g and u first rounded to bf16 (the
+//     values the two-kernel form stores and its quantiser reads);
+//   down: rows are h[route]; out y[route] = bf16(sum).
+struct Fp8Direct {
+    const uint16_t *act;      // gate-up: x [T, K]; down: h [P, K] bf16
+    const int32_t *topk_ids;  // [P]
+    const uint8_t *b;         // [E, rows_b, K] e4m3
+    const float *b_scale;     // [E, rows_b / 128, KB]
+    uint16_t *out;            // [P, n_out] bf16
+    int P, top_k, E, n_out, K, KB, NB;  // NB = rows_b / 128 (rows_b = 2 n_out for gate-up)
+    int RL;                             // rows per pass, 1..16
+};
+
+// LDS bytes of the direct form: RL rows of K codes, their scales, the K-split partial sums
+// and (SEG 2) the per-wave transpose buffers.
+__host__ __device__ inline size_t fp8_direct_lds(int K, int NW, int KSPLIT, int SEG, int RL)
+{
+    return (size_t)RL * K + (size_t)RL * (K / 128) * 4 +
+           (size_t)(KSPLIT > 1 ? KSPLIT - 1 : 1) * NW * 64 * 16 +
+           (SEG > 1 ? (size_t)KSPLIT * NW * 256 * 16 : 0);
+}
+
+template <bool GATE_UP, int NT, int KSPLIT, int STAGES, int SEG>
+__global__ __launch_bounds__(64 * KSPLIT) void k_fp8_direct(Fp8Direct d)
+{
+    static_assert(SEG == 1 || SEG == 2, "one- or two-k-step segments");
+    constexpr int NW = GATE_UP ? 2 * NT : NT;  // 16-row weight tiles per k-step
+    extern __shared__ moe_u32x4 s_dyn[];
+    const int lane = threadIdx.x & 63;
+    const int tid = threadIdx.x;
+    const int kw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int col0 = blockIdx.x * (16 * NT);
+    const int route0 = blockIdx.y;
+    const int K = d.K, KB = d.KB;
+
+    // ---- the expert of this route, and all routes of it (P <= 64: one id per lane)
+    const int e = d.topk_ids[route0];
+    if (e < 0 || e >= d.E)
+        return;
+    const int mine = lane < d.P ? d.topk_ids[lane] : -1;
+    const uint64_t members = __ballot(mine == e);
+    if (members & ((1ull << route0) - 1))
+        return;  // an earlier route of this expert owns it
+    const int n_rows = __popcll(members);
+
+    // ---- LDS: codes [RL][K], scales [RL][KB], K-split sums, transpose buffers
+    const int RL = d.RL;
+    uint8_t *s_codes = reinterpret_cast<uint8_t *>(s_dyn);
+    float *s_scale = reinterpret_cast<float *>(s_codes + (size_t)RL * K);
+    moe_f32x4 *s_red = reinterpret_cast<moe_f32x4 *>(s_scale + RL * KB);
+    moe_u32x4 *s_t = reinterpret_cast<moe_u32x4 *>(s_red + (KSPLIT > 1 ? KSPLIT - 1 : 1) * NW * 64);
+
+    const int rr = lane & 15, rq = lane >> 4;
+    const uint8_t *B = d.b + (size_t)e * (GATE_UP ? 2 * d.n_out : d.n_out) * K;
+    const uint8_t *wrow[NW];
+    int sb_base[NW];
+    bool tile_ok[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int c = col0 + 16 * nt;
+        tile_ok[nt] = c < d.n_out;
+        const int cc = tile_ok[nt] ? c : 0;
+#pragma unroll
+        for (int half = 0; half < (GATE_UP ? 2 : 1); ++half) {
+            const int row = cc + half * d.n_out;  // gate rows, then the up rows of the same columns
+            const int w = nt + half * NT;
+            wrow[w] = SEG == 1 ? B + (size_t)(row + rr) * K + 16 * rq
+                               : B + (size_t)(row + (lane >> 4)) * K + 16 * (lane & 15);
+            sb_base[w] = (e * d.NB + row / 128) * KB;
+        }
+    }
+    // K blocks of this wave (nseg segments of SEG blocks), visited from a rotated start
+    const int per = (KB + KSPLIT - 1) / KSPLIT;
+    const int kb0 = kw * per;
+    const int nk = max(0, min(KB, kb0 + per) - kb0);
+    const int nseg = nk / SEG;
+    const int rot =
+        nseg > 0 ? (int)((blockIdx.x * 7u + blockIdx.y * 13u) % (unsigned)nseg) : 0;
+    moe_u32x4 *tb = s_t + (SEG > 1 ? kw * NW * 256 : 0);
+    int wslot[2 * SEG], rslot[SEG][2];
+#pragma unroll
+    for (int j = 0; j < 2 * SEG; ++j) {
+        const int r = 4 * j + (lane >> 4);
+        wslot[j] = r * 16 + ((lane & 15) ^ r);
+    }
+#pragma unroll
+    for (int h = 0; h < SEG; ++h) {
+        rslot[h][0] = rr * 16 + ((8 * h + rq) ^ rr);
+        rslot[h][1] = rr * 16 + ((8 * h + 4 + rq) ^ rr);
+    }
+    const int rl = rr < RL ? rr : 0;  // this lane's B column reads LDS row rl
+    const moe_u32x4 *xrow = reinterpret_cast<const moe_u32x4 *>(s_codes + (size_t)rl * K);
+
+    moe_f32x4 acc[NW];
+    moe_u32x4 wv[STAGES][NW][2 * SEG];
+    float sb[STAGES][SEG][NW];
+    auto load = [&](int st, int i) {
+        const int kb = kb0 + ((i + rot) % nseg) * SEG;  // first K block of segment i
+        const int k = kb * 128;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            if (!tile_ok[w % NT])
+                continue;
+            if (SEG == 1) {
+                wv[st][w][0] = load_nt16(wrow[w] + k);
+                wv[st][w][1] = load_nt16(wrow[w] + k + 64);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 2 * SEG; ++j)
+                    wv[st][w][j] = load_nt16(wrow[w] + (size_t)(4 * j) * K + k);
+            }
+#pragma unroll
+            for (int h = 0; h < SEG; ++h)
+                sb[st][h][w] = d.b_scale[sb_base[w] + kb + h];
+        }
+    };
+    auto compute = [&](int st, int i) {
+        const int kb = kb0 + ((i + rot) % nseg) * SEG;
+        if (SEG > 1) {
+#pragma unroll
+            for (int w = 0; w < NW; ++w)
+                if (tile_ok[w % NT])
+#pragma unroll
+                    for (int j = 0; j < 2 * SEG; ++j)
+                        tb[w * 256 + wslot[j]] = wv[st][w][j];
+            moe_wave_sync();
+        }
+#pragma unroll
+        for (int h = 0; h < SEG; ++h) {
+            // bytes 16rq and 64 + 16rq of k-step kb + h of row rr: chunks 8(kb+h) + rq, + 4
+            const int c0 = 8 * (kb + h) + rq;
+            const moe_i32x8 bx = join(xrow[c0 ^ rl], xrow[(c0 + 4) ^ rl]);
+            const float sa = s_scale[rl * KB + kb + h];
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                if (!tile_ok[w % NT])
+                    continue;
+                const moe_i32x8 a = SEG == 1 ? join(wv[st][w][0], wv[st][w][1])
+                                             : join(tb[w * 256 + rslot[h][0]],
+                                                    tb[w * 256 + rslot[h][1]]);
+                const moe_f32x4 part = mfma_fp8_block(a, bx);
+                const float sscale = sa * sb[st][h][w];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    acc[w][q] = fmaf(part[q], sscale, acc[w][q]);
+            }
+        }
+        if (SEG > 1)
+            moe_wave_sync();  // this wave's transpose reads finish before its next writes
+    };
+    // the first segments of the weight stream go out before the rows are quantised: they do
+    // not depend on them
+    auto prologue = [&] {
+#pragma unroll
+        for (int st = 0; st < STAGES - 1; ++st)
+            if (st < nseg)
+                load(st, st);
+    };
+    prologue();
+
+    for (int pass0 = 0; pass0 < n_rows; pass0 += RL) {
+        // ---- quantise the pass's real rows: 16 lanes per (row, 1 x 128 group).  Rows past
+        // n_rows keep whatever LDS holds: an output element reads only its own row's codes and
+        // scale, and those rows are never written out.
+        const int nr = min(RL, n_rows - pass0);
+        for (int gi = tid / 16; gi < nr * KB; gi += 4 * KSPLIT) {
+            const int r = gi / KB, g = gi % KB, sub = tid & 15;
+            const int route = moe_ws::nth_set_bit(members, pass0 + r);
+            const int src = GATE_UP ? route / d.top_k : route;
+            float v[8];
+            const moe_u32x4 raw = *reinterpret_cast<const moe_u32x4 *>(
+                d.act + (size_t)src * K + 128 * g + 8 * sub);
+            const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[2 * i] = __uint_as_float(w4[i] << 16);
+                v[2 * i + 1] = __uint_as_float(w4[i] & 0xFFFF0000u);
+            }
+            float amax = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+            for (int dd = 1; dd < 16; dd <<= 1)
+                amax = fmaxf(amax, __shfl_xor(amax, dd, 16));
+            const float sc = amax == 0.0f ? 1.0f : amax / 448.0f;
+            if (sub == 0)
+                s_scale[r * KB + g] = sc;
+            uint32_t lo = 0, hi = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                lo |= moe::e4m3_code(v[i] / sc) << (8 * i);
+                hi |= moe::e4m3_code(v[4 + i] / sc) << (8 * i);
+            }
+            const int chunk = 8 * g + (sub >> 1);  // this lane's 8 codes: half (sub & 1) of it
+            moe_u32x2 packed;
+            packed.x = lo;
+            packed.y = hi;
+            *reinterpret_cast<moe_u32x2 *>(s_codes + (size_t)r * K + 16 * (chunk ^ r) +
+                                           8 * (sub & 1)) = packed;
+        }
+        __syncthreads();  // the pass's codes and scales are in LDS
+
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+            acc[w] = moe_f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < nseg; i += STAGES) {
+#pragma unroll
+            for (int st = 0; st < STAGES; ++st) {
+                const int cur = i + st;
+                if (cur < nseg) {
+                    const int nxt = cur + STAGES - 1;
+                    if (nxt < nseg)
+                        load((st + STAGES - 1) % STAGES, nxt);
+                    compute(st, cur);
+                }
+            }
+        }
+
+        // ---- fixed-order sum over the K-split waves
+        if (KSPLIT > 1) {
+            __syncthreads();
+            if (kw > 0) {
+#pragma unroll
+                for (int w = 0; w < NW; ++w)
+                    s_red[((kw - 1) * NW + w) * 64 + lane] = acc[w];
+            }
+            __syncthreads();
+            if (kw == 0) {
+#pragma unroll
+                for (int v = 0; v < KSPLIT - 1; ++v)
+#pragma unroll
+                    for (int w = 0; w < NW; ++w)
+                        acc[w] += s_red[(v * NW + w) * 64 + lane];
+            }
+        }
+
+        // ---- epilogue (wave 0): lane holds columns 4*(lane/16)+q of row pass0 + lane%16
+        const int s = pass0 + rr;
+        if (kw == 0 && rr < RL && s < n_rows) {
+            const int route = moe_ws::nth_set_bit(members, s);
+            uint16_t *orow = d.out + (size_t)route * d.n_out;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                if (!tile_ok[nt])
+                    continue;
+                float v[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (GATE_UP) {
+                        const float g = moe_bf16_to_f32(moe_f32_to_bf16(acc[nt][q]));
+                        const float u = moe_bf16_to_f32(moe_f32_to_bf16(acc[NT + nt][q]));
+                        v[q] = g / (1.0f + __expf(-g)) * u;
+                    } else {
+                        v[q] = acc[nt][q];
+                    }
+                }
+                moe_u32x2 packed;
+                packed.x = moe_pack_bf16x2(v[0], v[1]);
+                packed.y = moe_pack_bf16x2(v[2], v[3]);
+                *reinterpret_cast<moe_u32x2 *>(orow + col0 + 16 * nt + 4 * rq) = packed;
+            }
+        }
+        if (pass0 + RL < n_rows)
+            prologue();   // the next pass's weight stream
+        __syncthreads();  // the next pass overwrites the codes, scales and sums
     }
 }
 

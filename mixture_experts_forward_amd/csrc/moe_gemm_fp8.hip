@@ -4,6 +4,8 @@
 // fewer than two workgroups per CU, 128 columns per workgroup); the 64-row form also when K is
 // not a multiple of 512 or a_scale is not 16-byte aligned.  Tile shapes measured on MI355X on
 // the page's decode shapes.
+#include <algorithm>
+
 #include "moe_fp8_kernel.h"
 #include "moe_internal.h"
 
@@ -62,9 +64,78 @@ int device_cus()
     return n;
 }
 
+template <bool GATE_UP, int NT, int KSPLIT, int STAGES, int SEG>
+void launch_direct_one(const moe_fp8::Fp8Direct &d, hipStream_t stream)
+{
+    constexpr int NW = GATE_UP ? 2 * NT : NT;
+    const size_t lds = moe_fp8::fp8_direct_lds(d.K, NW, KSPLIT, SEG, d.RL);
+    const auto kernel = moe_fp8::k_fp8_direct<GATE_UP, NT, KSPLIT, STAGES, SEG>;
+    static const bool attr = [&] {
+        return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   (int)moe::kFp8DirectMaxLds) == hipSuccess;
+    }();
+    (void)attr;
+    const dim3 grid((d.n_out + 16 * NT - 1) / (16 * NT), d.P);
+    hipLaunchKernelGGL(kernel, grid, dim3(64 * KSPLIT), lds, stream, d);
+}
+
 }  // namespace
 
 namespace moe {
+
+// The shapes of the direct form: gate-up one gate and one up tile per workgroup, K split over
+// four waves; down two tiles, K split over four waves from 16 K blocks up, else two.  Rows of
+// a 1 KB multiple give each of four waves an even count of K blocks: two-k-step weight
+// segments (256 contiguous bytes per row and load), where their transpose buffers fit in LDS.
+static bool direct_seg2(int K)
+{
+    return K % 1024 == 0 && moe_fp8::fp8_direct_lds(K, 2, 4, 2, 16) <= kFp8DirectMaxLds;
+}
+
+bool fp8_direct_shape_ok(int K)
+{
+    return K > 0 && K % 256 == 0 && fp8_direct_lds_bytes(K) <= kFp8DirectMaxLds;
+}
+
+size_t fp8_direct_lds_bytes(int K)
+{
+    return moe_fp8::fp8_direct_lds(K, 2, 4, direct_seg2(K) ? 2 : 1, 16);
+}
+
+void launch_fp8_direct(bool gate_up, const uint16_t *act, const int32_t *topk_ids, int P,
+                       int top_k, int E, const uint8_t *b, const float *b_scale, int n_out, int K,
+                       uint16_t *out, hipStream_t stream)
+{
+    moe_fp8::Fp8Direct d;
+    d.act = act;
+    d.topk_ids = topk_ids;
+    d.b = b;
+    d.b_scale = b_scale;
+    d.out = out;
+    d.P = P;
+    d.top_k = top_k;
+    d.E = E;
+    d.n_out = n_out;
+    d.K = K;
+    d.KB = K / 128;
+    d.NB = (gate_up ? 2 * n_out : n_out) / 128;
+    d.RL = std::min(16, std::max(1, P / top_k));  // an expert's rows, when a token's are distinct
+    const bool seg2 = direct_seg2(K);
+    if (gate_up) {
+        if (seg2)
+            launch_direct_one<true, 1, 4, 2, 2>(d, stream);
+        else
+            launch_direct_one<true, 1, 4, 3, 1>(d, stream);
+    } else {
+        if (seg2)
+            launch_direct_one<false, 2, 4, 2, 2>(d, stream);
+        else if (d.KB >= 16)
+            launch_direct_one<false, 2, 4, 3, 1>(d, stream);
+        else
+            launch_direct_one<false, 2, 2, 3, 1>(d, stream);
+    }
+}
 
 void launch_fp8_gemm(const uint8_t *a, const float *a_scale, const uint8_t *b,
                      const float *b_scale, const int32_t *masked_m, int E, int max_m, int N,

@@ -119,6 +119,17 @@ void launch_fp8_gemm_contig(const uint8_t *a, const float *a_scale, const uint8_
                             const float *b_scale, const int32_t *offsets, int E, int P, int N,
                             int K, uint16_t *out, hipStream_t stream);
 
+// The direct FP8 pass for T*k <= 64 routes (moe_fp8_kernel.h, k_fp8_direct): one launch per
+// GEMM reading the routes from topk_ids and quantising its own activation rows (gate-up: rows
+// x[route / top_k], out h[route] = bf16(SiLU(g) * u), n_out = F; down: rows h[route], out
+// y[route], n_out = H).  K % 256 == 0 and its LDS within kFp8DirectMaxLds (fp8_direct_shape_ok).
+constexpr size_t kFp8DirectMaxLds = 160 * 1024;
+size_t fp8_direct_lds_bytes(int K);
+bool fp8_direct_shape_ok(int K);
+void launch_fp8_direct(bool gate_up, const uint16_t *act, const int32_t *topk_ids, int P,
+                       int top_k, int E, const uint8_t *b, const float *b_scale, int n_out, int K,
+                       uint16_t *out, hipStream_t stream);
+
 // ---------------------------------------------------------------- fp8 activation quantiser
 // x [M, K] bf16 -> q [M, K] e4m3 codes, scale [M, ceil(K/128)] f32 (moe_quant.hip); K % 8 == 0.
 void launch_quant_fp8(const uint16_t *x, int M, int K, uint8_t *q, float *scale,

@@ -11,36 +11,12 @@
 // group's amax is a 16-lane butterfly of maxima.  HBM-bound: 2 bytes in, 1 + 4/128 out per
 // element.
 #include "moe_device.h"
+#include "moe_fp8_quant.h"
 #include "moe_internal.h"
 
 namespace {
 
 constexpr int kThreads = 256;
-
-// f32 -> e4m3 code, round to nearest even, magnitudes from 448 up saturate to 448 (0x7E), NaN
-// -> 0x7F.  Normal range (|v| >= 2^-6): the e4m3 code is the f32 exponent rebiased (127 -> 7)
-// and the top 3 mantissa bits, plus one when the 20 dropped bits are above half or exactly
-// half with an odd code (a carry out of the mantissa steps the exponent, which is the next
-// e4m3 value).  Below 2^-6 the codes are the subnormals m * 2^-9: m = rint(|v| * 512) (exact
-// scaling, rint rounds half to even; m = 8 is the code of 2^-6).
-__device__ __forceinline__ uint32_t e4m3_code(float v)
-{
-    const uint32_t bits = __float_as_uint(v);
-    const uint32_t sign = (bits >> 24) & 0x80u;
-    const float a = fabsf(v);
-    uint32_t code;
-    if (!(a < 448.0f)) {
-        code = a != a ? 0x7Fu : 0x7Eu;
-    } else if (a < 0.015625f) {
-        code = (uint32_t)rintf(a * 512.0f);
-    } else {
-        const uint32_t ab = __float_as_uint(a);
-        const uint32_t base = ((((ab >> 23) - 127u + 7u)) << 3) | ((ab >> 20) & 7u);
-        const uint32_t rest = ab & 0xFFFFFu;
-        code = base + ((rest > 0x80000u || (rest == 0x80000u && (base & 1u))) ? 1u : 0u);
-    }
-    return code | sign;
-}
 
 // Source rows: SRC_ROWS, row r of x; SRC_GATHER, row row_src[r] / div of x (row_src[r] < 0: a
 // zero row); SRC_SWIGLU, h = bf16( SiLU(x[r, k]) * x[r, K + k] ) of a gate-up row x [M, 2K].
@@ -108,8 +84,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_fp8(const uint16_t *__restri
     uint32_t lo = 0, hi = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        lo |= e4m3_code(v[i] / s) << (8 * i);
-        hi |= e4m3_code(v[4 + i] / s) << (8 * i);
+        lo |= moe::e4m3_code(v[i] / s) << (8 * i);
+        hi |= moe::e4m3_code(v[4 + i] / s) << (8 * i);
     }
     moe_u32x2 packed;
     packed.x = lo;

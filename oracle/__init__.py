@@ -24,6 +24,8 @@ Functions (each follows the passage cited in ``moe_oracle.c``):
   double_to_f16(values) -> uint16 binary16 bits (one rounding, nearest-even)
   fp8_forward(x, gating, w_gate_up, w_gate_up_scale, w_down, w_down_scale, ...)
       -> the FP8 pass (1 x 128 activation groups, 128 x 128 weight blocks) for ``tokens``
+  fp8_experts(x, w_gate_up, w_gate_up_scale, w_down, w_down_scale, topk_ids, topk_weights)
+      -> its expert part with the routing given
   mxfp4_dequant(q, scale) -> float64 weights of MXFP4 codes and E8M0 block scales
   mxfp4_to_bf16(q, scale) -> the same values as bf16 bits (exact)
 """
@@ -282,17 +284,29 @@ def fp8_forward(x, gating, w_gate_up, w_gate_up_scale, w_down, w_down_scale, bia
                 scoring="softmax", renormalize=True, num_expert_group=1, topk_group=1, rsf=1.0,
                 tokens=None):
     """The MoE pass with FP8 expert weights (e4m3 codes with f32 scales per 128 x 128 block),
-    step by step: route; each routed x row quantised per 1 x 128 group (quant_fp8_1x128); per
-    expert the gate-up block-scaled GEMM (grouped_gemm_fp8_contiguous), rounded to bf16; h =
-    bf16(SiLU(gate) * up) (reading: h is stored in bf16 before it is quantised, as the 16-bit
-    passes store it) quantised the same way; the down GEMM; out[t] = bf16(sum_j w_j y_j) from the
-    unrounded down sums.  x [T,H] bf16 bits; returns (topk_ids, topk_weights, out [n,H] bf16
-    bits) for ``tokens`` (default all)."""
+    step by step: route, then fp8_experts.  x [T,H] bf16 bits; returns (topk_ids, topk_weights,
+    out [n,H] bf16 bits) for ``tokens`` (default all)."""
+    ids, w = route(gating, bias, k, scoring, renormalize, num_expert_group, topk_group, rsf)
+    return ids, w, fp8_experts(x, w_gate_up, w_gate_up_scale, w_down, w_down_scale, ids, w,
+                               tokens)
+
+
+def fp8_experts(x, w_gate_up, w_gate_up_scale, w_down, w_down_scale, topk_ids, topk_weights,
+                tokens=None):
+    """The expert part of the FP8 pass with the routing given (topk_ids [T,k] int32, ids outside
+    [0,E) skipped, repeats allowed; topk_weights [T,k] f32): each routed x row quantised per
+    1 x 128 group (quant_fp8_1x128); per expert the gate-up block-scaled GEMM
+    (grouped_gemm_fp8_contiguous), rounded to bf16; h = bf16(SiLU(gate) * up) (reading: h is
+    stored in bf16 before it is quantised, as the 16-bit passes store it) quantised the same
+    way; the down GEMM; out[t] = bf16(sum_j w_j y_j) from the unrounded down sums.  Returns out
+    [n,H] bf16 bits for ``tokens`` (default all)."""
     x = _c(x, np.uint16)
+    ids = np.asarray(topk_ids)
+    w = np.asarray(topk_weights)
     T, H = x.shape
+    k = ids.shape[1]
     E, F2 = w_gate_up.shape[0], w_gate_up.shape[1]
     F = F2 // 2
-    ids, w = route(gating, bias, k, scoring, renormalize, num_expert_group, topk_group, rsf)
     tok = np.arange(T) if tokens is None else np.asarray(tokens, np.int64)
     routes = [(int(t), j) for t in tok for j in range(k) if 0 <= ids[t, j] < E]
     order = sorted(range(len(routes)), key=lambda i: (ids[routes[i][0], routes[i][1]], i))
@@ -316,7 +330,7 @@ def fp8_forward(x, gating, w_gate_up, w_gate_up_scale, w_down, w_down_scale, bia
         for j in range(k):
             if (t, j) in row_of:
                 acc[i] += float(w[t, j]) * y[row_of[(t, j)]]
-    return ids, w, double_to_bf16(acc)
+    return double_to_bf16(acc)
 
 
 def mxfp4_dequant(q, scale):

@@ -229,6 +229,33 @@ def test_mxfp4_entry_points_reject_before_launch():
     assert call(moe.make_params(0, 2048, 128, 768, 8), None, 0) == 0             # T = 0
 
 
+def test_fp8_pass_path_rules():
+    """The FP8 pass's direct form: chosen by AUTO for a few routes, refused past 64 routes or
+    for K that is not a multiple of 256 or too long for one workgroup's LDS."""
+    L = moe.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    ws = lambda p: L.fused_moe_fp8_workspace_bytes(ctypes.byref(p))
+    call = lambda p: L.fused_moe_fp8_fwd(fake, fake, fake, fake, fake, fake, None,
+                                         ctypes.byref(p), fake, None, None, fake, 1 << 40, None)
+    # T = 1, k = 8 at Qwen3-30B-A3B dimensions: direct, ids / weights / h / y only
+    d = ws(moe.make_params(1, 2048, 128, 768, 8))
+    assert d == 2 * 256 + 8 * 768 * 2 + 8 * 2048 * 2
+    assert ws(moe.make_params(1, 2048, 128, 768, 8, path="direct")) == d
+    assert ws(moe.make_params(1, 2048, 128, 768, 8, path="sorted")) > d
+    # AUTO keeps the sorted form past 64 routes or 8 routes per expert
+    assert ws(moe.make_params(9, 2048, 128, 768, 8)) > 9 * 8 * (768 + 2048) * 2 + 512
+    assert ws(moe.make_params(8, 256, 4, 256, 8)) == \
+        ws(moe.make_params(8, 256, 4, 256, 8, path="sorted"))
+    # DIRECT refused: 65 routes, K % 256 != 0 (F = 384), K past the LDS limit (H = 9728)
+    assert call(moe.make_params(65, 2048, 128, 768, 1, path="direct")) == -3
+    assert call(moe.make_params(2, 2048, 128, 384, 8, path="direct")) == -3
+    assert call(moe.make_params(2, 9728, 128, 768, 8, path="direct")) == -3
+    assert ws(moe.make_params(65, 2048, 128, 768, 1, path="direct")) == 0
+    # the same shapes on AUTO fall to the sorted form
+    assert ws(moe.make_params(2, 2048, 128, 384, 8)) == \
+        ws(moe.make_params(2, 2048, 128, 384, 8, path="sorted"))
+
+
 def test_stream_read_rejects_before_launch():
     """The streaming-read measurement validates its arguments before any HIP call."""
     L = moe.lib()

@@ -32,6 +32,7 @@ static_assert(kThreads == moe::kAlignChunk, "a chunk of the chunked align is one
 struct AlignSmem {
     int count[kMaxExperts];
     int base[kMaxExperts];
+    int first[kMaxExperts];  // expert's first row (its segment start)
     uint32_t hist[kWaves][kMaxExperts / 2];  // two 16-bit counters per word
     alignas(16) int round_ids[kThreads];
     int wave_total[kWaves];
@@ -111,7 +112,8 @@ __device__ __forceinline__ void scan_layout(int E, int bm, int slots, int tiles_
                                             int32_t *__restrict__ offsets,
                                             int32_t *__restrict__ tile_expert,
                                             int32_t *__restrict__ n_tiles,
-                                            moe::TileSchedule *__restrict__ sched, AlignSmem &sm)
+                                            moe::TileSchedule *__restrict__ sched, bool balanced,
+                                            AlignSmem &sm)
 {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -130,6 +132,7 @@ __device__ __forceinline__ void scan_layout(int E, int bm, int slots, int tiles_
     if (tid < E) {
         offsets[tid] = excl;
         sm.base[tid] = excl;
+        sm.first[tid] = excl;
     }
     if (tid == E - 1) {
         offsets[E] = incl;
@@ -143,8 +146,18 @@ __device__ __forceinline__ void scan_layout(int E, int bm, int slots, int tiles_
     for (int e = wv; e < E; e += kWaves) {
         const int b = sm.base[e], ce = sm.count[e];
         const int pe = (ce + bm - 1) / bm * bm;
-        for (int s = b + ce + lane; s < b + pe; s += 64)
-            sorted_ids[s] = -1;
+        if (balanced && ce > 0) {
+            // tile j's rows are a prefix of it: q + 1 rows in the first rem tiles, q after
+            const int te = pe / bm, q = ce / te, rem = ce % te;
+            for (int j = 0; j < te; ++j) {
+                const int t0 = b + j * bm;
+                for (int s = t0 + q + (j < rem ? 1 : 0) + lane; s < t0 + bm; s += 64)
+                    sorted_ids[s] = -1;
+            }
+        } else {
+            for (int s = b + ce + lane; s < b + pe; s += 64)
+                sorted_ids[s] = -1;
+        }
         for (int i = b / bm + lane; i < (b + pe) / bm; i += 64)
             tile_expert[i] = e;
     }
@@ -155,11 +168,26 @@ __device__ __forceinline__ void scan_layout(int E, int bm, int slots, int tiles_
         tile_expert[i] = -1;
 }
 
+// Row of an expert's route of rank p (0-based, in route order) in the balanced layout: the
+// expert's ce routes fill its te = ceil(ce / bm) tiles as evenly as they can (the first
+// ce % te tiles one row more), each tile's rows a prefix of it.
+__device__ __forceinline__ int balanced_row(int first, int p, int ce, int bm)
+{
+    const int te = (ce + bm - 1) / bm;
+    const int q = ce / te, rem = ce % te;
+    const int big = (q + 1) * rem;  // routes in the first rem tiles
+    const int j = p < big ? p / (q + 1) : rem + (p - big) / q;
+    const int start = p < big ? j * (q + 1) : big + (j - rem) * q;
+    return first + j * bm + (p - start);
+}
+
 // Stable scatter of routes [r0, r0 + 1024): route r of expert e goes to row sm.base[e] + (its
-// rank among this round's routes of e).  With advance, sm.base moves past the round's routes.
-// sm.hist must be zero on entry and is zero again on return.
+// rank among this round's routes of e), or with bal (the tile height) to the balanced row of
+// that rank (sm.first and sm.count: the expert's first row and route count).  With advance,
+// sm.base moves past the round's routes.  sm.hist must be zero on entry and is zero again on
+// return.
 __device__ __forceinline__ void scatter_round(const int32_t *__restrict__ ids, int P, int E,
-                                              int r0, bool advance,
+                                              int r0, bool advance, int bal,
                                               int32_t *__restrict__ sorted_ids,
                                               int32_t *__restrict__ inverse, AlignSmem &sm)
 {
@@ -192,7 +220,9 @@ __device__ __forceinline__ void scatter_round(const int32_t *__restrict__ ids, i
         int before = 0;
         for (int w = 0; w < wv; ++w)
             before += (sm.hist[w][e >> 1] >> ((e & 1) * 16)) & 0xffff;
-        const int pos = sm.base[e] + before + rank;
+        int pos = sm.base[e] + before + rank;
+        if (bal)
+            pos = balanced_row(sm.first[e], pos - sm.first[e], sm.count[e], bal);
         sorted_ids[pos] = r;
         inverse[r] = pos;
     } else if (r < P) {
@@ -219,7 +249,8 @@ __device__ __forceinline__ void align_block(const int32_t *__restrict__ ids, int
                                             int32_t *__restrict__ tile_expert,
                                             int32_t *__restrict__ inverse,
                                             int32_t *__restrict__ n_tiles,
-                                            moe::TileSchedule *__restrict__ sched, AlignSmem &sm)
+                                            moe::TileSchedule *__restrict__ sched, bool balanced,
+                                            AlignSmem &sm)
 {
     const int tid = threadIdx.x;
     const int half_words = (E + 1) / 2;
@@ -234,9 +265,10 @@ __device__ __forceinline__ void align_block(const int32_t *__restrict__ ids, int
             atomicAdd(&sm.count[e], 1);
     }
     __syncthreads();
-    scan_layout(E, bm, slots, tiles_cap, sorted_ids, offsets, tile_expert, n_tiles, sched, sm);
+    scan_layout(E, bm, slots, tiles_cap, sorted_ids, offsets, tile_expert, n_tiles, sched,
+                balanced, sm);
     for (int r0 = 0; r0 < P; r0 += kThreads)
-        scatter_round(ids, P, E, r0, true, sorted_ids, inverse, sm);
+        scatter_round(ids, P, E, r0, true, balanced ? bm : 0, sorted_ids, inverse, sm);
 }
 
 // Chunked driver, launch 1: histogram of chunk b (routes [1024b, 1024b + 1024)) into
@@ -261,8 +293,9 @@ __global__ __launch_bounds__(kThreads) void k_align_hist(const int32_t *__restri
 }
 
 // Chunked driver, launch 2 (one workgroup): per-expert totals and the padded layout;
-// counts[b*E + e] becomes the number of expert e's routes in chunks before b.  The counts are
-// read 16 chunks at a time so that their loads overlap.
+// counts[b*E + e] becomes the number of expert e's routes in chunks before b (balanced: and
+// counts[chunks*E + e] its total).  The counts are read 16 chunks at a time so that their
+// loads overlap.
 __global__ __launch_bounds__(kThreads) void k_align_scan(int32_t *__restrict__ counts,
                                                          int chunks, int E, int bm, int slots,
                                                          int tiles_cap,
@@ -270,7 +303,8 @@ __global__ __launch_bounds__(kThreads) void k_align_scan(int32_t *__restrict__ c
                                                          int32_t *__restrict__ offsets,
                                                          int32_t *__restrict__ tile_expert,
                                                          int32_t *__restrict__ n_tiles,
-                                                         moe::TileSchedule *__restrict__ sched)
+                                                         moe::TileSchedule *__restrict__ sched,
+                                                         int balanced)
 {
     constexpr int kBatch = 16;
     __shared__ AlignSmem sm;
@@ -290,40 +324,48 @@ __global__ __launch_bounds__(kThreads) void k_align_scan(int32_t *__restrict__ c
             }
         }
         sm.count[tid] = run;
+        if (balanced)
+            counts[(size_t)chunks * E + tid] = run;
     }
     __syncthreads();
-    scan_layout(E, bm, slots, tiles_cap, sorted_ids, offsets, tile_expert, n_tiles, sched, sm);
+    scan_layout(E, bm, slots, tiles_cap, sorted_ids, offsets, tile_expert, n_tiles, sched,
+                balanced != 0, sm);
 }
 
-// Chunked driver, launch 3: the round of chunk b, its routes of expert e starting at row
-// expert_offsets[e] + (routes of e in earlier chunks).
+// Chunked driver, launch 3: the round of chunk b, its routes of expert e starting at rank
+// (routes of e in earlier chunks) of the expert's rows from expert_offsets[e] on (bal: the
+// tile height of the balanced layout, whose totals follow the chunk table).
 __global__ __launch_bounds__(kThreads) void k_align_scatter(const int32_t *__restrict__ ids,
-                                                            int P, int E,
+                                                            int P, int E, int chunks,
                                                             const int32_t *__restrict__ counts,
                                                             const int32_t *__restrict__ offsets,
                                                             int32_t *__restrict__ sorted_ids,
-                                                            int32_t *__restrict__ inverse)
+                                                            int32_t *__restrict__ inverse,
+                                                            int bal)
 {
     __shared__ AlignSmem sm;
     const int tid = threadIdx.x;
     const int half_words = (E + 1) / 2;
-    if (tid < E)
+    if (tid < E) {
+        sm.first[tid] = offsets[tid];
         sm.base[tid] = offsets[tid] + counts[blockIdx.x * E + tid];
+        sm.count[tid] = bal ? counts[(size_t)chunks * E + tid] : 0;
+    }
     for (int x = tid; x < kWaves * half_words; x += kThreads)
         sm.hist[x / half_words][x % half_words] = 0;
     __syncthreads();
-    scatter_round(ids, P, E, blockIdx.x * kThreads, false, sorted_ids, inverse, sm);
+    scatter_round(ids, P, E, blockIdx.x * kThreads, false, bal, sorted_ids, inverse, sm);
 }
 
 __global__ __launch_bounds__(kThreads) void k_align_sort(
     const int32_t *__restrict__ ids, int P, int E, int bm, int slots, int tiles_cap,
     int32_t *__restrict__ sorted_ids, int32_t *__restrict__ offsets,
     int32_t *__restrict__ tile_expert, int32_t *__restrict__ inverse,
-    int32_t *__restrict__ n_tiles, moe::TileSchedule *__restrict__ sched)
+    int32_t *__restrict__ n_tiles, moe::TileSchedule *__restrict__ sched, int balanced)
 {
     __shared__ AlignSmem sm;
     align_block(ids, P, E, bm, slots, tiles_cap, sorted_ids, offsets, tile_expert, inverse,
-                n_tiles, sched, sm);
+                n_tiles, sched, balanced != 0, sm);
 }
 
 }  // namespace
@@ -332,14 +374,15 @@ namespace moe {
 
 void launch_align_sort(const int32_t *ids, int P, int E, int block_m, int32_t *sorted_ids,
                        int32_t *offsets, int32_t *tile_expert, int32_t *inverse, int32_t *n_tiles,
-                       int32_t *scratch, hipStream_t stream, TileSchedule *sched)
+                       int32_t *scratch, hipStream_t stream, TileSchedule *sched, bool balanced)
 {
     const int slots = P + E * (block_m - 1);
     const int tiles_cap = P / block_m + E;
+    const int bal = balanced ? 1 : 0;
     if (scratch == nullptr || P <= kThreads) {
         hipLaunchKernelGGL(k_align_sort, dim3(1), dim3(kThreads), 0, stream, ids, P, E, block_m,
                            slots, tiles_cap, sorted_ids, offsets, tile_expert, inverse, n_tiles,
-                           sched);
+                           sched, bal);
         return;
     }
     const int chunks = (P + kThreads - 1) / kThreads;
@@ -347,9 +390,9 @@ void launch_align_sort(const int32_t *ids, int P, int E, int block_m, int32_t *s
                        scratch);
     hipLaunchKernelGGL(k_align_scan, dim3(1), dim3(kThreads), 0, stream, scratch, chunks, E,
                        block_m, slots, tiles_cap, sorted_ids, offsets, tile_expert, n_tiles,
-                       sched);
+                       sched, bal);
     hipLaunchKernelGGL(k_align_scatter, dim3(chunks), dim3(kThreads), 0, stream, ids, P, E,
-                       scratch, offsets, sorted_ids, inverse);
+                       chunks, scratch, offsets, sorted_ids, inverse, balanced ? block_m : 0);
 }
 
 }  // namespace moe

@@ -147,7 +147,8 @@ int run_stage(int stage, const moe::Plan &pl, const Ctx &c)
                                    pl.off_align ? ws_at<int32_t>(c.ws, pl.off_align) : nullptr,
                                    c.stream,
                                    pl.off_sched ? ws_at<moe::TileSchedule>(c.ws, pl.off_sched)
-                                                : nullptr);
+                                                : nullptr,
+                                   pl.balanced);
         break;
     case MOE_STAGE_GATE_UP:
         if (!launch_gemm(true, gate_up_problem(pl, c), src, pl.gate_up, c.stream))

@@ -34,6 +34,7 @@ bool dispatch(const GemmProblem &g, moe::WsTile t, hipStream_t s)
     MOE_TILED_CASE(64, 1, 3)
     MOE_TILED_CASE(64, 2, 3)
     MOE_TILED_CASE(64, 2, 2)
+    MOE_TILED_CASE(64, 4, 2)
 #undef MOE_TILED_CASE
     return false;
 }

@@ -30,10 +30,13 @@ struct TileSchedule {
 
 // scratch: NULL (one workgroup does everything) or align_scratch_ints(P, E) ints of device
 // memory (moe_plan.h) for the chunked three-launch form (used when P > 1024).  sched: NULL or
-// the TileSchedule to write.
+// the TileSchedule to write.  balanced: an expert's routes spread evenly over its block_m-row
+// tiles (each tile's rows a prefix of it) instead of filling them in order; the chunked form
+// then needs E more ints of scratch (align_scratch_ints(P, E, true)).
 void launch_align_sort(const int32_t *ids, int P, int E, int block_m, int32_t *sorted_ids,
                        int32_t *offsets, int32_t *tile_expert, int32_t *inverse, int32_t *n_tiles,
-                       int32_t *scratch, hipStream_t stream, TileSchedule *sched = nullptr);
+                       int32_t *scratch, hipStream_t stream, TileSchedule *sched = nullptr,
+                       bool balanced = false);
 
 // ---------------------------------------------------------------- expert GEMMs
 // Where a GEMM takes its rows from.

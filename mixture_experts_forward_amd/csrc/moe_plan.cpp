@@ -92,12 +92,14 @@ void make_plan(const moe_params_t *p, int32_t S, Plan *pl, int wfmt)
         pl->gate_up = {KERNEL_WS, 1, 1, 4, 3};
         pl->down = {KERNEL_WS, 2, 1, 4, 2};
     } else if (mean_rows <= 64.0) {
-        // the down GEMM's short K loop keeps one k-step ahead once the tiles are well filled:
-        // half the registers, twice the resident workgroups (qwen3-235b batch, 32 rows per
-        // expert: 0.341 -> 0.330 ms); sparser tiles need the deeper prefetch (Kimi-K2 at 512
-        // tokens, 11 rows: 1.08 -> 1.14 ms with one step ahead)
+        // the down GEMM's short K loop keeps one k-step ahead once the tiles are well filled,
+        // with four 16-column tiles per wave (qwen3-235b batch, 32 rows per expert: two tiles
+        // two steps ahead 0.341, one step ahead 0.330, four tiles one step ahead 0.310 ms);
+        // sparser tiles need the deeper prefetch (Kimi-K2 at 512 tokens, 11 rows: 1.03 ms with
+        // two tiles two steps ahead, 1.07 one step ahead, 1.10 with four tiles)
         pl->gate_up = {KERNEL_TILED, 1, 4, 1, 3};
-        pl->down = {KERNEL_TILED, 2, 4, 1, mean_rows >= 24.0 ? 2 : 3};
+        pl->down = mean_rows >= 24.0 ? TileChoice{KERNEL_TILED, 4, 4, 1, 2}
+                                     : TileChoice{KERNEL_TILED, 2, 4, 1, 3};
     } else {
         pl->gate_up = {KERNEL_WIDE, 0, 16, 1, 2};
         pl->down = {KERNEL_WIDE, 0, 16, 1, 2};
@@ -119,6 +121,10 @@ void make_plan(const moe_params_t *p, int32_t S, Plan *pl, int wfmt)
     pl->block_m = (pl->gate_up.kind == KERNEL_WS || pl->gate_up.kind == KERNEL_MX)
                       ? kSortedBlockM
                       : 16 * pl->gate_up.mt;
+    // 256-row tiles: an expert's routes spread evenly over its tiles, so that the tiles of a
+    // heavy expert (which read the same weight rows) run at the same pace and share those
+    // rows in L2, instead of a ragged last tile streaming them on its own
+    pl->balanced = pl->gate_up.kind == KERNEL_WIDE;
     pl->slots = P + pl->E * (pl->block_m - 1);
     pl->tiles_cap = P / pl->block_m + pl->E;
 
@@ -138,7 +144,7 @@ void make_plan(const moe_params_t *p, int32_t S, Plan *pl, int wfmt)
         pl->off_n_tiles = take(4);
         // per-XCD tile ranges of the 256 x 256 tile kernel (moe_internal.h's TileSchedule)
         pl->off_sched = pl->gate_up.kind == KERNEL_WIDE ? take(2 * 4 * 9) : 0;
-        const size_t scratch = align_scratch_ints(P, pl->E);
+        const size_t scratch = align_scratch_ints(P, pl->E, pl->balanced);
         pl->off_align = scratch ? take(scratch * 4) : 0;
         pl->off_h = take((size_t)pl->slots * pl->F * 2);
     } else {

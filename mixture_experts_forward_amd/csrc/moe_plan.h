@@ -21,9 +21,11 @@ constexpr int kMaxSplitSlots = 256;
 
 // Ints of device scratch the chunked align/sort needs for P routes and E experts (0: P fits one
 // workgroup, which needs none).
-inline size_t align_scratch_ints(int P, int E)
+inline size_t align_scratch_ints(int P, int E, bool balanced = false)
 {
-    return P > kAlignChunk ? (size_t)((P + kAlignChunk - 1) / kAlignChunk) * E : 0;
+    return P > kAlignChunk
+               ? (size_t)((P + kAlignChunk - 1) / kAlignChunk + (balanced ? 1 : 0)) * E
+               : 0;
 }
 
 enum KernelKind {
@@ -47,6 +49,7 @@ struct Plan {
     int T, H, E, F, k, S, P;
     int dtype;          // MOE_DTYPE_*
     int block_m;        // sorted path
+    bool balanced;      // sorted path: routes spread evenly over each expert's tiles
     int slots;          // rows of the padded sorted order
     int tiles_cap;
     TileChoice gate_up, down, shared_gate_up, shared_down;

@@ -420,6 +420,11 @@ def main():
         "staged_ms_per_step": round(staged_ms, 5),
         "stage_ms": {k: round(v, 5) for k, v in per_stage.items()},
         "stage_roofline": stage_roofline,
+        # the fused call runs the shared expert on a second stream beside the routed GEMMs;
+        # the in-order stages give it the same three eighths of the CUs, so its stage time
+        # alone is longer than its share of the fused call
+        "stage_notes": ({"shared": "3/8 of the CUs, overlapped in the fused call"}
+                        if S > 0 else {}),
         "roofline": ({"kernel": "gate-up GEMM of the routed experts", "bound": "mfma",
                       "achieved": round(gu_tflops, 1), "peak": peak_tflops, "unit": "TFLOP/s",
                       "frac": round(gu_tflops / peak_tflops, 4), "traffic": traffic,

@@ -219,6 +219,12 @@ int fused_moe_fwd_noalloc(const uint16_t *hidden_states, const float *gating_out
  * page, FusedMoESharedExpertFwd: shared_w_gate_up [2S,H], shared_w_down [H,S]).
  *   shared_w_gate_up [2S,H] bf16 (rows [0,S) gate, [S,2S) up); shared_w_down [H,S] bf16;
  *   shared_inter S >= 64, S % 64 == 0.  The routed scaling factor does not apply to it.
+ * The shared expert needs no routing, so its two GEMMs run on a second stream of the
+ * library's (one per device, default priority, made on first use) on three eighths of the
+ * CUs, beside the routing and the routed GEMMs on `stream`; an event forks that stream from
+ * `stream` at the call and another joins it back before the combine.  The call therefore
+ * stays ordered on `stream` (and can be captured into a graph from it).  The stages of
+ * fused_moe_experts_stage run the same kernels in order on one stream, with the same results.
  * Other arguments and errors as fused_moe_fwd. */
 int fused_moe_shared_fwd(const uint16_t *hidden_states, const float *gating_output,
                          const uint16_t *w_gate_up, const uint16_t *w_down,

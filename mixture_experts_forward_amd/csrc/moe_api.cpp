@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <rocprofiler-sdk-roctx/roctx.h>
 
+#include <mutex>
+
 #include "../../include/moe.h"
 #include "moe_internal.h"
 #include "moe_plan.h"
@@ -106,6 +108,7 @@ moe::GemmProblem shared_problem(const moe::Plan &pl, const Ctx &c, bool gate_up)
     g.num_experts = 1;
     g.dtype = pl.dtype;
     g.num_groups = (pl.T + 16 * t.mt - 1) / (16 * t.mt);
+    g.slot_eighths = pl.shared_slot_eighths;
     if (pl.off_partial) {
         g.partial = ws_at<float>(c.ws, pl.off_partial);
         g.partial_bytes = pl.partial_bytes;
@@ -192,6 +195,46 @@ int experts_impl(const moe::Plan &pl, const Ctx &c, int first_stage = MOE_STAGE_
     return MOE_OK;
 }
 
+// A second stream per device for the shared expert's GEMMs, with the two events that fork it
+// from and join it to the caller's stream.  Created on first use (default priority,
+// non-blocking), kept until the process ends.  The mutex is held over a whole fork-join
+// enqueue, so calls from several host threads never interleave their records and waits on
+// these shared events.
+struct SideStream {
+    hipStream_t stream = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_side_mu;
+SideStream g_side[kMaxDevices];
+
+// The side stream of the device of `stream` (g_side_mu held), or nullptr if it cannot be made.
+SideStream *side_stream_locked(hipStream_t stream)
+{
+    int dev = 0;
+    if (stream ? hipStreamGetDevice(stream, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess)
+        return nullptr;
+    if (dev < 0 || dev >= kMaxDevices)
+        return nullptr;
+    SideStream &ss = g_side[dev];
+    if (ss.stream && ss.fork && ss.join)
+        return &ss;
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess || (cur != dev && hipSetDevice(dev) != hipSuccess))
+        return nullptr;
+    bool ok = true;
+    if (!ss.stream)
+        ok = hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) == hipSuccess;
+    if (ok && !ss.fork)
+        ok = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) == hipSuccess;
+    if (ok && !ss.join)
+        ok = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) == hipSuccess;
+    if (cur != dev)
+        (void)hipSetDevice(cur);
+    (void)hipGetLastError();
+    return ok ? &ss : nullptr;
+}
+
 // MXFP4 weights (the plan of the bf16 pass with the MXFP4 GEMM for both expert GEMMs):
 // bf16 activations, H and F multiples of 128 (whole 128-element k-steps)
 int mx_check(const moe_params_t *p)
@@ -237,9 +280,38 @@ int fused_impl(const uint16_t *hidden, const float *gating, const uint16_t *w_ga
     float *weights = weights_out ? weights_out : ws_at<float>(ws, pl.off_weights);
     const Ctx c = {hidden, w_gate_up, w_down, s_gu, s_d, ids, weights, out, ws, s};
     const int sigmoid = p->scoring == MOE_SCORING_SIGMOID;
-    moe::launch_route(gating, bias, pl.T, pl.E, pl.k, sigmoid, p->renormalize,
-                      p->num_expert_group, p->topk_group, p->routed_scaling_factor, ids,
-                      weights, s);
+    auto route = [&] {
+        moe::launch_route(gating, bias, pl.T, pl.E, pl.k, sigmoid, p->renormalize,
+                          p->num_expert_group, p->topk_group, p->routed_scaling_factor, ids,
+                          weights, s);
+    };
+    if (S > 0) {
+        // The shared expert needs only hidden_states: it forks off before the routing and
+        // runs on the side stream, on its share of the CUs, beside route, align and the
+        // routed GEMMs; the combine (which adds its rows) waits for it.  Without a side
+        // stream the same kernels run in order on the caller's stream.
+        std::lock_guard<std::mutex> lock(g_side_mu);
+        if (SideStream *ss = side_stream_locked(s)) {
+            if (hipEventRecord(ss->fork, s) != hipSuccess ||
+                hipStreamWaitEvent(ss->stream, ss->fork, 0) != hipSuccess)
+                return MOE_ERR_LAUNCH;
+            Ctx side = c;
+            side.stream = ss->stream;
+            int st = run_stage(MOE_STAGE_SHARED, pl, side);
+            // the side stream is joined back whatever happens (a capture stays whole)
+            const bool rec = hipEventRecord(ss->join, ss->stream) == hipSuccess;
+            if (st == MOE_OK) {
+                route();
+                for (int stage : {MOE_STAGE_ALIGN, MOE_STAGE_GATE_UP, MOE_STAGE_DOWN})
+                    if (st == MOE_OK)
+                        st = run_stage(stage, pl, c);
+            }
+            if (!rec || hipStreamWaitEvent(s, ss->join, 0) != hipSuccess)
+                return MOE_ERR_LAUNCH;
+            return st == MOE_OK ? run_stage(MOE_STAGE_COMBINE, pl, c) : st;
+        }
+    }
+    route();
     return experts_impl(pl, c);
 }
 

@@ -41,7 +41,10 @@ void launch_typed(const GemmProblem &g_in, hipStream_t stream)
     // dense rows, and sorted rows with a schedule: one workgroup per resident slot; sorted rows
     // without one: one tile per workgroup
     const bool persistent = SRC == moe::ROWS_DENSE || g_in.sched != nullptr;
-    const int slots = persistent ? per_cu(kernel) * device_cus() : (1 << 30);
+    int slots = persistent ? per_cu(kernel) * device_cus() : (1 << 30);
+    if (SRC == moe::ROWS_DENSE && g_in.slot_eighths > 0)  // a share of the chip, the rest
+        slots = std::max(moe_wide::kXcds,                 // left to work on another stream
+                         slots * g_in.slot_eighths / 8 / moe_wide::kXcds * moe_wide::kXcds);
     const int total = n_blocks * m_tiles;
     GemmProblem g = g_in;
     g.split_tiles = g.split_parts = 0;

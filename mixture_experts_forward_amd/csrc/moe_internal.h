@@ -74,6 +74,8 @@ struct GemmProblem {
     size_t partial_bytes;       // bytes at partial
     int split_tiles;            // set by the launcher: tiles split along K ...
     int split_parts;            // ... into this many parts each
+    int slot_eighths;           // 256 x 256 tile kernel, dense rows: the eighths of the
+                                // resident workgroup slots it takes (0: all of them)
 };
 
 // f32 partial tile of the K-split 256 x 256 kernel: 256 activation rows x 256 weight rows.

@@ -118,6 +118,12 @@ void make_plan(const moe_params_t *p, int32_t S, Plan *pl, int wfmt)
     }
     pl->shared_gate_up = {KERNEL_WIDE, 0, 16, 1, 2};
     pl->shared_down = {KERNEL_WIDE, 0, 16, 1, 2};
+    // The shared expert's GEMMs take three eighths of the resident workgroup slots, and the
+    // fused entry runs them on a second stream beside the routed GEMMs, which fill the rest
+    // (Kimi-K2 at 512 tokens, align + routed GEMMs + shared expert: one stream 3.494 ms; two
+    // streams with the shared GEMMs on all slots 3.452, on 2/8 3.360, 3/8 3.338, 4/8 3.382).
+    // The stage-by-stage form uses the same share, so both give the same bits.
+    pl->shared_slot_eighths = S > 0 ? 3 : 0;
     pl->block_m = (pl->gate_up.kind == KERNEL_WS || pl->gate_up.kind == KERNEL_MX)
                       ? kSortedBlockM
                       : 16 * pl->gate_up.mt;

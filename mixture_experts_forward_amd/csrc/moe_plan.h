@@ -53,6 +53,7 @@ struct Plan {
     int slots;          // rows of the padded sorted order
     int tiles_cap;
     TileChoice gate_up, down, shared_gate_up, shared_down;
+    int shared_slot_eighths;  // share of the resident slots the shared expert's GEMMs take
     // byte offsets into the workspace
     size_t off_ids, off_weights, off_sorted, off_offsets, off_tile_expert, off_inverse,
         off_n_tiles, off_sched, off_align, off_h, off_y, off_hs, off_ys, off_partial;

@@ -219,3 +219,29 @@ def test_bitwise_deterministic_repeats(name, T):
     d = make_inputs(cfg, DEV, num_tokens=T)
     outs = [_fused(cfg, d)[0].clone() for _ in range(3)]
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+@pytest.mark.parametrize("T", [40, 512])
+def test_shared_fused_equals_stages(T):
+    """fused_moe_shared_fwd runs the shared expert on a second stream beside the routed GEMMs;
+    the stages run the same kernels in order on one stream: the same bits.  Kimi-K2 expert and
+    shared-expert dimensions (S = 18432) with 32 routed experts."""
+    cfg = replace(CONFIGS["kimi-k2-shared"], T=T, E=32)
+    d = make_inputs(cfg, DEV, seed=900 + T)
+    out, ids, w = moe.fused_moe_shared_fwd(
+        d["hidden_states"], d["gating_output"], d["w_gate_up"], d["w_down"],
+        d["shared_w_gate_up"], d["shared_w_down"], cfg.k, d["correction_bias"], cfg.scoring,
+        cfg.renormalize, cfg.num_expert_group, cfg.topk_group, cfg.rsf, return_routing=True)
+    p = moe.make_params(T, cfg.H, cfg.E, cfg.F, cfg.k)
+    ws = torch.empty(moe.workspace_bytes(p, cfg.S), dtype=torch.uint8, device=DEV)
+    staged = torch.full_like(out, float("nan"))
+    for s in (moe.STAGE_ALIGN, moe.STAGE_GATE_UP, moe.STAGE_DOWN, moe.STAGE_SHARED,
+              moe.STAGE_COMBINE):
+        moe.fused_moe_experts_stage(s, p, d["hidden_states"], d["w_gate_up"], d["w_down"], ids,
+                                    w, staged, ws, d["shared_w_gate_up"], d["shared_w_down"])
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), staged.view(torch.int16))
+    rid, rw = oracle_route(d, cfg)
+    tokens = sample_tokens(T, 6)
+    _, ref = oracle_experts_sampled(d, rid, rw, tokens, with_shared=True)
+    assert_output_close(out[torch.as_tensor(tokens, device=DEV)], ref, "shared T=%d" % T)

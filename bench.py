@@ -820,9 +820,10 @@ def summarize_trace(args):
     cfg = CONFIGS[args.config or BENCH_CONFIG]
     path = glob.glob(os.path.join(args.summarize_trace, "**", "*kernel_stats.csv"),
                      recursive=True)[0]
-    lines = ["# Kernel trace: fused MoE forward, workload %s (T=%d, H=%d, E=%d, F=%d, top-%d%s)"
-             % (cfg.name, cfg.T, cfg.H, cfg.E, cfg.F, cfg.k,
-                ", shared S=%d" % cfg.S if cfg.S else ""), ""]
+    wname = {"fp8": "FP8", "mxfp4": "MXFP4"}.get(args.weights)
+    lines = ["# Kernel trace: fused MoE forward%s, workload %s (T=%d, H=%d, E=%d, F=%d, top-%d%s)"
+             % (" with %s expert weights" % wname if wname else "", cfg.name, cfg.T, cfg.H,
+                cfg.E, cfg.F, cfg.k, ", shared S=%d" % cfg.S if cfg.S else ""), ""]
     for c in args.pmc_commands:
         lines += ["Command (from /tmp, repository at $R):", "", "    " + c, ""]
     lines += ["Input-generation and copy kernels, and the bench's context measurements (the "
@@ -843,7 +844,17 @@ def summarize_trace(args):
               "BM, NTW, STAGES, DT>; "
               "k_wide_gemm<GATE_UP, SRC, WS, DT> (WS weight stages); k_wide_reduce<GATE_UP, DT> (sum "
               "of the K-split dense tiles' parts); k_combine<DT>."]
-    out = os.path.join(PROFILE_DIR, "kernel_trace_%s.md" % cfg.name)
+    if args.weights == "fp8":
+        lines += ["", "FP8: k_fp8_direct<GATE_UP, NT, KSPLIT, STAGES, SEG> (routes straight from "
+                  "topk_ids, rows quantised in the kernel; NT 16-column tiles, K split over KSPLIT "
+                  "waves, STAGES segments in flight, SEG 128-element k-steps per weight load); "
+                  "k_fp8_ws<NT, KSPLIT, STAGES, SEG> (contiguous layout); k_quant_fp8<MODE> (0 "
+                  "plain rows, 1 rows gathered by route, 2 SiLU(gate)*up of gate-up rows)."]
+    if args.weights == "mxfp4":
+        lines += ["", "MXFP4: k_mx_gemm<GATE_UP, SRC, NT, KSPLIT, STAGES> (weight streaming); "
+                  "k_mx_tiled<GATE_UP, NTW, STAGES> (64-row tiles)."]
+    suffix = "" if args.weights == "16bit" else "_" + args.weights
+    out = os.path.join(PROFILE_DIR, "kernel_trace_%s%s.md" % (cfg.name, suffix))
     os.makedirs(PROFILE_DIR, exist_ok=True)
     open(out, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))

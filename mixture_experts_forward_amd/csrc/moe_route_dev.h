@@ -95,16 +95,18 @@ __device__ __forceinline__ void route_token(
     const float *g = gating + (size_t)t * E;
 
     float key[SLOTS];
+    double sig[SLOTS];      // sigmoid: the unbiased score in double, kept for the weights
     uint32_t eligible = 0;  // bit i: slot i holds an eligible expert
 #pragma unroll
     for (int i = 0; i < SLOTS; ++i) {
         const int e = 64 * i + lane;
         key[i] = 0.0f;
+        sig[i] = 0.0;
         if (e < E) {
             const float gv = g[e];
             if (sigmoid) {
-                const float s = (float)(1.0 / (1.0 + exp(-(double)gv)));
-                key[i] = s + (bias ? bias[e] : 0.0f);
+                sig[i] = 1.0 / (1.0 + exp(-(double)gv));
+                key[i] = (float)sig[i] + (bias ? bias[e] : 0.0f);
             } else {
                 key[i] = gv;
             }
@@ -112,9 +114,62 @@ __device__ __forceinline__ void route_token(
         }
     }
 
-    if (n_group > 1) {
+    const int gs = n_group > 1 ? E / n_group : 0;
+    if (n_group > 1 && gs <= 64 && (gs & (gs - 1)) == 0 && n_group <= 64) {
+        // Groups of a power-of-two size up to 64 lie within one slot's lanes: the two largest
+        // keys of each group by a butterfly over its gs lanes, merging (largest, second) pairs,
+        // all slots at once.  A group scores b1 + b2 (b1 alone for single-expert groups), as
+        // the scan below; which of two equal keys is "first" does not change the sum.
+        float b1[SLOTS], b2[SLOTS];
+#pragma unroll
+        for (int i = 0; i < SLOTS; ++i) {
+            // a NaN key never counts (the scan's strict comparisons skip it too)
+            b1[i] = (64 * i + lane < E && key[i] == key[i]) ? key[i] : -INFINITY;
+            b2[i] = -INFINITY;
+        }
+        for (int off = 1; off < gs; off <<= 1) {
+#pragma unroll
+            for (int i = 0; i < SLOTS; ++i) {
+                const float o1 = __shfl_xor(b1[i], off);
+                const float o2 = __shfl_xor(b2[i], off);
+                const float hi = fmaxf(b1[i], o1), lo = fminf(b1[i], o1);
+                b2[i] = fmaxf(lo, fmaxf(b2[i], o2));
+                b1[i] = hi;
+            }
+        }
+        // group gi = (64 * i + lane) / gs: its pair sits in every lane of its segment; lane
+        // gi < n_group gathers group gi's from the segment's first lane (every lane runs the
+        // shuffles; the others discard the result)
+        const int e0 = lane < n_group ? lane * gs : 0;  // first expert of group `lane`
+        const int slot = e0 >> 6, src = e0 & 63;
+        float s1 = -INFINITY, s2 = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < SLOTS; ++i) {
+            const float v1 = __shfl(b1[i], src), v2 = __shfl(b2[i], src);
+            if (i == slot) {
+                s1 = v1;
+                s2 = v2;
+            }
+        }
+        uint64_t gkey = 0;
+        if (lane < n_group)
+            gkey = select_key(gs == 1 ? s1 : s1 + s2, lane);
+        uint64_t kept = 0;  // bit gi: group gi kept
+        for (int n = 0; n < topk_group; ++n) {
+            const uint64_t best = wave_max_u64(gkey);
+            const int gi = select_index(best);
+            kept |= 1ull << gi;
+            if (lane == gi)
+                gkey = 0;
+        }
+#pragma unroll
+        for (int i = 0; i < SLOTS; ++i) {
+            const int e = 64 * i + lane;
+            if (e < E && !((kept >> (e / gs)) & 1ull))
+                eligible &= ~(1u << i);
+        }
+    } else if (n_group > 1) {
         // group scores: lane gi < n_group scans its contiguous group of E/n_group experts
-        const int gs = E / n_group;
 #pragma unroll
         for (int i = 0; i < SLOTS; ++i) {
             const int e = 64 * i + lane;
@@ -179,9 +234,17 @@ __device__ __forceinline__ void route_token(
     // softmax is never grouped, so the first chosen expert holds the row's largest logit
     const double m = (double)g[first_id];
     double s = 0.0;
-    if (lane < k) {
-        const double gv = (double)g[my_id];
-        s = sigmoid ? 1.0 / (1.0 + exp(-gv)) : exp(gv - m);
+    if (sigmoid) {
+        // the chosen expert's sigmoid from the lane and slot that computed it
+        const int src = my_id < 0 ? 0 : (my_id & 63), slot = my_id < 0 ? 0 : (my_id >> 6);
+#pragma unroll
+        for (int i = 0; i < SLOTS; ++i) {
+            const double v = __shfl(sig[i], src);
+            if (i == slot && lane < k)
+                s = v;
+        }
+    } else if (lane < k) {
+        s = exp((double)g[my_id] - m);
     }
     double denom = 1.0;
     if (renormalize) {

@@ -52,6 +52,11 @@ def test_route_token_sweep(name, T):
     dict(E=256, k=8, scoring="sigmoid", bias=False, renormalize=False),
     dict(E=32, k=32, scoring="softmax", renormalize=False),
     dict(E=48, k=3, scoring="sigmoid", bias=True, num_expert_group=2, topk_group=1, rsf=3.0),
+    # group sizes that are powers of two (group scores by a butterfly over the group's lanes):
+    # 16, 32 with 12 groups, 64
+    dict(E=128, k=6, scoring="sigmoid", bias=True, num_expert_group=8, topk_group=3),
+    dict(E=384, k=8, scoring="sigmoid", bias=True, num_expert_group=12, topk_group=5, rsf=2.0),
+    dict(E=512, k=8, scoring="sigmoid", bias=True, num_expert_group=8, topk_group=4),
 ])
 def test_route_variants(variant):
     cfg = replace(CONFIGS["tiny"], T=300, **variant)

@@ -245,3 +245,42 @@ def test_shared_fused_equals_stages(T):
     tokens = sample_tokens(T, 6)
     _, ref = oracle_experts_sampled(d, rid, rw, tokens, with_shared=True)
     assert_output_close(out[torch.as_tensor(tokens, device=DEV)], ref, "shared T=%d" % T)
+
+
+def test_shared_fused_concurrent_host_threads():
+    """Two host threads call fused_moe_shared_fwd at once, each on its own stream and
+    workspace: the per-device side stream and its fork/join events are shared (guarded by the
+    library), and every result equals the single-threaded one bit for bit."""
+    import threading
+    cfg = replace(CONFIGS["kimi-k2-shared"], T=64, E=16, S=1024)
+    inputs = [make_inputs(cfg, DEV, seed=950 + i) for i in range(2)]
+
+    def run(d, stream, out):
+        with torch.cuda.stream(stream):
+            out.copy_(moe.fused_moe_shared_fwd(
+                d["hidden_states"], d["gating_output"], d["w_gate_up"], d["w_down"],
+                d["shared_w_gate_up"], d["shared_w_down"], cfg.k, d["correction_bias"],
+                cfg.scoring, cfg.renormalize, cfg.num_expert_group, cfg.topk_group, cfg.rsf))
+
+    refs = []
+    for d in inputs:
+        o = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=DEV)
+        run(d, torch.cuda.current_stream(), o)
+        refs.append(o)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    outs = [[torch.empty_like(refs[0]) for _ in range(6)] for _ in range(2)]
+
+    def worker(i):
+        for j in range(6):
+            run(inputs[i], streams[i], outs[i][j])
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    for i in range(2):
+        for j in range(6):
+            assert torch.equal(outs[i][j], refs[i]), "thread %d call %d differs" % (i, j)

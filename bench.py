@@ -849,7 +849,7 @@ def summarize_trace(args):
                   "topk_ids, rows quantised in the kernel; NT 16-column tiles, K split over KSPLIT "
                   "waves, STAGES segments in flight, SEG 128-element k-steps per weight load); "
                   "k_fp8_ws<NT, KSPLIT, STAGES, SEG> (contiguous layout); k_quant_fp8<MODE> (0 "
-                  "plain rows, 1 rows gathered by route, 2 SiLU(gate)*up of gate-up rows)."]
+                  "plain rows, 2 SiLU(gate)*up of gate-up rows)."]
     if args.weights == "mxfp4":
         lines += ["", "MXFP4: k_mx_gemm<GATE_UP, SRC, NT, KSPLIT, STAGES> (weight streaming); "
                   "k_mx_tiled<GATE_UP, NTW, STAGES> (64-row tiles)."]

@@ -321,9 +321,10 @@ int fused_moe_mxfp4_stage(int stage, const uint16_t *hidden_states, const uint8_
  *   w_gate_up        [E, 2F, H] uint8 e4m3 (rows [0,F) gate, [F,2F) up);
  *   w_gate_up_scale  [E, 2F/128, H/128] f32;
  *   w_down           [E, H, F] uint8 e4m3; w_down_scale [E, H/128, F/128] f32.
- * The pass: route; the routes in expert order (align with block_m 1); each route's x row
- * quantised (moe_quant_fp8) in that order; the gate-up GEMM as moe_grouped_gemm_fp8_contiguous
- * (bf16 gate and up); h = bf16(SiLU(gate) * up) quantised the same way; the down GEMM (bf16
+ * The pass: route; the routes in expert order (align with block_m 1); each token's x row
+ * quantised once (moe_quant_fp8); the gate-up GEMM as moe_grouped_gemm_fp8_contiguous on the
+ * routes' rows (a route reads its token's codes; bf16 gate and up); h = bf16(SiLU(gate) * up)
+ * quantised the same way; the down GEMM (bf16
  * rows); the weighted combine of fused_moe_fwd.  Needs p->dtype == MOE_DTYPE_BF16,
  * H % 128 == 0, F % 128 == 0, no shared expert; 16-byte aligned hidden_states, weights, out
  * and workspace, 4-byte aligned scales.
@@ -343,7 +344,7 @@ int fused_moe_fp8_fwd(const uint16_t *hidden_states, const float *gating_output,
                       size_t workspace_bytes, void *stream);
 
 /* fused_moe_fp8_stage -- one step of fused_moe_fp8_fwd's expert part with the routing given:
- * MOE_STAGE_ALIGN (expert order and the quantised routed x rows; direct path: nothing),
+ * MOE_STAGE_ALIGN (expert order and the quantised x rows; direct path: nothing),
  * MOE_STAGE_GATE_UP, MOE_STAGE_DOWN (h quantised, then the down GEMM), MOE_STAGE_COMBINE, in
  * that order, enqueue exactly the expert kernels of the fused call.  A stage checks only the
  * pointers it reads (hidden_states: ALIGN on the sorted path, GATE_UP on the direct one).

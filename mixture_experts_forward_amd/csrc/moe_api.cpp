@@ -580,8 +580,8 @@ static void fp8_plan(const moe_params_t *p, Fp8Pass *f)
     f->off_n_tiles = take(4);
     const size_t scratch = moe::align_scratch_ints(f->P, f->E);
     f->off_align = scratch ? take(scratch * 4) : 0;
-    f->off_aq = take(P * f->H);
-    f->off_as = take(P * (f->H / 128) * 4);
+    f->off_aq = take((size_t)f->T * f->H);  // each token's x row quantised once
+    f->off_as = take((size_t)f->T * (f->H / 128) * 4);
     f->off_gu = take(P * 2 * f->F * 2);
     f->off_hq = take(P * f->F);
     f->off_hs = take(P * (f->F / 128) * 4);
@@ -625,15 +625,17 @@ static void fp8_stage(int stage, const Fp8Pass &f, const uint16_t *hidden, const
     switch (stage) {
     case MOE_STAGE_ALIGN:
         // expert order, tight (block 1): rows [offsets[e], offsets[e+1]) are expert e's routes;
-        // then the routes' x rows in that order, quantised
+        // then every token's x row quantised once (a route's row is its token's)
         moe::launch_align_sort(ids, f.P, f.E, 1, sorted, offsets,
                                ws_at<int32_t>(ws, f.off_tile_expert), inverse,
                                ws_at<int32_t>(ws, f.off_n_tiles),
                                f.off_align ? ws_at<int32_t>(ws, f.off_align) : nullptr, s);
-        moe::launch_quant_fp8_gather(hidden, sorted, f.k, f.P, f.H, aq, as, s);
+        moe::launch_quant_fp8(hidden, f.T, f.H, aq, as, s);
         break;
     case MOE_STAGE_GATE_UP:
-        moe::launch_fp8_gemm_contig(aq, as, w_gu, s_gu, offsets, f.E, f.P, 2 * f.F, f.H, gu, s);
+        // contiguous row q (the route sorted[q]) reads its token's codes, sorted[q] / k
+        moe::launch_fp8_gemm_contig(aq, as, w_gu, s_gu, offsets, f.E, f.P, 2 * f.F, f.H, gu, s,
+                                    sorted, f.k);
         break;
     case MOE_STAGE_DOWN:
         moe::launch_quant_fp8_swiglu(gu, f.P, f.F, hq, hs, s);

@@ -57,7 +57,18 @@ struct Fp8Problem {
     const int32_t *offsets;   // [E + 1] (contiguous layout), else nullptr
     uint16_t *out;            // [E, max_m, N] or [P, N] bf16
     int E, max_m, P, N, K, KB, NB;
+    // contiguous layout, optional: row q of a and a_scale is row a_route[q] / a_div of them
+    // (the FP8 pass quantises each token once and its gate-up GEMM reads a route's row as its
+    // token's); nullptr: row q is row q
+    const int32_t *a_route;
+    int a_div;
 };
+
+// Row of a / a_scale that contiguous row q reads.
+__device__ __forceinline__ size_t fp8_arow(const Fp8Problem &p, int q)
+{
+    return p.a_route ? (size_t)(p.a_route[q] / p.a_div) : (size_t)q;
+}
 
 constexpr int kWaves = 4;
 constexpr int kXcds = 8;
@@ -221,22 +232,21 @@ __global__ __launch_bounds__(64 * kWaves) void k_fp8_gemm(Fp8Problem p, int n_bl
 
     // ---- activation rows this lane loads: tile rows wv*BM/4 + 8*i + lane/8, chunk lane%8;
     // rows past the rows in use read the tile's first row (their results are never stored)
-    const uint8_t *A = p.a + (size_t)rbase * K;
     const uint8_t *xld[XI];
     int xslot[XI];
 #pragma unroll
     for (int i = 0; i < XI; ++i) {
         const int r = wv * (BM / kWaves) + 8 * i + lrow;
         const int src = r < n_rows ? r : 0;
-        xld[i] = A + (size_t)src * K + 16 * lchunk;
+        xld[i] = p.a + fp8_arow(p, rbase + src) * K + 16 * lchunk;
         xslot[i] = r * 8 + (lchunk ^ ((r >> 1) & 7));
     }
     // a_scale rows of this lane's results: row 16*mt + lane%16 of the tile
-    int sa_base[TM];
+    size_t sa_base[TM];
 #pragma unroll
     for (int mt = 0; mt < TM; ++mt) {
         const int r = 16 * mt + rr;
-        sa_base[mt] = (rbase + (r < n_rows ? r : 0)) * KB;
+        sa_base[mt] = fp8_arow(p, rbase + (r < n_rows ? r : 0)) * KB;
     }
 
     const int rot = (int)((expert * 7u) % (unsigned)KB);
@@ -413,7 +423,7 @@ void k_fp8_ws(Fp8Problem p)
         // its first row, whose results are never stored)
         const int r = pass0 + rr;
         const bool rok = r < n_rows;
-        const size_t arow_i = (size_t)r0 + (rok ? r : 0);
+        const size_t arow_i = fp8_arow(p, r0 + (rok ? r : 0));
         const uint8_t *arow = p.a + arow_i * K + 16 * rq;
         const float *asc = p.a_scale + arow_i * KB;
 
@@ -583,7 +593,6 @@ __global__ __launch_bounds__(moe_wide::kThreads) void k_fp8_wide(Fp8Problem p, i
     // wv*32 + 8j .. +7, lane l fetching chunk (l%8) ^ swizzle(row) of row wv*32 + 8j + l/8
     const int lrow = lane >> 3, lpos = lane & 7;
     const uint8_t *B = p.b + (size_t)expert * p.N * K;
-    const uint8_t *A = p.a + (size_t)rbase * K;
     const uint8_t *wsrc[WLoads];
 #pragma unroll
     for (int j = 0; j < WLoads; ++j) {
@@ -598,7 +607,8 @@ __global__ __launch_bounds__(moe_wide::kThreads) void k_fp8_wide(Fp8Problem p, i
         const int rfirst = wv * (kBM / moe_wide::kWaves) + 8 * j;
         const int r = rfirst + lrow;
         xload[j] = rfirst < n_real;
-        xsrc[j] = A + (size_t)(r < n_real ? r : 0) * K + 16 * (lpos ^ ((r >> 1) & 7));
+        xsrc[j] = p.a + fp8_arow(p, rbase + (r < n_real ? r : 0)) * K +
+                  16 * (lpos ^ ((r >> 1) & 7));
     }
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
     const uint32_t x_dst = lds0 + wv * (kBM / moe_wide::kWaves) * 128;
@@ -613,9 +623,9 @@ __global__ __launch_bounds__(moe_wide::kThreads) void k_fp8_wide(Fp8Problem p, i
     // each copy 64 rows x kG consecutive blocks (16 bytes a row, one load instruction; rows past
     // the rows in use copy row 0) -- instead of one strided load per row per k-step.  b_scale:
     // the block of this wave's 128 columns, one uniform load per k-step.
-    const float *sa_src = p.a_scale +
-                          ((size_t)rbase +
-                           (64 * (wv & 3) + lane < n_real ? 64 * (wv & 3) + lane : 0)) * KB;
+    const float *sa_src =
+        p.a_scale +
+        fp8_arow(p, rbase + (64 * (wv & 3) + lane < n_real ? 64 * (wv & 3) + lane : 0)) * KB;
     const uint32_t sa_dst = (uint32_t)(uintptr_t)&s_scale[0][0] + (wv & 3) * 64 * 16;
     const int wcol = col_wg + 16 * NT * wn;  // this wave's columns: one 128-column block
     const int sb_base = (expert * p.NB + (wcol < p.N ? wcol : 0) / 128) * KB;

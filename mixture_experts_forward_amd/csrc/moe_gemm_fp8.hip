@@ -142,6 +142,8 @@ void launch_fp8_gemm(const uint8_t *a, const float *a_scale, const uint8_t *b,
                      int K, uint16_t *out, hipStream_t stream)
 {
     moe_fp8::Fp8Problem p;
+    p.a_route = nullptr;
+    p.a_div = 1;
     p.a = a;
     p.a_scale = a_scale;
     p.b = b;
@@ -177,9 +179,12 @@ void launch_fp8_gemm(const uint8_t *a, const float *a_scale, const uint8_t *b,
 
 void launch_fp8_gemm_contig(const uint8_t *a, const float *a_scale, const uint8_t *b,
                             const float *b_scale, const int32_t *offsets, int E, int P, int N,
-                            int K, uint16_t *out, hipStream_t stream)
+                            int K, uint16_t *out, hipStream_t stream, const int32_t *a_route,
+                            int a_div)
 {
     moe_fp8::Fp8Problem p;
+    p.a_route = a_route;
+    p.a_div = a_div;
     p.a = a;
     p.a_scale = a_scale;
     p.b = b;

@@ -120,9 +120,11 @@ void launch_fp8_gemm(const uint8_t *a, const float *a_scale, const uint8_t *b,
                      const float *b_scale, const int32_t *masked_m, int E, int max_m, int N,
                      int K, uint16_t *out, hipStream_t stream);
 // the same GEMM on the contiguous layout: a [P, K], expert e owning rows [offsets[e], offsets[e+1])
+// a_route (optional): row q of a / a_scale is row a_route[q] / a_div of them
 void launch_fp8_gemm_contig(const uint8_t *a, const float *a_scale, const uint8_t *b,
                             const float *b_scale, const int32_t *offsets, int E, int P, int N,
-                            int K, uint16_t *out, hipStream_t stream);
+                            int K, uint16_t *out, hipStream_t stream,
+                            const int32_t *a_route = nullptr, int a_div = 1);
 
 // The direct FP8 pass for T*k <= 64 routes (moe_fp8_kernel.h, k_fp8_direct): one launch per
 // GEMM reading the routes from topk_ids and quantising its own activation rows (gate-up: rows
@@ -139,9 +141,6 @@ void launch_fp8_direct(bool gate_up, const uint16_t *act, const int32_t *topk_id
 // x [M, K] bf16 -> q [M, K] e4m3 codes, scale [M, ceil(K/128)] f32 (moe_quant.hip); K % 8 == 0.
 void launch_quant_fp8(const uint16_t *x, int M, int K, uint8_t *q, float *scale,
                       hipStream_t stream);
-// the same of rows row_src[r] / div of x (row_src[r] < 0: zero row)
-void launch_quant_fp8_gather(const uint16_t *x, const int32_t *row_src, int div, int M, int K,
-                             uint8_t *q, float *scale, hipStream_t stream);
 // the same of h = bf16(SiLU(gu[r, k]) * gu[r, K + k]) for gate-up rows gu [M, 2K]
 void launch_quant_fp8_swiglu(const uint16_t *gu, int M, int K, uint8_t *q, float *scale,
                              hipStream_t stream);

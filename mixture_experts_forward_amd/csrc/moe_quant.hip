@@ -2,8 +2,7 @@
 // a / a_scale operand pair of the block-scaled FP8 grouped GEMM (TileOPs "MoE" page,
 // MoEGroupedGemmFP8Fwd: a_scale [.., ceil_div(K, 128)] f32).
 //
-// Three sources: rows of x; rows gathered through a row map (the routed rows of a pass, in
-// expert order); and SiLU(gate) * up of gate-up GEMM rows (bf16, then quantised).
+// Two sources: rows of x, and SiLU(gate) * up of gate-up GEMM rows (bf16, then quantised).
 //
 // Per group: s = amax / 448 (448 = the largest finite e4m3 magnitude; s = 1 for an all-zero
 // group), code = e4m3 nearest to x / s, ties to the even code.  Both divisions are IEEE f32.
@@ -18,16 +17,14 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// Source rows: SRC_ROWS, row r of x; SRC_GATHER, row row_src[r] / div of x (row_src[r] < 0: a
-// zero row); SRC_SWIGLU, h = bf16( SiLU(x[r, k]) * x[r, K + k] ) of a gate-up row x [M, 2K].
-enum { SRC_ROWS = 0, SRC_GATHER = 1, SRC_SWIGLU = 2 };
+// Source rows: SRC_ROWS, row r of x; SRC_SWIGLU, h = bf16( SiLU(x[r, k]) * x[r, K + k] ) of a
+// gate-up row x [M, 2K].
+enum { SRC_ROWS = 0, SRC_SWIGLU = 2 };
 
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void k_quant_fp8(const uint16_t *__restrict__ x, int M,
                                                         int K, uint8_t *__restrict__ q,
-                                                        float *__restrict__ scale,
-                                                        const int32_t *__restrict__ row_src,
-                                                        int div)
+                                                        float *__restrict__ scale)
 {
     const int G = (K + 127) / 128;
     const long long gid = (long long)blockIdx.x * (kThreads / 16) + threadIdx.x / 16;
@@ -38,12 +35,9 @@ __global__ __launch_bounds__(kThreads) void k_quant_fp8(const uint16_t *__restri
     const int k = 128 * g + 8 * sub;  // first of this lane's 8 elements
     const bool in = k < K;            // K % 8 == 0: a lane's 8 are all in or all out
     float v[8];
-    int src = row;
-    if (MODE == SRC_GATHER)
-        src = row_src[row] < 0 ? -1 : row_src[row] / div;
-    if (in && src >= 0) {
+    if (in) {
         const size_t stride = MODE == SRC_SWIGLU ? 2 * (size_t)K : (size_t)K;
-        const moe_u32x4 raw = *reinterpret_cast<const moe_u32x4 *>(x + (size_t)src * stride + k);
+        const moe_u32x4 raw = *reinterpret_cast<const moe_u32x4 *>(x + (size_t)row * stride + k);
         const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -52,7 +46,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_fp8(const uint16_t *__restri
         }
         if (MODE == SRC_SWIGLU) {
             const moe_u32x4 rup =
-                *reinterpret_cast<const moe_u32x4 *>(x + (size_t)src * stride + K + k);
+                *reinterpret_cast<const moe_u32x4 *>(x + (size_t)row * stride + K + k);
             const uint32_t u[4] = {rup.x, rup.y, rup.z, rup.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -103,16 +97,7 @@ void launch_quant_fp8(const uint16_t *x, int M, int K, uint8_t *q, float *scale,
     const long long groups = (long long)M * ((K + 127) / 128);
     const long long blocks = (groups + kThreads / 16 - 1) / (kThreads / 16);
     hipLaunchKernelGGL(k_quant_fp8<SRC_ROWS>, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
-                       x, M, K, q, scale, nullptr, 1);
-}
-
-void launch_quant_fp8_gather(const uint16_t *x, const int32_t *row_src, int div, int M, int K,
-                             uint8_t *q, float *scale, hipStream_t stream)
-{
-    const long long groups = (long long)M * ((K + 127) / 128);
-    const long long blocks = (groups + kThreads / 16 - 1) / (kThreads / 16);
-    hipLaunchKernelGGL(k_quant_fp8<SRC_GATHER>, dim3((unsigned)blocks), dim3(kThreads), 0,
-                       stream, x, M, K, q, scale, row_src, div);
+                       x, M, K, q, scale);
 }
 
 void launch_quant_fp8_swiglu(const uint16_t *gu, int M, int K, uint8_t *q, float *scale,
@@ -121,7 +106,7 @@ void launch_quant_fp8_swiglu(const uint16_t *gu, int M, int K, uint8_t *q, float
     const long long groups = (long long)M * ((K + 127) / 128);
     const long long blocks = (groups + kThreads / 16 - 1) / (kThreads / 16);
     hipLaunchKernelGGL(k_quant_fp8<SRC_SWIGLU>, dim3((unsigned)blocks), dim3(kThreads), 0,
-                       stream, gu, M, K, q, scale, nullptr, 1);
+                       stream, gu, M, K, q, scale);
 }
 
 }  // namespace moe

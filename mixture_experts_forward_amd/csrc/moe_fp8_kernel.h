@@ -31,8 +31,8 @@
 // ~128 rows and more: 8 waves, both operands loaded straight into LDS (a 128-element FP8 k-step
 // is the 128-byte row segment that kernel's load path and swizzle are built for), 16-row tiles
 // without rows in use skipped, so each weight byte is requested once per 256 rows.  It needs
-// K % 512 == 0 and a 16-byte aligned a_scale (activation scales are staged 4 blocks at a
-// time).  The block sums of one weight tile are scaled while the next tile's MFMAs run.
+// K % 512 == 0, K <= 16384 and a 16-byte aligned a_scale (activation scales are staged 4
+// blocks at a time; a wave holds its column block's weight scales in two registers).  The block sums of one weight tile are scaled while the next tile's MFMAs run.
 #pragma once
 
 #include <type_traits>
@@ -92,14 +92,31 @@ __device__ __forceinline__ void contig_rows(const Fp8Problem &p, int e, int &r0,
     r1 = min(max(p.offsets[e + 1], r0), p.P);
 }
 
+// Row tile j of an expert with r rows: its first row and its row count (<= 0: no rows).
+template <int BM, bool EVEN>
+__device__ __forceinline__ void fp8_tile_rows(int r, int j, int &row0, int &n)
+{
+    const int te = (r + BM - 1) / BM;
+    if (!EVEN || j >= te) {
+        row0 = j * BM;
+        n = min(BM, r - row0);
+        return;
+    }
+    const int q = r / te, rm = r % te;
+    row0 = j * q + min(j, rm);
+    n = q + (j < rm ? 1 : 0);
+}
+
 // Tile of this workgroup.  Tiles are numbered expert by expert, column blocks, then the BM-row
 // tiles of the expert innermost, and blocks are dealt to the 8 XCDs (blockIdx % 8) as
 // contiguous ranges of tile numbers.  Masked layout: m_tiles row tiles per expert (tiles past
 // its rows in use are empty).  Contiguous layout: ceil(rows / BM) per expert; every wave sums
 // them over the experts itself (lane l a run of ceil(E/64) experts, then a wave prefix sum),
-// which gives the tile count and, by a ballot, the expert of tile t.  Wave-uniform; false: no
-// tile for this workgroup.
-template <int BM>
+// which gives the tile count and, by a ballot, the expert of tile t.  EVEN: an expert's r rows
+// are spread over its ceil(r / BM) row tiles as evenly as they go (the first r mod te tiles one
+// row more) instead of filling them in order, so its tiles move through the same weight slices
+// at one pace.  Wave-uniform; false: no tile for this workgroup.
+template <int BM, bool EVEN = false>
 __device__ __forceinline__ bool fp8_locate(const Fp8Problem &p, int n_blocks, int m_tiles,
                                            Fp8Tile &o)
 {
@@ -114,9 +131,10 @@ __device__ __forceinline__ bool fp8_locate(const Fp8Problem &p, int n_blocks, in
         o.expert = t / per_expert;
         const int rem = t - o.expert * per_expert;
         o.nblk = rem / m_tiles;
-        const int row0 = (rem - o.nblk * m_tiles) * BM;
+        const int j = rem - o.nblk * m_tiles;
         const int rows_used = min(max(p.masked_m[o.expert], 0), p.max_m);
-        o.n_rows = min(BM, rows_used - row0);
+        int row0;
+        fp8_tile_rows<BM, EVEN>(rows_used, j, row0, o.n_rows);
         o.rbase = o.expert * p.max_m + row0;
         return o.n_rows > 0;
     }
@@ -157,8 +175,8 @@ __device__ __forceinline__ bool fp8_locate(const Fp8Problem &p, int n_blocks, in
     const int rem = t - cum;
     o.expert = e;
     o.nblk = rem / mt_e;
-    const int row0 = (rem - o.nblk * mt_e) * BM;
-    o.n_rows = min(BM, r1 - r0 - row0);
+    int row0;
+    fp8_tile_rows<BM, EVEN>(r1 - r0, rem - o.nblk * mt_e, row0, o.n_rows);
     o.rbase = r0 + row0;
     return o.n_rows > 0;
 }
@@ -566,13 +584,22 @@ __global__ __launch_bounds__(moe_wide::kThreads) void k_fp8_wide(Fp8Problem p, i
     using moe_wide::kThreads;
     using moe_wide::Stage;
     using moe_wide::dma16;
-    using moe_wide::wait_loads;
+    using moe_wide::step_barrier;
     using St = Stage<64>;                 // 128-byte rows: 128 e4m3 codes (slot order)
     constexpr int BW = 32 * NT;           // output columns (weight rows) per workgroup
     constexpr int WLoads = BW / 64;       // weight DMA instructions per wave
-    constexpr int kStage = (kBM + BW) * 128;
     constexpr int kG = 4;               // k-steps per group of staged activation scales
-    __shared__ moe_u32x4 smem[2 * kStage / 16];
+    // A stage holds one k-step: the tile's activation rows, then its BW weight rows.  Tiles of
+    // more than kSmallRows rows take two stages of 256 activation rows (the next k-step loads
+    // while this one computes); smaller ones take three stages of kSmallRows activation rows in
+    // the same memory, so their weight stream runs two k-steps ahead -- such tiles have few
+    // MFMAs to hide a k-step's load latency behind.
+    constexpr int kSmallRows = 128;
+    constexpr int kW = BW * 128;
+    constexpr int kFullStage = kBM * 128 + kW;
+    constexpr int kSmallStage = kSmallRows * 128 + kW;
+    constexpr int kSmem = 2 * kFullStage > 3 * kSmallStage ? 2 * kFullStage : 3 * kSmallStage;
+    __shared__ moe_u32x4 smem[kSmem / 16];
     __shared__ float s_scale[2][kBM * kG];  // a_scale of the tile rows, two groups
 
     const int tid = threadIdx.x;
@@ -582,7 +609,7 @@ __global__ __launch_bounds__(moe_wide::kThreads) void k_fp8_wide(Fp8Problem p, i
 
     // ---- tile: expert-major, column blocks, row tiles innermost; XCD-contiguous ranges
     Fp8Tile tile;
-    if (!fp8_locate<kBM>(p, n_blocks, m_tiles, tile))
+    if (!fp8_locate<kBM, true>(p, n_blocks, m_tiles, tile))
         return;
     const int expert = tile.expert, nblk = tile.nblk, rbase = tile.rbase;
     const int n_real = __builtin_amdgcn_readfirstlane(tile.n_rows);
@@ -611,8 +638,12 @@ __global__ __launch_bounds__(moe_wide::kThreads) void k_fp8_wide(Fp8Problem p, i
                   16 * (lpos ^ ((r >> 1) & 7));
     }
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+    // (rows past kSmallRows have no loads in the three-stage form, so the offsets hold for both)
     const uint32_t x_dst = lds0 + wv * (kBM / moe_wide::kWaves) * 128;
-    const uint32_t w_dst = lds0 + kBM * 128 + wv * (BW / moe_wide::kWaves) * 128;
+    int nx = 0;  // this wave's activation DMAs per k-step
+#pragma unroll
+    for (int j = 0; j < St::kXLoads; ++j)
+        nx += xload[j] ? 1 : 0;
 
     const int rr = lane & 15, rq = lane >> 4;
     int mt_real = 0;
@@ -629,6 +660,14 @@ __global__ __launch_bounds__(moe_wide::kThreads) void k_fp8_wide(Fp8Problem p, i
     const uint32_t sa_dst = (uint32_t)(uintptr_t)&s_scale[0][0] + (wv & 3) * 64 * 16;
     const int wcol = col_wg + 16 * NT * wn;  // this wave's columns: one 128-column block
     const int sb_base = (expert * p.NB + (wcol < p.N ? wcol : 0) / 128) * KB;
+    // b_scale of that block, lane l holding k-blocks l and l + 64 (KB <= 128), loaded once per
+    // tile and picked per k-step by a lane read: the K loop then holds no vector-memory load
+    // the compiler knows of, since it cannot see the DMAs and would wait for every outstanding
+    // load, the next k-step's DMAs included, before such a load's first use.  The empty asm
+    // takes the values before the first DMA, so their wait comes before it.
+    const float sb_lo = lane < KB ? p.b_scale[sb_base + lane] : 0.f;
+    const float sb_hi = lane + 64 < KB ? p.b_scale[sb_base + lane + 64] : 0.f;
+    asm volatile("" ::"v"(sb_lo), "v"(sb_hi));
     // the K loop starts at a multiple of kG blocks (KB % kG == 0), so groups stay aligned
     const int rot = (int)((expert * 7u) % (unsigned)(KB / kG)) * kG;
 
@@ -639,46 +678,68 @@ __global__ __launch_bounds__(moe_wide::kThreads) void k_fp8_wide(Fp8Problem p, i
         for (int n = 0; n < NT; ++n)
             acc[m][n] = moe_f32x4{0.f, 0.f, 0.f, 0.f};
 
-    float sb[2];
-    auto issue = [&](int stage, int i) {
+    // k-step i's DMAs into the stage at byte offset so (weights at wd + so); a new group of kG
+    // k-steps also brings a_scale[rows][kb .. kb + kG) into its half of s_scale
+    auto issue = [&](uint32_t so, uint32_t wd, int i) {
         const int kb = (i + rot) % KB;
         const int k = kb * 128;
-        const uint32_t so = stage * kStage;
 #pragma unroll
         for (int j = 0; j < St::kXLoads; ++j)
             if (xload[j])
                 dma16(xsrc[j] + k, x_dst + so + j * 1024);
 #pragma unroll
         for (int j = 0; j < WLoads; ++j)
-            dma16(wsrc[j] + k, w_dst + so + j * 1024);
-        if (i % kG == 0 && wv < 4)  // a new group: a_scale[rows][kb .. kb + kG)
+            dma16(wsrc[j] + k, wd + so + j * 1024);
+        if (i % kG == 0 && wv < 4)
             dma16(sa_src + kb, sa_dst + ((i / kG) & 1) * (kBM * kG * 4));
-        sb[stage] = p.b_scale[sb_base + kb];
+    };
+    // this wave's DMAs of k-step i (0 past the K loop)
+    auto n_loads = [&](int i) {
+        return i < KB ? nx + WLoads + ((i % kG == 0 && wv < 4) ? 1 : 0) : 0;
     };
 
-    // Two LDS stages as in moe_wide_kernel.h: at the top of step i this wave's loads of k-step
-    // i (operands and scales) are the only ones outstanding; the barrier publishes the stage
-    // and frees the other one for k-step i+1.  Instantiated per count of real 16-row tiles.
-    auto k_loop = [&](auto mtr) {
+    // S stages, the loads S - 1 k-steps ahead.  At the top of step i this wave's outstanding
+    // loads are those of k-steps i .. i+S-2 (oldest first); waiting until only the later ones
+    // are left puts its part of k-step i in LDS, and the barrier publishes every wave's part
+    // and shows that every wave has finished step i-1, whose stage k-step i+S-1 then reuses.
+    // a_scale group g is loaded with k-step g*kG, S - 1 <= 2 steps before its first use, into
+    // the half that group g-2 used, whose last step (g-1)*kG - 1 is then finished.
+    // Instantiated per count of real 16-row tiles (MTR) and stage form.
+    auto k_loop = [&](auto mtr, auto small) {
         constexpr int MTR = decltype(mtr)::value;
-        issue(0, 0);
+        constexpr bool SMALL = decltype(small)::value;
+        constexpr int S = SMALL ? 3 : 2;
+        constexpr int kSt = SMALL ? kSmallStage : kFullStage;
+        constexpr int kX = kSt - kW;
+        const uint32_t wd = lds0 + kX + wv * (BW / moe_wide::kWaves) * 128;
+#pragma unroll
+        for (int i = 0; i < S - 1; ++i)
+            if (i < KB)
+                issue(i * kSt, wd, i);
         for (int i = 0; i < KB; ++i) {
-            wait_loads(0);
-            __syncthreads();
-            if (i + 1 < KB)
-                issue((i + 1) & 1, i + 1);
+            int later = 0;
+#pragma unroll
+            for (int j = 1; j < S - 1; ++j)
+                later += n_loads(i + j);
+            step_barrier(later);
+            if (i + S - 1 < KB)
+                issue(((i + S - 1) % S) * kSt, wd, i + S - 1);
             if (MTR == 0)
                 continue;
-            const moe_u32x4 *xb = smem + (i & 1) * (kStage / 16);
-            const moe_u32x4 *wb = xb + kBM * 8;
+            const moe_u32x4 *xb = smem + (i % S) * (kSt / 16);
+            const moe_u32x4 *wb = xb + kX / 16;
             moe_i32x8 bx[MTR > 0 ? MTR : 1];
             float s[MTR > 0 ? MTR : 1];
             const float *sa = s_scale[(i / kG) & 1];
+            const int kb = (i + rot) % KB;
+            const float sbv = __int_as_float(
+                kb < 64 ? __builtin_amdgcn_readlane(__float_as_int(sb_lo), kb)
+                        : __builtin_amdgcn_readlane(__float_as_int(sb_hi), kb - 64));
 #pragma unroll
             for (int m = 0; m < MTR; ++m) {
                 const int r = 16 * (wm + kWM * m) + rr;
                 bx[m] = join(xb[St::slot(r, rq)], xb[St::slot(r, rq + 4)]);
-                s[m] = sa[r * kG + i % kG] * sb[i & 1];
+                s[m] = sa[r * kG + i % kG] * sbv;
             }
             // The block sums of weight tile n are scaled into the accumulators while the MFMAs
             // of tile n+1 run (two sets of partials), so no FMA waits on the MFMA just issued.
@@ -703,12 +764,21 @@ __global__ __launch_bounds__(moe_wide::kThreads) void k_fp8_wide(Fp8Problem p, i
             }
         }
     };
-    switch (mt_real) {
-    case 0: k_loop(std::integral_constant<int, 0>()); break;
-    case 1: k_loop(std::integral_constant<int, 1>()); break;
-    case 2: k_loop(std::integral_constant<int, 2>()); break;
-    case 3: k_loop(std::integral_constant<int, 3>()); break;
-    default: k_loop(std::integral_constant<int, 4>()); break;
+    // more than kSmallRows rows give every wave 2 to 4 real 16-row tiles, fewer 0 to 2
+    using Full = std::false_type;
+    using Small = std::true_type;
+    if (n_real <= kSmallRows) {
+        switch (mt_real) {
+        case 0: k_loop(std::integral_constant<int, 0>(), Small()); break;
+        case 1: k_loop(std::integral_constant<int, 1>(), Small()); break;
+        default: k_loop(std::integral_constant<int, 2>(), Small()); break;
+        }
+    } else {
+        switch (mt_real) {
+        case 2: k_loop(std::integral_constant<int, 2>(), Full()); break;
+        case 3: k_loop(std::integral_constant<int, 3>(), Full()); break;
+        default: k_loop(std::integral_constant<int, 4>(), Full()); break;
+        }
     }
 
     // ---- epilogue: lane holds columns 4*(lane/16)+q of row 16*(wm + 4m) + lane%16

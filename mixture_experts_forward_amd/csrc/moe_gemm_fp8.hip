@@ -165,7 +165,7 @@ void launch_fp8_gemm(const uint8_t *a, const float *a_scale, const uint8_t *b,
         launch_fp8_ws(p, stream);
         return;
     }
-    if (max_m <= 64 || p.KB % 4 != 0 || ((uintptr_t)a_scale & 15u) != 0) {
+    if (max_m <= 64 || p.KB % 4 != 0 || p.KB > 128 || ((uintptr_t)a_scale & 15u) != 0) {
         launch_one<64, 4, 2>(p, stream);
         return;
     }
@@ -205,7 +205,7 @@ void launch_fp8_gemm_contig(const uint8_t *a, const float *a_scale, const uint8_
         launch_fp8_ws(p, stream);
         return;
     }
-    if (mean_rows <= 64 || p.KB % 4 != 0 || ((uintptr_t)a_scale & 15u) != 0) {
+    if (mean_rows <= 64 || p.KB % 4 != 0 || p.KB > 128 || ((uintptr_t)a_scale & 15u) != 0) {
         launch_one<64, 4, 2>(p, stream);
         return;
     }

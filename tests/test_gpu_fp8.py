@@ -123,6 +123,8 @@ def _contig_inputs(E, counts, N, K, seed, extra_rows=3):
     (4, [5, 0, 37, 64], 192, 384),            # 64-row form: ragged, an empty expert
     (3, [130, 1, 64], 128, 256),              # 64-row form: several row tiles of one expert
     (3, [300, 77, 256], 256, 1024),           # 256-row form (mean rows > 64), partial tiles
+    (2, [130, 90], 256, 9216),                # 256-row form past 64 k-blocks (a wave's weight
+                                              # scales span two registers)
     (6, [1, 0, 3, 17, 2, 5], 192, 384),       # weight-streaming form (mean rows <= 8): a
                                               # 17-row expert takes two 16-row passes
     (8, [2, 1, 0, 4, 3, 1, 2, 2], 256, 2048),  # weight-streaming form, 4-way K split

@@ -12,7 +12,8 @@ import torch
 import mixture_experts_forward_amd as moe
 import oracle
 from moe_harness.workloads import CONFIGS, make_fp8_weights, make_inputs, to_u16
-from parity import WEIGHT_ATOL, assert_output_close, oracle_route, sample_tokens
+from parity import (WEIGHT_ATOL, assert_output_close, oracle_route, routing_tokens,
+                    sample_tokens)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -141,3 +142,46 @@ def test_fp8_stages_given_routing(T, k, E, pattern):
             continue
         rel = assert_output_close(out, ref, "fp8 stages %s %s" % (pattern, path))
         print("fp8 stages %s %s: rel-L2 %.2e" % (pattern, path, rel), flush=True)
+
+
+def _oracle_fp8_sampled(cfg, d, fw, ids, w, tokens):
+    """The oracle's FP8 expert part for ``tokens``, with only the experts those tokens touch
+    copied to the host."""
+    sub = np.asarray(ids)[tokens]
+    ok = (sub >= 0) & (sub < cfg.E)
+    used = np.unique(sub[ok])
+    remap = np.full(cfg.E, -1, np.int64)
+    remap[used] = np.arange(used.size)
+    local = np.where(ok, remap[np.clip(sub, 0, cfg.E - 1)], -1).astype(np.int32)
+    sel = torch.as_tensor(used, device=DEV, dtype=torch.long)
+    h = {kk: v.index_select(0, sel).cpu().numpy() for kk, v in fw.items()}
+    x = to_u16(d["hidden_states"][torch.as_tensor(tokens, device=DEV)])
+    return oracle.fp8_experts(x, h["w_gate_up"], h["w_gate_up_scale"], h["w_down"],
+                              h["w_down_scale"], local, np.asarray(w, np.float32)[tokens])
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,E,T", [
+    ("qwen3-235b-prefill", None, None),      # full size: 256 routes per expert on average
+    ("ds-v3-grouped-prefill", 64, 1024),     # DeepSeek-V3 dimensions and routing, 128 routes
+                                             # per expert on average as at 4096 tokens of 256
+])
+def test_fp8_prefill_sampled(name, E, T):
+    """The 256-row FP8 tile (k_fp8_wide) in the pass's launch configuration: both stage forms
+    (tiles of at most 128 rows take three stages), evenly split experts, the route-to-token row
+    map; tokens chosen from the realized routing (the heaviest expert's last tile, every
+    eighth of the expert-sorted routes) against the oracle."""
+    cfg = CONFIGS[name] if E is None else replace(CONFIGS[name], E=E, T=T)
+    d = make_inputs(cfg, DEV, seed=11, weights=False)
+    fw = make_fp8_weights(cfg, DEV, seed=12)
+    out, ids, w = _run(cfg, d, fw, "auto")
+    torch.cuda.synchronize()
+    rid, rw = oracle_route(d, cfg)
+    assert np.array_equal(ids.cpu().numpy(), rid), "routing ids differ"
+    tokens = routing_tokens(rid, cfg.E, 256, n=40)
+    ref = _oracle_fp8_sampled(cfg, d, fw, rid, rw, tokens)
+    rel = assert_output_close(out[torch.as_tensor(tokens, device=DEV)], ref, "fp8 " + name)
+    print("fp8 %s E=%d T=%d: rel-L2 %.2e over %d tokens" % (name, cfg.E, cfg.T, rel, len(tokens)),
+          flush=True)
+    del d, fw
+    torch.cuda.empty_cache()

@@ -197,6 +197,10 @@ __global__ __launch_bounds__(64 * kWaves) void k_tiled_gemm(GemmProblem g, int n
 #pragma unroll
         for (int st = 0; st < STAGES; ++st) {
             load((st + STAGES - 1) % STAGES, i + st + STAGES - 1);
+            // keep the next k-step's loads ahead of this step's wait: the scheduler would
+            // otherwise sink them below this step's LDS writes, leaving nothing in flight
+            // while the wave waits for this step's operands
+            __builtin_amdgcn_sched_barrier(0);
             compute(st, i + st);
         }
     }

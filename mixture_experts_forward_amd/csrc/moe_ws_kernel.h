@@ -185,32 +185,32 @@ __device__ __forceinline__ void ws_body(const GemmProblem &g, int bx, int by, mo
     const int rot =
         nseg > 0 ? (int)((bx * 7u + by * 13u) % (unsigned)nseg) : 0;
 
+    // Every load below is issued on every path, the same number per segment: segments past
+    // the wave's K range (and the prefetch past its end) read one 16-byte line at the start of
+    // the activations, all lanes alike (a cache hit), instead of being skipped.  With loads
+    // under branches the compiler cannot count the outstanding ones and waits for all of them
+    // before each segment's compute, which drains the prefetch.  Weight tiles past the last
+    // column and row slots past the rows read clamped, in-bounds rows (wld, arow).
+    const uint16_t *const dummy = g.act;
+    const int nseg1 = max(nseg, 1);
     moe_u32x4 wraw[STAGES][NW][NLD];
     auto load_w = [&](int st, int i) {
-        const int k = (ks0 + ((i + rot) % nseg) * SEGK) * 64;
+        const bool on = i < nseg;
+        const int k = (ks0 + ((i + rot) % nseg1) * SEGK) * 64;
 #pragma unroll
         for (int nw = 0; nw < NW; ++nw) {
-            if (tile_ok[nw % NT]) {
 #pragma unroll
-                for (int j = 0; j < NLD; ++j)
-                    wraw[st][nw][j] = load_nt(wld[nw] + (size_t)(RPI * j) * K + k);
-            }
+            for (int j = 0; j < NLD; ++j)
+                wraw[st][nw][j] = load_nt(on ? wld[nw] + (size_t)(RPI * j) * K + k : dummy);
         }
     };
-    // The first pass's weight prefetch is issued before its row plan: the plan's dependent
-    // loads (sorted ids or scan -> route -> token row) then overlap the weight latency.
-#pragma unroll
-    for (int st = 0; st < STAGES - 1; ++st)
-        if (st < nseg)
-            load_w(st, st);
 
     for (int pass0 = 0; pass0 < n_rows; pass0 += ROWS) {
-        if (pass0 > 0) {
+        // The pass's weight prefetch is issued before its row plan: the plan's dependent loads
+        // (sorted ids or scan -> route -> token row) then overlap the weight latency.
 #pragma unroll
-            for (int st = 0; st < STAGES - 1; ++st)
-                if (st < nseg)
-                    load_w(st, st);
-        }
+        for (int st = 0; st < STAGES - 1; ++st)
+            load_w(st, st);
         // ---- row plan: activation row and output row of slot lane%16 of each m-tile
         const uint16_t *arow[MT];
         int dst[MT];
@@ -250,15 +250,14 @@ __device__ __forceinline__ void ws_body(const GemmProblem &g, int bx, int by, mo
 
         moe_u32x4 xv[STAGES][SEGK][MT][2];
         auto load_x = [&](int st, int i) {
-            const int k0 = (ks0 + ((i + rot) % nseg) * SEGK) * 64;
+            const bool on = i < nseg;
+            const int k0 = (ks0 + ((i + rot) % nseg1) * SEGK) * 64;
 #pragma unroll
             for (int h = 0; h < SEGK; ++h) {
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
-                    if (mt < mt_active) {
-                        xv[st][h][mt][0] = load_cached(arow[mt] + k0 + 64 * h);
-                        xv[st][h][mt][1] = load_cached(arow[mt] + k0 + 64 * h + 32);
-                    }
+                    xv[st][h][mt][0] = load_cached(on ? arow[mt] + k0 + 64 * h : dummy);
+                    xv[st][h][mt][1] = load_cached(on ? arow[mt] + k0 + 64 * h + 32 : dummy);
                 }
             }
         };
@@ -292,23 +291,20 @@ __device__ __forceinline__ void ws_body(const GemmProblem &g, int bx, int by, mo
             moe_wave_sync();
         };
 
-        // software pipeline: STAGES-1 segments in flight (their weights already requested)
+        // software pipeline: STAGES-1 segments in flight (their weights already requested);
+        // the loads are issued ahead of the segment's compute on every path (see above)
 #pragma unroll
         for (int st = 0; st < STAGES - 1; ++st)
-            if (st < nseg)
-                load_x(st, st);
+            load_x(st, st);
         for (int i = 0; i < nseg; i += STAGES) {
 #pragma unroll
             for (int st = 0; st < STAGES; ++st) {
                 const int cur = i + st;
-                if (cur < nseg) {
-                    const int nxt = cur + STAGES - 1;
-                    if (nxt < nseg) {
-                        load_w((st + STAGES - 1) % STAGES, nxt);
-                        load_x((st + STAGES - 1) % STAGES, nxt);
-                    }
+                load_w((st + STAGES - 1) % STAGES, cur + STAGES - 1);
+                load_x((st + STAGES - 1) % STAGES, cur + STAGES - 1);
+                __builtin_amdgcn_sched_barrier(0);
+                if (cur < nseg)
                     compute(st);
-                }
             }
         }
 

@@ -449,32 +449,39 @@ void k_fp8_ws(Fp8Problem p)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
             acc[nt] = moe_f32x4{0.f, 0.f, 0.f, 0.f};
+        // Every load is issued on every path, the same number per segment: past the wave's K
+        // range they read one cached line at the start of the weights' scales (all lanes
+        // alike), past the last column the clamped row 0.  With loads under branches the
+        // compiler cannot count the outstanding ones and waits for all of them before each
+        // segment's compute, which drains the prefetch.
+        const uint8_t *const dummy = reinterpret_cast<const uint8_t *>(p.b_scale);
+        const int nseg1 = max(nseg, 1);
         moe_u32x4 w[STAGES][NT][2 * SEG], x[STAGES][SEG][2];
         float sa[STAGES][SEG], sb[STAGES][SEG][NT];
         auto load = [&](int st, int i) {
-            const int kb = kb0 + ((i + rot) % nseg) * SEG;  // first K block of segment i
+            const bool on = i < nseg;
+            const int kb = kb0 + ((i + rot) % nseg1) * SEG;  // first K block of segment i
             const int k = kb * 128;
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-                if (tile_ok[nt]) {
-                    if (SEG == 1) {
-                        w[st][nt][0] = load_nt16(wrow[nt] + k);
-                        w[st][nt][1] = load_nt16(wrow[nt] + k + 64);
-                    } else {
+                if (SEG == 1) {
+                    w[st][nt][0] = load_nt16(on ? wrow[nt] + k : dummy);
+                    w[st][nt][1] = load_nt16(on ? wrow[nt] + k + 64 : dummy);
+                } else {
 #pragma unroll
-                        for (int j = 0; j < 2 * SEG; ++j)
-                            w[st][nt][j] = load_nt16(wrow[nt] + (size_t)(4 * j) * K + k);
-                    }
-#pragma unroll
-                    for (int h = 0; h < SEG; ++h)
-                        sb[st][h][nt] = p.b_scale[sb_base[nt] + kb + h];
+                    for (int j = 0; j < 2 * SEG; ++j)
+                        w[st][nt][j] = load_nt16(on ? wrow[nt] + (size_t)(4 * j) * K + k : dummy);
                 }
+#pragma unroll
+                for (int h = 0; h < SEG; ++h)
+                    sb[st][h][nt] = on ? p.b_scale[sb_base[nt] + kb + h]
+                                       : *reinterpret_cast<const float *>(dummy);
             }
 #pragma unroll
             for (int h = 0; h < SEG; ++h) {
-                x[st][h][0] = load16(arow + k + 128 * h);
-                x[st][h][1] = load16(arow + k + 128 * h + 64);
-                sa[st][h] = asc[kb + h];
+                x[st][h][0] = load16(on ? arow + k + 128 * h : dummy);
+                x[st][h][1] = load16(on ? arow + k + 128 * h + 64 : dummy);
+                sa[st][h] = on ? asc[kb + h] : *reinterpret_cast<const float *>(dummy);
             }
         };
         auto compute = [&](int st) {
@@ -510,18 +517,15 @@ void k_fp8_ws(Fp8Problem p)
         // software pipeline: STAGES-1 segments in flight
 #pragma unroll
         for (int st = 0; st < STAGES - 1; ++st)
-            if (st < nseg)
-                load(st, st);
+            load(st, st);
         for (int i = 0; i < nseg; i += STAGES) {
 #pragma unroll
             for (int st = 0; st < STAGES; ++st) {
                 const int cur = i + st;
-                if (cur < nseg) {
-                    const int nxt = cur + STAGES - 1;
-                    if (nxt < nseg)
-                        load((st + STAGES - 1) % STAGES, nxt);
+                load((st + STAGES - 1) % STAGES, cur + STAGES - 1);
+                __builtin_amdgcn_sched_barrier(0);
+                if (cur < nseg)
                     compute(st);
-                }
             }
         }
 
@@ -911,28 +915,34 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_fp8_direct(Fp8Direct d)
     moe_f32x4 acc[NW];
     moe_u32x4 wv[STAGES][NW][2 * SEG];
     float sb[STAGES][SEG][NW];
+    // Every load is issued on every path, the same number per segment (past the wave's K range:
+    // one cached line at the start of the weight scales; past the last column: the clamped row
+    // 0), so the compiler counts the outstanding loads exactly instead of waiting for all of
+    // them before each segment's compute.
+    const uint8_t *const dummy = reinterpret_cast<const uint8_t *>(d.b_scale);
+    const int nseg1 = max(nseg, 1);
     auto load = [&](int st, int i) {
-        const int kb = kb0 + ((i + rot) % nseg) * SEG;  // first K block of segment i
+        const bool on = i < nseg;
+        const int kb = kb0 + ((i + rot) % nseg1) * SEG;  // first K block of segment i
         const int k = kb * 128;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
-            if (!tile_ok[w % NT])
-                continue;
             if (SEG == 1) {
-                wv[st][w][0] = load_nt16(wrow[w] + k);
-                wv[st][w][1] = load_nt16(wrow[w] + k + 64);
+                wv[st][w][0] = load_nt16(on ? wrow[w] + k : dummy);
+                wv[st][w][1] = load_nt16(on ? wrow[w] + k + 64 : dummy);
             } else {
 #pragma unroll
                 for (int j = 0; j < 2 * SEG; ++j)
-                    wv[st][w][j] = load_nt16(wrow[w] + (size_t)(4 * j) * K + k);
+                    wv[st][w][j] = load_nt16(on ? wrow[w] + (size_t)(4 * j) * K + k : dummy);
             }
 #pragma unroll
             for (int h = 0; h < SEG; ++h)
-                sb[st][h][w] = d.b_scale[sb_base[w] + kb + h];
+                sb[st][h][w] = on ? d.b_scale[sb_base[w] + kb + h]
+                                  : *reinterpret_cast<const float *>(dummy);
         }
     };
     auto compute = [&](int st, int i) {
-        const int kb = kb0 + ((i + rot) % nseg) * SEG;
+        const int kb = kb0 + ((i + rot) % nseg1) * SEG;
         if (SEG > 1) {
 #pragma unroll
             for (int w = 0; w < NW; ++w)
@@ -970,8 +980,7 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_fp8_direct(Fp8Direct d)
     auto prologue = [&] {
 #pragma unroll
         for (int st = 0; st < STAGES - 1; ++st)
-            if (st < nseg)
-                load(st, st);
+            load(st, st);
     };
     prologue();
 
@@ -1025,12 +1034,10 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_fp8_direct(Fp8Direct d)
 #pragma unroll
             for (int st = 0; st < STAGES; ++st) {
                 const int cur = i + st;
-                if (cur < nseg) {
-                    const int nxt = cur + STAGES - 1;
-                    if (nxt < nseg)
-                        load((st + STAGES - 1) % STAGES, nxt);
+                load((st + STAGES - 1) % STAGES, cur + STAGES - 1);
+                __builtin_amdgcn_sched_barrier(0);
+                if (cur < nseg)
                     compute(st, cur);
-                }
             }
         }
 

@@ -138,14 +138,29 @@ __device__ __forceinline__ bool fp8_locate(const Fp8Problem &p, int n_blocks, in
         o.rbase = o.expert * p.max_m + row0;
         return o.n_rows > 0;
     }
+    // Lane l owns the run of experts [e0, e1), run = ceil(E / 64) <= 16 (E <= 1024): its
+    // run + 1 offsets are loaded together (indices clamped to E, so every load is in bounds and
+    // issued on every path; one wait), the run's tile counts summed and prefix-summed over the
+    // wave.  The lane whose range holds tile t finds the expert in its registers, and every
+    // lane reads that lane's result.
+    constexpr int kMaxRun = 16;
     const int lane = threadIdx.x & 63;
     const int run = (p.E + 63) / 64;
-    const int e0 = min(p.E, lane * run), e1 = min(p.E, e0 + run);
+    const int e0 = min(p.E, lane * run);
+    int off[kMaxRun + 1];
+#pragma unroll
+    for (int j = 0; j <= kMaxRun; ++j)
+        off[j] = p.offsets[min(e0 + j, p.E)];
+    // rows of expert e0 + j as contig_rows gives them: [lo_j, hi_j), lo_j = clamp(off_j, 0, P),
+    // hi_j = clamp(off_{j+1}, lo_j, P); experts past the run or past E count none
+    int cnt[kMaxRun], lo[kMaxRun];
     int mine = 0;
-    for (int e = e0; e < e1; ++e) {
-        int r0, r1;
-        contig_rows(p, e, r0, r1);
-        mine += (r1 - r0 + BM - 1) / BM * n_blocks;
+#pragma unroll
+    for (int j = 0; j < kMaxRun; ++j) {
+        lo[j] = min(max(off[j], 0), p.P);
+        const int hi = min(max(off[j + 1], lo[j]), p.P);
+        cnt[j] = (j < run && e0 + j < p.E) ? hi - lo[j] : 0;
+        mine += (cnt[j] + BM - 1) / BM * n_blocks;
     }
     int incl = mine;
 #pragma unroll
@@ -161,16 +176,23 @@ __device__ __forceinline__ bool fp8_locate(const Fp8Problem &p, int n_blocks, in
         return false;
     const unsigned long long hit = __ballot(t >= incl - mine && t < incl);
     const int owner = __ffsll((long long)hit) - 1;
-    int e = __shfl(e0, owner), cum = __shfl(incl - mine, owner);
-    const int e_end = __shfl(e1, owner);
-    int r0 = 0, r1 = 0;
-    for (; e < e_end; ++e) {
-        contig_rows(p, e, r0, r1);
-        const int te = (r1 - r0 + BM - 1) / BM * n_blocks;
-        if (t < cum + te)
-            break;
-        cum += te;
+    // every lane walks its own run for t (only the owner's walk is used)
+    int cum = incl - mine, je = 0, r0 = 0, c = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxRun; ++j) {
+        const int te = (cnt[j] + BM - 1) / BM * n_blocks;
+        if (t >= cum && t < cum + te && c == 0) {
+            je = j;
+            r0 = lo[j];
+            c = cnt[j];
+        }
+        if (c == 0)
+            cum += te;
     }
+    const int e = __builtin_amdgcn_readlane(e0 + je, owner);
+    cum = __builtin_amdgcn_readlane(cum, owner);
+    r0 = __builtin_amdgcn_readlane(r0, owner);
+    const int r1 = r0 + __builtin_amdgcn_readlane(c, owner);
     const int mt_e = (r1 - r0 + BM - 1) / BM;
     const int rem = t - cum;
     o.expert = e;

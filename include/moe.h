@@ -292,7 +292,11 @@ int fused_moe_experts_stage(int stage, const uint16_t *hidden_states, const uint
  * (rows [0,F) of w_gate_up are gate, [F,2F) up).  For scales up to 252 the dequantised
  * weights are exact in bf16, so the sums are those of the bf16 pass on those weights.  Needs p->dtype == MOE_DTYPE_BF16,
  * H % 128 == 0 and F % 128 == 0; 16-byte aligned hidden_states, the code tensors, out and the
- * workspace.  No shared expert.
+ * workspace, 4-byte aligned scale tensors.  No shared expert.
+ * Kernels by routed rows per expert (T*k/E): up to 8, weight streaming in 16-row passes; up to
+ * 64, 64-row tiles, each wave dequantising its weight rows into its MFMA operands; above, with
+ * H and F multiples of 256, 256 x 256 tiles whose weights arrive as codes and scales by DMA and
+ * are dequantised into the tile's bf16 LDS stage (the bf16 pass's prefill kernel otherwise).
  * Workspace: fused_moe_mxfp4_workspace_bytes(p) bytes.
  * Errors: as fused_moe_fwd. */
 size_t fused_moe_mxfp4_workspace_bytes(const moe_params_t *p);

@@ -15,6 +15,7 @@
 namespace {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
 
 // A roctx range around one entry point's enqueue, so that a profiler's marker trace shows which
 // kernels each forward call launched (a no-op unless a profiler is attached).
@@ -129,6 +130,8 @@ bool launch_gemm(bool gate_up, const moe::GemmProblem &g, moe::RowSource src,
         return moe::launch_mx(gate_up, g, src, ws_tile(t), stream);
     if (t.kind == moe::KERNEL_MX_TILED)
         return moe::launch_mx_tiled(gate_up, g, src, ws_tile(t), stream);
+    if (t.kind == moe::KERNEL_MX_WIDE)
+        return moe::launch_wide_mx(gate_up, g, src, stream);
     return gate_up ? moe::launch_gate_up(g, src, ws_tile(t), stream)
                    : moe::launch_down(g, src, ws_tile(t), stream);
 }
@@ -496,7 +499,8 @@ int fused_moe_mxfp4_fwd(const uint16_t *hidden_states, const float *gating_outpu
     if (workspace_bytes < pl.total)
         return MOE_ERR_WORKSPACE;
     if (!aligned16(hidden_states) || !aligned16(w_gate_up_q) || !aligned16(w_down_q) ||
-        !aligned16(out) || !aligned16(workspace))
+        !aligned4(w_gate_up_scale) || !aligned4(w_down_scale) || !aligned16(out) ||
+        !aligned16(workspace))
         return MOE_ERR_UNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(stream);
     int32_t *ids = topk_ids_out ? topk_ids_out : ws_at<int32_t>(workspace, pl.off_ids);
@@ -738,7 +742,7 @@ int fused_moe_mxfp4_stage(int stage, const uint16_t *hidden_states, const uint8_
         return MOE_ERR_WORKSPACE;
     if (!aligned16(workspace) || (hidden_states && !aligned16(hidden_states)) ||
         (w_gate_up_q && !aligned16(w_gate_up_q)) || (w_down_q && !aligned16(w_down_q)) ||
-        (out && !aligned16(out)))
+        !aligned4(w_gate_up_scale) || !aligned4(w_down_scale) || (out && !aligned16(out)))
         return MOE_ERR_UNSUPPORTED;
     Ctx c = {hidden_states, nullptr, nullptr, nullptr, nullptr, topk_ids, topk_weights, out,
              workspace, static_cast<hipStream_t>(stream)};

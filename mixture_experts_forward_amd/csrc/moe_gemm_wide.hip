@@ -85,9 +85,33 @@ void launch_one(const GemmProblem &g, hipStream_t stream)
         launch_typed<GATE_UP, SRC, 0>(g, stream);
 }
 
+template <bool GATE_UP>
+void launch_mx_typed(const GemmProblem &g, hipStream_t stream)
+{
+    const auto kernel = moe_wide::k_wide_mx<GATE_UP>;
+    const int cols = GATE_UP ? moe_wide::kBW / 2 : moe_wide::kBW;
+    const int n_blocks = (g.n_out + cols - 1) / cols;
+    const int m_tiles = g.num_groups;
+    const int grid = moe_wide::wide_grid(n_blocks * m_tiles, per_cu(kernel) * device_cus());
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(moe_wide::kThreads), 0, stream, g, n_blocks,
+                       m_tiles);
+}
+
 }  // namespace
 
 namespace moe {
+
+bool launch_wide_mx(bool gate_up, const GemmProblem &g, RowSource src, hipStream_t stream)
+{
+    // sorted rows with a schedule; K a multiple of 256 (whole scale groups of 4 k-steps)
+    if (src != ROWS_SORTED || g.sched == nullptr || g.K % 256 != 0)
+        return false;
+    if (gate_up)
+        launch_mx_typed<true>(g, stream);
+    else
+        launch_mx_typed<false>(g, stream);
+    return true;
+}
 
 bool launch_wide(bool gate_up, const GemmProblem &g, RowSource src, hipStream_t stream)
 {

@@ -113,6 +113,10 @@ bool launch_mx(bool gate_up, const GemmProblem &g, RowSource src, WsTile tile,
 // 16-column tiles per wave, tile.stages).
 bool launch_mx_tiled(bool gate_up, const GemmProblem &g, RowSource src, WsTile tile,
                      hipStream_t stream);
+// The 256 x 256 tile GEMM with MXFP4 weights dequantised into its bf16 weight stages
+// (moe_wide_kernel.h, k_wide_mx): ROWS_SORTED with block_m = 256, a schedule (g.sched) and
+// K % 256 == 0; false (nothing launched) otherwise.
+bool launch_wide_mx(bool gate_up, const GemmProblem &g, RowSource src, hipStream_t stream);
 
 // ---------------------------------------------------------------- fp8 grouped GEMM
 // out[e, m, n] for m < masked_m[e] (moe_fp8_kernel.h); K % 128 == 0, N % 64 == 0.

@@ -22,32 +22,13 @@
 
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "moe_mx_dequant.h"
 #include "moe_tiled_kernel.h"
 #include "moe_ws_kernel.h"
 
 namespace moe_mx {
 
 using moe::GemmProblem;
-
-typedef __bf16 moe_bf16x2 __attribute__((ext_vector_type(2)));
-
-// E8M0 scale byte -> f32: 2^(s-127) (s = 0 is the subnormal 2^-127, s = 255 is NaN)
-__device__ __forceinline__ float e8m0_to_f32(uint32_t s)
-{
-    const uint32_t bits = s == 0u ? 0x00400000u : (s == 255u ? 0x7FC00000u : s << 23);
-    return __uint_as_float(bits);
-}
-
-// one word of four code bytes -> eight bf16 (two per byte, low nibble first), times scale
-__device__ __forceinline__ moe_u32x4 dequant8(uint32_t w, float scale)
-{
-    moe_u32x4 o;
-    o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
-    o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
-    o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
-    o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
-    return o;
-}
 
 template <bool GATE_UP, int SRC, int NT, int KSPLIT, int STAGES>
 __global__ __launch_bounds__(64 * KSPLIT) void k_mx_gemm(GemmProblem g)

@@ -107,10 +107,14 @@ void make_plan(const moe_params_t *p, int32_t S, Plan *pl, int wfmt)
     if (wfmt == WEIGHTS_MXFP4) {
         // MXFP4 weights (W4A16): the weight-streaming form with 16-row passes up to 8 routed
         // rows per expert, the row-tiled form (64-row tiles, each weight byte feeding 64 rows)
-        // above
+        // up to 64, the 256 x 256 tile with the weights dequantised into its LDS stages above
+        // (both K, H and F, whole groups of 256)
         if (pl->path == MOE_PATH_DIRECT || mean_rows <= 8.0) {
             pl->gate_up = {KERNEL_MX, 1, 1, 2, 3};
             pl->down = {KERNEL_MX, 2, 1, 2, 3};
+        } else if (mean_rows > 64.0 && pl->H % 256 == 0 && pl->F % 256 == 0) {
+            pl->gate_up = {KERNEL_MX_WIDE, 0, 16, 1, 2};
+            pl->down = {KERNEL_MX_WIDE, 0, 16, 1, 2};
         } else {
             pl->gate_up = {KERNEL_MX_TILED, 1, 4, 1, 3};
             pl->down = {KERNEL_MX_TILED, 2, 4, 1, 3};
@@ -130,7 +134,7 @@ void make_plan(const moe_params_t *p, int32_t S, Plan *pl, int wfmt)
     // 256-row tiles: an expert's routes spread evenly over its tiles, so that the tiles of a
     // heavy expert (which read the same weight rows) run at the same pace and share those
     // rows in L2, instead of a ragged last tile streaming them on its own
-    pl->balanced = pl->gate_up.kind == KERNEL_WIDE;
+    pl->balanced = pl->gate_up.kind == KERNEL_WIDE || pl->gate_up.kind == KERNEL_MX_WIDE;
     pl->slots = P + pl->E * (pl->block_m - 1);
     pl->tiles_cap = P / pl->block_m + pl->E;
 
@@ -149,7 +153,7 @@ void make_plan(const moe_params_t *p, int32_t S, Plan *pl, int wfmt)
         pl->off_inverse = take((size_t)P * 4);
         pl->off_n_tiles = take(4);
         // per-XCD tile ranges of the 256 x 256 tile kernel (moe_internal.h's TileSchedule)
-        pl->off_sched = pl->gate_up.kind == KERNEL_WIDE ? take(2 * 4 * 9) : 0;
+        pl->off_sched = pl->balanced ? take(2 * 4 * 9) : 0;
         const size_t scratch = align_scratch_ints(P, pl->E, pl->balanced);
         pl->off_align = scratch ? take(scratch * 4) : 0;
         pl->off_h = take((size_t)pl->slots * pl->F * 2);

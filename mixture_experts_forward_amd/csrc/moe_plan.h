@@ -33,7 +33,8 @@ enum KernelKind {
     KERNEL_TILED = 1,
     KERNEL_WIDE = 3,
     KERNEL_MX = 4,
-    KERNEL_MX_TILED = 5
+    KERNEL_MX_TILED = 5,
+    KERNEL_MX_WIDE = 6
 };
 
 // Weight format of the routed experts: 16-bit (bf16 / f16) or MXFP4.

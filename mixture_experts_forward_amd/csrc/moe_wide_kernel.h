@@ -37,6 +37,7 @@
 
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "moe_mx_dequant.h"
 
 namespace moe_wide {
 
@@ -84,6 +85,15 @@ inline int wide_grid(int total_cap, int slots)
 __device__ __forceinline__ void dma16(const void *g, uint32_t lds_base)
 {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(g), "s"(lds_base)
+                 : "memory", "m0");
+}
+
+// The same for 4 bytes a lane (lane l writes LDS bytes lds_base + 4l .. + 3).
+__device__ __forceinline__ void dma4(const void *g, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
                  :
                  : "v"(g), "s"(lds_base)
                  : "memory", "m0");
@@ -219,7 +229,9 @@ struct NoHook {
     __device__ void operator()() const {}
 };
 
-template <bool GATE_UP, int SRC, int WS, int DT, typename Hook = NoHook>
+// MX: the weights are MXFP4 (g.wq, g.wscale) and are dequantised into the bf16 weight stages
+// (k_loop_mx below); sorted rows, the whole K range, K a multiple of 256.
+template <bool GATE_UP, int SRC, int WS, int DT, bool MX = false, typename Hook = NoHook>
 __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mtile, int expert,
                                           moe_u32x4 *smem, int kbeg = 0, int kcnt = -1,
                                           float *part = nullptr, Hook hook = Hook())
@@ -244,7 +256,7 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
     // that lane writes (a wave instruction fills 1 KB of LDS, lane l at 16 * l).
     const int lrow = lane / kSlots, lpos = lane % kSlots;
     const int w_rows = GATE_UP ? 2 * g.n_out : g.n_out;
-    const uint16_t *W = g.weight + (size_t)expert * w_rows * K;
+    const uint16_t *W = MX ? nullptr : g.weight + (size_t)expert * w_rows * K;
     const uint16_t *wsrc[kWLoads];
 #pragma unroll
     for (int j = 0; j < kWLoads; ++j) {
@@ -303,7 +315,9 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
     // before the tile's last)
     const int hook_at = nk > 3 ? nk - 3 : 0;
     const unsigned rkey = SRC == moe::ROWS_SORTED ? expert : nblk;
-    const int rot = (int)((rkey * 7u) % (unsigned)nk);
+    // (MX: a multiple of 4, so every run of 4 visits from a multiple of 4 is one scale group)
+    const int rot = MX ? (int)((rkey * 7u) % (unsigned)(nk / 4)) * 4
+                       : (int)((rkey * 7u) % (unsigned)nk);
 
     moe_f32x16 acc[kMT32][kNT32];
 #pragma unroll
@@ -373,6 +387,102 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
                 if (h + 1 < kStep / 16)
                     read((h + 1) & 1, h + 1);
                 __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of these MFMAs
+#pragma unroll
+                for (int n = 0; n < kNT32; ++n)
+#pragma unroll
+                    for (int m = 0; m < MTR; ++m)
+                        acc[m][n] = moe_mma32<DT>(a[h & 1][n], b[h & 1][m], acc[m][n]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
+    // ---- MXFP4 weights.  A k-step of the tile's 256 weight rows is 32 code bytes a row (two
+    // e2m1 codes per byte, low nibble first) and, per group of 4 k-steps, 8 E8M0 scale bytes a
+    // row (one per 32 elements); both come by DMA into LDS, the codes two k-steps ahead of the
+    // MFMAs (three 8 KB slots), the scales with the group's first k-step (two 2 KB buffers).
+    // One k-step ahead of the MFMAs each thread turns half a row's k-step (16 code bytes, one
+    // scale) into four bf16 chunks of the weight stage, in the slots the bf16 weight DMA fills,
+    // so the MFMA block is the bf16 one.  LDS: activation stages [0, 64 KB), bf16 weight stages
+    // [64, 128 KB), code slots [128, 152 KB), scale buffers [152, 156 KB).
+    // DMA lanes: lane l of wave w covers weight row 32w + l/2 (codes: bytes 16(l%2) .. +15 of
+    // the row's k-step; scales: the group's bytes 4(l%2) .. +3), writing LDS at 16l / 4l.
+    constexpr uint32_t kMxW = kXStages * kHalf;
+    constexpr uint32_t kMxCodeSlot = kBW * kStep / 2;
+    constexpr uint32_t kMxCodes = kMxW + 2 * kHalf;
+    constexpr uint32_t kMxScaleBuf = kBW * 8;
+    constexpr uint32_t kMxScales = kMxCodes + 3 * kMxCodeSlot;
+    static_assert(kMxScales + 2 * kMxScaleBuf <= wide_lds_bytes<3>(), "MX stages fit the LDS");
+    const uint8_t *mx_code = nullptr, *mx_scale = nullptr;
+    if (MX) {
+        const int r = wv * (kBW / kWaves) + (lane >> 1);  // weight row within the tile
+        const int c = col_wg + (GATE_UP ? r % (kBW / 2) : r);
+        const int src = (GATE_UP && r >= kBW / 2) ? c + g.n_out : c;
+        const size_t row = (size_t)expert * w_rows + (c < g.n_out ? src : 0);
+        mx_code = g.wq + row * (size_t)(K / 2) + 16 * (lane & 1);
+        mx_scale = g.wscale + row * (size_t)(K / 32) + 4 * (lane & 1);
+    }
+    auto issue_c = [&](int i) {  // codes of k-step i (and, at a group's first, its scales)
+        const int ks = (i + rot) % nk;
+        dma16(mx_code + ks * 32,
+              __builtin_amdgcn_readfirstlane(lds0 + kMxCodes + (i % 3) * kMxCodeSlot + wv * 1024));
+        if (i % 4 == 0)
+            dma4(mx_scale + ks * 2, __builtin_amdgcn_readfirstlane(
+                                        lds0 + kMxScales + ((i / 4) % 2) * kMxScaleBuf + wv * 256));
+    };
+    auto dequant = [&](int i) {  // k-step i's codes -> bf16 weight stage i % 2
+        const int r = tid >> 1, hh = tid & 1;
+        const int ks = (i + rot) % nk;
+        const uint8_t *sm8 = reinterpret_cast<const uint8_t *>(smem);
+        const moe_u32x4 q = *reinterpret_cast<const moe_u32x4 *>(
+            sm8 + kMxCodes + (i % 3) * kMxCodeSlot + r * 32 + 16 * hh);
+        const float sc = moe_mx::e8m0_to_f32(
+            sm8[kMxScales + ((i / 4) % 2) * kMxScaleBuf + r * 8 + (ks % 4) * 2 + hh]);
+        moe_u32x4 *wst = smem + (kMxW + (i % 2) * kHalf) / 16;
+        wst[St::slot(r, 4 * hh + 0)] = moe_mx::dequant8(q.x, sc);
+        wst[St::slot(r, 4 * hh + 1)] = moe_mx::dequant8(q.y, sc);
+        wst[St::slot(r, 4 * hh + 2)] = moe_mx::dequant8(q.z, sc);
+        wst[St::slot(r, 4 * hh + 3)] = moe_mx::dequant8(q.w, sc);
+    };
+    // Step i: wait for every load of this wave (x(i), the codes of i+1 and their group's
+    // scales), barrier (every wave's parts landed, its dequantised stage i written, its step
+    // i-1 reads done); issue x(i+1) and the codes of i+2 into buffers whose last readers were
+    // steps i-1 and i-2; dequantise k-step i+1 into the weight stage step i-1 read; MFMAs of i.
+    auto k_loop_mx = [&](auto mtr) {
+        constexpr int MTR = decltype(mtr)::value;
+        issue_x(0);
+        issue_c(0);
+        issue_c(1);
+        step_barrier(0);
+        dequant(0);
+        for (int i = 0; i < nk; ++i) {
+            step_barrier(0);
+            if (i + 1 < nk)
+                issue_x(i + 1);
+            if (i + 2 < nk)
+                issue_c(i + 2);
+            if (i == hook_at)
+                hook();
+            if (i + 1 < nk)
+                dequant(i + 1);
+            if (MTR == 0)
+                continue;
+            const moe_u32x4 *xb = smem + (i % kXStages) * (kHalf / 16);
+            const moe_u32x4 *wb = smem + (kMxW + (i % 2) * kHalf) / 16;
+            moe_u32x4 a[2][kNT32], b[2][MTR > 0 ? MTR : 1];
+            auto read = [&](int buf, int h) {
+#pragma unroll
+                for (int m = 0; m < MTR; ++m)
+                    b[buf][m] = xb[St::slot(32 * (wm + kWM * m) + rr, 2 * h + rq)];
+#pragma unroll
+                for (int n = 0; n < kNT32; ++n)
+                    a[buf][n] = wb[St::slot(wrow0[n] + rr, 2 * h + rq)];
+            };
+            read(0, 0);
+#pragma unroll
+            for (int h = 0; h < kStep / 16; ++h) {
+                if (h + 1 < kStep / 16)
+                    read((h + 1) & 1, h + 1);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int n = 0; n < kNT32; ++n)
 #pragma unroll
@@ -452,7 +562,13 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
             }
         }
     };
-    if (n_real <= kSmallRows) {
+    if (MX) {
+        switch (mt_real) {
+        case 0: k_loop_mx(std::integral_constant<int, 0>()); break;
+        case 1: k_loop_mx(std::integral_constant<int, 1>()); break;
+        default: k_loop_mx(std::integral_constant<int, 2>()); break;
+        }
+    } else if (n_real <= kSmallRows) {
         if (mt_real == 0)
             k_loop_small(std::integral_constant<int, 0>());
         else
@@ -577,7 +693,7 @@ __device__ __forceinline__ int sched_bound(const moe::TileSchedule *sched, int p
 // and share its L2), and once range x is used up, the next tiles of ranges x+1, x+2, ...  The
 // workgroup leaves when every range is used up; the last one to leave zeroes the counters for
 // the next launch.  No workgroup ever waits for another.
-template <bool GATE_UP, int SRC, int WS, int DT>
+template <bool GATE_UP, int SRC, int WS, int DT, bool MX = false>
 __device__ __forceinline__ void wide_queue_loop(const GemmProblem &g, int n_blocks, int total,
                                                 moe_u32x4 *smem)
 {
@@ -621,7 +737,7 @@ __device__ __forceinline__ void wide_queue_loop(const GemmProblem &g, int n_bloc
         // Three k-steps before the tile ends, thread 0 takes the next tile number from its
         // range's counter; the round trip overlaps the tile's last k-steps and the result is
         // first read after the tile (the take needs no load: the bounds are in registers).
-        wide_tile<GATE_UP, SRC, WS, DT>(g, nblk, mtile, expert, smem, 0, -1, nullptr, [&]() {
+        wide_tile<GATE_UP, SRC, WS, DT, MX>(g, nblk, mtile, expert, smem, 0, -1, nullptr, [&]() {
             if (threadIdx.x == 0 && tried < P && lo < hi)
                 pend = atomicAdd(&sched->queue[(home + tried) % P], 1);
         });
@@ -755,6 +871,15 @@ __global__ __launch_bounds__(kThreads) void k_wide_gemm(GemmProblem g, int n_blo
         wide_tile<GATE_UP, SRC, WS, DT>(g, nblk, mtile, expert, smem);
         __syncthreads();  // the next tile's first loads follow every wave's last reads
     }
+}
+
+// MXFP4 weights on sorted rows with a schedule (the queue loop above, k_loop_mx per tile).
+template <bool GATE_UP>
+__global__ __launch_bounds__(kThreads) void k_wide_mx(GemmProblem g, int n_blocks, int m_tiles)
+{
+    __shared__ moe_u32x4 smem[wide_lds_bytes<3>() / 16];
+    const int total = wide_total<moe::ROWS_SORTED>(g, n_blocks, m_tiles);
+    wide_queue_loop<GATE_UP, moe::ROWS_SORTED, 3, 0, true>(g, n_blocks, total, smem);
 }
 
 }  // namespace moe_wide

@@ -2,9 +2,9 @@
 E8M0 scales per 32 elements, bf16 activations) against the oracle: the routed experts'
 computation on the dequantised weights (exact in bf16 at these scales), with the bf16 pass's
 tolerance (tests/parity.py).  Covers the direct path (route and scan workgroups), the sorted
-path with 16-row passes (a few rows per expert) and with 64-row tiles (tens of rows per expert
-and more: the row-tiled form), full qwen3-30b decode and qwen3-235b batch dimensions on sampled
-tokens."""
+path with 16-row passes (a few rows per expert), with 64-row tiles (tens of rows per expert: the
+row-tiled form) and with 256 x 256 tiles (more than 64 rows per expert), full qwen3-30b decode
+and qwen3-235b batch dimensions and DeepSeek-V3 dimensions on sampled tokens."""
 from dataclasses import replace
 
 import numpy as np
@@ -14,7 +14,8 @@ import torch
 import mixture_experts_forward_amd as moe
 import oracle
 from moe_harness.workloads import CONFIGS, make_inputs, make_mxfp4_weights, to_u16
-from parity import WEIGHT_ATOL, assert_output_close, oracle_route, sample_tokens
+from parity import (WEIGHT_ATOL, assert_output_close, oracle_route, routing_tokens,
+                    sample_tokens)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -85,7 +86,8 @@ def test_mxfp4_grouped_sigmoid_routing():
 
 
 @pytest.mark.parametrize("T,E,k,H,F", [
-    (300, 8, 4, 256, 256),     # ~150 rows per expert: three 64-row tiles, a ragged last one
+    (300, 8, 4, 384, 256),     # ~150 rows per expert, H not a multiple of 256: 64-row tiles,
+                               # three per expert, a ragged last one
     (70, 16, 8, 384, 128),     # ~35 rows per expert: one partial tile each, 3 k-steps
     (33, 4, 2, 128, 128),      # 16-17 rows: one 16-row MFMA tile and a one-row one
 ])
@@ -94,6 +96,34 @@ def test_mxfp4_row_tiled_sizes(T, E, k, H, F):
     d = make_inputs(cfg, DEV, seed=T + 1, weights=False)
     mx = make_mxfp4_weights(cfg, DEV, seed=T + 1)
     _check(cfg, d, mx, "auto", what="mxfp4 tiled T=%d E=%d" % (T, E))
+
+
+@pytest.mark.parametrize("T,E,k,H,F", [
+    (300, 8, 4, 256, 256),     # ~150 rows per expert: one 256-row tile each; K 256 for both
+                               # GEMMs (4 k-steps: one scale group)
+    (512, 4, 2, 512, 256),     # ~256 rows: experts past 256 rows split evenly over two tiles;
+                               # gate-up K 512 (two scale groups, rotated start)
+    (200, 4, 2, 768, 512),     # ~100 rows; K 768 and 512 (three and two groups)
+])
+def test_mxfp4_wide_sizes(T, E, k, H, F):
+    """More than 64 routed rows per expert with H and F multiples of 256: the 256 x 256 tile
+    with the codes and scales brought in by DMA and dequantised into its bf16 LDS stage."""
+    cfg = replace(CONFIGS["tiny"], T=T, E=E, k=k, H=H, F=F)
+    d = make_inputs(cfg, DEV, seed=T + 2, weights=False)
+    mx = make_mxfp4_weights(cfg, DEV, seed=T + 2)
+    _check(cfg, d, mx, "auto", what="mxfp4 wide T=%d E=%d H=%d" % (T, E, H))
+
+
+def test_mxfp4_wide_ds_v3_dims_sampled():
+    """DeepSeek-V3 dimensions and routing with 32 experts at 512 tokens (128 routed rows per
+    expert, as at 4096 tokens of 256): the 256 x 256 MXFP4 tile over 112 and 32 k-steps, tokens
+    chosen from the realized routing (the heaviest expert's last tile, every eighth of the
+    sorted routes)."""
+    cfg = replace(CONFIGS["ds-v3-grouped-prefill"], T=512, E=32)
+    d = make_inputs(cfg, DEV, seed=13, weights=False)
+    mx = make_mxfp4_weights(cfg, DEV, seed=13)
+    rid, _ = oracle_route(d, cfg)
+    _check(cfg, d, mx, "auto", routing_tokens(rid, cfg.E, 256, n=16), "mxfp4 wide ds-v3 dims")
 
 
 def test_mxfp4_qwen3_235b_batch_sampled():

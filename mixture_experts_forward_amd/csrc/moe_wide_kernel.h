@@ -231,10 +231,13 @@ struct NoHook {
 
 // MX: the weights are MXFP4 (g.wq, g.wscale) and are dequantised into the bf16 weight stages
 // (k_loop_mx below); sorted rows, the whole K range, K a multiple of 256.
+// settle (optional): a value the hook loads (the next tile's number); the tile takes it after
+// its K loop, before its output stores, so that waiting for that load cannot include them.
 template <bool GATE_UP, int SRC, int WS, int DT, bool MX = false, typename Hook = NoHook>
 __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mtile, int expert,
                                           moe_u32x4 *smem, int kbeg = 0, int kcnt = -1,
-                                          float *part = nullptr, Hook hook = Hook())
+                                          float *part = nullptr, Hook hook = Hook(),
+                                          const int *settle = nullptr)
 {
     using St = Stage<kStep>;
     constexpr int kSlots = St::kSlots, kRows = St::kRowsPerLoad;
@@ -581,6 +584,9 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
         }
     }
 
+    if (settle != nullptr)
+        asm volatile("" ::"v"(*settle));
+
     // ---- epilogue.  For weight tile n, register 4q' + q holds column 8q' + 4*(lane/32) + q of
     // the tile, row 32*(wm + 4m) + lane%32.  The bf16 tile (kBM rows x TC columns) goes through
     // LDS so that global stores write whole rows: 16-byte chunk c of row r sits at chunk
@@ -675,6 +681,16 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
     }
 }
 
+// Barrier between tiles: only LDS accesses need ordering there (the epilogue's reads of its
+// staged output, a tile number passed through LDS), so it waits on lgkmcnt alone;
+// __syncthreads() would also wait for the tile's output stores to be acknowledged (vmcnt(0)),
+// exposing their write latency once per tile.  The next tile's counted DMA waits stay correct
+// with older stores outstanding: a load's data only returns after the loads issued before it.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Tile t of the schedule's range p (p = 0..8: the range starts, in tiles of a GEMM with
 // n_blocks column blocks; range 8's start is the tile count).
 __device__ __forceinline__ int sched_bound(const moe::TileSchedule *sched, int p, int n_blocks,
@@ -698,8 +714,11 @@ __device__ __forceinline__ void wide_queue_loop(const GemmProblem &g, int n_bloc
                                                 moe_u32x4 *smem)
 {
     constexpr int P = moe::kSchedParts;
-    // thread 0 passes the tile number through the first word of the (idle) stage memory
-    volatile int *s_next = reinterpret_cast<volatile int *>(smem);
+    // thread 0 passes the tile number through the first word of the (idle) stage memory (an
+    // LDS pointer: ds accesses, counted by lgkmcnt alone)
+    volatile __attribute__((address_space(3))) int *s_next =
+        (volatile __attribute__((address_space(3))) int *)(smem);
+
     moe::TileSchedule *sched = g.sched;
     const int home = blockIdx.x % kXcds;
     // thread 0's state: ranges found used up, the bounds [lo, hi) of the range it takes from,
@@ -728,25 +747,28 @@ __device__ __forceinline__ void wide_queue_loop(const GemmProblem &g, int n_bloc
         range();
         *s_next = next_tile();
     }
-    __syncthreads();
+    lds_barrier();
     int t = *s_next;
-    __syncthreads();  // every wave has read it before the tile's loads overwrite the stage
+    lds_barrier();  // every wave has read it before the tile's loads overwrite the stage
     while (t >= 0) {
         int nblk, mtile, expert;
         wide_decode<SRC>(g, t, n_blocks, 0, nblk, mtile, expert);
         // Three k-steps before the tile ends, thread 0 takes the next tile number from its
         // range's counter; the round trip overlaps the tile's last k-steps and the result is
         // first read after the tile (the take needs no load: the bounds are in registers).
-        wide_tile<GATE_UP, SRC, WS, DT, MX>(g, nblk, mtile, expert, smem, 0, -1, nullptr, [&]() {
-            if (threadIdx.x == 0 && tried < P && lo < hi)
-                pend = atomicAdd(&sched->queue[(home + tried) % P], 1);
-        });
-        __syncthreads();  // every wave is done with the tile's LDS
+        wide_tile<GATE_UP, SRC, WS, DT, MX>(
+            g, nblk, mtile, expert, smem, 0, -1, nullptr,
+            [&]() {
+                if (threadIdx.x == 0 && tried < P && lo < hi)
+                    pend = atomicAdd(&sched->queue[(home + tried) % P], 1);
+            },
+            &pend);
+        lds_barrier();  // every wave is done with the tile's LDS
         if (threadIdx.x == 0)
             *s_next = next_tile();
-        __syncthreads();
+        lds_barrier();
         t = *s_next;
-        __syncthreads();  // every wave has read it before the next tile's loads overwrite it
+        lds_barrier();  // every wave has read it before the next tile's loads overwrite it
     }
     if (threadIdx.x == 0) {
         // thread 0's counter updates are complete (their results were used); the last

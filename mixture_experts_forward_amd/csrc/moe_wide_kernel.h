@@ -682,10 +682,9 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
 }
 
 // Barrier between tiles: only LDS accesses need ordering there (the epilogue's reads of its
-// staged output, a tile number passed through LDS), so it waits on lgkmcnt alone;
-// __syncthreads() would also wait for the tile's output stores to be acknowledged (vmcnt(0)),
-// exposing their write latency once per tile.  The next tile's counted DMA waits stay correct
-// with older stores outstanding: a load's data only returns after the loads issued before it.
+// staged output, the tile number passed through LDS), so it waits on lgkmcnt alone and the
+// tile's output stores stay in flight.  The next tile's counted DMA waits stay correct with
+// older stores outstanding: a load's data only returns after the loads issued before it.
 __device__ __forceinline__ void lds_barrier()
 {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -714,8 +713,9 @@ __device__ __forceinline__ void wide_queue_loop(const GemmProblem &g, int n_bloc
                                                 moe_u32x4 *smem)
 {
     constexpr int P = moe::kSchedParts;
-    // thread 0 passes the tile number through the first word of the (idle) stage memory (an
-    // LDS pointer: ds accesses, counted by lgkmcnt alone)
+    // thread 0 passes the tile number through the first word of the (idle) stage memory.  An
+    // LDS-typed pointer: through a generic one these were flat accesses, which the compiler
+    // waits for with vmcnt(0) -- and so for every output store of the tile just finished.
     volatile __attribute__((address_space(3))) int *s_next =
         (volatile __attribute__((address_space(3))) int *)(smem);
 

@@ -130,9 +130,10 @@ __device__ __forceinline__ void wait_loads(int n)
 // Workgroup barrier of a k-loop whose stages are filled by dma16: waits until at most n
 // (0 <= n <= 63) of this wave's vector-memory loads are outstanding and its LDS reads are
 // done, then s_barrier.  After it every wave's DMA of the awaited k-steps has landed in LDS and
-// every wave has finished reading the previous stage.  __syncthreads() is not used here: its
-// release fence also waits for every outstanding load (vmcnt(0)), which would drain the loads
-// of later k-steps at each step.  The "memory" clobber keeps LDS accesses on their side.
+// every wave has finished reading the previous stage.  The DMAs' LDS writes are counted by
+// vmcnt, which __syncthreads() (lgkmcnt(0) and s_barrier here) does not wait on, and the
+// compiler cannot see them; so the wait is explicit, counted to leave the later k-steps' loads
+// in flight.  The "memory" clobber keeps LDS accesses on their side.
 __device__ __forceinline__ void step_barrier(int n)
 {
 #define MOE_BAR_CASE(N)                                                                          \

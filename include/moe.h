@@ -296,7 +296,7 @@ int fused_moe_experts_stage(int stage, const uint16_t *hidden_states, const uint
  * Kernels by routed rows per expert (T*k/E): up to 8, weight streaming in 16-row passes; up to
  * 64, 64-row tiles, each wave dequantising its weight rows into its MFMA operands; above, with
  * H and F multiples of 256, 256 x 256 tiles whose weights arrive as codes and scales by DMA and
- * are dequantised into the tile's bf16 LDS stage (the bf16 pass's prefill kernel otherwise).
+ * are dequantised by each wave into its MFMA operands (the bf16 pass's prefill tile otherwise).
  * Workspace: fused_moe_mxfp4_workspace_bytes(p) bytes.
  * Errors: as fused_moe_fwd. */
 size_t fused_moe_mxfp4_workspace_bytes(const moe_params_t *p);

@@ -402,19 +402,21 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
     };
     // ---- MXFP4 weights.  A k-step of the tile's 256 weight rows is 32 code bytes a row (two
     // e2m1 codes per byte, low nibble first) and, per group of 4 k-steps, 8 E8M0 scale bytes a
-    // row (one per 32 elements); both come by DMA into LDS, the codes two k-steps ahead of the
-    // MFMAs (three 8 KB slots), the scales with the group's first k-step (two 2 KB buffers).
-    // One k-step ahead of the MFMAs each thread turns half a row's k-step (16 code bytes, one
-    // scale) into four bf16 chunks of the weight stage, in the slots the bf16 weight DMA fills,
-    // so the MFMA block is the bf16 one.  LDS: activation stages [0, 64 KB), bf16 weight stages
-    // [64, 128 KB), code slots [128, 152 KB), scale buffers [152, 156 KB).
+    // row (one per 32 elements); both come by DMA into LDS beside the activation rows, two
+    // k-steps ahead (three stages each; the scales with a group's first k-step, two buffers).
+    // No bf16 weight stage: each wave reads the codes of its own weight rows (one 16-byte read
+    // per 32-row tile and k-step, conflict-free) and turns them into its MFMA A operands in
+    // registers with v_cvt_scalef32_pk_bf16_fp4.  Within a k-step both operands take the k
+    // order permuted alike: sub-step h, lane group rq takes elements 32rq + 8h .. + 7 (a lane's
+    // 16 code bytes then serve all four sub-steps; each dot product is unchanged).  LDS:
+    // activation stages [0, 96 KB), code slots [96, 120 KB), scale buffers [120, 124 KB).
     // DMA lanes: lane l of wave w covers weight row 32w + l/2 (codes: bytes 16(l%2) .. +15 of
     // the row's k-step; scales: the group's bytes 4(l%2) .. +3), writing LDS at 16l / 4l.
-    constexpr uint32_t kMxW = kXStages * kHalf;
+    constexpr int kMxStages = 3;
     constexpr uint32_t kMxCodeSlot = kBW * kStep / 2;
-    constexpr uint32_t kMxCodes = kMxW + 2 * kHalf;
+    constexpr uint32_t kMxCodes = kMxStages * kHalf;
     constexpr uint32_t kMxScaleBuf = kBW * 8;
-    constexpr uint32_t kMxScales = kMxCodes + 3 * kMxCodeSlot;
+    constexpr uint32_t kMxScales = kMxCodes + kMxStages * kMxCodeSlot;
     static_assert(kMxScales + 2 * kMxScaleBuf <= wide_lds_bytes<3>(), "MX stages fit the LDS");
     const uint8_t *mx_code = nullptr, *mx_scale = nullptr;
     if (MX) {
@@ -425,73 +427,80 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
         mx_code = g.wq + row * (size_t)(K / 2) + 16 * (lane & 1);
         mx_scale = g.wscale + row * (size_t)(K / 32) + 4 * (lane & 1);
     }
-    auto issue_c = [&](int i) {  // codes of k-step i (and, at a group's first, its scales)
+    int mx_nx = 0;  // this wave's activation DMAs per k-step
+#pragma unroll
+    for (int j = 0; j < kXLoads; ++j)
+        mx_nx += xload[j] ? 1 : 0;
+    // k-step i's activation rows, codes and (at a group's first k-step) scales
+    auto issue_mx = [&](int i) {
         const int ks = (i + rot) % nk;
+        const int st = i % kMxStages;
+#pragma unroll
+        for (int j = 0; j < kXLoads; ++j)
+            if (xload[j])
+                dma16(xsrc[j] + ks * kStep, x_dst + st * kHalf + j * 1024);
         dma16(mx_code + ks * 32,
-              __builtin_amdgcn_readfirstlane(lds0 + kMxCodes + (i % 3) * kMxCodeSlot + wv * 1024));
+              __builtin_amdgcn_readfirstlane(lds0 + kMxCodes + st * kMxCodeSlot + wv * 1024));
         if (i % 4 == 0)
             dma4(mx_scale + ks * 2, __builtin_amdgcn_readfirstlane(
                                         lds0 + kMxScales + ((i / 4) % 2) * kMxScaleBuf + wv * 256));
     };
-    auto dequant = [&](int i) {  // k-step i's codes -> bf16 weight stage i % 2
-        const int r = tid >> 1, hh = tid & 1;
-        const int ks = (i + rot) % nk;
-        const uint8_t *sm8 = reinterpret_cast<const uint8_t *>(smem);
-        const moe_u32x4 q = *reinterpret_cast<const moe_u32x4 *>(
-            sm8 + kMxCodes + (i % 3) * kMxCodeSlot + r * 32 + 16 * hh);
-        const float sc = moe_mx::e8m0_to_f32(
-            sm8[kMxScales + ((i / 4) % 2) * kMxScaleBuf + r * 8 + (ks % 4) * 2 + hh]);
-        moe_u32x4 *wst = smem + (kMxW + (i % 2) * kHalf) / 16;
-        wst[St::slot(r, 4 * hh + 0)] = moe_mx::dequant8(q.x, sc);
-        wst[St::slot(r, 4 * hh + 1)] = moe_mx::dequant8(q.y, sc);
-        wst[St::slot(r, 4 * hh + 2)] = moe_mx::dequant8(q.z, sc);
-        wst[St::slot(r, 4 * hh + 3)] = moe_mx::dequant8(q.w, sc);
+    auto mx_loads = [&](int i) {  // this wave's DMAs of k-step i (0 past the K loop)
+        return i < nk ? mx_nx + 1 + (i % 4 == 0 ? 1 : 0) : 0;
     };
-    // Step i: wait for every load of this wave (x(i), the codes of i+1 and their group's
-    // scales), barrier (every wave's parts landed, its dequantised stage i written, its step
-    // i-1 reads done); issue x(i+1) and the codes of i+2 into buffers whose last readers were
-    // steps i-1 and i-2; dequantise k-step i+1 into the weight stage step i-1 read; MFMAs of i.
+    // Step i: wait until only k-step i+1's loads are outstanding, barrier (every wave's parts
+    // of k-step i landed, every wave done with step i-1); issue k-step i+2 into the stage and
+    // slot step i-1 read (its scales into the buffer of group (i+2)/4 - 2, last read at step
+    // i-3 or before); MFMAs of step i.
     auto k_loop_mx = [&](auto mtr) {
         constexpr int MTR = decltype(mtr)::value;
-        issue_x(0);
-        issue_c(0);
-        issue_c(1);
-        step_barrier(0);
-        dequant(0);
+        issue_mx(0);
+        if (1 < nk)
+            issue_mx(1);
         for (int i = 0; i < nk; ++i) {
-            step_barrier(0);
-            if (i + 1 < nk)
-                issue_x(i + 1);
+            step_barrier(mx_loads(i + 1));
             if (i + 2 < nk)
-                issue_c(i + 2);
+                issue_mx(i + 2);
             if (i == hook_at)
                 hook();
-            if (i + 1 < nk)
-                dequant(i + 1);
             if (MTR == 0)
                 continue;
-            const moe_u32x4 *xb = smem + (i % kXStages) * (kHalf / 16);
-            const moe_u32x4 *wb = smem + (kMxW + (i % 2) * kHalf) / 16;
-            moe_u32x4 a[2][kNT32], b[2][MTR > 0 ? MTR : 1];
-            auto read = [&](int buf, int h) {
+            const int ks = (i + rot) % nk;
+            const moe_u32x4 *xb = smem + (i % kMxStages) * (kHalf / 16);
+            const uint8_t *sm8 = reinterpret_cast<const uint8_t *>(smem);
+            const uint8_t *cs = sm8 + kMxCodes + (i % kMxStages) * kMxCodeSlot;
+            const uint8_t *ss = sm8 + kMxScales + ((i / 4) % 2) * kMxScaleBuf;
+            moe_u32x4 q[kNT32];
+            float sc[kNT32];
+#pragma unroll
+            for (int n = 0; n < kNT32; ++n) {
+                const int r = wrow0[n] + rr;
+                q[n] = *reinterpret_cast<const moe_u32x4 *>(cs + r * 32 + 16 * rq);
+                sc[n] = moe_mx::e8m0_to_f32(ss[r * 8 + (ks % 4) * 2 + rq]);
+            }
+            moe_u32x4 b[2][MTR > 0 ? MTR : 1];
+            auto read_b = [&](int buf, int h) {
 #pragma unroll
                 for (int m = 0; m < MTR; ++m)
-                    b[buf][m] = xb[St::slot(32 * (wm + kWM * m) + rr, 2 * h + rq)];
-#pragma unroll
-                for (int n = 0; n < kNT32; ++n)
-                    a[buf][n] = wb[St::slot(wrow0[n] + rr, 2 * h + rq)];
+                    b[buf][m] = xb[St::slot(32 * (wm + kWM * m) + rr, 4 * rq + h)];
             };
-            read(0, 0);
+            read_b(0, 0);
 #pragma unroll
             for (int h = 0; h < kStep / 16; ++h) {
                 if (h + 1 < kStep / 16)
-                    read((h + 1) & 1, h + 1);
+                    read_b((h + 1) & 1, h + 1);
+                moe_u32x4 a[kNT32];
+#pragma unroll
+                for (int n = 0; n < kNT32; ++n) {
+                    const uint32_t w = h == 0 ? q[n].x : h == 1 ? q[n].y : h == 2 ? q[n].z : q[n].w;
+                    a[n] = moe_mx::dequant8(w, sc[n]);
+                }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int n = 0; n < kNT32; ++n)
 #pragma unroll
                     for (int m = 0; m < MTR; ++m)
-                        acc[m][n] = moe_mma32<DT>(a[h & 1][n], b[h & 1][m], acc[m][n]);
+                        acc[m][n] = moe_mma32<DT>(a[n], b[h & 1][m], acc[m][n]);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }

@@ -852,7 +852,8 @@ def summarize_trace(args):
                   "plain rows, 2 SiLU(gate)*up of gate-up rows)."]
     if args.weights == "mxfp4":
         lines += ["", "MXFP4: k_mx_gemm<GATE_UP, SRC, NT, KSPLIT, STAGES> (weight streaming); "
-                  "k_mx_tiled<GATE_UP, NTW, STAGES> (64-row tiles)."]
+                  "k_mx_tiled<GATE_UP, NTW, STAGES> (64-row tiles); k_wide_mx<GATE_UP> (256 x 256 "
+                  "tiles, codes dequantised into the MFMA operands)."]
     suffix = "" if args.weights == "16bit" else "_" + args.weights
     out = os.path.join(PROFILE_DIR, "kernel_trace_%s%s.md" % (cfg.name, suffix))
     os.makedirs(PROFILE_DIR, exist_ok=True)

@@ -63,7 +63,8 @@ def test_mxfp4_small(T, path):
 
 
 def test_mxfp4_several_tiles_per_expert():
-    # about 64 rows per expert: the row-tiled form, one or two 64-row tiles per expert
+    # about 64 rows per expert (H and F multiples of 256): the 256 x 256 tile, some experts
+    # past 64 rows
     cfg = replace(CONFIGS["tiny"], T=128, H=256, E=4, F=256, k=2)
     d = make_inputs(cfg, DEV, seed=5, weights=False)
     mx = make_mxfp4_weights(cfg, DEV, seed=5)
@@ -89,6 +90,8 @@ def test_mxfp4_grouped_sigmoid_routing():
     (300, 8, 4, 384, 256),     # ~150 rows per expert, H not a multiple of 256: 64-row tiles,
                                # three per expert, a ragged last one
     (70, 16, 8, 384, 128),     # ~35 rows per expert: one partial tile each, 3 k-steps
+    (96, 4, 2, 256, 256),      # ~48 rows per expert, H and F multiples of 256: still 64-row
+                               # tiles (the 256 x 256 tile takes over above 48)
     (33, 4, 2, 128, 128),      # 16-17 rows: one 16-row MFMA tile and a one-row one
 ])
 def test_mxfp4_row_tiled_sizes(T, E, k, H, F):

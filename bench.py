@@ -826,17 +826,30 @@ def summarize_trace(args):
                 cfg.E, cfg.F, cfg.k, ", shared S=%d" % cfg.S if cfg.S else ""), ""]
     for c in args.pmc_commands:
         lines += ["Command (from /tmp, repository at $R):", "", "    " + c, ""]
+    # per-dispatch durations for the median (the average includes the first, colder calls)
+    durs = {}
+    for tpath in glob.glob(os.path.join(args.summarize_trace, "**", "*kernel_trace.csv"),
+                           recursive=True):
+        for r in csv.DictReader(open(tpath)):
+            if r.get("Kernel_Name") and r.get("Start_Timestamp") and r.get("End_Timestamp"):
+                durs.setdefault(r["Kernel_Name"], []).append(
+                    int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     lines += ["Input-generation and copy kernels, and the bench's context measurements (the "
-              "streaming-read kernel and the library GEMM of its matmul), are omitted.", "",
-              "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+              "streaming-read kernel and the library GEMM of its matmul), are omitted.  The "
+              "median is over the kernel's dispatches; the average also weighs the first, colder "
+              "ones.", "",
+              "| kernel | calls | average us | median us | min us | max us |",
+              "|---|---|---|---|---|---|"]
     for r in csv.DictReader(open(path)):
         n = r["Name"]
         if "at::native" in n or "rocclr" in n or n.startswith("Cijk_") or "k_stream_read" in n:
             continue
         short = n.replace("(anonymous namespace)::", "").replace("void ", "")
         short = short.split("(")[0] if "(" in short else short
-        lines.append("| `%s` | %s | %.2f | %.2f | %.2f |" % (
-            short, r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+        d = sorted(durs.get(n, []))
+        med = "%.2f" % (0.5 * (d[(len(d) - 1) // 2] + d[len(d) // 2]) / 1e3) if d else "-"
+        lines.append("| `%s` | %s | %.2f | %s | %.2f | %.2f |" % (
+            short, r["Calls"], float(r["AverageNs"]) / 1e3, med, float(r["MinNs"]) / 1e3,
             float(r["MaxNs"]) / 1e3))
     lines += ["", "Template arguments: k_ws_gemm<GATE_UP, SRC, NT, MT, KSPLIT, STAGES, DT, SEGK> "
               "(SRC 0 sorted, 1 direct, 2 dense, 3 scan; DT 0 bf16, 1 f16; SEGK k-steps per weight "

@@ -347,11 +347,11 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
     };
 
     // Pipeline, A = WS - 1 weight k-steps ahead.  Issue order: x(0) w(0) .. w(A-1), then in step
-    // i x(i+1) w(i+A).  At the top of step i this wave's outstanding loads are therefore (oldest
-    // first) ... x(i) w(i+1) .. w(i+A-1): waiting until only those weight steps are left leaves
-    // its parts of x(i) and w(i) in LDS, and the barrier publishes every wave's parts.  The
-    // barrier also guarantees that every wave has finished step i-1, whose stages x(i+1) and
-    // w(i+A) then overwrite.  The loop is
+    // i x(i+1) w(i+A).  Loads complete in issue order, so at the top of step i it is enough that
+    // only the loads issued after x(i) and w(i) are left: w(i+A-1), which step i-1 issued after
+    // x(i) (at step 0: w(1) .. w(A-1)).  That leaves this wave's parts of x(i) and w(i) in LDS,
+    // and the barrier publishes every wave's parts.  It also guarantees that every wave has
+    // finished step i-1, whose stages x(i+1) and w(i+A) then overwrite.  The loop is
     // instantiated per count MTR of real 32-row tiles of this wave, so the MFMA block has no
     // branches (a wave with none still loads its share and meets every barrier).
     auto k_loop = [&](auto mtr) {
@@ -363,7 +363,7 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
             if (s < nk)
                 issue_w(s);
         for (int i = 0; i < nk; ++i) {
-            step_barrier(min(A - 1, nk - 1 - i) * kWLoads);
+            step_barrier((i == 0 ? min(A - 1, nk - 1) : (i + A - 1 < nk ? 1 : 0)) * kWLoads);
             if (i + 1 < nk)
                 issue_x(i + 1);
             if (i + A < nk)
@@ -410,8 +410,10 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
     // order permuted alike: sub-step h, lane group rq takes elements 32rq + 8h .. + 7 (a lane's
     // 16 code bytes then serve all four sub-steps; each dot product is unchanged).  LDS:
     // activation stages [0, 96 KB), code slots [96, 120 KB), scale buffers [120, 124 KB).
-    // DMA lanes: lane l of wave w covers weight row 32w + l/2 (codes: bytes 16(l%2) .. +15 of
-    // the row's k-step; scales: the group's bytes 4(l%2) .. +3), writing LDS at 16l / 4l.
+    // DMA lanes: lane l of wave w covers weight row r = 32w + l/2 (codes: the row's 16-byte
+    // half (l%2) ^ ((r >> 3) & 1) of the k-step, so that the halves of rows 8..15 of every 16
+    // sit swapped and the 16-byte reads of 16 consecutive rows at one half hit distinct banks;
+    // scales: the group's bytes 4(l%2) .. +3), writing LDS at 16l / 4l.
     constexpr int kMxStages = 3;
     constexpr uint32_t kMxCodeSlot = kBW * kStep / 2;
     constexpr uint32_t kMxCodes = kMxStages * kHalf;
@@ -424,7 +426,7 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
         const int c = col_wg + (GATE_UP ? r % (kBW / 2) : r);
         const int src = (GATE_UP && r >= kBW / 2) ? c + g.n_out : c;
         const size_t row = (size_t)expert * w_rows + (c < g.n_out ? src : 0);
-        mx_code = g.wq + row * (size_t)(K / 2) + 16 * (lane & 1);
+        mx_code = g.wq + row * (size_t)(K / 2) + 16 * ((lane & 1) ^ ((r >> 3) & 1));
         mx_scale = g.wscale + row * (size_t)(K / 32) + 4 * (lane & 1);
     }
     int mx_nx = 0;  // this wave's activation DMAs per k-step
@@ -475,7 +477,7 @@ __device__ __forceinline__ void wide_tile(const GemmProblem &g, int nblk, int mt
 #pragma unroll
             for (int n = 0; n < kNT32; ++n) {
                 const int r = wrow0[n] + rr;
-                q[n] = *reinterpret_cast<const moe_u32x4 *>(cs + r * 32 + 16 * rq);
+                q[n] = *reinterpret_cast<const moe_u32x4 *>(cs + r * 32 + 16 * (rq ^ ((r >> 3) & 1)));
                 sc[n] = moe_mx::e8m0_to_f32(ss[r * 8 + (ks % 4) * 2 + rq]);
             }
             moe_u32x4 b[2][MTR > 0 ? MTR : 1];

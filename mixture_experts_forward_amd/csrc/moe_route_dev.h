@@ -230,9 +230,19 @@ __device__ __forceinline__ void route_token(
             first_id = e;
     }
 
-    // weights: lane j < k owns route j
-    // softmax is never grouped, so the first chosen expert holds the row's largest logit
-    const double m = (double)g[first_id];
+    // weights: lane j < k owns route j.  Softmax keys are the logits themselves, so the logits
+    // the weights need come from the registers that hold them (no second read of the row).
+    // Softmax is never grouped, so the first chosen expert holds the row's largest logit.
+    double m = 0.0;
+    if (!sigmoid) {
+        const int fe = __builtin_amdgcn_readfirstlane(first_id);  // wave-uniform already
+        float mv = 0.0f;
+#pragma unroll
+        for (int i = 0; i < SLOTS; ++i)
+            if (i == (fe >> 6))
+                mv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(key[i]), fe & 63));
+        m = (double)mv;
+    }
     double s = 0.0;
     if (sigmoid) {
         // the chosen expert's sigmoid from the lane and slot that computed it
@@ -243,8 +253,17 @@ __device__ __forceinline__ void route_token(
             if (i == slot && lane < k)
                 s = v;
         }
-    } else if (lane < k) {
-        s = exp((double)g[my_id] - m);
+    } else {
+        const int src = my_id < 0 ? 0 : (my_id & 63), slot = my_id < 0 ? 0 : (my_id >> 6);
+        float gl = 0.0f;
+#pragma unroll
+        for (int i = 0; i < SLOTS; ++i) {
+            const float v = __shfl(key[i], src);
+            if (i == slot)
+                gl = v;
+        }
+        if (lane < k)
+            s = exp((double)gl - m);
     }
     double denom = 1.0;
     if (renormalize) {
@@ -256,7 +275,7 @@ __device__ __forceinline__ void route_token(
         for (int i = 0; i < SLOTS; ++i) {
             const int e = 64 * i + lane;
             if (e < E)
-                z += exp((double)g[e] - m);
+                z += exp((double)key[i] - m);
         }
         denom = wave_sum_f64(z);
     }

@@ -367,7 +367,9 @@ def main():
                 stage_roofline[name].update(achieved_tflops=round(tf, 1),
                                             frac_of_mfma_peak=round(tf / peak_tflops, 4))
     # the committed counter summaries are of the bf16 kernels with bf16 weights
-    traffic = read_traffic(cfg.name) if args.dtype == "bf16" and args.weights == "16bit" else None
+    traffic = None
+    if args.dtype == "bf16" and args.weights in ("16bit", "mxfp4"):
+        traffic = read_traffic(cfg.name, "_mxfp4" if args.weights == "mxfp4" else "")
 
     # ---- CPU baseline: the oracle on this host
     if args.no_cpu_baseline:
@@ -722,11 +724,12 @@ BASELINE_MS = {
 }
 
 
-def read_traffic(workload):
+def read_traffic(workload, suffix=""):
     """HBM traffic of the dominant kernel from the committed rocprofv3 counter summary
-    (profiles/gate_up_<workload>_pmc.txt: a line 'traffic_bytes_per_launch: N' and the
-    library hash it was taken on), or None when absent or taken on another build."""
-    path = os.path.join(PROFILE_DIR, "gate_up_%s_pmc.txt" % workload)
+    (profiles/gate_up_<workload><suffix>_pmc.txt, suffix "_mxfp4" for MXFP4 weights: a line
+    'traffic_bytes_per_launch: N' and the hash of the kernel sources it was taken on), or None
+    when absent or taken on other sources."""
+    path = os.path.join(PROFILE_DIR, "gate_up_%s%s_pmc.txt" % (workload, suffix))
     if not os.path.exists(path):
         return None
     vals = {}
@@ -747,7 +750,14 @@ KERNEL_FAMILY_SOURCES = {
     "k_ws_gemm": ("moe_ws_kernel.h", "moe_gemm_ws.hip"),
     "k_tiled_gemm": ("moe_tiled_kernel.h", "moe_gemm_tiled.hip"),
     "k_wide_gemm": ("moe_wide_kernel.h", "moe_gemm_wide.hip"),
+    "k_mx_gemm": ("moe_mx_kernel.h", "moe_mx_dequant.h", "moe_gemm_mx.hip"),
+    "k_mx_tiled": ("moe_mx_kernel.h", "moe_mx_dequant.h", "moe_gemm_mx.hip"),
+    "k_wide_mx": ("moe_wide_kernel.h", "moe_mx_dequant.h", "moe_gemm_wide.hip"),
 }
+# template argument that holds the row source (SRC 2: the shared expert's dense rows), by
+# family; the MXFP4 row-tiled and 256 x 256 kernels run on sorted rows only
+KERNEL_FAMILY_SRC_ARG = {"k_ws_gemm": 1, "k_tiled_gemm": 1, "k_wide_gemm": 1, "k_mx_gemm": 1,
+                         "k_mx_tiled": None, "k_wide_mx": None}
 
 # GEMM roles with a counter summary each: profiles/<role>_<workload>_pmc.txt
 PMC_ROLES = ("gate_up", "down", "shared_gate_up", "shared_down")
@@ -792,7 +802,8 @@ def _role(name):
         if key in name:
             args = name.split(key, 1)[1].split(">", 1)[0].split(",")
             gate_up = args[0].strip() == "true"
-            dense = args[1].strip() == "2"
+            src = KERNEL_FAMILY_SRC_ARG[fam]
+            dense = src is not None and args[src].strip() == "2"
             return ("shared_" if dense else "") + ("gate_up" if gate_up else "down")
     return None
 
@@ -885,11 +896,14 @@ def summarize_pmc(args):
               "down": "the down GEMM of the routed experts",
               "shared_gate_up": "the shared expert's gate-up GEMM",
               "shared_down": "the shared expert's down GEMM"}
+    wsuffix = "_mxfp4" if args.weights == "mxfp4" else ""
+    wnote = " (MXFP4 expert weights)" if wsuffix else ""
     for role in PMC_ROLES:
         if not any(_role(n) == role for n, _ in runs[0].values()):
             continue
         res = {}
-        lines = ["# HBM traffic and MFMA activity of %s, workload %s" % (titles[role], cfg.name),
+        lines = ["# HBM traffic and MFMA activity of %s%s, workload %s"
+                 % (titles[role], wnote, cfg.name),
                  "# FETCH_SIZE / WRITE_SIZE are per-dispatch KiB; each is scaled by the reading of "
                  "the same counter for one plain device-to-device copy of known size in the same "
                  "run.", "#"]
@@ -920,7 +934,7 @@ def summarize_pmc(args):
                   "fetch_bytes_per_launch: %.0f" % res["FETCH_SIZE"],
                   "write_bytes_per_launch: %.0f" % res["WRITE_SIZE"],
                   "traffic_bytes_per_launch: %.0f" % (res["FETCH_SIZE"] + res["WRITE_SIZE"])]
-        path = os.path.join(PROFILE_DIR, "%s_%s_pmc.txt" % (role, cfg.name))
+        path = os.path.join(PROFILE_DIR, "%s_%s%s_pmc.txt" % (role, cfg.name, wsuffix))
         os.makedirs(PROFILE_DIR, exist_ok=True)
         open(path, "w").write("\n".join(lines) + "\n")
         print("\n".join(lines))

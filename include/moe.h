@@ -294,7 +294,8 @@ int fused_moe_experts_stage(int stage, const uint16_t *hidden_states, const uint
  * H % 128 == 0 and F % 128 == 0; 16-byte aligned hidden_states, the code tensors, out and the
  * workspace, 4-byte aligned scale tensors.  No shared expert.
  * Kernels by routed rows per expert (T*k/E): up to 8, weight streaming in 16-row passes; up to
- * 48, 64-row tiles, each wave dequantising its weight rows into its MFMA operands; above, with
+ * 64 (48 with grouped routing, whose busiest experts take far more than the mean), 64-row
+ * tiles, each wave dequantising its weight rows into its MFMA operands; above, with
  * H and F multiples of 256, 256 x 256 tiles whose weights arrive as codes and scales by DMA and
  * are dequantised by each wave into its MFMA operands (the bf16 pass's prefill tile otherwise).
  * Workspace: fused_moe_mxfp4_workspace_bytes(p) bytes.

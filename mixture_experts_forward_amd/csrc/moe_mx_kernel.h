@@ -8,7 +8,7 @@
 //
 // Built for the decode shapes it is meant for (weight-bound):
 //   - lane l of a wave owns weight row l%16 of each 16-row tile and 32-element block l/16 of each
-//     128-element k-step: one 16-byte non-temporal load (32 codes) and one scale byte per tile
+//     128-element k-step: one 16-byte load (32 codes) and one scale byte per tile
 //     and k-step, STAGES-1 k-steps ahead in registers;
 //   - the gfx950 conversion v_cvt_scalef32_pk_bf16_fp4 turns a byte into two bf16 values times
 //     the block's scale (exact: an e2m1 value has at most two significant bits), sixteen of them
@@ -137,8 +137,7 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_mx_gemm(GemmProblem g)
 #pragma unroll
             for (int nw = 0; nw < NW; ++nw) {
                 if (tile_ok[nw % NT]) {
-                    wraw[st][nw] = __builtin_nontemporal_load(
-                        reinterpret_cast<const moe_u32x4 *>(wq[nw] + k / 2));
+                    wraw[st][nw] = *(reinterpret_cast<const moe_u32x4 *>(wq[nw] + k / 2));
                     sraw[st][nw] = wsc[nw][k / 32];
                 }
             }
@@ -240,8 +239,13 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_mx_gemm(GemmProblem g)
 //     4p + j of 16 different rows) and the row-wise writes are free of bank conflicts; one
 //     barrier per k-step;
 //   - the 16-row MFMA tiles past the tile's last routed row are skipped;
-//   - tile numbering and the rotated K start as the bf16 row-tiled kernel (row tiles of one
-//     column block consecutive on one XCD).
+//   - tile numbering and the rotated K start as the bf16 row-tiled kernel on sorted rows (the
+//     column blocks of one row tile consecutive on one XCD, sharing its activation rows through
+//     L2; only the real row tiles dealt out): Qwen3-235B batch 0.532 -> 0.519 ms, Qwen3-30B at
+//     160 tokens 0.166 -> 0.158 ms.
+// The code loads of both kernels are plain loads: a k-step reads 64 of a weight row's 128-byte
+// line and the next k-step the other half, so the lines are worth keeping in L2 (non-temporal
+// loads measured 15 % slower here at 11 and 32 rows per expert).
 template <bool GATE_UP, int NTW, int STAGES>
 __global__ __launch_bounds__(256) void k_mx_tiled(GemmProblem g, int n_blocks, int m_tiles)
 {
@@ -254,13 +258,17 @@ __global__ __launch_bounds__(256) void k_mx_tiled(GemmProblem g, int n_blocks, i
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-    const int nb_total = moe_tiled::tiled_grid(n_blocks, m_tiles);
-    const int per_xcd = nb_total / moe_tiled::kXcds;
-    const int logical = (blockIdx.x % moe_tiled::kXcds) * per_xcd + blockIdx.x / moe_tiled::kXcds;
-    if (logical >= n_blocks * m_tiles)
+    const int real_tiles = g.offsets[g.num_experts] / BM;
+    const int total = real_tiles * n_blocks;
+    const int per_xcd = (total + moe_tiled::kXcds - 1) / moe_tiled::kXcds;
+    const int idx = blockIdx.x / moe_tiled::kXcds;
+    if (idx >= per_xcd)
         return;
-    const int nblk = logical / m_tiles;
-    const int mtile = logical % m_tiles;
+    const int logical = (blockIdx.x % moe_tiled::kXcds) * per_xcd + idx;
+    if (logical >= total)
+        return;
+    const int mtile = logical / n_blocks;
+    const int nblk = logical % n_blocks;
     const int row0 = mtile * BM;
     const int expert = g.tile_expert[mtile];
     if (expert < 0)
@@ -324,8 +332,7 @@ __global__ __launch_bounds__(256) void k_mx_tiled(GemmProblem g, int n_blocks, i
         const int k = ((i + rot) % nk) * 128;
 #pragma unroll
         for (int nw = 0; nw < NW; ++nw) {
-            wraw[st][nw] = __builtin_nontemporal_load(
-                reinterpret_cast<const moe_u32x4 *>(wq[nw] + k / 2));
+            wraw[st][nw] = *(reinterpret_cast<const moe_u32x4 *>(wq[nw] + k / 2));
             sraw[st][nw] = wsc[nw][k / 32];
         }
 #pragma unroll

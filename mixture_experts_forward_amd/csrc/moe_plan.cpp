@@ -107,13 +107,18 @@ void make_plan(const moe_params_t *p, int32_t S, Plan *pl, int wfmt)
     if (wfmt == WEIGHTS_MXFP4) {
         // MXFP4 weights (W4A16): the weight-streaming form with 16-row passes up to 8 routed
         // rows per expert, the row-tiled form (64-row tiles, each weight byte feeding 64 rows)
-        // up to 48, the 256 x 256 tile with the codes dequantised into its MFMA operands above
-        // (both K, H and F, whole groups of 256).  Qwen3-235B dimensions, 256 x 256 against
-        // 64-row tiles: 32 rows per expert 0.721 against 0.606 ms, 64 rows 0.846 against 0.913.
+        // up to 64 (48 with grouped routing), the 256 x 256 tile with the codes dequantised
+        // into its MFMA operands above (both K, H and F, whole groups of 256).  256 x 256
+        // against 64-row tiles, Qwen3-235B dimensions (softmax routing): 56 rows per expert
+        // 0.795 against 0.658 ms, 64 rows 0.829 against 0.759, 80 and 96 rows even; DeepSeek-V3
+        // and Kimi-K2 dimensions with grouped routing, whose busiest experts take hundreds of
+        // rows (the 256-row tile streams their weights once per 256 rows): 64 rows 2.91 against
+        // 3.13 ms and 2.79 against 3.07.
         if (pl->path == MOE_PATH_DIRECT || mean_rows <= 8.0) {
             pl->gate_up = {KERNEL_MX, 1, 1, 2, 3};
             pl->down = {KERNEL_MX, 2, 1, 2, 3};
-        } else if (mean_rows > 48.0 && pl->H % 256 == 0 && pl->F % 256 == 0) {
+        } else if (mean_rows > (p->num_expert_group > 1 ? 48.0 : 64.0) && pl->H % 256 == 0 &&
+                   pl->F % 256 == 0) {
             pl->gate_up = {KERNEL_MX_WIDE, 0, 16, 1, 2};
             pl->down = {KERNEL_MX_WIDE, 0, 16, 1, 2};
         } else {

@@ -58,3 +58,19 @@ def test_kernel_source_hash_follows_the_kernel_family(tmp_path, monkeypatch):
     with open(csrc / "moe_device.h", "a") as f:
         f.write("\n")
     assert bench.kernel_source_hash(WIDE) != wide1 and bench.kernel_source_hash(WS) != ws1
+
+
+def test_gemm_roles_of_kernel_names():
+    """Counter summaries are filed by the GEMM role read from the kernel name: the 16-bit
+    families carry their row source as the second template argument (2: the shared expert's
+    dense rows); the MXFP4 row-tiled and 256 x 256 kernels run on sorted rows only, so their
+    second argument (a tile width) never marks them as the shared expert."""
+    assert bench._role(WIDE) == "gate_up"
+    assert bench._role(WS) == "down"
+    assert bench._role("void moe_wide::k_wide_gemm<false, 2, 3, 0>(moe::GemmProblem, int, int)") \
+        == "shared_down"
+    assert bench._role("void moe_wide::k_wide_mx<true>(moe::GemmProblem, int, int)") == "gate_up"
+    assert bench._role("void moe_mx::k_mx_tiled<false, 2, 3>(moe::GemmProblem, int, int)") \
+        == "down"
+    assert bench._role("void moe_mx::k_mx_gemm<true, 3, 1, 2, 3>(moe::GemmProblem)") == "gate_up"
+    assert bench._role("void k_combine<0>(unsigned short const*)") is None

@@ -90,8 +90,9 @@ def test_mxfp4_grouped_sigmoid_routing():
     (300, 8, 4, 384, 256),     # ~150 rows per expert, H not a multiple of 256: 64-row tiles,
                                # three per expert, a ragged last one
     (70, 16, 8, 384, 128),     # ~35 rows per expert: one partial tile each, 3 k-steps
-    (96, 4, 2, 256, 256),      # ~48 rows per expert, H and F multiples of 256: still 64-row
-                               # tiles (the 256 x 256 tile takes over above 48)
+    (96, 4, 2, 256, 256),      # ~48 rows per expert, H and F multiples of 256: 64-row tiles
+    (128, 4, 2, 256, 256),     # 64 rows, ungrouped routing: still 64-row tiles (the 256 x 256
+                               # tile takes over above 64, above 48 with grouped routing)
     (33, 4, 2, 128, 128),      # 16-17 rows: one 16-row MFMA tile and a one-row one
 ])
 def test_mxfp4_row_tiled_sizes(T, E, k, H, F):

@@ -75,7 +75,7 @@ bool launch_mx_tiled(bool gate_up, const GemmProblem &g, RowSource src, WsTile t
         return true;                                                                             \
     }
     MOE_MXT_CASE(true, 1, 3)
-    MOE_MXT_CASE(false, 2, 3)
+    MOE_MXT_CASE(false, 2, 2)
 #undef MOE_MXT_CASE
     return false;
 }

@@ -117,7 +117,9 @@ void make_plan(const moe_params_t *p, int32_t S, Plan *pl, int wfmt)
         // 0.795 against 0.658 ms, 64 rows 0.829 against 0.759, 80 and 96 rows even; DeepSeek-V3
         // and Kimi-K2 dimensions with grouped routing, whose busiest experts take hundreds of
         // rows (the 256-row tile streams their weights once per 256 rows): 64 rows 2.91 against
-        // 3.13 ms and 2.79 against 3.07.
+        // 3.13 ms and 2.79 against 3.07.  The row-tiled down GEMM keeps one k-step ahead (its K
+        // loop is short: Qwen3-235B batch 0.515 -> 0.503 ms, 16 rows per expert at Kimi-K2 and
+        // DeepSeek-V3 dimensions 1.593 -> 1.565 and 1.636 -> 1.607 ms against two steps ahead).
         if (pl->path == MOE_PATH_DIRECT || mean_rows <= 8.0) {
             pl->gate_up = {KERNEL_MX, 1, 1, 2, 3};
             pl->down = {KERNEL_MX, 2, 1, 2, 3};
@@ -127,7 +129,7 @@ void make_plan(const moe_params_t *p, int32_t S, Plan *pl, int wfmt)
             pl->down = {KERNEL_MX_WIDE, 0, 16, 1, 2};
         } else {
             pl->gate_up = {KERNEL_MX_TILED, 1, 4, 1, 3};
-            pl->down = {KERNEL_MX_TILED, 2, 4, 1, 3};
+            pl->down = {KERNEL_MX_TILED, 2, 4, 1, 2};
         }
     }
     pl->shared_gate_up = {KERNEL_WIDE, 0, 16, 1, 2};

@@ -85,7 +85,7 @@ def main():
         summarize_trace(args)
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d "
+        print("bench.py measures one GPU: the library has no multi-GPU path (--gpus %d "
               "requested). Run with --gpus 1." % args.gpus, file=sys.stderr)
         sys.exit(2)
 

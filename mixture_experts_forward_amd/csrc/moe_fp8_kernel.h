@@ -1034,12 +1034,8 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_fp8_direct(Fp8Direct d)
             const float sc = amax == 0.0f ? 1.0f : amax / 448.0f;
             if (sub == 0)
                 s_scale[r * KB + g] = sc;
-            uint32_t lo = 0, hi = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                lo |= moe::e4m3_code(v[i] / sc) << (8 * i);
-                hi |= moe::e4m3_code(v[4 + i] / sc) << (8 * i);
-            }
+            const uint32_t lo = moe::e4m3_pack4(v[0] / sc, v[1] / sc, v[2] / sc, v[3] / sc);
+            const uint32_t hi = moe::e4m3_pack4(v[4] / sc, v[5] / sc, v[6] / sc, v[7] / sc);
             const int chunk = 8 * g + (sub >> 1);  // this lane's 8 codes: half (sub & 1) of it
             moe_u32x2 packed;
             packed.x = lo;

@@ -32,4 +32,19 @@ __device__ __forceinline__ uint32_t e4m3_code(float v)
     return code | sign;
 }
 
+// The codes of v0..v3 as bytes 0..3 of a word, equal to e4m3_code of each.  Below 464 in
+// magnitude (448 is the largest code; the quantiser's quotients never exceed 448 by more than
+// rounding) gfx950's v_cvt_pk_fp8_f32 rounds every f32 exactly as e4m3_code does (checked
+// against it on all 2^32 bit patterns); from 464 up it gives NaN where e4m3_code saturates,
+// so such lanes, and NaN, take e4m3_code.
+__device__ __forceinline__ uint32_t e4m3_pack4(float v0, float v1, float v2, float v3)
+{
+    const float m = fmaxf(fmaxf(fabsf(v0), fabsf(v1)), fmaxf(fabsf(v2), fabsf(v3)));
+    if (m < 464.0f) {  // false for NaN too
+        const int w = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+        return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, w, true);
+    }
+    return e4m3_code(v0) | (e4m3_code(v1) << 8) | (e4m3_code(v2) << 16) | (e4m3_code(v3) << 24);
+}
+
 }  // namespace moe

@@ -75,12 +75,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_fp8(const uint16_t *__restri
         scale[(size_t)row * G + g] = s;
     if (!in)
         return;
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        lo |= moe::e4m3_code(v[i] / s) << (8 * i);
-        hi |= moe::e4m3_code(v[4 + i] / s) << (8 * i);
-    }
+    const uint32_t lo = moe::e4m3_pack4(v[0] / s, v[1] / s, v[2] / s, v[3] / s);
+    const uint32_t hi = moe::e4m3_pack4(v[4] / s, v[5] / s, v[6] / s, v[7] / s);
     moe_u32x2 packed;
     packed.x = lo;
     packed.y = hi;

@@ -22,15 +22,8 @@ bool dispatch(const GemmProblem &g, moe::WsTile t, hipStream_t s)
         launch_one<GATE_UP, SRC, NT_, KS_, ST_>(g, s);                                           \
         return true;                                                                             \
     }
-    MOE_MX_CASE(1, 4, 3)
     MOE_MX_CASE(1, 2, 3)
-    MOE_MX_CASE(1, 2, 5)
-    MOE_MX_CASE(2, 2, 5)
-    MOE_MX_CASE(2, 1, 4)
     MOE_MX_CASE(2, 2, 3)
-    MOE_MX_CASE(2, 4, 3)
-    MOE_MX_CASE(4, 1, 4)
-    MOE_MX_CASE(4, 2, 3)
 #undef MOE_MX_CASE
     return false;
 }

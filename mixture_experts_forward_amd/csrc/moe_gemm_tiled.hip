@@ -31,7 +31,6 @@ bool dispatch(const GemmProblem &g, moe::WsTile t, hipStream_t s)
         launch_one<GATE_UP, SRC, BM_, NTW_, ST_>(g, s);                                          \
         return true;                                                                             \
     }
-    MOE_TILED_CASE(64, 1, 3)
     MOE_TILED_CASE(64, 2, 3)
     MOE_TILED_CASE(64, 2, 2)
     MOE_TILED_CASE(64, 4, 2)

@@ -13,7 +13,8 @@ void launch_one(const GemmProblem &g, hipStream_t stream)
                        dim3(64 * KSPLIT), 0, stream, g);
 }
 
-// Instantiated shapes (NT 16-column tiles per workgroup, KSPLIT waves, STAGES).
+// Instantiated shapes (NT 16-column tiles per workgroup, KSPLIT waves, STAGES), per
+// direction: those the host plan picks.
 template <bool GATE_UP, int SRC>
 bool dispatch(const GemmProblem &g, moe::WsTile t, hipStream_t s)
 {
@@ -22,8 +23,11 @@ bool dispatch(const GemmProblem &g, moe::WsTile t, hipStream_t s)
         launch_one<GATE_UP, SRC, NT_, KS_, ST_>(g, s);                                           \
         return true;                                                                             \
     }
-    MOE_MX_CASE(1, 2, 3)
-    MOE_MX_CASE(2, 2, 3)
+    if constexpr (GATE_UP) {
+        MOE_MX_CASE(1, 2, 3)
+    } else {
+        MOE_MX_CASE(2, 2, 3)
+    }
 #undef MOE_MX_CASE
     return false;
 }

@@ -22,7 +22,8 @@ void launch_one(const GemmProblem &g, hipStream_t stream)
                            m_tiles);
 }
 
-// Instantiated tile shapes (BM rows, NTW 16-column tiles per wave, STAGES).
+// Instantiated tile shapes (BM rows, NTW 16-column tiles per wave, STAGES), per direction:
+// those the host plan picks.
 template <bool GATE_UP, int SRC>
 bool dispatch(const GemmProblem &g, moe::WsTile t, hipStream_t s)
 {
@@ -31,9 +32,12 @@ bool dispatch(const GemmProblem &g, moe::WsTile t, hipStream_t s)
         launch_one<GATE_UP, SRC, BM_, NTW_, ST_>(g, s);                                          \
         return true;                                                                             \
     }
-    MOE_TILED_CASE(64, 2, 3)
-    MOE_TILED_CASE(64, 2, 2)
-    MOE_TILED_CASE(64, 4, 2)
+    if constexpr (GATE_UP) {
+        MOE_TILED_CASE(64, 2, 2)
+    } else {
+        MOE_TILED_CASE(64, 2, 3)
+        MOE_TILED_CASE(64, 4, 2)
+    }
 #undef MOE_TILED_CASE
     return false;
 }

@@ -35,7 +35,8 @@ void launch_one(const GemmProblem &g, hipStream_t stream)
         launch_seg<GATE_UP, SRC, NT, MT, KSPLIT, STAGES, 1>(g, stream);
 }
 
-// Instantiated tile shapes.  Every shape the host plan may pick must be listed here.
+// Instantiated tile shapes, per direction.  Every shape the host plan may pick must be
+// listed here, and nothing else.
 template <bool GATE_UP, int SRC>
 bool dispatch(const GemmProblem &g, moe::WsTile t, hipStream_t s)
 {
@@ -44,9 +45,12 @@ bool dispatch(const GemmProblem &g, moe::WsTile t, hipStream_t s)
         launch_one<GATE_UP, SRC, NT_, MT_, KS_, ST_>(g, s);                                      \
         return true;                                                                             \
     }
-    MOE_WS_CASE(1, 1, 4, 3)
-    MOE_WS_CASE(2, 1, 4, 2)
-    MOE_WS_CASE(2, 1, 2, 3)
+    if constexpr (GATE_UP) {
+        MOE_WS_CASE(1, 1, 4, 3)
+    } else {
+        MOE_WS_CASE(2, 1, 4, 2)
+        MOE_WS_CASE(2, 1, 2, 3)
+    }
 #undef MOE_WS_CASE
     return false;
 }
